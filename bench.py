@@ -1,0 +1,267 @@
+"""Benchmark of the 2D relative-position attention forward on one MI355X.
+
+A step is one forward pass of the headline workload (DeiT-S with iRPE
+contextual Product keys: batch 64, 14 x 14 grid + class token, 6 heads,
+d = 64, bf16, an 81 x 64 key table shared by the heads) over one batch of
+synthetic input already in HBM.  The timed steps cycle through enough input
+copies that the working set is larger than the 256 MB Infinity Cache, so
+every step reads its inputs from HBM; the same launch on one resident buffer
+set is reported as "warm".  The other bf16 workloads (Swin-T stage-1 windows,
+DeiT-S with query/key/value terms, the 56 x 56 high-resolution grid) are
+timed the same way and reported under "secondary".
+
+Per-launch kernel time comes from HIP events on the stream the kernel is
+launched on.  Algorithmic counts: FLOP = 4 T^2 d per unit (QK^T and PV) +
+2 n K d per contextual term (n positioned tokens, K table rows); bytes = q,
+k, v read once + o written once.
+
+The CPU baseline is the fp64 oracle, run in a process pool over (batch,
+head) images of the same workload before the GPU is touched.
+"""
+
+import argparse
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from vision_transformer_attention_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
+
+METRIC = "2D-RPE attention fwd TFLOP/s and % bf16 MFMA peak (DeiT-S iRPE-K, Swin-T W7)"
+HEADLINE = "deit_s_irpe_k"
+SECONDARY = ("swin_t_w7", "deit_s_irpe_qkv", "highres_irpe_k")
+PEAK_MFMA_BF16 = 2500.0      # TFLOP/s, dense, MI355X
+PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
+MALL_BYTES = 256 << 20
+COLD_SET_BYTES = 512 << 20   # cycle through at least this much input per step sequence
+
+
+def flops_bytes(w):
+    """Algorithmic FLOP and HBM bytes of one forward of workload w."""
+    r, c = (w.window, w.window) if w.window else (w.grid_h, w.grid_w)
+    n = r * c
+    t = w.prefix + n
+    units = w.batch * w.heads * ((w.grid_h // w.window) * (w.grid_w // w.window) if w.window else 1)
+    terms = len(w.terms) if w.mode == "contextual" else 0
+    flop = units * (4.0 * t * t * w.head_dim + terms * 2.0 * n * w.table_rows * w.head_dim)
+    elem = 2 if w.dtype == "bf16" else 4
+    nbytes = 4.0 * w.batch * w.heads * w.tokens * w.head_dim * elem
+    return flop, nbytes
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+
+_CPU = {}
+
+
+def _oracle_worker(args):
+    name, pairs = args
+    from oracle import Spec, attention
+    import numpy as np
+    w = WORKLOADS[name]
+    x = _CPU["x"]
+    spec = Spec(w.grid_h, w.grid_w, window=w.window, prefix=w.prefix, mode=w.mode, terms=w.terms, map=w.map,
+                alpha=w.alpha, beta=w.beta, gamma=w.gamma, reading=w.reading,
+                tables_per_head=w.tables_per_head)
+    for b, h in pairs:
+        attention(spec, x["q"], x["k"], x["v"], bias=x.get("bias"), rq=x.get("rq"), rk=x.get("rk"),
+                  rv=x.get("rv"), batch_sel=[b], heads_sel=[h])
+    return len(pairs)
+
+
+def cpu_baseline(name, budget_s=20.0):
+    """Time the oracle over a bounded sample of (batch, head) images of `name`."""
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:
+        limiter = None
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    _CPU["x"] = x
+    # estimate the per-image cost on one image
+    t0 = time.perf_counter()
+    _oracle_worker((name, [(0, 0)]))
+    per_img = max(time.perf_counter() - t0, 1e-3)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    n_img = w.batch * w.heads
+    n_sample = max(cores, min(n_img, int(budget_s / per_img)))
+    pairs = [(i // w.heads, i % w.heads) for i in range(n_sample)]
+    chunks = [pairs[i::cores] for i in range(cores)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_worker, [(name, c) for c in chunks if c]))
+        wall = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    flop, _ = flops_bytes(w)
+    flop_sample = flop * done / n_img
+    _CPU.clear()
+    return {"value": flop_sample / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {n_img} (batch, head) images of {name}, fp64 NumPy oracle, "
+                      f"{wall:.2f} s wall on {cores} processes (1 BLAS thread each)",
+            "seconds": wall}
+
+
+# ------------------------------------------------------------------------------ GPU timing
+
+def _device_inputs(w, copies, dev):
+    import torch
+    x = make_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    base = {n: torch.from_numpy(a).to(torch.float32 if n == "bias" else tdt).to(dev).contiguous()
+            for n, a in x.items()}
+    sets = [base]
+    for _ in range(copies - 1):
+        sets.append({n: (t.clone() if n in ("q", "k", "v") else t) for n, t in base.items()})
+    outs = [torch.empty_like(base["q"]) for _ in range(copies)]
+    return sets, outs
+
+
+def _prepared(w, d, o):
+    import vision_transformer_attention_amd as pkg
+    return pkg.prepare_fwd(d["q"], d["k"], d["v"], out=o, grid=(w.grid_h, w.grid_w), window=w.window,
+                           prefix_tokens=w.prefix, mode=w.mode, terms="".join(sorted(w.terms)), map=w.map,
+                           alpha=w.alpha, beta=w.beta, gamma=w.gamma, rounding=w.reading,
+                           bias=d.get("bias"), rq=d.get("rq"), rk=d.get("rk"), rv=d.get("rv"))
+
+
+def time_workload(name, steps, warmup, dev, cold=True):
+    """Average per-launch time (ms) over `steps` launches, HIP events on the launch stream."""
+    import torch
+    w = WORKLOADS[name]
+    _, nbytes = flops_bytes(w)
+    copies = max(1, math.ceil(COLD_SET_BYTES / nbytes)) if cold else 1
+    sets, outs = _device_inputs(w, copies, dev)
+    calls = [_prepared(w, sets[i], outs[i]) for i in range(copies)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    for i in range(warmup):
+        calls[i % copies](sp)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        calls[i % copies](sp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    ok = bool(torch.isfinite(outs[0]).all().item())
+    del sets, outs, calls
+    torch.cuda.empty_cache()
+    return ms, wall, copies, ok
+
+
+def summarize(name, ms):
+    w = WORKLOADS[name]
+    flop, nbytes = flops_bytes(w)
+    tflops = flop / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "tflops": tflops, "mfma_frac": tflops / PEAK_MFMA_BF16, "gbs": gbs,
+            "hbm_frac": gbs / PEAK_HBM, "flop": flop, "bytes": nbytes}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--warm-only", action="store_true", help="time one resident buffer set only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards by batch/head with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload)       # before any GPU call (forks a pool)
+        print(f"cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
+
+    import torch
+    dev = torch.device("cuda:0")
+    import vision_transformer_attention_amd as pkg
+    pkg.load()
+
+    torch.cuda.synchronize()
+    ms_cold, wall, copies, ok = time_workload(args.workload, args.steps, args.warmup, dev,
+                                              cold=not args.warm_only)
+    print(f"{args.workload}: {ms_cold * 1e3:.2f} us/launch over {copies} buffer sets, finite={ok}",
+          file=sys.stderr, flush=True)
+    ms_warm, _, _, _ = time_workload(args.workload, args.steps, args.warmup, dev, cold=False)
+    head = summarize(args.workload, ms_cold)
+    warm = summarize(args.workload, ms_warm)
+    w = WORKLOADS[args.workload]
+    secondary = {}
+    if not args.no_secondary:
+        for name in SECONDARY:
+            if name == args.workload:
+                continue
+            mc, _, _, okc = time_workload(name, args.steps, args.warmup, dev, cold=True)
+            mw, _, _, _ = time_workload(name, args.steps, args.warmup, dev, cold=False)
+            s = summarize(name, mc)
+            sw = summarize(name, mw)
+            secondary[name] = {"description": WORKLOADS[name].description, "us_per_launch": mc * 1e3,
+                               "tflops": s["tflops"], "mfma_frac": s["mfma_frac"], "gbs": s["gbs"],
+                               "hbm_frac": s["hbm_frac"], "warm_us_per_launch": mw * 1e3,
+                               "warm_tflops": sw["tflops"], "warm_mfma_frac": sw["mfma_frac"],
+                               "finite": okc}
+            print(f"{name}: {mc * 1e3:.2f} us cold, {mw * 1e3:.2f} us warm", file=sys.stderr, flush=True)
+    flop, nbytes = flops_bytes(w)
+    intensity = flop / nbytes
+    ridge = PEAK_MFMA_BF16 * 1e12 / (PEAK_HBM * 1e9)
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM, "unit": "GB/s",
+                "frac": head["gbs"] / PEAK_HBM, "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_MFMA_BF16, "unit": "TFLOP/s",
+                "frac": head["tflops"] / PEAK_MFMA_BF16, "traffic": None}
+    roof["kernel"] = "rpe_fwd_kernel"
+    roof["algorithmic_bytes_per_launch"] = nbytes
+    roof["algorithmic_flop_per_launch"] = flop
+    line = {
+        "metric": METRIC,
+        "value": head["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_cold,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) tables; inputs cycled through "
+                f"{copies} HBM-resident copies so each step reads from HBM)",
+        "config": {"workload": w.description, "global_batch": w.batch, "seq_len": w.tokens,
+                   "parallelism": "none (1 GPU)"},
+        "mfma_frac": head["mfma_frac"],
+        "roofline": roof,
+        "warm": {"us_per_launch": ms_warm * 1e3, "tflops": warm["tflops"], "mfma_frac": warm["mfma_frac"],
+                 "gbs": warm["gbs"]},
+        "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

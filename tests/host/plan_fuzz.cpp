@@ -1,0 +1,110 @@
+// Host fuzz of the launch planner (built with -fsanitize=address,undefined by
+// tests/test_host_plan.py).  For random descriptors it checks that validation
+// never crashes, and that every accepted plan keeps its LDS regions inside the
+// budget, disjoint and in order, and its work split consistent.
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+
+#include "../../vision_transformer_attention_amd/csrc/plan.h"
+
+static int fails = 0;
+#define REQUIRE(c)                                                          \
+  do {                                                                      \
+    if (!(c)) {                                                             \
+      std::printf("FAIL line %d: %s\n", __LINE__, #c);                      \
+      ++fails;                                                              \
+    }                                                                       \
+  } while (0)
+
+int main(int argc, char** argv) {
+  const int n = argc > 1 ? std::atoi(argv[1]) : 20000;
+  std::mt19937 rng(1234);
+  auto U = [&](int lo, int hi) { return std::uniform_int_distribution<int>(lo, hi)(rng); };
+  auto F = [&](double lo, double hi) { return std::uniform_real_distribution<double>(lo, hi)(rng); };
+  int accepted = 0;
+  // the null descriptor
+  REQUIRE(rpe::validate(nullptr) == RPE_E_NULL);
+  for (int it = 0; it < n; ++it) {
+    rpe_attn_desc d{};
+    const bool valid_ish = it % 2 == 1;  // half the draws stay inside the documented ranges
+    d.batch = U(-1, 8);
+    d.heads = U(0, 8);
+    const int dims[] = {8, 16, 32, 48, 64, 128};
+    d.head_dim = dims[U(0, 5)];
+    d.grid_h = U(0, 70);
+    d.grid_w = U(0, 70);
+    d.window = U(0, 3) == 0 ? U(-1, 9) : 0;
+    d.prefix_tokens = U(0, 3) == 0 ? U(-1, 17) : 0;
+    d.dtype = U(-1, 2);
+    d.mode = U(-1, 3);
+    d.terms = static_cast<uint32_t>(U(0, 9));
+    d.map = U(-1, 2);
+    d.rounding = U(-1, 2);
+    d.alpha = F(-1.0, 6.0);
+    d.beta = d.alpha + F(-1.0, 10.0);
+    d.gamma = d.alpha + F(-1.0, 60.0);
+    d.scale = U(0, 5) == 0 ? 0.0f : static_cast<float>(F(-2.0, 2.0));
+    d.tables_per_head = U(-1, 2);
+    if (valid_ish) {
+      d.batch = U(0, 8);
+      d.heads = U(1, 8);
+      d.head_dim = dims[U(1, 4) == 3 ? 4 : U(1, 2)];
+      d.dtype = U(0, 1);
+      d.mode = U(0, 2);
+      d.terms = d.mode == RPE_MODE_CONTEXTUAL ? static_cast<uint32_t>(U(1, 7)) : 0u;
+      d.map = U(0, 1);
+      d.rounding = U(0, 1);
+      d.alpha = F(0.2, 6.0);
+      d.beta = d.alpha + F(0.0, 8.0);
+      d.gamma = d.alpha + F(0.1, 60.0);
+      d.tables_per_head = U(0, 1);
+      if (U(0, 1)) {
+        const int m = U(1, 9);
+        d.window = m;
+        d.grid_h = m * U(1, 8);
+        d.grid_w = m * U(1, 8);
+        d.prefix_tokens = 0;
+      } else {
+        d.window = 0;
+        d.grid_h = U(1, 64);
+        d.grid_w = U(1, 64);
+        d.prefix_tokens = U(0, 3) == 0 ? U(0, 16) : U(0, 1);
+      }
+    }
+    rpe::Params p;
+    const int st = rpe::make_plan(&d, &p);
+    REQUIRE(st <= 0 && st >= -9);
+    REQUIRE(rpe::validate(&d) == RPE_OK || st == rpe::validate(&d));
+    if (st != RPE_OK) continue;
+    ++accepted;
+    REQUIRE(p.lds_words * 4 <= rpe::kMaxLdsBytes);
+    REQUIRE(p.off_k[0] < p.off_v[0] && p.off_v[0] < p.off_k[1] && p.off_k[1] < p.off_v[1]);
+    REQUIRE(p.off_v[1] < p.off_tab || (p.off_tab == p.off_zero));
+    REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr);
+    REQUIRE(p.zr == (p.S - 1) * p.S + 1);
+    REQUIRE(p.off_ry >= p.off_neg + p.zr);
+    REQUIRE(p.off_cx == p.off_ry + 2 * p.R - 1);
+    REQUIRE(p.off_cx + 2 * p.C - 1 <= p.lds_words);
+    REQUIRE(p.kpitch >= p.D && p.vpitch >= rpe::kBlockSlots);
+    REQUIRE(p.Wp >= p.C && p.Wp <= 16 * rpe::kMaxKP);
+    REQUIRE(p.Wp == 4 || p.Wp == 8 || p.Wp % 16 == 0);
+    REQUIRE(p.grid_blocks * rpe::kBlockSlots >= p.R * p.Wp);
+    REQUIRE(p.n_wt * 16 >= p.T && p.n_qt * p.NW >= p.n_wt);
+    REQUIRE(p.n_wg == p.n_units * p.n_qt);
+    REQUIRE(p.T == p.P + p.R * p.C);
+    REQUIRE(p.N == p.P + d.grid_h * d.grid_w);
+    REQUIRE(p.p_tab >= p.nb);
+    if (d.mode == RPE_MODE_CONTEXTUAL && (d.terms & RPE_TERM_V)) {
+      REQUIRE(p.off_w >= p.off_neg + p.zr);
+    }
+    if (d.mode == RPE_MODE_CONTEXTUAL && (d.terms & RPE_TERM_Q)) {
+      REQUIRE(p.off_tq >= p.off_neg + p.zr && p.p_tq >= p.nb);
+      REQUIRE(p.off_tqz == p.off_tq + rpe::kBlockSlots * p.p_tq && p.off_tqn == p.off_tqz + p.zr);
+    }
+    if (p.prefix_in_tail) REQUIRE(p.P <= p.Wp - p.C);
+    REQUIRE(p.prefix_block == (p.P > 0 && !p.prefix_in_tail));
+  }
+  std::printf("checked %d descriptors, %d accepted, %d failures\n", n, accepted, fails);
+  return fails ? 1 : 0;
+}

@@ -1,0 +1,134 @@
+"""C-ABI library on the CPU: it loads, exports every declared symbol, and its
+validation and size queries agree with the oracle.  No compute call is made
+(none of these entry points touches the device)."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import vision_transformer_attention_amd as pkg
+from vision_transformer_attention_amd import _lib
+from vision_transformer_attention_amd.workloads import WORKLOADS
+
+from oracle import Spec, num_buckets
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("librpe_attn.so not built (run __graft_entry__.build())")
+    return pkg.load()
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib_or_skip()
+    header = open(os.path.join(ROOT, "include", "rpe_attn.h")).read()
+    declared = set(re.findall(r"^(?:rpe_status|const char\*)\s+(rpe_\w+)\s*\(", header, re.M))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+        for name in declared:
+            assert re.search(rf"\bT {name}\b", out), name
+    assert lib.rpe_attn_version().decode().startswith("rpe_attn")
+
+
+def _w_desc(w, **over):
+    kw = dict(batch=w.batch, heads=w.heads, head_dim=w.head_dim, grid=(w.grid_h, w.grid_w),
+              window=w.window, prefix_tokens=w.prefix, dtype=w.dtype, mode=w.mode,
+              terms="".join(sorted(w.terms)), map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma,
+              rounding=w.reading, tables_per_head=w.tables_per_head)
+    kw.update(over)
+    return pkg.make_desc(**kw)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_geometry_matches_oracle(name):
+    _lib_or_skip()
+    w = WORKLOADS[name]
+    d = _w_desc(w)
+    assert pkg.rpe_attn_validate(d) == 0
+    spec = Spec(w.grid_h, w.grid_w, window=w.window, prefix=w.prefix, mode=w.mode, terms=w.terms,
+                map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma, reading=w.reading)
+    assert pkg.rpe_attn_num_buckets(d) == num_buckets(spec)
+    assert pkg.rpe_attn_num_buckets(d)[2] == w.table_rows
+    n, t, u = pkg.rpe_attn_unit_size(d)
+    assert (n, t, u) == (spec.tokens_per_image, spec.unit_tokens, spec.units_per_image)
+
+
+@pytest.mark.parametrize("reading,beta,per_axis", [("capped", 3.8, 9), ("trunc", 3.8, 7),
+                                                   ("capped", 7.6, 17), ("trunc", 7.6, 15),
+                                                   ("capped", 3.5, 9), ("trunc", 3.5, 7)])
+def test_half_width_readings(reading, beta, per_axis):
+    _lib_or_skip()
+    d = pkg.make_desc(grid=(14, 14), mode="contextual", terms="k", map="piecewise", alpha=1.0,
+                      beta=beta, gamma=4 * beta, rounding=reading)
+    assert pkg.rpe_attn_num_buckets(d)[1] == per_axis
+
+
+BAD = [
+    (dict(batch=-1), -2), (dict(heads=0), -2), (dict(grid=(0, 4)), -2), (dict(grid=(2000, 4)), -2),
+    (dict(window=3, grid=(8, 8)), -2), (dict(window=4, grid=(8, 8), prefix_tokens=1), -2),
+    (dict(prefix_tokens=17), -2), (dict(dtype=7), -3), (dict(mode=9), -4),
+    (dict(mode="bias", map="swin", terms="v"), -5), (dict(mode="bias", terms="k"), -4),
+    (dict(mode="contextual", terms=""), -4), (dict(mode="none", terms="k"), -4),
+    (dict(mode="contextual", terms="k", map="piecewise", alpha=0.0, beta=2.0, gamma=8.0), -7),
+    (dict(mode="contextual", terms="k", map="piecewise", alpha=2.0, beta=1.0, gamma=8.0), -7),
+    (dict(mode="contextual", terms="k", map="piecewise", alpha=2.0, beta=3.0, gamma=2.0), -7),
+    (dict(mode="contextual", terms="k", map="piecewise", alpha=2.0, beta=3.0, gamma=8.0, rounding=5), -4),
+    (dict(head_dim=48), -8), (dict(head_dim=128), -8), (dict(scale=float("nan")), -7),
+    (dict(grid=(4, 70)), -8),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD)
+def test_validation_codes(over, code):
+    lib = _lib_or_skip()
+    base = dict(batch=2, heads=2, head_dim=32, grid=(8, 8), dtype="bf16", mode="none")
+    base.update(over)
+    d = pkg.make_desc(**base)
+    st = pkg.rpe_attn_validate(d)
+    if code == -8 and st == 0:
+        # unsupported configurations may pass validation and be refused by the planner:
+        # rpe_attn_fwd must refuse them before touching the device
+        st = lib.rpe_attn_fwd(ctypes.byref(d), *([ctypes.c_void_p(16)] * 4), None, None, None, None,
+                              ctypes.c_void_p(16), None, None)
+    assert st == code, (over, st, lib.rpe_status_str(st))
+
+
+def test_fwd_rejects_before_device():
+    lib = _lib_or_skip()
+    one = ctypes.c_void_p(16)
+    d = pkg.make_desc(batch=1, heads=1, head_dim=32, grid=(7, 7), window=7, mode="bias", map="swin")
+    # bias table missing
+    assert lib.rpe_attn_fwd(ctypes.byref(d), one, one, one, None, None, None, None, one, None, None) == -1
+    # output missing
+    assert lib.rpe_attn_fwd(ctypes.byref(d), one, one, one, one, None, None, None, None, None, None) == -1
+    d = pkg.make_desc(batch=1, heads=1, head_dim=64, grid=(14, 14), prefix_tokens=1, mode="contextual",
+                      terms="kv", map="piecewise", alpha=1.9, beta=3.8, gamma=15.2)
+    assert lib.rpe_attn_fwd(ctypes.byref(d), one, one, one, None, None, one, None, one, None, None) == -1
+    assert lib.rpe_attn_fwd(None, one, one, one, None, None, None, None, one, None, None) == -1
+    assert lib.rpe_attn_bucket_map(ctypes.byref(d), None, None) == -1
+    assert lib.rpe_attn_axis_index(ctypes.byref(d), 0, one, None) == -2
+    assert lib.rpe_status_str(-5).decode().startswith("the value term")
+
+
+def test_host_plan_fuzz_sanitized(tmp_path):
+    gxx = shutil.which("g++")
+    if not gxx:
+        pytest.skip("g++ missing")
+    exe = str(tmp_path / "plan_fuzz")
+    subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+                    os.path.join(ROOT, "tests", "host", "plan_fuzz.cpp"),
+                    os.path.join(ROOT, "vision_transformer_attention_amd", "csrc", "plan.cpp"), "-o", exe],
+                   check=True)
+    r = subprocess.run([exe, "40000"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 failures" in r.stdout

@@ -1,0 +1,326 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bucket ids and per-axis indices must match bit-exactly; attention outputs
+within 2e-2 max-abs for bf16 inputs (fp32 accumulation) and 1e-5 for fp32.
+Every case prints what it runs before it touches the GPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import Spec, attention, axis_index_table, num_buckets
+from oracle.attention import bucket_map_array
+from vision_transformer_attention_amd.workloads import WORKLOADS, make_inputs, round_to_dtype
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp32": 1e-5}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vision_transformer_attention_amd as pkg
+    pkg.load()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def spec_of(w, **over):
+    kw = dict(window=w.window, prefix=w.prefix, mode=w.mode, terms=w.terms, map=w.map, alpha=w.alpha,
+              beta=w.beta, gamma=w.gamma, reading=w.reading, tables_per_head=w.tables_per_head)
+    kw.update(over)
+    return Spec(w.grid_h, w.grid_w, **kw)
+
+
+def desc_of(w):
+    import vision_transformer_attention_amd as pkg
+    return pkg.make_desc(batch=w.batch, heads=w.heads, head_dim=w.head_dim, grid=(w.grid_h, w.grid_w),
+                         window=w.window, prefix_tokens=w.prefix, dtype=w.dtype, mode=w.mode,
+                         terms="".join(sorted(w.terms)), map=w.map, alpha=w.alpha, beta=w.beta,
+                         gamma=w.gamma, rounding=w.reading, tables_per_head=w.tables_per_head)
+
+
+def fit(w):
+    """The workload with its table size taken from the oracle's geometry."""
+    return w.resized(table_rows=num_buckets(spec_of(w))[2])
+
+
+def run_gpu(w, x, dev, scale=None, return_lse=True):
+    import torch
+    import vision_transformer_attention_amd as pkg
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = {n: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32 if n == "bias" else tdt).to(dev)
+         for n, a in x.items()}
+    o, lse = pkg.rpe_attn_fwd(d["q"], d["k"], d["v"], grid=(w.grid_h, w.grid_w), window=w.window,
+                              prefix_tokens=w.prefix, mode=w.mode, terms="".join(sorted(w.terms)),
+                              map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma, rounding=w.reading,
+                              scale=scale, bias=d.get("bias"), rq=d.get("rq"), rk=d.get("rk"),
+                              rv=d.get("rv"), return_lse=True)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def run_oracle(w, x, scale=None, **sel):
+    spec = spec_of(w, scale=scale)
+    return attention(spec, x["q"], x["k"], x["v"], bias=x.get("bias"), rq=x.get("rq"), rk=x.get("rk"),
+                     rv=x.get("rv"), **sel)
+
+
+def compare(w, x, dev, tol=None, scale=None, **sel):
+    go, gl = run_gpu(w, x, dev, scale=scale)
+    ro, rl = run_oracle(w, x, scale=scale, **sel)
+    mask = ~np.isnan(ro)
+    assert np.isfinite(go).all(), "non-finite GPU output"
+    err = float(np.abs(go - ro)[mask].max())
+    lmask = ~np.isnan(rl)
+    lerr = float(np.abs(gl - rl)[lmask].max())
+    tol = TOL[w.dtype] if tol is None else tol
+    print(f"    max|o - oracle| = {err:.3e}  max|lse - oracle| = {lerr:.3e}  (tol {tol})", flush=True)
+    assert err <= tol, err
+    assert lerr <= tol, lerr
+    return err
+
+
+# ------------------------------------------------------------------------------ index + map
+
+@pytest.mark.parametrize("abg,reading", [((1.9, 3.8, 15.2), "capped"), ((1.9, 3.8, 15.2), "trunc"),
+                                         ((3.8, 7.6, 30.4), "capped"), ((3.8, 7.6, 30.4), "trunc"),
+                                         ((2.0, 4.0, 16.0), "capped"), ((1.3, 5.7, 9.1), "capped"),
+                                         ((3.0, 3.0, 9.0), "trunc"), ((0.5, 1.6, 5.0), "capped")])
+def test_axis_index_bit_exact(dev, abg, reading):
+    import vision_transformer_attention_amd as pkg
+    a, b, g = abg
+    say("axis_index", abg, reading)
+    d = pkg.make_desc(mode="contextual", terms="k", map="piecewise", alpha=a, beta=b, gamma=g,
+                      rounding=reading, grid=(64, 64))
+    got = pkg.rpe_attn_axis_index(d, 200, device=dev).cpu().numpy().tolist()
+    assert got == axis_index_table(200, a, b, g, reading)
+
+
+MAP_CASES = [(name, reading) for name in WORKLOADS for reading in ("capped", "trunc")
+             if WORKLOADS[name].map == "piecewise" or reading == "capped"]
+
+
+@pytest.mark.parametrize("name,reading", MAP_CASES)
+def test_bucket_map_bit_exact(dev, name, reading):
+    import vision_transformer_attention_amd as pkg
+    w = WORKLOADS[name].resized(reading=reading)
+    say("bucket_map", name, reading)
+    got = pkg.rpe_attn_bucket_map(desc_of(w), device=dev).cpu().numpy()
+    ref = bucket_map_array(spec_of(w))
+    assert got.dtype == np.int16 and got.shape == ref.shape
+    assert (got.astype(np.int64) == ref).all()
+
+
+@pytest.mark.parametrize("gh,gw,window,prefix", [(1, 1, 0, 0), (3, 7, 0, 2), (9, 4, 0, 1), (6, 6, 3, 0),
+                                                 (8, 12, 4, 0), (5, 5, 0, 16)])
+def test_bucket_map_shapes(dev, gh, gw, window, prefix):
+    import vision_transformer_attention_amd as pkg
+    say("bucket_map shape", gh, gw, window, prefix)
+    for mode, mp in (("bias", "swin"), ("contextual", "piecewise")):
+        if mp == "swin" and prefix:
+            continue
+        spec = Spec(gh, gw, window=window, prefix=prefix, mode=mode, terms={"k"} if mode == "contextual" else set(),
+                    map=mp, alpha=1.2, beta=2.9, gamma=7.0)
+        d = pkg.make_desc(grid=(gh, gw), window=window, prefix_tokens=prefix, mode=mode,
+                          terms="k" if mode == "contextual" else "", map=mp, alpha=1.2, beta=2.9, gamma=7.0)
+        got = pkg.rpe_attn_bucket_map(d, device=dev).cpu().numpy().astype(np.int64)
+        assert (got == bucket_map_array(spec)).all()
+
+
+# ------------------------------------------------------------------------------ attention
+
+SMALL = {
+    "swin_tiny": WORKLOADS["swin_tiny"],
+    "swin_t_w7": WORKLOADS["swin_t_w7"].resized(batch=2, heads=3, grid_h=14, grid_w=21),
+    "deit_s_irpe_k": WORKLOADS["deit_s_irpe_k"].resized(batch=2, heads=2),
+    "deit_s_irpe_qkv": WORKLOADS["deit_s_irpe_qkv"].resized(batch=2, heads=2),
+    "highres_irpe_k": WORKLOADS["highres_irpe_k"].resized(batch=1, heads=1, grid_h=24, grid_w=56),
+}
+
+
+@pytest.mark.parametrize("sigma", [0.02, 1.0])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(dev, name, sigma):
+    w = SMALL[name]
+    say("parity", name, w.qkv_shape, "sigma", sigma)
+    compare(w, make_inputs(w, sigma=sigma), dev)
+
+
+@pytest.mark.parametrize("name", ["swin_t_w7", "deit_s_irpe_k", "deit_s_irpe_qkv", "highres_irpe_k"])
+def test_parity_fp32(dev, name):
+    # fp32 reruns of the bf16 workload shapes, at the fp32 tolerance
+    w = SMALL[name].resized(dtype="fp32")
+    if name == "highres_irpe_k":
+        w = w.resized(grid_h=12)
+    say("parity fp32", name, w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=3000 + w.index), dev)
+
+
+def test_isolation_terms(dev):
+    # k = 0: logits are the position terms alone; v = 0: the output is the value term alone.
+    w = SMALL["deit_s_irpe_qkv"]
+    x = make_inputs(w, sigma=1.0, seed=4000)
+    say("isolation k=0", w.qkv_shape)
+    x0 = dict(x, k=np.zeros_like(x["k"]))
+    compare(w, x0, dev)
+    say("isolation v=0", w.qkv_shape)
+    x1 = dict(x, v=np.zeros_like(x["v"]))
+    compare(w, x1, dev)
+    say("isolation q=0", w.qkv_shape)
+    compare(w, dict(x, q=np.zeros_like(x["q"])), dev)
+
+
+TERMS = ["k", "q", "v", "kq", "kv", "qv", "kqv"]
+
+
+@pytest.mark.parametrize("terms", TERMS)
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 32), ("fp32", 16), ("bf16", 16)])
+def test_term_combinations(dev, terms, dtype, d):
+    w = WORKLOADS["deit_s_irpe_qkv"].resized(batch=1, heads=2, head_dim=d, grid_h=7, grid_w=9,
+                                             terms=frozenset(terms), dtype=dtype)
+    say("terms", terms, dtype, d, w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=5000), dev)
+
+
+EDGE = [
+    # (label, overrides on the DeiT QKV workload)
+    ("grid 1x1 + cls", dict(grid_h=1, grid_w=1)),
+    ("grid 1x1 no cls", dict(grid_h=1, grid_w=1, prefix=0)),
+    ("no cls 5x11", dict(grid_h=5, grid_w=11, prefix=0)),
+    ("prefix block (no room in the padded row)", dict(grid_h=4, grid_w=16, prefix=1)),
+    ("prefix 3 in tail", dict(grid_h=5, grid_w=13, prefix=3)),
+    ("prefix 16 block", dict(grid_h=3, grid_w=5, prefix=16)),
+    ("two subtiles per row", dict(grid_h=3, grid_w=27, prefix=1)),
+    ("four subtiles per row", dict(grid_h=2, grid_w=61, prefix=1)),
+    ("width 8", dict(grid_h=9, grid_w=8, prefix=1)),
+    ("width 3", dict(grid_h=11, grid_w=3, prefix=2)),
+    ("trunc reading", dict(reading="trunc")),
+    ("per-head tables", dict(tables_per_head=True, heads=3)),
+    ("odd tokens 17x17", dict(grid_h=17, grid_w=17, alpha=2.0, beta=4.0, gamma=16.0)),
+]
+
+
+@pytest.mark.parametrize("label,over", EDGE)
+def test_edge_shapes(dev, label, over):
+    base = dict(batch=2, heads=2, grid_h=6, grid_w=7)
+    base.update(over)
+    w = fit(WORKLOADS["deit_s_irpe_qkv"].resized(**base))
+    say("edge", label, w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=6000), dev)
+
+
+SWIN_EDGE = [
+    ("window 2", dict(grid_h=6, grid_w=8, window=2)),
+    ("window 3", dict(grid_h=9, grid_w=6, window=3)),
+    ("window 5", dict(grid_h=10, grid_w=15, window=5)),
+    ("window 8", dict(grid_h=16, grid_w=8, window=8)),
+    ("window 9 (wide rows)", dict(grid_h=9, grid_w=18, window=9)),
+    ("shared bias", dict(tables_per_head=False)),
+    ("global swin map", dict(grid_h=5, grid_w=6, window=0)),
+    ("fp32 d32", dict(dtype="fp32")),
+    ("d64", dict(head_dim=64)),
+]
+
+
+@pytest.mark.parametrize("label,over", SWIN_EDGE)
+def test_swin_edge(dev, label, over):
+    base = dict(batch=2, heads=2, grid_h=14, grid_w=14)
+    base.update(over)
+    w = fit(WORKLOADS["swin_t_w7"].resized(**base))
+    say("swin edge", label, w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=7000), dev)
+
+
+def test_no_position_mode(dev):
+    import torch
+    import vision_transformer_attention_amd as pkg
+    w = WORKLOADS["deit_s_irpe_k"].resized(batch=2, heads=2, mode="none", terms=frozenset(), map="swin")
+    x = make_inputs(w, seed=8000)
+    say("mode none", w.qkv_shape)
+    q, k, v = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev) for n in "qkv")
+    o = pkg.rpe_attn_fwd(q, k, v, grid=(14, 14), prefix_tokens=1, mode="none")
+    torch.cuda.synchronize()
+    ref, _ = attention(Spec(14, 14, prefix=1, mode="none"), x["q"], x["k"], x["v"])
+    err = float(np.abs(o.float().cpu().numpy() - ref).max())
+    print(f"    max err {err:.3e}", flush=True)
+    assert err <= 2e-2
+
+
+def test_explicit_scale(dev):
+    w = SMALL["deit_s_irpe_qkv"]
+    say("explicit scale 0.05", w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=9000), dev, scale=0.05)
+    w = SMALL["swin_t_w7"]
+    say("explicit scale 0.3 swin", w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=9001), dev, scale=0.3)
+
+
+def test_shaw_page_example_on_gpu(dev):
+    # The Shaw-style page's layer as a 1 x 6 grid with clip 3, zero-padded from d = 4 to 16
+    # (padding adds zero products), scale 1/sqrt(4) given explicitly; fp32.
+    import test_oracle_attention as toa
+    q, k, v, a_k, a_v = toa._shaw_page_setup()
+    spec, rk, rv = toa._shaw_as_2d(a_k, a_v)
+    pad = lambda a: np.concatenate([a, np.zeros(a.shape[:-1] + (12,))], axis=-1)
+    x = {"q": round_to_dtype(pad(q)[None, None], "fp32"), "k": round_to_dtype(pad(k)[None, None], "fp32"),
+         "v": round_to_dtype(pad(v)[None, None], "fp32"), "rk": round_to_dtype(pad(rk), "fp32"),
+         "rv": round_to_dtype(pad(rv), "fp32")}
+    w = WORKLOADS["deit_s_irpe_k"].resized(batch=1, heads=1, head_dim=16, grid_h=1, grid_w=6, prefix=0,
+                                           terms=frozenset("kv"), alpha=3.0, beta=3.0, gamma=10.0,
+                                           dtype="fp32", table_rows=rk.shape[1])
+    say("shaw page example", w.qkv_shape)
+    compare(w, x, dev, scale=0.5)
+
+
+def test_empty_batch(dev):
+    import torch
+    import vision_transformer_attention_amd as pkg
+    say("empty batch")
+    q = torch.zeros((0, 2, 197, 64), dtype=torch.bfloat16, device=dev)
+    rk = torch.zeros((1, 81, 64), dtype=torch.bfloat16, device=dev)
+    o = pkg.rpe_attn_fwd(q, q, q, grid=(14, 14), prefix_tokens=1, mode="contextual", terms="k",
+                         map="piecewise", alpha=1.9, beta=3.8, gamma=15.2, rk=rk)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape
+
+
+def test_deterministic(dev):
+    w = SMALL["deit_s_irpe_qkv"]
+    x = make_inputs(w, sigma=1.0, seed=9100)
+    say("determinism", w.qkv_shape)
+    a, la = run_gpu(w, x, dev)
+    b, lb = run_gpu(w, x, dev)
+    assert (a == b).all() and (la == lb).all()
+
+
+# ------------------------------------------------------------------------------ full sizes
+
+FULL_SAMPLES = {
+    # workload: (batch indices, head indices) checked against the oracle
+    "swin_tiny": (None, None),
+    "swin_t_w7": ([0, 31], [0, 2]),
+    "deit_s_irpe_k": ([0, 37, 63], [0, 5]),
+    "deit_s_irpe_qkv": ([0, 63], [1, 4]),
+    "highres_irpe_k": ([3], [5]),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_full_size_sampled(dev, name):
+    w = WORKLOADS[name]
+    bs, hs = FULL_SAMPLES[name]
+    say("full size", name, w.qkv_shape, "sampled (b, h):", bs, hs)
+    x = make_inputs(w)
+    units = None
+    if name == "swin_t_w7":
+        units = [0, 9, 27, 63]
+    compare(w, x, dev, batch_sel=bs, heads_sel=hs, units=units)

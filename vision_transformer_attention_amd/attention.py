@@ -1,0 +1,193 @@
+"""Python binding of librpe_attn (argument marshalling only).
+
+Names mirror the C entry points of include/rpe_attn.h.  PyTorch provides the
+device memory and the current HIP stream; every step of the computation runs
+in the library's kernels.  There is no fallback path: a missing library or a
+rejected call raises.
+"""
+
+import ctypes
+
+from . import _lib
+from ._lib import Desc, check, load
+
+_MODES = {"none": _lib.RPE_MODE_NONE, "bias": _lib.RPE_MODE_BIAS,
+          "contextual": _lib.RPE_MODE_CONTEXTUAL}
+_MAPS = {"swin": _lib.RPE_MAP_SWIN, "piecewise": _lib.RPE_MAP_PIECEWISE}
+_ROUNDING = {"capped": _lib.RPE_ROUND_CAPPED, "trunc": _lib.RPE_ROUND_TRUNC}
+_TERM_BITS = {"k": _lib.RPE_TERM_K, "q": _lib.RPE_TERM_Q, "v": _lib.RPE_TERM_V}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def make_desc(*, batch=1, heads=1, head_dim=64, grid=(1, 1), window=0, prefix_tokens=0,
+              dtype="bf16", mode="none", terms="", map="swin", alpha=0.0, beta=0.0, gamma=0.0,
+              rounding="capped", scale=None, tables_per_head=False):
+    """Build an ``rpe_attn_desc``.  ``terms`` is a string or set over 'k', 'q', 'v'."""
+    d = Desc()
+    d.batch, d.heads, d.head_dim = int(batch), int(heads), int(head_dim)
+    d.grid_h, d.grid_w = int(grid[0]), int(grid[1])
+    d.window, d.prefix_tokens = int(window), int(prefix_tokens)
+    d.dtype = {"bf16": _lib.RPE_BF16, "fp32": _lib.RPE_FP32}[dtype] if isinstance(dtype, str) else int(dtype)
+    d.mode = _MODES[mode] if isinstance(mode, str) else int(mode)
+    bits = 0
+    for t in terms:
+        bits |= _TERM_BITS[t]
+    d.terms = bits
+    d.map = _MAPS[map] if isinstance(map, str) else int(map)
+    d.rounding = _ROUNDING[rounding] if isinstance(rounding, str) else int(rounding)
+    d.alpha, d.beta, d.gamma = float(alpha), float(beta), float(gamma)
+    d.scale = 0.0 if scale is None else float(scale)
+    d.tables_per_head = 1 if tables_per_head else 0
+    return d
+
+
+def rpe_attn_validate(desc):
+    return load().rpe_attn_validate(ctypes.byref(desc))
+
+
+def rpe_attn_num_buckets(desc):
+    """(half_width, per_axis, total) of the bucket table."""
+    h, s, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    check("rpe_attn_num_buckets",
+          load().rpe_attn_num_buckets(ctypes.byref(desc), ctypes.byref(h), ctypes.byref(s), ctypes.byref(t)))
+    return h.value, s.value, t.value
+
+
+def rpe_attn_unit_size(desc):
+    """(tokens per image N, tokens per unit T, units per image)."""
+    n, t, u = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    check("rpe_attn_unit_size",
+          load().rpe_attn_unit_size(ctypes.byref(desc), ctypes.byref(n), ctypes.byref(t), ctypes.byref(u)))
+    return n.value, t.value, u.value
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def rpe_attn_axis_index(desc, length, device="cuda"):
+    """g(x) for x = -(length-1) .. length-1 as an int16 device tensor."""
+    torch = _torch()
+    out = torch.empty(2 * length - 1, dtype=torch.int16, device=device)
+    check("rpe_attn_axis_index",
+          load().rpe_attn_axis_index(ctypes.byref(desc), int(length), ctypes.c_void_p(out.data_ptr()),
+                                     _stream(out.device)))
+    return out
+
+
+def rpe_attn_bucket_map(desc, device="cuda"):
+    """[T, T] int16 bucket ids of one unit (-1 where a prefix token takes part)."""
+    torch = _torch()
+    _, t, _ = rpe_attn_unit_size(desc)
+    out = torch.empty((t, t), dtype=torch.int16, device=device)
+    check("rpe_attn_bucket_map",
+          load().rpe_attn_bucket_map(ctypes.byref(desc), ctypes.c_void_p(out.data_ptr()),
+                                     _stream(out.device)))
+    return out
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def rpe_attn_fwd(q, k, v, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
+                 alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None,
+                 rq=None, rk=None, rv=None, out=None, return_lse=False):
+    """Attention forward with 2D relative position terms.
+
+    q, k, v: [B, H, N, d] contiguous device tensors (bfloat16 or float32),
+    N = prefix_tokens + grid[0] * grid[1].  bias: [H or 1, S*S] float32;
+    rq / rk / rv: [H or 1, S*S, d] in the dtype of q.  Returns o (and the
+    float32 log-sum-exp [B, H, N] with ``return_lse``).
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [B, H, N, d] of one shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, N, d = q.shape
+    dtype = "bf16" if q.dtype == torch.bfloat16 else "fp32"
+    tabs = [t for t in (bias, rq, rk, rv) if t is not None]
+    per_head = any(t.shape[0] == H and H > 1 for t in tabs)
+    desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
+                     dtype=dtype, mode=mode, terms=terms, map=map, alpha=alpha, beta=beta, gamma=gamma,
+                     rounding=rounding, scale=scale, tables_per_head=per_head)
+    n_img, _, _ = rpe_attn_unit_size(desc)
+    if n_img != N:
+        raise ValueError(f"N = {N} but prefix_tokens + grid gives {n_img}")
+    if mode != "none":
+        _, _, nb = rpe_attn_num_buckets(desc)
+        th = H if per_head else 1
+        if bias is not None:
+            if bias.dtype != torch.float32 or tuple(bias.shape) != (th, nb) or not bias.is_contiguous():
+                raise ValueError(f"bias must be contiguous float32 [{th}, {nb}]")
+        for name, t in (("rq", rq), ("rk", rk), ("rv", rv)):
+            if t is not None and name[1] in terms:
+                if t.dtype != q.dtype or tuple(t.shape) != (th, nb, d) or not t.is_contiguous():
+                    raise ValueError(f"{name} must be contiguous {q.dtype} [{th}, {nb}, {d}]")
+    for t in tabs:
+        if not t.is_cuda:
+            raise ValueError("tables must be device tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    check("rpe_attn_fwd",
+          load().rpe_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                              _ptr(rq if "q" in terms else None), _ptr(rk if "k" in terms else None),
+                              _ptr(rv if "v" in terms else None), _ptr(out), _ptr(lse),
+                              _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+class PreparedFwd:
+    """A validated rpe_attn_fwd call with fixed tensors: each call() is one
+    library call with pre-marshalled arguments (for launch loops and timing).
+
+    The tensors passed to ``prepare_fwd`` must stay alive and keep their
+    storage while this object is used.
+    """
+
+    def __init__(self, desc, ptrs, keep, device):
+        self._lib = load()
+        self._desc = desc
+        self._args = ptrs
+        self._keep = keep
+        self._device = device
+
+    def __call__(self, stream=None):
+        torch = _torch()
+        s = ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream if stream is None else stream)
+        check("rpe_attn_fwd", self._lib.rpe_attn_fwd(ctypes.byref(self._desc), *self._args, s))
+
+
+def prepare_fwd(q, k, v, *, out, lse=None, **kw):
+    """Validate once (by running the call) and return a PreparedFwd for repeats."""
+    torch = _torch()
+    rpe_attn_fwd(q, k, v, out=out, **kw)
+    B, H, N, d = q.shape
+    mode, terms = kw.get("mode", "none"), kw.get("terms", "")
+    tabs = [kw.get(n) for n in ("bias", "rq", "rk", "rv") if kw.get(n) is not None]
+    per_head = any(t.shape[0] == H and H > 1 for t in tabs)
+    desc = make_desc(batch=B, heads=H, head_dim=d, grid=kw["grid"], window=kw.get("window", 0),
+                     prefix_tokens=kw.get("prefix_tokens", 0),
+                     dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms,
+                     map=kw.get("map", "swin"), alpha=kw.get("alpha", 0.0), beta=kw.get("beta", 0.0),
+                     gamma=kw.get("gamma", 0.0), rounding=kw.get("rounding", "capped"),
+                     scale=kw.get("scale"), tables_per_head=per_head)
+    rq = kw.get("rq") if "q" in terms else None
+    rk = kw.get("rk") if "k" in terms else None
+    rv = kw.get("rv") if "v" in terms else None
+    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(kw.get("bias")), _ptr(rq), _ptr(rk), _ptr(rv), _ptr(out), _ptr(lse)]
+    return PreparedFwd(desc, ptrs, (q, k, v, out, lse, tabs), q.device)

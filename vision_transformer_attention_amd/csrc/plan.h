@@ -1,0 +1,81 @@
+// Launch plan of the 2D relative-position attention forward: descriptor
+// validation and every size the kernels derive from it.  Pure C++17 (no HIP),
+// so it can be built and sanitised on a host without a GPU.
+#pragma once
+
+#include <cstdint>
+
+#include "../../include/rpe_attn.h"
+
+namespace rpe {
+
+// Keys of a unit are staged through LDS in blocks of 32 "slots" (two 16-key
+// MFMA sub-tiles).  Grid keys are laid out row by row with each grid row
+// padded to Wp slots (Wp in {4, 8} or a multiple of 16), so that a 16-slot
+// sub-tile always covers whole grid rows or a fixed column range of one row.
+// With this layout the column part of a key's bucket id is the same for a
+// lane in every sub-tile (only the row part changes), which is what lets the
+// kernel turn the bucket lookup into one add per pair.
+constexpr int kBlockSlots = 32;
+constexpr int kSubtile = 16;
+constexpr int kMaxKP = 4;           // sub-tiles per padded grid row the kernels are built for
+constexpr int kMaxLdsBytes = 160 * 1024;
+
+struct Params {
+  // tensors
+  const void* q; const void* k; const void* v; void* o; float* lse;
+  const float* bias; const void* rq; const void* rk; const void* rv;
+  // problem
+  int B, H, N, D;
+  int gw;                 // grid width (token addressing in window mode)
+  int M;                  // window side, 0 = global
+  int P;                  // prefix tokens
+  int R, C;               // positioned rows / cols of one unit
+  int T;                  // tokens of one unit
+  int U;                  // units per image
+  int wins_per_row;       // gw / M in window mode
+  int half, S, nb;        // table half-width, entries per axis, S*S
+  int map, rounding;
+  double alpha, beta, gamma;
+  float c;                // logit scale * log2(e)   (contextual: applies to all terms)
+  float bias_mul;         // log2(e) (bias mode: the bias is added after the scale)
+  int64_t tab_head_stride;    // elements between heads of a table (0: shared)
+  // key-slot geometry
+  int Wp, KP, SR;         // padded row width, sub-tiles per padded row, grid rows per sub-tile
+  int prefix_in_tail;     // prefix keys live in the pad columns of the last grid row
+  int prefix_block;       // 1: a separate leading block holds the prefix keys
+  int grid_blocks;        // blocks of 32 slots covering R * Wp grid slots
+  int n_blocks;           // prefix_block + grid_blocks
+  // work split
+  int n_wt;               // 16-row query tiles per unit
+  int NW;                 // waves per workgroup
+  int n_qt;               // workgroups per unit
+  int64_t n_units;        // B * H * U
+  int64_t n_wg;           // n_units * n_qt
+  // LDS layout, in 4-byte words
+  int off_k[2], off_v[2]; // K block [32][kpitch] and transposed V block [D][vpitch]
+  int kpitch, vpitch;     // in elements of the storage dtype
+  int off_tab;            // gather target: per-row bucket scores (contextual K) or bias table
+  int p_tab;              // row pitch of the per-row bucket scores
+  int zr;                 // size of each guard region: (S-1)*S + 1
+  int off_zero, off_neg;  // guard regions (all 0 / all -inf) addressed as guard + row part
+  int off_w;              // value-term weight sums; same layout as [off_tab, off_neg + zr)
+  int off_tq, p_tq;       // query-term bucket scores of the current key block [32][p_tq]
+  int off_tqz, off_tqn;   // guard regions of the query-term scores
+  int off_ry, off_cx;     // per-axis tables: (g(dy)+H)*S and g(dx)+H
+  int lds_words;
+  int dtype, mode;
+  uint32_t terms;
+  int elem_bytes;
+};
+
+// Validation only (no derived plan).  Returns an rpe_status.
+int validate(const rpe_attn_desc* d);
+
+// Table geometry; returns an rpe_status.
+int table_geometry(const rpe_attn_desc* d, int* half, int* S, int* nb);
+
+// Full plan for rpe_attn_fwd (pointers left null).  Returns an rpe_status.
+int make_plan(const rpe_attn_desc* d, Params* p);
+
+}  // namespace rpe
