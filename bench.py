@@ -86,9 +86,10 @@ def cpu_baseline(name, budget_s=20.0):
     w = WORKLOADS[name]
     x = make_inputs(w)
     _CPU["x"] = x
-    # estimate the per-image cost on one image
-    t0 = time.perf_counter()
+    # estimate the per-image cost (after one warm-up image)
     _oracle_worker((name, [(0, 0)]))
+    t0 = time.perf_counter()
+    _oracle_worker((name, [(0, 1 % w.heads)]))
     per_img = max(time.perf_counter() - t0, 1e-3)
     try:
         cores = len(os.sched_getaffinity(0))
@@ -96,8 +97,9 @@ def cpu_baseline(name, budget_s=20.0):
         cores = os.cpu_count() or 1
     cores = max(1, min(cores, 16))
     n_img = w.batch * w.heads
-    n_sample = max(cores, min(n_img, int(budget_s / per_img)))
-    pairs = [(i // w.heads, i % w.heads) for i in range(n_sample)]
+    # about budget_s seconds of single-core oracle work, cycling over the workload's images
+    n_sample = max(cores, int(budget_s / per_img))
+    pairs = [((i % n_img) // w.heads, (i % n_img) % w.heads) for i in range(n_sample)]
     chunks = [pairs[i::cores] for i in range(cores)]
     ctx = mp.get_context("fork")
     with ctx.Pool(cores) as pool:
@@ -110,8 +112,9 @@ def cpu_baseline(name, budget_s=20.0):
     flop_sample = flop * done / n_img
     _CPU.clear()
     return {"value": flop_sample / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {n_img} (batch, head) images of {name}, fp64 NumPy oracle, "
-                      f"{wall:.2f} s wall on {cores} processes (1 BLAS thread each)",
+            "sample": f"{done} (batch, head) images of {name} (the workload has {n_img}; images repeat "
+                      f"when the sample is larger), fp64 NumPy oracle, {wall:.2f} s wall on {cores} "
+                      f"processes (1 BLAS thread each)",
             "seconds": wall}
 
 

@@ -79,19 +79,32 @@ int main(int argc, char** argv) {
     if (st != RPE_OK) continue;
     ++accepted;
     REQUIRE(p.lds_words * 4 <= rpe::kMaxLdsBytes);
-    REQUIRE(p.off_k[0] < p.off_v[0] && p.off_v[0] < p.off_k[1] && p.off_k[1] < p.off_v[1]);
-    REQUIRE(p.off_v[1] < p.off_tab || (p.off_tab == p.off_zero));
+    if (p.resident) {
+      REQUIRE(p.off_v[0] == 0 && p.vpitch >= p.n_blocks * rpe::kBlockSlots);
+      REQUIRE(p.n_blocks * rpe::kBlockSlots <= rpe::kResidentSlots);
+      REQUIRE(d.mode != RPE_MODE_CONTEXTUAL || d.terms == RPE_TERM_K);
+      REQUIRE((p.dv * p.vpitch * p.elem_bytes + 3) / 4 <= p.off_rq);
+    } else {
+      REQUIRE(p.off_k[0] < p.off_v[0] && p.off_v[0] < p.off_k[1] && p.off_k[1] < p.off_v[1]);
+      REQUIRE(p.off_v[1] < p.off_rq);
+    }
+    REQUIRE(p.off_rq <= p.off_tab);
     REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr);
     REQUIRE(p.zr == (p.S - 1) * p.S + 1);
     REQUIRE(p.off_ry >= p.off_neg + p.zr);
     REQUIRE(p.off_cx == p.off_ry + 2 * p.R - 1);
     REQUIRE(p.off_cx + 2 * p.C - 1 <= p.lds_words);
-    REQUIRE(p.kpitch >= p.D && p.vpitch >= rpe::kBlockSlots);
-    REQUIRE(p.Wp >= p.C && p.Wp <= 16 * rpe::kMaxKP);
-    REQUIRE(p.Wp == 4 || p.Wp == 8 || p.Wp % 16 == 0);
+    REQUIRE(p.kpitch >= p.D && p.vpitch >= rpe::kBlockSlots && p.dv >= p.D && p.dv >= 32);
+    REQUIRE(p.Wp >= p.C && p.Wp <= rpe::kMaxWp && (1 << p.lwp) == p.Wp && p.Wp >= 4);
     REQUIRE(p.grid_blocks * rpe::kBlockSlots >= p.R * p.Wp);
-    REQUIRE(p.n_wt * 16 >= p.T && p.n_qt * p.NW >= p.n_wt);
-    REQUIRE(p.n_wg == p.n_units * p.n_qt);
+    REQUIRE(p.n_rt * rpe::kRowTile >= p.T && p.n_qc * p.NW >= p.n_rt);
+    REQUIRE(p.NW >= 2 && p.NW <= rpe::kMaxWaves);
+    for (int qc = 0; qc < p.n_qc; ++qc) {
+      const int rt0 = qc * p.n_rt / p.n_qc, rt1 = (qc + 1) * p.n_rt / p.n_qc;
+      REQUIRE(rt1 - rt0 <= p.NW && rt1 >= rt0);
+    }
+    REQUIRE(p.n_wg == p.n_units * p.n_qc);
+    REQUIRE(p.nbt * rpe::kRowTile >= p.nb);
     REQUIRE(p.T == p.P + p.R * p.C);
     REQUIRE(p.N == p.P + d.grid_h * d.grid_w);
     REQUIRE(p.p_tab >= p.nb);

@@ -19,7 +19,9 @@ ARCH = "gfx950"
 # Packed-FP32 instructions are kept out of the device code on purpose.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["plan.cpp", "api.cpp", "kernels.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "fwd_dispatch.cpp",
+           "fwd_bf16_d16.hip", "fwd_bf16_d32.hip", "fwd_bf16_d64.hip",
+           "fwd_f32_d16.hip", "fwd_f32_d32.hip", "fwd_f32_d64.hip"]
 
 
 def _run(cmd, verbose):
@@ -39,7 +41,7 @@ def build(verbose=True):
     for src in SOURCES:
         obj = os.path.join(OBJ, src + ".o")
         jobs.append(([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
-    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs], verbose)

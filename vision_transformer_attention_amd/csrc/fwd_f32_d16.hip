@@ -1,0 +1,6 @@
+// Instances of the fused forward for float inputs, head dim 16.
+#include "fwd_kernel.h"
+
+namespace rpe {
+hipError_t launch_fwd_f32_d16(const Params& p, hipStream_t stream) { return launch_fwd_d<float, 16>(p, stream); }
+}  // namespace rpe

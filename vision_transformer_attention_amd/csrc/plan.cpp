@@ -15,9 +15,70 @@ int unit_rows(const rpe_attn_desc* d) { return d->window ? d->window : d->grid_h
 int unit_cols(const rpe_attn_desc* d) { return d->window ? d->window : d->grid_w; }
 
 int padded_width(int C) {
-  if (C <= 4) return 4;
-  if (C <= 8) return 8;
-  return (C + 15) / 16 * 16;
+  int w = 4;
+  while (w < C) w *= 2;
+  return w;
+}
+
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+
+// LDS layout (4-byte words) for the wave count already in p->NW.
+int lds_layout(const rpe_attn_desc* d, Params* p) {
+  // LDS layout (words)
+  const int eb = p->elem_bytes;
+  const bool ctx = d->mode == RPE_MODE_CONTEXTUAL;
+  const bool tq = ctx && (d->terms & RPE_TERM_Q);
+  p->dv = p->D > kBlockSlots ? p->D : kBlockSlots;
+  p->kpitch = d->dtype == RPE_BF16 ? p->D + 8 : p->D + 1;
+  p->vpitch = d->dtype == RPE_BF16 ? kBlockSlots + 8 : kBlockSlots + 1;
+  int off = 0;
+  if (p->resident) {
+    // the whole unit's V^T; K comes straight from global memory
+    p->vpitch = p->n_blocks * kBlockSlots + (d->dtype == RPE_BF16 ? 8 : 1);
+    const int vwords = (p->dv * p->vpitch * eb + 3) / 4;
+    p->off_k[0] = p->off_k[1] = 0;
+    p->off_v[0] = p->off_v[1] = 0;
+    off += (vwords + 3) / 4 * 4;
+  } else {
+    const int kwords = (kBlockSlots * p->kpitch * eb + 3) / 4;
+    const int vwords = (p->dv * p->vpitch * eb + 3) / 4;
+    for (int i = 0; i < 2; ++i) {
+      p->off_k[i] = off; off += (kwords + 3) / 4 * 4;
+      p->off_v[i] = off; off += (vwords + 3) / 4 * 4;
+    }
+  }
+  p->off_rq = off;
+  if (tq) off += ((p->nbt * kRowTile * p->kpitch * eb + 3) / 4 + 3) / 4 * 4;
+  p->zr = (p->S - 1) * p->S + 1;  // 1 when there is no table
+  const bool row_area = ctx && (d->terms & (RPE_TERM_K | RPE_TERM_V));
+  p->p_tab = p->nb | 1;
+  p->off_tab = off;
+  if (d->mode == RPE_MODE_BIAS || d->mode == RPE_MODE_NONE) {
+    off += p->nb;
+  } else if (row_area) {
+    off += p->NW * kRowTile * p->p_tab;
+  }
+  p->off_zero = off; off += p->zr;
+  p->off_neg = off; off += p->zr;
+  if (ctx && (d->terms & RPE_TERM_V)) {
+    p->off_w = off;
+    off += p->off_neg + p->zr - p->off_tab;
+  }
+  if (tq) {
+    p->p_tq = p->nb | 1;
+    p->off_tq = off; off += kBlockSlots * p->p_tq;
+    p->off_tqz = off; off += p->zr;
+    p->off_tqn = off; off += p->zr;
+  }
+  p->off_ry = off; off += 2 * p->R - 1;
+  p->off_cx = off; off += 2 * p->C - 1;
+  p->lds_words = (off + 3) / 4 * 4;
+  return p->lds_words * 4 > kMaxLdsBytes ? RPE_E_BUCKETS : RPE_OK;
 }
 
 }  // namespace
@@ -114,59 +175,34 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
 
   // key slots
   p->Wp = padded_width(p->C);
-  if (p->Wp / kSubtile > kMaxKP) return RPE_E_UNSUPPORTED;
-  p->KP = p->Wp >= kSubtile ? p->Wp / kSubtile : 1;
-  p->SR = p->Wp < kSubtile ? kSubtile / p->Wp : 1;
+  if (p->Wp > kMaxWp) return RPE_E_UNSUPPORTED;
+  p->lwp = log2_exact(p->Wp);
   p->prefix_in_tail = (p->P > 0 && p->P <= p->Wp - p->C) ? 1 : 0;
   p->prefix_block = (p->P > 0 && !p->prefix_in_tail) ? 1 : 0;
   p->grid_blocks = (p->R * p->Wp + kBlockSlots - 1) / kBlockSlots;
   p->n_blocks = p->prefix_block + p->grid_blocks;
+  p->nbt = (p->nb + kRowTile - 1) / kRowTile;
 
-  // work split
-  p->NW = 4;
-  p->n_wt = (p->T + 15) / 16;
-  p->n_qt = (p->n_wt + p->NW - 1) / p->NW;
+  p->n_rt = (p->T + kRowTile - 1) / kRowTile;
   p->n_units = (int64_t)p->B * p->H * p->U;
-  p->n_wg = p->n_units * p->n_qt;
-
-  // LDS layout (words)
-  const int eb = p->elem_bytes;
-  p->kpitch = d->dtype == RPE_BF16 ? p->D + 8 : p->D + 1;
-  p->vpitch = d->dtype == RPE_BF16 ? kBlockSlots + 8 : kBlockSlots + 1;
-  const int kwords = (kBlockSlots * p->kpitch * eb + 3) / 4;
-  const int vwords = (p->D * p->vpitch * eb + 3) / 4;
-  int off = 0;
-  for (int i = 0; i < 2; ++i) {
-    p->off_k[i] = off; off += (kwords + 3) / 4 * 4;
-    p->off_v[i] = off; off += (vwords + 3) / 4 * 4;
+  // work split: one 32-row query tile per wave, the unit's tiles spread evenly
+  // over its workgroups; the widest workgroup (<= kMaxWaves waves, >= 2) whose
+  // LDS plan fits is taken.
+  // The resident variant (no per-block barriers) serves units of at most
+  // kResidentSlots key slots with a key or bias term only.
+  const bool can_res = (d->mode != RPE_MODE_CONTEXTUAL || d->terms == RPE_TERM_K) &&
+                       p->n_blocks * kBlockSlots <= kResidentSlots;
+  for (int res = can_res ? 1 : 0; res >= 0; --res) {
+    p->resident = res;
+    for (int max_w = kMaxWaves; max_w >= 2; --max_w) {
+      p->n_qc = (p->n_rt + max_w - 1) / max_w;
+      p->NW = (p->n_rt + p->n_qc - 1) / p->n_qc;
+      if (p->NW < 2) p->NW = 2;  // the block loader assumes at least two waves
+      p->n_wg = p->n_units * p->n_qc;
+      if (lds_layout(d, p) == RPE_OK) return RPE_OK;
+    }
   }
-  p->zr = (p->S - 1) * p->S + 1;  // 1 when there is no table
-  const bool ctx = d->mode == RPE_MODE_CONTEXTUAL;
-  const bool row_area = ctx && (d->terms & (RPE_TERM_K | RPE_TERM_V));
-  p->p_tab = p->nb | 1;
-  p->off_tab = off;
-  if (d->mode == RPE_MODE_BIAS || d->mode == RPE_MODE_NONE) {
-    off += p->nb;
-  } else if (row_area) {
-    off += p->NW * 16 * p->p_tab;
-  }
-  p->off_zero = off; off += p->zr;
-  p->off_neg = off; off += p->zr;
-  if (ctx && (d->terms & RPE_TERM_V)) {
-    p->off_w = off;
-    off += p->off_neg + p->zr - p->off_tab;
-  }
-  if (ctx && (d->terms & RPE_TERM_Q)) {
-    p->p_tq = p->nb | 1;
-    p->off_tq = off; off += kBlockSlots * p->p_tq;
-    p->off_tqz = off; off += p->zr;
-    p->off_tqn = off; off += p->zr;
-  }
-  p->off_ry = off; off += 2 * p->R - 1;
-  p->off_cx = off; off += 2 * p->C - 1;
-  p->lds_words = (off + 3) / 4 * 4;
-  if (p->lds_words * 4 > kMaxLdsBytes) return RPE_E_BUCKETS;
-  return RPE_OK;
+  return RPE_E_BUCKETS;
 }
 
 }  // namespace rpe

@@ -9,17 +9,18 @@
 
 namespace rpe {
 
-// Keys of a unit are staged through LDS in blocks of 32 "slots" (two 16-key
-// MFMA sub-tiles).  Grid keys are laid out row by row with each grid row
-// padded to Wp slots (Wp in {4, 8} or a multiple of 16), so that a 16-slot
-// sub-tile always covers whole grid rows or a fixed column range of one row.
-// With this layout the column part of a key's bucket id is the same for a
-// lane in every sub-tile (only the row part changes), which is what lets the
-// kernel turn the bucket lookup into one add per pair.
+// Keys of a unit are staged through LDS in blocks of 32 "slots" (one 32-key
+// MFMA tile).  Grid keys are laid out row by row with each grid row padded to
+// Wp slots, Wp = the power of two >= the unit width (at least 4), so a block
+// covers whole grid rows (Wp <= 32) or half a row (Wp = 64).  With this layout
+// the column part of a key's bucket id is fixed for a lane across blocks (only
+// the row part changes), which turns the bucket lookup into one add per pair.
 constexpr int kBlockSlots = 32;
-constexpr int kSubtile = 16;
-constexpr int kMaxKP = 4;           // sub-tiles per padded grid row the kernels are built for
+constexpr int kRowTile = 32;        // query rows per wave (one 32x32 MFMA tile)
+constexpr int kMaxWp = 64;          // widest padded grid row the kernel is built for
+constexpr int kMaxWaves = 4;
 constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr int kResidentSlots = 256;  // largest unit (in key slots) staged whole in LDS
 
 struct Params {
   // tensors
@@ -35,27 +36,31 @@ struct Params {
   int U;                  // units per image
   int wins_per_row;       // gw / M in window mode
   int half, S, nb;        // table half-width, entries per axis, S*S
+  int nbt;                // 32-row tiles covering the nb table rows
   int map, rounding;
   double alpha, beta, gamma;
   float c;                // logit scale * log2(e)   (contextual: applies to all terms)
   float bias_mul;         // log2(e) (bias mode: the bias is added after the scale)
   int64_t tab_head_stride;    // elements between heads of a table (0: shared)
   // key-slot geometry
-  int Wp, KP, SR;         // padded row width, sub-tiles per padded row, grid rows per sub-tile
+  int Wp, lwp;            // padded row width and its log2
   int prefix_in_tail;     // prefix keys live in the pad columns of the last grid row
   int prefix_block;       // 1: a separate leading block holds the prefix keys
   int grid_blocks;        // blocks of 32 slots covering R * Wp grid slots
   int n_blocks;           // prefix_block + grid_blocks
+  int resident;           // 1: the unit's transposed V lives in LDS for the whole kernel
   // work split
-  int n_wt;               // 16-row query tiles per unit
-  int NW;                 // waves per workgroup
-  int n_qt;               // workgroups per unit
+  int n_rt;               // 32-row query tiles per unit
+  int NW;                 // waves per workgroup (one row tile each)
+  int n_qc;               // workgroups (query chunks) per unit
   int64_t n_units;        // B * H * U
-  int64_t n_wg;           // n_units * n_qt
+  int64_t n_wg;           // n_units * n_qc
   // LDS layout, in 4-byte words
-  int off_k[2], off_v[2]; // K block [32][kpitch] and transposed V block [D][vpitch]
+  int off_k[2], off_v[2]; // K block [32][kpitch], transposed V block [DV][vpitch]
   int kpitch, vpitch;     // in elements of the storage dtype
-  int off_tab;            // gather target: per-row bucket scores (contextual K) or bias table
+  int dv;                 // rows of the transposed V block (max(D, 32))
+  int off_rq;             // query-term table staged as [nbt*32][kpitch]
+  int off_tab;            // gather target: per-row bucket scores (contextual) or bias table
   int p_tab;              // row pitch of the per-row bucket scores
   int zr;                 // size of each guard region: (S-1)*S + 1
   int off_zero, off_neg;  // guard regions (all 0 / all -inf) addressed as guard + row part
