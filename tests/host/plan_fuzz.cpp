@@ -79,22 +79,15 @@ int main(int argc, char** argv) {
     if (st != RPE_OK) continue;
     ++accepted;
     REQUIRE(p.lds_words * 4 <= rpe::kMaxLdsBytes);
-    if (p.resident) {
-      REQUIRE(p.off_v[0] == 0 && p.vpitch >= p.n_blocks * rpe::kBlockSlots);
-      REQUIRE(p.n_blocks * rpe::kBlockSlots <= rpe::kResidentSlots);
-      REQUIRE(d.mode != RPE_MODE_CONTEXTUAL || d.terms == RPE_TERM_K);
-      REQUIRE((p.dv * p.vpitch * p.elem_bytes + 3) / 4 <= p.off_rq);
-    } else {
-      REQUIRE(p.off_k[0] < p.off_v[0] && p.off_v[0] < p.off_k[1] && p.off_k[1] < p.off_v[1]);
-      REQUIRE(p.off_v[1] < p.off_rq);
-    }
+    REQUIRE(p.off_stage == 0);
+    REQUIRE(p.off_rq * 4 >= rpe::kStages * 2 * rpe::kBlockSlots * p.D * p.elem_bytes);
     REQUIRE(p.off_rq <= p.off_tab);
     REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr);
     REQUIRE(p.zr == (p.S - 1) * p.S + 1);
     REQUIRE(p.off_ry >= p.off_neg + p.zr);
     REQUIRE(p.off_cx == p.off_ry + 2 * p.R - 1);
     REQUIRE(p.off_cx + 2 * p.C - 1 <= p.lds_words);
-    REQUIRE(p.kpitch >= p.D && p.vpitch >= rpe::kBlockSlots && p.dv >= p.D && p.dv >= 32);
+    REQUIRE(p.kpitch >= p.D);
     REQUIRE(p.Wp >= p.C && p.Wp <= rpe::kMaxWp && (1 << p.lwp) == p.Wp && p.Wp >= 4);
     REQUIRE(p.grid_blocks * rpe::kBlockSlots >= p.R * p.Wp);
     REQUIRE(p.n_rt * rpe::kRowTile >= p.T && p.n_qc * p.NW >= p.n_rt);

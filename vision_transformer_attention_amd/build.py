@@ -16,9 +16,12 @@ LIB = os.path.join(HERE, "librpe_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-# Packed-FP32 instructions are kept out of the device code on purpose.
+# Packed-FP32 instructions are kept out of the device code on purpose; MFMA
+# operands and accumulators stay in ordinary VGPRs (no AGPR round trips
+# between the matrix products and the softmax arithmetic).
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "fwd_dispatch.cpp",
            "fwd_bf16_d16.hip", "fwd_bf16_d32.hip", "fwd_bf16_d64.hip",
            "fwd_f32_d16.hip", "fwd_f32_d32.hip", "fwd_f32_d64.hip"]

@@ -11,16 +11,24 @@
 // rows 8j + 4h + i (h = l/32, j, i in 0..3) (its 16 keys of the block), so a
 // row's softmax state lives in two lanes and reduces with one exchange.
 //
+// Data movement: the workgroup walks one stream of 32-row blocks -- rows of
+// the key table rK (for the bucket scores), then the unit's key/value blocks,
+// then rows of the value table rV -- through a ring of kStages LDS stages.
+// Blocks are copied global -> LDS by the direct-to-LDS loads of gfx950
+// (global_load_lds_dwordx4, no registers involved) kStages-1 blocks ahead of
+// the block being computed; each stage holds row-major K and V tiles with the
+// 16-byte chunks of a row XOR-swizzled by the row index.  The V^T operand of
+// the PV product is read with the LDS transpose load ds_read_b64_tr_b16.
+//
 // Position terms (iRPE summary page, "Rethinking and Improving Relative
 // Position Encoding for Vision Transformer", Method, eqs. 13-17 and 25-28;
 // Swin 2D RPE post, sections 3.1-3.2; Swin relative-bias record, "The claim"):
 //   contextual key term:  TK[i][b] = c * q_i . rK[b] is computed once per row
-//       and bucket (eqs. 26-27) with the same MFMA as S^T (rK streamed through
-//       the key buffer), kept in LDS, and gathered per pair (eq. 28);
+//       and bucket (eqs. 26-27) with the same MFMA as S^T, kept in LDS, and
+//       gathered per pair (eq. 28);
 //   query term: TQ[j][b] = c * k_j . rQ[b] per key block, gathered per pair;
 //   value term: softmax weights are summed per (row, bucket) into LDS with
-//       float atomics, and O^T += rV^T W^T at the end reuses the PV MFMA with
-//       rV streamed through the value buffer;
+//       float atomics, and O^T += rV^T W^T at the end reuses the PV MFMA;
 //   bias mode: the head's (2M-1)^2 table, prescaled by log2(e), is gathered.
 // The bucket of a pair is b = (g(dy)+H)*S + (g(dx)+H) with (dy, dx) = query -
 // key; its LDS address is ry(dy) + cx(lane, key column): ry is read from a
@@ -30,8 +38,7 @@
 //
 // Softmax runs in log2 units with a lazily moved running max (moved only when
 // a row's block max exceeds it by more than 2^8), so most blocks skip the
-// rescale.  Key blocks are prefetched two ahead into registers and staged
-// through double-buffered LDS (V is transposed on the way in).
+// rescale.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,8 +57,11 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
 constexpr int kThreadsMax = kMaxWaves * 64;
 constexpr float kLazyTau = 8.0f;
@@ -72,6 +82,53 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8); the counters not waited on are left at their maxima.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+
+// Wait until at most n vector-memory loads of this wave are outstanding.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(waitcnt_vm(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(waitcnt_vm(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(waitcnt_vm(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(waitcnt_vm(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(waitcnt_vm(11)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(waitcnt_vm(12)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(waitcnt_vm(13)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(waitcnt_vm(14)); break;
+    case 15: __builtin_amdgcn_s_waitcnt(waitcnt_vm(15)); break;
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(16)); break;
+  }
+}
+
+// One 16-byte direct-to-LDS load per lane: lane l's 16 bytes from g land at
+// LDS byte address lds + 16 * l (lds is the same for the whole wave and goes in
+// M0).  Issued from inline assembly so that the compiler does not order later
+// LDS reads behind it: completion is tracked explicitly with s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(const void* g, const char* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)const_cast<char*>(lds))));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(base) : "memory", "m0");
+}
+
+// Workgroup barrier that orders LDS traffic but leaves the direct-to-LDS loads
+// in flight (a plain __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename DT>
 struct Traits;
 template <>
@@ -85,10 +142,10 @@ struct Traits<float> {
 
 }  // namespace
 
-// RES: "resident" variant for small units: the unit's transposed V is staged in
-// LDS once, each wave streams its K operand from global memory one block ahead,
-// and the key loop runs without workgroup barriers (key and bias terms only).
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool RES>
+// Stream element kinds.
+enum : int { kElemKeyTable = 0, kElemKeys = 1, kElemValueTable = 2 };
+
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE>
 __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
   constexpr bool BF = std::is_same<DT, __bf16>::value;
   constexpr bool CTX = MODE == RPE_MODE_CONTEXTUAL;
@@ -100,13 +157,17 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
   // term the row area is zero and the gather only supplies the -inf of padding
   // keys, unless the query-term gather already does that.
   constexpr bool GATHER = !CTX || TK || !TQ;
+  constexpr int EB = sizeof(DT);
   constexpr int EPC = Traits<DT>::kEpc;
-  constexpr int CH = D / EPC;                      // 16-byte chunks per token row
+  constexpr int RB = D * EB;                       // bytes per token row
+  constexpr int CPR = RB / 16;                     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                    // rows per direct-to-LDS instruction (1 KB)
+  constexpr int IPB = kBlockSlots / RPI;           // instructions per 32-row tile
+  constexpr int TILE = kBlockSlots * RB;           // bytes per 32-row tile
   constexpr int KS = BF ? (D + 15) / 16 : D / 2;   // MFMA k-steps over the head dim
   constexpr int DTL = (D + 31) / 32;               // 32-row tiles of O^T over the head dim
-  constexpr int ITEMS = (kBlockSlots * CH + 127) / 128;  // 16-byte chunks per thread per tensor (>= 2 waves)
   constexpr int NPH = WIDE ? 2 : 1;                // address phases (a 64-slot grid row spans 2 blocks)
-  static_assert(!RES || (!TQ && !TV), "the resident variant has no query or value term");
+  static_assert(RPI * CPR == 64 && IPB >= 1, "row size");
 
   extern __shared__ float smem[];
   int* smem_i = reinterpret_cast<int*>(smem);
@@ -114,7 +175,8 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
 
   const int nth = blockDim.x;
   const int NW = nth >> 6;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, h = lane >> 5, r32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r32 = lane & 31;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) wave index
 
   // ---- workgroup -> (unit, query chunk); consecutive chunks of a unit on one XCD.
   const int64_t bid = blockIdx.x;
@@ -137,6 +199,8 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
   const DT* __restrict__ kg = reinterpret_cast<const DT*>(p.k) + base;
   const DT* __restrict__ vg = reinterpret_cast<const DT*>(p.v) + base;
   DT* __restrict__ og = reinterpret_cast<DT*>(p.o) + base;
+  const DT* rk = reinterpret_cast<const DT*>(p.rk) + head * p.tab_head_stride;
+  const DT* rv = reinterpret_cast<const DT*>(p.rv) + head * p.tab_head_stride;
 
   // ---- prologue: per-axis tables, guards, bias table, weight sums, staged rQ.
   for (int i = tid; i < 2 * p.R - 1; i += nth)
@@ -169,7 +233,9 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
     for (int i = tid; i < NW * kRowTile * p.p_tab; i += nth) smem[p.off_tab + i] = 0.0f;
   }
   if constexpr (TQ) {
+    // rQ staged as [nbt*32][kpitch] (rows past nb zero)
     const DT* rq = reinterpret_cast<const DT*>(p.rq) + head * p.tab_head_stride;
+    constexpr int CH = D / EPC;
     for (int it = tid; it < p.nbt * kRowTile * CH; it += nth) {
       const int row = it / CH, ch = it - (it / CH) * CH;
       const uint4 u = row < p.nb ? ld16(rq + static_cast<int64_t>(row) * D + ch * EPC) : make_uint4(0, 0, 0, 0);
@@ -180,12 +246,6 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
 #pragma unroll
         for (int q = 0; q < EPC; ++q) smem[p.off_rq + row * p.kpitch + ch * EPC + q] = e[q];
       }
-    }
-  }
-  if (p.dv > D) {  // transposed-V rows beyond the head dim stay zero
-    for (int i = tid; i < (p.dv - D) * p.vpitch; i += nth) {
-      reinterpret_cast<DT*>(smem_b + p.off_v[0] * 4)[D * p.vpitch + i] = static_cast<DT>(0.0f);
-      if constexpr (!RES) reinterpret_cast<DT*>(smem_b + p.off_v[1] * 4)[D * p.vpitch + i] = static_cast<DT>(0.0f);
     }
   }
 
@@ -213,252 +273,148 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
     for (int kk = 0; kk < KS; ++kk) qf[kk] = qvalid ? qg[static_cast<int64_t>(qn) * D + 2 * kk + h] : 0.0f;
   }
 
-  // ---- block staging.
-  auto slot_n = [&](int blk, int s) -> int {      // N index of a key slot, -1 for padding
+  // ---- the block stream.
+  const int n_kt = TK ? p.nbt : 0;                 // rK blocks first
+  const int n_vt = TV ? p.nbt : 0;                 // rV blocks last
+  const int L = n_kt + p.n_blocks + n_vt;
+  auto kind_of = [&](int e) -> int {
+    return e < n_kt ? kElemKeyTable : (e < n_kt + p.n_blocks ? kElemKeys : kElemValueTable);
+  };
+  // N index of a key slot; padding slots read a valid token (their values are masked)
+  auto slot_n = [&](int blk, int s) -> int {
     if (p.prefix_block) {
-      if (blk == 0) return s < p.P ? s : -1;
+      if (blk == 0) return s < p.P ? s : wbase;
       blk -= 1;
     }
     const int sigma = blk * kBlockSlots + s;
     const int y = sigma >> p.lwp, x = sigma & (p.Wp - 1);
-    if (y >= p.R) return -1;
-    if (x < p.C) return wbase + y * rowstride + x;
-    if (p.prefix_in_tail && y == p.R - 1 && x - p.C < p.P) return x - p.C;
-    return -1;
+    if (y < p.R && x < p.C) return wbase + y * rowstride + x;
+    if (p.prefix_in_tail && y == p.R - 1 && x >= p.C && x - p.C < p.P) return x - p.C;
+    return wbase;
   };
-  auto load_rows = [&](const DT* src, int blk, uint4 (&kr)[ITEMS], uint4 (&vr)[ITEMS], const DT* src2) {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int item = tid + it * nth;
-      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-      if (item < kBlockSlots * CH) {
-        const int s = item / CH, ch = item - (item / CH) * CH;
-        const int n = slot_n(blk, s);
-        if (n >= 0) {
-          const int64_t off = static_cast<int64_t>(n) * D + ch * EPC;
-          a = ld16(src + off);
-          if (src2) b = ld16(src2 + off);
-        }
-      }
-      kr[it] = a;
-      vr[it] = b;
+  // direct-to-LDS instructions this wave issues per 32-row tile
+  const int my_ipb = wid < IPB ? (IPB - wid + NW - 1) / NW : 0;
+  auto elem_loads = [&](int e) -> int { return kind_of(e) == kElemKeys ? 2 * my_ipb : my_ipb; };
+  auto stage_k = [&](int e) -> char* { return smem_b + p.off_stage * 4 + (e % kStages) * 2 * TILE; };
+  auto stage_v = [&](int e) -> char* { return stage_k(e) + TILE; };
+  // copy 32 rows of a [rows][D] tensor into a swizzled row-major tile: instruction i
+  // covers rows [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR
+  // with global chunk (l % CPR) ^ (row % CPR).
+  auto dma_tile = [&](char* tile, const DT* src, auto&& row_index) {
+    for (int i = wid; i < IPB; i += NW) {
+      const int row = i * RPI + lane / CPR;
+      const int pos = lane % CPR;
+      const int c = pos ^ (row & (CPR - 1));
+      const DT* g = src + static_cast<int64_t>(row_index(row)) * D + c * EPC;
+      dma16(g, tile + i * 1024);
     }
   };
-  auto store_k = [&](int buf, const uint4 (&kr)[ITEMS]) {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int item = tid + it * nth;
-      if (item < kBlockSlots * CH) {
-        const int s = item / CH, ch = item - (item / CH) * CH;
-        if constexpr (BF) {
-          *reinterpret_cast<uint4*>(smem_b + p.off_k[buf] * 4 + (s * p.kpitch + ch * EPC) * 2) = kr[it];
-        } else {
-          const float* e = reinterpret_cast<const float*>(&kr[it]);
-          float* kt = smem + p.off_k[buf] + s * p.kpitch + ch * EPC;
-#pragma unroll
-          for (int q = 0; q < EPC; ++q) kt[q] = e[q];
-        }
-      }
-    }
-  };
-  auto store_vt = [&](int buf, const uint4 (&vr)[ITEMS]) {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int item = tid + it * nth;
-      if (item < kBlockSlots * CH) {
-        const int s = item / CH, ch = item - (item / CH) * CH;
-        const DT* e = reinterpret_cast<const DT*>(&vr[it]);
-        DT* vt = reinterpret_cast<DT*>(smem_b + p.off_v[buf] * 4);
-#pragma unroll
-        for (int q = 0; q < EPC; ++q) vt[(ch * EPC + q) * p.vpitch + s] = e[q];
-      }
-    }
-  };
-  // rows [32t, 32t+32) of a table [nb][D] as a "block" (zero past nb)
-  auto load_table = [&](const DT* tab, int t, uint4 (&kr)[ITEMS]) {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int item = tid + it * nth;
-      uint4 a = make_uint4(0, 0, 0, 0);
-      if (item < kBlockSlots * CH) {
-        const int s = item / CH, ch = item - (item / CH) * CH;
-        const int row = kRowTile * t + s;
-        if (row < p.nb) a = ld16(tab + static_cast<int64_t>(row) * D + ch * EPC);
-      }
-      kr[it] = a;
-    }
-  };
-
-  // S^T tile of the block in LDS buffer `buf` (or a staged table) against this lane's Q.
-  auto s_tile = [&](int koff_words, int kpitch) -> f32x16 {
-    f32x16 acc = {};
-    if constexpr (BF) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int d0 = 16 * kk + 8 * h;
-        uint4 kv = make_uint4(0, 0, 0, 0);
-        if (d0 < D) kv = *reinterpret_cast<const uint4*>(smem_b + koff_words * 4 + (r32 * kpitch + d0) * 2);
-        acc = mfma32(as_bf16x8(kv), qb[kk], acc);
-      }
+  auto issue = [&](int e) {
+    const int kind = kind_of(e);
+    if (kind == kElemKeyTable) {
+      const int t = e;
+      dma_tile(stage_k(e), rk, [&](int r) { const int b = kRowTile * t + r; return b < p.nb ? b : 0; });
+    } else if (kind == kElemKeys) {
+      const int blk = e - n_kt;
+      dma_tile(stage_k(e), kg, [&](int r) { return slot_n(blk, r); });
+      dma_tile(stage_v(e), vg, [&](int r) { return slot_n(blk, r); });
     } else {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) acc = mfma32(smem[koff_words + r32 * kpitch + 2 * kk + h], qf[kk], acc);
+      const int t = e - n_kt - p.n_blocks;
+      dma_tile(stage_v(e), rv, [&](int r) { const int b = kRowTile * t + r; return b < p.nb ? b : 0; });
     }
-    return acc;
   };
 
-  // S^T from a K operand held in registers (resident variant): kop[kk] is
-  // K[slot r32][k-slice h of step kk].
-  using KOp = typename std::conditional<BF, uint4, float>::type;
-  auto s_regs = [&](const KOp (&kop)[KS]) -> f32x16 {
+  // K operand (A of S^T): lane holds K[slot r32][d 16kk + 8h .. +7] (bf16) / [2kk + h] (fp32).
+  auto s_tile = [&](const char* tile) -> f32x16 {
     f32x16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      if constexpr (BF)
-        acc = mfma32(as_bf16x8(kop[kk]), qb[kk], acc);
-      else
-        acc = mfma32(kop[kk], qf[kk], acc);
-    }
-    return acc;
-  };
-  // K operand of one block (or of rows [32t, 32t+32) of a table) straight from global memory.
-  auto load_kop = [&](const DT* src, int n, KOp (&kop)[KS]) {
+    const int sw = r32 & (CPR - 1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       if constexpr (BF) {
-        const int d0 = 16 * kk + 8 * h;
-        kop[kk] = (n >= 0 && d0 < D) ? ld16(src + static_cast<int64_t>(n) * D + d0) : make_uint4(0, 0, 0, 0);
+        const int c = 2 * kk + h;
+        uint4 kv = make_uint4(0, 0, 0, 0);
+        if (c < CPR) kv = *reinterpret_cast<const uint4*>(tile + r32 * RB + ((c ^ sw) << 4));
+        acc = mfma32(as_bf16x8(kv), qb[kk], acc);
       } else {
-        kop[kk] = n >= 0 ? src[static_cast<int64_t>(n) * D + 2 * kk + h] : 0.0f;
+        const int col = (2 * kk + h) * 4;  // byte column
+        const float kv = *reinterpret_cast<const float*>(tile + r32 * RB + (((col >> 4) ^ sw) << 4) + (col & 15));
+        acc = mfma32(kv, qf[kk], acc);
       }
     }
+    return acc;
   };
 
-  // O^T += V^T P^T with V^T in LDS buffer `buf`; pv[j][i] is this lane's weight
-  // for key 8j + 4h + i (bf16: k slots 8h..8h+7 of step kk hold keys
-  // 16kk + 4h + (0..3) and 16kk + 8 + 4h + (0..3)).
+  // O^T += V^T P^T from a swizzled row-major [32 keys][D] tile.  pv[j][i] is this
+  // lane's weight for key 8j + 4h + i.  bf16: the k slots 8h..8h+7 of step kk hold
+  // keys 16kk + 4h + (0..3) and 16kk + 8 + 4h + (0..3), read with two transpose
+  // loads (within each 16-lane group, lane 4m + a reads 4 head-dim values of key
+  // base + m at column 4a, and lane 4a + k' receives column 4a + k' of keys base..base+3).
   f32x16 oacc[DTL];
 #pragma unroll
   for (int c = 0; c < DTL; ++c) oacc[c] = f32x16{};
-  auto pv_tile = [&](int voff_words, int vpitch, int col0, const float (&pv)[4][4], bool split) {
+  auto pv_tile = [&](const char* tile, const float (&pv)[4][4], bool split) {
     if constexpr (BF) {
+      const int g16 = lane >> 4, i16 = lane & 15;
+      const int m = i16 >> 2, a = i16 & 3;
+      const int dsub = (g16 & 1) * 16;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 pb, pl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float a = pv[2 * kk][i], b = pv[2 * kk + 1][i];
-          pb[i] = static_cast<__bf16>(a);
-          pb[4 + i] = static_cast<__bf16>(b);
+          const float x0 = pv[2 * kk][i], x1 = pv[2 * kk + 1][i];
+          pb[i] = static_cast<__bf16>(x0);
+          pb[4 + i] = static_cast<__bf16>(x1);
           if (split) {
-            pl[i] = static_cast<__bf16>(a - static_cast<float>(pb[i]));
-            pl[4 + i] = static_cast<__bf16>(b - static_cast<float>(pb[4 + i]));
+            pl[i] = static_cast<__bf16>(x0 - static_cast<float>(pb[i]));
+            pl[4 + i] = static_cast<__bf16>(x1 - static_cast<float>(pb[4 + i]));
           }
         }
-        const char* vt = smem_b + voff_words * 4;
+        const int row0 = 16 * kk + 4 * (g16 >> 1) + m, row1 = row0 + 8;
 #pragma unroll
         for (int c = 0; c < DTL; ++c) {
-          const int d = 32 * c + r32;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vt + (d * vpitch + col0 + 16 * kk + 4 * h) * 2);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vt + (d * vpitch + col0 + 16 * kk + 8 + 4 * h) * 2);
-          const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-          oacc[c] = mfma32(a, pb, oacc[c]);
-          if (split) oacc[c] = mfma32(a, pl, oacc[c]);
+          int col = 32 * c + dsub + 4 * a;   // head-dim column (element)
+          if (col >= D) col = 0;             // beyond the head dim: any in-row value (unused outputs)
+          const int cb = col * 2;
+          const int o0 = row0 * RB + (((cb >> 4) ^ (row0 & (CPR - 1))) << 4) + (cb & 15);
+          const int o1 = row1 * RB + (((cb >> 4) ^ (row1 & (CPR - 1))) << 4) + (cb & 15);
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tile + o0));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tile + o1));
+          bf16x8 av;
+          __builtin_memcpy(&av, &v0, 8);
+          __builtin_memcpy(reinterpret_cast<char*>(&av) + 8, &v1, 8);
+          oacc[c] = mfma32(av, pb, oacc[c]);
+          if (split) oacc[c] = mfma32(av, pl, oacc[c]);
         }
       }
     } else {
-      const float* vt = smem + voff_words;
 #pragma unroll
       for (int c = 0; c < DTL; ++c) {
         const int d = 32 * c + r32;
+        const int cb = (d < D ? d : 0) * 4;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[c] = mfma32(vt[d * vpitch + col0 + 8 * j + 4 * h + i], pv[j][i], oacc[c]);
+          for (int i = 0; i < 4; ++i) {
+            const int key = 8 * j + 4 * h + i;
+            float vv = *reinterpret_cast<const float*>(tile + key * RB + (((cb >> 4) ^ (key & (CPR - 1))) << 4) + (cb & 15));
+            if (d >= D) vv = 0.0f;
+            oacc[c] = mfma32(vv, pv[j][i], oacc[c]);
+          }
       }
     }
   };
 
-  uint4 ra[ITEMS], rb[ITEMS], rc[ITEMS], rd[ITEMS];
-
-  // ---- resident variant: the unit's V, transposed, into LDS ([dv][n_blocks*32 + pad]).
-  if constexpr (RES) {
-    const int total = p.n_blocks * kBlockSlots * CH;
-    DT* vt = reinterpret_cast<DT*>(smem_b + p.off_v[0] * 4);
-    for (int base0 = 0; base0 < total; base0 += 4 * nth) {
-      uint4 vr[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int item = base0 + u * nth + tid;
-        vr[u] = make_uint4(0, 0, 0, 0);
-        if (item < total) {
-          const int slot = item / CH, ch = item - (item / CH) * CH;
-          const int n = slot_n(slot / kBlockSlots, slot % kBlockSlots);
-          if (n >= 0) vr[u] = ld16(vg + static_cast<int64_t>(n) * D + ch * EPC);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int item = base0 + u * nth + tid;
-        if (item < total) {
-          const int slot = item / CH, ch = item - (item / CH) * CH;
-          const DT* e = reinterpret_cast<const DT*>(&vr[u]);
-#pragma unroll
-          for (int q = 0; q < EPC; ++q) vt[(ch * EPC + q) * p.vpitch + slot] = e[q];
-        }
-      }
-    }
-  }
-
-  // ---- contextual key term: TK[row][b] = c * q_row . rK[b] (rK streamed as key blocks).
-  const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab : p.off_tab;
-  __syncthreads();
-  if constexpr (TK && RES) {
-    if (active) {
-      const DT* rk = reinterpret_cast<const DT*>(p.rk) + head * p.tab_head_stride;
-      KOp ka[KS], kb[KS];
-      load_kop(rk, r32 < p.nb ? r32 : -1, ka);
-      for (int t = 0; t < p.nbt; ++t) {
-        const int nxt = kRowTile * (t + 1) + r32;
-        if (t + 1 < p.nbt) load_kop(rk, nxt < p.nb ? nxt : -1, kb);
-        const f32x16 acc = s_regs(ka);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int b = kRowTile * t + 8 * j + 4 * h + i;
-            if (b < p.nb) smem[rowbase + b] = acc[4 * j + i] * p.c;
-          }
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) ka[kk] = kb[kk];
-      }
-    }
-  }
-  if constexpr (TK && !RES) {
-    const DT* rk = reinterpret_cast<const DT*>(p.rk) + head * p.tab_head_stride;
-    for (int t = 0; t < p.nbt; ++t) {
-      load_table(rk, t, ra);
-      store_k(0, ra);
-      __syncthreads();
-      if (active) {
-        const f32x16 acc = s_tile(p.off_k[0], p.kpitch);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int b = kRowTile * t + 8 * j + 4 * h + i;
-            if (b < p.nb) smem[rowbase + b] = acc[4 * j + i] * p.c;
-          }
-      }
-      __syncthreads();
-    }
-  }
-
   // ---- column parts of the LDS addresses: cx[ph][j][i] for this lane's key 8j + 4h + i
   // of a block at phase ph (ph = block index & 1 when a grid row spans two blocks).
+  const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab : p.off_tab;
   const int w_off = TV ? p.off_w - p.off_tab : 0;
-  int cx[NPH][4][4];
-  int cxq[NPH][4][4];
+  __syncthreads();  // prologue tables visible; no direct-to-LDS load is in flight yet
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // Q and table loads done before the ring starts
+  // byte addresses: cxb = gather-target column part, cqb = query-term column part;
+  // the row part ry (a word offset in the per-axis table) is added as bytes below
+  int cxb[NPH][4][4];
+  int cqb[NPH][4][4];
 #pragma unroll
   for (int ph = 0; ph < NPH; ++ph)
 #pragma unroll
@@ -478,74 +434,78 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
             aq = p.off_tq + s * p.p_tq + cpart;
           }
         }
-        cx[ph][j][i] = a;
-        cxq[ph][j][i] = aq;
+        cxb[ph][j][i] = 4 * a;
+        cqb[ph][j][i] = 4 * aq;
       }
-  (void)cxq;
+  (void)cqb;
+  const int* __restrict__ ryt = smem_i + p.off_ry + (qpos ? yi : 0) + p.R - 1;  // ry table at yq - y + R - 1
+  const int w_offb = 4 * w_off;
 
   // ---- running state of this lane's row (shared with the lane l ^ 32).
   float m_run = kNegBig;
   float l_part = 0.0f;
 
-  auto process_block = [&](auto ph_tag, const f32x16& s, int voff, int vpitch, int col0, int gblk,
-                           bool prefix_blk) {
+  // Logit of pair (row, key) in log2 units given the LDS byte addresses of its terms.
+  auto logit = [&](float sv, int ab, int aqb) -> float {
+    float add = 0.0f;
+    if constexpr (GATHER) add = *reinterpret_cast<const float*>(smem_b + ab);
+    if constexpr (TQ) add += *reinterpret_cast<const float*>(smem_b + aqb);
+    return fmaf(sv, p.c, add);
+  };
+
+  auto process_block = [&](auto ph_tag, const f32x16& s, const char* vtile, int gblk, bool prefix_blk) {
     constexpr int PH = decltype(ph_tag)::value;
-    int addr[4][4], addrq[4][4];
-    if (prefix_blk) {
+    float x[4][4];
+    int ab[4][4];          // gather addresses, kept for the value-term scatter
+    const bool tail = !prefix_blk && (((gblk * kBlockSlots + kBlockSlots - 1) >> p.lwp) >= p.R - 1);
+    if (__builtin_expect(!prefix_blk && !tail, 1)) {
+      // interior block: every key is a grid key of rows < R-1 or a padding column
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        const int yj = (gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
+        const int ryb = 4 * ryt[-yj];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool pre = 8 * j + 4 * h + i < p.P;
-          addr[j][i] = pre ? p.off_zero : p.off_neg;
-          addrq[j][i] = pre ? p.off_tqz : p.off_tqn;
+          ab[j][i] = ryb + cxb[PH][j][i];
+          x[j][i] = logit(s[4 * j + i], ab[j][i], ryb + cqb[PH][j][i]);
         }
+      }
     } else {
-      const int yq = qpos ? yi : 0;
+      // prefix block or the last grid rows: padding rows, and prefix keys kept in
+      // the padding columns of the last row, get their guard regions
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int yj = (gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
         const int yk = yj < p.R ? yj : p.R - 1;
-        const int ry = smem_i[p.off_ry + yq - yk + p.R - 1];
+        const int ryb = 4 * ryt[-yk];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          addr[j][i] = ry + cx[PH][j][i];
-          addrq[j][i] = ry + cxq[PH][j][i];
-        }
-      }
-      if (((gblk * kBlockSlots + kBlockSlots - 1) >> p.lwp) >= p.R - 1) {  // tail block (wave-uniform)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int yj = (gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int xj = (gblk * kBlockSlots + 8 * j + 4 * h + i) & (p.Wp - 1);
-            if (yj >= p.R) {
-              addr[j][i] = p.off_neg;
-              addrq[j][i] = p.off_tqn;
-            } else if (p.prefix_in_tail && yj == p.R - 1 && xj >= p.C && xj - p.C < p.P) {
-              addr[j][i] = p.off_zero;
-              addrq[j][i] = p.off_tqz;
-            }
+          const int slot = 8 * j + 4 * h + i;
+          const int xj = (gblk * kBlockSlots + slot) & (p.Wp - 1);
+          int a = ryb + cxb[PH][j][i], aq = ryb + cqb[PH][j][i];
+          if (prefix_blk) {
+            const bool pre = slot < p.P;
+            a = 4 * (pre ? p.off_zero : p.off_neg);
+            aq = 4 * (pre ? p.off_tqz : p.off_tqn);
+          } else if (yj >= p.R) {
+            a = 4 * p.off_neg;
+            aq = 4 * p.off_tqn;
+          } else if (p.prefix_in_tail && yj == p.R - 1 && xj >= p.C && xj - p.C < p.P) {
+            a = 4 * p.off_zero;
+            aq = 4 * p.off_tqz;
           }
+          ab[j][i] = a;
+          x[j][i] = logit(s[4 * j + i], a, aq);
         }
       }
     }
-    float x[4][4];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float add = 0.0f;
-        if constexpr (GATHER) add = smem[addr[j][i]];
-        if constexpr (TQ) add += smem[addrq[j][i]];
-        x[j][i] = fmaf(s[4 * j + i], p.c, add);
-        bmax = fmaxf(bmax, x[j][i]);
-      }
+    float bmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    bmax = fmaxf(bmax, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
+                             fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const bool need = bmax > m_run + kLazyTau;
-    if (__any(need)) {
+    if (__builtin_expect(__any(need), 0)) {
       const float m_new = need ? bmax : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_part *= alpha;
@@ -570,32 +530,32 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(&smem[addr[j][i] + w_off], pr[j][i]);
+        for (int i = 0; i < 4; ++i) atomicAdd(reinterpret_cast<float*>(smem_b + ab[j][i] + w_offb), pr[j][i]);
     }
-    pv_tile(voff, vpitch, col0, pr, false);
+    pv_tile(vtile, pr, false);
   };
 
-  // Query-term scores of the block: TQ[slot][b] = c * k_slot . rQ[b]; tiles over waves.
-  auto block_query_scores = [&](int buf) {
+  // Query-term scores of a key block: TQ[slot][b] = c * k_slot . rQ[b]; tiles over waves.
+  auto block_query_scores = [&](const char* ktile) {
     if constexpr (TQ) {
+      const int sw = r32 & (CPR - 1);
       for (int t = wid; t < p.nbt; t += NW) {
         f32x16 acc = {};
-        if constexpr (BF) {
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) {
-            const int d0 = 16 * kk + 8 * h;
+        for (int kk = 0; kk < KS; ++kk) {
+          if constexpr (BF) {
+            const int c = 2 * kk + h, d0 = 16 * kk + 8 * h;
             uint4 a = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
-            if (d0 < D) {
+            if (c < CPR) {
               a = *reinterpret_cast<const uint4*>(smem_b + p.off_rq * 4 + ((kRowTile * t + r32) * p.kpitch + d0) * 2);
-              kv = *reinterpret_cast<const uint4*>(smem_b + p.off_k[buf] * 4 + (r32 * p.kpitch + d0) * 2);
+              kv = *reinterpret_cast<const uint4*>(ktile + r32 * RB + ((c ^ sw) << 4));
             }
             acc = mfma32(as_bf16x8(a), as_bf16x8(kv), acc);
+          } else {
+            const int col = (2 * kk + h) * 4;
+            const float kv = *reinterpret_cast<const float*>(ktile + r32 * RB + (((col >> 4) ^ sw) << 4) + (col & 15));
+            acc = mfma32(smem[p.off_rq + (kRowTile * t + r32) * p.kpitch + 2 * kk + h], kv, acc);
           }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk)
-            acc = mfma32(smem[p.off_rq + (kRowTile * t + r32) * p.kpitch + 2 * kk + h],
-                         smem[p.off_k[buf] + r32 * p.kpitch + 2 * kk + h], acc);
         }
         // lane holds TQ[slot r32][32t + 8j + 4h + i]
 #pragma unroll
@@ -609,102 +569,65 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
     }
   };
 
-  auto run_block = [&](int blk, int buf) {
-    if constexpr (TQ) {
-      block_query_scores(buf);
-      __syncthreads();
-    }
-    if (active) {
-      const bool pre = p.prefix_block && blk == 0;
-      const int gblk = blk - p.prefix_block;
-      const f32x16 s = s_tile(p.off_k[buf], p.kpitch);
-      if constexpr (WIDE) {
-        if (gblk & 1)
-          process_block(std::integral_constant<int, 1>{}, s, p.off_v[buf], p.vpitch, 0, gblk, pre);
-        else
-          process_block(std::integral_constant<int, 0>{}, s, p.off_v[buf], p.vpitch, 0, gblk, pre);
-      } else {
-        process_block(std::integral_constant<int, 0>{}, s, p.off_v[buf], p.vpitch, 0, gblk, pre);
+  // ---- walk the stream: element e is computed while elements e+1 .. e+kStages-2
+  // are in flight; element e+kStages-1 is issued into the stage element e-1 used.
+  for (int e = 0; e < kStages - 1 && e < L; ++e) issue(e);
+  for (int e = 0; e < L; ++e) {
+    int after = 0;  // this wave's loads issued after element e's
+    for (int f = e + 1; f < L && f < e + kStages - 1; ++f) after += elem_loads(f);
+    wait_vmcnt(after);
+    lds_barrier();
+    if (e + kStages - 1 < L) issue(e + kStages - 1);
+    const int kind = kind_of(e);
+    if (kind == kElemKeyTable) {
+      if constexpr (TK) {
+        if (active) {
+          const int t = e;
+          const f32x16 acc = s_tile(stage_k(e));
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int b = kRowTile * t + 8 * j + 4 * h + i;
+              if (b < p.nb) smem[rowbase + b] = acc[4 * j + i] * p.c;
+            }
+        }
       }
-    }
-  };
-
-  // ---- main loop: block n computed from LDS while block n+1 waits in registers
-  // and block n+2 is being fetched.
-  const int NB = p.n_blocks;
-  if constexpr (RES) {
-    // The unit's transposed V is already in LDS (staged in the prologue).
-    auto run_res = [&](int blk, const KOp (&kop)[KS]) {
-      const bool pre = p.prefix_block && blk == 0;
-      const int gblk = blk - p.prefix_block;
-      const f32x16 s = s_regs(kop);
-      if constexpr (WIDE) {
-        if (gblk & 1)
-          process_block(std::integral_constant<int, 1>{}, s, p.off_v[0], p.vpitch, blk * kBlockSlots, gblk, pre);
-        else
-          process_block(std::integral_constant<int, 0>{}, s, p.off_v[0], p.vpitch, blk * kBlockSlots, gblk, pre);
-      } else {
-        process_block(std::integral_constant<int, 0>{}, s, p.off_v[0], p.vpitch, blk * kBlockSlots, gblk, pre);
+    } else if (kind == kElemKeys) {
+      const int blk = e - n_kt;
+      if constexpr (TQ) {
+        block_query_scores(stage_k(e));
+        lds_barrier();
       }
-    };
-    if (active) {
-      KOp ka[KS], kb[KS];
-      load_kop(kg, slot_n(0, r32), ka);
-      for (int n = 0; n < NB; n += 2) {
-        if (n + 1 < NB) load_kop(kg, slot_n(n + 1, r32), kb);
-        run_res(n, ka);
-        if (n + 1 >= NB) break;
-        if (n + 2 < NB) load_kop(kg, slot_n(n + 2, r32), ka);
-        run_res(n + 1, kb);
-      }
-    }
-  } else {
-  load_rows(kg, 0, ra, rb, vg);
-  store_k(0, ra);
-  store_vt(0, rb);
-  if (NB > 1) load_rows(kg, 1, rc, rd, vg);
-  __syncthreads();
-  for (int n = 0; n < NB; n += 2) {
-    // even step: block n in buffer 0, block n+1 in (rc, rd)
-    if (n + 2 < NB) load_rows(kg, n + 2, ra, rb, vg);
-    run_block(n, 0);
-    if (n + 1 < NB) {
-      store_k(1, rc);
-      store_vt(1, rd);
-    }
-    __syncthreads();
-    if (n + 1 >= NB) break;
-    // odd step: block n+1 in buffer 1, block n+2 in (ra, rb)
-    if (n + 3 < NB) load_rows(kg, n + 3, rc, rd, vg);
-    run_block(n + 1, 1);
-    if (n + 2 < NB) {
-      store_k(0, ra);
-      store_vt(0, rb);
-    }
-    __syncthreads();
-  }
-  }
-
-  // ---- value term: O^T += rV^T W^T (rV streamed through the value buffer, W split
-  // into two bf16 parts for accuracy).
-  if constexpr (TV) {
-    const DT* rv = reinterpret_cast<const DT*>(p.rv) + head * p.tab_head_stride;
-    for (int t = 0; t < p.nbt; ++t) {
-      load_table(rv, t, ra);
-      store_vt(0, ra);
-      __syncthreads();
       if (active) {
-        float wv[4][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int b = kRowTile * t + 8 * j + 4 * h + i;
-            wv[j][i] = b < p.nb ? smem[rowbase + w_off + b] : 0.0f;
-          }
-        pv_tile(p.off_v[0], p.vpitch, 0, wv, true);
+        const bool pre = p.prefix_block && blk == 0;
+        const int gblk = blk - p.prefix_block;
+        const f32x16 s = s_tile(stage_k(e));
+        if constexpr (WIDE) {
+          if (gblk & 1)
+            process_block(std::integral_constant<int, 1>{}, s, stage_v(e), gblk, pre);
+          else
+            process_block(std::integral_constant<int, 0>{}, s, stage_v(e), gblk, pre);
+        } else {
+          process_block(std::integral_constant<int, 0>{}, s, stage_v(e), gblk, pre);
+        }
       }
-      __syncthreads();
+    } else {
+      // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
+      if constexpr (TV) {
+        if (active) {
+          const int t = e - n_kt - p.n_blocks;
+          float wv[4][4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int b = kRowTile * t + 8 * j + 4 * h + i;
+              wv[j][i] = b < p.nb ? smem[rowbase + w_off + b] : 0.0f;
+            }
+          pv_tile(stage_v(e), wv, true);
+        }
+      }
     }
   }
 
@@ -734,24 +657,18 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
   if (p.lse && h == 0) p.lse[bh * p.N + qn] = (m_run + log2f(l)) * 0.6931471805599453f;
 }
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool RES>
-hipError_t launch_fwd_r(const Params& p, hipStream_t stream) {
-  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, RES>;
+// ----------------------------------------------------------------------------------------
+// Launch dispatch.
+
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE>
+hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
+  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE>;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(p.n_wg)), dim3(p.NW * 64),
                      static_cast<size_t>(p.lds_words) * 4, stream, p);
   return hipGetLastError();
-}
-
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE>
-hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
-  constexpr bool kCanRes = MODE != RPE_MODE_CONTEXTUAL || TERMS == RPE_TERM_K;
-  if constexpr (kCanRes) {
-    if (p.resident) return launch_fwd_r<DT, D, MODE, TERMS, WIDE, true>(p, stream);
-  }
-  return launch_fwd_r<DT, D, MODE, TERMS, WIDE, false>(p, stream);
 }
 
 template <typename DT, int D, int MODE, unsigned TERMS>

@@ -33,25 +33,10 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   const int eb = p->elem_bytes;
   const bool ctx = d->mode == RPE_MODE_CONTEXTUAL;
   const bool tq = ctx && (d->terms & RPE_TERM_Q);
-  p->dv = p->D > kBlockSlots ? p->D : kBlockSlots;
   p->kpitch = d->dtype == RPE_BF16 ? p->D + 8 : p->D + 1;
-  p->vpitch = d->dtype == RPE_BF16 ? kBlockSlots + 8 : kBlockSlots + 1;
   int off = 0;
-  if (p->resident) {
-    // the whole unit's V^T; K comes straight from global memory
-    p->vpitch = p->n_blocks * kBlockSlots + (d->dtype == RPE_BF16 ? 8 : 1);
-    const int vwords = (p->dv * p->vpitch * eb + 3) / 4;
-    p->off_k[0] = p->off_k[1] = 0;
-    p->off_v[0] = p->off_v[1] = 0;
-    off += (vwords + 3) / 4 * 4;
-  } else {
-    const int kwords = (kBlockSlots * p->kpitch * eb + 3) / 4;
-    const int vwords = (p->dv * p->vpitch * eb + 3) / 4;
-    for (int i = 0; i < 2; ++i) {
-      p->off_k[i] = off; off += (kwords + 3) / 4 * 4;
-      p->off_v[i] = off; off += (vwords + 3) / 4 * 4;
-    }
-  }
+  p->off_stage = off;
+  off += kStages * 2 * kBlockSlots * p->D * eb / 4;
   p->off_rq = off;
   if (tq) off += ((p->nbt * kRowTile * p->kpitch * eb + 3) / 4 + 3) / 4 * 4;
   p->zr = (p->S - 1) * p->S + 1;  // 1 when there is no table
@@ -188,19 +173,12 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   // work split: one 32-row query tile per wave, the unit's tiles spread evenly
   // over its workgroups; the widest workgroup (<= kMaxWaves waves, >= 2) whose
   // LDS plan fits is taken.
-  // The resident variant (no per-block barriers) serves units of at most
-  // kResidentSlots key slots with a key or bias term only.
-  const bool can_res = (d->mode != RPE_MODE_CONTEXTUAL || d->terms == RPE_TERM_K) &&
-                       p->n_blocks * kBlockSlots <= kResidentSlots;
-  for (int res = can_res ? 1 : 0; res >= 0; --res) {
-    p->resident = res;
-    for (int max_w = kMaxWaves; max_w >= 2; --max_w) {
-      p->n_qc = (p->n_rt + max_w - 1) / max_w;
-      p->NW = (p->n_rt + p->n_qc - 1) / p->n_qc;
-      if (p->NW < 2) p->NW = 2;  // the block loader assumes at least two waves
-      p->n_wg = p->n_units * p->n_qc;
-      if (lds_layout(d, p) == RPE_OK) return RPE_OK;
-    }
+  for (int max_w = kMaxWaves; max_w >= 2; --max_w) {
+    p->n_qc = (p->n_rt + max_w - 1) / max_w;
+    p->NW = (p->n_rt + p->n_qc - 1) / p->n_qc;
+    if (p->NW < 2) p->NW = 2;  // at least two waves share each stream
+    p->n_wg = p->n_units * p->n_qc;
+    if (lds_layout(d, p) == RPE_OK) return RPE_OK;
   }
   return RPE_E_BUCKETS;
 }

@@ -20,7 +20,7 @@ constexpr int kRowTile = 32;        // query rows per wave (one 32x32 MFMA tile)
 constexpr int kMaxWp = 64;          // widest padded grid row the kernel is built for
 constexpr int kMaxWaves = 4;
 constexpr int kMaxLdsBytes = 160 * 1024;
-constexpr int kResidentSlots = 256;  // largest unit (in key slots) staged whole in LDS
+constexpr int kStages = 4;          // LDS ring depth of the block stream
 
 struct Params {
   // tensors
@@ -48,7 +48,6 @@ struct Params {
   int prefix_block;       // 1: a separate leading block holds the prefix keys
   int grid_blocks;        // blocks of 32 slots covering R * Wp grid slots
   int n_blocks;           // prefix_block + grid_blocks
-  int resident;           // 1: the unit's transposed V lives in LDS for the whole kernel
   // work split
   int n_rt;               // 32-row query tiles per unit
   int NW;                 // waves per workgroup (one row tile each)
@@ -56,9 +55,8 @@ struct Params {
   int64_t n_units;        // B * H * U
   int64_t n_wg;           // n_units * n_qc
   // LDS layout, in 4-byte words
-  int off_k[2], off_v[2]; // K block [32][kpitch], transposed V block [DV][vpitch]
-  int kpitch, vpitch;     // in elements of the storage dtype
-  int dv;                 // rows of the transposed V block (max(D, 32))
+  int off_stage;          // kStages x {K tile, V tile}, each [32][D] row-major, swizzled
+  int kpitch;             // row pitch (elements) of the staged query-term table
   int off_rq;             // query-term table staged as [nbt*32][kpitch]
   int off_tab;            // gather target: per-row bucket scores (contextual) or bias table
   int p_tab;              // row pitch of the per-row bucket scores
