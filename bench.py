@@ -5,8 +5,8 @@ contextual Product keys: batch 64, 14 x 14 grid + class token, 6 heads,
 d = 64, bf16, an 81 x 64 key table shared by the heads) over one batch of
 synthetic input already in HBM.  The timed steps cycle through enough input
 copies that the working set is larger than the 256 MB Infinity Cache, so
-every step reads its inputs from HBM; the same launch on one resident buffer
-set is reported as "warm".  The other bf16 workloads (Swin-T stage-1 windows,
+every step reads its inputs from HBM; with --warm the same launch on one
+resident buffer set is also reported, as "warm".  The other bf16 workloads (Swin-T stage-1 windows,
 DeiT-S with query/key/value terms, the 56 x 56 high-resolution grid) are
 timed the same way and reported under "secondary".
 
@@ -17,6 +17,12 @@ k, v read once + o written once.
 
 The CPU baseline is the fp64 oracle, run in a process pool over (batch,
 head) images of the same workload before the GPU is touched.
+
+HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+over this script with ``--copy-probe`` (a plain device copy of known size
+calibrates the counters); the figure is read from profiles/ and reported only
+while the forward kernel's sources still hash to the value it was measured
+with.
 """
 
 import argparse
@@ -39,6 +45,7 @@ SECONDARY = ("swin_t_w7", "deit_s_irpe_qkv", "highres_irpe_k")
 PEAK_MFMA_BF16 = 2500.0      # TFLOP/s, dense, MI355X
 PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
 MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
 COLD_SET_BYTES = 512 << 20   # cycle through at least this much input per step sequence
 
 
@@ -118,6 +125,27 @@ def cpu_baseline(name, budget_s=20.0):
             "seconds": wall}
 
 
+def measured_traffic(name):
+    """(bytes per launch, note) from profiles/traffic_<name>.txt if the kernel is unchanged."""
+    from vision_transformer_attention_amd.profile_summary import kernel_source_hash
+    path = os.path.join(PROFILES, f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        fetch = float(kv["fetch_bytes_per_launch"])
+        write = float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None, "counter summary incomplete"
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return {"fetch": fetch, "write": write, "total": fetch + write}, path
+
+
 # ------------------------------------------------------------------------------ GPU timing
 
 def _device_inputs(w, copies, dev):
@@ -187,6 +215,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--warm-only", action="store_true", help="time one resident buffer set only")
+    ap.add_argument("--warm", action="store_true", help="also time the headline on one resident buffer set")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after timing, run 3 plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -209,9 +240,10 @@ def main():
                                               cold=not args.warm_only)
     print(f"{args.workload}: {ms_cold * 1e3:.2f} us/launch over {copies} buffer sets, finite={ok}",
           file=sys.stderr, flush=True)
-    ms_warm, _, _, _ = time_workload(args.workload, args.steps, args.warmup, dev, cold=False)
+    ms_warm = None
+    if args.warm:
+        ms_warm, _, _, _ = time_workload(args.workload, args.steps, args.warmup, dev, cold=False)
     head = summarize(args.workload, ms_cold)
-    warm = summarize(args.workload, ms_warm)
     w = WORKLOADS[args.workload]
     secondary = {}
     if not args.no_secondary:
@@ -228,6 +260,15 @@ def main():
                                "warm_tflops": sw["tflops"], "warm_mfma_frac": sw["mfma_frac"],
                                "finite": okc}
             print(f"{name}: {mc * 1e3:.2f} us cold, {mw * 1e3:.2f} us warm", file=sys.stderr, flush=True)
+    if args.copy_probe > 0:
+        n = args.copy_probe << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     flop, nbytes = flops_bytes(w)
     intensity = flop / nbytes
     ridge = PEAK_MFMA_BF16 * 1e12 / (PEAK_HBM * 1e9)
@@ -237,6 +278,12 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_MFMA_BF16, "unit": "TFLOP/s",
                 "frac": head["tflops"] / PEAK_MFMA_BF16, "traffic": None}
+    traffic, tnote = measured_traffic(args.workload)
+    if traffic is not None:
+        roof["traffic"] = traffic["total"]
+        roof["traffic_fetch"] = traffic["fetch"]
+        roof["traffic_write"] = traffic["write"]
+    roof["traffic_source"] = tnote if traffic is None else os.path.relpath(tnote, ROOT)
     roof["kernel"] = "rpe_fwd_kernel"
     roof["algorithmic_bytes_per_launch"] = nbytes
     roof["algorithmic_flop_per_launch"] = flop
@@ -258,11 +305,14 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "mfma_frac": head["mfma_frac"],
         "roofline": roof,
-        "warm": {"us_per_launch": ms_warm * 1e3, "tflops": warm["tflops"], "mfma_frac": warm["mfma_frac"],
-                 "gbs": warm["gbs"]},
+        "us_per_launch": ms_cold * 1e3,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
         "secondary": secondary,
     }
+    if ms_warm is not None:
+        warm = summarize(args.workload, ms_warm)
+        line["warm"] = {"us_per_launch": ms_warm * 1e3, "tflops": warm["tflops"],
+                        "mfma_frac": warm["mfma_frac"], "gbs": warm["gbs"]}
     print(json.dumps(line), flush=True)
 
 

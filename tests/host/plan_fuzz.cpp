@@ -78,16 +78,39 @@ int main(int argc, char** argv) {
     REQUIRE(rpe::validate(&d) == RPE_OK || st == rpe::validate(&d));
     if (st != RPE_OK) continue;
     ++accepted;
-    REQUIRE(p.lds_words * 4 <= rpe::kMaxLdsBytes);
+    const bool ctx = d.mode == RPE_MODE_CONTEXTUAL;
+    const bool tq = ctx && (d.terms & RPE_TERM_Q), tv = ctx && (d.terms & RPE_TERM_V);
+    const bool rows = ctx && (d.terms & (RPE_TERM_K | RPE_TERM_V));
+    REQUIRE(p.lds_bytes <= rpe::kMaxLdsBytes && p.lds_bytes % 16 == 0);
+    REQUIRE(p.stages >= rpe::kMinStages && p.stages <= rpe::kMaxStages);
+    REQUIRE(p.gsz == ((d.dtype == RPE_BF16 && ctx && !tv) ? 2 : 4));
     REQUIRE(p.off_stage == 0);
-    REQUIRE(p.off_rq * 4 >= rpe::kStages * 2 * rpe::kBlockSlots * p.D * p.elem_bytes);
+    REQUIRE(p.off_rq >= p.stages * 2 * rpe::kBlockSlots * p.D * p.elem_bytes && p.off_rq % 16 == 0);
     REQUIRE(p.off_rq <= p.off_tab);
-    REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr);
+    if (tq) REQUIRE(p.off_rq + p.nbt * rpe::kRowTile * p.kpitch * p.elem_bytes <= p.off_tab);
+    // the per-row scores take a whole 32-bucket tile per store, in rows of an odd number of words
+    REQUIRE(p.p_tab >= p.nbt * rpe::kRowTile && (p.p_tab * p.gsz) % 4 == 0 && ((p.p_tab * p.gsz / 4) & 1));
+    if (rows) REQUIRE(p.off_zero >= p.off_tab + p.NW * rpe::kRowTile * p.p_tab * p.gsz);
+    if (!ctx) REQUIRE(p.off_zero >= p.off_tab + p.nb * p.gsz);
+    REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr * p.gsz);
     REQUIRE(p.zr == (p.S - 1) * p.S + 1);
-    REQUIRE(p.off_ry >= p.off_neg + p.zr);
-    REQUIRE(p.off_cx == p.off_ry + 2 * p.R - 1);
-    REQUIRE(p.off_cx + 2 * p.C - 1 <= p.lds_words);
+    int end_g = p.off_neg + p.zr * p.gsz;
+    if (tv) {
+      REQUIRE(p.off_w >= end_g && p.off_w % 16 == 0);
+      end_g = p.off_w + (p.off_neg + p.zr * p.gsz - p.off_tab);
+    }
+    if (tq) {
+      REQUIRE(p.off_tq >= end_g && p.p_tq >= p.nbt * rpe::kRowTile && (p.p_tq & 1));
+      REQUIRE(p.off_tqz == p.off_tq + rpe::kBlockSlots * p.p_tq * 4 && p.off_tqn == p.off_tqz + p.zr * 4);
+      end_g = p.off_tqn + p.zr * 4;
+    }
+    REQUIRE(p.off_ry >= end_g);
+    REQUIRE(p.off_cx == p.off_ry + (2 * p.R - 1) * 4);
+    REQUIRE(p.off_cx + (2 * p.C - 1) * 4 <= p.lds_bytes);
     REQUIRE(p.kpitch >= p.D);
+    REQUIRE(p.first_tail * rpe::kBlockSlots <= (p.R - 1) * p.Wp &&
+            (p.R - 1) * p.Wp < (p.first_tail + 1) * rpe::kBlockSlots);
+    REQUIRE(p.first_tail < p.grid_blocks);
     REQUIRE(p.Wp >= p.C && p.Wp <= rpe::kMaxWp && (1 << p.lwp) == p.Wp && p.Wp >= 4);
     REQUIRE(p.grid_blocks * rpe::kBlockSlots >= p.R * p.Wp);
     REQUIRE(p.n_rt * rpe::kRowTile >= p.T && p.n_qc * p.NW >= p.n_rt);
@@ -100,14 +123,6 @@ int main(int argc, char** argv) {
     REQUIRE(p.nbt * rpe::kRowTile >= p.nb);
     REQUIRE(p.T == p.P + p.R * p.C);
     REQUIRE(p.N == p.P + d.grid_h * d.grid_w);
-    REQUIRE(p.p_tab >= p.nb);
-    if (d.mode == RPE_MODE_CONTEXTUAL && (d.terms & RPE_TERM_V)) {
-      REQUIRE(p.off_w >= p.off_neg + p.zr);
-    }
-    if (d.mode == RPE_MODE_CONTEXTUAL && (d.terms & RPE_TERM_Q)) {
-      REQUIRE(p.off_tq >= p.off_neg + p.zr && p.p_tq >= p.nb);
-      REQUIRE(p.off_tqz == p.off_tq + rpe::kBlockSlots * p.p_tq && p.off_tqn == p.off_tqz + p.zr);
-    }
     if (p.prefix_in_tail) REQUIRE(p.P <= p.Wp - p.C);
     REQUIRE(p.prefix_block == (p.P > 0 && !p.prefix_in_tail));
   }

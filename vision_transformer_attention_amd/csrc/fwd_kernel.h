@@ -9,13 +9,13 @@
 //
 // In the 32x32 output layout lane l holds column l%32 (its query row) and the
 // rows 8j + 4h + i (h = l/32, j, i in 0..3) (its 16 keys of the block), so a
-// row's softmax state lives in two lanes and reduces with one exchange.
+// row's softmax state lives in two lanes and reduces with one lane swap.
 //
 // Data movement: the workgroup walks one stream of 32-row blocks -- rows of
 // the key table rK (for the bucket scores), then the unit's key/value blocks,
-// then rows of the value table rV -- through a ring of kStages LDS stages.
-// Blocks are copied global -> LDS by the direct-to-LDS loads of gfx950
-// (global_load_lds_dwordx4, no registers involved) kStages-1 blocks ahead of
+// then rows of the value table rV -- through a ring of LDS stages.  Blocks are
+// copied global -> LDS by the direct-to-LDS loads of gfx950
+// (global_load_lds_dwordx4, no registers involved) stages-1 blocks ahead of
 // the block being computed; each stage holds row-major K and V tiles with the
 // 16-byte chunks of a row XOR-swizzled by the row index.  The V^T operand of
 // the PV product is read with the LDS transpose load ds_read_b64_tr_b16.
@@ -24,8 +24,8 @@
 // Position Encoding for Vision Transformer", Method, eqs. 13-17 and 25-28;
 // Swin 2D RPE post, sections 3.1-3.2; Swin relative-bias record, "The claim"):
 //   contextual key term:  TK[i][b] = c * q_i . rK[b] is computed once per row
-//       and bucket (eqs. 26-27) with the same MFMA as S^T, kept in LDS, and
-//       gathered per pair (eq. 28);
+//       and bucket (eqs. 26-27) with the same MFMA as S^T, kept in LDS (fp16
+//       for bf16 inputs), and gathered per pair (eq. 28);
 //   query term: TQ[j][b] = c * k_j . rQ[b] per key block, gathered per pair;
 //   value term: softmax weights are summed per (row, bucket) into LDS with
 //       float atomics, and O^T += rV^T W^T at the end reuses the PV MFMA;
@@ -36,9 +36,11 @@
 // holds the row base and g(dx)+H).  Pairs without a position term address a
 // zero guard region, padding keys a -inf guard region.
 //
-// Softmax runs in log2 units with a lazily moved running max (moved only when
-// a row's block max exceeds it by more than 2^8), so most blocks skip the
-// rescale.
+// Softmax runs in log2 units against a running row maximum m that moves only
+// when a block's maximum exceeds it by more than 2^8 (so most blocks skip the
+// rescale).  m enters the logits through the accumulator of the S^T product,
+// which starts at -m / c instead of zero: the gathered logit then comes out
+// already shifted and feeds exp2 directly.  The first key block sets m.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -65,7 +67,8 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
 constexpr int kThreadsMax = kMaxWaves * 64;
 constexpr float kLazyTau = 8.0f;
-constexpr float kNegBig = -FLT_MAX;
+// bucket scores are clamped into the fp16 range before they are stored
+constexpr float kGatherMax = 65000.0f;
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -82,31 +85,43 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 splat16(float v) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = v;
+  return r;
+}
+
+// max over the two lanes of a row (lanes l and l ^ 32)
+__device__ __forceinline__ float row_max2(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8); the counters not waited on are left at their maxima.
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
-// Wait until at most n vector-memory loads of this wave are outstanding.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(1)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(5)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(6)); break;
-    case 7: __builtin_amdgcn_s_waitcnt(waitcnt_vm(7)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(waitcnt_vm(8)); break;
-    case 9: __builtin_amdgcn_s_waitcnt(waitcnt_vm(9)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(waitcnt_vm(10)); break;
-    case 11: __builtin_amdgcn_s_waitcnt(waitcnt_vm(11)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(waitcnt_vm(12)); break;
-    case 13: __builtin_amdgcn_s_waitcnt(waitcnt_vm(13)); break;
-    case 14: __builtin_amdgcn_s_waitcnt(waitcnt_vm(14)); break;
-    case 15: __builtin_amdgcn_s_waitcnt(waitcnt_vm(15)); break;
-    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(16)); break;
+// Wait until at most n' vector-memory loads of this wave are outstanding, n'
+// the largest of 0, 1, 2, 4, 8, 16 not above n (waiting for more than asked is
+// always safe; the rounding keeps the branch tree short).
+__device__ __forceinline__ void wait_vmcnt_floor(int n) {
+  if (n >= 4) {
+    if (n >= 8) {
+      if (n >= 16)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+    }
+  } else if (n >= 2) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2));
+  } else if (n == 1) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(1));
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
 }
 
@@ -114,9 +129,8 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // LDS byte address lds + 16 * l (lds is the same for the whole wave and goes in
 // M0).  Issued from inline assembly so that the compiler does not order later
 // LDS reads behind it: completion is tracked explicitly with s_waitcnt vmcnt.
-__device__ __forceinline__ void dma16(const void* g, const char* lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)const_cast<char*>(lds))));
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(base) : "memory", "m0");
 }
 
@@ -140,13 +154,14 @@ struct Traits<float> {
   static constexpr int kEpc = 4;
 };
 
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
+
 }  // namespace
 
-// Stream element kinds.
-enum : int { kElemKeyTable = 0, kElemKeys = 1, kElemValueTable = 2 };
-
 template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE>
-__global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
+__global__ void __launch_bounds__(kThreadsMax) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE))))
+rpe_fwd_kernel(Params p) {
   constexpr bool BF = std::is_same<DT, __bf16>::value;
   constexpr bool CTX = MODE == RPE_MODE_CONTEXTUAL;
   constexpr bool TK = CTX && (TERMS & RPE_TERM_K);
@@ -157,6 +172,10 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
   // term the row area is zero and the gather only supplies the -inf of padding
   // keys, unless the query-term gather already does that.
   constexpr bool GATHER = !CTX || TK || !TQ;
+  // gather entries: fp16 per-row scores for bf16 inputs without a value term
+  constexpr bool G16 = BF && CTX && !TV;
+  using GT = typename std::conditional<G16, _Float16, float>::type;
+  constexpr int GSZ = sizeof(GT);
   constexpr int EB = sizeof(DT);
   constexpr int EPC = Traits<DT>::kEpc;
   constexpr int RB = D * EB;                       // bytes per token row
@@ -169,9 +188,7 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
   constexpr int NPH = WIDE ? 2 : 1;                // address phases (a 64-slot grid row spans 2 blocks)
   static_assert(RPI * CPR == 64 && IPB >= 1, "row size");
 
-  extern __shared__ float smem[];
-  int* smem_i = reinterpret_cast<int*>(smem);
-  char* smem_b = reinterpret_cast<char*>(smem);
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int nth = blockDim.x;
   const int NW = nth >> 6;
@@ -196,41 +213,55 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
 
   const int64_t base = bh * static_cast<int64_t>(p.N) * D;
   const DT* __restrict__ qg = reinterpret_cast<const DT*>(p.q) + base;
-  const DT* __restrict__ kg = reinterpret_cast<const DT*>(p.k) + base;
-  const DT* __restrict__ vg = reinterpret_cast<const DT*>(p.v) + base;
+  const char* __restrict__ kgb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.k) + base);
+  const char* __restrict__ vgb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.v) + base);
   DT* __restrict__ og = reinterpret_cast<DT*>(p.o) + base;
-  const DT* rk = reinterpret_cast<const DT*>(p.rk) + head * p.tab_head_stride;
-  const DT* rv = reinterpret_cast<const DT*>(p.rv) + head * p.tab_head_stride;
+  const char* rkb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.rk) + head * p.tab_head_stride);
+  const char* rvb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.rv) + head * p.tab_head_stride);
+
+  int* const ry_tab = reinterpret_cast<int*>(smem + p.off_ry);
+  int* const cx_tab = reinterpret_cast<int*>(smem + p.off_cx);
+  GT* const gtab = reinterpret_cast<GT*>(smem + p.off_tab);
+  GT* const gzero = reinterpret_cast<GT*>(smem + p.off_zero);
+  GT* const gneg = reinterpret_cast<GT*>(smem + p.off_neg);
+  float* const wsum = reinterpret_cast<float*>(smem + p.off_w);
+  float* const tqs = reinterpret_cast<float*>(smem + p.off_tq);
 
   // ---- prologue: per-axis tables, guards, bias table, weight sums, staged rQ.
-  for (int i = tid; i < 2 * p.R - 1; i += nth)
-    smem_i[p.off_ry + i] =
-        MODE == RPE_MODE_NONE ? 0
-                              : (axis_index(i - (p.R - 1), p.map, p.rounding, p.alpha, p.beta, p.gamma) + p.half) * p.S;
-  for (int i = tid; i < 2 * p.C - 1; i += nth)
-    smem_i[p.off_cx + i] =
-        MODE == RPE_MODE_NONE ? 0 : axis_index(i - (p.C - 1), p.map, p.rounding, p.alpha, p.beta, p.gamma) + p.half;
+  // ry holds byte offsets of the row part, (g(dy)+H)*S*GSZ; cx holds g(dx)+H.
+  {
+    const int nry = 2 * p.R - 1, ncx = 2 * p.C - 1;
+    for (int i = tid; i < nry + ncx; i += nth) {
+      const bool is_row = i < nry;
+      const int x = is_row ? i - (p.R - 1) : i - nry - (p.C - 1);
+      const int g = MODE == RPE_MODE_NONE ? 0 : axis_index(x, p.map, p.rounding, p.alpha, p.beta, p.gamma) + p.half;
+      if (is_row)
+        ry_tab[i] = g * p.S * GSZ;
+      else
+        cx_tab[i - nry] = g;
+    }
+  }
   for (int i = tid; i < p.zr; i += nth) {
-    smem[p.off_zero + i] = 0.0f;
-    smem[p.off_neg + i] = -INFINITY;
+    gzero[i] = static_cast<GT>(0.0f);
+    gneg[i] = static_cast<GT>(-INFINITY);
     if constexpr (TQ) {
-      smem[p.off_tqz + i] = 0.0f;
-      smem[p.off_tqn + i] = -INFINITY;
+      reinterpret_cast<float*>(smem + p.off_tqz)[i] = 0.0f;
+      reinterpret_cast<float*>(smem + p.off_tqn)[i] = -INFINITY;
     }
   }
   if constexpr (MODE == RPE_MODE_BIAS) {
     const float* bt = p.bias + head * p.tab_head_stride;
-    for (int i = tid; i < p.nb; i += nth) smem[p.off_tab + i] = bt[i] * p.bias_mul;
+    for (int i = tid; i < p.nb; i += nth) gtab[i] = bt[i] * p.bias_mul;
   }
   if constexpr (MODE == RPE_MODE_NONE) {
-    for (int i = tid; i < p.nb; i += nth) smem[p.off_tab + i] = 0.0f;
+    for (int i = tid; i < p.nb; i += nth) gtab[i] = 0.0f;
   }
   if constexpr (TV) {
-    const int wsz = p.off_neg + p.zr - p.off_tab;
-    for (int i = tid; i < wsz; i += nth) smem[p.off_w + i] = 0.0f;
+    const int wsz = (p.off_neg + p.zr * GSZ - p.off_tab) / 4;
+    for (int i = tid; i < wsz; i += nth) wsum[i] = 0.0f;
   }
   if constexpr (CTX && GATHER && !TK) {
-    for (int i = tid; i < NW * kRowTile * p.p_tab; i += nth) smem[p.off_tab + i] = 0.0f;
+    for (int i = tid; i < NW * kRowTile * p.p_tab; i += nth) gtab[i] = static_cast<GT>(0.0f);
   }
   if constexpr (TQ) {
     // rQ staged as [nbt*32][kpitch] (rows past nb zero)
@@ -240,11 +271,11 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
       const int row = it / CH, ch = it - (it / CH) * CH;
       const uint4 u = row < p.nb ? ld16(rq + static_cast<int64_t>(row) * D + ch * EPC) : make_uint4(0, 0, 0, 0);
       if constexpr (BF) {
-        *reinterpret_cast<uint4*>(smem_b + p.off_rq * 4 + (row * p.kpitch + ch * EPC) * 2) = u;
+        *reinterpret_cast<uint4*>(smem + p.off_rq + (row * p.kpitch + ch * EPC) * 2) = u;
       } else {
         const float* e = reinterpret_cast<const float*>(&u);
 #pragma unroll
-        for (int q = 0; q < EPC; ++q) smem[p.off_rq + row * p.kpitch + ch * EPC + q] = e[q];
+        for (int q = 0; q < EPC; ++q) reinterpret_cast<float*>(smem + p.off_rq)[row * p.kpitch + ch * EPC + q] = e[q];
       }
     }
   }
@@ -273,13 +304,19 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
     for (int kk = 0; kk < KS; ++kk) qf[kk] = qvalid ? qg[static_cast<int64_t>(qn) * D + 2 * kk + h] : 0.0f;
   }
 
-  // ---- the block stream.
-  const int n_kt = TK ? p.nbt : 0;                 // rK blocks first
-  const int n_vt = TV ? p.nbt : 0;                 // rV blocks last
-  const int L = n_kt + p.n_blocks + n_vt;
-  auto kind_of = [&](int e) -> int {
-    return e < n_kt ? kElemKeyTable : (e < n_kt + p.n_blocks ? kElemKeys : kElemValueTable);
-  };
+  // ---- the block stream: [rK tiles][key/value blocks][rV tiles]
+  const int n_kt = TK ? p.nbt : 0;
+  const int n_vt = TV ? p.nbt : 0;
+  const int nblk = p.n_blocks;
+  const int L = n_kt + nblk + n_vt;
+  const int ST = p.stages;
+  // direct-to-LDS instructions this wave issues per 32-row tile; every stream
+  // element costs two per instruction (table tiles are copied into both halves
+  // of their stage), so the loads issued after an element are a simple count
+  const int my_ipb = wid < IPB ? (IPB - wid + NW - 1) / NW : 0;
+  const int lpe = 2 * my_ipb;
+  char* const ring = smem + p.off_stage;
+  const uint32_t lds_ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)smem)) + p.off_stage;
   // N index of a key slot; padding slots read a valid token (their values are masked)
   auto slot_n = [&](int blk, int s) -> int {
     if (p.prefix_block) {
@@ -288,52 +325,47 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
     }
     const int sigma = blk * kBlockSlots + s;
     const int y = sigma >> p.lwp, x = sigma & (p.Wp - 1);
-    if (y < p.R && x < p.C) return wbase + y * rowstride + x;
-    if (p.prefix_in_tail && y == p.R - 1 && x >= p.C && x - p.C < p.P) return x - p.C;
-    return wbase;
+    int n = (y < p.R && x < p.C) ? wbase + y * rowstride + x : wbase;
+    if (p.prefix_in_tail) n = (y == p.R - 1 && x >= p.C && x - p.C < p.P) ? x - p.C : n;
+    return n;
   };
-  // direct-to-LDS instructions this wave issues per 32-row tile
-  const int my_ipb = wid < IPB ? (IPB - wid + NW - 1) / NW : 0;
-  auto elem_loads = [&](int e) -> int { return kind_of(e) == kElemKeys ? 2 * my_ipb : my_ipb; };
-  auto stage_k = [&](int e) -> char* { return smem_b + p.off_stage * 4 + (e % kStages) * 2 * TILE; };
-  auto stage_v = [&](int e) -> char* { return stage_k(e) + TILE; };
-  // copy 32 rows of a [rows][D] tensor into a swizzled row-major tile: instruction i
-  // covers rows [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR
-  // with global chunk (l % CPR) ^ (row % CPR).
-  auto dma_tile = [&](char* tile, const DT* src, auto&& row_index) {
+  // Copy 32 rows into a swizzled row-major tile: instruction i covers rows
+  // [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR with
+  // global chunk (l % CPR) ^ (row % CPR).
+  auto issue = [&](int f, int stage) {
+    const uint32_t kt = lds_ring + stage * (2 * TILE);
+    const uint32_t vt = kt + TILE;
     for (int i = wid; i < IPB; i += NW) {
       const int row = i * RPI + lane / CPR;
-      const int pos = lane % CPR;
-      const int c = pos ^ (row & (CPR - 1));
-      const DT* g = src + static_cast<int64_t>(row_index(row)) * D + c * EPC;
-      dma16(g, tile + i * 1024);
-    }
-  };
-  auto issue = [&](int e) {
-    const int kind = kind_of(e);
-    if (kind == kElemKeyTable) {
-      const int t = e;
-      dma_tile(stage_k(e), rk, [&](int r) { const int b = kRowTile * t + r; return b < p.nb ? b : 0; });
-    } else if (kind == kElemKeys) {
-      const int blk = e - n_kt;
-      dma_tile(stage_k(e), kg, [&](int r) { return slot_n(blk, r); });
-      dma_tile(stage_v(e), vg, [&](int r) { return slot_n(blk, r); });
-    } else {
-      const int t = e - n_kt - p.n_blocks;
-      dma_tile(stage_v(e), rv, [&](int r) { const int b = kRowTile * t + r; return b < p.nb ? b : 0; });
+      const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
+      if (f < n_kt) {
+        const int b = kRowTile * f + row;
+        const uint32_t off = static_cast<uint32_t>(b < p.nb ? b : 0) * RB + cb;
+        dma16(rkb + off, kt + i * 1024);
+        dma16(rkb + off, vt + i * 1024);
+      } else if (f < n_kt + nblk) {
+        const uint32_t off = static_cast<uint32_t>(slot_n(f - n_kt, row)) * RB + cb;
+        dma16(kgb + off, kt + i * 1024);
+        dma16(vgb + off, vt + i * 1024);
+      } else {
+        const int b = kRowTile * (f - n_kt - nblk) + row;
+        const uint32_t off = static_cast<uint32_t>(b < p.nb ? b : 0) * RB + cb;
+        dma16(rvb + off, kt + i * 1024);
+        dma16(rvb + off, vt + i * 1024);
+      }
     }
   };
 
-  // K operand (A of S^T): lane holds K[slot r32][d 16kk + 8h .. +7] (bf16) / [2kk + h] (fp32).
-  auto s_tile = [&](const char* tile) -> f32x16 {
-    f32x16 acc = {};
+  // S^T tile (plus init) from a swizzled row-major K tile.  K operand (A): lane
+  // holds K[slot r32][d 16kk + 8h .. +7] (bf16) / [2kk + h] (fp32).
+  auto s_tile = [&](const char* tile, const f32x16& init) -> f32x16 {
+    f32x16 acc = init;
     const int sw = r32 & (CPR - 1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       if constexpr (BF) {
         const int c = 2 * kk + h;
-        uint4 kv = make_uint4(0, 0, 0, 0);
-        if (c < CPR) kv = *reinterpret_cast<const uint4*>(tile + r32 * RB + ((c ^ sw) << 4));
+        const uint4 kv = *reinterpret_cast<const uint4*>(tile + r32 * RB + ((c ^ sw) << 4));
         acc = mfma32(as_bf16x8(kv), qb[kk], acc);
       } else {
         const int col = (2 * kk + h) * 4;  // byte column
@@ -405,16 +437,15 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
     }
   };
 
-  // ---- column parts of the LDS addresses: cx[ph][j][i] for this lane's key 8j + 4h + i
-  // of a block at phase ph (ph = block index & 1 when a grid row spans two blocks).
-  const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab : p.off_tab;
-  const int w_off = TV ? p.off_w - p.off_tab : 0;
+  // ---- column parts of the LDS byte addresses: cxb[ph][j][i] for this lane's key
+  // 8j + 4h + i of a block at phase ph (ph = block index & 1 when a grid row spans
+  // two blocks); cqb the same for the query-term scores (fp32).
+  const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab * GSZ : p.off_tab;
+  const int w_delta = TV ? p.off_w - p.off_tab : 0;   // byte distance gather target -> weight sums
   __syncthreads();  // prologue tables visible; no direct-to-LDS load is in flight yet
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // Q and table loads done before the ring starts
-  // byte addresses: cxb = gather-target column part, cqb = query-term column part;
-  // the row part ry (a word offset in the per-axis table) is added as bytes below
   int cxb[NPH][4][4];
-  int cqb[NPH][4][4];
+  int cqb[TQ ? NPH : 1][4][4];
 #pragma unroll
   for (int ph = 0; ph < NPH; ++ph)
 #pragma unroll
@@ -429,45 +460,58 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
             a = p.off_zero;
             aq = p.off_tqz;
           } else {
-            const int cpart = smem_i[p.off_cx + xi - xj + p.C - 1];
-            a = rowbase + cpart;
-            aq = p.off_tq + s * p.p_tq + cpart;
+            const int cpart = cx_tab[xi - xj + p.C - 1];
+            a = rowbase + cpart * GSZ;
+            aq = p.off_tq + (s * p.p_tq + cpart) * 4;
           }
         }
-        cxb[ph][j][i] = 4 * a;
-        cqb[ph][j][i] = 4 * aq;
+        cxb[ph][j][i] = a;
+        if constexpr (TQ) cqb[ph][j][i] = aq;
       }
   (void)cqb;
-  const int* __restrict__ ryt = smem_i + p.off_ry + (qpos ? yi : 0) + p.R - 1;  // ry table at yq - y + R - 1
-  const int w_offb = 4 * w_off;
+  // row part: ry(yq - y) at ry_tab[yq - y + R - 1]
+  const int* __restrict__ ryt = ry_tab + (qpos ? yi : 0) + p.R - 1;
+  // grid rows covered per block (Wp <= 32) and this lane's row within a block for each j
+  const int rpb = WIDE ? 0 : kBlockSlots >> p.lwp;
+  int rj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rj[j] = WIDE ? 0 : (8 * j + 4 * h) >> p.lwp;
 
   // ---- running state of this lane's row (shared with the lane l ^ 32).
-  float m_run = kNegBig;
+  float m_run = 0.0f;
   float l_part = 0.0f;
+  const float inv_c = 1.0f / p.c;
+  f32x16 mneg = f32x16{};   // -m_run / c, the S^T accumulator's starting value
 
-  // Logit of pair (row, key) in log2 units given the LDS byte addresses of its terms.
+  // Logit (log2 units, relative to m_run) of a pair from the LDS byte addresses of its terms.
   auto logit = [&](float sv, int ab, int aqb) -> float {
     float add = 0.0f;
-    if constexpr (GATHER) add = *reinterpret_cast<const float*>(smem_b + ab);
-    if constexpr (TQ) add += *reinterpret_cast<const float*>(smem_b + aqb);
+    if constexpr (GATHER) add = static_cast<float>(*reinterpret_cast<const GT*>(smem + ab));
+    if constexpr (TQ) add += *reinterpret_cast<const float*>(smem + aqb);
     return fmaf(sv, p.c, add);
   };
+  // byte offset of the query-term row part from the gather row part
+  auto tq_row = [&](int ryb) -> int { return GSZ == 4 ? ryb : ryb * (4 / GSZ); };
 
-  auto process_block = [&](auto ph_tag, const f32x16& s, const char* vtile, int gblk, bool prefix_blk) {
-    constexpr int PH = decltype(ph_tag)::value;
+  // One key block: logits, lazy online softmax, PV (and the value-term scatter).
+  // INTERIOR: every slot is a grid key of rows < R-1 or a padding column.
+  // FIRST: the first block of the stream sets the running maximum.
+  auto process_block = [&](auto interior_c, auto first_c, auto ph_c, const char* ktile, const char* vtile,
+                           int gblk, bool prefix_blk) {
+    constexpr bool INTERIOR = decltype(interior_c)::value;
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr int PH = decltype(ph_c)::value;
+    const f32x16 s = s_tile(ktile, FIRST ? f32x16{} : mneg);
     float x[4][4];
     int ab[4][4];          // gather addresses, kept for the value-term scatter
-    const bool tail = !prefix_blk && (((gblk * kBlockSlots + kBlockSlots - 1) >> p.lwp) >= p.R - 1);
-    if (__builtin_expect(!prefix_blk && !tail, 1)) {
-      // interior block: every key is a grid key of rows < R-1 or a padding column
+    if constexpr (INTERIOR) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int yj = (gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
-        const int ryb = 4 * ryt[-yj];
+        const int ryb = WIDE ? ryt[-(gblk >> 1)] : ryt[-(gblk * rpb + rj[j])];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ab[j][i] = ryb + cxb[PH][j][i];
-          x[j][i] = logit(s[4 * j + i], ab[j][i], ryb + cqb[PH][j][i]);
+          x[j][i] = logit(s[4 * j + i], ab[j][i], TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0);
         }
       }
     } else {
@@ -476,23 +520,24 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int yj = (gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
-        const int yk = yj < p.R ? yj : p.R - 1;
-        const int ryb = 4 * ryt[-yk];
+        const int yk = yj < 0 ? 0 : (yj < p.R ? yj : p.R - 1);
+        const int ryb = ryt[-yk];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int slot = 8 * j + 4 * h + i;
           const int xj = (gblk * kBlockSlots + slot) & (p.Wp - 1);
-          int a = ryb + cxb[PH][j][i], aq = ryb + cqb[PH][j][i];
+          int a = ryb + cxb[PH][j][i];
+          int aq = TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0;
           if (prefix_blk) {
             const bool pre = slot < p.P;
-            a = 4 * (pre ? p.off_zero : p.off_neg);
-            aq = 4 * (pre ? p.off_tqz : p.off_tqn);
+            a = pre ? p.off_zero : p.off_neg;
+            aq = pre ? p.off_tqz : p.off_tqn;
           } else if (yj >= p.R) {
-            a = 4 * p.off_neg;
-            aq = 4 * p.off_tqn;
+            a = p.off_neg;
+            aq = p.off_tqn;
           } else if (p.prefix_in_tail && yj == p.R - 1 && xj >= p.C && xj - p.C < p.P) {
-            a = 4 * p.off_zero;
-            aq = 4 * p.off_tqz;
+            a = p.off_zero;
+            aq = p.off_tqz;
           }
           ab[j][i] = a;
           x[j][i] = logit(s[4 * j + i], a, aq);
@@ -503,136 +548,195 @@ __global__ void __launch_bounds__(kThreadsMax) rpe_fwd_kernel(Params p) {
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
     bmax = fmaxf(bmax, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
                              fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const bool need = bmax > m_run + kLazyTau;
-    if (__builtin_expect(__any(need), 0)) {
-      const float m_new = need ? bmax : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_part *= alpha;
+    bmax = row_max2(bmax);
+    if constexpr (FIRST) {
+      // every block holds at least one real key, so bmax is finite
+      m_run = bmax;
+      mneg = splat16(-m_run * inv_c);
 #pragma unroll
-      for (int c = 0; c < DTL; ++c) oacc[c] *= alpha;
-      if constexpr (TV) {
-        if (need) {
-          for (int b = h; b < p.nb; b += 2) smem[rowbase + w_off + b] *= alpha;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[j][i] -= bmax;
+    } else {
+      const bool need = bmax > kLazyTau;
+      if (__builtin_expect(__any(need), 0)) {
+        const float dm = need ? bmax : 0.0f;
+        const float alpha = __builtin_amdgcn_exp2f(-dm);
+        l_part *= alpha;
+#pragma unroll
+        for (int c = 0; c < DTL; ++c) oacc[c] *= alpha;
+        if constexpr (TV) {
+          if (need) {
+            float* wrow = reinterpret_cast<float*>(smem + rowbase + w_delta);
+            for (int b = h; b < p.nb; b += 2) wrow[b] *= alpha;
+          }
         }
+        m_run += dm;
+        mneg = splat16(-m_run * inv_c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[j][i] -= dm;
       }
-      m_run = m_new;
     }
     float pr[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pr[j][i] = __builtin_amdgcn_exp2f(x[j][i] - m_run);
+        pr[j][i] = __builtin_amdgcn_exp2f(x[j][i]);
         l_part += pr[j][i];
       }
     if constexpr (TV) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(reinterpret_cast<float*>(smem_b + ab[j][i] + w_offb), pr[j][i]);
+        for (int i = 0; i < 4; ++i) atomicAdd(reinterpret_cast<float*>(smem + ab[j][i] + w_delta), pr[j][i]);
     }
     pv_tile(vtile, pr, false);
+  };
+  // phase dispatch (a 64-slot grid row spans two blocks)
+  auto process = [&](auto interior_c, auto first_c, const char* kt, const char* vt, int gblk, bool pre) {
+    if constexpr (WIDE) {
+      if (gblk & 1)
+        process_block(interior_c, first_c, std::integral_constant<int, 1>{}, kt, vt, gblk, pre);
+      else
+        process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre);
+    } else {
+      process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre);
+    }
   };
 
   // Query-term scores of a key block: TQ[slot][b] = c * k_slot . rQ[b]; tiles over waves.
   auto block_query_scores = [&](const char* ktile) {
     if constexpr (TQ) {
       const int sw = r32 & (CPR - 1);
+      const char* rqs = smem + p.off_rq;
       for (int t = wid; t < p.nbt; t += NW) {
         f32x16 acc = {};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
           if constexpr (BF) {
             const int c = 2 * kk + h, d0 = 16 * kk + 8 * h;
-            uint4 a = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
-            if (c < CPR) {
-              a = *reinterpret_cast<const uint4*>(smem_b + p.off_rq * 4 + ((kRowTile * t + r32) * p.kpitch + d0) * 2);
-              kv = *reinterpret_cast<const uint4*>(ktile + r32 * RB + ((c ^ sw) << 4));
-            }
+            const uint4 a = *reinterpret_cast<const uint4*>(rqs + ((kRowTile * t + r32) * p.kpitch + d0) * 2);
+            const uint4 kv = *reinterpret_cast<const uint4*>(ktile + r32 * RB + ((c ^ sw) << 4));
             acc = mfma32(as_bf16x8(a), as_bf16x8(kv), acc);
           } else {
             const int col = (2 * kk + h) * 4;
             const float kv = *reinterpret_cast<const float*>(ktile + r32 * RB + (((col >> 4) ^ sw) << 4) + (col & 15));
-            acc = mfma32(smem[p.off_rq + (kRowTile * t + r32) * p.kpitch + 2 * kk + h], kv, acc);
+            acc = mfma32(reinterpret_cast<const float*>(rqs)[(kRowTile * t + r32) * p.kpitch + 2 * kk + h], kv, acc);
           }
         }
-        // lane holds TQ[slot r32][32t + 8j + 4h + i]
+        // lane holds TQ[slot r32][32t + 8j + 4h + i]; rows hold nbt*32 entries
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            tqs[r32 * p.p_tq + kRowTile * t + 8 * j + 4 * h + i] = acc[4 * j + i] * p.c;
+      }
+    }
+  };
+
+  // ---- walk the stream: element e is computed while the next stages-2 elements
+  // are in flight; element e+stages-1 is issued into the stage element e-1 used.
+  int st_cur = 0, st_iss = 0;
+  for (int f = 0; f < ST - 1 && f < L; ++f) {
+    issue(f, st_iss);
+    st_iss = st_iss + 1 == ST ? 0 : st_iss + 1;
+  }
+  // wait for element e, then refill the ring; returns e's stage
+  auto step = [&](int e) -> int {
+    // this wave's loads issued after element e's: those of elements e+1 .. e+ST-2
+    const int ahead = (L - 1 - e) < (ST - 2) ? (L - 1 - e) : (ST - 2);
+    wait_vmcnt_floor(ahead * lpe);
+    lds_barrier();
+    if (e + ST - 1 < L) {
+      issue(e + ST - 1, st_iss);
+      st_iss = st_iss + 1 == ST ? 0 : st_iss + 1;
+    }
+    const int s = st_cur;
+    st_cur = st_cur + 1 == ST ? 0 : st_cur + 1;
+    return s;
+  };
+  auto ktile_of = [&](int s) -> const char* { return ring + s * (2 * TILE); };
+  auto vtile_of = [&](int s) -> const char* { return ring + s * (2 * TILE) + TILE; };
+
+  int e = 0;
+  // rK tiles: TK[row][32t + ...] = c * q_row . rK[...] into this wave's row area
+  if constexpr (TK) {
+    for (; e < n_kt; ++e) {
+      const int s = step(e);
+      if (active) {
+        const f32x16 acc = s_tile(ktile_of(s), f32x16{});
+        GT* row = reinterpret_cast<GT*>(smem + rowbase);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            row[kRowTile * e + 8 * j + 4 * h + i] =
+                static_cast<GT>(fminf(fmaxf(acc[4 * j + i] * p.c, -kGatherMax), kGatherMax));
+      }
+    }
+  }
+  // key/value blocks: the first one sets the running maximum
+  {
+    int gb = 0;
+    {
+      const int s = step(e);
+      if constexpr (TQ) {
+        block_query_scores(ktile_of(s));
+        lds_barrier();
+      }
+      if (active) {
+        if (p.prefix_block)
+          process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), -1, true);
+        else if (p.first_tail > 0)
+          process(bool_c<true>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false);
+        else
+          process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false);
+      }
+      if (!p.prefix_block) gb = 1;
+      ++e;
+    }
+    for (; gb < p.first_tail; ++gb, ++e) {
+      const int s = step(e);
+      if constexpr (TQ) {
+        block_query_scores(ktile_of(s));
+        lds_barrier();
+      }
+      if (active) process(bool_c<true>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false);
+    }
+    for (; gb < p.grid_blocks; ++gb, ++e) {
+      const int s = step(e);
+      if constexpr (TQ) {
+        block_query_scores(ktile_of(s));
+        lds_barrier();
+      }
+      if (active) process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false);
+    }
+  }
+  // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
+  if constexpr (TV) {
+    for (; e < L; ++e) {
+      const int s = step(e);
+      if (active) {
+        const int t = e - n_kt - nblk;
+        const float* wrow = reinterpret_cast<const float*>(smem + rowbase + w_delta);
+        float wv[4][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int b = kRowTile * t + 8 * j + 4 * h + i;
-            if (b < p.nb) smem[p.off_tq + r32 * p.p_tq + b] = acc[4 * j + i] * p.c;
+            wv[j][i] = b < p.nb ? wrow[b] : 0.0f;
           }
-      }
-    }
-  };
-
-  // ---- walk the stream: element e is computed while elements e+1 .. e+kStages-2
-  // are in flight; element e+kStages-1 is issued into the stage element e-1 used.
-  for (int e = 0; e < kStages - 1 && e < L; ++e) issue(e);
-  for (int e = 0; e < L; ++e) {
-    int after = 0;  // this wave's loads issued after element e's
-    for (int f = e + 1; f < L && f < e + kStages - 1; ++f) after += elem_loads(f);
-    wait_vmcnt(after);
-    lds_barrier();
-    if (e + kStages - 1 < L) issue(e + kStages - 1);
-    const int kind = kind_of(e);
-    if (kind == kElemKeyTable) {
-      if constexpr (TK) {
-        if (active) {
-          const int t = e;
-          const f32x16 acc = s_tile(stage_k(e));
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int b = kRowTile * t + 8 * j + 4 * h + i;
-              if (b < p.nb) smem[rowbase + b] = acc[4 * j + i] * p.c;
-            }
-        }
-      }
-    } else if (kind == kElemKeys) {
-      const int blk = e - n_kt;
-      if constexpr (TQ) {
-        block_query_scores(stage_k(e));
-        lds_barrier();
-      }
-      if (active) {
-        const bool pre = p.prefix_block && blk == 0;
-        const int gblk = blk - p.prefix_block;
-        const f32x16 s = s_tile(stage_k(e));
-        if constexpr (WIDE) {
-          if (gblk & 1)
-            process_block(std::integral_constant<int, 1>{}, s, stage_v(e), gblk, pre);
-          else
-            process_block(std::integral_constant<int, 0>{}, s, stage_v(e), gblk, pre);
-        } else {
-          process_block(std::integral_constant<int, 0>{}, s, stage_v(e), gblk, pre);
-        }
-      }
-    } else {
-      // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
-      if constexpr (TV) {
-        if (active) {
-          const int t = e - n_kt - p.n_blocks;
-          float wv[4][4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int b = kRowTile * t + 8 * j + 4 * h + i;
-              wv[j][i] = b < p.nb ? smem[rowbase + w_off + b] : 0.0f;
-            }
-          pv_tile(stage_v(e), wv, true);
-        }
+        pv_tile(vtile_of(s), wv, true);
       }
     }
   }
 
   if (!qvalid) return;
-  float l = l_part + __shfl_xor(l_part, 32);
+  const float l = l_part + __shfl_xor(l_part, 32);
   const float inv = 1.0f / l;
   DT* orow = og + static_cast<int64_t>(qn) * D;
 #pragma unroll
@@ -667,7 +771,7 @@ hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(p.n_wg)), dim3(p.NW * 64),
-                     static_cast<size_t>(p.lds_words) * 4, stream, p);
+                     static_cast<size_t>(p.lds_bytes), stream, p);
   return hipGetLastError();
 }
 

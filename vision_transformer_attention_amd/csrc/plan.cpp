@@ -27,43 +27,56 @@ int log2_exact(int v) {
 }
 
 
-// LDS layout (4-byte words) for the wave count already in p->NW.
+int align(int v, int a) { return (v + a - 1) / a * a; }
+
+// Smallest pitch >= n whose byte size is an odd number of 4-byte words (rows of
+// a row-parallel gather then fall in different LDS banks).
+int odd_word_pitch(int n, int esz) {
+  int p = n;
+  while (((p * esz) % 4) != 0 || ((p * esz / 4) % 2) == 0) ++p;
+  return p;
+}
+
+// LDS layout (bytes) for the wave count and ring depth already in p.
 int lds_layout(const rpe_attn_desc* d, Params* p) {
-  // LDS layout (words)
   const int eb = p->elem_bytes;
   const bool ctx = d->mode == RPE_MODE_CONTEXTUAL;
   const bool tq = ctx && (d->terms & RPE_TERM_Q);
+  const bool tv = ctx && (d->terms & RPE_TERM_V);
+  const bool row_area = ctx && (d->terms & (RPE_TERM_K | RPE_TERM_V));
+  p->gsz = (d->dtype == RPE_BF16 && ctx && !tv) ? 2 : 4;
   p->kpitch = d->dtype == RPE_BF16 ? p->D + 8 : p->D + 1;
   int off = 0;
   p->off_stage = off;
-  off += kStages * 2 * kBlockSlots * p->D * eb / 4;
+  off += p->stages * 2 * kBlockSlots * p->D * eb;
   p->off_rq = off;
-  if (tq) off += ((p->nbt * kRowTile * p->kpitch * eb + 3) / 4 + 3) / 4 * 4;
+  if (tq) off += align(p->nbt * kRowTile * p->kpitch * eb, 16);
   p->zr = (p->S - 1) * p->S + 1;  // 1 when there is no table
-  const bool row_area = ctx && (d->terms & (RPE_TERM_K | RPE_TERM_V));
-  p->p_tab = p->nb | 1;
+  // per-row scores are stored a whole 32-bucket tile at a time, so rows hold nbt*32 entries
+  p->p_tab = odd_word_pitch(p->nbt * kRowTile, p->gsz);
   p->off_tab = off;
   if (d->mode == RPE_MODE_BIAS || d->mode == RPE_MODE_NONE) {
-    off += p->nb;
+    off += p->nb * p->gsz;
   } else if (row_area) {
-    off += p->NW * kRowTile * p->p_tab;
+    off += p->NW * kRowTile * p->p_tab * p->gsz;
   }
-  p->off_zero = off; off += p->zr;
-  p->off_neg = off; off += p->zr;
-  if (ctx && (d->terms & RPE_TERM_V)) {
-    p->off_w = off;
-    off += p->off_neg + p->zr - p->off_tab;
+  p->off_zero = off; off += p->zr * p->gsz;
+  p->off_neg = off; off += p->zr * p->gsz;
+  off = align(off, 16);
+  if (tv) {
+    p->off_w = off;  // gsz is 4 here, so the mirror has the same byte layout
+    off += align(p->off_neg + p->zr * p->gsz - p->off_tab, 16);
   }
   if (tq) {
-    p->p_tq = p->nb | 1;
-    p->off_tq = off; off += kBlockSlots * p->p_tq;
-    p->off_tqz = off; off += p->zr;
-    p->off_tqn = off; off += p->zr;
+    p->p_tq = odd_word_pitch(p->nbt * kRowTile, 4);
+    p->off_tq = off; off += kBlockSlots * p->p_tq * 4;
+    p->off_tqz = off; off += p->zr * 4;
+    p->off_tqn = off; off += p->zr * 4;
   }
-  p->off_ry = off; off += 2 * p->R - 1;
-  p->off_cx = off; off += 2 * p->C - 1;
-  p->lds_words = (off + 3) / 4 * 4;
-  return p->lds_words * 4 > kMaxLdsBytes ? RPE_E_BUCKETS : RPE_OK;
+  p->off_ry = off; off += (2 * p->R - 1) * 4;
+  p->off_cx = off; off += (2 * p->C - 1) * 4;
+  p->lds_bytes = align(off, 16);
+  return p->lds_bytes > kMaxLdsBytes ? RPE_E_BUCKETS : RPE_OK;
 }
 
 }  // namespace
@@ -170,17 +183,35 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
 
   p->n_rt = (p->T + kRowTile - 1) / kRowTile;
   p->n_units = (int64_t)p->B * p->H * p->U;
-  // work split: one 32-row query tile per wave, the unit's tiles spread evenly
-  // over its workgroups; the widest workgroup (<= kMaxWaves waves, >= 2) whose
-  // LDS plan fits is taken.
+  p->first_tail = ((p->R - 1) << p->lwp) / kBlockSlots;
+  // Work split: one 32-row query tile per wave, the unit's tiles spread evenly
+  // over its workgroups.  Among workgroup widths (2..kMaxWaves waves) and ring
+  // depths whose LDS plan fits, take the one with the most resident waves per
+  // CU (4 SIMDs x waves_per_simd waves, and as many workgroups as LDS allows),
+  // then the deeper ring, then the wider workgroup.
+  Params best;
+  int best_waves = -1;
   for (int max_w = kMaxWaves; max_w >= 2; --max_w) {
-    p->n_qc = (p->n_rt + max_w - 1) / max_w;
-    p->NW = (p->n_rt + p->n_qc - 1) / p->n_qc;
-    if (p->NW < 2) p->NW = 2;  // at least two waves share each stream
-    p->n_wg = p->n_units * p->n_qc;
-    if (lds_layout(d, p) == RPE_OK) return RPE_OK;
+    for (int stages = kMaxStages; stages >= kMinStages; --stages) {
+      Params t = *p;
+      t.n_qc = (t.n_rt + max_w - 1) / max_w;
+      t.NW = (t.n_rt + t.n_qc - 1) / t.n_qc;
+      if (t.NW < 2) t.NW = 2;  // at least two waves share each stream
+      t.n_wg = t.n_units * t.n_qc;
+      t.stages = stages;
+      if (lds_layout(d, &t) != RPE_OK) continue;
+      const int by_regs = 4 * waves_per_simd(d->mode, d->terms, t.Wp == 64) / t.NW;
+      const int by_lds = kMaxLdsBytes / t.lds_bytes;
+      const int waves = (by_regs < by_lds ? by_regs : by_lds) * t.NW;
+      if (waves > best_waves) {
+        best_waves = waves;
+        best = t;
+      }
+    }
   }
-  return RPE_E_BUCKETS;
+  if (best_waves < 0) return RPE_E_BUCKETS;
+  *p = best;
+  return RPE_OK;
 }
 
 }  // namespace rpe

@@ -19,8 +19,16 @@ constexpr int kBlockSlots = 32;
 constexpr int kRowTile = 32;        // query rows per wave (one 32x32 MFMA tile)
 constexpr int kMaxWp = 64;          // widest padded grid row the kernel is built for
 constexpr int kMaxWaves = 4;
+constexpr int kMaxStages = 4;       // deepest LDS ring of the block stream
+constexpr int kMinStages = 2;
 constexpr int kMaxLdsBytes = 160 * 1024;
-constexpr int kStages = 4;          // LDS ring depth of the block stream
+// Resident waves per SIMD each forward instance is compiled for (register
+// budget 512 / waves): instances with only the key term or a bias fit three;
+// wide rows (two column phases of gather offsets) and the query / value terms
+// need the larger budget of two.  The planner sizes LDS to match.
+constexpr int waves_per_simd(int mode, uint32_t terms, bool wide) {
+  return (wide || (mode == RPE_MODE_CONTEXTUAL && (terms & (RPE_TERM_Q | RPE_TERM_V)))) ? 2 : 3;
+}
 
 struct Params {
   // tensors
@@ -48,25 +56,30 @@ struct Params {
   int prefix_block;       // 1: a separate leading block holds the prefix keys
   int grid_blocks;        // blocks of 32 slots covering R * Wp grid slots
   int n_blocks;           // prefix_block + grid_blocks
+  int first_tail;         // first grid block that holds a slot of grid row R-1 (or beyond)
   // work split
   int n_rt;               // 32-row query tiles per unit
   int NW;                 // waves per workgroup (one row tile each)
   int n_qc;               // workgroups (query chunks) per unit
   int64_t n_units;        // B * H * U
   int64_t n_wg;           // n_units * n_qc
-  // LDS layout, in 4-byte words
-  int off_stage;          // kStages x {K tile, V tile}, each [32][D] row-major, swizzled
+  int stages;             // LDS ring depth of the block stream
+  // LDS layout, byte offsets.  "Gather" entries (the per-row bucket scores of
+  // the contextual key term, or the bias table, and their guard regions) are
+  // gsz bytes: fp16 for bf16 inputs without a value term, else fp32.
+  int gsz;
+  int off_stage;          // stages x {K tile, V tile}, each [32][D] row-major, swizzled
   int kpitch;             // row pitch (elements) of the staged query-term table
   int off_rq;             // query-term table staged as [nbt*32][kpitch]
   int off_tab;            // gather target: per-row bucket scores (contextual) or bias table
-  int p_tab;              // row pitch of the per-row bucket scores
-  int zr;                 // size of each guard region: (S-1)*S + 1
+  int p_tab;              // row pitch (gather entries) of the per-row bucket scores
+  int zr;                 // entries of each guard region: (S-1)*S + 1
   int off_zero, off_neg;  // guard regions (all 0 / all -inf) addressed as guard + row part
-  int off_w;              // value-term weight sums; same layout as [off_tab, off_neg + zr)
-  int off_tq, p_tq;       // query-term bucket scores of the current key block [32][p_tq]
+  int off_w;              // value-term weight sums (fp32); same layout as [off_tab, off_neg + zr)
+  int off_tq, p_tq;       // query-term bucket scores (fp32) of the current key block [32][p_tq]
   int off_tqz, off_tqn;   // guard regions of the query-term scores
-  int off_ry, off_cx;     // per-axis tables: (g(dy)+H)*S and g(dx)+H
-  int lds_words;
+  int off_ry, off_cx;     // per-axis tables (int32): (g(dy)+H)*S*gsz and g(dx)+H
+  int lds_bytes;
   int dtype, mode;
   uint32_t terms;
   int elem_bytes;

@@ -1,0 +1,121 @@
+"""Condense rocprofv3 CSV output into the short text summaries kept with the
+benchmarks.
+
+Two inputs are understood:
+
+* ``--stats DIR``: the ``*_kernel_stats.csv`` of a ``rocprofv3 --kernel-trace
+  --stats --output-format csv`` run; prints per-kernel calls and durations.
+* ``--pmc DIR``: the ``*counter_collection.csv`` of a ``rocprofv3 --pmc
+  FETCH_SIZE`` (or ``WRITE_SIZE``) run of ``bench.py --copy-probe MIB``; prints
+  the counter per dispatch of the attention kernel and of the plain copy
+  probe that ran after it, the copy's scale factor (counter / known bytes) and
+  the attention kernel's scaled bytes per launch.
+
+``kernel_source_hash()`` is the SHA-256 of the sources that decide what the
+forward kernel reads and writes; a traffic figure is only reported for the
+hash it was measured with.
+"""
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/fwd_kernel.h", "csrc/plan.h", "csrc/plan.cpp", "csrc/device_index.h")
+FWD_KERNEL = "rpe_fwd_kernel"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()[:16]
+
+
+def demangle(names):
+    try:
+        r = subprocess.run(["c++filt"], input="\n".join(names), stdout=subprocess.PIPE, text=True, timeout=10)
+        out = r.stdout.splitlines()
+        if len(out) == len(names):
+            return out
+    except Exception:
+        pass
+    return list(names)
+
+
+def _one(pattern, d):
+    files = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not files:
+        raise SystemExit(f"no {pattern} under {d}")
+    return files[0]
+
+
+def stats_summary(d):
+    rows = list(csv.DictReader(open(_one("*kernel_stats.csv", d))))
+    names = demangle([r["Name"] for r in rows])
+    lines = [f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}  kernel"]
+    for r, n in zip(rows, names):
+        if len(n) > 110:
+            n = n[:107] + "..."
+        lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}  {n}")
+    return "\n".join(lines)
+
+
+def pmc_summary(d, copy_mib):
+    rows = list(csv.DictReader(open(_one("*counter_collection.csv", d))))
+    by = collections.defaultdict(lambda: collections.defaultdict(list))
+    last_fwd = max((int(r["Dispatch_Id"]) for r in rows if FWD_KERNEL in r["Kernel_Name"]), default=-1)
+    counters = sorted({r["Counter_Name"] for r in rows})
+    for r in rows:
+        name = r["Kernel_Name"]
+        if FWD_KERNEL in name:
+            key = demangle([name])[0]
+        elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_fwd:
+            key = "copy probe"
+        else:
+            continue
+        by[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = []
+    copy_bytes = copy_mib * (1 << 20)
+    for c in counters:
+        copy_vals = by.get("copy probe", {}).get(c, [])
+        factor = None
+        if copy_vals:
+            factor = (sum(copy_vals) / len(copy_vals)) * 1024.0 / copy_bytes
+            out.append(f"copy probe ({copy_mib} MiB read + {copy_mib} MiB written): {c} mean "
+                       f"{sum(copy_vals) / len(copy_vals):.1f} KiB over {len(copy_vals)} dispatches; "
+                       f"factor = {factor:.4f} (counter / known bytes)")
+        for k, cs in by.items():
+            if k == "copy probe" or c not in cs:
+                continue
+            v = cs[c]
+            mean_kib = sum(v) / len(v)
+            scaled = mean_kib * 1024.0 / factor if factor else float("nan")
+            out.append(f"{k}: {c} mean {mean_kib:.1f} KiB over {len(v)} dispatches "
+                       f"(min {min(v):.1f}, max {max(v):.1f}); scaled bytes per launch {scaled:.0f}")
+    return "\n".join(out)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--stats")
+    ap.add_argument("--pmc")
+    ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--hash", action="store_true", help="print the forward kernel's source hash")
+    a = ap.parse_args()
+    if a.hash:
+        print(kernel_source_hash())
+    if a.stats:
+        print(stats_summary(a.stats))
+    if a.pmc:
+        print(pmc_summary(a.pmc, a.copy_mib))
+
+
+if __name__ == "__main__":
+    main()
