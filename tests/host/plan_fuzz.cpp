@@ -88,8 +88,19 @@ int main(int argc, char** argv) {
     REQUIRE(p.off_rq >= p.stages * 2 * rpe::kBlockSlots * p.D * p.elem_bytes && p.off_rq % 16 == 0);
     REQUIRE(p.off_rq <= p.off_tab);
     if (tq) REQUIRE(p.off_rq + p.nbt * rpe::kRowTile * p.kpitch * p.elem_bytes <= p.off_tab);
-    // the per-row scores take a whole 32-bucket tile per store, in rows of an odd number of words
-    REQUIRE(p.p_tab >= p.nbt * rpe::kRowTile && (p.p_tab * p.gsz) % 4 == 0 && ((p.p_tab * p.gsz / 4) & 1));
+    // per-row scores: nb entries in rows of an odd number of words
+    REQUIRE(p.p_tab >= p.nb && (p.p_tab * p.gsz) % 4 == 0 && ((p.p_tab * p.gsz / 4) & 1));
+    // the thresholds reproduce g on every offset of the unit
+    if (d.mode != RPE_MODE_NONE && p.map == RPE_MAP_PIECEWISE && p.n_thr >= 0) {
+      const int amax = (p.R > p.C ? p.R : p.C) - 1;
+      for (int a = 0; a <= amax; ++a) {
+        int cnt = 0;
+        for (int k = 0; k < p.n_thr; ++k) cnt += p.thr[k] <= a;
+        REQUIRE(cnt == rpe::axis_index_host(a, p.map, p.rounding, p.alpha, p.beta, p.gamma));
+        REQUIRE(-cnt == rpe::axis_index_host(-a, p.map, p.rounding, p.alpha, p.beta, p.gamma));
+      }
+      REQUIRE(p.n_thr <= p.half && p.n_thr <= rpe::kMaxThresholds);
+    }
     if (rows) REQUIRE(p.off_zero >= p.off_tab + p.NW * rpe::kRowTile * p.p_tab * p.gsz);
     if (!ctx) REQUIRE(p.off_zero >= p.off_tab + p.nb * p.gsz);
     REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr * p.gsz);

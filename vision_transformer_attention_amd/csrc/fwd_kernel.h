@@ -36,11 +36,12 @@
 // holds the row base and g(dx)+H).  Pairs without a position term address a
 // zero guard region, padding keys a -inf guard region.
 //
-// Softmax runs in log2 units against a running row maximum m that moves only
-// when a block's maximum exceeds it by more than 2^8 (so most blocks skip the
-// rescale).  m enters the logits through the accumulator of the S^T product,
+// Softmax runs in log2 units against a running row maximum m that the first
+// key block sets and that later blocks move only when their weights could
+// overflow (a lane's block sum above 2^64), so blocks normally need no maximum
+// at all.  m enters the logits through the accumulator of the S^T product,
 // which starts at -m / c instead of zero: the gathered logit then comes out
-// already shifted and feeds exp2 directly.  The first key block sets m.
+// already shifted and feeds exp2 directly.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,6 +68,7 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
 constexpr int kThreadsMax = kMaxWaves * 64;
 constexpr float kLazyTau = 8.0f;
+constexpr float kSumMax = 18446744073709551616.0f;   // 2^64
 // bucket scores are clamped into the fp16 range before they are stored
 constexpr float kGatherMax = 65000.0f;
 
@@ -160,7 +162,7 @@ using bool_c = std::integral_constant<bool, B>;
 }  // namespace
 
 template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE>
-__global__ void __launch_bounds__(kThreadsMax) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE))))
+__global__ void __launch_bounds__(kThreadsMax) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE, D))))
 rpe_fwd_kernel(Params p) {
   constexpr bool BF = std::is_same<DT, __bf16>::value;
   constexpr bool CTX = MODE == RPE_MODE_CONTEXTUAL;
@@ -195,28 +197,29 @@ rpe_fwd_kernel(Params p) {
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r32 = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) wave index
 
-  // ---- workgroup -> (unit, query chunk); consecutive chunks of a unit on one XCD.
-  const int64_t bid = blockIdx.x;
-  const int64_t per = p.n_wg / 8, rem = p.n_wg % 8;
-  const int64_t xcd = bid % 8, idx = bid / 8;
-  const int64_t task = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  const int64_t unit = task / p.n_qc;
-  const int qc = static_cast<int>(task - unit * p.n_qc);
-  const int w_img = static_cast<int>(unit % p.U);
-  const int64_t bh = unit / p.U;
-  const int head = static_cast<int>(bh % p.H);
+  // ---- workgroup -> (unit, query chunk); consecutive chunks of a unit on one XCD
+  // (workgroup ids are dealt round-robin over the 8 XCDs).  32-bit arithmetic:
+  // the planner keeps the workgroup count below 2^31.
+  const uint32_t bid = blockIdx.x;
+  const uint32_t nwg = static_cast<uint32_t>(p.n_wg);
+  const uint32_t per = nwg >> 3, rem = nwg & 7u, xcd = bid & 7u, idx = bid >> 3;
+  const uint32_t task = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  const uint32_t unit = task / static_cast<uint32_t>(p.n_qc);
+  const int qc = static_cast<int>(task - unit * static_cast<uint32_t>(p.n_qc));
+  const uint32_t bh = unit / static_cast<uint32_t>(p.U);
+  const int w_img = static_cast<int>(unit - bh * static_cast<uint32_t>(p.U));
+  const int head = static_cast<int>(bh % static_cast<uint32_t>(p.H));
   const int wy = w_img / p.wins_per_row, wx = w_img - wy * p.wins_per_row;
   const int wbase = p.M ? (wy * p.M) * p.gw + wx * p.M : p.P;   // N index of the unit's grid (0,0)
   const int rowstride = p.M ? p.gw : p.C;
   const int rt0 = qc * p.n_rt / p.n_qc, rt1 = (qc + 1) * p.n_rt / p.n_qc;
   const bool active = rt0 + wid < rt1;
 
-  const int64_t base = bh * static_cast<int64_t>(p.N) * D;
+  const int64_t base = static_cast<int64_t>(bh) * p.N * D;
   const DT* __restrict__ qg = reinterpret_cast<const DT*>(p.q) + base;
   const char* __restrict__ kgb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.k) + base);
   const char* __restrict__ vgb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.v) + base);
   DT* __restrict__ og = reinterpret_cast<DT*>(p.o) + base;
-  const char* rkb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.rk) + head * p.tab_head_stride);
   const char* rvb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.rv) + head * p.tab_head_stride);
 
   int* const ry_tab = reinterpret_cast<int*>(smem + p.off_ry);
@@ -227,6 +230,110 @@ rpe_fwd_kernel(Params p) {
   float* const wsum = reinterpret_cast<float*>(smem + p.off_w);
   float* const tqs = reinterpret_cast<float*>(smem + p.off_tq);
 
+  // ---- this lane's query row.
+  const int qi = (rt0 + wid) * kRowTile + r32;     // unit token
+  const bool qvalid = active && qi < p.T;
+  const bool qpos = qvalid && qi >= p.P;
+  const int qt = qpos ? qi - p.P : 0;
+  const int yi = qt / p.C, xi = qt - (qt / p.C) * p.C;
+  const int qn = qpos ? wbase + yi * rowstride + xi : (qvalid ? qi : 0);
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[row r32][k-slice h of each step].
+  bf16x8 qb[BF ? KS : 1];
+  float qf[BF ? 1 : KS];
+  if constexpr (BF) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int d0 = 16 * kk + 8 * h;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (qvalid && d0 < D) u = ld16(qg + static_cast<int64_t>(qn) * D + d0);
+      qb[kk] = as_bf16x8(u);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = qvalid ? qg[static_cast<int64_t>(qn) * D + 2 * kk + h] : 0.0f;
+  }
+
+  // rK rows as the A operand of TK^T = rK Q^T, loaded straight to registers in
+  // batches of KB 32-row tiles; the first batch is issued here, with Q, so its
+  // latency overlaps the prologue.  Rows past nb read row 0 (their scores land
+  // in row-area columns that are never gathered).
+  constexpr int KB = BF ? 3 : 1;
+  const DT* rkt = reinterpret_cast<const DT*>(p.rk) + head * p.tab_head_stride;
+  bf16x8 rka[TK && BF ? KB : 1][BF ? KS : 1];
+  float rkf[TK && !BF ? KB : 1][BF ? 1 : KS];
+  auto load_rk = [&](int t0) {
+    if constexpr (TK) {
+#pragma unroll
+      for (int bt = 0; bt < KB; ++bt) {
+        const int t = t0 + bt, b = kRowTile * t + r32;
+        const int64_t row = (t < p.nbt && b < p.nb) ? b : 0;
+        if constexpr (BF) {
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) rka[bt][kk] = as_bf16x8(ld16(rkt + row * D + 16 * kk + 8 * h));
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) rkf[bt][kk] = rkt[row * D + 2 * kk + h];
+        }
+      }
+    }
+  };
+  load_rk(0);
+
+  // ---- the block stream: [key/value blocks][rV tiles]
+  const int n_vt = TV ? p.nbt : 0;
+  const int nblk = p.n_blocks;
+  const int L = nblk + n_vt;
+  const int ST = p.stages;
+  // direct-to-LDS instructions this wave issues per 32-row tile; every stream
+  // element costs two per instruction (rV tiles are copied into both halves of
+  // their stage), so the loads issued after an element are a simple count
+  const int my_ipb = wid < IPB ? (IPB - wid + NW - 1) / NW : 0;
+  const int lpe = 2 * my_ipb;
+  char* const ring = smem + p.off_stage;
+  const uint32_t lds_ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)smem)) + p.off_stage;
+  // N index of a key slot; padding slots read a valid token (their values are masked)
+  auto slot_n = [&](int blk, int s) -> int {
+    if (p.prefix_block) {
+      if (blk == 0) return s < p.P ? s : wbase;
+      blk -= 1;
+    }
+    const int sigma = blk * kBlockSlots + s;
+    const int y = sigma >> p.lwp, x = sigma & (p.Wp - 1);
+    int n = (y < p.R && x < p.C) ? wbase + y * rowstride + x : wbase;
+    if (p.prefix_in_tail) n = (y == p.R - 1 && x >= p.C && x - p.C < p.P) ? x - p.C : n;
+    return n;
+  };
+  // Copy 32 rows into a swizzled row-major tile: instruction i covers rows
+  // [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR with
+  // global chunk (l % CPR) ^ (row % CPR).
+  auto issue = [&](int f, int stage) {
+    const uint32_t kt = lds_ring + stage * (2 * TILE);
+    const uint32_t vt = kt + TILE;
+    for (int i = wid; i < IPB; i += NW) {
+      const int row = i * RPI + lane / CPR;
+      const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
+      if (f < nblk) {
+        const uint32_t off = static_cast<uint32_t>(slot_n(f, row)) * RB + cb;
+        dma16(kgb + off, kt + i * 1024);
+        dma16(vgb + off, vt + i * 1024);
+      } else {
+        const int b = kRowTile * (f - nblk) + row;
+        const uint32_t off = static_cast<uint32_t>(b < p.nb ? b : 0) * RB + cb;
+        dma16(rvb + off, kt + i * 1024);
+        dma16(rvb + off, vt + i * 1024);
+      }
+    }
+  };
+
+  // ---- start the ring now (the prologue below overlaps its latency); the Q
+  // loads above are older, so waiting for element 0 also covers them.
+  int st_cur = 0, st_iss = 0;
+  for (int f = 0; f < ST - 1 && f < L; ++f) {
+    issue(f, st_iss);
+    st_iss = st_iss + 1 == ST ? 0 : st_iss + 1;
+  }
+
   // ---- prologue: per-axis tables, guards, bias table, weight sums, staged rQ.
   // ry holds byte offsets of the row part, (g(dy)+H)*S*GSZ; cx holds g(dx)+H.
   {
@@ -234,7 +341,20 @@ rpe_fwd_kernel(Params p) {
     for (int i = tid; i < nry + ncx; i += nth) {
       const bool is_row = i < nry;
       const int x = is_row ? i - (p.R - 1) : i - nry - (p.C - 1);
-      const int g = MODE == RPE_MODE_NONE ? 0 : axis_index(x, p.map, p.rounding, p.alpha, p.beta, p.gamma) + p.half;
+      int g = 0;
+      if constexpr (MODE != RPE_MODE_NONE) {
+        if (p.map == RPE_MAP_SWIN) {
+          g = x;
+        } else if (p.n_thr >= 0) {
+          const int ax = x < 0 ? -x : x;
+          int cnt = 0;
+          for (int k = 0; k < p.n_thr; ++k) cnt += p.thr[k] <= ax ? 1 : 0;
+          g = x < 0 ? -cnt : cnt;
+        } else {
+          g = axis_index(x, p.map, p.rounding, p.alpha, p.beta, p.gamma);
+        }
+        g += p.half;
+      }
       if (is_row)
         ry_tab[i] = g * p.S * GSZ;
       else
@@ -279,82 +399,6 @@ rpe_fwd_kernel(Params p) {
       }
     }
   }
-
-  // ---- this lane's query row.
-  const int qi = (rt0 + wid) * kRowTile + r32;     // unit token
-  const bool qvalid = active && qi < p.T;
-  const bool qpos = qvalid && qi >= p.P;
-  const int qt = qpos ? qi - p.P : 0;
-  const int yi = qt / p.C, xi = qt - (qt / p.C) * p.C;
-  const int qn = qpos ? wbase + yi * rowstride + xi : (qvalid ? qi : 0);
-
-  // Q as the B operand of S^T = K Q^T: lane holds Q[row r32][k-slice h of each step].
-  bf16x8 qb[BF ? KS : 1];
-  float qf[BF ? 1 : KS];
-  if constexpr (BF) {
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int d0 = 16 * kk + 8 * h;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (qvalid && d0 < D) u = ld16(qg + static_cast<int64_t>(qn) * D + d0);
-      qb[kk] = as_bf16x8(u);
-    }
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = qvalid ? qg[static_cast<int64_t>(qn) * D + 2 * kk + h] : 0.0f;
-  }
-
-  // ---- the block stream: [rK tiles][key/value blocks][rV tiles]
-  const int n_kt = TK ? p.nbt : 0;
-  const int n_vt = TV ? p.nbt : 0;
-  const int nblk = p.n_blocks;
-  const int L = n_kt + nblk + n_vt;
-  const int ST = p.stages;
-  // direct-to-LDS instructions this wave issues per 32-row tile; every stream
-  // element costs two per instruction (table tiles are copied into both halves
-  // of their stage), so the loads issued after an element are a simple count
-  const int my_ipb = wid < IPB ? (IPB - wid + NW - 1) / NW : 0;
-  const int lpe = 2 * my_ipb;
-  char* const ring = smem + p.off_stage;
-  const uint32_t lds_ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)smem)) + p.off_stage;
-  // N index of a key slot; padding slots read a valid token (their values are masked)
-  auto slot_n = [&](int blk, int s) -> int {
-    if (p.prefix_block) {
-      if (blk == 0) return s < p.P ? s : wbase;
-      blk -= 1;
-    }
-    const int sigma = blk * kBlockSlots + s;
-    const int y = sigma >> p.lwp, x = sigma & (p.Wp - 1);
-    int n = (y < p.R && x < p.C) ? wbase + y * rowstride + x : wbase;
-    if (p.prefix_in_tail) n = (y == p.R - 1 && x >= p.C && x - p.C < p.P) ? x - p.C : n;
-    return n;
-  };
-  // Copy 32 rows into a swizzled row-major tile: instruction i covers rows
-  // [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR with
-  // global chunk (l % CPR) ^ (row % CPR).
-  auto issue = [&](int f, int stage) {
-    const uint32_t kt = lds_ring + stage * (2 * TILE);
-    const uint32_t vt = kt + TILE;
-    for (int i = wid; i < IPB; i += NW) {
-      const int row = i * RPI + lane / CPR;
-      const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
-      if (f < n_kt) {
-        const int b = kRowTile * f + row;
-        const uint32_t off = static_cast<uint32_t>(b < p.nb ? b : 0) * RB + cb;
-        dma16(rkb + off, kt + i * 1024);
-        dma16(rkb + off, vt + i * 1024);
-      } else if (f < n_kt + nblk) {
-        const uint32_t off = static_cast<uint32_t>(slot_n(f - n_kt, row)) * RB + cb;
-        dma16(kgb + off, kt + i * 1024);
-        dma16(vgb + off, vt + i * 1024);
-      } else {
-        const int b = kRowTile * (f - n_kt - nblk) + row;
-        const uint32_t off = static_cast<uint32_t>(b < p.nb ? b : 0) * RB + cb;
-        dma16(rvb + off, kt + i * 1024);
-        dma16(rvb + off, vt + i * 1024);
-      }
-    }
-  };
 
   // S^T tile (plus init) from a swizzled row-major K tile.  K operand (A): lane
   // holds K[slot r32][d 16kk + 8h .. +7] (bf16) / [2kk + h] (fp32).
@@ -442,8 +486,7 @@ rpe_fwd_kernel(Params p) {
   // two blocks); cqb the same for the query-term scores (fp32).
   const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab * GSZ : p.off_tab;
   const int w_delta = TV ? p.off_w - p.off_tab : 0;   // byte distance gather target -> weight sums
-  __syncthreads();  // prologue tables visible; no direct-to-LDS load is in flight yet
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // Q and table loads done before the ring starts
+  lds_barrier();  // prologue tables visible (ring loads stay in flight)
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
 #pragma unroll
@@ -496,8 +539,13 @@ rpe_fwd_kernel(Params p) {
   // One key block: logits, lazy online softmax, PV (and the value-term scatter).
   // INTERIOR: every slot is a grid key of rows < R-1 or a padding column.
   // FIRST: the first block of the stream sets the running maximum.
+  // Row parts ry(yq - y) of this lane's keys 8j + 4h + i of interior block g.
+  auto load_ry = [&](int g, int (&r)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = WIDE ? ryt[-(g >> 1)] : ryt[-(g * rpb + rj[j])];
+  };
   auto process_block = [&](auto interior_c, auto first_c, auto ph_c, const char* ktile, const char* vtile,
-                           int gblk, bool prefix_blk) {
+                           int gblk, bool prefix_blk, const int (&ryv)[4]) {
     constexpr bool INTERIOR = decltype(interior_c)::value;
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr int PH = decltype(ph_c)::value;
@@ -507,7 +555,7 @@ rpe_fwd_kernel(Params p) {
     if constexpr (INTERIOR) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ryb = WIDE ? ryt[-(gblk >> 1)] : ryt[-(gblk * rpb + rj[j])];
+        const int ryb = ryv[j];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ab[j][i] = ryb + cxb[PH][j][i];
@@ -544,22 +592,43 @@ rpe_fwd_kernel(Params p) {
         }
       }
     }
-    float bmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+    auto block_max = [&]() -> float {
+      float bm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    bmax = fmaxf(bmax, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
-                             fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
-    bmax = row_max2(bmax);
+      bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[2][2], x[2][3])),
+                           fmaxf(fmaxf(x[3][0], x[3][1]), fmaxf(x[3][2], x[3][3]))));
+      return row_max2(bm);
+    };
+    float pr[4][4];
+    float bsum = 0.0f;
+    auto weights = [&]() {
+      bsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[j][i] = __builtin_amdgcn_exp2f(x[j][i]);
+          bsum += pr[j][i];
+        }
+    };
     if constexpr (FIRST) {
-      // every block holds at least one real key, so bmax is finite
+      // every block holds at least one real key, so the block maximum is finite
+      const float bmax = block_max();
       m_run = bmax;
       mneg = splat16(-m_run * inv_c);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[j][i] -= bmax;
+      weights();
     } else {
-      const bool need = bmax > kLazyTau;
-      if (__builtin_expect(__any(need), 0)) {
+      // The running maximum only has to keep the weights finite: a block moves it
+      // (to the row's block maximum) only when some lane's weights sum past 2^64
+      // or overflow, which also catches every logit more than 64 above it.
+      weights();
+      if (__builtin_expect(__any(!(bsum <= kSumMax)), 0)) {
+        const float bmax = block_max();
+        const bool need = bmax > kLazyTau;
         const float dm = need ? bmax : 0.0f;
         const float alpha = __builtin_amdgcn_exp2f(-dm);
         l_part *= alpha;
@@ -577,16 +646,10 @@ rpe_fwd_kernel(Params p) {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[j][i] -= dm;
+        weights();
       }
     }
-    float pr[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[j][i] = __builtin_amdgcn_exp2f(x[j][i]);
-        l_part += pr[j][i];
-      }
+    l_part += bsum;
     if constexpr (TV) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -596,14 +659,15 @@ rpe_fwd_kernel(Params p) {
     pv_tile(vtile, pr, false);
   };
   // phase dispatch (a 64-slot grid row spans two blocks)
-  auto process = [&](auto interior_c, auto first_c, const char* kt, const char* vt, int gblk, bool pre) {
+  auto process = [&](auto interior_c, auto first_c, const char* kt, const char* vt, int gblk, bool pre,
+                     const int (&ryv)[4]) {
     if constexpr (WIDE) {
       if (gblk & 1)
-        process_block(interior_c, first_c, std::integral_constant<int, 1>{}, kt, vt, gblk, pre);
+        process_block(interior_c, first_c, std::integral_constant<int, 1>{}, kt, vt, gblk, pre, ryv);
       else
-        process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre);
+        process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre, ryv);
     } else {
-      process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre);
+      process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre, ryv);
     }
   };
 
@@ -639,11 +703,6 @@ rpe_fwd_kernel(Params p) {
 
   // ---- walk the stream: element e is computed while the next stages-2 elements
   // are in flight; element e+stages-1 is issued into the stage element e-1 used.
-  int st_cur = 0, st_iss = 0;
-  for (int f = 0; f < ST - 1 && f < L; ++f) {
-    issue(f, st_iss);
-    st_iss = st_iss + 1 == ST ? 0 : st_iss + 1;
-  }
   // wait for element e, then refill the ring; returns e's stage
   auto step = [&](int e) -> int {
     // this wave's loads issued after element e's: those of elements e+1 .. e+ST-2
@@ -661,23 +720,61 @@ rpe_fwd_kernel(Params p) {
   auto ktile_of = [&](int s) -> const char* { return ring + s * (2 * TILE); };
   auto vtile_of = [&](int s) -> const char* { return ring + s * (2 * TILE) + TILE; };
 
-  int e = 0;
-  // rK tiles: TK[row][32t + ...] = c * q_row . rK[...] into this wave's row area
+  // ---- key-term scores of this wave's rows: TK[row][b] = c * q_row . rK[b],
+  // written a 32-bucket tile at a time (rows hold nbt*32 entries; each wave
+  // reads only its own rows, so no barrier is needed before the gathers).
   if constexpr (TK) {
-    for (; e < n_kt; ++e) {
-      const int s = step(e);
-      if (active) {
-        const f32x16 acc = s_tile(ktile_of(s), f32x16{});
-        GT* row = reinterpret_cast<GT*>(smem + rowbase);
+    GT* const trow = reinterpret_cast<GT*>(smem + rowbase);
+    for (int t0 = 0; t0 < p.nbt; t0 += KB) {
+      if (t0 > 0) load_rk(t0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int bt = 0; bt < KB; ++bt) {
+        const int t = t0 + bt;
+        if (t < p.nbt && active) {
+          f32x16 acc = {};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            row[kRowTile * e + 8 * j + 4 * h + i] =
-                static_cast<GT>(fminf(fmaxf(acc[4 * j + i] * p.c, -kGatherMax), kGatherMax));
+          for (int kk = 0; kk < KS; ++kk) {
+            if constexpr (BF)
+              acc = mfma32(rka[bt][kk], qb[kk], acc);
+            else
+              acc = mfma32(rkf[bt][kk], qf[kk], acc);
+          }
+          // rows hold nb entries (fp16 rows: an even count, so a pair never
+          // crosses into the next row)
+          const int b0 = kRowTile * t + 4 * h;
+          GT* const dst = trow + b0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            GT v4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v4[i] = static_cast<GT>(fminf(fmaxf(acc[4 * j + i] * p.c, -kGatherMax), kGatherMax));
+            if constexpr (G16) {
+              uint32_t w0, w1;
+              __builtin_memcpy(&w0, &v4[0], 4);
+              __builtin_memcpy(&w1, &v4[2], 4);
+              if (b0 + 8 * j < p.nb) reinterpret_cast<uint32_t*>(dst + 8 * j)[0] = w0;
+              if (b0 + 8 * j + 2 < p.nb) reinterpret_cast<uint32_t*>(dst + 8 * j)[1] = w1;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (b0 + 8 * j + i < p.nb) dst[8 * j + i] = v4[i];
+            }
+          }
+        }
       }
     }
   }
+  // Q is in registers before the ring moves on: otherwise the first use of Q
+  // waits for every load issued before it, including ring loads just issued.
+  if constexpr (BF) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(qb[kk]));
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(qf[kk]));
+  }
+
+  int e = 0;
   // key/value blocks: the first one sets the running maximum
   {
     int gb = 0;
@@ -687,24 +784,33 @@ rpe_fwd_kernel(Params p) {
         block_query_scores(ktile_of(s));
         lds_barrier();
       }
+      int ry0[4];
+      load_ry(0, ry0);
       if (active) {
         if (p.prefix_block)
-          process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), -1, true);
+          process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), -1, true, ry0);
         else if (p.first_tail > 0)
-          process(bool_c<true>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false);
+          process(bool_c<true>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false, ry0);
         else
-          process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false);
+          process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false, ry0);
       }
       if (!p.prefix_block) gb = 1;
       ++e;
     }
+    // interior blocks: the row parts of the next block are read one block ahead
+    int ryn[4];
+    load_ry(gb, ryn);
     for (; gb < p.first_tail; ++gb, ++e) {
       const int s = step(e);
+      int ryc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ryc[j] = ryn[j];
+      load_ry(gb + 1, ryn);
       if constexpr (TQ) {
         block_query_scores(ktile_of(s));
         lds_barrier();
       }
-      if (active) process(bool_c<true>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false);
+      if (active) process(bool_c<true>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryc);
     }
     for (; gb < p.grid_blocks; ++gb, ++e) {
       const int s = step(e);
@@ -712,7 +818,7 @@ rpe_fwd_kernel(Params p) {
         block_query_scores(ktile_of(s));
         lds_barrier();
       }
-      if (active) process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false);
+      if (active) process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryn);
     }
   }
   // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
@@ -720,7 +826,7 @@ rpe_fwd_kernel(Params p) {
     for (; e < L; ++e) {
       const int s = step(e);
       if (active) {
-        const int t = e - n_kt - nblk;
+        const int t = e - nblk;
         const float* wrow = reinterpret_cast<const float*>(smem + rowbase + w_delta);
         float wv[4][4];
 #pragma unroll
@@ -758,7 +864,7 @@ rpe_fwd_kernel(Params p) {
         }
       }
     }
-  if (p.lse && h == 0) p.lse[bh * p.N + qn] = (m_run + log2f(l)) * 0.6931471805599453f;
+  if (p.lse && h == 0) p.lse[static_cast<int64_t>(bh) * p.N + qn] = (m_run + log2f(l)) * 0.6931471805599453f;
 }
 
 // ----------------------------------------------------------------------------------------

@@ -52,8 +52,7 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   p->off_rq = off;
   if (tq) off += align(p->nbt * kRowTile * p->kpitch * eb, 16);
   p->zr = (p->S - 1) * p->S + 1;  // 1 when there is no table
-  // per-row scores are stored a whole 32-bucket tile at a time, so rows hold nbt*32 entries
-  p->p_tab = odd_word_pitch(p->nbt * kRowTile, p->gsz);
+  p->p_tab = odd_word_pitch(p->nb, p->gsz);
   p->off_tab = off;
   if (d->mode == RPE_MODE_BIAS || d->mode == RPE_MODE_NONE) {
     off += p->nb * p->gsz;
@@ -132,6 +131,17 @@ int table_geometry(const rpe_attn_desc* d, int* half, int* S, int* nb) {
   return RPE_OK;
 }
 
+int axis_index_host(int x, int map, int rounding, double alpha, double beta, double gamma) {
+  if (map == RPE_MAP_SWIN) return x;
+  const double ax = std::fabs(static_cast<double>(x));
+  if (ax <= alpha) return x;
+  const double s = alpha + std::log(ax / alpha) / std::log(gamma / alpha) * (beta - alpha);
+  const double cap = std::fmin(beta, std::floor(s + 0.5));
+  const int mag = rounding == RPE_ROUND_CAPPED ? static_cast<int>(std::floor(cap + 0.5))
+                                               : static_cast<int>(std::floor(cap));
+  return x > 0 ? mag : -mag;
+}
+
 int make_plan(const rpe_attn_desc* d, Params* p) {
   int st = validate(d);
   if (st != RPE_OK) return st;
@@ -171,6 +181,24 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
     p->tab_head_stride = d->mode == RPE_MODE_BIAS ? (int64_t)p->nb : (int64_t)p->nb * p->D;
   }
 
+  // thresholds of g over the unit's offsets 0 .. max(R, C) - 1
+  p->n_thr = 0;
+  if (d->mode != RPE_MODE_NONE && p->map == RPE_MAP_PIECEWISE) {
+    const int amax = (p->R > p->C ? p->R : p->C) - 1;
+    int k = 0;
+    for (int a = 0; a <= amax && k >= 0; ++a) {
+      const int g = axis_index_host(a, p->map, p->rounding, p->alpha, p->beta, p->gamma);
+      while (k < g) {
+        if (k == kMaxThresholds) {
+          k = -1;
+          break;
+        }
+        p->thr[k++] = static_cast<int16_t>(a);
+      }
+    }
+    p->n_thr = k;
+  }
+
   // key slots
   p->Wp = padded_width(p->C);
   if (p->Wp > kMaxWp) return RPE_E_UNSUPPORTED;
@@ -200,8 +228,8 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
       t.n_wg = t.n_units * t.n_qc;
       t.stages = stages;
       if (lds_layout(d, &t) != RPE_OK) continue;
-      const int by_regs = 4 * waves_per_simd(d->mode, d->terms, t.Wp == 64) / t.NW;
-      const int by_lds = kMaxLdsBytes / t.lds_bytes;
+      const int by_regs = 4 * waves_per_simd(d->mode, d->terms, t.Wp == 64, d->head_dim) / t.NW;
+      const int by_lds = kMaxLdsBytes / ((t.lds_bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule);
       const int waves = (by_regs < by_lds ? by_regs : by_lds) * t.NW;
       if (waves > best_waves) {
         best_waves = waves;
@@ -210,6 +238,7 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
     }
   }
   if (best_waves < 0) return RPE_E_BUCKETS;
+  if (best.n_wg > 0x7fffffff) return RPE_E_SHAPE;  // workgroup ids are 32-bit in the kernel
   *p = best;
   return RPE_OK;
 }

@@ -22,12 +22,23 @@ constexpr int kMaxWaves = 4;
 constexpr int kMaxStages = 4;       // deepest LDS ring of the block stream
 constexpr int kMinStages = 2;
 constexpr int kMaxLdsBytes = 160 * 1024;
+// LDS is allocated to workgroups in granules of this many bytes.
+constexpr int kLdsGranule = 512;
+// The piecewise index g is odd and non-decreasing in |x| (iRPE page, eq. 18),
+// so on the offsets of a unit it is g(x) = sign(x) * #{k : t_k <= |x|} with
+// thresholds t_k = min{a >= 0 : g(a) >= k}.  The planner evaluates g on the
+// host and passes up to kMaxThresholds thresholds; beyond that the kernel
+// evaluates g itself.
+constexpr int kMaxThresholds = 64;
 // Resident waves per SIMD each forward instance is compiled for (register
-// budget 512 / waves): instances with only the key term or a bias fit three;
-// wide rows (two column phases of gather offsets) and the query / value terms
-// need the larger budget of two.  The planner sizes LDS to match.
-constexpr int waves_per_simd(int mode, uint32_t terms, bool wide) {
-  return (wide || (mode == RPE_MODE_CONTEXTUAL && (terms & (RPE_TERM_Q | RPE_TERM_V)))) ? 2 : 3;
+// budget 512 / waves): four for head dims up to 32 and three for 64 with only
+// the key term or a bias; wide rows (two column phases of gather offsets) and
+// the query / value terms take the larger budget of two.  The planner sizes
+// LDS to match.
+constexpr int waves_per_simd(int mode, uint32_t terms, bool wide, int head_dim) {
+  return (wide || (mode == RPE_MODE_CONTEXTUAL && (terms & (RPE_TERM_Q | RPE_TERM_V)))) ? 2
+         : head_dim <= 32                                                             ? 4
+                                                                                       : 3;
 }
 
 struct Params {
@@ -83,6 +94,8 @@ struct Params {
   int dtype, mode;
   uint32_t terms;
   int elem_bytes;
+  int n_thr;                // piecewise map: number of thresholds, -1: evaluate g on the device
+  int16_t thr[kMaxThresholds];
 };
 
 // Validation only (no derived plan).  Returns an rpe_status.
@@ -90,6 +103,9 @@ int validate(const rpe_attn_desc* d);
 
 // Table geometry; returns an rpe_status.
 int table_geometry(const rpe_attn_desc* d, int* half, int* S, int* nb);
+
+// g(x) of one integer offset in float64 (the same formula the device evaluates).
+int axis_index_host(int x, int map, int rounding, double alpha, double beta, double gamma);
 
 // Full plan for rpe_attn_fwd (pointers left null).  Returns an rpe_status.
 int make_plan(const rpe_attn_desc* d, Params* p);
