@@ -209,12 +209,14 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("terms", ["kqv", "k"])
 @pytest.mark.parametrize("label,over", EDGE)
-def test_edge_shapes(dev, label, over):
-    base = dict(batch=2, heads=2, grid_h=6, grid_w=7)
+def test_edge_shapes(dev, label, over, terms):
+    # "k" alone keeps the per-row key scores in fp16; with the value term they are fp32
+    base = dict(batch=2, heads=2, grid_h=6, grid_w=7, terms=frozenset(terms))
     base.update(over)
     w = fit(WORKLOADS["deit_s_irpe_qkv"].resized(**base))
-    say("edge", label, w.qkv_shape)
+    say("edge", label, terms, w.qkv_shape)
     compare(w, make_inputs(w, sigma=1.0, seed=6000), dev)
 
 
