@@ -22,6 +22,7 @@ import csv
 import glob
 import hashlib
 import os
+import re
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,15 +38,33 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+_FWD = re.compile(r"_ZN3rpe14rpe_fwd_kernelI(DF16b|f)Li(\d+)ELi(\d)ELj(\d)ELb(\d)EEEvNS_6ParamsE")
+_MODES = {"0": "none", "1": "bias", "2": "contextual"}
+
+
+def fwd_name(name):
+    """Readable name of a forward-kernel instance, or None."""
+    m = _FWD.search(name)
+    if not m:
+        return None
+    dt, d, mode, terms, wide = m.groups()
+    t = "".join(c for bit, c in ((1, "K"), (2, "Q"), (4, "V")) if int(terms) & bit)
+    return (f"rpe_fwd_kernel<{'bf16' if dt == 'DF16b' else 'fp32'}, d{d}, {_MODES[mode]}"
+            f"{' ' + t if t else ''}{', wide rows' if wide == '1' else ''}>")
+
+
 def demangle(names):
+    own = [fwd_name(n) for n in names]
+    if all(own):
+        return own
     try:
         r = subprocess.run(["c++filt"], input="\n".join(names), stdout=subprocess.PIPE, text=True, timeout=10)
         out = r.stdout.splitlines()
         if len(out) == len(names):
-            return out
+            return [o if f is None else f for o, f in zip(out, own)]
     except Exception:
         pass
-    return list(names)
+    return [n if f is None else f for n, f in zip(names, own)]
 
 
 def _one(pattern, d):
