@@ -122,6 +122,11 @@ int main(int argc, char** argv) {
     REQUIRE(p.first_tail * rpe::kBlockSlots <= (p.R - 1) * p.Wp &&
             (p.R - 1) * p.Wp < (p.first_tail + 1) * rpe::kBlockSlots);
     REQUIRE(p.first_tail < p.grid_blocks);
+    if (p.rk_lds) {  // rK tiles fit the row area, at most 3 (the kernel's register batch), bf16
+      REQUIRE(ctx && (d.terms & RPE_TERM_K) && d.dtype == RPE_BF16 && p.nbt <= 3);
+      REQUIRE(p.nbt * rpe::kRowTile * p.D * p.elem_bytes <= p.NW * rpe::kRowTile * p.p_tab * p.gsz);
+      REQUIRE(p.off_tab % 16 == 0);
+    }
     REQUIRE(p.Wp >= p.C && p.Wp <= rpe::kMaxWp && (1 << p.lwp) == p.Wp && p.Wp >= 4);
     REQUIRE(p.grid_blocks * rpe::kBlockSlots >= p.R * p.Wp);
     REQUIRE(p.n_rt * rpe::kRowTile >= p.T && p.n_qc * p.NW >= p.n_rt);

@@ -254,10 +254,12 @@ rpe_fwd_kernel(Params p) {
     for (int kk = 0; kk < KS; ++kk) qf[kk] = qvalid ? qg[static_cast<int64_t>(qn) * D + 2 * kk + h] : 0.0f;
   }
 
-  // rK rows as the A operand of TK^T = rK Q^T, loaded straight to registers in
-  // batches of KB 32-row tiles; the first batch is issued here, with Q, so its
-  // latency overlaps the prologue.  Rows past nb read row 0 (their scores land
-  // in row-area columns that are never gathered).
+  // rK rows as the A operand of TK^T = rK Q^T.  Small tables (p.rk_lds) are
+  // copied once per workgroup into the key-term row area, which is free until
+  // the scores are written; larger ones are loaded straight to registers, per
+  // wave, in batches of KB 32-row tiles.  Either way the loads are issued here,
+  // with Q, so their latency overlaps the prologue.  Rows past nb read row 0
+  // (their scores land in row-area columns that are never gathered).
   constexpr int KB = BF ? 3 : 1;
   const DT* rkt = reinterpret_cast<const DT*>(p.rk) + head * p.tab_head_stride;
   bf16x8 rka[TK && BF ? KB : 1][BF ? KS : 1];
@@ -278,7 +280,7 @@ rpe_fwd_kernel(Params p) {
       }
     }
   };
-  load_rk(0);
+  if (!p.rk_lds) load_rk(0);
 
   // ---- the block stream: [key/value blocks][rV tiles]
   const int n_vt = TV ? p.nbt : 0;
@@ -326,8 +328,23 @@ rpe_fwd_kernel(Params p) {
     }
   };
 
+  // ---- rK tiles into the row area (same swizzled layout as the ring tiles)
+  if constexpr (TK) {
+    if (p.rk_lds) {
+      const uint32_t lds_tab = lds_ring - p.off_stage + p.off_tab;
+      for (int ii = wid; ii < p.nbt * IPB; ii += NW) {
+        const int t = ii / IPB, i = ii - t * IPB;
+        const int row = i * RPI + lane / CPR;
+        const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
+        const int b = kRowTile * t + row;
+        dma16(reinterpret_cast<const char*>(rkt) + static_cast<uint32_t>(b < p.nb ? b : 0) * RB + cb,
+              lds_tab + t * TILE + i * 1024);
+      }
+    }
+  }
+
   // ---- start the ring now (the prologue below overlaps its latency); the Q
-  // loads above are older, so waiting for element 0 also covers them.
+  // and rK loads above are older, so waiting for element 0 also covers them.
   int st_cur = 0, st_iss = 0;
   for (int f = 0; f < ST - 1 && f < L; ++f) {
     issue(f, st_iss);
@@ -348,7 +365,9 @@ rpe_fwd_kernel(Params p) {
         } else if (p.n_thr >= 0) {
           const int ax = x < 0 ? -x : x;
           int cnt = 0;
-          for (int k = 0; k < p.n_thr; ++k) cnt += p.thr[k] <= ax ? 1 : 0;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) cnt += (k < p.n_thr && p.thr[k] <= ax) ? 1 : 0;
+          for (int k = 16; k < p.n_thr; ++k) cnt += p.thr[k] <= ax ? 1 : 0;
           g = x < 0 ? -cnt : cnt;
         } else {
           g = axis_index(x, p.map, p.rounding, p.alpha, p.beta, p.gamma);
@@ -486,7 +505,11 @@ rpe_fwd_kernel(Params p) {
   // two blocks); cqb the same for the query-term scores (fp32).
   const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab * GSZ : p.off_tab;
   const int w_delta = TV ? p.off_w - p.off_tab : 0;   // byte distance gather target -> weight sums
-  lds_barrier();  // prologue tables visible (ring loads stay in flight)
+  if constexpr (TK) {
+    // this wave's rK copies are older than its ring loads
+    if (p.rk_lds) wait_vmcnt_floor((L < ST - 1 ? L : ST - 1) * lpe);
+  }
+  lds_barrier();  // prologue tables (and rK copies) visible; ring loads stay in flight
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
 #pragma unroll
@@ -497,17 +520,13 @@ rpe_fwd_kernel(Params p) {
       for (int i = 0; i < 4; ++i) {
         const int s = 8 * j + 4 * h + i;
         const int xj = WIDE ? 32 * ph + s : (s & (p.Wp - 1));
-        int a = p.off_neg, aq = p.off_tqn;
-        if (xj < p.C) {
-          if (!qpos) {
-            a = p.off_zero;
-            aq = p.off_tqz;
-          } else {
-            const int cpart = cx_tab[xi - xj + p.C - 1];
-            a = rowbase + cpart * GSZ;
-            aq = p.off_tq + (s * p.p_tq + cpart) * 4;
-          }
-        }
+        // (branch-free so that the 16 table reads overlap)
+        int xx = xi - xj + p.C - 1;
+        xx = xx < 0 ? 0 : xx;
+        const int cpart = cx_tab[xx];
+        const bool col = xj < p.C;
+        const int a = !col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero);
+        const int aq = !col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz);
         cxb[ph][j][i] = a;
         if constexpr (TQ) cqb[ph][j][i] = aq;
       }
@@ -725,40 +744,65 @@ rpe_fwd_kernel(Params p) {
   // reads only its own rows, so no barrier is needed before the gathers).
   if constexpr (TK) {
     GT* const trow = reinterpret_cast<GT*>(smem + rowbase);
-    for (int t0 = 0; t0 < p.nbt; t0 += KB) {
-      if (t0 > 0) load_rk(t0);
+    // scores of tile t from the products in acc: lane holds bucket 32t + 8j + 4h + i.
+    // Rows hold nb entries (fp16 rows: an even count, so a pair never crosses
+    // into the next row).
+    auto to_gt = [&](float a) -> GT { return static_cast<GT>(fminf(fmaxf(a * p.c, -kGatherMax), kGatherMax)); };
+    auto store_tile = [&](int t, const GT (&v)[16]) {
+      const int b0 = kRowTile * t + 4 * h;
+      GT* const dst = trow + b0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (G16) {
+          uint32_t w0, w1;
+          __builtin_memcpy(&w0, &v[4 * j], 4);
+          __builtin_memcpy(&w1, &v[4 * j + 2], 4);
+          if (b0 + 8 * j < p.nb) reinterpret_cast<uint32_t*>(dst + 8 * j)[0] = w0;
+          if (b0 + 8 * j + 2 < p.nb) reinterpret_cast<uint32_t*>(dst + 8 * j)[1] = w1;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (b0 + 8 * j + i < p.nb) dst[8 * j + i] = v[4 * j + i];
+        }
+      }
+    };
+    if (p.rk_lds) {
+      // rK sits in the row area: every wave takes all its products (already in
+      // the row format) before any row is written
+      GT tv[KB][16];
 #pragma unroll
       for (int bt = 0; bt < KB; ++bt) {
-        const int t = t0 + bt;
-        if (t < p.nbt && active) {
-          f32x16 acc = {};
+        if (bt < p.nbt) {
+          const f32x16 acc = s_tile(smem + p.off_tab + bt * TILE, f32x16{});
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) {
-            if constexpr (BF)
-              acc = mfma32(rka[bt][kk], qb[kk], acc);
-            else
-              acc = mfma32(rkf[bt][kk], qf[kk], acc);
-          }
-          // rows hold nb entries (fp16 rows: an even count, so a pair never
-          // crosses into the next row)
-          const int b0 = kRowTile * t + 4 * h;
-          GT* const dst = trow + b0;
+          for (int k = 0; k < 16; ++k) tv[bt][k] = to_gt(acc[k]);
+        }
+      }
+      lds_barrier();
+      if (active) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            GT v4[4];
+        for (int bt = 0; bt < KB; ++bt)
+          if (bt < p.nbt) store_tile(bt, tv[bt]);
+      }
+    } else {
+      for (int t0 = 0; t0 < p.nbt; t0 += KB) {
+        if (t0 > 0) load_rk(t0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v4[i] = static_cast<GT>(fminf(fmaxf(acc[4 * j + i] * p.c, -kGatherMax), kGatherMax));
-            if constexpr (G16) {
-              uint32_t w0, w1;
-              __builtin_memcpy(&w0, &v4[0], 4);
-              __builtin_memcpy(&w1, &v4[2], 4);
-              if (b0 + 8 * j < p.nb) reinterpret_cast<uint32_t*>(dst + 8 * j)[0] = w0;
-              if (b0 + 8 * j + 2 < p.nb) reinterpret_cast<uint32_t*>(dst + 8 * j)[1] = w1;
-            } else {
+        for (int bt = 0; bt < KB; ++bt) {
+          const int t = t0 + bt;
+          if (t < p.nbt && active) {
+            f32x16 acc = {};
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (b0 + 8 * j + i < p.nb) dst[8 * j + i] = v4[i];
+            for (int kk = 0; kk < KS; ++kk) {
+              if constexpr (BF)
+                acc = mfma32(rka[bt][kk], qb[kk], acc);
+              else
+                acc = mfma32(rkf[bt][kk], qf[kk], acc);
             }
+            GT v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[k] = to_gt(acc[k]);
+            store_tile(t, v);
           }
         }
       }

@@ -238,6 +238,13 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
     }
   }
   if (best_waves < 0) return RPE_E_BUCKETS;
+  {
+    const int tile = kRowTile * best.D * best.elem_bytes;
+    // (bf16 only: the kernel holds the products of up to 3 tiles in registers)
+    best.rk_lds = (d->mode == RPE_MODE_CONTEXTUAL && (d->terms & RPE_TERM_K) && d->dtype == RPE_BF16 && best.nbt <= 3 &&
+                   best.nbt * tile <= best.NW * kRowTile * best.p_tab * best.gsz && best.off_tab % 16 == 0)
+                      ? 1 : 0;
+  }
   if (best.n_wg > 0x7fffffff) return RPE_E_SHAPE;  // workgroup ids are 32-bit in the kernel
   *p = best;
   return RPE_OK;

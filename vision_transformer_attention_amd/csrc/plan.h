@@ -94,6 +94,7 @@ struct Params {
   int dtype, mode;
   uint32_t terms;
   int elem_bytes;
+  int rk_lds;               // key term: rK (<= 3 tiles) is copied into the row area once per workgroup
   int n_thr;                // piecewise map: number of thresholds, -1: evaluate g on the device
   int16_t thr[kMaxThresholds];
 };
