@@ -192,6 +192,15 @@ rpe_fwd_kernel(Params p) {
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
+  // The launch parameters the prologue needs, read into scalar registers in one
+  // batch: left to itself the compiler loads each just before its first use and
+  // waits for each in turn.
+  asm volatile("" ::"s"(p.n_wg), "s"(p.n_qc), "s"(p.U), "s"(p.H), "s"(p.wins_per_row), "s"(p.M), "s"(p.gw),
+               "s"(p.C), "s"(p.P), "s"(p.R), "s"(p.T), "s"(p.N), "s"(p.n_rt));
+  asm volatile("" ::"s"(p.Wp), "s"(p.lwp), "s"(p.prefix_block), "s"(p.prefix_in_tail), "s"(p.nb), "s"(p.nbt),
+               "s"(p.stages), "s"(p.n_blocks), "s"(p.rk_lds), "s"(p.off_stage), "s"(p.off_tab));
+  asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.rk), "s"(p.tab_head_stride));
+
   const int nth = blockDim.x;
   const int NW = nth >> 6;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r32 = lane & 31;
@@ -512,24 +521,38 @@ rpe_fwd_kernel(Params p) {
   lds_barrier();  // prologue tables (and rK copies) visible; ring loads stay in flight
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
+  {
+    // all 16 (32) table reads first, unconditionally (the empty asm keeps the
+    // compiler from moving each read under its own branch), then the selects
+    int cp[NPH][4][4];
 #pragma unroll
-  for (int ph = 0; ph < NPH; ++ph)
+    for (int ph = 0; ph < NPH; ++ph)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = 8 * j + 4 * h + i;
-        const int xj = WIDE ? 32 * ph + s : (s & (p.Wp - 1));
-        // (branch-free so that the 16 table reads overlap)
-        int xx = xi - xj + p.C - 1;
-        xx = xx < 0 ? 0 : xx;
-        const int cpart = cx_tab[xx];
-        const bool col = xj < p.C;
-        const int a = !col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero);
-        const int aq = !col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz);
-        cxb[ph][j][i] = a;
-        if constexpr (TQ) cqb[ph][j][i] = aq;
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int s = 8 * j + 4 * h + i;
+          const int xj = WIDE ? 32 * ph + s : (s & (p.Wp - 1));
+          int xx = xi - xj + p.C - 1;
+          xx = xx < 0 ? 0 : xx;
+          cp[ph][j][i] = cx_tab[xx];
+          asm volatile("" : "+v"(cp[ph][j][i]));
+        }
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 8 * j + 4 * h + i;
+          const int xj = WIDE ? 32 * ph + s : (s & (p.Wp - 1));
+          const int cpart = cp[ph][j][i];
+          const bool col = xj < p.C;
+          cxb[ph][j][i] = !col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero);
+          if constexpr (TQ)
+            cqb[ph][j][i] = !col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz);
+        }
+  }
   (void)cqb;
   // row part: ry(yq - y) at ry_tab[yq - y + R - 1]
   const int* __restrict__ ryt = ry_tab + (qpos ? yi : 0) + p.R - 1;
