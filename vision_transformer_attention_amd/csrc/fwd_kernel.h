@@ -60,6 +60,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -315,6 +316,18 @@ rpe_fwd_kernel(Params p) {
     if (p.prefix_in_tail) n = (y == p.R - 1 && x >= p.C && x - p.C < p.P) ? x - p.C : n;
     return n;
   };
+  // Interior grid blocks (rows < R-1, Wp <= 32): a slot's column is the same in
+  // every block and its row advances by 32/Wp grid rows, so the byte offset of
+  // this wave's first instruction (i = wid) is ioff0 + block * idoff.
+  uint32_t ioff0 = 0, idoff = 0;
+  if constexpr (!WIDE) {
+    const int row = wid * RPI + lane / CPR;
+    const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
+    const int x = row & (p.Wp - 1), y0 = row >> p.lwp;
+    const bool col = x < p.C;
+    ioff0 = static_cast<uint32_t>(col ? wbase + y0 * rowstride + x : wbase) * RB + cb;
+    idoff = col ? static_cast<uint32_t>((kBlockSlots >> p.lwp) * rowstride * RB) : 0u;
+  }
   // Copy 32 rows into a swizzled row-major tile: instruction i covers rows
   // [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR with
   // global chunk (l % CPR) ^ (row % CPR).
@@ -325,7 +338,10 @@ rpe_fwd_kernel(Params p) {
       const int row = i * RPI + lane / CPR;
       const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
       if (f < nblk) {
-        const uint32_t off = static_cast<uint32_t>(slot_n(f, row)) * RB + cb;
+        const int gb = f - p.prefix_block;
+        const uint32_t off = (!WIDE && i == wid && gb >= 0 && gb < p.first_tail)
+                                 ? ioff0 + static_cast<uint32_t>(gb) * idoff
+                                 : static_cast<uint32_t>(slot_n(f, row)) * RB + cb;
         dma16(kgb + off, kt + i * 1024);
         dma16(vgb + off, vt + i * 1024);
       } else {
@@ -456,6 +472,32 @@ rpe_fwd_kernel(Params p) {
   f32x16 oacc[DTL];
 #pragma unroll
   for (int c = 0; c < DTL; ++c) oacc[c] = f32x16{};
+  // bf16: O^T += V^T P^T with P already packed, pk[kk] = the B operand of step kk
+  auto pv_packed = [&](const char* tile, const bf16x8 (&pk)[2]) {
+    if constexpr (BF) {
+      const int g16 = lane >> 4, i16 = lane & 15;
+      const int m = i16 >> 2, a = i16 & 3;
+      const int dsub = (g16 & 1) * 16;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int row0 = 16 * kk + 4 * (g16 >> 1) + m, row1 = row0 + 8;
+#pragma unroll
+        for (int c = 0; c < DTL; ++c) {
+          int col = 32 * c + dsub + 4 * a;
+          if (col >= D) col = 0;
+          const int cb = col * 2;
+          const int o0 = row0 * RB + (((cb >> 4) ^ (row0 & (CPR - 1))) << 4) + (cb & 15);
+          const int o1 = row1 * RB + (((cb >> 4) ^ (row1 & (CPR - 1))) << 4) + (cb & 15);
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tile + o0));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tile + o1));
+          bf16x8 av;
+          __builtin_memcpy(&av, &v0, 8);
+          __builtin_memcpy(reinterpret_cast<char*>(&av) + 8, &v1, 8);
+          oacc[c] = mfma32(av, pk[kk], oacc[c]);
+        }
+      }
+    }
+  };
   auto pv_tile = [&](const char* tile, const float (&pv)[4][4], bool split) {
     if constexpr (BF) {
       const int g16 = lane >> 4, i16 = lane & 15;
@@ -522,8 +564,13 @@ rpe_fwd_kernel(Params p) {
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
   {
-    // all 16 (32) table reads first, unconditionally (the empty asm keeps the
-    // compiler from moving each read under its own branch), then the selects
+    // Key column of entry (j, i) at phase ph: xj = (32 ph + 8j + 4h + i) & (Wp-1)
+    // = xu + hx with a wave-uniform part xu = ((32 ph + 8j) & (Wp-1)) + i and the
+    // lane part hx = 4h & (Wp-1) (no carries: Wp >= 4 and 8j has no low bits).
+    // All table reads are issued first, unconditionally (the empty asm keeps the
+    // compiler from moving each read under its own branch), then the selects.
+    const int hx = (4 * h) & (p.Wp - 1);
+    const int bx = xi + p.C - 1 - hx;        // xi - xj + C - 1 = bx - xu
     int cp[NPH][4][4];
 #pragma unroll
     for (int ph = 0; ph < NPH; ++ph)
@@ -531,11 +578,9 @@ rpe_fwd_kernel(Params p) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int s = 8 * j + 4 * h + i;
-          const int xj = WIDE ? 32 * ph + s : (s & (p.Wp - 1));
-          int xx = xi - xj + p.C - 1;
-          xx = xx < 0 ? 0 : xx;
-          cp[ph][j][i] = cx_tab[xx];
+          const int xu = ((32 * ph + 8 * j) & (p.Wp - 1)) + i;
+          const int xx = bx - xu;
+          cp[ph][j][i] = cx_tab[xx < 0 ? 0 : xx];
           asm volatile("" : "+v"(cp[ph][j][i]));
         }
 #pragma unroll
@@ -545,9 +590,9 @@ rpe_fwd_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 8 * j + 4 * h + i;
-          const int xj = WIDE ? 32 * ph + s : (s & (p.Wp - 1));
+          const int xu = ((32 * ph + 8 * j) & (p.Wp - 1)) + i;
           const int cpart = cp[ph][j][i];
-          const bool col = xj < p.C;
+          const bool col = hx < p.C - xu;   // xj < C
           cxb[ph][j][i] = !col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero);
           if constexpr (TQ)
             cqb[ph][j][i] = !col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz);
@@ -642,16 +687,37 @@ rpe_fwd_kernel(Params p) {
       return row_max2(bm);
     };
     float pr[4][4];
+    bf16x8 pk[2];          // bf16: P packed as the B operands of the two PV steps
     float bsum = 0.0f;
+    // Weights of the block and this lane's part of the row sum.  bf16, narrow
+    // rows: P is packed here and the sum adds the bf16-rounded weights (the ones
+    // the PV product uses) pairwise with v_dot2 against (1, 1).
     auto weights = [&]() {
       bsum = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[j][i] = __builtin_amdgcn_exp2f(x[j][i]);
-          bsum += pr[j][i];
+        for (int i = 0; i < 4; ++i) pr[j][i] = __builtin_amdgcn_exp2f(x[j][i]);
+      if constexpr (BF && !WIDE) {
+        const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pk[kk][i] = static_cast<__bf16>(pr[2 * kk][i]);
+            pk[kk][4 + i] = static_cast<__bf16>(pr[2 * kk + 1][i]);
+          }
+          bf16x2 pr2[4];
+          __builtin_memcpy(pr2, &pk[kk], 16);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bsum = __builtin_amdgcn_fdot2_f32_bf16(pr2[q], one2, bsum, false);
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bsum += pr[j][i];
+      }
     };
     if constexpr (FIRST) {
       // every block holds at least one real key, so the block maximum is finite
@@ -698,7 +764,12 @@ rpe_fwd_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) atomicAdd(reinterpret_cast<float*>(smem + ab[j][i] + w_delta), pr[j][i]);
     }
-    pv_tile(vtile, pr, false);
+    // (wide rows run at low occupancy, where converting P inside the PV loop
+    // schedules better)
+    if constexpr (BF && !WIDE)
+      pv_packed(vtile, pk);
+    else
+      pv_tile(vtile, pr, false);
   };
   // phase dispatch (a 64-slot grid row spans two blocks)
   auto process = [&](auto interior_c, auto first_c, const char* kt, const char* vt, int gblk, bool pre,
