@@ -135,7 +135,8 @@ int main(int argc, char** argv) {
       const int rt0 = qc * p.n_rt / p.n_qc, rt1 = (qc + 1) * p.n_rt / p.n_qc;
       REQUIRE(rt1 - rt0 <= p.NW && rt1 >= rt0);
     }
-    REQUIRE(p.n_wg == p.n_units * p.n_qc);
+    REQUIRE(p.upw >= 1 && p.U % p.upw == 0 && p.n_wg * p.upw == p.n_units * p.n_qc);
+    if (p.upw > 1) REQUIRE(d.mode != RPE_MODE_CONTEXTUAL && p.n_qc == 1 && p.U > 1 && p.Wp != 64);
     REQUIRE(p.nbt * rpe::kRowTile >= p.nb);
     REQUIRE(p.T == p.P + p.R * p.C);
     REQUIRE(p.N == p.P + d.grid_h * d.grid_w);

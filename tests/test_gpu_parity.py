@@ -306,6 +306,32 @@ def test_deterministic(dev):
 
 # ------------------------------------------------------------------------------ full sizes
 
+# Shapes with more small windows than resident workgroups: the planner then has
+# each workgroup walk several consecutive windows of one (batch, head), taking
+# each window's queries through the load ring.  (label, workload, batch, head
+# and window samples checked against the oracle)
+_SW = WORKLOADS["swin_t_w7"]
+MULTI_UNIT = [
+    ("bias, 4x4 windows, 2 per workgroup", _SW.resized(batch=3, heads=4, grid_h=64, grid_w=64, window=4),
+     [0, 2], [0, 3], [0, 1, 2, 3, 130, 255]),
+    ("no position, 4x4 windows", _SW.resized(batch=3, heads=4, grid_h=64, grid_w=64, window=4, mode="none",
+                                             map="swin"), [1], [0, 2], [0, 1, 77, 255]),
+    ("fp32 d16 bias, 4x4 windows", WORKLOADS["swin_tiny"].resized(batch=3, heads=4, grid_h=64, grid_w=64),
+     [0, 2], [1, 3], [0, 1, 200, 255]),
+    ("bias, 8x8 windows (two key blocks)", _SW.resized(batch=16, heads=3, grid_h=64, grid_w=64, window=8),
+     [0, 15], [0, 2], [0, 1, 2, 3, 62, 63]),
+    ("bias, 10x10 windows (4 waves, two query elements, 4 per workgroup)",
+     _SW.resized(batch=16, heads=3, grid_h=80, grid_w=80, window=10), [0, 15], [0, 2], [0, 1, 2, 3, 4, 63]),
+]
+
+
+@pytest.mark.parametrize("label,w,bs,hs,units", MULTI_UNIT)
+def test_multi_unit_workgroups(dev, label, w, bs, hs, units):
+    w = fit(w) if w.mode != "none" else w
+    say("multi-unit", label, w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=9000), dev, batch_sel=bs, heads_sel=hs, units=units)
+
+
 FULL_SAMPLES = {
     # workload: (batch indices, head indices) checked against the oracle
     "swin_tiny": (None, None),

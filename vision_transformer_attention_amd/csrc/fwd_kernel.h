@@ -162,8 +162,8 @@ using bool_c = std::integral_constant<bool, B>;
 
 }  // namespace
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE>
-__global__ void __launch_bounds__(kThreadsMax) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE, D))))
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI>
+__global__ void __launch_bounds__(kThreadsMax) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE, D, MULTI))))
 rpe_fwd_kernel(Params p) {
   constexpr bool BF = std::is_same<DT, __bf16>::value;
   constexpr bool CTX = MODE == RPE_MODE_CONTEXTUAL;
@@ -214,13 +214,24 @@ rpe_fwd_kernel(Params p) {
   const uint32_t nwg = static_cast<uint32_t>(p.n_wg);
   const uint32_t per = nwg >> 3, rem = nwg & 7u, xcd = bid & 7u, idx = bid >> 3;
   const uint32_t task = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  const uint32_t unit = task / static_cast<uint32_t>(p.n_qc);
-  const int qc = static_cast<int>(task - unit * static_cast<uint32_t>(p.n_qc));
-  const uint32_t bh = unit / static_cast<uint32_t>(p.U);
-  const int w_img = static_cast<int>(unit - bh * static_cast<uint32_t>(p.U));
+  // A workgroup takes p.upw consecutive units of one (batch, head) (p.upw > 1
+  // only for small units without contextual terms, n_qc = 1 then).
+  const uint32_t ugrp = task / static_cast<uint32_t>(p.n_qc);
+  const int qc = static_cast<int>(task - ugrp * static_cast<uint32_t>(p.n_qc));
+  const uint32_t unit0 = ugrp * static_cast<uint32_t>(p.upw);
+  const uint32_t bh = unit0 / static_cast<uint32_t>(p.U);
+  const int w_img0 = static_cast<int>(unit0 - bh * static_cast<uint32_t>(p.U));
   const int head = static_cast<int>(bh % static_cast<uint32_t>(p.H));
-  const int wy = w_img / p.wins_per_row, wx = w_img - wy * p.wins_per_row;
-  const int wbase = p.M ? (wy * p.M) * p.gw + wx * p.M : p.P;   // N index of the unit's grid (0,0)
+  // MULTI instances serve p.upw > 1 (the launch picks them); the others one unit
+  constexpr bool multi = MULTI;
+  static_assert(!MULTI || MODE != RPE_MODE_CONTEXTUAL, "multi-unit workgroups have no contextual terms");
+  const int upw = MULTI ? p.upw : 1;
+  // N index of grid (0,0) of the unit with window index w
+  auto wbase_of = [&](int w) -> int {
+    const int wy = w / p.wins_per_row, wx = w - wy * p.wins_per_row;
+    return p.M ? (wy * p.M) * p.gw + wx * p.M : p.P;
+  };
+  const int wbase = wbase_of(w_img0);
   const int rowstride = p.M ? p.gw : p.C;
   const int rt0 = qc * p.n_rt / p.n_qc, rt1 = (qc + 1) * p.n_rt / p.n_qc;
   const bool active = rt0 + wid < rt1;
@@ -251,17 +262,18 @@ rpe_fwd_kernel(Params p) {
   // Q as the B operand of S^T = K Q^T: lane holds Q[row r32][k-slice h of each step].
   bf16x8 qb[BF ? KS : 1];
   float qf[BF ? 1 : KS];
+  // (multi-unit workgroups take Q through the ring instead)
   if constexpr (BF) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int d0 = 16 * kk + 8 * h;
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (qvalid && d0 < D) u = ld16(qg + static_cast<int64_t>(qn) * D + d0);
+      if (!multi && qvalid && d0 < D) u = ld16(qg + static_cast<int64_t>(qn) * D + d0);
       qb[kk] = as_bf16x8(u);
     }
   } else {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = qvalid ? qg[static_cast<int64_t>(qn) * D + 2 * kk + h] : 0.0f;
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = (!multi && qvalid) ? qg[static_cast<int64_t>(qn) * D + 2 * kk + h] : 0.0f;
   }
 
   // rK rows as the A operand of TK^T = rK Q^T.  Small tables (p.rk_lds) are
@@ -292,10 +304,13 @@ rpe_fwd_kernel(Params p) {
   };
   if (!p.rk_lds) load_rk(0);
 
-  // ---- the block stream: [key/value blocks][rV tiles]
+  // ---- the block stream: per unit [Q tiles (multi-unit only)][key/value blocks]
+  // [rV tiles]; a Q element carries 64 query rows (32 in each half of a stage)
   const int n_vt = TV ? p.nbt : 0;
   const int nblk = p.n_blocks;
-  const int L = nblk + n_vt;
+  const int nqe = multi ? (NW + 1) >> 1 : 0;
+  const int epu = nqe + nblk + n_vt;            // elements per unit
+  const int L = upw * epu;
   const int ST = p.stages;
   // direct-to-LDS instructions this wave issues per 32-row tile; every stream
   // element costs two per instruction (rV tiles are copied into both halves of
@@ -305,47 +320,58 @@ rpe_fwd_kernel(Params p) {
   char* const ring = smem + p.off_stage;
   const uint32_t lds_ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)smem)) + p.off_stage;
   // N index of a key slot; padding slots read a valid token (their values are masked)
-  auto slot_n = [&](int blk, int s) -> int {
+  auto slot_n = [&](int blk, int s, int wb) -> int {
     if (p.prefix_block) {
-      if (blk == 0) return s < p.P ? s : wbase;
+      if (blk == 0) return s < p.P ? s : wb;
       blk -= 1;
     }
     const int sigma = blk * kBlockSlots + s;
     const int y = sigma >> p.lwp, x = sigma & (p.Wp - 1);
-    int n = (y < p.R && x < p.C) ? wbase + y * rowstride + x : wbase;
+    int n = (y < p.R && x < p.C) ? wb + y * rowstride + x : wb;
     if (p.prefix_in_tail) n = (y == p.R - 1 && x >= p.C && x - p.C < p.P) ? x - p.C : n;
     return n;
   };
   // Interior grid blocks (rows < R-1, Wp <= 32): a slot's column is the same in
   // every block and its row advances by 32/Wp grid rows, so the byte offset of
-  // this wave's first instruction (i = wid) is ioff0 + block * idoff.
+  // this wave's first instruction (i = wid) is (wbase * RB + ioff0) + block * idoff.
   uint32_t ioff0 = 0, idoff = 0;
   if constexpr (!WIDE) {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
     const int x = row & (p.Wp - 1), y0 = row >> p.lwp;
     const bool col = x < p.C;
-    ioff0 = static_cast<uint32_t>(col ? wbase + y0 * rowstride + x : wbase) * RB + cb;
+    ioff0 = static_cast<uint32_t>(col ? y0 * rowstride + x : 0) * RB + cb;
     idoff = col ? static_cast<uint32_t>((kBlockSlots >> p.lwp) * rowstride * RB) : 0u;
   }
   // Copy 32 rows into a swizzled row-major tile: instruction i covers rows
   // [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR with
   // global chunk (l % CPR) ^ (row % CPR).
-  auto issue = [&](int f, int stage) {
+  // element loc of unit k (k counts this workgroup's units) into ring stage `stage`
+  auto issue = [&](int k, int loc, int stage) {
     const uint32_t kt = lds_ring + stage * (2 * TILE);
     const uint32_t vt = kt + TILE;
+    const int wb = (MULTI && k != 0) ? wbase_of(w_img0 + k) : wbase;
     for (int i = wid; i < IPB; i += NW) {
       const int row = i * RPI + lane / CPR;
       const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
-      if (f < nblk) {
+      if (MULTI && loc < nqe) {
+        // query rows 64 loc + row (first half) and 64 loc + 32 + row (second half)
+        auto q_off = [&](int qi) -> uint32_t {
+          const int y = qi / p.C, x = qi - (qi / p.C) * p.C;
+          return static_cast<uint32_t>(qi < p.T ? wb + y * rowstride + x : wb) * RB + cb;
+        };
+        dma16(reinterpret_cast<const char*>(qg) + q_off(64 * loc + row), kt + i * 1024);
+        dma16(reinterpret_cast<const char*>(qg) + q_off(64 * loc + 32 + row), vt + i * 1024);
+      } else if (loc < nqe + nblk) {
+        const int f = loc - nqe;
         const int gb = f - p.prefix_block;
         const uint32_t off = (!WIDE && i == wid && gb >= 0 && gb < p.first_tail)
-                                 ? ioff0 + static_cast<uint32_t>(gb) * idoff
-                                 : static_cast<uint32_t>(slot_n(f, row)) * RB + cb;
+                                 ? static_cast<uint32_t>(wb) * RB + ioff0 + static_cast<uint32_t>(gb) * idoff
+                                 : static_cast<uint32_t>(slot_n(f, row, wb)) * RB + cb;
         dma16(kgb + off, kt + i * 1024);
         dma16(vgb + off, vt + i * 1024);
       } else {
-        const int b = kRowTile * (f - nblk) + row;
+        const int b = kRowTile * (loc - nqe - nblk) + row;
         const uint32_t off = static_cast<uint32_t>(b < p.nb ? b : 0) * RB + cb;
         dma16(rvb + off, kt + i * 1024);
         dma16(rvb + off, vt + i * 1024);
@@ -371,10 +397,19 @@ rpe_fwd_kernel(Params p) {
   // ---- start the ring now (the prologue below overlaps its latency); the Q
   // and rK loads above are older, so waiting for element 0 also covers them.
   int st_cur = 0, st_iss = 0;
-  for (int f = 0; f < ST - 1 && f < L; ++f) {
-    issue(f, st_iss);
+  int iss_k = 0, iss_loc = 0;   // unit and position of the next element to issue
+  auto issue_next = [&]() {
+    issue(iss_k, iss_loc, st_iss);
     st_iss = st_iss + 1 == ST ? 0 : st_iss + 1;
-  }
+    ++iss_loc;
+    if constexpr (MULTI) {
+      if (iss_loc == epu) {
+        iss_loc = 0;
+        ++iss_k;
+      }
+    }
+  };
+  for (int f = 0; f < ST - 1 && f < L; ++f) issue_next();
 
   // ---- prologue: per-axis tables, guards, bias table, weight sums, staged rQ.
   // ry holds byte offsets of the row part, (g(dy)+H)*S*GSZ; cx holds g(dx)+H.
@@ -823,8 +858,12 @@ rpe_fwd_kernel(Params p) {
     wait_vmcnt_floor(ahead * lpe);
     lds_barrier();
     if (e + ST - 1 < L) {
-      issue(e + ST - 1, st_iss);
-      st_iss = st_iss + 1 == ST ? 0 : st_iss + 1;
+      if constexpr (MULTI) {
+        issue_next();
+      } else {
+        issue(0, e + ST - 1, st_iss);
+        st_iss = st_iss + 1 == ST ? 0 : st_iss + 1;
+      }
     }
     const int s = st_cur;
     st_cur = st_cur + 1 == ST ? 0 : st_cur + 1;
@@ -912,105 +951,136 @@ rpe_fwd_kernel(Params p) {
     for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(qf[kk]));
   }
 
-  int e = 0;
-  // key/value blocks: the first one sets the running maximum
-  {
-    int gb = 0;
-    {
-      const int s = step(e);
-      if constexpr (TQ) {
-        block_query_scores(ktile_of(s));
-        lds_barrier();
-      }
-      int ry0[4];
-      load_ry(0, ry0);
-      if (active) {
-        if (p.prefix_block)
-          process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), -1, true, ry0);
-        else if (p.first_tail > 0)
-          process(bool_c<true>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false, ry0);
-        else
-          process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false, ry0);
-      }
-      if (!p.prefix_block) gb = 1;
-      ++e;
-    }
-    // interior blocks: the row parts of the next block are read one block ahead
-    int ryn[4];
-    load_ry(gb, ryn);
-    for (; gb < p.first_tail; ++gb, ++e) {
-      const int s = step(e);
-      int ryc[4];
+  // Q rows of this wave from a Q element of the ring (multi-unit workgroups):
+  // the same swizzled layout and lane mapping as the K operand
+  auto read_q = [&](const char* tile) {
+    const int sw = r32 & (CPR - 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ryc[j] = ryn[j];
-      load_ry(gb + 1, ryn);
-      if constexpr (TQ) {
-        block_query_scores(ktile_of(s));
-        lds_barrier();
-      }
-      if (active) process(bool_c<true>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryc);
-    }
-    for (; gb < p.grid_blocks; ++gb, ++e) {
-      const int s = step(e);
-      if constexpr (TQ) {
-        block_query_scores(ktile_of(s));
-        lds_barrier();
-      }
-      if (active) process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryn);
-    }
-  }
-  // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
-  if constexpr (TV) {
-    for (; e < L; ++e) {
-      const int s = step(e);
-      if (active) {
-        const int t = e - nblk;
-        const float* wrow = reinterpret_cast<const float*>(smem + rowbase + w_delta);
-        float wv[4][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int b = kRowTile * t + 8 * j + 4 * h + i;
-            wv[j][i] = b < p.nb ? wrow[b] : 0.0f;
-          }
-        pv_tile(vtile_of(s), wv, true);
+    for (int kk = 0; kk < KS; ++kk) {
+      if constexpr (BF) {
+        const int c = 2 * kk + h;
+        qb[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(tile + r32 * RB + ((c ^ sw) << 4)));
+      } else {
+        const int col = (2 * kk + h) * 4;
+        qf[kk] = *reinterpret_cast<const float*>(tile + r32 * RB + (((col >> 4) ^ sw) << 4) + (col & 15));
       }
     }
-  }
+  };
 
-  if (!qvalid) return;
-  const float l = l_part + __shfl_xor(l_part, 32);
-  const float inv = 1.0f / l;
-  DT* orow = og + static_cast<int64_t>(qn) * D;
+  int e = 0;
+  for (int k = 0; k < upw; ++k) {
+    int qnk = qn;
+    if (multi) {
+      const int wbk = wbase_of(w_img0 + k);
+      qnk = qpos ? wbk + yi * rowstride + xi : (qvalid ? qi : 0);
+      for (int qe = 0; qe < nqe; ++qe, ++e) {
+        const int s = step(e);
+        if ((wid >> 1) == qe) read_q(ktile_of(s) + (wid & 1) * TILE);
+      }
+      l_part = 0.0f;
 #pragma unroll
-  for (int c = 0; c < DTL; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d0 = 32 * c + 8 * j + 4 * h;
-      if (d0 < D) {
-        if constexpr (BF) {
-          bf16x4 o4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(oacc[c][4 * j + i] * inv);
-          *reinterpret_cast<bf16x4*>(orow + d0) = o4;
-        } else {
-          f32x4 o4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o4[i] = oacc[c][4 * j + i] * inv;
-          *reinterpret_cast<f32x4*>(orow + d0) = o4;
+      for (int c = 0; c < DTL; ++c) oacc[c] = f32x16{};
+    }
+    // key/value blocks: the first one sets the running maximum
+    {
+      int gb = 0;
+      {
+        const int s = step(e);
+        if constexpr (TQ) {
+          block_query_scores(ktile_of(s));
+          lds_barrier();
+        }
+        int ry0[4];
+        load_ry(0, ry0);
+        if (active) {
+          if (p.prefix_block)
+            process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), -1, true, ry0);
+          else if (p.first_tail > 0)
+            process(bool_c<true>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false, ry0);
+          else
+            process(bool_c<false>{}, bool_c<true>{}, ktile_of(s), vtile_of(s), 0, false, ry0);
+        }
+        if (!p.prefix_block) gb = 1;
+        ++e;
+      }
+      // interior blocks: the row parts of the next block are read one block ahead
+      int ryn[4];
+      load_ry(gb, ryn);
+      for (; gb < p.first_tail; ++gb, ++e) {
+        const int s = step(e);
+        int ryc[4];
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) ryc[j] = ryn[j];
+        load_ry(gb + 1, ryn);
+        if constexpr (TQ) {
+          block_query_scores(ktile_of(s));
+          lds_barrier();
+        }
+        if (active) process(bool_c<true>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryc);
+      }
+      for (; gb < p.grid_blocks; ++gb, ++e) {
+        const int s = step(e);
+        if constexpr (TQ) {
+          block_query_scores(ktile_of(s));
+          lds_barrier();
+        }
+        if (active) process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryn);
+      }
+    }
+    // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
+    if constexpr (TV) {
+      for (; e < L; ++e) {
+        const int s = step(e);
+        if (active) {
+          const int t = e - nblk;
+          const float* wrow = reinterpret_cast<const float*>(smem + rowbase + w_delta);
+          float wv[4][4];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int b = kRowTile * t + 8 * j + 4 * h + i;
+              wv[j][i] = b < p.nb ? wrow[b] : 0.0f;
+            }
+          pv_tile(vtile_of(s), wv, true);
         }
       }
     }
-  if (p.lse && h == 0) p.lse[static_cast<int64_t>(bh) * p.N + qn] = (m_run + log2f(l)) * 0.6931471805599453f;
+
+    if (qvalid) {
+    const float l = l_part + __shfl_xor(l_part, 32);
+    const float inv = 1.0f / l;
+    DT* orow = og + static_cast<int64_t>(qnk) * D;
+  #pragma unroll
+    for (int c = 0; c < DTL; ++c)
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * c + 8 * j + 4 * h;
+        if (d0 < D) {
+          if constexpr (BF) {
+            bf16x4 o4;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(oacc[c][4 * j + i] * inv);
+            *reinterpret_cast<bf16x4*>(orow + d0) = o4;
+          } else {
+            f32x4 o4;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = oacc[c][4 * j + i] * inv;
+            *reinterpret_cast<f32x4*>(orow + d0) = o4;
+          }
+        }
+      }
+    if (p.lse && h == 0) p.lse[static_cast<int64_t>(bh) * p.N + qnk] = (m_run + log2f(l)) * 0.6931471805599453f;
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------------------
 // Launch dispatch.
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE>
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI>
 hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
-  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE>;
+  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, MULTI>;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   if (attr != hipSuccess) return attr;
@@ -1021,8 +1091,13 @@ hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
 
 template <typename DT, int D, int MODE, unsigned TERMS>
 hipError_t launch_fwd_t(const Params& p, hipStream_t stream) {
-  return p.Wp == 64 ? launch_fwd_w<DT, D, MODE, TERMS, true>(p, stream)
-                    : launch_fwd_w<DT, D, MODE, TERMS, false>(p, stream);
+  // (several units per workgroup only arise for units of at most 4 query tiles,
+  // so never with wide rows)
+  if constexpr (MODE != RPE_MODE_CONTEXTUAL) {
+    if (p.upw > 1 && p.Wp != 64) return launch_fwd_w<DT, D, MODE, TERMS, false, true>(p, stream);
+  }
+  return p.Wp == 64 ? launch_fwd_w<DT, D, MODE, TERMS, true, false>(p, stream)
+                    : launch_fwd_w<DT, D, MODE, TERMS, false, false>(p, stream);
 }
 
 // All mode / term instances of one (dtype, head dim).

@@ -238,6 +238,24 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
     }
   }
   if (best_waves < 0) return RPE_E_BUCKETS;
+  // Small units without contextual terms: when there are more units than
+  // resident workgroups, a workgroup takes several consecutive units of one
+  // (batch, head) (a divisor of the units per image), so that its set-up
+  // (tables, guards, column offsets) is shared and the grid fits one round.
+  best.upw = 1;
+  if (d->mode != RPE_MODE_CONTEXTUAL && best.n_qc == 1 && best.U > 1 && best.Wp != 64) {
+    const int by_regs = 4 * waves_per_simd(d->mode, d->terms, best.Wp == 64, d->head_dim, true) / best.NW;
+    const int by_lds = kMaxLdsBytes / ((best.lds_bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule);
+    const int64_t cap = static_cast<int64_t>(kNumCUs) * (by_regs < by_lds ? by_regs : by_lds);
+    if (best.n_units > cap) {
+      for (int u = 2; u <= best.U; ++u) {
+        if (best.U % u) continue;
+        best.upw = u;
+        if (best.n_units / u <= cap) break;
+      }
+    }
+    best.n_wg = best.n_units / best.upw;
+  }
   {
     const int tile = kRowTile * best.D * best.elem_bytes;
     // (bf16 only: the kernel holds the products of up to 3 tiles in registers)

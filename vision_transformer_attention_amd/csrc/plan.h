@@ -22,6 +22,7 @@ constexpr int kMaxWaves = 4;
 constexpr int kMaxStages = 4;       // deepest LDS ring of the block stream
 constexpr int kMinStages = 2;
 constexpr int kMaxLdsBytes = 160 * 1024;
+constexpr int kNumCUs = 256;        // compute units of the gfx950 part the plan is sized for
 // LDS is allocated to workgroups in granules of this many bytes.
 constexpr int kLdsGranule = 512;
 // The piecewise index g is odd and non-decreasing in |x| (iRPE page, eq. 18),
@@ -33,12 +34,14 @@ constexpr int kMaxThresholds = 64;
 // Resident waves per SIMD each forward instance is compiled for (register
 // budget 512 / waves): four for head dims up to 32 and three for 64 with only
 // the key term or a bias; wide rows (two column phases of gather offsets) and
-// the query / value terms take the larger budget of two.  The planner sizes
-// LDS to match.
-constexpr int waves_per_simd(int mode, uint32_t terms, bool wide, int head_dim) {
+// the query / value terms take the larger budget of two.  Instances whose
+// workgroups walk several units (multi) keep more state live across units:
+// three waves up to d32, else two.  The planner sizes LDS to match.
+constexpr int waves_per_simd(int mode, uint32_t terms, bool wide, int head_dim, bool multi = false) {
   return (wide || (mode == RPE_MODE_CONTEXTUAL && (terms & (RPE_TERM_Q | RPE_TERM_V)))) ? 2
-         : head_dim <= 32                                                             ? 4
-                                                                                       : 3;
+         : multi                                                                        ? (head_dim <= 32 ? 3 : 2)
+         : head_dim <= 32                                                               ? 4
+                                                                                        : 3;
 }
 
 struct Params {
@@ -73,7 +76,8 @@ struct Params {
   int NW;                 // waves per workgroup (one row tile each)
   int n_qc;               // workgroups (query chunks) per unit
   int64_t n_units;        // B * H * U
-  int64_t n_wg;           // n_units * n_qc
+  int upw;                // units per workgroup (> 1 only without contextual terms, n_qc = 1)
+  int64_t n_wg;           // n_units * n_qc / upw
   int stages;             // LDS ring depth of the block stream
   // LDS layout, byte offsets.  "Gather" entries (the per-row bucket scores of
   // the contextual key term, or the bias table, and their guard regions) are
