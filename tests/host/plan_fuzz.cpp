@@ -143,6 +143,29 @@ int main(int argc, char** argv) {
     if (p.prefix_in_tail) REQUIRE(p.P <= p.Wp - p.C);
     REQUIRE(p.prefix_block == (p.P > 0 && !p.prefix_in_tail));
   }
+  // the planner's division constants against plain division: small, power-of-two
+  // and random divisors, each with edge and random numerators
+  {
+    auto check_div = [&](uint32_t d, uint32_t x) {
+      const rpe::FastDiv f = rpe::make_fastdiv(d);
+      const uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(x) * f.m) >> 32);
+      const uint32_t q = (t + ((x - t) >> f.s1)) >> f.s2;
+      REQUIRE(q == x / d);
+    };
+    std::uniform_int_distribution<uint32_t> any(0u, 0xffffffffu);
+    for (uint32_t d = 1; d < 4200; ++d) {
+      const uint32_t xs[] = {0u, 1u, d - 1, d, d + 1, 2 * d - 1, 0x7fffffffu, 0xffffffffu, 0xfffffffeu};
+      for (uint32_t x : xs) check_div(d, x);
+      for (int k = 0; k < 64; ++k) check_div(d, any(rng));
+    }
+    for (int sft = 0; sft < 32; ++sft) {
+      const uint32_t d = 1u << sft;
+      for (uint32_t x : {0u, d - 1, d, 0xffffffffu}) check_div(d, x);
+      for (int k = 0; k < 64; ++k) check_div(d, any(rng));
+      if (d > 2) check_div(d - 1, any(rng)), check_div(d + 1, any(rng));
+    }
+    for (int k = 0; k < 200000; ++k) check_div(1u + any(rng) % 0x7fffffffu, any(rng));
+  }
   std::printf("checked %d descriptors, %d accepted, %d failures\n", n, accepted, fails);
   return fails ? 1 : 0;
 }

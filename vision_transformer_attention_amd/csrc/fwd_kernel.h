@@ -137,6 +137,12 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(base) : "memory", "m0");
 }
 
+// n / d for a launch constant d (host-made multiplier; see FastDiv).
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  const uint32_t t = __umulhi(n, f.m);
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 // Workgroup barrier that orders LDS traffic but leaves the direct-to-LDS loads
 // in flight (a plain __syncthreads would drain them).
 __device__ __forceinline__ void lds_barrier() {
@@ -198,6 +204,8 @@ rpe_fwd_kernel(Params p) {
   // waits for each in turn.
   asm volatile("" ::"s"(p.n_wg), "s"(p.n_qc), "s"(p.U), "s"(p.H), "s"(p.wins_per_row), "s"(p.M), "s"(p.gw),
                "s"(p.C), "s"(p.P), "s"(p.R), "s"(p.T), "s"(p.N), "s"(p.n_rt));
+  asm volatile("" ::"s"(p.dv_qc.m), "s"(p.dv_qc.s1), "s"(p.dv_qc.s2), "s"(p.dv_U.m), "s"(p.dv_U.s1), "s"(p.dv_U.s2),
+               "s"(p.dv_H.m), "s"(p.dv_H.s1), "s"(p.dv_H.s2));
   asm volatile("" ::"s"(p.Wp), "s"(p.lwp), "s"(p.prefix_block), "s"(p.prefix_in_tail), "s"(p.nb), "s"(p.nbt),
                "s"(p.stages), "s"(p.n_blocks), "s"(p.rk_lds), "s"(p.off_stage), "s"(p.off_tab));
   asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.rk), "s"(p.tab_head_stride));
@@ -216,24 +224,25 @@ rpe_fwd_kernel(Params p) {
   const uint32_t task = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
   // A workgroup takes p.upw consecutive units of one (batch, head) (p.upw > 1
   // only for small units without contextual terms, n_qc = 1 then).
-  const uint32_t ugrp = task / static_cast<uint32_t>(p.n_qc);
+  const uint32_t ugrp = fdiv(task, p.dv_qc);
   const int qc = static_cast<int>(task - ugrp * static_cast<uint32_t>(p.n_qc));
   const uint32_t unit0 = ugrp * static_cast<uint32_t>(p.upw);
-  const uint32_t bh = unit0 / static_cast<uint32_t>(p.U);
+  const uint32_t bh = fdiv(unit0, p.dv_U);
   const int w_img0 = static_cast<int>(unit0 - bh * static_cast<uint32_t>(p.U));
-  const int head = static_cast<int>(bh % static_cast<uint32_t>(p.H));
+  const int head = static_cast<int>(bh - fdiv(bh, p.dv_H) * static_cast<uint32_t>(p.H));
   // MULTI instances serve p.upw > 1 (the launch picks them); the others one unit
   constexpr bool multi = MULTI;
   static_assert(!MULTI || MODE != RPE_MODE_CONTEXTUAL, "multi-unit workgroups have no contextual terms");
   const int upw = MULTI ? p.upw : 1;
   // N index of grid (0,0) of the unit with window index w
   auto wbase_of = [&](int w) -> int {
-    const int wy = w / p.wins_per_row, wx = w - wy * p.wins_per_row;
+    const int wy = static_cast<int>(fdiv(static_cast<uint32_t>(w), p.dv_wpr)), wx = w - wy * p.wins_per_row;
     return p.M ? (wy * p.M) * p.gw + wx * p.M : p.P;
   };
   const int wbase = wbase_of(w_img0);
   const int rowstride = p.M ? p.gw : p.C;
-  const int rt0 = qc * p.n_rt / p.n_qc, rt1 = (qc + 1) * p.n_rt / p.n_qc;
+  const int rt0 = static_cast<int>(fdiv(static_cast<uint32_t>(qc * p.n_rt), p.dv_qc));
+  const int rt1 = static_cast<int>(fdiv(static_cast<uint32_t>((qc + 1) * p.n_rt), p.dv_qc));
   const bool active = rt0 + wid < rt1;
 
   const int64_t base = static_cast<int64_t>(bh) * p.N * D;
@@ -256,7 +265,7 @@ rpe_fwd_kernel(Params p) {
   const bool qvalid = active && qi < p.T;
   const bool qpos = qvalid && qi >= p.P;
   const int qt = qpos ? qi - p.P : 0;
-  const int yi = qt / p.C, xi = qt - (qt / p.C) * p.C;
+  const int yi = static_cast<int>(fdiv(static_cast<uint32_t>(qt), p.dv_C)), xi = qt - yi * p.C;
   const int qn = qpos ? wbase + yi * rowstride + xi : (qvalid ? qi : 0);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[row r32][k-slice h of each step].
@@ -315,7 +324,8 @@ rpe_fwd_kernel(Params p) {
   // direct-to-LDS instructions this wave issues per 32-row tile; every stream
   // element costs two per instruction (rV tiles are copied into both halves of
   // their stage), so the loads issued after an element are a simple count
-  const int my_ipb = wid < IPB ? (IPB - wid + NW - 1) / NW : 0;
+  int my_ipb = 0;
+  for (int i = wid; i < IPB; i += NW) ++my_ipb;
   const int lpe = 2 * my_ipb;
   char* const ring = smem + p.off_stage;
   const uint32_t lds_ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)smem)) + p.off_stage;
@@ -357,7 +367,7 @@ rpe_fwd_kernel(Params p) {
       if (MULTI && loc < nqe) {
         // query rows 64 loc + row (first half) and 64 loc + 32 + row (second half)
         auto q_off = [&](int qi) -> uint32_t {
-          const int y = qi / p.C, x = qi - (qi / p.C) * p.C;
+          const int y = static_cast<int>(fdiv(static_cast<uint32_t>(qi), p.dv_C)), x = qi - y * p.C;
           return static_cast<uint32_t>(qi < p.T ? wb + y * rowstride + x : wb) * RB + cb;
         };
         dma16(reinterpret_cast<const char*>(qg) + q_off(64 * loc + row), kt + i * 1024);
@@ -645,7 +655,7 @@ rpe_fwd_kernel(Params p) {
   // ---- running state of this lane's row (shared with the lane l ^ 32).
   float m_run = 0.0f;
   float l_part = 0.0f;
-  const float inv_c = 1.0f / p.c;
+  const float inv_c = p.inv_c;
   f32x16 mneg = f32x16{};   // -m_run / c, the S^T accumulator's starting value
 
   // Logit (log2 units, relative to m_run) of a pair from the LDS byte addresses of its terms.

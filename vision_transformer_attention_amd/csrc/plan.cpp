@@ -142,6 +142,17 @@ int axis_index_host(int x, int map, int rounding, double alpha, double beta, dou
   return x > 0 ? mag : -mag;
 }
 
+FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f{d, 0u, 0u, 0u};
+  if (d == 0) return f;
+  uint32_t l = 0;
+  while (l < 32 && (uint64_t{1} << l) < d) ++l;
+  f.m = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
+  f.s1 = l > 0 ? 1u : 0u;
+  f.s2 = l > 0 ? l - 1 : 0u;
+  return f;
+}
+
 int make_plan(const rpe_attn_desc* d, Params* p) {
   int st = validate(d);
   if (st != RPE_OK) return st;
@@ -264,6 +275,12 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
                       ? 1 : 0;
   }
   if (best.n_wg > 0x7fffffff) return RPE_E_SHAPE;  // workgroup ids are 32-bit in the kernel
+  best.dv_qc = make_fastdiv(static_cast<uint32_t>(best.n_qc));
+  best.dv_U = make_fastdiv(static_cast<uint32_t>(best.U));
+  best.dv_H = make_fastdiv(static_cast<uint32_t>(best.H));
+  best.dv_wpr = make_fastdiv(static_cast<uint32_t>(best.wins_per_row > 0 ? best.wins_per_row : 1));
+  best.dv_C = make_fastdiv(static_cast<uint32_t>(best.C > 0 ? best.C : 1));
+  best.inv_c = 1.0f / best.c;
   *p = best;
   return RPE_OK;
 }

@@ -44,6 +44,16 @@ constexpr int waves_per_simd(int mode, uint32_t terms, bool wide, int head_dim, 
                                                                                         : 3;
 }
 
+// Division by a launch constant d >= 1 without a divide sequence (round-down
+// multiply-high method, exact for every 32-bit n): with l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1, t = mulhi(n, m), n / d = (t + ((n - t) >> s1)) >> s2,
+// s1 = min(l, 1), s2 = max(l - 1, 0).  The planner fills these on the host; the
+// kernel's uniform quotients then take two scalar multiplies and shifts.
+struct FastDiv {
+  uint32_t d, m, s1, s2;
+};
+FastDiv make_fastdiv(uint32_t d);
+
 struct Params {
   // tensors
   const void* q; const void* k; const void* v; void* o; float* lse;
@@ -77,6 +87,8 @@ struct Params {
   int n_qc;               // workgroups (query chunks) per unit
   int64_t n_units;        // B * H * U
   int upw;                // units per workgroup (> 1 only without contextual terms, n_qc = 1)
+  FastDiv dv_qc, dv_U, dv_H, dv_wpr, dv_C;   // n_qc, U, H, wins_per_row, C
+  float inv_c;            // 1 / c
   int64_t n_wg;           // n_units * n_qc / upw
   int stages;             // LDS ring depth of the block stream
   // LDS layout, byte offsets.  "Gather" entries (the per-row bucket scores of
