@@ -242,6 +242,41 @@ def test_swin_edge(dev, label, over):
     compare(w, make_inputs(w, sigma=1.0, seed=7000), dev)
 
 
+# Mode and mapping variants on the same kernel: the iRPE bias mode on a global
+# grid with the piecewise index (shared or per-head table, with and without a
+# class token), and contextual terms inside Swin windows (both maps).
+_D = WORKLOADS["deit_s_irpe_k"]
+MODE_VARIANTS = [
+    ("iRPE bias, global 14x14 + cls, shared table", _D.resized(batch=2, heads=3, mode="bias", terms=frozenset())),
+    ("iRPE bias, global 14x14 + cls, per-head tables",
+     _D.resized(batch=2, heads=3, mode="bias", terms=frozenset(), tables_per_head=True)),
+    ("iRPE bias, global 9x13 no cls, trunc reading",
+     _D.resized(batch=2, heads=2, grid_h=9, grid_w=13, prefix=0, mode="bias", terms=frozenset(), reading="trunc")),
+    ("iRPE bias fp32 d32, global 10x10 + 2 prefix",
+     _D.resized(batch=2, heads=2, head_dim=32, grid_h=10, grid_w=10, prefix=2, mode="bias", terms=frozenset(),
+                dtype="fp32")),
+    ("iRPE bias, wide 12x40 global grid", WORKLOADS["highres_irpe_k"].resized(batch=1, heads=2, grid_h=12,
+                                                                             grid_w=40, mode="bias",
+                                                                             terms=frozenset())),
+    ("contextual K in 7x7 windows, piecewise", _D.resized(batch=2, heads=2, grid_h=14, grid_w=21, window=7,
+                                                          prefix=0)),
+    ("contextual QKV in 7x7 windows, piecewise",
+     _D.resized(batch=2, heads=2, grid_h=14, grid_w=14, window=7, prefix=0, terms=frozenset("kqv"))),
+    ("contextual QKV in 7x7 windows, Swin map, per-head tables",
+     _D.resized(batch=2, heads=3, head_dim=32, grid_h=14, grid_w=14, window=7, prefix=0, terms=frozenset("kqv"),
+                map="swin", tables_per_head=True)),
+    ("contextual K in 4x4 windows fp32 d16",
+     _D.resized(batch=2, heads=2, head_dim=16, grid_h=8, grid_w=12, window=4, prefix=0, dtype="fp32")),
+]
+
+
+@pytest.mark.parametrize("label,w", MODE_VARIANTS)
+def test_mode_variants(dev, label, w):
+    w = fit(w)
+    say("mode variant", label, w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=9500), dev)
+
+
 def test_no_position_mode(dev):
     import torch
     import vision_transformer_attention_amd as pkg
