@@ -389,6 +389,32 @@ rpe_fwd_kernel(Params p) {
     }
   };
 
+  // Interior block gb (grid rows < R-1, no prefix keys) of a single-unit
+  // workgroup into ring stage `stage`: the common case of issue(), without its
+  // element-kind tests.
+  const uint32_t wbi = static_cast<uint32_t>(wbase) * RB + ioff0;
+  auto interior_off = [&](int i, int gb) -> uint32_t {
+    const int row = i * RPI + lane / CPR;
+    const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
+    const int y = WIDE ? gb >> 1 : (gb * kBlockSlots + row) >> p.lwp;
+    const int x = WIDE ? ((gb & 1) << 5) + row : (gb * kBlockSlots + row) & (p.Wp - 1);
+    return static_cast<uint32_t>(x < p.C ? wbase + y * rowstride + x : wbase) * RB + cb;
+  };
+  auto issue_interior = [&](int gb, int stage) {
+    const uint32_t kt = lds_ring + stage * (2 * TILE);
+    const uint32_t vt = kt + TILE;
+    if (wid < IPB) {
+      const uint32_t off = WIDE ? interior_off(wid, gb) : wbi + static_cast<uint32_t>(gb) * idoff;
+      dma16(kgb + off, kt + wid * 1024);
+      dma16(vgb + off, vt + wid * 1024);
+    }
+    for (int i = wid + NW; i < IPB; i += NW) {
+      const uint32_t off = interior_off(i, gb);
+      dma16(kgb + off, kt + i * 1024);
+      dma16(vgb + off, vt + i * 1024);
+    }
+  };
+
   // ---- rK tiles into the row area (same swizzled layout as the ring tiles)
   if constexpr (TK) {
     if (p.rk_lds) {
@@ -879,6 +905,17 @@ rpe_fwd_kernel(Params p) {
     st_cur = st_cur + 1 == ST ? 0 : st_cur + 1;
     return s;
   };
+  // step() for a single-unit workgroup whose element e + ST - 1 is the interior
+  // block gb_iss (so it exists, and ST - 2 elements follow e)
+  auto step_interior = [&](int gb_iss) -> int {
+    wait_vmcnt_floor((ST - 2) * lpe);
+    lds_barrier();
+    issue_interior(gb_iss, st_iss);
+    st_iss = st_iss + 1 == ST ? 0 : st_iss + 1;
+    const int s = st_cur;
+    st_cur = st_cur + 1 == ST ? 0 : st_cur + 1;
+    return s;
+  };
   auto ktile_of = [&](int s) -> const char* { return ring + s * (2 * TILE); };
   auto vtile_of = [&](int s) -> const char* { return ring + s * (2 * TILE) + TILE; };
 
@@ -1016,10 +1053,9 @@ rpe_fwd_kernel(Params p) {
       // interior blocks: the row parts of the next block are read one block ahead
       int ryn[4];
       load_ry(gb, ryn);
-      for (; gb < p.first_tail; ++gb, ++e) {
-        const int s = step(e);
+      auto interior_block = [&](int s) {
         int ryc[4];
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 4; ++j) ryc[j] = ryn[j];
         load_ry(gb + 1, ryn);
         if constexpr (TQ) {
@@ -1027,7 +1063,12 @@ rpe_fwd_kernel(Params p) {
           lds_barrier();
         }
         if (active) process(bool_c<true>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryc);
+      };
+      if constexpr (!MULTI) {
+        // the element issued at step e is block gb + ST - 1 (e = gb + prefix_block)
+        for (; gb < p.first_tail - (ST - 1); ++gb, ++e) interior_block(step_interior(gb + ST - 1));
       }
+      for (; gb < p.first_tail; ++gb, ++e) interior_block(step(e));
       for (; gb < p.grid_blocks; ++gb, ++e) {
         const int s = step(e);
         if constexpr (TQ) {
