@@ -674,9 +674,9 @@ rpe_fwd_kernel(Params p) {
   const int* __restrict__ ryt = ry_tab + (qpos ? yi : 0) + p.R - 1;
   // grid rows covered per block (Wp <= 32) and this lane's row within a block for each j
   const int rpb = WIDE ? 0 : kBlockSlots >> p.lwp;
-  int rj[4];
+  const int* ryj[4];   // ryt - (this lane's row within a block for entry j)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) rj[j] = WIDE ? 0 : (8 * j + 4 * h) >> p.lwp;
+  for (int j = 0; j < 4; ++j) ryj[j] = ryt - (WIDE ? 0 : (8 * j + 4 * h) >> p.lwp);
 
   // ---- running state of this lane's row (shared with the lane l ^ 32).
   float m_run = 0.0f;
@@ -700,7 +700,7 @@ rpe_fwd_kernel(Params p) {
   // Row parts ry(yq - y) of this lane's keys 8j + 4h + i of interior block g.
   auto load_ry = [&](int g, int (&r)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = WIDE ? ryt[-(g >> 1)] : ryt[-(g * rpb + rj[j])];
+    for (int j = 0; j < 4; ++j) r[j] = WIDE ? ryt[-(g >> 1)] : ryj[j][-(g * rpb)];
   };
   auto process_block = [&](auto interior_c, auto first_c, auto ph_c, const char* ktile, const char* vtile,
                            int gblk, bool prefix_blk, const int (&ryv)[4]) {
@@ -1050,14 +1050,11 @@ rpe_fwd_kernel(Params p) {
         if (!p.prefix_block) gb = 1;
         ++e;
       }
-      // interior blocks: the row parts of the next block are read one block ahead
-      int ryn[4];
-      load_ry(gb, ryn);
+      // interior blocks
       auto interior_block = [&](int s) {
+        // (the row parts' LDS latency hides behind the K reads and the S product)
         int ryc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ryc[j] = ryn[j];
-        load_ry(gb + 1, ryn);
+        load_ry(gb, ryc);
         if constexpr (TQ) {
           block_query_scores(ktile_of(s));
           lds_barrier();
@@ -1069,13 +1066,14 @@ rpe_fwd_kernel(Params p) {
         for (; gb < p.first_tail - (ST - 1); ++gb, ++e) interior_block(step_interior(gb + ST - 1));
       }
       for (; gb < p.first_tail; ++gb, ++e) interior_block(step(e));
+      const int ry_unused[4] = {0, 0, 0, 0};   // the tail blocks read their row parts themselves
       for (; gb < p.grid_blocks; ++gb, ++e) {
         const int s = step(e);
         if constexpr (TQ) {
           block_query_scores(ktile_of(s));
           lds_barrier();
         }
-        if (active) process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryn);
+        if (active) process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ry_unused);
       }
     }
     // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
