@@ -13,7 +13,8 @@ What it computes, and the passages it follows:
   the shift by M-1 (Swin 2D RPE post, sections 3.1-3.2).
 * ``buckets``   - token positions of one attention unit (a window or a whole
   grid) and the per-pair bucket id of the Product mapping (iRPE page, eq. 25;
-  Swin post, section 3.2), with no bucket for prefix (class) tokens.
+  Swin post, section 3.2), or the two rows of the Cross mapping (eqs. 22-24),
+  with no bucket for prefix (class) tokens.
 * ``attention`` - the attention forward written as a per-pair definition:
   offset -> index -> table row -> logit term, softmax, value sum
   (iRPE page eqs. 1-3 and 13-17; Swin relative-bias record, "The claim").
@@ -37,6 +38,11 @@ Parity status (pins live in tests/test_oracle_*.py):
   order, and by literal-vs-vectorised agreement on tiny grids.
 * The value term (r^V) is pinned only by closed forms (constant table,
   isolation); no page prints a value-term output.
+* The Cross mapping (iRPE page, Method, eqs. 22-24): pinned by the Shaw-style
+  page's printed weights along a one-row and a one-column grid (which also
+  fixes the row half [0, S) / column half [S, 2S) split of its table), by
+  its identity with the Product mapping of the summed rows, and by
+  literal-vs-vectorised agreement.
 """
 
 from .index import (  # noqa: F401

@@ -8,6 +8,10 @@ token i and key token j of the unit (prefix tokens first):
     c_ij   = q_i . k_j                                   (iRPE page, eqs. 1-3)
     b_ij   = bucket id of the pair, -1 if i or j is a prefix token
     rho_ij = [K] q_i . rK[b_ij] + [Q] k_j . rQ[b_ij]     (eqs. 13, 15, 16)
+
+With the Cross mapping (eqs. 22-24) a pair has two table rows, a row-offset
+row and a column-offset row, and every table term above is the sum of the
+two rows' terms (X[b_ij] reads X[by_ij] + X[bx_ij]).
     logit  = (c_ij + rho_ij) * s             contextual mode (eq. 13; the
                                              position term is added before the
                                              division by sqrt(d), Method,
@@ -35,7 +39,7 @@ import math
 
 import numpy as np
 
-from .buckets import num_buckets, pair_bucket, unit_positions
+from .buckets import num_buckets, pair_rows, unit_positions
 
 
 def unit_token_indices(spec, unit):
@@ -76,6 +80,21 @@ def bucket_map_array(spec, unit=0):
     gx = gx_tab[dx + (span_x - 1)]
     out[n_pre:, n_pre:] = (gy + h) * s + (gx + h)
     return out
+
+
+def pair_rows_arrays(spec, unit=0):
+    """Table rows of every pair of one unit: a list of int64 [T, T] arrays
+    (-1 where the pair has no position term) whose rows' encodings add up:
+    the Product id alone, or the Cross mapping's row-offset and
+    column-offset rows (same definition as ``buckets.pair_rows``)."""
+    if spec.method != "cross":
+        return [bucket_map_array(spec, unit)]
+    h, s, _ = num_buckets(spec)
+    prod = bucket_map_array(spec, unit)
+    has = prod >= 0
+    gy = np.where(has, prod // s, -1)          # g(dy) + H
+    gx = np.where(has, s + prod % s, -1)       # S + g(dx) + H
+    return [gy, gx]
 
 
 def _check_tables(spec, heads, d, bias, rk, rq, rv):
@@ -146,9 +165,9 @@ def attention(spec, q, k, v, bias=None, rk=None, rq=None, rv=None,
 
     for u in unit_list:
         idx = np.array(unit_token_indices(spec, u), dtype=np.int64)
-        bmap = bucket_map_array(spec, u)
-        has = bmap >= 0
-        safe = np.where(has, bmap, 0)
+        rows = pair_rows_arrays(spec, u)
+        has = rows[0] >= 0
+        safes = [np.where(has, r, 0) for r in rows]
         T = len(idx)
         chunk = max(1, (1 << 25) // max(1, T * d))
         for b in b_list:
@@ -160,18 +179,22 @@ def attention(spec, q, k, v, bias=None, rk=None, rq=None, rv=None,
                     i1 = min(T, i0 + chunk)
                     c = Q[i0:i1] @ K.T
                     m = has[i0:i1]
-                    bid = safe[i0:i1]
                     if spec.mode == "contextual":
                         rho = np.zeros_like(c)
-                        if rk_t is not None:
-                            tab = _head_table(rk_t, h)[bid]            # [i, j, d]
-                            rho += np.where(m, np.einsum("id,ijd->ij", Q[i0:i1], tab), 0.0)
-                        if rq_t is not None:
-                            tab = _head_table(rq_t, h)[bid]
-                            rho += np.where(m, np.einsum("jd,ijd->ij", K, tab), 0.0)
+                        for safe in safes:
+                            bid = safe[i0:i1]
+                            if rk_t is not None:
+                                tab = _head_table(rk_t, h)[bid]            # [i, j, d]
+                                rho += np.where(m, np.einsum("id,ijd->ij", Q[i0:i1], tab), 0.0)
+                            if rq_t is not None:
+                                tab = _head_table(rq_t, h)[bid]
+                                rho += np.where(m, np.einsum("jd,ijd->ij", K, tab), 0.0)
                         logits[i0:i1] = (c + rho) * s
                     elif spec.mode == "bias":
-                        logits[i0:i1] = c * s + np.where(m, _head_table(bias_t, h)[bid], 0.0)
+                        add = np.zeros_like(c)
+                        for safe in safes:
+                            add += np.where(m, _head_table(bias_t, h)[safe[i0:i1]], 0.0)
+                        logits[i0:i1] = c * s + add
                     else:
                         logits[i0:i1] = c * s
                 mx = logits.max(axis=1, keepdims=True)
@@ -183,8 +206,9 @@ def attention(spec, q, k, v, bias=None, rk=None, rq=None, rv=None,
                     tv = _head_table(rv_t, h)
                     for i0 in range(0, T, chunk):
                         i1 = min(T, i0 + chunk)
-                        tab = tv[safe[i0:i1]] * has[i0:i1, :, None]
-                        out_v[i0:i1] = np.einsum("ij,ijd->id", a[i0:i1], tab)
+                        for safe in safes:
+                            tab = tv[safe[i0:i1]] * has[i0:i1, :, None]
+                            out_v[i0:i1] += np.einsum("ij,ijd->id", a[i0:i1], tab)
                     out = out + out_v
                 o[b, h, idx] = out
                 lse[b, h, idx] = (mx + np.log(den))[:, 0]
@@ -217,18 +241,19 @@ def attention_literal(spec, q, k, v, bias=None, rk=None, rq=None, rv=None):
                     logits = []
                     for tj, pj in toks:
                         c = sum(q[b, h, ti, e] * k[b, h, tj, e] for e in range(d))
-                        bid = pair_bucket(spec, pi, pj)
+                        rows = pair_rows(spec, pi, pj)
                         if spec.mode == "contextual":
                             rho = 0.0
-                            if bid >= 0 and rk_t is not None:
-                                row = _head_table(rk_t, h)[bid]
-                                rho += sum(q[b, h, ti, e] * row[e] for e in range(d))
-                            if bid >= 0 and rq_t is not None:
-                                row = _head_table(rq_t, h)[bid]
-                                rho += sum(k[b, h, tj, e] * row[e] for e in range(d))
+                            for bid in rows:
+                                if rk_t is not None:
+                                    row = _head_table(rk_t, h)[bid]
+                                    rho += sum(q[b, h, ti, e] * row[e] for e in range(d))
+                                if rq_t is not None:
+                                    row = _head_table(rq_t, h)[bid]
+                                    rho += sum(k[b, h, tj, e] * row[e] for e in range(d))
                             logits.append((c + rho) * s)
                         elif spec.mode == "bias":
-                            add = _head_table(bias_t, h)[bid] if bid >= 0 else 0.0
+                            add = sum(_head_table(bias_t, h)[bid] for bid in rows)
                             logits.append(c * s + add)
                         else:
                             logits.append(c * s)
@@ -238,11 +263,12 @@ def attention_literal(spec, q, k, v, bias=None, rk=None, rq=None, rv=None):
                     acc = [0.0] * d
                     for (tj, pj), w in zip(toks, ex):
                         a = w / den
-                        bid = pair_bucket(spec, pi, pj)
+                        rows = pair_rows(spec, pi, pj)
                         for e in range(d):
                             val = v[b, h, tj, e]
-                            if rv_t is not None and bid >= 0:
-                                val += _head_table(rv_t, h)[bid][e]
+                            if rv_t is not None:
+                                for bid in rows:
+                                    val += _head_table(rv_t, h)[bid][e]
                             acc[e] += a * val
                     o[b, h, ti] = acc
                     lse[b, h, ti] = mx + math.log(den)

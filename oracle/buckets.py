@@ -20,6 +20,13 @@ Sources:
   attention and the bias are restricted to non-overlapping 7 x 7 windows and
   indexed by within-window offsets.
 
+* iRPE page, Method, Cross mapping (eqs. 22-24): a directed mapping with one
+  bucket for the row offset and one for the column offset, whose two
+  encodings are added; 2 x (2*beta+1) buckets.  The page fixes no order of
+  the two halves in one table; here rows [0, S) hold the row-offset
+  encodings (index g(dy) + H) and rows [S, 2S) the column-offset encodings
+  (index S + g(dx) + H), row part first as in the Product id.
+
 Offset convention: delta = p_query - p_key, rows first (dy, dx); this is the
 sign of the Swin post's worked example.
 """
@@ -30,6 +37,7 @@ from .index import ROUND_CAPPED, half_width, piecewise_index
 
 MODES = ("none", "bias", "contextual")
 MAPS = ("swin", "piecewise")
+METHODS = ("product", "cross")
 
 
 @dataclass(frozen=True)
@@ -46,6 +54,8 @@ class Spec:
     alpha, beta, gamma, reading : piecewise index parameters
     scale          : logit scale s; None -> 1/sqrt(head_dim)
     tables_per_head: True -> one table per head, False -> one shared table
+    method         : "product" (one bucket per (row, column) index pair) or
+                     "cross" (a row-offset bucket plus a column-offset bucket)
     """
 
     grid_h: int
@@ -61,12 +71,15 @@ class Spec:
     reading: str = ROUND_CAPPED
     scale: float = None
     tables_per_head: bool = False
+    method: str = "product"
 
     def __post_init__(self):
         if self.mode not in MODES:
             raise ValueError(f"mode {self.mode!r}")
         if self.map not in MAPS:
             raise ValueError(f"map {self.map!r}")
+        if self.method not in METHODS:
+            raise ValueError(f"method {self.method!r}")
         if self.window:
             if self.grid_h % self.window or self.grid_w % self.window:
                 raise ValueError("window must divide the grid")
@@ -114,14 +127,15 @@ class Spec:
 
 
 def num_buckets(spec):
-    """(H, S, S*S): half-width, entries per axis, Product table rows.
+    """(H, S, rows): half-width, entries per axis, table rows.
 
-    (2H+1)^2 buckets for the Product mapping (iRPE page, Method, "Product");
-    (2M-1)^2 for a Swin window (Swin post, section 3.1).
+    (2H+1)^2 rows for the Product mapping (iRPE page, Method, "Product");
+    (2M-1)^2 for a Swin window (Swin post, section 3.1); 2 (2H+1) for the
+    Cross mapping (iRPE page, Method, "Cross").
     """
     h = spec.half_width()
     s = 2 * h + 1
-    return h, s, s * s
+    return h, s, (2 * s if spec.method == "cross" else s * s)
 
 
 def unit_positions(spec, unit=0):
@@ -151,8 +165,23 @@ def unit_positions(spec, unit=0):
     return out
 
 
+def pair_rows(spec, p_query, p_key):
+    """Table rows whose encodings add up to the pair's term: [] if either
+    position is None, [Product id] for the Product mapping, [row-offset row,
+    column-offset row] for the Cross mapping."""
+    if p_query is None or p_key is None:
+        return []
+    h, s, _ = num_buckets(spec)
+    gy, gx = spec.g(p_query[0] - p_key[0]), spec.g(p_query[1] - p_key[1])
+    if not (-h <= gy <= h and -h <= gx <= h):
+        raise ValueError(f"index ({gy},{gx}) outside the table half-width {h}")
+    if spec.method == "cross":
+        return [gy + h, s + gx + h]
+    return [(gy + h) * s + (gx + h)]
+
+
 def pair_bucket(spec, p_query, p_key):
-    """Bucket id of one ordered pair of positions, or -1 if either is None."""
+    """Product bucket id of one ordered pair of positions, or -1 if either is None."""
     if p_query is None or p_key is None:
         return -1
     h, s, _ = num_buckets(spec)

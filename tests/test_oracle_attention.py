@@ -321,3 +321,94 @@ def test_scale_placement():
     lg = (q[0, 0] @ k[0, 0].T + np.einsum("id,ijd->ij", q[0, 0], rk[0][bm])) * 0.25
     np.testing.assert_allclose(w[(0, 0, 0)], torch.softmax(torch.from_numpy(lg), -1).numpy(),
                                atol=1e-13)
+
+
+# ------------------------------------------------------------------ Cross mapping
+
+def _shaw_as_cross(a_k, a_v, axis):
+    """The 1D clipped method as the Cross mapping on a 1 x 6 (axis "x") or 6 x 1
+    (axis "y") grid: the moving axis's half of each table holds the page's table
+    (mirrored, as in _shaw_as_2d), the other half is zero."""
+    gh, gw = (1, 6) if axis == "x" else (6, 1)
+    spec = Spec(gh, gw, mode="contextual", terms={"k", "v"}, map="piecewise",
+                alpha=3.0, beta=3.0, gamma=10.0, method="cross")
+    _, s, nb = num_buckets(spec)
+    assert nb == 2 * s == 14
+    rk = np.zeros((1, nb, 4))
+    rv = np.zeros((1, nb, 4))
+    base = s if axis == "x" else 0
+    for c in range(7):
+        rk[0, base + c] = a_k[6 - c]
+        rv[0, base + c] = a_v[6 - c]
+    return spec, rk, rv
+
+
+@pytest.mark.parametrize("axis", ["x", "y"])
+def test_cross_shaw_page_printed_weights(golden_dir, axis):
+    # iRPE page, Method, Cross (eqs. 22-24): on a grid with one row (one column) the
+    # row-offset (column-offset) index is always 0, so with that half of the table at
+    # zero the method is the 1D clipped encoding of the Shaw-style page, whose printed
+    # 6x6 weights (3 decimals) it must reproduce.  Pins the split of the table into a
+    # row half [0, S) and a column half [S, 2S).
+    printed = np.loadtxt(os.path.join(golden_dir, "shaw_1d_weights.txt"))
+    q, k, v, a_k, a_v = _shaw_page_setup()
+    spec, rk, rv = _shaw_as_cross(a_k, a_v, axis)
+    o, _, wts = attention(spec, q[None, None], k[None, None], v[None, None], rk=rk, rv=rv,
+                          return_weights=True)
+    assert np.abs(wts[(0, 0, 0)] - printed).max() <= 5e-4 + 1e-12
+    a = wts[(0, 0, 0)]
+    ref = np.zeros((6, 4))
+    for i in range(6):
+        for j in range(6):
+            ref[i] += a[i, j] * (v[j] + a_v[max(-3, min(3, j - i)) + 3])
+    np.testing.assert_allclose(o[0, 0], ref, atol=1e-12)
+    # the same table in the other half misses (its axis never moves: a constant term)
+    other = "y" if axis == "x" else "x"
+    _, rk2, rv2 = _shaw_as_cross(a_k, a_v, other)
+    _, _, w2 = attention(spec, q[None, None], k[None, None], v[None, None], rk=rk2, rv=rv2,
+                         return_weights=True)
+    assert np.abs(w2[(0, 0, 0)] - printed).max() > 0.1
+
+
+CROSS_TINY = [
+    Spec(3, 4, prefix=1, mode="contextual", terms={"k", "q", "v"}, map="piecewise",
+         alpha=0.9, beta=1.7, gamma=3.0, method="cross"),
+    Spec(4, 4, window=2, mode="bias", map="swin", method="cross"),
+    Spec(3, 5, prefix=1, mode="bias", map="piecewise", alpha=1.0, beta=2.0, gamma=4.0, method="cross"),
+]
+
+
+@pytest.mark.parametrize("spec", CROSS_TINY)
+def test_cross_literal_matches_vectorised(spec):
+    rng = np.random.default_rng(17)
+    q, k, v, tabs = _inputs(spec, 2, 2, 5, rng, per_head=True)
+    o1, l1 = attention_literal(spec, q, k, v, **tabs)
+    o2, l2 = attention(spec, q, k, v, **tabs)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("spec", CROSS_TINY)
+def test_cross_is_product_of_summed_rows(spec):
+    # The two encodings of a Cross pair add (eqs. 22-24), so a Cross table T equals the
+    # Product table P[by * S + bx] = T[by] + T[S + bx] over the same index function.
+    rng = np.random.default_rng(19)
+    q, k, v, tabs = _inputs(spec, 2, 2, 5, rng, per_head=True)
+    _, s, _ = num_buckets(spec)
+    prod = Spec(**{f: getattr(spec, f) for f in spec.__dataclass_fields__ if f != "method"})
+    ptabs = {}
+    for n, t in tabs.items():
+        by = np.arange(s * s) // s
+        bx = s + np.arange(s * s) % s
+        ptabs[n] = t[:, by] + t[:, bx]
+    o1, l1 = attention(spec, q, k, v, **tabs)
+    o2, l2 = attention(prod, q, k, v, **ptabs)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+    # dropping either half changes the result
+    for half in (slice(0, s), slice(s, 2 * s)):
+        t2 = {n: t.copy() for n, t in tabs.items()}
+        for t in t2.values():
+            t[:, half] = 0.0
+        o3, _ = attention(spec, q, k, v, **t2)
+        assert np.abs(o3 - o1).max() > 1e-3
