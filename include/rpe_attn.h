@@ -79,6 +79,7 @@ enum { RPE_MODE_NONE = 0, RPE_MODE_BIAS = 1, RPE_MODE_CONTEXTUAL = 2 };
 enum { RPE_TERM_K = 1, RPE_TERM_Q = 2, RPE_TERM_V = 4 };
 enum { RPE_MAP_SWIN = 0, RPE_MAP_PIECEWISE = 1 };
 enum { RPE_ROUND_CAPPED = 0, RPE_ROUND_TRUNC = 1 };
+enum { RPE_TABLE_BIAS = 0, RPE_TABLE_VECTOR = 1 };   /* rpe_attn_cross_to_product */
 
 typedef struct rpe_attn_desc {
   int32_t batch;            /* >= 0 (0: nothing to do)                               */
@@ -121,6 +122,27 @@ rpe_status rpe_attn_axis_index(const rpe_attn_desc* desc, int32_t length, int16_
  * (bucket ids depend only on offsets: Swin 2D RPE post, section 2.2).
  * Requires T*T <= 2^31 - 1. */
 rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void* stream);
+
+/* Cross mapping (iRPE page, Method, "Cross", eqs. 22-24): the encoding of a
+ * pair is the sum of a row-offset entry and a column-offset entry.  That is
+ * the Product mapping of the same index function with the table
+ *     product[by * S + bx] = cross[by] + cross[S + bx]      (by = g(dy)+H, bx = g(dx)+H)
+ * so a Cross table runs through rpe_attn_fwd after this conversion, with the
+ * same descriptor.
+ *   cross   : device, [tables][2*S][width]: rows [0, S) hold the row-offset
+ *             encodings, rows [S, 2S) the column-offset encodings
+ *   product : device, [tables][S*S][width], written (caller-owned; must not
+ *             overlap cross)
+ *   kind    : RPE_TABLE_BIAS   - float32 entries, width 1 (bias mode only)
+ *             RPE_TABLE_VECTOR - desc.dtype entries, width head_dim
+ *                                (contextual mode only: rq, rk or rv)
+ *   tables  : heads if desc.tables_per_head, else 1
+ * Each sum is formed in float32 and rounded once to the entry type (bf16:
+ * round to nearest even).  Asynchronous on `stream`.  Errors: descriptor
+ * validation; RPE_E_MODE for an unknown kind or a kind the mode has no table
+ * for; RPE_E_NULL for a NULL table. */
+rpe_status rpe_attn_cross_to_product(const rpe_attn_desc* desc, int32_t kind, const void* cross,
+                                     void* product, void* stream);
 
 /* The attention forward.  q, k, v, o required (may be NULL when batch == 0, which
  * launches nothing); bias required in bias mode;

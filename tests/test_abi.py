@@ -132,3 +132,26 @@ def test_host_plan_fuzz_sanitized(tmp_path):
     r = subprocess.run([exe, "40000"], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "0 failures" in r.stdout
+
+
+def test_cross_to_product_rejects_before_device():
+    lib = _lib_or_skip()
+    one = ctypes.c_void_p(16)
+    B, V = _lib.RPE_TABLE_BIAS, _lib.RPE_TABLE_VECTOR
+    ctx = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), prefix_tokens=1, mode="contextual",
+                        terms="k", map="piecewise", alpha=1.9, beta=3.8, gamma=15.2)
+    bias = pkg.make_desc(batch=1, heads=2, head_dim=32, grid=(7, 7), window=7, mode="bias", map="swin")
+    none = pkg.make_desc(batch=1, heads=2, head_dim=32, grid=(7, 7), mode="none")
+    f = lib.rpe_attn_cross_to_product
+    assert f(None, V, one, one, None) == -1
+    assert f(ctypes.byref(ctx), V, None, one, None) == -1
+    assert f(ctypes.byref(ctx), V, one, None, None) == -1
+    # a kind the mode has no table for, an unknown kind, no position mode
+    assert f(ctypes.byref(ctx), B, one, one, None) == -4
+    assert f(ctypes.byref(bias), V, one, one, None) == -4
+    assert f(ctypes.byref(ctx), 7, one, one, None) == -4
+    assert f(ctypes.byref(none), B, one, one, None) == -4
+    # descriptor validation comes first
+    bad = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), mode="contextual", terms="k",
+                        map="piecewise", alpha=-1.0, beta=3.8, gamma=15.2)
+    assert f(ctypes.byref(bad), V, one, one, None) == -7

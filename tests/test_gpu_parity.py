@@ -35,7 +35,8 @@ def say(*a):
 
 def spec_of(w, **over):
     kw = dict(window=w.window, prefix=w.prefix, mode=w.mode, terms=w.terms, map=w.map, alpha=w.alpha,
-              beta=w.beta, gamma=w.gamma, reading=w.reading, tables_per_head=w.tables_per_head)
+              beta=w.beta, gamma=w.gamma, reading=w.reading, tables_per_head=w.tables_per_head,
+              method=w.method)
     kw.update(over)
     return Spec(w.grid_h, w.grid_w, **kw)
 
@@ -63,7 +64,7 @@ def run_gpu(w, x, dev, scale=None, return_lse=True):
                               prefix_tokens=w.prefix, mode=w.mode, terms="".join(sorted(w.terms)),
                               map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma, rounding=w.reading,
                               scale=scale, bias=d.get("bias"), rq=d.get("rq"), rk=d.get("rk"),
-                              rv=d.get("rv"), return_lse=True)
+                              rv=d.get("rv"), return_lse=True, method=w.method)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -275,6 +276,93 @@ def test_mode_variants(dev, label, w):
     w = fit(w)
     say("mode variant", label, w.qkv_shape)
     compare(w, make_inputs(w, sigma=1.0, seed=9500), dev)
+
+
+# The Cross mapping: Cross tables (row-offset half, column-offset half) are
+# rewritten as Product tables by rpe_attn_cross_to_product, then the Product
+# forward runs.  The conversion is checked exactly against its definition, the
+# attention against the oracle's own Cross mapping.
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_cross_to_product_exact(dev, dtype):
+    import torch
+    import vision_transformer_attention_amd as pkg
+    say("cross_to_product", dtype)
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    d = pkg.make_desc(batch=1, heads=3, head_dim=32, grid=(14, 14), prefix_tokens=1, dtype=dtype,
+                      mode="contextual", terms="kqv", map="piecewise", alpha=1.9, beta=3.8, gamma=15.2,
+                      tables_per_head=True)
+    _, s, nb = pkg.rpe_attn_num_buckets(d)
+    rng = np.random.default_rng(31)
+    cross = torch.from_numpy(rng.standard_normal((3, 2 * s, 32)).astype(np.float32)).to(tdt)
+    got = pkg.rpe_attn_cross_to_product(d, cross.to(dev)).cpu()
+    torch.cuda.synchronize()
+    c32 = cross.float()
+    by, bx = np.arange(nb) // s, s + np.arange(nb) % s
+    ref = (c32[:, by] + c32[:, bx]).to(tdt)          # one fp32 sum, one rounding
+    assert got.dtype == tdt and tuple(got.shape) == (3, nb, 32)
+    assert torch.equal(got, ref)
+    db = pkg.make_desc(batch=1, heads=3, head_dim=32, grid=(7, 7), window=7, mode="bias", map="swin")
+    _, s, nb = pkg.rpe_attn_num_buckets(db)
+    cb = torch.from_numpy(rng.standard_normal((1, 2 * s)).astype(np.float32))
+    got = pkg.rpe_attn_cross_to_product(db, cb.to(dev)).cpu()
+    by, bx = np.arange(nb) // s, s + np.arange(nb) % s
+    assert torch.equal(got, cb[:, by] + cb[:, bx])
+
+
+CROSS_CASES = [
+    ("cross bias, global 14x14 + cls", _D.resized(batch=2, heads=3, mode="bias", terms=frozenset(),
+                                                  method="cross")),
+    ("cross bias, Swin 7x7 windows, per-head", WORKLOADS["swin_t_w7"].resized(batch=2, heads=3, grid_h=14,
+                                                                             grid_w=14, tables_per_head=True,
+                                                                             method="cross")),
+    ("cross contextual K, global 14x14 + cls", _D.resized(batch=2, heads=2, method="cross")),
+    ("cross contextual KQV, global 14x14 + cls", _D.resized(batch=2, heads=2, terms=frozenset("kqv"),
+                                                            method="cross")),
+    ("cross contextual QKV fp32 d16, 7x7 windows",
+     _D.resized(batch=2, heads=2, head_dim=16, grid_h=14, grid_w=14, window=7, prefix=0, terms=frozenset("kqv"),
+                dtype="fp32", method="cross")),
+    ("cross contextual K, wide 10x40 grid", WORKLOADS["highres_irpe_k"].resized(batch=1, heads=2, grid_h=10,
+                                                                               grid_w=40, method="cross")),
+]
+
+
+def _cross_as_product(w, x):
+    """The Product workload and tables the conversion defines: entry by*S + bx is
+    the float32 sum of the two halves' rows, rounded once to the table dtype."""
+    _, s, _ = num_buckets(spec_of(w))
+    nb = s * s
+    by, bx = np.arange(nb) // s, s + np.arange(nb) % s
+    px = dict(x)
+    for n in ("bias", "rq", "rk", "rv"):
+        if n in x:
+            t = x[n].astype(np.float32)
+            px[n] = round_to_dtype((t[:, by] + t[:, bx]).astype(np.float64), "fp32" if n == "bias" else w.dtype)
+    return w.resized(method="product", table_rows=nb), px
+
+
+@pytest.mark.parametrize("label,w", CROSS_CASES)
+def test_cross_mapping(dev, label, w):
+    # The GPU path is held to the usual tolerance against the oracle's Product mapping
+    # on the converted tables (the conversion itself is exact: test_cross_to_product_exact);
+    # the oracle's Cross mapping on the unrounded tables differs from that only by the
+    # one rounding of each summed entry (bf16: <= 2^-8 relative), reported here.
+    w = fit(w)
+    say("cross", label, w.qkv_shape, "table rows", w.table_rows)
+    x = make_inputs(w, sigma=1.0, seed=9700)
+    pw, px = _cross_as_product(w, x)
+    go, gl = run_gpu(w, x, dev)
+    ro, rl = run_oracle(pw, px)
+    co, cl = run_oracle(w, x)
+    assert np.isfinite(go).all()
+    err = float(np.abs(go - ro).max())
+    lerr = float(np.abs(gl - rl).max())
+    rnd = float(np.abs(ro - co).max())
+    tol = TOL[w.dtype]
+    print(f"    max|o - oracle(product of converted tables)| = {err:.3e}  lse {lerr:.3e}  (tol {tol});"
+          f" table rounding moves the oracle by {rnd:.3e}", flush=True)
+    assert err <= tol and lerr <= tol, (err, lerr)
+    if w.dtype == "fp32":
+        assert rnd <= 1e-5
 
 
 def test_no_position_mode(dev):

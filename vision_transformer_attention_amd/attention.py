@@ -95,17 +95,54 @@ def _ptr(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+def rpe_attn_cross_to_product(desc, table):
+    """The Product table [T, S*S(, d)] equal to a Cross table [T, 2S(, d)]
+    (rows [0, S): row-offset encodings, [S, 2S): column-offset encodings).
+    A 2-D float32 table is a bias table, a 3-D one a contextual table."""
+    torch = _torch()
+    _, s, nb = rpe_attn_num_buckets(desc)
+    kind = _lib.RPE_TABLE_BIAS if table.dim() == 2 else _lib.RPE_TABLE_VECTOR
+    th = desc.heads if desc.tables_per_head else 1
+    want = (th, 2 * s) if kind == _lib.RPE_TABLE_BIAS else (th, 2 * s, desc.head_dim)
+    if tuple(table.shape) != want or not table.is_contiguous() or not table.is_cuda:
+        raise ValueError(f"cross table must be a contiguous device tensor {list(want)}")
+    out = torch.empty((th, nb) + tuple(table.shape[2:]), dtype=table.dtype, device=table.device)
+    check("rpe_attn_cross_to_product",
+          load().rpe_attn_cross_to_product(ctypes.byref(desc), int(kind), _ptr(table), _ptr(out),
+                                           _stream(table.device)))
+    return out
+
+
 def rpe_attn_fwd(q, k, v, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
                  alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None,
-                 rq=None, rk=None, rv=None, out=None, return_lse=False):
+                 rq=None, rk=None, rv=None, out=None, return_lse=False, method="product"):
     """Attention forward with 2D relative position terms.
 
     q, k, v: [B, H, N, d] contiguous device tensors (bfloat16 or float32),
     N = prefix_tokens + grid[0] * grid[1].  bias: [H or 1, S*S] float32;
     rq / rk / rv: [H or 1, S*S, d] in the dtype of q.  Returns o (and the
     float32 log-sum-exp [B, H, N] with ``return_lse``).
+
+    method="cross": the tables are Cross-mapping tables with 2S rows (row-offset
+    half, then column-offset half); they are rewritten as Product tables by
+    ``rpe_attn_cross_to_product`` and the Product forward runs on those.
     """
     torch = _torch()
+    if method == "cross":
+        if mode == "none":
+            raise ValueError("the Cross mapping needs bias or contextual mode")
+        B, H, _, d = q.shape
+        tabs = [t for t in (bias, rq, rk, rv) if t is not None]
+        per_head = any(t.shape[0] == H and H > 1 for t in tabs)
+        desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
+                         dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms,
+                         map=map, alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale,
+                         tables_per_head=per_head)
+        conv = lambda t, used: rpe_attn_cross_to_product(desc, t) if (t is not None and used) else None
+        bias = conv(bias, mode == "bias")
+        rq, rk, rv = (conv(t, mode == "contextual" and n in terms) for n, t in (("q", rq), ("k", rk), ("v", rv)))
+    elif method != "product":
+        raise ValueError(f"method {method!r}")
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must be [B, H, N, d] of one shape")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):

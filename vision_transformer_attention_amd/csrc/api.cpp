@@ -11,6 +11,8 @@ hipError_t launch_axis_index(int length, int map, int rounding, double alpha, do
 hipError_t launch_bucket_map(int P, int R, int C, int half, int S, int map, int rounding,
                              double alpha, double beta, double gamma, int16_t* out,
                              hipStream_t stream);
+hipError_t launch_cross_to_product(bool bf16, const void* cross, void* product, int S, int width,
+                                   int64_t total, hipStream_t stream);
 }  // namespace rpe
 
 extern "C" {
@@ -68,6 +70,29 @@ rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void
   const hipError_t e = rpe::launch_bucket_map(desc->prefix_tokens, R, C, h, s, map, desc->rounding,
                                               desc->alpha, desc->beta, desc->gamma, dev_map,
                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RPE_OK : RPE_E_HIP;
+}
+
+rpe_status rpe_attn_cross_to_product(const rpe_attn_desc* desc, int32_t kind, const void* cross,
+                                     void* product, void* stream) {
+  int h = 0, s = 0, nb = 0;
+  const int st = rpe::table_geometry(desc, &h, &s, &nb);
+  if (st != RPE_OK) return static_cast<rpe_status>(st);
+  int width = 0;
+  bool bf16 = false;
+  if (kind == RPE_TABLE_BIAS && desc->mode == RPE_MODE_BIAS) {
+    width = 1;
+  } else if (kind == RPE_TABLE_VECTOR && desc->mode == RPE_MODE_CONTEXTUAL) {
+    width = desc->head_dim;
+    bf16 = desc->dtype == RPE_BF16;
+  } else {
+    return RPE_E_MODE;
+  }
+  if (!cross || !product) return RPE_E_NULL;
+  const int64_t tables = desc->tables_per_head ? desc->heads : 1;
+  const int64_t total = tables * nb * width;
+  const hipError_t e = rpe::launch_cross_to_product(bf16, cross, product, s, width, total,
+                                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RPE_OK : RPE_E_HIP;
 }
 

@@ -1,7 +1,9 @@
 // gfx950 kernels that expose the bucket geometry on its own: the per-axis
 // index g(x) for a range of offsets, and the int16 bucket id of every ordered
 // pair of one attention unit (iRPE summary page, Method, eqs. 18 and 25; Swin
-// 2D RPE post, sections 3.1-3.2).  The fused attention forward is in fwd.hip.
+// 2D RPE post, sections 3.1-3.2); and the Cross mapping's tables rewritten as
+// Product tables (iRPE page, Method, eqs. 22-24).  The fused attention
+// forward is in fwd_kernel.h.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -55,6 +57,41 @@ __global__ void bucket_map_kernel(int P, int R, int C, int half, int S, int map,
     }
     out[e] = static_cast<int16_t>(b);
   }
+}
+
+// product[t][by*S + bx][w] = cross[t][by][w] + cross[t][S + bx][w], summed in
+// float32 and rounded once to T; one thread per product entry.
+template <typename T>
+__global__ void cross_to_product_kernel(const T* __restrict__ cross, T* __restrict__ product, int S,
+                                        int width, int64_t total) {
+  const int64_t per_table = static_cast<int64_t>(S) * S * width;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = e / per_table;
+    const int64_t r = e - t * per_table;
+    const int b = static_cast<int>(r / width), w = static_cast<int>(r - static_cast<int64_t>(b) * width);
+    const int by = b / S, bx = b - by * S;
+    const T* src = cross + t * (2 * static_cast<int64_t>(S) * width);
+    const float sum = static_cast<float>(src[static_cast<int64_t>(by) * width + w]) +
+                      static_cast<float>(src[static_cast<int64_t>(S + bx) * width + w]);
+    product[e] = static_cast<T>(sum);
+  }
+}
+
+hipError_t launch_cross_to_product(bool bf16, const void* cross, void* product, int S, int width,
+                                   int64_t total, hipStream_t stream) {
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  if (bf16)
+    hipLaunchKernelGGL(cross_to_product_kernel<__bf16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, static_cast<const __bf16*>(cross), static_cast<__bf16*>(product), S, width,
+                       total);
+  else
+    hipLaunchKernelGGL(cross_to_product_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, static_cast<const float*>(cross), static_cast<float*>(product), S, width,
+                       total);
+  return hipGetLastError();
 }
 
 hipError_t launch_axis_index(int length, int map, int rounding, double alpha, double beta,

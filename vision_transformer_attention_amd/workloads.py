@@ -47,6 +47,7 @@ class Workload:
     table_rows: int = 0        # rows of each position table (S * S)
     tables_per_head: bool = False
     description: str = ""
+    method: str = "product"    # "product" | "cross" (table rows: S*S or 2S)
 
     @property
     def tokens(self):
