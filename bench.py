@@ -41,7 +41,8 @@ from vision_transformer_attention_amd.workloads import WORKLOADS, make_inputs  #
 
 METRIC = "2D-RPE attention fwd TFLOP/s and % bf16 MFMA peak (DeiT-S iRPE-K, Swin-T W7)"
 HEADLINE = "deit_s_irpe_k"
-SECONDARY = ("swin_t_w7", "deit_s_irpe_qkv", "highres_irpe_k")
+SECONDARY = ("swin_t_w7", "deit_s_irpe_qkv", "highres_irpe_k", "deit_s_irpe_bias", "deit_s_irpe_k_cross",
+             "detr_irpe_k")
 PEAK_MFMA_BF16 = 2500.0      # TFLOP/s, dense, MI355X
 PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
 MALL_BYTES = 256 << 20
@@ -75,7 +76,7 @@ def _oracle_worker(args):
     x = _CPU["x"]
     spec = Spec(w.grid_h, w.grid_w, window=w.window, prefix=w.prefix, mode=w.mode, terms=w.terms, map=w.map,
                 alpha=w.alpha, beta=w.beta, gamma=w.gamma, reading=w.reading,
-                tables_per_head=w.tables_per_head)
+                tables_per_head=w.tables_per_head, method=w.method)
     for b, h in pairs:
         attention(spec, x["q"], x["k"], x["v"], bias=x.get("bias"), rq=x.get("rq"), rk=x.get("rk"),
                   rv=x.get("rv"), batch_sel=[b], heads_sel=[h])
@@ -166,7 +167,8 @@ def _prepared(w, d, o):
     return pkg.prepare_fwd(d["q"], d["k"], d["v"], out=o, grid=(w.grid_h, w.grid_w), window=w.window,
                            prefix_tokens=w.prefix, mode=w.mode, terms="".join(sorted(w.terms)), map=w.map,
                            alpha=w.alpha, beta=w.beta, gamma=w.gamma, rounding=w.reading,
-                           bias=d.get("bias"), rq=d.get("rq"), rk=d.get("rk"), rv=d.get("rv"))
+                           bias=d.get("bias"), rq=d.get("rq"), rk=d.get("rk"), rv=d.get("rv"),
+                           method=w.method)
 
 
 def time_workload(name, steps, warmup, dev, cold=True):

@@ -56,9 +56,10 @@ def test_workload_geometry_matches_oracle(name):
     d = _w_desc(w)
     assert pkg.rpe_attn_validate(d) == 0
     spec = Spec(w.grid_h, w.grid_w, window=w.window, prefix=w.prefix, mode=w.mode, terms=w.terms,
-                map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma, reading=w.reading)
-    assert pkg.rpe_attn_num_buckets(d) == num_buckets(spec)
-    assert pkg.rpe_attn_num_buckets(d)[2] == w.table_rows
+                map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma, reading=w.reading, method=w.method)
+    h, s, rows = pkg.rpe_attn_num_buckets(d)        # the library's (Product) geometry
+    assert num_buckets(spec) == (h, s, 2 * s if w.method == "cross" else rows)
+    assert num_buckets(spec)[2] == w.table_rows
     n, t, u = pkg.rpe_attn_unit_size(d)
     assert (n, t, u) == (spec.tokens_per_image, spec.unit_tokens, spec.units_per_image)
 

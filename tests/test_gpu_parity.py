@@ -271,6 +271,19 @@ MODE_VARIANTS = [
 ]
 
 
+# Variable resolution: the DeiT-S key term over the grids of 112^2 .. 384^2 inputs
+# (7x7 .. 24x24 patches + cls) and DETR-like non-square grids; every grid gets its
+# own thresholds, key-slot layout and launch plan.
+RESOLUTIONS = [(7, 7), (10, 10), (18, 18), (24, 24), (9, 38), (17, 25)]
+
+
+@pytest.mark.parametrize("gh,gw", RESOLUTIONS)
+def test_resolution_sweep(dev, gh, gw):
+    w = fit(_D.resized(batch=2, heads=2, grid_h=gh, grid_w=gw, prefix=1 if gh == gw else 0))
+    say("resolution", gh, gw, w.qkv_shape)
+    compare(w, make_inputs(w, sigma=1.0, seed=9800 + gh * 100 + gw), dev)
+
+
 @pytest.mark.parametrize("label,w", MODE_VARIANTS)
 def test_mode_variants(dev, label, w):
     w = fit(w)
@@ -462,6 +475,9 @@ FULL_SAMPLES = {
     "deit_s_irpe_k": ([0, 37, 63], [0, 5]),
     "deit_s_irpe_qkv": ([0, 63], [1, 4]),
     "highres_irpe_k": ([3], [5]),
+    "deit_s_irpe_bias": ([0, 63], [0, 5]),
+    "deit_s_irpe_k_cross": ([0, 63], [2]),
+    "detr_irpe_k": ([0, 7], [0, 7]),
 }
 
 

@@ -196,21 +196,28 @@ class PreparedFwd:
     storage while this object is used.
     """
 
-    def __init__(self, desc, ptrs, keep, device):
+    def __init__(self, desc, ptrs, keep, device, convert=()):
         self._lib = load()
         self._desc = desc
         self._args = ptrs
         self._keep = keep
         self._device = device
+        self._convert = convert    # (kind, cross, product) launches before the forward (Cross mapping)
 
     def __call__(self, stream=None):
         torch = _torch()
         s = ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream if stream is None else stream)
+        for kind, src, dst in self._convert:
+            check("rpe_attn_cross_to_product",
+                  self._lib.rpe_attn_cross_to_product(ctypes.byref(self._desc), kind, src, dst, s))
         check("rpe_attn_fwd", self._lib.rpe_attn_fwd(ctypes.byref(self._desc), *self._args, s))
 
 
 def prepare_fwd(q, k, v, *, out, lse=None, **kw):
-    """Validate once (by running the call) and return a PreparedFwd for repeats."""
+    """Validate once (by running the call) and return a PreparedFwd for repeats.
+
+    With method="cross" every call first rewrites the Cross tables into Product
+    tables held by the PreparedFwd, then runs the forward on those."""
     torch = _torch()
     rpe_attn_fwd(q, k, v, out=out, **kw)
     B, H, N, d = q.shape
@@ -223,8 +230,22 @@ def prepare_fwd(q, k, v, *, out, lse=None, **kw):
                      map=kw.get("map", "swin"), alpha=kw.get("alpha", 0.0), beta=kw.get("beta", 0.0),
                      gamma=kw.get("gamma", 0.0), rounding=kw.get("rounding", "capped"),
                      scale=kw.get("scale"), tables_per_head=per_head)
+    bias = kw.get("bias") if mode == "bias" else None
     rq = kw.get("rq") if "q" in terms else None
     rk = kw.get("rk") if "k" in terms else None
     rv = kw.get("rv") if "v" in terms else None
-    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(kw.get("bias")), _ptr(rq), _ptr(rk), _ptr(rv), _ptr(out), _ptr(lse)]
-    return PreparedFwd(desc, ptrs, (q, k, v, out, lse, tabs), q.device)
+    convert = []
+    if kw.get("method", "product") == "cross":
+        prod = []
+        for t in (bias, rq, rk, rv):
+            if t is None:
+                prod.append(None)
+                continue
+            p = rpe_attn_cross_to_product(desc, t)
+            kind = _lib.RPE_TABLE_BIAS if t.dim() == 2 else _lib.RPE_TABLE_VECTOR
+            convert.append((kind, _ptr(t), _ptr(p)))
+            prod.append(p)
+        tabs = tabs + [t for t in prod if t is not None]
+        bias, rq, rk, rv = prod
+    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(rq), _ptr(rk), _ptr(rv), _ptr(out), _ptr(lse)]
+    return PreparedFwd(desc, ptrs, (q, k, v, out, lse, tabs), q.device, tuple(convert))

@@ -89,6 +89,24 @@ WORKLOADS = {
         alpha=3.8, beta=7.6, gamma=30.4, dtype=BF16, table_rows=289, tables_per_head=False,
         description="High-resolution iRPE on keys: B4, 56x56 grid (3136 tokens), h6 d64 bf16, "
                     "r^K 289x64 shared"),
+    # The mode and mapping variants the kernel also runs (measured as secondaries).
+    "deit_s_irpe_bias": Workload(
+        6, "deit_s_irpe_bias", batch=64, heads=6, head_dim=64, grid_h=14, grid_w=14, window=0,
+        prefix=1, mode="bias", map="piecewise", alpha=1.9, beta=3.8, gamma=15.2, dtype=BF16,
+        table_rows=81, tables_per_head=True,
+        description="DeiT-S iRPE bias mode: B64, 14x14+cls (197 tokens), h6 d64 bf16, 81-entry bias per head"),
+    "deit_s_irpe_k_cross": Workload(
+        7, "deit_s_irpe_k_cross", batch=64, heads=6, head_dim=64, grid_h=14, grid_w=14, window=0,
+        prefix=1, mode="contextual", terms=frozenset("k"), map="piecewise", alpha=1.9, beta=3.8,
+        gamma=15.2, dtype=BF16, table_rows=18, tables_per_head=False, method="cross",
+        description="DeiT-S iRPE contextual Cross mapping on keys: B64, 197 tokens, h6 d64 bf16, "
+                    "r^K 18x64 (9 row + 9 column) shared"),
+    "detr_irpe_k": Workload(
+        8, "detr_irpe_k", batch=8, heads=8, head_dim=32, grid_h=25, grid_w=38, window=0,
+        prefix=0, mode="contextual", terms=frozenset("k"), map="piecewise", alpha=1.9, beta=3.8,
+        gamma=15.2, dtype=BF16, table_rows=81, tables_per_head=False,
+        description="DETR-like encoder iRPE on keys, non-square 25x38 grid (950 tokens, an 800x1216 "
+                    "image at stride 32): B8, h8 d32 bf16, r^K 81x32 shared"),
 }
 
 
