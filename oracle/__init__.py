@@ -38,6 +38,12 @@ Parity status (pins live in tests/test_oracle_*.py):
   order, and by literal-vs-vectorised agreement on tiny grids.
 * The value term (r^V) is pinned only by closed forms (constant table,
   isolation); no page prints a value-term output.
+* The undirected mappings (``undirected``; Euclidean eqs. 19-20 and
+  Quantization eq. 21, each in the page's and the code's reading): pinned by
+  the page's distance list and its adjacent-offsets example, a Fermat
+  sum-of-two-squares count, Pythagorean offsets, symmetry and saturation
+  invariants, the reduction to the directed index on an axis, and an
+  attention-level reduction to a symmetric Product table on one row.
 * The Cross mapping (iRPE page, Method, eqs. 22-24): pinned by the Shaw-style
   page's printed weights along a one-row and a one-column grid (which also
   fixes the row half [0, S) / column half [S, 2S) split of its table), by
@@ -54,4 +60,5 @@ from .index import (  # noqa: F401
     axis_index_table,
 )
 from .buckets import Spec, unit_positions, bucket_map, num_buckets  # noqa: F401
+from .undirected import UNDIRECTED_MAPS, undirected_index  # noqa: F401
 from .attention import attention, attention_literal, unit_token_indices  # noqa: F401

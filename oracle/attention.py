@@ -87,6 +87,20 @@ def pair_rows_arrays(spec, unit=0):
     (-1 where the pair has no position term) whose rows' encodings add up:
     the Product id alone, or the Cross mapping's row-offset and
     column-offset rows (same definition as ``buckets.pair_rows``)."""
+    if spec.undirected:
+        toks = unit_positions(spec, unit)
+        h, _, _ = num_buckets(spec)
+        cache = {}
+        out = np.full((len(toks), len(toks)), -1, dtype=np.int64)
+        for i, (_, pi) in enumerate(toks):
+            for j, (_, pj) in enumerate(toks):
+                if pi is None or pj is None:
+                    continue
+                key = (abs(pi[0] - pj[0]), abs(pi[1] - pj[1]))
+                if key not in cache:
+                    cache[key] = spec.u(*key) + h
+                out[i, j] = cache[key]
+        return [out]
     if spec.method != "cross":
         return [bucket_map_array(spec, unit)]
     h, s, _ = num_buckets(spec)

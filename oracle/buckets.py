@@ -34,9 +34,10 @@ sign of the Swin post's worked example.
 from dataclasses import dataclass, field
 
 from .index import ROUND_CAPPED, half_width, piecewise_index
+from .undirected import UNDIRECTED_MAPS, undirected_index
 
 MODES = ("none", "bias", "contextual")
-MAPS = ("swin", "piecewise")
+MAPS = ("swin", "piecewise") + UNDIRECTED_MAPS
 METHODS = ("product", "cross")
 
 
@@ -50,7 +51,10 @@ class Spec:
     prefix         : number of prefix (class) tokens at sequence start (0 or 1)
     mode           : "none" | "bias" | "contextual"
     terms          : subset of {"k", "q", "v"} (contextual mode)
-    map            : "swin" (identity index, H = M-1) | "piecewise" (eq. 18)
+    map            : "swin" (identity index, H = M-1) | "piecewise" (eq. 18), or
+                     an undirected map of the offset's distance (see
+                     ``oracle.undirected``: "euclidean", "euclidean_rounded",
+                     "quantized", "quantized_squared")
     alpha, beta, gamma, reading : piecewise index parameters
     scale          : logit scale s; None -> 1/sqrt(head_dim)
     tables_per_head: True -> one table per head, False -> one shared table
@@ -80,6 +84,8 @@ class Spec:
             raise ValueError(f"map {self.map!r}")
         if self.method not in METHODS:
             raise ValueError(f"method {self.method!r}")
+        if self.map in UNDIRECTED_MAPS and self.method != "product":
+            raise ValueError("an undirected map has one bucket per pair")
         if self.window:
             if self.grid_h % self.window or self.grid_w % self.window:
                 raise ValueError("window must divide the grid")
@@ -119,11 +125,21 @@ class Spec:
             return half_width(window=max(r, c))
         return half_width(self.alpha, self.beta, self.gamma, self.reading)
 
+    @property
+    def undirected(self):
+        return self.map in UNDIRECTED_MAPS
+
     def g(self, x):
         """Per-axis index of offset x (identity for the Swin map)."""
+        if self.undirected:
+            raise ValueError("an undirected map has no per-axis index")
         if self.map == "swin":
             return int(x)
         return piecewise_index(x, self.alpha, self.beta, self.gamma, self.reading)
+
+    def u(self, dy, dx):
+        """Undirected index in [0, H] of the offset (dy, dx)."""
+        return undirected_index(dy, dx, self.map, self.alpha, self.beta, self.gamma, self.reading)
 
 
 def num_buckets(spec):
@@ -131,10 +147,13 @@ def num_buckets(spec):
 
     (2H+1)^2 rows for the Product mapping (iRPE page, Method, "Product");
     (2M-1)^2 for a Swin window (Swin post, section 3.1); 2 (2H+1) for the
-    Cross mapping (iRPE page, Method, "Cross").
+    Cross mapping (iRPE page, Method, "Cross"); 2H+1 for the undirected
+    maps (eqs. 19-21; only rows H..2H are reached).
     """
     h = spec.half_width()
     s = 2 * h + 1
+    if spec.undirected:
+        return h, s, s
     return h, s, (2 * s if spec.method == "cross" else s * s)
 
 
@@ -172,6 +191,8 @@ def pair_rows(spec, p_query, p_key):
     if p_query is None or p_key is None:
         return []
     h, s, _ = num_buckets(spec)
+    if spec.undirected:
+        return [spec.u(p_query[0] - p_key[0], p_query[1] - p_key[1]) + h]
     gy, gx = spec.g(p_query[0] - p_key[0]), spec.g(p_query[1] - p_key[1])
     if not (-h <= gy <= h and -h <= gx <= h):
         raise ValueError(f"index ({gy},{gx}) outside the table half-width {h}")
