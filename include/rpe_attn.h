@@ -77,7 +77,24 @@ typedef enum rpe_status {
 enum { RPE_BF16 = 0, RPE_FP32 = 1 };
 enum { RPE_MODE_NONE = 0, RPE_MODE_BIAS = 1, RPE_MODE_CONTEXTUAL = 2 };
 enum { RPE_TERM_K = 1, RPE_TERM_Q = 2, RPE_TERM_V = 4 };
-enum { RPE_MAP_SWIN = 0, RPE_MAP_PIECEWISE = 1 };
+enum {
+  RPE_MAP_SWIN = 0,
+  RPE_MAP_PIECEWISE = 1,
+  /* Undirected maps of the offset's distance (iRPE page, Method, Euclidean eqs. 19-20 and
+   * Quantization eq. 21, with the page's and the released code's readings; "Paper vs code").
+   * The index u(dy, dx) = g(m) >= 0 with g of eq. 18 (alpha, beta, gamma, rounding) and
+   *   EUCLIDEAN:           m = sqrt(dy^2 + dx^2), real-valued (|m| <= alpha: rounded)
+   *   EUCLIDEAN_ROUNDED:   m = sqrt(dy^2 + dx^2) rounded half away first
+   *   QUANTIZED:           m = position of sqrt(dy^2 + dx^2) among the distances integer
+   *                        offsets can have (the sums of two squares, numbered from 0)
+   *   QUANTIZED_SQUARED:   m = dy^2 + dx^2
+   * Their tables have S = 2H+1 rows, row u + H for a pair.  rpe_attn_fwd takes them
+   * after rpe_attn_undirected_to_product. */
+  RPE_MAP_EUCLIDEAN = 2,
+  RPE_MAP_EUCLIDEAN_ROUNDED = 3,
+  RPE_MAP_QUANTIZED = 4,
+  RPE_MAP_QUANTIZED_SQUARED = 5
+};
 enum { RPE_ROUND_CAPPED = 0, RPE_ROUND_TRUNC = 1 };
 enum { RPE_TABLE_BIAS = 0, RPE_TABLE_VECTOR = 1 };   /* rpe_attn_cross_to_product */
 
@@ -102,7 +119,8 @@ typedef struct rpe_attn_desc {
 rpe_status rpe_attn_validate(const rpe_attn_desc* desc);
 
 /* Table geometry of a descriptor: half-width H, S = 2H+1 entries per axis and
- * S*S table rows.  Host only; any output pointer may be NULL. */
+ * S*S table rows (S rows for an undirected map).  Host only; any output pointer
+ * may be NULL. */
 rpe_status rpe_attn_num_buckets(const rpe_attn_desc* desc, int32_t* half_width,
                                 int32_t* per_axis, int32_t* total);
 
@@ -144,7 +162,23 @@ rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void
 rpe_status rpe_attn_cross_to_product(const rpe_attn_desc* desc, int32_t kind, const void* cross,
                                      void* product, void* stream);
 
-/* The attention forward.  q, k, v, o required (may be NULL when batch == 0, which
+/* Undirected maps (RPE_MAP_EUCLIDEAN .. RPE_MAP_QUANTIZED_SQUARED): the index of a
+ * pair depends on its offset (dy, dx) only, so the Swin map's table over raw
+ * offsets, H' = max(R, C) - 1 for a unit of R x C positions and S' = 2H'+1,
+ *     product[(dy + H') * S' + (dx + H')] = table[u(dy, dx) + H]   (|dy| < R, |dx| < C; other rows 0)
+ * gives the same attention: call rpe_attn_fwd with this descriptor's map set to
+ * RPE_MAP_SWIN and the product table.
+ *   table   : device, [tables][S][width] (S = 2H+1 from rpe_attn_num_buckets)
+ *   product : device, [tables][S'*S'][width], written (caller-owned; no overlap)
+ *   kind, width, tables: as for rpe_attn_cross_to_product.
+ * The indices are computed on the device in float64.  Asynchronous on `stream`.
+ * Errors: descriptor validation; RPE_E_MODE if desc.map is not undirected or for a
+ * kind the mode has no table for; RPE_E_BUCKETS if S'*S' > 32767; RPE_E_NULL. */
+rpe_status rpe_attn_undirected_to_product(const rpe_attn_desc* desc, int32_t kind, const void* table,
+                                          void* product, void* stream);
+
+/* The attention forward (maps RPE_MAP_SWIN and RPE_MAP_PIECEWISE; RPE_E_MODE for
+ * an undirected map).  q, k, v, o required (may be NULL when batch == 0, which
  * launches nothing); bias required in bias mode;
  * rk / rq / rv required for the contextual terms requested (others ignored);
  * lse nullable.  o must not alias q, k or v.  Asynchronous on `stream`. */

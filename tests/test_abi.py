@@ -156,3 +156,28 @@ def test_cross_to_product_rejects_before_device():
     bad = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), mode="contextual", terms="k",
                         map="piecewise", alpha=-1.0, beta=3.8, gamma=15.2)
     assert f(ctypes.byref(bad), V, one, one, None) == -7
+
+
+@pytest.mark.parametrize("m", ["euclidean", "euclidean_rounded", "quantized", "quantized_squared"])
+def test_undirected_maps_geometry_and_rejections(m):
+    lib = _lib_or_skip()
+    one = ctypes.c_void_p(16)
+    d = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), prefix_tokens=1, mode="contextual",
+                      terms="k", map=m, alpha=1.9, beta=3.8, gamma=15.2)
+    assert pkg.rpe_attn_validate(d) == 0
+    spec = Spec(14, 14, prefix=1, mode="contextual", terms={"k"}, map=m, alpha=1.9, beta=3.8, gamma=15.2)
+    assert pkg.rpe_attn_num_buckets(d) == num_buckets(spec) == (4, 9, 9)
+    # the forward and the per-axis tools take the expanded tables only
+    assert lib.rpe_attn_fwd(ctypes.byref(d), one, one, one, None, None, one, None, one, None, None) == -4
+    assert lib.rpe_attn_bucket_map(ctypes.byref(d), one, None) == -4
+    assert lib.rpe_attn_axis_index(ctypes.byref(d), 5, one, None) == -4
+    assert lib.rpe_attn_cross_to_product(ctypes.byref(d), _lib.RPE_TABLE_VECTOR, one, one, None) == -4
+    f = lib.rpe_attn_undirected_to_product
+    assert f(ctypes.byref(d), _lib.RPE_TABLE_VECTOR, None, one, None) == -1
+    assert f(ctypes.byref(d), _lib.RPE_TABLE_BIAS, one, one, None) == -4
+    big = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(100, 100), mode="bias", map=m,
+                        alpha=1.9, beta=3.8, gamma=15.2)
+    assert f(ctypes.byref(big), _lib.RPE_TABLE_BIAS, one, one, None) == -6     # 199^2 raw offsets
+    pw = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), mode="bias", map="piecewise",
+                       alpha=1.9, beta=3.8, gamma=15.2)
+    assert f(ctypes.byref(pw), _lib.RPE_TABLE_BIAS, one, one, None) == -4       # not undirected

@@ -16,6 +16,7 @@ RPE_BF16, RPE_FP32 = 0, 1
 RPE_MODE_NONE, RPE_MODE_BIAS, RPE_MODE_CONTEXTUAL = 0, 1, 2
 RPE_TERM_K, RPE_TERM_Q, RPE_TERM_V = 1, 2, 4
 RPE_MAP_SWIN, RPE_MAP_PIECEWISE = 0, 1
+RPE_MAP_EUCLIDEAN, RPE_MAP_EUCLIDEAN_ROUNDED, RPE_MAP_QUANTIZED, RPE_MAP_QUANTIZED_SQUARED = 2, 3, 4, 5
 RPE_ROUND_CAPPED, RPE_ROUND_TRUNC = 0, 1
 RPE_TABLE_BIAS, RPE_TABLE_VECTOR = 0, 1
 
@@ -27,8 +28,8 @@ STATUS_NAMES = {
 
 # Every symbol include/rpe_attn.h declares.
 EXPORTS = ("rpe_attn_validate", "rpe_attn_num_buckets", "rpe_attn_unit_size", "rpe_attn_axis_index",
-           "rpe_attn_bucket_map", "rpe_attn_cross_to_product", "rpe_attn_fwd", "rpe_status_str",
-           "rpe_attn_version")
+           "rpe_attn_bucket_map", "rpe_attn_cross_to_product", "rpe_attn_undirected_to_product", "rpe_attn_fwd",
+           "rpe_status_str", "rpe_attn_version")
 
 
 class Desc(ctypes.Structure):
@@ -80,6 +81,8 @@ def load():
         lib.rpe_attn_bucket_map.restype = i32
         lib.rpe_attn_cross_to_product.argtypes = [P(Desc), i32, vp, vp, vp]
         lib.rpe_attn_cross_to_product.restype = i32
+        lib.rpe_attn_undirected_to_product.argtypes = [P(Desc), i32, vp, vp, vp]
+        lib.rpe_attn_undirected_to_product.restype = i32
         lib.rpe_attn_fwd.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.rpe_attn_fwd.restype = i32
         lib.rpe_status_str.argtypes = [i32]

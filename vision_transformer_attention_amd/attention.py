@@ -13,7 +13,10 @@ from ._lib import Desc, check, load
 
 _MODES = {"none": _lib.RPE_MODE_NONE, "bias": _lib.RPE_MODE_BIAS,
           "contextual": _lib.RPE_MODE_CONTEXTUAL}
-_MAPS = {"swin": _lib.RPE_MAP_SWIN, "piecewise": _lib.RPE_MAP_PIECEWISE}
+_MAPS = {"swin": _lib.RPE_MAP_SWIN, "piecewise": _lib.RPE_MAP_PIECEWISE, "euclidean": _lib.RPE_MAP_EUCLIDEAN,
+         "euclidean_rounded": _lib.RPE_MAP_EUCLIDEAN_ROUNDED, "quantized": _lib.RPE_MAP_QUANTIZED,
+         "quantized_squared": _lib.RPE_MAP_QUANTIZED_SQUARED}
+UNDIRECTED = ("euclidean", "euclidean_rounded", "quantized", "quantized_squared")
 _ROUNDING = {"capped": _lib.RPE_ROUND_CAPPED, "trunc": _lib.RPE_ROUND_TRUNC}
 _TERM_BITS = {"k": _lib.RPE_TERM_K, "q": _lib.RPE_TERM_Q, "v": _lib.RPE_TERM_V}
 
@@ -113,6 +116,34 @@ def rpe_attn_cross_to_product(desc, table):
     return out
 
 
+def rpe_attn_undirected_to_product(desc, table):
+    """The Swin-map table over raw offsets [T, S'*S'(, d)] equal to an undirected-map
+    table [T, S(, d)] (S from rpe_attn_num_buckets, S' = 2 max(R, C) - 1)."""
+    torch = _torch()
+    _, s, rows = rpe_attn_num_buckets(desc)
+    kind = _lib.RPE_TABLE_BIAS if table.dim() == 2 else _lib.RPE_TABLE_VECTOR
+    th = desc.heads if desc.tables_per_head else 1
+    want = (th, rows) if kind == _lib.RPE_TABLE_BIAS else (th, rows, desc.head_dim)
+    if tuple(table.shape) != want or not table.is_contiguous() or not table.is_cuda:
+        raise ValueError(f"undirected table must be a contiguous device tensor {list(want)}")
+    r = desc.window if desc.window else desc.grid_h
+    c = desc.window if desc.window else desc.grid_w
+    sp = 2 * max(r, c) - 1
+    out = torch.empty((th, sp * sp) + tuple(table.shape[2:]), dtype=table.dtype, device=table.device)
+    check("rpe_attn_undirected_to_product",
+          load().rpe_attn_undirected_to_product(ctypes.byref(desc), int(kind), _ptr(table), _ptr(out),
+                                                _stream(table.device)))
+    return out
+
+
+def _swin_desc(desc):
+    """The same descriptor with the Swin map (the expanded tables' geometry)."""
+    d = Desc()
+    ctypes.memmove(ctypes.byref(d), ctypes.byref(desc), ctypes.sizeof(Desc))
+    d.map = _lib.RPE_MAP_SWIN
+    return d
+
+
 def rpe_attn_fwd(q, k, v, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
                  alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None,
                  rq=None, rk=None, rv=None, out=None, return_lse=False, method="product"):
@@ -126,8 +157,26 @@ def rpe_attn_fwd(q, k, v, *, grid, window=0, prefix_tokens=0, mode="none", terms
     method="cross": the tables are Cross-mapping tables with 2S rows (row-offset
     half, then column-offset half); they are rewritten as Product tables by
     ``rpe_attn_cross_to_product`` and the Product forward runs on those.
+
+    An undirected map ("euclidean", "euclidean_rounded", "quantized",
+    "quantized_squared") takes tables of S rows; they are expanded by
+    ``rpe_attn_undirected_to_product`` and the forward runs with the Swin map.
     """
     torch = _torch()
+    if map in UNDIRECTED:
+        if mode == "none":
+            raise ValueError("an undirected map needs bias or contextual mode")
+        B, H, _, d = q.shape
+        tabs = [t for t in (bias, rq, rk, rv) if t is not None]
+        per_head = any(t.shape[0] == H and H > 1 for t in tabs)
+        desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
+                         dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms,
+                         map=map, alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale,
+                         tables_per_head=per_head)
+        conv = lambda t, used: rpe_attn_undirected_to_product(desc, t) if (t is not None and used) else None
+        bias = conv(bias, mode == "bias")
+        rq, rk, rv = (conv(t, mode == "contextual" and n in terms) for n, t in (("q", rq), ("k", rk), ("v", rv)))
+        map = "swin"
     if method == "cross":
         if mode == "none":
             raise ValueError("the Cross mapping needs bias or contextual mode")
@@ -199,6 +248,11 @@ class PreparedFwd:
     def __init__(self, desc, ptrs, keep, device, convert=()):
         self._lib = load()
         self._desc = desc
+        # an undirected map's tables are expanded under its own descriptor; the
+        # forward then runs with the Swin map
+        self._undirected = desc.map in (_lib.RPE_MAP_EUCLIDEAN, _lib.RPE_MAP_EUCLIDEAN_ROUNDED,
+                                        _lib.RPE_MAP_QUANTIZED, _lib.RPE_MAP_QUANTIZED_SQUARED) and desc.mode
+        self._fdesc = _swin_desc(desc) if self._undirected else desc
         self._args = ptrs
         self._keep = keep
         self._device = device
@@ -207,10 +261,10 @@ class PreparedFwd:
     def __call__(self, stream=None):
         torch = _torch()
         s = ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream if stream is None else stream)
+        conv = self._lib.rpe_attn_undirected_to_product if self._undirected else self._lib.rpe_attn_cross_to_product
         for kind, src, dst in self._convert:
-            check("rpe_attn_cross_to_product",
-                  self._lib.rpe_attn_cross_to_product(ctypes.byref(self._desc), kind, src, dst, s))
-        check("rpe_attn_fwd", self._lib.rpe_attn_fwd(ctypes.byref(self._desc), *self._args, s))
+            check("table conversion", conv(ctypes.byref(self._desc), kind, src, dst, s))
+        check("rpe_attn_fwd", self._lib.rpe_attn_fwd(ctypes.byref(self._fdesc), *self._args, s))
 
 
 def prepare_fwd(q, k, v, *, out, lse=None, **kw):
@@ -235,13 +289,14 @@ def prepare_fwd(q, k, v, *, out, lse=None, **kw):
     rk = kw.get("rk") if "k" in terms else None
     rv = kw.get("rv") if "v" in terms else None
     convert = []
-    if kw.get("method", "product") == "cross":
+    undirected = kw.get("map", "swin") in UNDIRECTED
+    if kw.get("method", "product") == "cross" or undirected:
         prod = []
         for t in (bias, rq, rk, rv):
             if t is None:
                 prod.append(None)
                 continue
-            p = rpe_attn_cross_to_product(desc, t)
+            p = rpe_attn_undirected_to_product(desc, t) if undirected else rpe_attn_cross_to_product(desc, t)
             kind = _lib.RPE_TABLE_BIAS if t.dim() == 2 else _lib.RPE_TABLE_VECTOR
             convert.append((kind, _ptr(t), _ptr(p)))
             prod.append(p)

@@ -13,6 +13,9 @@ hipError_t launch_bucket_map(int P, int R, int C, int half, int S, int map, int 
                              hipStream_t stream);
 hipError_t launch_cross_to_product(bool bf16, const void* cross, void* product, int S, int width,
                                    int64_t total, hipStream_t stream);
+hipError_t launch_undirected_to_product(bool bf16, bool f32, const void* table, void* product, int R, int C,
+                                        int Hp, int half, int map, int rounding, double alpha, double beta,
+                                        double gamma, int width, int64_t total, hipStream_t stream);
 }  // namespace rpe
 
 extern "C" {
@@ -49,6 +52,7 @@ rpe_status rpe_attn_axis_index(const rpe_attn_desc* desc, int32_t length, int16_
                                void* stream) {
   const int st = rpe::validate(desc);
   if (st != RPE_OK) return static_cast<rpe_status>(st);
+  if (rpe::is_undirected(desc)) return RPE_E_MODE;
   if (!dev_out) return RPE_E_NULL;
   if (length < 1 || length > 4096) return RPE_E_SHAPE;
   const int map = desc->mode == RPE_MODE_NONE ? RPE_MAP_SWIN : desc->map;
@@ -61,6 +65,7 @@ rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void
   int h = 0, s = 0, nb = 0;
   const int st = rpe::table_geometry(desc, &h, &s, &nb);
   if (st != RPE_OK) return static_cast<rpe_status>(st);
+  if (rpe::is_undirected(desc)) return RPE_E_MODE;
   if (!dev_map) return RPE_E_NULL;
   const int R = desc->window ? desc->window : desc->grid_h;
   const int C = desc->window ? desc->window : desc->grid_w;
@@ -88,11 +93,42 @@ rpe_status rpe_attn_cross_to_product(const rpe_attn_desc* desc, int32_t kind, co
   } else {
     return RPE_E_MODE;
   }
+  if (rpe::is_undirected(desc)) return RPE_E_MODE;
   if (!cross || !product) return RPE_E_NULL;
   const int64_t tables = desc->tables_per_head ? desc->heads : 1;
   const int64_t total = tables * nb * width;
   const hipError_t e = rpe::launch_cross_to_product(bf16, cross, product, s, width, total,
                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RPE_OK : RPE_E_HIP;
+}
+
+rpe_status rpe_attn_undirected_to_product(const rpe_attn_desc* desc, int32_t kind, const void* table,
+                                          void* product, void* stream) {
+  int h = 0, s = 0, nb = 0;
+  const int st = rpe::table_geometry(desc, &h, &s, &nb);
+  if (st != RPE_OK) return static_cast<rpe_status>(st);
+  if (!rpe::is_undirected(desc)) return RPE_E_MODE;
+  int width = 0;
+  bool bf16 = false;
+  if (kind == RPE_TABLE_BIAS && desc->mode == RPE_MODE_BIAS) {
+    width = 1;
+  } else if (kind == RPE_TABLE_VECTOR && desc->mode == RPE_MODE_CONTEXTUAL) {
+    width = desc->head_dim;
+    bf16 = desc->dtype == RPE_BF16;
+  } else {
+    return RPE_E_MODE;
+  }
+  const int R = desc->window ? desc->window : desc->grid_h;
+  const int C = desc->window ? desc->window : desc->grid_w;
+  const int Hp = (R > C ? R : C) - 1;
+  const int64_t sp = 2 * Hp + 1;
+  if (sp * sp > 32767) return RPE_E_BUCKETS;
+  if (!table || !product) return RPE_E_NULL;
+  const int64_t tables = desc->tables_per_head ? desc->heads : 1;
+  const int64_t total = tables * sp * sp * width;
+  const hipError_t e = rpe::launch_undirected_to_product(bf16, !bf16, table, product, R, C, Hp, h, desc->map,
+                                                         desc->rounding, desc->alpha, desc->beta, desc->gamma,
+                                                         width, total, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RPE_OK : RPE_E_HIP;
 }
 

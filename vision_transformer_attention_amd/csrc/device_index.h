@@ -26,4 +26,14 @@ __device__ __forceinline__ int axis_index(int x, int map, int rounding, double a
   return x > 0 ? mag : -mag;
 }
 
+// Eq. 18 for a real r >= 0 (an offset's distance): r <= alpha keeps its
+// rounded value (half away from zero); beyond alpha as for an integer offset.
+__device__ __forceinline__ int axis_index_real(double r, int rounding, double alpha, double beta,
+                                               double gamma) {
+  if (r <= alpha) return static_cast<int>(floor(r + 0.5));
+  const double s = alpha + log(r / alpha) / log(gamma / alpha) * (beta - alpha);
+  const double cap = fmin(beta, floor(s + 0.5));
+  return rounding == RPE_ROUND_CAPPED ? static_cast<int>(floor(cap + 0.5)) : static_cast<int>(floor(cap));
+}
+
 }  // namespace rpe

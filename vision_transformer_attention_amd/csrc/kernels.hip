@@ -94,6 +94,106 @@ hipError_t launch_cross_to_product(bool bf16, const void* cross, void* product, 
   return hipGetLastError();
 }
 
+// Undirected maps as the Swin map's table over raw offsets (see
+// rpe_attn_undirected_to_product): product[t][(dy+H')*S' + dx+H'][w] =
+// table[t][u(dy, dx) + H][w] for |dy| < R, |dx| < C, else 0.  Each workgroup
+// first numbers the sums of two squares up to (R-1)^2 + (C-1)^2 in LDS (the
+// Quantization map's distance positions, eq. 21), then copies its share.
+constexpr int kMaxSquares = 16384;   // (R-1)^2 + (C-1)^2 < this (S'*S' <= 32767 keeps R, C <= 90)
+
+template <typename T>
+__global__ void __launch_bounds__(256) undirected_to_product_kernel(const T* __restrict__ table,
+                                                                    T* __restrict__ product, int R, int C,
+                                                                    int Hp, int half, int map, int rounding,
+                                                                    double alpha, double beta, double gamma,
+                                                                    int width, int64_t total) {
+  __shared__ unsigned short rank[kMaxSquares];
+  __shared__ unsigned char is_sum[kMaxSquares];
+  __shared__ int part[256];
+  const int kmax = (R - 1) * (R - 1) + (C - 1) * (C - 1);
+  if (map == RPE_MAP_QUANTIZED) {
+    for (int m = threadIdx.x; m <= kmax; m += blockDim.x) is_sum[m] = 0;
+    __syncthreads();
+    int amax = 0;
+    while ((amax + 1) * (amax + 1) <= kmax) ++amax;
+    const int na = amax + 1;
+    for (int e = threadIdx.x; e < na * na; e += blockDim.x) {
+      const int a = e / na, b = e - (e / na) * na;
+      if (a * a + b * b <= kmax) is_sum[a * a + b * b] = 1;
+    }
+    __syncthreads();
+    // rank[m] = number of sums of two squares below m: chunked count, then a scan
+    const int chunk = (kmax + 1 + blockDim.x - 1) / blockDim.x;
+    const int m0 = threadIdx.x * chunk;
+    int cnt = 0;
+    for (int m = m0; m < m0 + chunk && m <= kmax; ++m) cnt += is_sum[m];
+    part[threadIdx.x] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int run = 0;
+      for (int i = 0; i < static_cast<int>(blockDim.x); ++i) {
+        const int c = part[i];
+        part[i] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+    int run = part[threadIdx.x];
+    for (int m = m0; m < m0 + chunk && m <= kmax; ++m) {
+      rank[m] = static_cast<unsigned short>(run);
+      run += is_sum[m];
+    }
+    __syncthreads();
+  }
+  const int Sp = 2 * Hp + 1;
+  const int64_t per_table = static_cast<int64_t>(Sp) * Sp * width;
+  const int S = 2 * half + 1;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = e / per_table;
+    const int64_t r = e - t * per_table;
+    const int cell = static_cast<int>(r / width), w = static_cast<int>(r - static_cast<int64_t>(cell) * width);
+    const int dy = cell / Sp - Hp, dx = cell - (cell / Sp) * Sp - Hp;
+    T val = static_cast<T>(0.0f);
+    if (dy > -R && dy < R && dx > -C && dx < C) {
+      const int k = dy * dy + dx * dx;
+      int u;
+      if (map == RPE_MAP_EUCLIDEAN) {
+        u = axis_index_real(sqrt(static_cast<double>(k)), rounding, alpha, beta, gamma);
+      } else if (map == RPE_MAP_EUCLIDEAN_ROUNDED) {
+        u = axis_index(static_cast<int>(floor(sqrt(static_cast<double>(k)) + 0.5)), RPE_MAP_PIECEWISE, rounding,
+                       alpha, beta, gamma);
+      } else if (map == RPE_MAP_QUANTIZED) {
+        u = axis_index(rank[k], RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
+      } else {
+        u = axis_index(k, RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
+      }
+      u = u < 0 ? 0 : (u > half ? half : u);   // in [0, H] by construction
+      val = table[t * static_cast<int64_t>(S) * width + static_cast<int64_t>(u + half) * width + w];
+    }
+    product[e] = val;
+  }
+}
+
+hipError_t launch_undirected_to_product(bool bf16, bool f32, const void* table, void* product, int R, int C,
+                                        int Hp, int half, int map, int rounding, double alpha, double beta,
+                                        double gamma, int width, int64_t total, hipStream_t stream) {
+  if ((R - 1) * (R - 1) + (C - 1) * (C - 1) >= kMaxSquares) return hipErrorInvalidValue;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  (void)f32;
+  if (bf16)
+    hipLaunchKernelGGL(undirected_to_product_kernel<__bf16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, static_cast<const __bf16*>(table), static_cast<__bf16*>(product), R, C, Hp, half,
+                       map, rounding, alpha, beta, gamma, width, total);
+  else
+    hipLaunchKernelGGL(undirected_to_product_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, static_cast<const float*>(table), static_cast<float*>(product), R, C, Hp, half,
+                       map, rounding, alpha, beta, gamma, width, total);
+  return hipGetLastError();
+}
+
 hipError_t launch_axis_index(int length, int map, int rounding, double alpha, double beta,
                              double gamma, int16_t* out, hipStream_t stream) {
   const int n = 2 * length - 1;

@@ -98,8 +98,8 @@ int validate(const rpe_attn_desc* d) {
   if (d->mode != RPE_MODE_CONTEXTUAL && d->terms) return RPE_E_MODE;
   if (d->mode == RPE_MODE_CONTEXTUAL && !d->terms) return RPE_E_MODE;
   if (d->mode != RPE_MODE_NONE) {
-    if (d->map != RPE_MAP_SWIN && d->map != RPE_MAP_PIECEWISE) return RPE_E_MODE;
-    if (d->map == RPE_MAP_PIECEWISE) {
+    if (d->map < RPE_MAP_SWIN || d->map > RPE_MAP_QUANTIZED_SQUARED) return RPE_E_MODE;
+    if (d->map != RPE_MAP_SWIN) {
       if (d->rounding != RPE_ROUND_CAPPED && d->rounding != RPE_ROUND_TRUNC) return RPE_E_MODE;
       if (!finite(d->alpha) || !finite(d->beta) || !finite(d->gamma)) return RPE_E_PARAMS;
       if (!(d->alpha > 0) || !(d->gamma > d->alpha) || !(d->beta >= d->alpha)) return RPE_E_PARAMS;
@@ -127,7 +127,7 @@ int table_geometry(const rpe_attn_desc* d, int* half, int* S, int* nb) {
   if (static_cast<int64_t>(s) * s > 32767) return RPE_E_BUCKETS;
   if (half) *half = h;
   if (S) *S = s;
-  if (nb) *nb = s * s;
+  if (nb) *nb = is_undirected(d) ? s : s * s;   // undirected: one index per pair
   return RPE_OK;
 }
 
@@ -156,6 +156,7 @@ FastDiv make_fastdiv(uint32_t d) {
 int make_plan(const rpe_attn_desc* d, Params* p) {
   int st = validate(d);
   if (st != RPE_OK) return st;
+  if (is_undirected(d)) return RPE_E_MODE;   // the forward takes their expanded Product tables
   std::memset(p, 0, sizeof(*p));
   if (d->mode == RPE_MODE_NONE) {
     p->half = 0; p->S = 1; p->nb = 1;  // no table

@@ -118,6 +118,11 @@ struct Params {
 // Validation only (no derived plan).  Returns an rpe_status.
 int validate(const rpe_attn_desc* d);
 
+// A descriptor with a table and an undirected map (Euclidean or Quantization).
+inline bool is_undirected(const rpe_attn_desc* d) {
+  return d->mode != RPE_MODE_NONE && d->map >= RPE_MAP_EUCLIDEAN && d->map <= RPE_MAP_QUANTIZED_SQUARED;
+}
+
 // Table geometry; returns an rpe_status.
 int table_geometry(const rpe_attn_desc* d, int* half, int* S, int* nb);
 

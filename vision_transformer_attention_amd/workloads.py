@@ -107,6 +107,12 @@ WORKLOADS = {
         gamma=15.2, dtype=BF16, table_rows=81, tables_per_head=False,
         description="DETR-like encoder iRPE on keys, non-square 25x38 grid (950 tokens, an 800x1216 "
                     "image at stride 32): B8, h8 d32 bf16, r^K 81x32 shared"),
+    "deit_s_irpe_bias_euclid": Workload(
+        9, "deit_s_irpe_bias_euclid", batch=64, heads=6, head_dim=64, grid_h=14, grid_w=14, window=0,
+        prefix=1, mode="bias", map="euclidean", alpha=1.9, beta=3.8, gamma=15.2, dtype=BF16,
+        table_rows=9, tables_per_head=True,
+        description="DeiT-S iRPE bias mode with the undirected Euclidean mapping: B64, 197 tokens, "
+                    "h6 d64 bf16, 9-entry bias per head"),
 }
 
 
