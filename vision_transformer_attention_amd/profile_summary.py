@@ -5,6 +5,10 @@ Two inputs are understood:
 
 * ``--stats DIR``: the ``*_kernel_stats.csv`` of a ``rocprofv3 --kernel-trace
   --stats --output-format csv`` run; prints per-kernel calls and durations.
+* ``--trace DIR --kernel SUBSTR --skip A --count B``: from the
+  ``*_kernel_trace.csv`` of the same run, the durations of dispatches A .. A+B-1
+  (in dispatch order) of the kernels whose name contains SUBSTR: the timed
+  launches of one workload when several workloads share a kernel instance.
 * ``--pmc DIR``: the ``*counter_collection.csv`` of a ``rocprofv3 --pmc
   FETCH_SIZE`` (or ``WRITE_SIZE``) run of ``bench.py --copy-probe MIB``; prints
   the counter per dispatch of the attention kernel and of the plain copy
@@ -87,6 +91,18 @@ def stats_summary(d):
     return "\n".join(lines)
 
 
+def trace_summary(d, substr, skip, count):
+    rows = [r for r in csv.DictReader(open(_one("*kernel_trace.csv", d))) if substr in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    sel = rows[skip:skip + count]
+    if len(sel) < count:
+        raise SystemExit(f"only {len(rows)} dispatches of {substr}")
+    us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel]
+    name = demangle([sel[0]["Kernel_Name"]])[0]
+    return (f"{name}: dispatches {skip}..{skip + count - 1} of {len(rows)} (dispatch order): "
+            f"avg {sum(us) / len(us):.2f} us, min {min(us):.2f}, max {max(us):.2f}")
+
+
 def pmc_summary(d, copy_mib):
     rows = list(csv.DictReader(open(_one("*counter_collection.csv", d))))
     by = collections.defaultdict(lambda: collections.defaultdict(list))
@@ -126,6 +142,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--stats")
     ap.add_argument("--pmc")
+    ap.add_argument("--trace")
+    ap.add_argument("--kernel", default=FWD_KERNEL)
+    ap.add_argument("--skip", type=int, default=0)
+    ap.add_argument("--count", type=int, default=1)
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--hash", action="store_true", help="print the forward kernel's source hash")
     a = ap.parse_args()
@@ -133,6 +153,8 @@ def main():
         print(kernel_source_hash())
     if a.stats:
         print(stats_summary(a.stats))
+    if a.trace:
+        print(trace_summary(a.trace, a.kernel, a.skip, a.count))
     if a.pmc:
         print(pmc_summary(a.pmc, a.copy_mib))
 
