@@ -6,7 +6,6 @@
 // forward is in fwd_kernel.h.
 #include <hip/hip_runtime.h>
 
-#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -15,15 +14,6 @@
 #include "plan.h"
 
 namespace rpe {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kNW = 4;               // waves per workgroup
-constexpr int kThreads = kNW * 64;
-constexpr float kLazyTau = 8.0f;     // running max moves only when a row grows by > 2^8
-constexpr float kNegBig = -FLT_MAX;  // initial running max (finite: keeps x - m free of NaN)
 
 __global__ void axis_index_kernel(int length, int map, int rounding, double alpha, double beta,
                                   double gamma, int16_t* out) {
