@@ -225,7 +225,17 @@ rpe_fwd_kernel(Params p) {
   // A workgroup takes p.upw consecutive units of one (batch, head) (p.upw > 1
   // only for small units without contextual terms, n_qc = 1 then).
   const uint32_t ugrp = fdiv(task, p.dv_qc);
-  const int qc = static_cast<int>(task - ugrp * static_cast<uint32_t>(p.n_qc));
+  // Chunk qc of the unit, with the chunk order rotated every 32 tasks.  The
+  // dispatcher hands an XCD's workgroups to its 32 CUs in turn, so without the
+  // rotation a CU would hold the same chunk of every unit it gets, and with
+  // uneven chunks (7 tiles as 3 + 4) some CUs would get only long ones.  The
+  // rotation depends on the unit alone, so the unit's chunks stay a permutation.
+  int qc;
+  {
+    const uint32_t raw = task - ugrp * static_cast<uint32_t>(p.n_qc);
+    const uint32_t rot = ((ugrp * static_cast<uint32_t>(p.n_qc)) >> 5) + raw;
+    qc = static_cast<int>(rot - fdiv(rot, p.dv_qc) * static_cast<uint32_t>(p.n_qc));
+  }
   const uint32_t unit0 = ugrp * static_cast<uint32_t>(p.upw);
   const uint32_t bh = fdiv(unit0, p.dv_U);
   const int w_img0 = static_cast<int>(unit0 - bh * static_cast<uint32_t>(p.U));
