@@ -143,6 +143,12 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   return (t + ((n - t) >> f.s1)) >> f.s2;
 }
 
+// The 4-byte form of dma16: lane l's 4 bytes from g land at LDS byte address lds + 4 * l.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(base) : "memory", "m0");
+}
+
 // Workgroup barrier that orders LDS traffic but leaves the direct-to-LDS loads
 // in flight (a plain __syncthreads would drain them).
 __device__ __forceinline__ void lds_barrier() {
@@ -440,8 +446,18 @@ rpe_fwd_kernel(Params p) {
     }
   }
 
-  // ---- start the ring now (the prologue below overlaps its latency); the Q
-  // and rK loads above are older, so waiting for element 0 also covers them.
+  // ---- bias mode: the head's table goes straight to LDS (64 entries per
+  // instruction, instruction k from wave k % NW); each lane scales its own
+  // entries by log2(e) once its copies have landed, before the prologue barrier.
+  if constexpr (MODE == RPE_MODE_BIAS) {
+    const char* bt = reinterpret_cast<const char*>(p.bias + head * p.tab_head_stride);
+    const uint32_t lds_tab = lds_ring - p.off_stage + p.off_tab;
+    for (int k = wid; k * 64 < p.nb; k += NW)
+      if (k * 64 + lane < p.nb) dma4(bt + (k * 64 + lane) * 4, lds_tab + k * 256);
+  }
+
+  // ---- start the ring now (the prologue below overlaps its latency); the Q,
+  // rK and bias loads above are older, so waiting for element 0 also covers them.
   int st_cur = 0, st_iss = 0;
   int iss_k = 0, iss_loc = 0;   // unit and position of the next element to issue
   auto issue_next = [&]() {
@@ -493,10 +509,6 @@ rpe_fwd_kernel(Params p) {
       reinterpret_cast<float*>(smem + p.off_tqz)[i] = 0.0f;
       reinterpret_cast<float*>(smem + p.off_tqn)[i] = -INFINITY;
     }
-  }
-  if constexpr (MODE == RPE_MODE_BIAS) {
-    const float* bt = p.bias + head * p.tab_head_stride;
-    for (int i = tid; i < p.nb; i += nth) gtab[i] = bt[i] * p.bias_mul;
   }
   if constexpr (MODE == RPE_MODE_NONE) {
     for (int i = tid; i < p.nb; i += nth) gtab[i] = 0.0f;
@@ -641,7 +653,13 @@ rpe_fwd_kernel(Params p) {
     // this wave's rK copies are older than its ring loads
     if (p.rk_lds) wait_vmcnt_floor((L < ST - 1 ? L : ST - 1) * lpe);
   }
-  lds_barrier();  // prologue tables (and rK copies) visible; ring loads stay in flight
+  if constexpr (MODE == RPE_MODE_BIAS) {
+    // this wave's bias copies are older than its ring loads
+    wait_vmcnt_floor((L < ST - 1 ? L : ST - 1) * lpe);
+    for (int k = wid; k * 64 < p.nb; k += NW)
+      if (k * 64 + lane < p.nb) gtab[k * 64 + lane] *= p.bias_mul;
+  }
+  lds_barrier();  // prologue tables (and rK / bias copies) visible; ring loads stay in flight
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
   {
