@@ -15,6 +15,8 @@ What it computes, and the passages it follows:
   grid) and the per-pair bucket id of the Product mapping (iRPE page, eq. 25;
   Swin post, section 3.2), or the two rows of the Cross mapping (eqs. 22-24),
   with no bucket for prefix (class) tokens.
+* ``backward``  - gradients of the forward with respect to q, k, v and every
+  table, from the same per-pair definition (softmax, scale, bucket sums).
 * ``attention`` - the attention forward written as a per-pair definition:
   offset -> index -> table row -> logit term, softmax, value sum
   (iRPE page eqs. 1-3 and 13-17; Swin relative-bias record, "The claim").
@@ -44,6 +46,9 @@ Parity status (pins live in tests/test_oracle_*.py):
   sum-of-two-squares count, Pythagorean offsets, symmetry and saturation
   invariants, the reduction to the directed index on an axis, and an
   attention-level reduction to a symmetric Product table on one row.
+* The backward pass: pinned by central finite differences of the (pinned)
+  forward for every input and table, in every mode and mapping, and by
+  torch's autograd of a library softmax attention without position terms.
 * The Cross mapping (iRPE page, Method, eqs. 22-24): pinned by the Shaw-style
   page's printed weights along a one-row and a one-column grid (which also
   fixes the row half [0, S) / column half [S, 2S) split of its table), by
