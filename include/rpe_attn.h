@@ -186,6 +186,35 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
                         const float* bias, const void* rq, const void* rk, const void* rv,
                         void* o, float* lse, void* stream);
 
+/* Backward pass: gradients of o = rpe_attn_fwd(...) for a given dO = dL/do, with
+ * respect to q, k, v and every table the descriptor uses (product maps, i.e.
+ * RPE_MAP_SWIN or RPE_MAP_PIECEWISE; RPE_E_MODE for an undirected map).  Per
+ * unit, with P the softmax weights recomputed from `lse` and s the logit scale:
+ *   dP_ij = dO_i . (v_j + [V] rV[b]),  dL_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
+ *   dq_i = s sum_j dL_ij (k_j + [K] rK[b]),  dk_j = s sum_i dL_ij (q_i + [Q] rQ[b]),
+ *   dv_j = sum_i P_ij dO_i,  drK[b] = s sum dL_ij q_i,  drQ[b] = s sum dL_ij k_j,
+ *   drV[b] = sum P_ij dO_i,  dbias[b] = sum dL_ij     (sums over the pairs of bucket b;
+ *   a shared table sums over heads)
+ * (the gradient of the definition of iRPE page, Method, eqs. 13-17 and the Swin
+ * relative-bias record, "The claim").
+ *   q, k, v, dout : [B][H][N][d], desc.dtype;  lse: [B][H][N] float32 from rpe_attn_fwd
+ *   bias, rq, rk, rv : as for rpe_attn_fwd (NULL where unused)
+ *   dq, dk, dv    : [B][H][N][d] float32, written
+ *   dbias         : [H|1][S*S] float32, written in bias mode (else ignored)
+ *   drq, drk, drv : [H|1][S*S][d] float32, written for the terms present (else ignored)
+ *   workspace     : device, at least rpe_attn_bwd_workspace_size() bytes, caller-owned;
+ *                   it holds the weights and score gradients of every unit (2 B H U T^2
+ *                   floats) and per-row bucket sums
+ * Computed in float32, one thread per output element (a reference-grade pass).
+ * Asynchronous on `stream`.  Errors: descriptor validation; RPE_E_NULL for a
+ * missing pointer; RPE_E_SHAPE if the workspace is too small or T*T >= 2^31. */
+rpe_status rpe_attn_bwd_workspace_size(const rpe_attn_desc* desc, uint64_t* bytes);
+rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* bias, const void* rq,
+                        const void* rk, const void* rv, float* dq, float* dk, float* dv, float* dbias,
+                        float* drq, float* drk, float* drv, void* workspace, uint64_t workspace_bytes,
+                        void* stream);
+
 /* Static string for a status code. */
 const char* rpe_status_str(int32_t status);
 

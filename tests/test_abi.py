@@ -181,3 +181,25 @@ def test_undirected_maps_geometry_and_rejections(m):
     pw = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), mode="bias", map="piecewise",
                        alpha=1.9, beta=3.8, gamma=15.2)
     assert f(ctypes.byref(pw), _lib.RPE_TABLE_BIAS, one, one, None) == -4       # not undirected
+
+
+def test_bwd_rejects_before_device():
+    lib = _lib_or_skip()
+    one = ctypes.c_void_p(16)
+    d = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), prefix_tokens=1, mode="contextual",
+                      terms="kv", map="piecewise", alpha=1.9, beta=3.8, gamma=15.2)
+    n = ctypes.c_uint64()
+    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    T = 197
+    # bucket map + P + dL of 2 units, then the K and V bucket sums (81 per row), each 256-B aligned
+    up = lambda v: (v + 255) // 256 * 256
+    assert n.value == up(T * T * 2) + 2 * up(2 * T * T * 4) + 2 * up(2 * T * 81 * 4)
+    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(d), None) == -1
+    args = [one] * 16
+    # the value table's gradient missing (rv given, drv NULL)
+    a = list(args)
+    a[15] = None
+    assert lib.rpe_attn_bwd(ctypes.byref(d), *a, one, ctypes.c_uint64(n.value), None) == -1
+    # workspace too small
+    assert lib.rpe_attn_bwd(ctypes.byref(d), *args, one, ctypes.c_uint64(n.value - 1), None) == -2
+    assert lib.rpe_attn_bwd(None, *args, one, ctypes.c_uint64(n.value), None) == -1

@@ -304,3 +304,47 @@ def prepare_fwd(q, k, v, *, out, lse=None, **kw):
         bias, rq, rk, rv = prod
     ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(rq), _ptr(rk), _ptr(rv), _ptr(out), _ptr(lse)]
     return PreparedFwd(desc, ptrs, (q, k, v, out, lse, tabs), q.device, tuple(convert))
+
+
+def rpe_attn_bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
+                 alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None, rq=None, rk=None,
+                 rv=None):
+    """Gradients of rpe_attn_fwd's output for the output gradient ``dout``.
+
+    ``lse`` is the float32 log-sum-exp the forward returned (return_lse=True).
+    Returns a dict of float32 tensors: dq, dk, dv and, for the tables the mode
+    and terms use, dbias / drq / drk / drv (Product maps only)."""
+    torch = _torch()
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, dout)):
+        raise ValueError("q, k, v, dout must be [B, H, N, d] of one shape")
+    if any(t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda for t in (k, v, dout)):
+        raise ValueError("q, k, v, dout must be contiguous device tensors of one dtype")
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    tabs = [t for t in (bias, rq, rk, rv) if t is not None]
+    per_head = any(t.shape[0] == H and H > 1 for t in tabs)
+    desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
+                     dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms, map=map,
+                     alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale, tables_per_head=per_head)
+    nbytes = ctypes.c_uint64()
+    check("rpe_attn_bwd_workspace_size", load().rpe_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
+    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(q.shape, **f32), "dv": torch.empty(q.shape, **f32)}
+    use = {"bias": mode == "bias", "rq": mode == "contextual" and "q" in terms,
+           "rk": mode == "contextual" and "k" in terms, "rv": mode == "contextual" and "v" in terms}
+    src = {"bias": bias, "rq": rq, "rk": rk, "rv": rv}
+    for n in ("bias", "rq", "rk", "rv"):
+        if use[n]:
+            if src[n] is None:
+                raise ValueError(f"{n} is required by mode {mode!r} and terms {terms!r}")
+            g["d" + n] = torch.empty(src[n].shape, **f32)
+    gp = lambda n: _ptr(g.get(n))
+    check("rpe_attn_bwd",
+          load().rpe_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                              _ptr(bias if use["bias"] else None), _ptr(rq if use["rq"] else None),
+                              _ptr(rk if use["rk"] else None), _ptr(rv if use["rv"] else None),
+                              gp("dq"), gp("dk"), gp("dv"), gp("dbias"), gp("drq"), gp("drk"), gp("drv"),
+                              _ptr(ws), ctypes.c_uint64(nbytes.value), _stream(q.device)))
+    return g

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]
-SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "fwd_dispatch.cpp",
+SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "bwd.hip", "fwd_dispatch.cpp",
            "fwd_bf16_d16.hip", "fwd_bf16_d32.hip", "fwd_bf16_d64.hip",
            "fwd_f32_d16.hip", "fwd_f32_d32.hip", "fwd_f32_d64.hip"]
 

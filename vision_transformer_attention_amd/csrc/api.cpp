@@ -1,7 +1,10 @@
 // extern "C" entry points of librpe_attn: validation, planning and launch.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "../../include/rpe_attn.h"
+#include "bwd.h"
 #include "plan.h"
 
 namespace rpe {
@@ -13,6 +16,7 @@ hipError_t launch_bucket_map(int P, int R, int C, int half, int S, int map, int 
                              hipStream_t stream);
 hipError_t launch_cross_to_product(bool bf16, const void* cross, void* product, int S, int width,
                                    int64_t total, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_undirected_to_product(bool bf16, bool f32, const void* table, void* product, int R, int C,
                                         int Hp, int half, int map, int rounding, double alpha, double beta,
                                         double gamma, int width, int64_t total, hipStream_t stream);
@@ -149,6 +153,131 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.bias = bias; p.rq = rq; p.rk = rk; p.rv = rv;
   const hipError_t e = rpe::launch_fwd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RPE_OK : RPE_E_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of rpe_attn_bwd: the unit's bucket map, P and dL of every unit and
+// the per-row bucket sums the present terms need, each 256-byte aligned.
+struct BwdLayout {
+  uint64_t bmap, P, dL, Wq, Wk, Wv, total;
+};
+
+uint64_t up256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+int bwd_layout(const rpe_attn_desc* d, BwdLayout* L, int* T_out, int* U_out, int* nb_out) {
+  int st = rpe::validate(d);
+  if (st != RPE_OK) return st;
+  if (rpe::is_undirected(d)) return RPE_E_MODE;
+  int h = 0, s = 0, nb = 1;
+  if (d->mode != RPE_MODE_NONE) {
+    st = rpe::table_geometry(d, &h, &s, &nb);
+    if (st != RPE_OK) return st;
+  }
+  const int R = d->window ? d->window : d->grid_h;
+  const int C = d->window ? d->window : d->grid_w;
+  const int T = d->prefix_tokens + R * C;
+  const int U = d->window ? (d->grid_h / d->window) * (d->grid_w / d->window) : 1;
+  const uint64_t units = static_cast<uint64_t>(d->batch) * d->heads * U;
+  const uint64_t tt = static_cast<uint64_t>(T) * T;
+  if (tt > 2147483647ULL) return RPE_E_SHAPE;
+  const bool ctx = d->mode == RPE_MODE_CONTEXTUAL;
+  const bool wq = d->mode == RPE_MODE_BIAS || (ctx && (d->terms & RPE_TERM_K));
+  const bool wk = ctx && (d->terms & RPE_TERM_Q);
+  const bool wv = ctx && (d->terms & RPE_TERM_V);
+  const uint64_t rows = units * T * static_cast<uint64_t>(nb) * 4;
+  uint64_t off = 0;
+  L->bmap = off; off += up256(tt * 2);
+  L->P = off; off += up256(units * tt * 4);
+  L->dL = off; off += up256(units * tt * 4);
+  L->Wq = wq ? off : ~0ULL; off += wq ? up256(rows) : 0;
+  L->Wk = wk ? off : ~0ULL; off += wk ? up256(rows) : 0;
+  L->Wv = wv ? off : ~0ULL; off += wv ? up256(rows) : 0;
+  L->total = off;
+  if (T_out) *T_out = T;
+  if (U_out) *U_out = U;
+  if (nb_out) *nb_out = nb;
+  return RPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rpe_status rpe_attn_bwd_workspace_size(const rpe_attn_desc* desc, uint64_t* bytes) {
+  BwdLayout L;
+  const int st = bwd_layout(desc, &L, nullptr, nullptr, nullptr);
+  if (st != RPE_OK) return static_cast<rpe_status>(st);
+  if (!bytes) return RPE_E_NULL;
+  *bytes = L.total;
+  return RPE_OK;
+}
+
+rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* bias, const void* rq, const void* rk,
+                        const void* rv, float* dq, float* dk, float* dv, float* dbias, float* drq, float* drk,
+                        float* drv, void* workspace, uint64_t workspace_bytes, void* stream) {
+  BwdLayout L;
+  int T = 0, U = 0, nb = 1;
+  const int st = bwd_layout(desc, &L, &T, &U, &nb);
+  if (st != RPE_OK) return static_cast<rpe_status>(st);
+  const uint64_t units = static_cast<uint64_t>(desc->batch) * desc->heads * U;
+  if (units == 0) return RPE_OK;
+  if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv || !workspace) return RPE_E_NULL;
+  if (workspace_bytes < L.total) return RPE_E_SHAPE;
+  const bool ctx = desc->mode == RPE_MODE_CONTEXTUAL;
+  const bool tk = ctx && (desc->terms & RPE_TERM_K), tq = ctx && (desc->terms & RPE_TERM_Q);
+  const bool tv = ctx && (desc->terms & RPE_TERM_V);
+  if (desc->mode == RPE_MODE_BIAS && (!bias || !dbias)) return RPE_E_NULL;
+  if ((tk && (!rk || !drk)) || (tq && (!rq || !drq)) || (tv && (!rv || !drv))) return RPE_E_NULL;
+  char* ws = static_cast<char*>(workspace);
+  rpe::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout;
+  a.rq = tq ? rq : nullptr; a.rk = tk ? rk : nullptr; a.rv = tv ? rv : nullptr;
+  a.bias = desc->mode == RPE_MODE_BIAS ? bias : nullptr;
+  a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dbias = desc->mode == RPE_MODE_BIAS ? dbias : nullptr;
+  a.drq = tq ? drq : nullptr; a.drk = tk ? drk : nullptr; a.drv = tv ? drv : nullptr;
+  a.bmap = reinterpret_cast<const int16_t*>(ws + L.bmap);
+  a.P = reinterpret_cast<float*>(ws + L.P);
+  a.dL = reinterpret_cast<float*>(ws + L.dL);
+  a.Wq = L.Wq != ~0ULL ? reinterpret_cast<float*>(ws + L.Wq) : nullptr;
+  a.Wk = L.Wk != ~0ULL ? reinterpret_cast<float*>(ws + L.Wk) : nullptr;
+  a.Wv = L.Wv != ~0ULL ? reinterpret_cast<float*>(ws + L.Wv) : nullptr;
+  a.bf16 = desc->dtype == RPE_BF16;
+  a.D = desc->head_dim;
+  a.N = desc->prefix_tokens + desc->grid_h * desc->grid_w;
+  a.H = desc->heads;
+  a.U = U;
+  a.T = T;
+  a.npre = desc->prefix_tokens;
+  a.C = desc->window ? desc->window : desc->grid_w;
+  a.M = desc->window;
+  a.gw = desc->grid_w;
+  a.wpr = desc->window ? desc->grid_w / desc->window : 1;
+  a.nb = nb;
+  a.tables_per_head = desc->tables_per_head;
+  a.n_units = static_cast<int64_t>(units);
+  a.scale = desc->scale != 0.0f ? desc->scale : 1.0f / std::sqrt(static_cast<float>(desc->head_dim));
+  // the unit's bucket map (Swin geometry when there is no table)
+  int h = 0, s = 0, nbg = 0;
+  rpe_attn_desc g = *desc;
+  if (g.mode == RPE_MODE_NONE) {
+    g.mode = RPE_MODE_BIAS;
+    g.map = RPE_MAP_SWIN;
+  }
+  const int stg = rpe::table_geometry(&g, &h, &s, &nbg);
+  if (stg != RPE_OK) return static_cast<rpe_status>(stg);
+  const int R = desc->window ? desc->window : desc->grid_h;
+  hipError_t e = rpe::launch_bucket_map(desc->prefix_tokens, R, a.C, h, s, g.map, g.rounding, g.alpha, g.beta,
+                                        g.gamma, reinterpret_cast<int16_t*>(ws + L.bmap),
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return RPE_E_HIP;
+  e = rpe::launch_bwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RPE_OK : RPE_E_HIP;
 }
 
