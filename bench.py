@@ -199,6 +199,37 @@ def time_workload(name, steps, warmup, dev, cold=True):
     return ms, wall, copies, ok
 
 
+def time_backward(name, steps, warmup, dev):
+    """Average time (ms) of one rpe_attn_bwd call on `name` (one resident buffer set),
+    HIP events on the launch stream; the log-sum-exp comes from the forward."""
+    import numpy as np
+    import torch
+    import vision_transformer_attention_amd as pkg
+    w = WORKLOADS[name]
+    sets, outs = _device_inputs(w, 1, dev)
+    d = sets[0]
+    dout = torch.from_numpy(np.random.default_rng(77).standard_normal(w.qkv_shape)).to(d["q"].dtype).to(dev)
+    kw = dict(grid=(w.grid_h, w.grid_w), window=w.window, prefix_tokens=w.prefix, mode=w.mode,
+              terms="".join(sorted(w.terms)), map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma,
+              rounding=w.reading, bias=d.get("bias"), rq=d.get("rq"), rk=d.get("rk"), rv=d.get("rv"))
+    _, lse = pkg.rpe_attn_fwd(d["q"], d["k"], d["v"], return_lse=True, **kw)
+    g, call = pkg.prepare_bwd(d["q"], d["k"], d["v"], dout, lse, **kw)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        call(stream.cuda_stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call(stream.cuda_stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ok = all(bool(torch.isfinite(t).all().item()) for t in g.values())
+    del sets, outs, g, call
+    torch.cuda.empty_cache()
+    return ev0.elapsed_time(ev1) / steps, ok
+
+
 def summarize(name, ms):
     w = WORKLOADS[name]
     flop, nbytes = flops_bytes(w)
@@ -262,6 +293,14 @@ def main():
                                "warm_tflops": sw["tflops"], "warm_mfma_frac": sw["mfma_frac"],
                                "finite": okc}
             print(f"{name}: {mc * 1e3:.2f} us cold, {mw * 1e3:.2f} us warm", file=sys.stderr, flush=True)
+    backward = None
+    if not args.no_secondary:
+        mb, okb = time_backward(args.workload, 10, 2, dev)
+        fb, _ = flops_bytes(w)
+        backward = {"workload": w.description, "us_per_call": mb * 1e3,
+                    "tflops": 2.5 * fb / (mb * 1e-3) / 1e12, "finite": okb,
+                    "note": "float32 per-element reference kernels; TFLOP/s counts 2.5x the forward's FLOP"}
+        print(f"backward {args.workload}: {mb * 1e3:.1f} us per call", file=sys.stderr, flush=True)
     if args.copy_probe > 0:
         n = args.copy_probe << 20
         src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
@@ -310,6 +349,7 @@ def main():
         "us_per_launch": ms_cold * 1e3,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
         "secondary": secondary,
+        "backward": backward,
     }
     if ms_warm is not None:
         warm = summarize(args.workload, ms_warm)

@@ -8,8 +8,10 @@ for device memory and streams.
 """
 
 from .attention import (  # noqa: F401
+    PreparedBwd,
     PreparedFwd,
     make_desc,
+    prepare_bwd,
     prepare_fwd,
     rpe_attn_axis_index,
     rpe_attn_bucket_map,

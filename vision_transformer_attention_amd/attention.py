@@ -306,14 +306,40 @@ def prepare_fwd(q, k, v, *, out, lse=None, **kw):
     return PreparedFwd(desc, ptrs, (q, k, v, out, lse, tabs), q.device, tuple(convert))
 
 
-def rpe_attn_bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
-                 alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None, rq=None, rk=None,
-                 rv=None):
+class PreparedBwd:
+    """A validated rpe_attn_bwd call with fixed tensors and workspace (for timing)."""
+
+    def __init__(self, desc, args, keep, device):
+        self._lib = load()
+        self._desc = desc
+        self._args = args
+        self._keep = keep
+        self._device = device
+
+    def __call__(self, stream=None):
+        torch = _torch()
+        s = ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream if stream is None else stream)
+        check("rpe_attn_bwd", self._lib.rpe_attn_bwd(ctypes.byref(self._desc), *self._args, s))
+
+
+def prepare_bwd(q, k, v, dout, lse, **kw):
+    """Run rpe_attn_bwd once and return (gradients, PreparedBwd) that repeats it in place."""
+    g, desc, args, keep = _bwd(q, k, v, dout, lse, **kw)
+    return g, PreparedBwd(desc, args, keep, q.device)
+
+
+def rpe_attn_bwd(q, k, v, dout, lse, **kw):
     """Gradients of rpe_attn_fwd's output for the output gradient ``dout``.
 
     ``lse`` is the float32 log-sum-exp the forward returned (return_lse=True).
     Returns a dict of float32 tensors: dq, dk, dv and, for the tables the mode
     and terms use, dbias / drq / drk / drv (Product maps only)."""
+    return _bwd(q, k, v, dout, lse, **kw)[0]
+
+
+def _bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
+                 alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None, rq=None, rk=None,
+                 rv=None):
     torch = _torch()
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, dout)):
         raise ValueError("q, k, v, dout must be [B, H, N, d] of one shape")
@@ -341,10 +367,10 @@ def rpe_attn_bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="n
                 raise ValueError(f"{n} is required by mode {mode!r} and terms {terms!r}")
             g["d" + n] = torch.empty(src[n].shape, **f32)
     gp = lambda n: _ptr(g.get(n))
-    check("rpe_attn_bwd",
-          load().rpe_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
-                              _ptr(bias if use["bias"] else None), _ptr(rq if use["rq"] else None),
-                              _ptr(rk if use["rk"] else None), _ptr(rv if use["rv"] else None),
-                              gp("dq"), gp("dk"), gp("dv"), gp("dbias"), gp("drq"), gp("drk"), gp("drv"),
-                              _ptr(ws), ctypes.c_uint64(nbytes.value), _stream(q.device)))
-    return g
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+            _ptr(bias if use["bias"] else None), _ptr(rq if use["rq"] else None),
+            _ptr(rk if use["rk"] else None), _ptr(rv if use["rv"] else None),
+            gp("dq"), gp("dk"), gp("dv"), gp("dbias"), gp("drq"), gp("drk"), gp("drv"),
+            _ptr(ws), ctypes.c_uint64(nbytes.value)]
+    check("rpe_attn_bwd", load().rpe_attn_bwd(ctypes.byref(desc), *args, _stream(q.device)))
+    return g, desc, args, (q, k, v, dout, lse, ws, g, tabs)
