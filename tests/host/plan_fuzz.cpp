@@ -83,7 +83,7 @@ int main(int argc, char** argv) {
     const bool rows = ctx && (d.terms & (RPE_TERM_K | RPE_TERM_V));
     REQUIRE(p.lds_bytes <= rpe::kMaxLdsBytes && p.lds_bytes % 16 == 0);
     REQUIRE(p.stages >= rpe::kMinStages && p.stages <= rpe::kMaxStages);
-    REQUIRE(p.gsz == ((d.dtype == RPE_BF16 && ctx && !tv) ? 2 : 4));
+    REQUIRE(p.gsz == ((d.dtype == RPE_BF16 && ctx) ? 2 : 4));
     REQUIRE(p.off_stage == 0);
     REQUIRE(p.off_rq >= p.stages * 2 * rpe::kBlockSlots * p.D * p.elem_bytes && p.off_rq % 16 == 0);
     REQUIRE(p.off_rq <= p.off_tab);
@@ -106,9 +106,29 @@ int main(int argc, char** argv) {
     REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr * p.gsz);
     REQUIRE(p.zr == (p.S - 1) * p.S + 1);
     int end_g = p.off_neg + p.zr * p.gsz;
-    if (tv) {
+    if (tv && p.vw) {
+      // per-column weight sums: [S][Wp] fp32 rows of an odd number of 16-byte chunks
+      REQUIRE(p.Wp >= 8 && p.Wp <= 32);
+      REQUIRE(p.off_vw >= end_g && p.off_vw % 16 == 0);
+      REQUIRE(p.vw_pitch >= p.S * p.Wp * 4 && p.vw_pitch % 16 == 0 && ((p.vw_pitch / 16) & 1));
+      REQUIRE(p.off_vd >= p.off_vw + p.NW * rpe::kRowTile * p.vw_pitch && p.off_vd % 16 == 0);
+      REQUIRE(p.off_cr >= p.off_vd + p.NW * 64 * 16);
+      end_g = p.off_cr + p.S * 4;
+      // exact divisions by S * gsz (row parts) and S (bucket ids)
+      for (int a = 0; a < p.S; ++a) {
+        const uint64_t rp = static_cast<uint64_t>(a) * p.S * p.gsz;
+        REQUIRE(((rp * p.vw_mg) >> 32) == static_cast<uint64_t>(a));
+      }
+      for (int b = 0; b < p.nb; ++b) REQUIRE(((static_cast<uint64_t>(b) * p.vw_ms) >> 32) == static_cast<uint64_t>(b / p.S));
+      // g is non-decreasing over the unit's column offsets, so each column
+      // bucket is a contiguous run of them (the kernel reads its dx range off
+      // the run's ends)
+      for (int dx = -(p.C - 1); dx < p.C - 1; ++dx)
+        REQUIRE(rpe::axis_index_host(dx, p.map, p.rounding, p.alpha, p.beta, p.gamma) <=
+                rpe::axis_index_host(dx + 1, p.map, p.rounding, p.alpha, p.beta, p.gamma));
+    } else if (tv) {
       REQUIRE(p.off_w >= end_g && p.off_w % 16 == 0);
-      end_g = p.off_w + (p.off_neg + p.zr * p.gsz - p.off_tab);
+      end_g = p.off_w + (p.off_neg + p.zr * p.gsz - p.off_tab) * (4 / p.gsz);
     }
     if (tq) {
       REQUIRE(p.off_tq >= end_g && p.p_tq >= p.nbt * rpe::kRowTile && (p.p_tq & 1));

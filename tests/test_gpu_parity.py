@@ -490,6 +490,42 @@ def test_empty_batch(dev):
     assert o.shape == q.shape
 
 
+# Keys whose logits climb steeply along the key stream: the running maximum
+# starts at the first block's and has to move several times (by more than 2^64
+# in the weights), rescaling O, the row sum and the value-term weight sums
+# mid-stream.  Every query gets +4 along the all-ones direction and each key
+# ramp * (row / (rows - 1) - 1) along it (row within the unit; prefix keys as
+# row 0), so the logits climb by about 4 * ramp * sqrt(d) to values near 0 at
+# the last key row: the weights that matter come from logits of ordinary size.
+_QKV = WORKLOADS["deit_s_irpe_qkv"]
+RAMP_CASES = [
+    ("DeiT-S QKV 14x14 + cls (per-column weight sums)", _QKV.resized(batch=1, heads=2), 5.0),
+    ("QKV 7x7 windows (per-column sums, rows of 8)",
+     _QKV.resized(batch=1, heads=2, grid_h=14, grid_w=14, window=7, prefix=0), 5.0),
+    ("QKV 9x27 + cls (per-column sums, rows of 32)", _QKV.resized(batch=1, heads=2, grid_h=9, grid_w=27), 5.0),
+    ("QKV 11x3 + 2 prefix (per-bucket sums, rows of 4)",
+     _QKV.resized(batch=1, heads=2, grid_h=11, grid_w=3, prefix=2), 5.0),
+    ("QKV 3x61 + cls (per-bucket sums, wide rows)", _QKV.resized(batch=1, heads=2, grid_h=3, grid_w=61), 5.0),
+    ("V only 14x14 + cls", _QKV.resized(batch=1, heads=2, terms=frozenset("v")), 5.0),
+    ("QKV fp32 d32 10x10 + cls", _QKV.resized(batch=1, heads=2, head_dim=32, grid_h=10, grid_w=10,
+                                              dtype="fp32"), 3.0),
+]
+
+
+@pytest.mark.parametrize("label,w,ramp", RAMP_CASES)
+def test_running_max_moves(dev, label, w, ramp):
+    w = fit(w)
+    x = make_inputs(w, seed=9200)
+    rows = w.window or w.grid_h
+    y = np.arange(w.grid_h * w.grid_w) // w.grid_w
+    yy = (y % w.window) if w.window else y
+    t = np.concatenate([np.full(w.prefix, -ramp), ramp * (yy / max(rows - 1, 1) - 1.0)])
+    x["q"] = round_to_dtype(x["q"] + 4.0, w.dtype)
+    x["k"] = round_to_dtype(x["k"] + t[None, None, :, None], w.dtype)
+    say("running max moves", label, w.qkv_shape)
+    compare(w, x, dev)
+
+
 def test_deterministic(dev):
     w = SMALL["deit_s_irpe_qkv"]
     x = make_inputs(w, sigma=1.0, seed=9100)

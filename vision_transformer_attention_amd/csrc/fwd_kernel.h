@@ -183,12 +183,15 @@ rpe_fwd_kernel(Params p) {
   constexpr bool TQ = CTX && (TERMS & RPE_TERM_Q);
   constexpr bool TV = CTX && (TERMS & RPE_TERM_V);
   constexpr bool ROWS = TK || TV;                  // per-row bucket area in LDS
+  // value term with per-column weight sums (the launch plan's vw; never with
+  // wide rows, whose [S][64] row areas rarely fit)
+  constexpr bool VW = TV && !WIDE;
   // One gathered addend per pair from the row area / bias table.  Without a key
   // term the row area is zero and the gather only supplies the -inf of padding
   // keys, unless the query-term gather already does that.
   constexpr bool GATHER = !CTX || TK || !TQ;
-  // gather entries: fp16 per-row scores for bf16 inputs without a value term
-  constexpr bool G16 = BF && CTX && !TV;
+  // gather entries: fp16 per-row scores for bf16 inputs
+  constexpr bool G16 = BF && CTX;
   using GT = typename std::conditional<G16, _Float16, float>::type;
   constexpr int GSZ = sizeof(GT);
   constexpr int EB = sizeof(DT);
@@ -274,6 +277,7 @@ rpe_fwd_kernel(Params p) {
   GT* const gzero = reinterpret_cast<GT*>(smem + p.off_zero);
   GT* const gneg = reinterpret_cast<GT*>(smem + p.off_neg);
   float* const wsum = reinterpret_cast<float*>(smem + p.off_w);
+  int* const cr_tab = reinterpret_cast<int*>(smem + p.off_cr);
   float* const tqs = reinterpret_cast<float*>(smem + p.off_tq);
 
   // ---- this lane's query row.
@@ -514,8 +518,16 @@ rpe_fwd_kernel(Params p) {
     for (int i = tid; i < p.nb; i += nth) gtab[i] = 0.0f;
   }
   if constexpr (TV) {
-    const int wsz = (p.off_neg + p.zr * GSZ - p.off_tab) / 4;
-    for (int i = tid; i < wsz; i += nth) wsum[i] = 0.0f;
+    if (VW && p.vw) {
+      const int nch = NW * kRowTile * p.vw_pitch / 16;
+      for (int i = tid; i < nch; i += nth) reinterpret_cast<f32x4*>(smem + p.off_vw)[i] = f32x4{};
+      // dx range [lo, hi] of each column bucket c (g(dx) = c - H): empty here,
+      // set from the column table once it is visible
+      for (int c = tid; c < p.S; c += nth) cr_tab[c] = (p.C & 0xffff) | (-p.C << 16);
+    } else {
+      const int wsz = (p.off_neg + p.zr * GSZ - p.off_tab) * (4 / GSZ) / 4;
+      for (int i = tid; i < wsz; i += nth) wsum[i] = 0.0f;
+    }
   }
   if constexpr (CTX && GATHER && !TK) {
     for (int i = tid; i < NW * kRowTile * p.p_tab; i += nth) gtab[i] = static_cast<GT>(0.0f);
@@ -648,7 +660,20 @@ rpe_fwd_kernel(Params p) {
   // 8j + 4h + i of a block at phase ph (ph = block index & 1 when a grid row spans
   // two blocks); cqb the same for the query-term scores (fp32).
   const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab * GSZ : p.off_tab;
-  const int w_delta = TV ? p.off_w - p.off_tab : 0;   // byte distance gather target -> weight sums
+  // per-bucket weight sums (vw = 0): the entry of a gather address, 4-byte entries
+  auto waddr = [&](int ga) -> int { return p.off_w + (ga - p.off_tab) * (4 / GSZ); };
+  // per-column weight sums (vw = 1): this row's [S][Wp] area, the byte offset of
+  // this lane's 4-column group j at phase ph within a row bucket, and the lane's
+  // 16-byte slot for the writes of merged entries
+  const int vrowoff = TV ? p.off_vw + (wid * kRowTile + r32) * p.vw_pitch : 0;
+  const int vdum = TV ? p.off_vd + (wid * 64 + lane) * 16 : 0;
+  int vcol[TV ? NPH : 1][4];
+#pragma unroll
+  for (int ph = 0; ph < (TV ? NPH : 1); ++ph)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      vcol[ph][j] = vrowoff + 4 * (WIDE ? 32 * ph + 8 * j + 4 * h : (8 * j + 4 * h) & (p.Wp - 1));
+  (void)vcol;
   if constexpr (TK) {
     // this wave's rK copies are older than its ring loads
     if (p.rk_lds) wait_vmcnt_floor((L < ST - 1 ? L : ST - 1) * lpe);
@@ -660,6 +685,19 @@ rpe_fwd_kernel(Params p) {
       if (k * 64 + lane < p.nb) gtab[k * 64 + lane] *= p.bias_mul;
   }
   lds_barrier();  // prologue tables (and rK / bias copies) visible; ring loads stay in flight
+  if constexpr (VW) {
+    // g is non-decreasing, so each column bucket holds a contiguous run of the
+    // column table; its first and last entries give the bucket's dx range
+    // (read in the epilogue, many barriers later)
+    if (p.vw) {
+      int16_t* const cr16 = reinterpret_cast<int16_t*>(cr_tab);
+      for (int k = tid; k < 2 * p.C - 1; k += nth) {
+        const int c = cx_tab[k];
+        if (k == 0 || cx_tab[k - 1] != c) cr16[2 * c] = static_cast<int16_t>(k - (p.C - 1));
+        if (k == 2 * p.C - 2 || cx_tab[k + 1] != c) cr16[2 * c + 1] = static_cast<int16_t>(k - (p.C - 1));
+      }
+    }
+  }
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
   {
@@ -730,18 +768,22 @@ rpe_fwd_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = WIDE ? ryt[-(g >> 1)] : ryj[j][-(g * rpb)];
   };
+  // (always inlined: an outlined call would move every captured variable to scratch)
   auto process_block = [&](auto interior_c, auto first_c, auto ph_c, const char* ktile, const char* vtile,
-                           int gblk, bool prefix_blk, const int (&ryv)[4]) {
+                           int gblk, bool prefix_blk, const int (&ryv)[4]) __attribute__((always_inline)) {
     constexpr bool INTERIOR = decltype(interior_c)::value;
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr int PH = decltype(ph_c)::value;
     const f32x16 s = s_tile(ktile, FIRST ? f32x16{} : mneg);
     float x[4][4];
     int ab[4][4];          // gather addresses, kept for the value-term scatter
+    int rp[4];             // row parts of this lane's keys
+    bool vz[4][4];         // prefix keys kept in padding columns (no value term)
     if constexpr (INTERIOR) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ryb = ryv[j];
+        rp[j] = ryb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ab[j][i] = ryb + cxb[PH][j][i];
@@ -756,9 +798,11 @@ rpe_fwd_kernel(Params p) {
         const int yj = (gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
         const int yk = yj < 0 ? 0 : (yj < p.R ? yj : p.R - 1);
         const int ryb = ryt[-yk];
+        rp[j] = ryb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int slot = 8 * j + 4 * h + i;
+          vz[j][i] = false;
           const int xj = (gblk * kBlockSlots + slot) & (p.Wp - 1);
           int a = ryb + cxb[PH][j][i];
           int aq = TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0;
@@ -772,6 +816,7 @@ rpe_fwd_kernel(Params p) {
           } else if (p.prefix_in_tail && yj == p.R - 1 && xj >= p.C && xj - p.C < p.P) {
             a = p.off_zero;
             aq = p.off_tqz;
+            vz[j][i] = true;
           }
           ab[j][i] = a;
           x[j][i] = logit(s[4 * j + i], a, aq);
@@ -843,8 +888,13 @@ rpe_fwd_kernel(Params p) {
         for (int c = 0; c < DTL; ++c) oacc[c] *= alpha;
         if constexpr (TV) {
           if (need) {
-            float* wrow = reinterpret_cast<float*>(smem + rowbase + w_delta);
-            for (int b = h; b < p.nb; b += 2) wrow[b] *= alpha;
+            if (VW && p.vw) {
+              f32x4* const vr = reinterpret_cast<f32x4*>(smem + vrowoff);
+              for (int k = h; k < (p.S << p.lwp) >> 2; k += 2) vr[k] = vr[k] * alpha;
+            } else {
+              float* wrow = reinterpret_cast<float*>(smem + waddr(rowbase));
+              for (int b = h; b < p.nb; b += 2) wrow[b] *= alpha;
+            }
           }
         }
         m_run += dm;
@@ -858,10 +908,59 @@ rpe_fwd_kernel(Params p) {
     }
     l_part += bsum;
     if constexpr (TV) {
+      if (VW && p.vw) {
+        // (the prefix block's keys carry no value term)
+        if (!prefix_blk) {
+          // Entry (row bucket, key column) of each of this lane's 4-key groups.
+          // The lane's groups alias only where two of its grid rows share a row
+          // bucket (grid rows of 8 padded columns: consecutive j; of 16: j and
+          // j + 2); those are summed into the first and the others write to
+          // the lane's spare slot, so the read-modify-writes below touch
+          // distinct entries, and no other lane touches this row's columns.
+          f32x4 u[4];
+          int wr[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(reinterpret_cast<float*>(smem + ab[j][i] + w_delta), pr[j][i]);
+            for (int i = 0; i < 4; ++i) u[j][i] = (!INTERIOR && vz[j][i]) ? 0.0f : pr[j][i];
+            wr[j] = static_cast<int>(__umulhi(static_cast<uint32_t>(rp[j]), p.vw_mg) << (p.lwp + 2));
+          }
+          bool mg[4] = {false, false, false, false};
+          if constexpr (!WIDE) {
+            if (p.Wp == 8) {
+#pragma unroll
+              for (int j = 2; j >= 0; --j) {
+                mg[j + 1] = wr[j] == wr[j + 1];
+                const float f = mg[j + 1] ? 1.0f : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[j][i] = fmaf(f, u[j + 1][i], u[j][i]);
+              }
+            } else if (p.Wp == 16) {
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                mg[j + 2] = wr[j] == wr[j + 2];
+                const float f = mg[j + 2] ? 1.0f : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[j][i] = fmaf(f, u[j + 2][i], u[j][i]);
+              }
+            }
+          }
+          int dst[4];
+          f32x4 old[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dst[j] = (mg[j] || !qpos) ? vdum : wr[j] + vcol[PH][j];
+            old[j] = *reinterpret_cast<const f32x4*>(smem + dst[j]);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(smem + dst[j]) = old[j] + u[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) atomicAdd(reinterpret_cast<float*>(smem + waddr(ab[j][i])), pr[j][i]);
+      }
     }
     // (wide rows run at low occupancy, where converting P inside the PV loop
     // schedules better)
@@ -872,7 +971,7 @@ rpe_fwd_kernel(Params p) {
   };
   // phase dispatch (a 64-slot grid row spans two blocks)
   auto process = [&](auto interior_c, auto first_c, const char* kt, const char* vt, int gblk, bool pre,
-                     const int (&ryv)[4]) {
+                     const int (&ryv)[4]) __attribute__((always_inline)) {
     if constexpr (WIDE) {
       if (gblk & 1)
         process_block(interior_c, first_c, std::integral_constant<int, 1>{}, kt, vt, gblk, pre, ryv);
@@ -1106,19 +1205,60 @@ rpe_fwd_kernel(Params p) {
     }
     // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
     if constexpr (TV) {
+      if (VW && p.vw && active) {
+        // per-column sums -> prefix sums over the key columns, each lane of the
+        // row taking every other row bucket
+        for (int a = h; a < p.S; a += 2) {
+          char* const ar = smem + vrowoff + (a << (p.lwp + 2));
+          float run = 0.0f;
+          for (int x0 = 0; x0 < p.C; x0 += 4) {
+            f32x4 v = *reinterpret_cast<const f32x4*>(ar + 4 * x0);
+            v[0] += run;
+            v[1] += v[0];
+            v[2] += v[1];
+            v[3] += v[2];
+            run = v[3];
+            *reinterpret_cast<f32x4*>(ar + 4 * x0) = v;
+          }
+        }
+      }
       for (; e < L; ++e) {
         const int s = step(e);
         if (active) {
           const int t = e - nblk;
-          const float* wrow = reinterpret_cast<const float*>(smem + rowbase + w_delta);
           float wv[4][4];
+          if (VW && p.vw) {
+            // W[b] for b = (a, c): the prefix sums of row bucket a over the key
+            // columns x with g(xi - x) + H = c, a contiguous range
   #pragma unroll
-          for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
   #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int b = kRowTile * t + 8 * j + 4 * h + i;
-              wv[j][i] = b < p.nb ? wrow[b] : 0.0f;
-            }
+              for (int i = 0; i < 4; ++i) {
+                const int b = kRowTile * t + 8 * j + 4 * h + i;
+                float w = 0.0f;
+                if (b < p.nb) {
+                  const int a = static_cast<int>(__umulhi(static_cast<uint32_t>(b), p.vw_ms));
+                  const int cr = cr_tab[b - a * p.S];
+                  const int lo = static_cast<int16_t>(cr & 0xffff), hi = cr >> 16;
+                  const int xlo = xi - hi < 0 ? 0 : xi - hi;
+                  const int xhi = xi - lo > p.C - 1 ? p.C - 1 : xi - lo;
+                  if (xlo <= xhi) {
+                    const float* const f = reinterpret_cast<const float*>(smem + vrowoff + (a << (p.lwp + 2)));
+                    w = f[xhi] - (xlo > 0 ? f[xlo - 1] : 0.0f);
+                  }
+                }
+                wv[j][i] = w;
+              }
+          } else {
+            const float* wrow = reinterpret_cast<const float*>(smem + waddr(rowbase));
+  #pragma unroll
+            for (int j = 0; j < 4; ++j)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int b = kRowTile * t + 8 * j + 4 * h + i;
+                wv[j][i] = b < p.nb ? wrow[b] : 0.0f;
+              }
+          }
           pv_tile(vtile_of(s), wv, true);
         }
       }

@@ -44,7 +44,7 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   const bool tq = ctx && (d->terms & RPE_TERM_Q);
   const bool tv = ctx && (d->terms & RPE_TERM_V);
   const bool row_area = ctx && (d->terms & (RPE_TERM_K | RPE_TERM_V));
-  p->gsz = (d->dtype == RPE_BF16 && ctx && !tv) ? 2 : 4;
+  p->gsz = (d->dtype == RPE_BF16 && ctx) ? 2 : 4;
   p->kpitch = d->dtype == RPE_BF16 ? p->D + 8 : p->D + 1;
   int off = 0;
   p->off_stage = off;
@@ -62,9 +62,18 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   p->off_zero = off; off += p->zr * p->gsz;
   p->off_neg = off; off += p->zr * p->gsz;
   off = align(off, 16);
-  if (tv) {
-    p->off_w = off;  // gsz is 4 here, so the mirror has the same byte layout
-    off += align(p->off_neg + p->zr * p->gsz - p->off_tab, 16);
+  if (tv && p->vw) {
+    // [S][Wp] fp32 per query row; the row pitch is an odd number of 16-byte
+    // chunks, so that the 16-byte accesses of consecutive rows fall in
+    // different LDS banks
+    p->vw_pitch = p->S * p->Wp * 4;
+    if ((p->vw_pitch / 16) % 2 == 0) p->vw_pitch += 16;
+    p->off_vw = off; off += p->NW * kRowTile * p->vw_pitch;
+    p->off_vd = off; off += p->NW * 64 * 16;
+    p->off_cr = off; off += align(p->S * 4, 16);
+  } else if (tv) {
+    p->off_w = off;
+    off += align((p->off_neg + p->zr * p->gsz - p->off_tab) * (4 / p->gsz), 16);
   }
   if (tq) {
     p->p_tq = odd_word_pitch(p->nbt * kRowTile, 4);
@@ -229,11 +238,22 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   // depths whose LDS plan fits, take the one with the most resident waves per
   // CU (4 SIMDs x waves_per_simd waves, and as many workgroups as LDS allows),
   // then the deeper ring, then the wider workgroup.
+  // The value term sums weights per (row bucket, key column) (vw = 1) when
+  // that fits: two lanes share each query row, and with grid rows of 4 padded
+  // columns they would share key columns as well; grid rows of 64 (two blocks
+  // each) are left to the per-bucket layout.  It is taken unless it halves the
+  // resident waves of the per-bucket layout, whose LDS float atomics cost more.
+  const bool tv = d->mode == RPE_MODE_CONTEXTUAL && (d->terms & RPE_TERM_V);
+  const bool vw_ok = tv && p->Wp >= 8 && p->Wp <= 32;
   Params best;
   int best_waves = -1;
+  Params best_vw;
+  int best_vw_waves = -1;
+  for (int vw = vw_ok ? 1 : 0; vw >= 0; --vw)
   for (int max_w = kMaxWaves; max_w >= 2; --max_w) {
     for (int stages = kMaxStages; stages >= kMinStages; --stages) {
       Params t = *p;
+      t.vw = vw;
       t.n_qc = (t.n_rt + max_w - 1) / max_w;
       t.NW = (t.n_rt + t.n_qc - 1) / t.n_qc;
       if (t.NW < 2) t.NW = 2;  // at least two waves share each stream
@@ -243,11 +263,18 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
       const int by_regs = 4 * waves_per_simd(d->mode, d->terms, t.Wp == 64, d->head_dim) / t.NW;
       const int by_lds = kMaxLdsBytes / ((t.lds_bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule);
       const int waves = (by_regs < by_lds ? by_regs : by_lds) * t.NW;
-      if (waves > best_waves) {
+      if (vw && waves > best_vw_waves) {
+        best_vw_waves = waves;
+        best_vw = t;
+      } else if (!vw && waves > best_waves) {
         best_waves = waves;
         best = t;
       }
     }
+  }
+  if (best_vw_waves > 0 && 2 * best_vw_waves >= best_waves) {
+    best = best_vw;
+    best_waves = best_vw_waves;
   }
   if (best_waves < 0) return RPE_E_BUCKETS;
   // Small units without contextual terms: when there are more units than
@@ -282,6 +309,8 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   best.dv_wpr = make_fastdiv(static_cast<uint32_t>(best.wins_per_row > 0 ? best.wins_per_row : 1));
   best.dv_C = make_fastdiv(static_cast<uint32_t>(best.C > 0 ? best.C : 1));
   best.inv_c = 1.0f / best.c;
+  best.vw_mg = static_cast<uint32_t>(((uint64_t{1} << 32) + best.S * best.gsz - 1) / (best.S * best.gsz));
+  best.vw_ms = static_cast<uint32_t>(((uint64_t{1} << 32) + best.S - 1) / best.S);
   *p = best;
   return RPE_OK;
 }

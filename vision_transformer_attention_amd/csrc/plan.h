@@ -93,7 +93,7 @@ struct Params {
   int stages;             // LDS ring depth of the block stream
   // LDS layout, byte offsets.  "Gather" entries (the per-row bucket scores of
   // the contextual key term, or the bias table, and their guard regions) are
-  // gsz bytes: fp16 for bf16 inputs without a value term, else fp32.
+  // gsz bytes: fp16 for bf16 inputs in contextual mode, else fp32.
   int gsz;
   int off_stage;          // stages x {K tile, V tile}, each [32][D] row-major, swizzled
   int kpitch;             // row pitch (elements) of the staged query-term table
@@ -102,7 +102,17 @@ struct Params {
   int p_tab;              // row pitch (gather entries) of the per-row bucket scores
   int zr;                 // entries of each guard region: (S-1)*S + 1
   int off_zero, off_neg;  // guard regions (all 0 / all -inf) addressed as guard + row part
-  int off_w;              // value-term weight sums (fp32); same layout as [off_tab, off_neg + zr)
+  int off_w;              // value term, vw = 0: weight sums (fp32) mirroring [off_tab, off_neg + zr) with 4-byte entries
+  // Value term, vw = 1: the weights of a query row are summed per (row bucket a,
+  // key column x), [S][Wp] fp32 at off_vw + row * vw_pitch, so that the two
+  // lanes of a row own disjoint entries and plain read-modify-writes replace
+  // LDS atomics; the epilogue turns them into per-bucket sums by prefix sums
+  // over x and the column range of each column bucket (off_cr: the dx range
+  // of each column bucket, int16 lo | hi << 16).  off_vd: 16 bytes per lane that
+  // take the writes of merged entries.
+  int vw, off_vw, vw_pitch, off_vd, off_cr;
+  uint32_t vw_mg;         // ceil(2^32 / (S * gsz)): row bucket from a gather row part
+  uint32_t vw_ms;         // ceil(2^32 / S): row bucket from a bucket id
   int off_tq, p_tq;       // query-term bucket scores (fp32) of the current key block [32][p_tq]
   int off_tqz, off_tqn;   // guard regions of the query-term scores
   int off_ry, off_cx;     // per-axis tables (int32): (g(dy)+H)*S*gsz and g(dx)+H
