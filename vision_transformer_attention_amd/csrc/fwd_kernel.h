@@ -1207,19 +1207,29 @@ rpe_fwd_kernel(Params p) {
     if constexpr (TV) {
       if (VW && p.vw && active) {
         // per-column sums -> prefix sums over the key columns, each lane of the
-        // row taking every other row bucket
+        // row taking every other row bucket (a row bucket's Wp / 4 chunks are
+        // read before any is written; chunks past column C hold sums never read)
+        const int nch = p.Wp >> 2;
         for (int a = h; a < p.S; a += 2) {
-          char* const ar = smem + vrowoff + (a << (p.lwp + 2));
+          f32x4* const ar = reinterpret_cast<f32x4*>(smem + vrowoff + (a << (p.lwp + 2)));
+          f32x4 v[kMaxWp / 4 / 2];
+#pragma unroll
+          for (int k = 0; k < kMaxWp / 4 / 2; ++k)
+            if (k < nch) v[k] = ar[k];
           float run = 0.0f;
-          for (int x0 = 0; x0 < p.C; x0 += 4) {
-            f32x4 v = *reinterpret_cast<const f32x4*>(ar + 4 * x0);
-            v[0] += run;
-            v[1] += v[0];
-            v[2] += v[1];
-            v[3] += v[2];
-            run = v[3];
-            *reinterpret_cast<f32x4*>(ar + 4 * x0) = v;
+#pragma unroll
+          for (int k = 0; k < kMaxWp / 4 / 2; ++k) {
+            if (k < nch) {
+              v[k][0] += run;
+              v[k][1] += v[k][0];
+              v[k][2] += v[k][1];
+              v[k][3] += v[k][2];
+              run = v[k][3];
+            }
           }
+#pragma unroll
+          for (int k = 0; k < kMaxWp / 4 / 2; ++k)
+            if (k < nch) ar[k] = v[k];
         }
       }
       for (; e < L; ++e) {
@@ -1229,26 +1239,44 @@ rpe_fwd_kernel(Params p) {
           float wv[4][4];
           if (VW && p.vw) {
             // W[b] for b = (a, c): the prefix sums of row bucket a over the key
-            // columns x with g(xi - x) + H = c, a contiguous range
+            // columns x with g(xi - x) + H = c, a contiguous range.  Branch-free
+            // in three rounds (range ends, prefix sums, differences) so that each
+            // round's LDS reads are in flight together; buckets past nb read
+            // bucket nb - 1 and are dropped.
+            int fa[4][4], fb[4][4];
+            bool ok[4][4], lo0[4][4];
   #pragma unroll
             for (int j = 0; j < 4; ++j)
   #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const int b = kRowTile * t + 8 * j + 4 * h + i;
-                float w = 0.0f;
-                if (b < p.nb) {
-                  const int a = static_cast<int>(__umulhi(static_cast<uint32_t>(b), p.vw_ms));
-                  const int cr = cr_tab[b - a * p.S];
-                  const int lo = static_cast<int16_t>(cr & 0xffff), hi = cr >> 16;
-                  const int xlo = xi - hi < 0 ? 0 : xi - hi;
-                  const int xhi = xi - lo > p.C - 1 ? p.C - 1 : xi - lo;
-                  if (xlo <= xhi) {
-                    const float* const f = reinterpret_cast<const float*>(smem + vrowoff + (a << (p.lwp + 2)));
-                    w = f[xhi] - (xlo > 0 ? f[xlo - 1] : 0.0f);
-                  }
-                }
-                wv[j][i] = w;
+                const int b0 = kRowTile * t + 8 * j + 4 * h + i;
+                const int b = b0 < p.nb ? b0 : p.nb - 1;
+                const int a = static_cast<int>(__umulhi(static_cast<uint32_t>(b), p.vw_ms));
+                fa[j][i] = vrowoff + (a << (p.lwp + 2));
+                fb[j][i] = cr_tab[b - a * p.S];
               }
+            float fh[4][4], fl[4][4];
+  #pragma unroll
+            for (int j = 0; j < 4; ++j)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int cr = fb[j][i];
+                const int lo = static_cast<int16_t>(cr & 0xffff), hi = cr >> 16;
+                const int xlo = xi - hi < 0 ? 0 : xi - hi;
+                const int xhi = xi - lo > p.C - 1 ? p.C - 1 : xi - lo;
+                const int b0 = kRowTile * t + 8 * j + 4 * h + i;
+                ok[j][i] = b0 < p.nb && xlo <= xhi;
+                const int ih = xhi < 0 ? 0 : xhi;
+                const int il = xlo > 0 ? xlo - 1 : 0;
+                lo0[j][i] = xlo == 0;
+                fh[j][i] = *reinterpret_cast<const float*>(smem + fa[j][i] + 4 * ih);
+                fl[j][i] = *reinterpret_cast<const float*>(smem + fa[j][i] + 4 * il);
+              }
+  #pragma unroll
+            for (int j = 0; j < 4; ++j)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i)
+                wv[j][i] = ok[j][i] ? fh[j][i] - (lo0[j][i] ? 0.0f : fl[j][i]) : 0.0f;
           } else {
             const float* wrow = reinterpret_cast<const float*>(smem + waddr(rowbase));
   #pragma unroll
