@@ -1206,30 +1206,52 @@ rpe_fwd_kernel(Params p) {
     // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
     if constexpr (TV) {
       if (VW && p.vw && active) {
-        // per-column sums -> prefix sums over the key columns, each lane of the
-        // row taking every other row bucket (a row bucket's Wp / 4 chunks are
-        // read before any is written; chunks past column C hold sums never read)
-        const int nch = p.Wp >> 2;
-        for (int a = h; a < p.S; a += 2) {
-          f32x4* const ar = reinterpret_cast<f32x4*>(smem + vrowoff + (a << (p.lwp + 2)));
-          f32x4 v[kMaxWp / 4 / 2];
+        // per-column sums -> prefix sums over the key columns.  Each lane of the
+        // row takes every other row bucket, four at a time as independent add
+        // chains, over the chunks that cover the C columns in passes of four;
+        // each pass reads all its chunks before writing any.  (A lane with
+        // fewer than four buckets left reads its first bucket for the others
+        // and does not write them.)
+        const int nch = (p.C + 3) >> 2;
+        for (int a0 = h; a0 < p.S; a0 += 8) {
+          f32x4* ar[4];
+          bool va[4];
+          float run[4];
 #pragma unroll
-          for (int k = 0; k < kMaxWp / 4 / 2; ++k)
-            if (k < nch) v[k] = ar[k];
-          float run = 0.0f;
-#pragma unroll
-          for (int k = 0; k < kMaxWp / 4 / 2; ++k) {
-            if (k < nch) {
-              v[k][0] += run;
-              v[k][1] += v[k][0];
-              v[k][2] += v[k][1];
-              v[k][3] += v[k][2];
-              run = v[k][3];
-            }
+          for (int u = 0; u < 4; ++u) {
+            const int a = a0 + 2 * u;
+            va[u] = a < p.S;
+            ar[u] = reinterpret_cast<f32x4*>(smem + vrowoff + ((va[u] ? a : a0) << (p.lwp + 2)));
+            run[u] = 0.0f;
           }
+          for (int c0 = 0; c0 < nch; c0 += 4) {
+            f32x4 v[4][4];
 #pragma unroll
-          for (int k = 0; k < kMaxWp / 4 / 2; ++k)
-            if (k < nch) ar[k] = v[k];
+            for (int k = 0; k < 4; ++k)
+              if (c0 + k < nch) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u][k] = ar[u][c0 + k];
+              }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (c0 + k < nch) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  v[u][k][0] += run[u];
+                  v[u][k][1] += v[u][k][0];
+                  v[u][k][2] += v[u][k][1];
+                  v[u][k][3] += v[u][k][2];
+                  run[u] = v[u][k][3];
+                }
+              }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (va[u]) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                  if (c0 + k < nch) ar[u][c0 + k] = v[u][k];
+              }
+          }
         }
       }
       for (; e < L; ++e) {
