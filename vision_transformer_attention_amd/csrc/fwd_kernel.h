@@ -137,6 +137,20 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(base) : "memory", "m0");
 }
 
+// Load of a T from LDS byte address a.
+template <typename T>
+__device__ __forceinline__ T lds_at(int a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(static_cast<uintptr_t>(static_cast<uint32_t>(a)));
+}
+
+// dma16 with a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset (the scalar-base form of the instruction).
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(base)
+               : "memory", "m0");
+}
+
 // n / d for a launch constant d (host-made multiplier; see FastDiv).
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   const uint32_t t = __umulhi(n, f.m);
@@ -348,7 +362,10 @@ rpe_fwd_kernel(Params p) {
   for (int i = wid; i < IPB; i += NW) ++my_ipb;
   const int lpe = 2 * my_ipb;
   char* const ring = smem + p.off_stage;
-  const uint32_t lds_ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)smem)) + p.off_stage;
+  // LDS byte address of smem: the gather addresses below are absolute, so that
+  // a gather's address is one add (row part + column part)
+  const int lds0 = static_cast<int>(reinterpret_cast<uintptr_t>((lds_ptr_t)smem));
+  const uint32_t lds_ring = static_cast<uint32_t>(lds0) + p.off_stage;
   // N index of a key slot; padding slots read a valid token (their values are masked)
   auto slot_n = [&](int blk, int s, int wb) -> int {
     if (p.prefix_block) {
@@ -363,15 +380,16 @@ rpe_fwd_kernel(Params p) {
   };
   // Interior grid blocks (rows < R-1, Wp <= 32): a slot's column is the same in
   // every block and its row advances by 32/Wp grid rows, so the byte offset of
-  // this wave's first instruction (i = wid) is (wbase * RB + ioff0) + block * idoff.
+  // this wave's first instruction (i = wid) is wbase * RB + ioff0 + block * idoff,
+  // with a per-lane part ioff0 and a uniform step idoff.  Padding columns load
+  // the row's last token (any token would do: their weights are zero).
   uint32_t ioff0 = 0, idoff = 0;
   if constexpr (!WIDE) {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
     const int x = row & (p.Wp - 1), y0 = row >> p.lwp;
-    const bool col = x < p.C;
-    ioff0 = static_cast<uint32_t>(col ? y0 * rowstride + x : 0) * RB + cb;
-    idoff = col ? static_cast<uint32_t>((kBlockSlots >> p.lwp) * rowstride * RB) : 0u;
+    ioff0 = static_cast<uint32_t>(y0 * rowstride + (x < p.C ? x : p.C - 1)) * RB + cb;
+    idoff = static_cast<uint32_t>((kBlockSlots >> p.lwp) * rowstride * RB);
   }
   // Copy 32 rows into a swizzled row-major tile: instruction i covers rows
   // [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR with
@@ -412,7 +430,6 @@ rpe_fwd_kernel(Params p) {
   // Interior block gb (grid rows < R-1, no prefix keys) of a single-unit
   // workgroup into ring stage `stage`: the common case of issue(), without its
   // element-kind tests.
-  const uint32_t wbi = static_cast<uint32_t>(wbase) * RB + ioff0;
   auto interior_off = [&](int i, int gb) -> uint32_t {
     const int row = i * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
@@ -424,9 +441,16 @@ rpe_fwd_kernel(Params p) {
     const uint32_t kt = lds_ring + stage * (2 * TILE);
     const uint32_t vt = kt + TILE;
     if (wid < IPB) {
-      const uint32_t off = WIDE ? interior_off(wid, gb) : wbi + static_cast<uint32_t>(gb) * idoff;
-      dma16(kgb + off, kt + wid * 1024);
-      dma16(vgb + off, vt + wid * 1024);
+      if constexpr (WIDE) {
+        const uint32_t off = interior_off(wid, gb);
+        dma16(kgb + off, kt + wid * 1024);
+        dma16(vgb + off, vt + wid * 1024);
+      } else {
+        // uniform part in the scalar base, per-lane part fixed across blocks
+        const uint32_t ub = static_cast<uint32_t>(wbase) * RB + static_cast<uint32_t>(gb) * idoff;
+        dma16s(kgb + ub, ioff0, kt + wid * 1024);
+        dma16s(vgb + ub, ioff0, vt + wid * 1024);
+      }
     }
     for (int i = wid + NW; i < IPB; i += NW) {
       const uint32_t off = interior_off(i, gb);
@@ -578,23 +602,35 @@ rpe_fwd_kernel(Params p) {
 #pragma unroll
   for (int c = 0; c < DTL; ++c) oacc[c] = f32x16{};
   // bf16: O^T += V^T P^T with P already packed, pk[kk] = the B operand of step kk
+  // Per-lane byte offsets of the transpose reads of head-dim tile c for key rows
+  // row0 = 4 (g16 >> 1) + m (+ 8, + 16 kk): rows 8 and 16 apart share the row
+  // swizzle (CPR <= 8), so one base per tile serves all four reads of a block
+  // and the rest are immediate offsets.
+  int tro[DTL];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int m = i16 >> 2, a = i16 & 3;
+    const int dsub = (g16 & 1) * 16;
+    const int row0 = 4 * (g16 >> 1) + m;
+#pragma unroll
+    for (int c = 0; c < DTL; ++c) {
+      int col = 32 * c + dsub + 4 * a;   // head-dim column (element)
+      if (col >= D) col = 0;             // beyond the head dim: any in-row value (unused outputs)
+      const int cb = col * 2;
+      tro[c] = row0 * RB + (((cb >> 4) ^ (row0 & (CPR - 1))) << 4) + (cb & 15);
+    }
+  }
+  static_assert(!BF || CPR <= 8, "transpose-read rows 8 apart share the swizzle");
   auto pv_packed = [&](const char* tile, const bf16x8 (&pk)[2]) {
     if constexpr (BF) {
-      const int g16 = lane >> 4, i16 = lane & 15;
-      const int m = i16 >> 2, a = i16 & 3;
-      const int dsub = (g16 & 1) * 16;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int row0 = 16 * kk + 4 * (g16 >> 1) + m, row1 = row0 + 8;
 #pragma unroll
         for (int c = 0; c < DTL; ++c) {
-          int col = 32 * c + dsub + 4 * a;
-          if (col >= D) col = 0;
-          const int cb = col * 2;
-          const int o0 = row0 * RB + (((cb >> 4) ^ (row0 & (CPR - 1))) << 4) + (cb & 15);
-          const int o1 = row1 * RB + (((cb >> 4) ^ (row1 & (CPR - 1))) << 4) + (cb & 15);
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tile + o0));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tile + o1));
+          const char* const tb = tile + tro[c];
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tb + 16 * kk * RB));
+          const s16x4 v1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tb + (16 * kk + 8) * RB));
           bf16x8 av;
           __builtin_memcpy(&av, &v0, 8);
           __builtin_memcpy(reinterpret_cast<char*>(&av) + 8, &v1, 8);
@@ -605,9 +641,6 @@ rpe_fwd_kernel(Params p) {
   };
   auto pv_tile = [&](const char* tile, const float (&pv)[4][4], bool split) {
     if constexpr (BF) {
-      const int g16 = lane >> 4, i16 = lane & 15;
-      const int m = i16 >> 2, a = i16 & 3;
-      const int dsub = (g16 & 1) * 16;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 pb, pl;
@@ -621,16 +654,12 @@ rpe_fwd_kernel(Params p) {
             pl[4 + i] = static_cast<__bf16>(x1 - static_cast<float>(pb[4 + i]));
           }
         }
-        const int row0 = 16 * kk + 4 * (g16 >> 1) + m, row1 = row0 + 8;
 #pragma unroll
         for (int c = 0; c < DTL; ++c) {
-          int col = 32 * c + dsub + 4 * a;   // head-dim column (element)
-          if (col >= D) col = 0;             // beyond the head dim: any in-row value (unused outputs)
-          const int cb = col * 2;
-          const int o0 = row0 * RB + (((cb >> 4) ^ (row0 & (CPR - 1))) << 4) + (cb & 15);
-          const int o1 = row1 * RB + (((cb >> 4) ^ (row1 & (CPR - 1))) << 4) + (cb & 15);
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tile + o0));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tile + o1));
+          const char* const tb = tile + tro[c];
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tb + 16 * kk * RB));
+          const s16x4 v1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)const_cast<char*>(tb + (16 * kk + 8) * RB));
           bf16x8 av;
           __builtin_memcpy(&av, &v0, 8);
           __builtin_memcpy(reinterpret_cast<char*>(&av) + 8, &v1, 8);
@@ -661,7 +690,7 @@ rpe_fwd_kernel(Params p) {
   // two blocks); cqb the same for the query-term scores (fp32).
   const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab * GSZ : p.off_tab;
   // per-bucket weight sums (vw = 0): the entry of a gather address, 4-byte entries
-  auto waddr = [&](int ga) -> int { return p.off_w + (ga - p.off_tab) * (4 / GSZ); };
+  auto waddr = [&](int ga) -> int { return p.off_w + (ga - lds0 - p.off_tab) * (4 / GSZ); };
   // per-column weight sums (vw = 1): this row's [S][Wp] area, the byte offset of
   // this lane's 4-column group j at phase ph within a row bucket, and the lane's
   // 16-byte slot for the writes of merged entries
@@ -730,9 +759,9 @@ rpe_fwd_kernel(Params p) {
           const int xu = ((32 * ph + 8 * j) & (p.Wp - 1)) + i;
           const int cpart = cp[ph][j][i];
           const bool col = hx < p.C - xu;   // xj < C
-          cxb[ph][j][i] = !col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero);
+          cxb[ph][j][i] = lds0 + (!col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero));
           if constexpr (TQ)
-            cqb[ph][j][i] = !col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz);
+            cqb[ph][j][i] = lds0 + (!col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz));
         }
   }
   (void)cqb;
@@ -753,8 +782,8 @@ rpe_fwd_kernel(Params p) {
   // Logit (log2 units, relative to m_run) of a pair from the LDS byte addresses of its terms.
   auto logit = [&](float sv, int ab, int aqb) -> float {
     float add = 0.0f;
-    if constexpr (GATHER) add = static_cast<float>(*reinterpret_cast<const GT*>(smem + ab));
-    if constexpr (TQ) add += *reinterpret_cast<const float*>(smem + aqb);
+    if constexpr (GATHER) add = static_cast<float>(lds_at<GT>(ab));
+    if constexpr (TQ) add += lds_at<float>(aqb);
     return fmaf(sv, p.c, add);
   };
   // byte offset of the query-term row part from the gather row part
@@ -808,14 +837,14 @@ rpe_fwd_kernel(Params p) {
           int aq = TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0;
           if (prefix_blk) {
             const bool pre = slot < p.P;
-            a = pre ? p.off_zero : p.off_neg;
-            aq = pre ? p.off_tqz : p.off_tqn;
+            a = lds0 + (pre ? p.off_zero : p.off_neg);
+            aq = lds0 + (pre ? p.off_tqz : p.off_tqn);
           } else if (yj >= p.R) {
-            a = p.off_neg;
-            aq = p.off_tqn;
+            a = lds0 + p.off_neg;
+            aq = lds0 + p.off_tqn;
           } else if (p.prefix_in_tail && yj == p.R - 1 && xj >= p.C && xj - p.C < p.P) {
-            a = p.off_zero;
-            aq = p.off_tqz;
+            a = lds0 + p.off_zero;
+            aq = lds0 + p.off_tqz;
             vz[j][i] = true;
           }
           ab[j][i] = a;
@@ -892,7 +921,7 @@ rpe_fwd_kernel(Params p) {
               f32x4* const vr = reinterpret_cast<f32x4*>(smem + vrowoff);
               for (int k = h; k < (p.S << p.lwp) >> 2; k += 2) vr[k] = vr[k] * alpha;
             } else {
-              float* wrow = reinterpret_cast<float*>(smem + waddr(rowbase));
+              float* wrow = reinterpret_cast<float*>(smem + waddr(lds0 + rowbase));
               for (int b = h; b < p.nb; b += 2) wrow[b] *= alpha;
             }
           }
@@ -1300,7 +1329,7 @@ rpe_fwd_kernel(Params p) {
               for (int i = 0; i < 4; ++i)
                 wv[j][i] = ok[j][i] ? fh[j][i] - (lo0[j][i] ? 0.0f : fl[j][i]) : 0.0f;
           } else {
-            const float* wrow = reinterpret_cast<const float*>(smem + waddr(rowbase));
+            const float* wrow = reinterpret_cast<const float*>(smem + waddr(lds0 + rowbase));
   #pragma unroll
             for (int j = 0; j < 4; ++j)
   #pragma unroll
