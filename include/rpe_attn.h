@@ -205,9 +205,10 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
  *   workspace     : device, at least rpe_attn_bwd_workspace_size() bytes, caller-owned;
  *                   it holds the weights and score gradients of every unit (2 B H U T^2
  *                   floats) and per-row bucket sums
- * Computed in float32, one thread per output element (a reference-grade pass); the
- * table gradients are summed over units with float atomics, so their last bits can
- * vary from call to call.
+ * Computed in float32 with per-element kernels (not a fused pass).  The table
+ * gradients are summed over units in a fixed order when the per-unit partial sums fit
+ * in the workspace's weight region (B H U nb (terms x d + 1) <= B H U T^2 floats), and
+ * with float atomics otherwise, when their last bits can vary from call to call.
  * Asynchronous on `stream`.  Errors: descriptor validation; RPE_E_NULL for a
  * missing pointer; RPE_E_SHAPE if the workspace is too small or T*T >= 2^31. */
 rpe_status rpe_attn_bwd_workspace_size(const rpe_attn_desc* desc, uint64_t* bytes);

@@ -7,10 +7,11 @@
 //   dq_i  = s sum_j dL_ij (k_j + [K] rK[b]),  dk_j = s sum_i dL_ij (q_i + [Q] rQ[b])
 //   dv_j  = sum_i P_ij dO_i
 //   drK[b] = s sum dL_ij q_i,  drQ[b] = s sum dL_ij k_j,  drV[b] = sum P_ij dO_i,  dB[b] = sum dL_ij
-// One thread per output element (table gradients: per unit, added with float
-// atomics, so their last bits depend on the order).  P and dL of every unit live in the caller's
-// workspace, with the per-row bucket sums W (sum_j dL_ij, sum_i dL_ij and
-// sum_j P_ij per bucket) that turn the table terms into small contractions.
+// Per-element kernels (threads take a few outputs each to reuse their loads).
+// P and dL of every unit live in the caller's workspace, with the per-row
+// bucket sums W (sum_j dL_ij, sum_i dL_ij and sum_j P_ij per bucket) that turn
+// the table terms into small contractions; before the row pass the same
+// buffers hold the per-row bucket scores q_i . rK[b], k_j . rQ[b], dO_i . rV[b].
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -41,14 +42,40 @@ __device__ __forceinline__ void ld8(const __bf16* p, int64_t i, float (&o)[8]) {
 
 __global__ void bwd_zero_kernel(float* p, int64_t n);
 
-// Token index (into N) of position t of unit u.
+// n / d for grid indices, in 32-bit arithmetic whenever both fit.
+__device__ __forceinline__ int64_t div_idx(int64_t n, int64_t d) {
+  if (n <= 0x7fffffff && d <= 0x7fffffff) return static_cast<uint32_t>(n) / static_cast<uint32_t>(d);
+  return n / d;
+}
+
+// Token index (into N) of position t of unit u (the identity for a whole grid:
+// prefix tokens first, then the grid row by row, and C = gw).
 __device__ __forceinline__ int token_of(const BwdArgs& a, int u, int t) {
-  if (t < a.npre) return t;
-  const int r = (t - a.npre) / a.C, c = (t - a.npre) - ((t - a.npre) / a.C) * a.C;
-  if (a.M == 0) return a.npre + r * a.gw + c;
+  if (a.M == 0) return t;
+  const int r = t / a.M, c = t - (t / a.M) * a.M;   // (windows hold no prefix tokens)
   const int wy = u / a.wpr, wx = u - (u / a.wpr) * a.wpr;
   return (wy * a.M + r) * a.gw + wx * a.M + c;
 }
+
+// Token indices of positions 0, 1, 2, ... of a unit without divisions: the
+// identity for a whole grid (prefix tokens first, then the grid row by row),
+// row by row inside an M x M window otherwise.
+struct TokIter {
+  int tok, cc, M, skip;
+  __device__ __forceinline__ TokIter(const BwdArgs& a, int u) : tok(0), cc(0), M(a.M), skip(a.gw - a.M) {
+    if (a.M) {
+      const int wy = u / a.wpr, wx = u - (u / a.wpr) * a.wpr;
+      tok = wy * a.M * a.gw + wx * a.M;
+    }
+  }
+  __device__ __forceinline__ void next() {
+    ++tok;
+    if (M && ++cc == M) {
+      cc = 0;
+      tok += skip;
+    }
+  }
+};
 
 struct Unit {
   int64_t bh;       // batch * H + head
@@ -58,83 +85,131 @@ struct Unit {
 
 __device__ __forceinline__ Unit unit_of(const BwdArgs& a, int64_t ub) {
   Unit x;
-  x.bh = ub / a.U;
+  x.bh = div_idx(ub, a.U);
   x.u = static_cast<int>(ub - x.bh * a.U);
-  x.head = static_cast<int>(x.bh % a.H);
+  x.head = static_cast<int>(x.bh - div_idx(x.bh, a.H) * a.H);
   x.base = x.bh * a.N * a.D;
   return x;
 }
 
-// P and dP of every pair; one thread per (unit, i, j).
+// Per-row bucket scores of each unit, into the bucket-sum buffers before the
+// row pass takes them over: q_t . rK[b] -> Wq (grid row 0), k_t . rQ[b] -> Wk
+// (1), dO_t . rV[b] -> Wv (2); one thread per (unit, t, b).
+template <typename DT>
+__global__ void bwd_rowtab_kernel(BwdArgs a) {
+  const DT* x;
+  const DT* tab;
+  float* out;
+  if (blockIdx.y == 0) {
+    x = static_cast<const DT*>(a.q); tab = static_cast<const DT*>(a.rk); out = a.Wq;
+  } else if (blockIdx.y == 1) {
+    x = static_cast<const DT*>(a.k); tab = static_cast<const DT*>(a.rq); out = a.Wk;
+  } else {
+    x = static_cast<const DT*>(a.dout); tab = static_cast<const DT*>(a.rv); out = a.Wv;
+  }
+  if (!tab || !out) return;
+  const int64_t per = static_cast<int64_t>(a.T) * a.nb;
+  const int64_t total = a.n_units * per;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t ub = div_idx(e, per);
+    const int r = static_cast<int>(e - ub * per);
+    const int t = r / a.nb, bk = r - (r / a.nb) * a.nb;
+    const Unit u = unit_of(a, ub);
+    const int64_t xr = u.base + static_cast<int64_t>(token_of(a, u.u, t)) * a.D;
+    const int64_t tr = ((a.tables_per_head ? u.head : 0) * static_cast<int64_t>(a.nb) + bk) * a.D;
+    float acc = 0.0f;
+    for (int d0 = 0; d0 < a.D; d0 += 8) {
+      float xd[8], td[8];
+      ld8(x, xr + d0, xd);
+      ld8(tab, tr + d0, td);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc += xd[c] * td[c];
+    }
+    out[e] = acc;
+  }
+}
+
+// P and dP of every pair: a thread takes kIB consecutive query rows i at one
+// key j (the lanes of a wave run over j), so each K and V row it loads serves
+// kIB pairs and the Q and dO rows are shared by the wave; the position terms
+// come from the per-row bucket scores.
+constexpr int kIB = 4;
 template <typename DT>
 __global__ void bwd_scores_kernel(BwdArgs a) {
   const DT* q = static_cast<const DT*>(a.q);
   const DT* k = static_cast<const DT*>(a.k);
   const DT* v = static_cast<const DT*>(a.v);
   const DT* dO = static_cast<const DT*>(a.dout);
-  const DT* rk = static_cast<const DT*>(a.rk);
-  const DT* rq = static_cast<const DT*>(a.rq);
-  const DT* rv = static_cast<const DT*>(a.rv);
-  const int64_t TT = static_cast<int64_t>(a.T) * a.T;
-  const int64_t total = a.n_units * TT;
+  const int nib = (a.T + kIB - 1) / kIB;
+  const int64_t per = static_cast<int64_t>(nib) * a.T;
+  const int64_t total = a.n_units * per;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t ub = e / TT;
-    const int ij = static_cast<int>(e - ub * TT);
-    const int i = ij / a.T, j = ij - (ij / a.T) * a.T;
+    const int64_t ub = div_idx(e, per);
+    const int r = static_cast<int>(e - ub * per);
+    const int ib = r / a.T, j = r - (r / a.T) * a.T;
+    const int i0 = ib * kIB;
     const Unit x = unit_of(a, ub);
-    const int64_t qi = x.base + static_cast<int64_t>(token_of(a, x.u, i)) * a.D;
     const int64_t kj = x.base + static_cast<int64_t>(token_of(a, x.u, j)) * a.D;
-    const int bkt = a.bmap[ij];
-    const int64_t tb = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
-    float qk = 0.0f, rho = 0.0f, dp = 0.0f;
+    int ii[kIB], ti[kIB];
+#pragma unroll
+    for (int m = 0; m < kIB; ++m) {
+      ii[m] = i0 + m < a.T ? i0 + m : a.T - 1;
+      ti[m] = token_of(a, x.u, ii[m]);
+    }
+    float qk[kIB] = {}, dp[kIB] = {};
     for (int d0 = 0; d0 < a.D; d0 += 8) {
-      float qd[8], kd[8], od[8], t8[8];
-      ld8(q, qi + d0, qd);
+      float kd[8], vd[8], t8[8];
       ld8(k, kj + d0, kd);
-      ld8(dO, qi + d0, od);
-      ld8(v, kj + d0, t8);
+      ld8(v, kj + d0, vd);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        qk += qd[c] * kd[c];
-        dp += od[c] * t8[c];
-      }
-      if (bkt >= 0) {
-        const int64_t row = (tb + bkt) * a.D + d0;
-        if (a.rk) {
-          ld8(rk, row, t8);
+      for (int m = 0; m < kIB; ++m) {
+        const int64_t qr = x.base + static_cast<int64_t>(ti[m]) * a.D + d0;
+        ld8(q, qr, t8);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) rho += qd[c] * t8[c];
-        }
-        if (a.rq) {
-          ld8(rq, row, t8);
+        for (int c = 0; c < 8; ++c) qk[m] += t8[c] * kd[c];
+        ld8(dO, qr, t8);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) rho += kd[c] * t8[c];
-        }
-        if (a.rv) {
-          ld8(rv, row, t8);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) dp += od[c] * t8[c];
-        }
+        for (int c = 0; c < 8; ++c) dp[m] += t8[c] * vd[c];
       }
     }
-    float logit = (qk + rho) * a.scale;
-    if (a.bias && bkt >= 0) logit += a.bias[tb + bkt];
-    const float p = expf(logit - a.lse[x.bh * a.N + token_of(a, x.u, i)]);
-    a.P[e] = p;
-    a.dL[e] = dp;
+    const int64_t tb = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
+#pragma unroll
+    for (int m = 0; m < kIB; ++m) {
+      if (i0 + m >= a.T) break;
+      const int bkt = a.bmap[static_cast<int64_t>(ii[m]) * a.T + j];
+      float rho = 0.0f, dpm = dp[m];
+      if (bkt >= 0) {
+        if (a.rk) rho += a.Wq[(ub * a.T + ii[m]) * a.nb + bkt];
+        if (a.rq) rho += a.Wk[(ub * a.T + j) * a.nb + bkt];
+        if (a.rv) dpm += a.Wv[(ub * a.T + ii[m]) * a.nb + bkt];
+      }
+      float logit = (qk[m] + rho) * a.scale;
+      if (a.bias && bkt >= 0) logit += a.bias[tb + bkt];
+      const float p = expf(logit - a.lse[x.bh * a.N + ti[m]]);
+      const int64_t o = (ub * a.T + ii[m]) * a.T + j;
+      a.P[o] = p;
+      a.dL[o] = dpm;
+    }
   }
 }
 
 // Per query row: dL = P (dP - sum_j P dP) in place, and the row's bucket sums
-// Wq[b] += dL_ij and Wv[b] += P_ij (zeroed beforehand; float atomics); one
-// wave per (unit, i), its lanes over j.
+// Wq[b] = sum_j dL_ij and Wv[b] = sum_j P_ij; one wave per (unit, i), its
+// lanes over j.  LDS: the sums are formed in the wave's own 2 * nb floats
+// (zeroed, LDS float atomics, then written out in full); global: float
+// atomics into the zeroed rows (tables too large for LDS).
+template <bool LDS>
 __global__ void bwd_rows_kernel(BwdArgs a) {
+  extern __shared__ float wsh[];
   const int lane = threadIdx.x & 63;
+  float* const wq_s = wsh + (threadIdx.x >> 6) * 2 * a.nb;
+  float* const wv_s = wq_s + a.nb;
   const int64_t rows = a.n_units * a.T;
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); e < rows; e += waves) {
-    const int64_t ub = e / a.T;
+    const int64_t ub = div_idx(e, a.T);
     const int i = static_cast<int>(e - ub * a.T);
     float* pr = a.P + (ub * a.T + i) * a.T;
     float* dr = a.dL + (ub * a.T + i) * a.T;
@@ -144,14 +219,23 @@ __global__ void bwd_rows_kernel(BwdArgs a) {
     for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m);
     float* wq = a.Wq ? a.Wq + (ub * a.T + i) * a.nb : nullptr;
     float* wv = a.Wv ? a.Wv + (ub * a.T + i) * a.nb : nullptr;
+    if (LDS) {
+      for (int b = lane; b < 2 * a.nb; b += 64) wq_s[b] = 0.0f;
+    }
     const int16_t* brow = a.bmap + static_cast<int64_t>(i) * a.T;
     for (int j = lane; j < a.T; j += 64) {
       const float l = pr[j] * (dr[j] - dsum);
       dr[j] = l;
       const int bkt = brow[j];
       if (bkt >= 0) {
-        if (wq) atomicAdd(wq + bkt, l);
-        if (wv) atomicAdd(wv + bkt, pr[j]);
+        if (wq) atomicAdd((LDS ? wq_s : wq) + bkt, l);
+        if (wv) atomicAdd((LDS ? wv_s : wv) + bkt, pr[j]);
+      }
+    }
+    if (LDS) {
+      for (int b = lane; b < a.nb; b += 64) {
+        if (wq) wq[b] = wq_s[b];
+        if (wv) wv[b] = wv_s[b];
       }
     }
   }
@@ -162,7 +246,7 @@ __global__ void bwd_cols_kernel(BwdArgs a) {
   const int64_t total = a.n_units * a.T;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t ub = e / a.T;
+    const int64_t ub = div_idx(e, a.T);
     const int j = static_cast<int>(e - ub * a.T);
     float* wk = a.Wk + (ub * a.T + j) * a.nb;
     for (int b = 0; b < a.nb; ++b) wk[b] = 0.0f;
@@ -173,8 +257,12 @@ __global__ void bwd_cols_kernel(BwdArgs a) {
   }
 }
 
-// dq (grid row 0: one thread per (unit, i, d)) and dk, dv (grid row 1: one
-// thread per (unit, j, d)).
+// dq (grid row 0) and dk, dv (grid row 1).  A thread takes kTB consecutive
+// query rows (dq) or key columns (dk, dv) at one head-dim element d, so each
+// K, Q or dO element it loads serves kTB outputs; a wave's lanes run over d
+// (and neighbouring blocks of rows when D < 64), so its dL and P reads are the
+// same across the lanes of a block.
+constexpr int kTB = 4;
 template <typename DT>
 __global__ void bwd_grads_kernel(BwdArgs a) {
   const DT* q = static_cast<const DT*>(a.q);
@@ -182,84 +270,193 @@ __global__ void bwd_grads_kernel(BwdArgs a) {
   const DT* dO = static_cast<const DT*>(a.dout);
   const DT* rk = static_cast<const DT*>(a.rk);
   const DT* rq = static_cast<const DT*>(a.rq);
-  const int64_t per = static_cast<int64_t>(a.T) * a.D;
+  const int nblk = (a.T + kTB - 1) / kTB;
+  const int64_t per = static_cast<int64_t>(nblk) * a.D;
   const int64_t total = a.n_units * per;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t ub = e / per;
+    const int64_t ub = div_idx(e, per);
     const int r = static_cast<int>(e - ub * per);
-    const int t = r / a.D, d = r - (r / a.D) * a.D;
+    const int tb = r / a.D, d = r - (r / a.D) * a.D;
+    const int t0 = tb * kTB;
     const Unit x = unit_of(a, ub);
-    const int64_t tb = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
-    const float* Prow = a.P + ub * a.T * a.T;
-    const float* Lrow = a.dL + ub * a.T * a.T;
-    const int64_t o = x.base + static_cast<int64_t>(token_of(a, x.u, t)) * a.D + d;
+    const int64_t tbo = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
+    const float* Pu = a.P + ub * a.T * a.T;
+    const float* Lu = a.dL + ub * a.T * a.T;
+    int tr[kTB];   // this thread's rows / columns (clamped; the extra ones are not written)
+#pragma unroll
+    for (int m = 0; m < kTB; ++m) tr[m] = t0 + m < a.T ? t0 + m : a.T - 1;
+    const DT* qb = q + x.base + d;
+    const DT* kb = k + x.base + d;
+    const DT* ob = dO + x.base + d;
     if (blockIdx.y == 0) {
-      // as a query row t
-      float gq = 0.0f;
-#pragma unroll 8
-      for (int j = 0; j < a.T; ++j)
-        gq += Lrow[static_cast<int64_t>(t) * a.T + j] * ld(k, x.base + static_cast<int64_t>(token_of(a, x.u, j)) * a.D + d);
-      if (a.rk) {
-        const float* wq = a.Wq + (ub * a.T + t) * a.nb;
-        for (int b = 0; b < a.nb; ++b) gq += wq[b] * ld(rk, (tb + b) * a.D + d);
+      // as query rows t0 ..: dq_t = s (sum_j dL_tj k_j + sum_b Wq[t][b] rK[b])
+      float g[kTB] = {};
+      TokIter it(a, x.u);
+#pragma unroll 4
+      for (int j = 0; j < a.T; ++j, it.next()) {
+        const float kv = ld(kb, static_cast<int64_t>(it.tok) * a.D);
+#pragma unroll
+        for (int m = 0; m < kTB; ++m) g[m] += Lu[static_cast<int64_t>(tr[m]) * a.T + j] * kv;
       }
-      a.dq[o] = gq * a.scale;
+      if (a.rk) {
+        for (int bk = 0; bk < a.nb; ++bk) {
+          const float rv = ld(rk, (tbo + bk) * a.D + d);
+#pragma unroll
+          for (int m = 0; m < kTB; ++m) g[m] += a.Wq[(ub * a.T + tr[m]) * a.nb + bk] * rv;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < kTB; ++m)
+        if (t0 + m < a.T) a.dq[x.base + static_cast<int64_t>(token_of(a, x.u, t0 + m)) * a.D + d] = g[m] * a.scale;
     } else {
-      // as a key column t
-      float gk = 0.0f, gv = 0.0f;
-#pragma unroll 8
-      for (int i = 0; i < a.T; ++i) {
-        const int64_t qi = x.base + static_cast<int64_t>(token_of(a, x.u, i)) * a.D + d;
-        gk += Lrow[static_cast<int64_t>(i) * a.T + t] * ld(q, qi);
-        gv += Prow[static_cast<int64_t>(i) * a.T + t] * ld(dO, qi);
+      // as key columns t0 ..: dk_t = s (sum_i dL_it q_i + sum_b Wk[t][b] rQ[b]), dv_t = sum_i P_it dO_i
+      float gk[kTB] = {}, gv[kTB] = {};
+      TokIter it(a, x.u);
+#pragma unroll 4
+      for (int i = 0; i < a.T; ++i, it.next()) {
+        const int64_t ti = static_cast<int64_t>(it.tok) * a.D;
+        const float qv = ld(qb, ti), ov = ld(ob, ti);
+        const float* Li = Lu + static_cast<int64_t>(i) * a.T;
+        const float* Pi = Pu + static_cast<int64_t>(i) * a.T;
+#pragma unroll
+        for (int m = 0; m < kTB; ++m) {
+          gk[m] += Li[tr[m]] * qv;
+          gv[m] += Pi[tr[m]] * ov;
+        }
       }
       if (a.rq) {
-        const float* wk = a.Wk + (ub * a.T + t) * a.nb;
-        for (int b = 0; b < a.nb; ++b) gk += wk[b] * ld(rq, (tb + b) * a.D + d);
+        for (int bk = 0; bk < a.nb; ++bk) {
+          const float rv = ld(rq, (tbo + bk) * a.D + d);
+#pragma unroll
+          for (int m = 0; m < kTB; ++m) gk[m] += a.Wk[(ub * a.T + tr[m]) * a.nb + bk] * rv;
+        }
       }
-      a.dk[o] = gk * a.scale;
-      a.dv[o] = gv;
+#pragma unroll
+      for (int m = 0; m < kTB; ++m)
+        if (t0 + m < a.T) {
+          const int64_t o = x.base + static_cast<int64_t>(token_of(a, x.u, t0 + m)) * a.D + d;
+          a.dk[o] = gk[m] * a.scale;
+          a.dv[o] = gv[m];
+        }
     }
   }
 }
 
-// Table gradients: one thread per (unit, bucket, d) summing the unit's rows,
-// added into the (zeroed) table gradients with float atomics.
+// Table gradients.  Stage 1: one thread per (unit, 4 buckets, d) sums the
+// unit's rows (each Q, K or dO element it loads serves four buckets).  PART:
+// the per-unit sums go to part (regions drK, drQ, drV of n_units * nb * D
+// floats each, then dB of n_units * nb), and stage 2 adds them up per table
+// entry in a fixed order; otherwise they are added into the zeroed gradients
+// with float atomics.
 __global__ void bwd_zero_kernel(float* p, int64_t n) {
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[e] = 0.0f;
 }
 
-template <typename DT>
-__global__ void bwd_tables_kernel(BwdArgs a) {
+constexpr int kBB = 4;
+template <typename DT, bool PART>
+__global__ void bwd_tables_kernel(BwdArgs a, float* part) {
   const DT* q = static_cast<const DT*>(a.q);
   const DT* k = static_cast<const DT*>(a.k);
   const DT* dO = static_cast<const DT*>(a.dout);
-  const int64_t per = static_cast<int64_t>(a.nb) * a.D;
+  const int nbb = (a.nb + kBB - 1) / kBB;
+  const int De = (a.drk || a.drq || a.drv) ? a.D : 1;   // bias gradient only: no head-dim elements
+  const int64_t per = static_cast<int64_t>(nbb) * De;
   const int64_t total = a.n_units * per;
+  const int64_t region = a.n_units * a.nb * a.D;
+  float* const pk = part;
+  float* const pq = part + (a.drk ? region : 0);
+  float* const pv = pq + (a.drq ? region : 0);
+  float* const pb = pv + (a.drv ? region : 0);
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t ub = e / per;
+    const int64_t ub = div_idx(e, per);
     const int r = static_cast<int>(e - ub * per);
-    const int b = r / a.D, d = r - (r / a.D) * a.D;
+    const int bq = r / De, d = r - (r / De) * De;
+    const int b0 = bq * kBB;
+    int bb[kBB];
+#pragma unroll
+    for (int m = 0; m < kBB; ++m) bb[m] = b0 + m < a.nb ? b0 + m : a.nb - 1;
     const Unit x = unit_of(a, ub);
     const int tbl = a.tables_per_head ? x.head : 0;
-    float gk = 0.0f, gq = 0.0f, gv = 0.0f, gb = 0.0f;
-    for (int t = 0; t < a.T; ++t) {
-      const int64_t ti = x.base + static_cast<int64_t>(token_of(a, x.u, t)) * a.D + d;
-      const int64_t w = (ub * a.T + t) * a.nb + b;
-      if (a.drk) gk += a.Wq[w] * ld(q, ti);
-      if (a.dbias) gb += a.Wq[w];
-      if (a.drq) gq += a.Wk[w] * ld(k, ti);
-      if (a.drv) gv += a.Wv[w] * ld(dO, ti);
+    float gk[kBB] = {}, gq[kBB] = {}, gv[kBB] = {}, gb[kBB] = {};
+    TokIter it(a, x.u);
+#pragma unroll 4
+    for (int t = 0; t < a.T; ++t, it.next()) {
+      const int64_t ti = x.base + static_cast<int64_t>(it.tok) * a.D + d;
+      const int64_t w = (ub * a.T + t) * a.nb;
+      const float qv = a.drk ? ld(q, ti) : 0.0f;
+      const float kv = a.drq ? ld(k, ti) : 0.0f;
+      const float ov = a.drv ? ld(dO, ti) : 0.0f;
+#pragma unroll
+      for (int m = 0; m < kBB; ++m) {
+        if (a.drk || a.dbias) {
+          const float wq = a.Wq[w + bb[m]];
+          gk[m] += wq * qv;
+          gb[m] += wq;
+        }
+        if (a.drq) gq[m] += a.Wk[w + bb[m]] * kv;
+        if (a.drv) gv[m] += a.Wv[w + bb[m]] * ov;
+      }
     }
-    const int64_t o = (static_cast<int64_t>(tbl) * a.nb + b) * a.D + d;
-    if (a.drk && gk != 0.0f) atomicAdd(a.drk + o, gk * a.scale);
-    if (a.drq && gq != 0.0f) atomicAdd(a.drq + o, gq * a.scale);
-    if (a.drv && gv != 0.0f) atomicAdd(a.drv + o, gv);
-    if (a.dbias && d == 0 && gb != 0.0f) atomicAdd(a.dbias + static_cast<int64_t>(tbl) * a.nb + b, gb);
+#pragma unroll
+    for (int m = 0; m < kBB; ++m) {
+      if (b0 + m >= a.nb) break;
+      if (PART) {
+        const int64_t o = (ub * a.nb + b0 + m) * a.D + d;
+        if (a.drk) pk[o] = gk[m];
+        if (a.drq) pq[o] = gq[m];
+        if (a.drv) pv[o] = gv[m];
+        if (a.dbias && d == 0) pb[ub * a.nb + b0 + m] = gb[m];
+      } else {
+        const int64_t o = (static_cast<int64_t>(tbl) * a.nb + b0 + m) * a.D + d;
+        if (a.drk && gk[m] != 0.0f) atomicAdd(a.drk + o, gk[m] * a.scale);
+        if (a.drq && gq[m] != 0.0f) atomicAdd(a.drq + o, gq[m] * a.scale);
+        if (a.drv && gv[m] != 0.0f) atomicAdd(a.drv + o, gv[m]);
+        if (a.dbias && d == 0 && gb[m] != 0.0f) atomicAdd(a.dbias + static_cast<int64_t>(tbl) * a.nb + b0 + m, gb[m]);
+      }
+    }
+  }
+}
+
+// Stage 2: one wave per table-gradient element (kind, table, b, d); its lanes
+// take the table's units in turn, then a fixed shuffle tree adds the lanes.
+__global__ void bwd_tables_reduce_kernel(BwdArgs a, const float* part) {
+  const int lane = threadIdx.x & 63;
+  const int G = a.tables_per_head ? a.H : 1;
+  const int64_t NU = a.n_units / G;
+  const int64_t region = a.n_units * a.nb * a.D;
+  const float* const pk = part;
+  const float* const pq = part + (a.drk ? region : 0);
+  const float* const pv = pq + (a.drq ? region : 0);
+  const float* const pb = pv + (a.drv ? region : 0);
+  const int64_t ne = static_cast<int64_t>(G) * a.nb * a.D;   // elements per kind
+  const int64_t total = 3 * ne + static_cast<int64_t>(G) * a.nb;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); e < total; e += waves) {
+    const int kind = e < 3 * ne ? static_cast<int>(div_idx(e, ne)) : 3;
+    const int64_t r = kind < 3 ? e - kind * ne : e - 3 * ne;
+    const float* src = kind == 0 ? pk : kind == 1 ? pq : kind == 2 ? pv : pb;
+    float* dst = kind == 0 ? a.drk : kind == 1 ? a.drq : kind == 2 ? a.drv : a.dbias;
+    if (!dst) continue;
+    const int De = kind < 3 ? a.D : 1;
+    const int64_t gbd = r;                      // (table g, b, d) or (table g, b)
+    const int64_t g = div_idx(gbd, static_cast<int64_t>(a.nb) * De);
+    const int64_t bd = gbd - g * a.nb * De;     // b * De + d
+    float acc = 0.0f;
+    for (int64_t kk = lane; kk < NU; kk += 64) {
+      int64_t ub = kk;
+      if (a.tables_per_head) {
+        const int64_t bb = div_idx(kk, a.U), uu = kk - bb * a.U;
+        ub = (bb * a.H + g) * a.U + uu;
+      }
+      acc += src[ub * a.nb * De + bd];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (lane == 0) dst[gbd] = kind < 2 ? acc * a.scale : acc;
   }
 }
 
@@ -273,20 +470,34 @@ unsigned blocks_for(int64_t n) {
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.n_units == 0) return hipSuccess;
-  const int64_t pairs = a.n_units * a.T * a.T, rows = a.n_units * a.T;
-  const int64_t elems = rows * a.D;
+  const int64_t rows = a.n_units * a.T;
+  const int64_t elems = a.n_units * ((a.T + kTB - 1) / kTB) * a.D;
   const int tables = a.tables_per_head ? a.H : 1;
   const bool bf16 = a.bf16 != 0;
+  if (a.rk || a.rq || a.rv) {
+    const int64_t n = rows * a.nb;
+    if (bf16)
+      hipLaunchKernelGGL(bwd_rowtab_kernel<__bf16>, dim3(blocks_for(n), 3), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(bwd_rowtab_kernel<float>, dim3(blocks_for(n), 3), dim3(256), 0, stream, a);
+  }
+  const int64_t spairs = a.n_units * ((a.T + kIB - 1) / kIB) * a.T;
   if (bf16)
-    hipLaunchKernelGGL(bwd_scores_kernel<__bf16>, dim3(blocks_for(pairs)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_scores_kernel<__bf16>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_scores_kernel<float>, dim3(blocks_for(pairs)), dim3(256), 0, stream, a);
-  for (float* w : {a.Wq, a.Wv})
-    if (w) {
-      const int64_t n = rows * a.nb;
-      hipLaunchKernelGGL(bwd_zero_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, w, n);
-    }
-  hipLaunchKernelGGL(bwd_rows_kernel, dim3(blocks_for(rows * 64)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_scores_kernel<float>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
+  // (LDS sums: 4 waves x 2 x nb floats per block, up to 64 KB)
+  if (a.nb <= 2048) {
+    hipLaunchKernelGGL(bwd_rows_kernel<true>, dim3(blocks_for(rows * 64)), dim3(256),
+                       static_cast<size_t>(4 * 2 * a.nb) * sizeof(float), stream, a);
+  } else {
+    for (float* w : {a.Wq, a.Wv})
+      if (w) {
+        const int64_t n = rows * a.nb;
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, w, n);
+      }
+    hipLaunchKernelGGL(bwd_rows_kernel<false>, dim3(blocks_for(rows * 64)), dim3(256), 0, stream, a);
+  }
   if (a.Wk) hipLaunchKernelGGL(bwd_cols_kernel, dim3(blocks_for(rows)), dim3(256), 0, stream, a);
   if (bf16)
     hipLaunchKernelGGL(bwd_grads_kernel<__bf16>, dim3(blocks_for(elems), 2), dim3(256), 0, stream, a);
@@ -294,14 +505,26 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_grads_kernel<float>, dim3(blocks_for(elems), 2), dim3(256), 0, stream, a);
   if (a.drk || a.drq || a.drv || a.dbias) {
     const int64_t nt = static_cast<int64_t>(tables) * a.nb;
-    for (float* g : {a.drk, a.drq, a.drv})
-      if (g) hipLaunchKernelGGL(bwd_zero_kernel, dim3(blocks_for(nt * a.D)), dim3(256), 0, stream, g, nt * a.D);
-    if (a.dbias) hipLaunchKernelGGL(bwd_zero_kernel, dim3(blocks_for(nt)), dim3(256), 0, stream, a.dbias, nt);
-    const int64_t n = a.n_units * a.nb * a.D;
-    if (bf16)
-      hipLaunchKernelGGL(bwd_tables_kernel<__bf16>, dim3(blocks_for(n)), dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL(bwd_tables_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, stream, a);
+    const int64_t n = a.n_units * ((a.nb + kBB - 1) / kBB) * ((a.drk || a.drq || a.drv) ? a.D : 1);
+    // per-unit partial sums in the P buffer (free once dq, dk, dv are formed) when they fit
+    const int64_t kinds = (a.drk ? 1 : 0) + (a.drq ? 1 : 0) + (a.drv ? 1 : 0);
+    const int64_t need = a.n_units * a.nb * (kinds * a.D + (a.dbias ? 1 : 0));
+    if (need <= a.n_units * a.T * a.T) {
+      if (bf16)
+        hipLaunchKernelGGL((bwd_tables_kernel<__bf16, true>), dim3(blocks_for(n)), dim3(256), 0, stream, a, a.P);
+      else
+        hipLaunchKernelGGL((bwd_tables_kernel<float, true>), dim3(blocks_for(n)), dim3(256), 0, stream, a, a.P);
+      const int64_t nw = 3 * nt * a.D + nt;
+      hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nw * 64)), dim3(256), 0, stream, a, a.P);
+    } else {
+      for (float* g : {a.drk, a.drq, a.drv})
+        if (g) hipLaunchKernelGGL(bwd_zero_kernel, dim3(blocks_for(nt * a.D)), dim3(256), 0, stream, g, nt * a.D);
+      if (a.dbias) hipLaunchKernelGGL(bwd_zero_kernel, dim3(blocks_for(nt)), dim3(256), 0, stream, a.dbias, nt);
+      if (bf16)
+        hipLaunchKernelGGL((bwd_tables_kernel<__bf16, false>), dim3(blocks_for(n)), dim3(256), 0, stream, a, nullptr);
+      else
+        hipLaunchKernelGGL((bwd_tables_kernel<float, false>), dim3(blocks_for(n)), dim3(256), 0, stream, a, nullptr);
+    }
   }
   return hipGetLastError();
 }
