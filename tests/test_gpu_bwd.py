@@ -52,6 +52,9 @@ CASES = [
                                                        terms=frozenset("kqv"))),
     ("no position terms, 9x9 + cls, fp32", _D.resized(batch=1, heads=2, grid_h=9, grid_w=9, mode="none",
                                                       terms=frozenset(), map="swin", dtype="fp32")),
+    # 47 x 47 = 2209 table entries: the row pass sums into global memory (more than its LDS takes)
+    ("bias, one 24x24 window, fp32 d16", _S.resized(batch=1, heads=1, head_dim=16, grid_h=24, grid_w=24,
+                                                     window=24, dtype="fp32")),
 ]
 
 
