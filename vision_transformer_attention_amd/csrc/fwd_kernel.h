@@ -384,6 +384,16 @@ rpe_fwd_kernel(Params p) {
   // with a per-lane part ioff0 and a uniform step idoff.  Padding columns load
   // the row's last token (any token would do: their weights are zero).
   uint32_t ioff0 = 0, idoff = 0;
+  // Wide rows (64 slots, two blocks per grid row): per-lane offsets of the
+  // even and odd blocks of a row (padding columns load the row's last token);
+  // block gb adds the uniform (gb >> 1) * rowstride * RB.
+  uint32_t ioffe = 0, ioffo = 0;
+  if constexpr (WIDE) {
+    const int row = wid * RPI + lane / CPR;
+    const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
+    ioffe = static_cast<uint32_t>(row < p.C ? row : p.C - 1) * RB + cb;
+    ioffo = static_cast<uint32_t>(32 + row < p.C ? 32 + row : p.C - 1) * RB + cb;
+  }
   if constexpr (!WIDE) {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
@@ -442,9 +452,10 @@ rpe_fwd_kernel(Params p) {
     const uint32_t vt = kt + TILE;
     if (wid < IPB) {
       if constexpr (WIDE) {
-        const uint32_t off = interior_off(wid, gb);
-        dma16(kgb + off, kt + wid * 1024);
-        dma16(vgb + off, vt + wid * 1024);
+        const uint32_t ub = (static_cast<uint32_t>(wbase) + static_cast<uint32_t>(gb >> 1) * rowstride) * RB;
+        const uint32_t vo = (gb & 1) ? ioffo : ioffe;
+        dma16s(kgb + ub, vo, kt + wid * 1024);
+        dma16s(vgb + ub, vo, vt + wid * 1024);
       } else {
         // uniform part in the scalar base, per-lane part fixed across blocks
         const uint32_t ub = static_cast<uint32_t>(wbase) * RB + static_cast<uint32_t>(gb) * idoff;
