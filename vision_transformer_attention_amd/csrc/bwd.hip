@@ -40,7 +40,7 @@ __device__ __forceinline__ void ld8(const __bf16* p, int64_t i, float (&o)[8]) {
   }
 }
 
-__global__ void bwd_zero_kernel(float* p, int64_t n);
+__global__ void __launch_bounds__(256) bwd_zero_kernel(float* p, int64_t n);
 
 // n / d for grid indices, in 32-bit arithmetic whenever both fit.
 __device__ __forceinline__ int64_t div_idx(int64_t n, int64_t d) {
@@ -96,7 +96,7 @@ __device__ __forceinline__ Unit unit_of(const BwdArgs& a, int64_t ub) {
 // row pass takes them over: q_t . rK[b] -> Wq (grid row 0), k_t . rQ[b] -> Wk
 // (1), dO_t . rV[b] -> Wv (2); one thread per (unit, t, b).
 template <typename DT>
-__global__ void bwd_rowtab_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) bwd_rowtab_kernel(BwdArgs a) {
   const DT* x;
   const DT* tab;
   float* out;
@@ -136,7 +136,7 @@ __global__ void bwd_rowtab_kernel(BwdArgs a) {
 // come from the per-row bucket scores.
 constexpr int kIB = 4;
 template <typename DT>
-__global__ void bwd_scores_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) bwd_scores_kernel(BwdArgs a) {
   const DT* q = static_cast<const DT*>(a.q);
   const DT* k = static_cast<const DT*>(a.k);
   const DT* v = static_cast<const DT*>(a.v);
@@ -201,7 +201,7 @@ __global__ void bwd_scores_kernel(BwdArgs a) {
 // (zeroed, LDS float atomics, then written out in full); global: float
 // atomics into the zeroed rows (tables too large for LDS).
 template <bool LDS>
-__global__ void bwd_rows_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
   extern __shared__ float wsh[];
   const int lane = threadIdx.x & 63;
   float* const wq_s = wsh + (threadIdx.x >> 6) * 2 * a.nb;
@@ -242,7 +242,7 @@ __global__ void bwd_rows_kernel(BwdArgs a) {
 }
 
 // Per key column: Wk[b] = sum_i dL_ij; one thread per (unit, j).
-__global__ void bwd_cols_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) bwd_cols_kernel(BwdArgs a) {
   const int64_t total = a.n_units * a.T;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -264,7 +264,7 @@ __global__ void bwd_cols_kernel(BwdArgs a) {
 // same across the lanes of a block.
 constexpr int kTB = 4;
 template <typename DT>
-__global__ void bwd_grads_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) bwd_grads_kernel(BwdArgs a) {
   const DT* q = static_cast<const DT*>(a.q);
   const DT* k = static_cast<const DT*>(a.k);
   const DT* dO = static_cast<const DT*>(a.dout);
@@ -349,7 +349,7 @@ __global__ void bwd_grads_kernel(BwdArgs a) {
 // floats each, then dB of n_units * nb), and stage 2 adds them up per table
 // entry in a fixed order; otherwise they are added into the zeroed gradients
 // with float atomics.
-__global__ void bwd_zero_kernel(float* p, int64_t n) {
+__global__ void __launch_bounds__(256) bwd_zero_kernel(float* p, int64_t n) {
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[e] = 0.0f;
@@ -357,6 +357,8 @@ __global__ void bwd_zero_kernel(float* p, int64_t n) {
 
 constexpr int kBB = 4;
 template <typename DT, bool PART>
+// (no launch bounds: at the default register cap it keeps 4 waves per SIMD, which
+// measured faster than a spill-free 3)
 __global__ void bwd_tables_kernel(BwdArgs a, float* part) {
   const DT* q = static_cast<const DT*>(a.q);
   const DT* k = static_cast<const DT*>(a.k);
@@ -423,7 +425,7 @@ __global__ void bwd_tables_kernel(BwdArgs a, float* part) {
 
 // Stage 2: one wave per table-gradient element (kind, table, b, d); its lanes
 // take the table's units in turn, then a fixed shuffle tree adds the lanes.
-__global__ void bwd_tables_reduce_kernel(BwdArgs a, const float* part) {
+__global__ void __launch_bounds__(256) bwd_tables_reduce_kernel(BwdArgs a, const float* part) {
   const int lane = threadIdx.x & 63;
   const int G = a.tables_per_head ? a.H : 1;
   const int64_t NU = a.n_units / G;
