@@ -343,6 +343,202 @@ __global__ void __launch_bounds__(256) bwd_grads_kernel(BwdArgs a) {
   }
 }
 
+// dq, dk, dv on the matrix cores (bf16 inputs, head dim 32 or 64).  One wave
+// per (unit, 32-row tile, kind): kind 0 forms dq^T = K^T dL^T (+ rK^T Wq^T) for
+// query rows r0 .. r0 + 31, kind 1 forms dk^T = Q^T dL (+ rQ^T Wk^T) and
+// dv^T = dO^T P for key columns r0 .. r0 + 31.  The A operands (K, Q, dO or a
+// table, transposed) come from [32][D] tiles staged in LDS with a 16-byte
+// chunk swizzle and read with transpose loads; the B operands are dL, P or
+// bucket-sum values, split into bf16 high and low parts (two products each),
+// so about 16 bits of them survive.  The k slots 8h .. 8h + 7 of step kk are
+// tile rows 16 kk + 4h + (0..3) and 16 kk + 8 + 4h + (0..3), the order the
+// transpose loads deliver.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
+
+template <int D>
+__global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
+  constexpr int RB = D * 2, CPR = RB / 16, DTL = D / 32;
+  static_assert(D == 32 || D == 64, "head dim");
+  __shared__ __attribute__((aligned(16))) char tiles[2][32 * RB];
+  const __bf16* const q = static_cast<const __bf16*>(a.q);
+  const __bf16* const k = static_cast<const __bf16*>(a.k);
+  const __bf16* const dO = static_cast<const __bf16*>(a.dout);
+  const __bf16* const rk = static_cast<const __bf16*>(a.rk);
+  const __bf16* const rq = static_cast<const __bf16*>(a.rq);
+  const int lane = threadIdx.x, h = lane >> 5, r32 = lane & 31;
+  const int kind = blockIdx.y;
+  const int nrt = (a.T + 31) / 32, nbt = (a.nb + 31) / 32;
+  // transpose-read offsets of head-dim tile c (A operand), as in the forward's PV step
+  int tro[DTL];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int m = i16 >> 2, aa = i16 & 3;
+    const int row0 = 4 * (g16 >> 1) + m;
+#pragma unroll
+    for (int c = 0; c < DTL; ++c) {
+      const int cb = (32 * c + (g16 & 1) * 16 + 4 * aa) * 2;
+      tro[c] = row0 * RB + (((cb >> 4) ^ (row0 & (CPR - 1))) << 4) + (cb & 15);
+    }
+  }
+  const int64_t wgs = a.n_units * nrt;
+  for (int64_t wg = blockIdx.x; wg < wgs; wg += gridDim.x) {
+    const int64_t ub = div_idx(wg, nrt);
+    const int r0 = static_cast<int>(wg - ub * nrt) * 32;
+    const Unit x = unit_of(a, ub);
+    const int64_t tbo = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
+    // [32][D] rows of src into tile buf: row r is src + off(r) (rows r >= nrows: zeros)
+    auto stage = [&](char* buf, const __bf16* src, int t0, int nrows, bool table) {
+#pragma unroll
+      for (int s = 0; s < CPR / 2; ++s) {
+        const int qc = lane + 64 * s;
+        const int row = qc / CPR, c = qc - (qc / CPR) * CPR;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t0 + row < nrows) {
+          const int64_t off = table ? (tbo + t0 + row) * D
+                                    : x.base + static_cast<int64_t>(token_of(a, x.u, t0 + row)) * D;
+          v = *reinterpret_cast<const uint4*>(src + off + c * 8);
+        }
+        *reinterpret_cast<uint4*>(buf + row * RB + ((c ^ (row & (CPR - 1))) << 4)) = v;
+      }
+      asm volatile("" ::: "memory");
+    };
+    // A operand of step kk, head-dim tile c, from tile buf
+    auto a_op = [&](const char* buf, int kk, int c) -> bf16x8_t {
+      const char* tb = buf + tro[c];
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)const_cast<char*>(tb + 16 * kk * RB));
+      const s16x4_t v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)const_cast<char*>(tb + (16 * kk + 8) * RB));
+      bf16x8_t av;
+      __builtin_memcpy(&av, &v0, 8);
+      __builtin_memcpy(reinterpret_cast<char*>(&av) + 8, &v1, 8);
+      return av;
+    };
+    // acc[c] += A(buf) * B for the 16 k slots of step kk given as fp32 values bv[8]
+    auto mma = [&](f32x16_t (&acc)[DTL], const char* buf, int kk, const float (&bv)[8]) {
+      bf16x8_t hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = static_cast<__bf16>(bv[e]);
+        lo[e] = static_cast<__bf16>(bv[e] - static_cast<float>(hi[e]));
+      }
+#pragma unroll
+      for (int c = 0; c < DTL; ++c) {
+        const bf16x8_t av = a_op(buf, kk, c);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, hi, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, lo, acc[c], 0, 0, 0);
+      }
+    };
+    f32x16_t acc0[DTL], acc1[DTL];
+#pragma unroll
+    for (int c = 0; c < DTL; ++c) {
+      acc0[c] = f32x16_t{};
+      acc1[c] = f32x16_t{};
+    }
+    const int n = r0 + r32;                 // this lane's output row (kind 0) / column (kind 1)
+    const int nc = n < a.T ? n : a.T - 1;
+    const bool nok = n < a.T;
+    if (kind == 0) {
+      const float* Lr = a.dL + (ub * a.T + nc) * a.T;
+      for (int jt = 0; jt < nrt; ++jt) {
+        stage(tiles[0], k, jt * 32, a.T, false);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          float bv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = jt * 32 + 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
+            bv[e] = (nok && j < a.T) ? Lr[j] : 0.0f;
+          }
+          mma(acc0, tiles[0], kk, bv);
+        }
+        asm volatile("" ::: "memory");
+      }
+      if (a.rk) {
+        const float* Wr = a.Wq + (ub * a.T + nc) * a.nb;
+        for (int bt = 0; bt < nbt; ++bt) {
+          stage(tiles[0], rk, bt * 32, a.nb, true);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            float bv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int b = bt * 32 + 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
+              bv[e] = (nok && b < a.nb) ? Wr[b] : 0.0f;
+            }
+            mma(acc0, tiles[0], kk, bv);
+          }
+          asm volatile("" ::: "memory");
+        }
+      }
+    } else {
+      const float* Lc = a.dL + ub * a.T * a.T + nc;
+      const float* Pc = a.P + ub * a.T * a.T + nc;
+      for (int it = 0; it < nrt; ++it) {
+        stage(tiles[0], q, it * 32, a.T, false);
+        stage(tiles[1], dO, it * 32, a.T, false);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          float bl[8], bp[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = it * 32 + 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
+            const bool ok = nok && i < a.T;
+            const int64_t o = static_cast<int64_t>(ok ? i : 0) * a.T;
+            bl[e] = ok ? Lc[o] : 0.0f;
+            bp[e] = ok ? Pc[o] : 0.0f;
+          }
+          mma(acc0, tiles[0], kk, bl);
+          mma(acc1, tiles[1], kk, bp);
+        }
+        asm volatile("" ::: "memory");
+      }
+      if (a.rq) {
+        const float* Wr = a.Wk + (ub * a.T + nc) * a.nb;
+        for (int bt = 0; bt < nbt; ++bt) {
+          stage(tiles[0], rq, bt * 32, a.nb, true);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            float bv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int b = bt * 32 + 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
+              bv[e] = (nok && b < a.nb) ? Wr[b] : 0.0f;
+            }
+            mma(acc0, tiles[0], kk, bv);
+          }
+          asm volatile("" ::: "memory");
+        }
+      }
+    }
+    // lane holds (head dim 32 c + 8 j + 4 h + i, row / column n) in element 4 j + i
+    if (nok) {
+      const int64_t o = x.base + static_cast<int64_t>(token_of(a, x.u, n)) * D;
+#pragma unroll
+      for (int c = 0; c < DTL; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = 32 * c + 8 * j + 4 * h;
+          f32x4_t v0, v1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v0[i] = acc0[c][4 * j + i];
+            v1[i] = acc1[c][4 * j + i];
+          }
+          if (kind == 0) {
+            *reinterpret_cast<f32x4_t*>(a.dq + o + d0) = v0 * a.scale;
+          } else {
+            *reinterpret_cast<f32x4_t*>(a.dk + o + d0) = v0 * a.scale;
+            *reinterpret_cast<f32x4_t*>(a.dv + o + d0) = v1;
+          }
+        }
+    }
+  }
+}
+
 // Table gradients.  Stage 1: one thread per (unit, 4 buckets, d) sums the
 // unit's rows (each Q, K or dO element it loads serves four buckets).  PART:
 // the per-unit sums go to part (regions drK, drQ, drV of n_units * nb * D
@@ -501,7 +697,13 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_rows_kernel<false>, dim3(blocks_for(rows * 64)), dim3(256), 0, stream, a);
   }
   if (a.Wk) hipLaunchKernelGGL(bwd_cols_kernel, dim3(blocks_for(rows)), dim3(256), 0, stream, a);
-  if (bf16)
+  const int64_t tiles = a.n_units * ((a.T + 31) / 32);
+  const unsigned tgrid = static_cast<unsigned>(tiles < 65536 ? tiles : 65536);
+  if (bf16 && a.D == 64)
+    hipLaunchKernelGGL(bwd_grads_mfma_kernel<64>, dim3(tgrid, 2), dim3(64), 0, stream, a);
+  else if (bf16 && a.D == 32)
+    hipLaunchKernelGGL(bwd_grads_mfma_kernel<32>, dim3(tgrid, 2), dim3(64), 0, stream, a);
+  else if (bf16)
     hipLaunchKernelGGL(bwd_grads_kernel<__bf16>, dim3(blocks_for(elems), 2), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(bwd_grads_kernel<float>, dim3(blocks_for(elems), 2), dim3(256), 0, stream, a);
