@@ -359,22 +359,13 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
 
+// Matrix-core helpers for one wave and [32][D] bf16 tiles in LDS.
 template <int D>
-__global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
-  constexpr int RB = D * 2, CPR = RB / 16, DTL = D / 32;
+struct Mt {
+  static constexpr int RB = D * 2, CPR = RB / 16, DTL = D / 32;
   static_assert(D == 32 || D == 64, "head dim");
-  __shared__ __attribute__((aligned(16))) char tiles[2][32 * RB];
-  const __bf16* const q = static_cast<const __bf16*>(a.q);
-  const __bf16* const k = static_cast<const __bf16*>(a.k);
-  const __bf16* const dO = static_cast<const __bf16*>(a.dout);
-  const __bf16* const rk = static_cast<const __bf16*>(a.rk);
-  const __bf16* const rq = static_cast<const __bf16*>(a.rq);
-  const int lane = threadIdx.x, h = lane >> 5, r32 = lane & 31;
-  const int kind = blockIdx.y;
-  const int nrt = (a.T + 31) / 32, nbt = (a.nb + 31) / 32;
-  // transpose-read offsets of head-dim tile c (A operand), as in the forward's PV step
-  int tro[DTL];
-  {
+  int tro[DTL];   // transpose-read offsets of head-dim tile c (A operand)
+  __device__ explicit Mt(int lane) {
     const int g16 = lane >> 4, i16 = lane & 15;
     const int m = i16 >> 2, aa = i16 & 3;
     const int row0 = 4 * (g16 >> 1) + m;
@@ -384,54 +375,78 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
       tro[c] = row0 * RB + (((cb >> 4) ^ (row0 & (CPR - 1))) << 4) + (cb & 15);
     }
   }
+  // rows 0 .. 31 of a tile into buf (16-byte chunk c of row r at chunk c ^ (r % CPR));
+  // row r is at src + off(r) when ok(r), else zero
+  template <typename Ok, typename Off>
+  __device__ void stage(char* buf, const __bf16* src, int lane, Ok ok, Off off) const {
+#pragma unroll
+    for (int s = 0; s < CPR / 2; ++s) {
+      const int qc = lane + 64 * s;
+      const int row = qc / CPR, c = qc - (qc / CPR) * CPR;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ok(row)) v = *reinterpret_cast<const uint4*>(src + off(row) + c * 8);
+      *reinterpret_cast<uint4*>(buf + row * RB + ((c ^ (row & (CPR - 1))) << 4)) = v;
+    }
+    asm volatile("" ::: "memory");
+  }
+  // A operand of step kk, head-dim tile c
+  __device__ bf16x8_t a_op(const char* buf, int kk, int c) const {
+    const char* tb = buf + tro[c];
+    const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)const_cast<char*>(tb + 16 * kk * RB));
+    const s16x4_t v1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)const_cast<char*>(tb + (16 * kk + 8) * RB));
+    bf16x8_t av;
+    __builtin_memcpy(&av, &v0, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&av) + 8, &v1, 8);
+    return av;
+  }
+  // acc[c] += A(buf) * B for the 16 k slots of step kk, B given as fp32 values bv[8]
+  __device__ void mma(f32x16_t (&acc)[DTL], const char* buf, int kk, const float (&bv)[8]) const {
+    bf16x8_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = static_cast<__bf16>(bv[e]);
+      lo[e] = static_cast<__bf16>(bv[e] - static_cast<float>(hi[e]));
+    }
+#pragma unroll
+    for (int c = 0; c < DTL; ++c) {
+      const bf16x8_t av = a_op(buf, kk, c);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, hi, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, lo, acc[c], 0, 0, 0);
+    }
+  }
+};
+
+// k slot e (0..7) of lane half h in step kk: tile row 16 kk + 8 (e / 4) + 4 h + e % 4
+__device__ __forceinline__ int kslot(int kk, int e, int h) { return 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3); }
+
+template <int D>
+__global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
+  constexpr int RB = D * 2, DTL = D / 32;
+  __shared__ __attribute__((aligned(16))) char tiles[2][32 * RB];
+  const __bf16* const q = static_cast<const __bf16*>(a.q);
+  const __bf16* const k = static_cast<const __bf16*>(a.k);
+  const __bf16* const dO = static_cast<const __bf16*>(a.dout);
+  const __bf16* const rk = static_cast<const __bf16*>(a.rk);
+  const __bf16* const rq = static_cast<const __bf16*>(a.rq);
+  const int lane = threadIdx.x, h = lane >> 5, r32 = lane & 31;
+  const int kind = blockIdx.y;
+  const int nrt = (a.T + 31) / 32, nbt = (a.nb + 31) / 32;
+  const Mt<D> mt(lane);
   const int64_t wgs = a.n_units * nrt;
   for (int64_t wg = blockIdx.x; wg < wgs; wg += gridDim.x) {
     const int64_t ub = div_idx(wg, nrt);
     const int r0 = static_cast<int>(wg - ub * nrt) * 32;
     const Unit x = unit_of(a, ub);
     const int64_t tbo = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
-    // [32][D] rows of src into tile buf: row r is src + off(r) (rows r >= nrows: zeros)
+    // token rows t0 + r (zero past T) / table rows t0 + r (zero past nb) of src into buf
     auto stage = [&](char* buf, const __bf16* src, int t0, int nrows, bool table) {
-#pragma unroll
-      for (int s = 0; s < CPR / 2; ++s) {
-        const int qc = lane + 64 * s;
-        const int row = qc / CPR, c = qc - (qc / CPR) * CPR;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t0 + row < nrows) {
-          const int64_t off = table ? (tbo + t0 + row) * D
-                                    : x.base + static_cast<int64_t>(token_of(a, x.u, t0 + row)) * D;
-          v = *reinterpret_cast<const uint4*>(src + off + c * 8);
-        }
-        *reinterpret_cast<uint4*>(buf + row * RB + ((c ^ (row & (CPR - 1))) << 4)) = v;
-      }
-      asm volatile("" ::: "memory");
+      mt.stage(buf, src, lane, [&](int r) { return t0 + r < nrows; },
+               [&](int r) -> int64_t {
+                 return table ? (tbo + t0 + r) * D : x.base + static_cast<int64_t>(token_of(a, x.u, t0 + r)) * D;
+               });
     };
-    // A operand of step kk, head-dim tile c, from tile buf
-    auto a_op = [&](const char* buf, int kk, int c) -> bf16x8_t {
-      const char* tb = buf + tro[c];
-      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)const_cast<char*>(tb + 16 * kk * RB));
-      const s16x4_t v1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)const_cast<char*>(tb + (16 * kk + 8) * RB));
-      bf16x8_t av;
-      __builtin_memcpy(&av, &v0, 8);
-      __builtin_memcpy(reinterpret_cast<char*>(&av) + 8, &v1, 8);
-      return av;
-    };
-    // acc[c] += A(buf) * B for the 16 k slots of step kk given as fp32 values bv[8]
-    auto mma = [&](f32x16_t (&acc)[DTL], const char* buf, int kk, const float (&bv)[8]) {
-      bf16x8_t hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = static_cast<__bf16>(bv[e]);
-        lo[e] = static_cast<__bf16>(bv[e] - static_cast<float>(hi[e]));
-      }
-#pragma unroll
-      for (int c = 0; c < DTL; ++c) {
-        const bf16x8_t av = a_op(buf, kk, c);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, hi, acc[c], 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, lo, acc[c], 0, 0, 0);
-      }
-    };
+    auto mma = [&](f32x16_t (&acc)[DTL], const char* buf, int kk, const float (&bv)[8]) { mt.mma(acc, buf, kk, bv); };
     f32x16_t acc0[DTL], acc1[DTL];
 #pragma unroll
     for (int c = 0; c < DTL; ++c) {
@@ -450,7 +465,7 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
           float bv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int j = jt * 32 + 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int j = jt * 32 + kslot(kk, e, h);
             bv[e] = (nok && j < a.T) ? Lr[j] : 0.0f;
           }
           mma(acc0, tiles[0], kk, bv);
@@ -466,7 +481,7 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
             float bv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int b = bt * 32 + 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
+              const int b = bt * 32 + kslot(kk, e, h);
               bv[e] = (nok && b < a.nb) ? Wr[b] : 0.0f;
             }
             mma(acc0, tiles[0], kk, bv);
@@ -485,7 +500,7 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
           float bl[8], bp[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int i = it * 32 + 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int i = it * 32 + kslot(kk, e, h);
             const bool ok = nok && i < a.T;
             const int64_t o = static_cast<int64_t>(ok ? i : 0) * a.T;
             bl[e] = ok ? Lc[o] : 0.0f;
@@ -505,7 +520,7 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
             float bv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int b = bt * 32 + 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
+              const int b = bt * 32 + kslot(kk, e, h);
               bv[e] = (nok && b < a.nb) ? Wr[b] : 0.0f;
             }
             mma(acc0, tiles[0], kk, bv);
@@ -534,6 +549,67 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
             *reinterpret_cast<f32x4_t*>(a.dk + o + d0) = v0 * a.scale;
             *reinterpret_cast<f32x4_t*>(a.dv + o + d0) = v1;
           }
+        }
+    }
+  }
+}
+
+// Table-gradient partials on the matrix cores (bf16 inputs, head dim 32 or
+// 64): one wave per (unit, 32-bucket tile, kind) forms the unit's
+// drK^T = Q^T Wq (kind 0), drQ^T = K^T Wk (1) or drV^T = dO^T Wv (2) for its
+// buckets, over the unit's rows in tiles of 32, into the partial regions that
+// bwd_tables_reduce_kernel adds up (unscaled, as the other stage-1 kernel).
+template <int D>
+__global__ void __launch_bounds__(64) bwd_tables_mfma_kernel(BwdArgs a, float* part) {
+  constexpr int RB = D * 2, DTL = D / 32;
+  __shared__ __attribute__((aligned(16))) char tile[32 * RB];
+  const int lane = threadIdx.x, h = lane >> 5, r32 = lane & 31;
+  const int kind = blockIdx.y;
+  const __bf16* const src = static_cast<const __bf16*>(kind == 0 ? a.q : kind == 1 ? a.k : a.dout);
+  const float* const W = kind == 0 ? a.Wq : kind == 1 ? a.Wk : a.Wv;
+  const float* const out = kind == 0 ? a.drk : kind == 1 ? a.drq : a.drv;
+  if (!out) return;
+  const int64_t region = a.n_units * a.nb * a.D;
+  float* const dst = part + (kind >= 1 && a.drk ? region : 0) + (kind == 2 && a.drq ? region : 0);
+  const int nrt = (a.T + 31) / 32, nbt = (a.nb + 31) / 32;
+  const Mt<D> mt(lane);
+  const int64_t wgs = a.n_units * nbt;
+  for (int64_t wg = blockIdx.x; wg < wgs; wg += gridDim.x) {
+    const int64_t ub = div_idx(wg, nbt);
+    const int b = static_cast<int>(wg - ub * nbt) * 32 + r32;   // this lane's bucket (column)
+    const bool bok = b < a.nb;
+    const Unit x = unit_of(a, ub);
+    const float* const Wc = W + ub * a.T * a.nb + (bok ? b : 0);
+    f32x16_t acc[DTL];
+#pragma unroll
+    for (int c = 0; c < DTL; ++c) acc[c] = f32x16_t{};
+    for (int tt = 0; tt < nrt; ++tt) {
+      const int t0 = tt * 32;
+      mt.stage(tile, src, lane, [&](int r) { return t0 + r < a.T; },
+               [&](int r) -> int64_t { return x.base + static_cast<int64_t>(token_of(a, x.u, t0 + r)) * D; });
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float bv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = t0 + kslot(kk, e, h);
+          bv[e] = (bok && t < a.T) ? Wc[static_cast<int64_t>(t) * a.nb] : 0.0f;
+        }
+        mt.mma(acc, tile, kk, bv);
+      }
+      asm volatile("" ::: "memory");
+    }
+    // lane holds (head dim 32 c + 8 j + 4 h + i, bucket b) in element 4 j + i
+    if (bok) {
+      float* const o = dst + (ub * a.nb + b) * D;
+#pragma unroll
+      for (int c = 0; c < DTL; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4_t v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[c][4 * j + i];
+          *reinterpret_cast<f32x4_t*>(o + 32 * c + 8 * j + 4 * h) = v;
         }
     }
   }
@@ -714,7 +790,13 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     const int64_t kinds = (a.drk ? 1 : 0) + (a.drq ? 1 : 0) + (a.drv ? 1 : 0);
     const int64_t need = a.n_units * a.nb * (kinds * a.D + (a.dbias ? 1 : 0));
     if (need <= a.n_units * a.T * a.T) {
-      if (bf16)
+      const int64_t bt = a.n_units * ((a.nb + 31) / 32);
+      const unsigned bgrid = static_cast<unsigned>(bt < 65536 ? bt : 65536);
+      if (bf16 && kinds > 0 && a.D == 64)
+        hipLaunchKernelGGL(bwd_tables_mfma_kernel<64>, dim3(bgrid, 3), dim3(64), 0, stream, a, a.P);
+      else if (bf16 && kinds > 0 && a.D == 32)
+        hipLaunchKernelGGL(bwd_tables_mfma_kernel<32>, dim3(bgrid, 3), dim3(64), 0, stream, a, a.P);
+      else if (bf16)
         hipLaunchKernelGGL((bwd_tables_kernel<__bf16, true>), dim3(blocks_for(n)), dim3(256), 0, stream, a, a.P);
       else
         hipLaunchKernelGGL((bwd_tables_kernel<float, true>), dim3(blocks_for(n)), dim3(256), 0, stream, a, a.P);
