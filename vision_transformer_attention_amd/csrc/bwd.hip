@@ -42,6 +42,12 @@ __device__ __forceinline__ void ld8(const __bf16* p, int64_t i, float (&o)[8]) {
 
 __global__ void __launch_bounds__(256) bwd_zero_kernel(float* p, int64_t n);
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
+
 // n / d for grid indices, in 32-bit arithmetic whenever both fit.
 __device__ __forceinline__ int64_t div_idx(int64_t n, int64_t d) {
   if (n <= 0x7fffffff && d <= 0x7fffffff) return static_cast<uint32_t>(n) / static_cast<uint32_t>(d);
@@ -191,6 +197,86 @@ __global__ void __launch_bounds__(256) bwd_scores_kernel(BwdArgs a) {
       const int64_t o = (ub * a.T + ii[m]) * a.T + j;
       a.P[o] = p;
       a.dL[o] = dpm;
+    }
+  }
+}
+
+// P and dP on the matrix cores (bf16 inputs, head dim 32 or 64): one wave per
+// (unit, 32-query tile) keeps its Q and dO rows in registers (A operands) and
+// walks the unit's keys 32 at a time, S = Q K^T and dO V^T from 16-byte chunks
+// of the K and V rows (B operands); lane l then holds key column l % 32 of
+// query rows 8 j + 4 (l / 32) + i, so each store of P and dP covers 32
+// consecutive keys of a row.  Position terms, bias and exp as in
+// bwd_scores_kernel.
+template <int D>
+__global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;
+  const __bf16* const q = static_cast<const __bf16*>(a.q);
+  const __bf16* const k = static_cast<const __bf16*>(a.k);
+  const __bf16* const v = static_cast<const __bf16*>(a.v);
+  const __bf16* const dO = static_cast<const __bf16*>(a.dout);
+  const int lane = threadIdx.x, h = lane >> 5, r32 = lane & 31;
+  const int nrt = (a.T + 31) / 32;
+  const int64_t wgs = a.n_units * nrt;
+  for (int64_t wg = blockIdx.x; wg < wgs; wg += gridDim.x) {
+    const int64_t ub = div_idx(wg, nrt);
+    const int i0 = static_cast<int>(wg - ub * nrt) * 32;
+    const Unit x = unit_of(a, ub);
+    const int64_t tb = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
+    // A operands: query row i0 + r32 (clamped), head-dim slice 16 kk + 8 h
+    bf16x8_t qa[KS], da[KS];
+    {
+      const int ir = i0 + r32 < a.T ? i0 + r32 : a.T - 1;
+      const int64_t ro = x.base + static_cast<int64_t>(token_of(a, x.u, ir)) * D + 8 * h;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 u = *reinterpret_cast<const uint4*>(q + ro + 16 * kk);
+        const uint4 w = *reinterpret_cast<const uint4*>(dO + ro + 16 * kk);
+        __builtin_memcpy(&qa[kk], &u, 16);
+        __builtin_memcpy(&da[kk], &w, 16);
+      }
+    }
+    // this lane's 16 query rows: 8 j + 4 h + i (clamped), their tokens' log-sum-exp
+    float lse[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
+      lse[e] = a.lse[x.bh * a.N + token_of(a, x.u, i < a.T ? i : a.T - 1)];
+    }
+    for (int j0 = 0; j0 < a.T; j0 += 32) {
+      const int j = j0 + r32;
+      const int jr = j < a.T ? j : a.T - 1;
+      const int64_t co = x.base + static_cast<int64_t>(token_of(a, x.u, jr)) * D + 8 * h;
+      f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 u = *reinterpret_cast<const uint4*>(k + co + 16 * kk);
+        const uint4 w = *reinterpret_cast<const uint4*>(v + co + 16 * kk);
+        bf16x8_t kb, vb;
+        __builtin_memcpy(&kb, &u, 16);
+        __builtin_memcpy(&vb, &w, 16);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kb, sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vb, pacc, 0, 0, 0);
+      }
+      if (j < a.T) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (i >= a.T) continue;
+          const int bkt = a.bmap[static_cast<int64_t>(i) * a.T + j];
+          float rho = 0.0f, dpm = pacc[e];
+          if (bkt >= 0) {
+            if (a.rk) rho += a.Wq[(ub * a.T + i) * a.nb + bkt];
+            if (a.rq) rho += a.Wk[(ub * a.T + j) * a.nb + bkt];
+            if (a.rv) dpm += a.Wv[(ub * a.T + i) * a.nb + bkt];
+          }
+          float logit = (sacc[e] + rho) * a.scale;
+          if (a.bias && bkt >= 0) logit += a.bias[tb + bkt];
+          const int64_t o = (ub * a.T + i) * a.T + j;
+          a.P[o] = expf(logit - lse[e]);
+          a.dL[o] = dpm;
+        }
+      }
     }
   }
 }
@@ -353,11 +439,6 @@ __global__ void __launch_bounds__(256) bwd_grads_kernel(BwdArgs a) {
 // so about 16 bits of them survive.  The k slots 8h .. 8h + 7 of step kk are
 // tile rows 16 kk + 4h + (0..3) and 16 kk + 8 + 4h + (0..3), the order the
 // transpose loads deliver.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
 
 // Matrix-core helpers for one wave and [32][D] bf16 tiles in LDS.
 template <int D>
@@ -756,7 +837,13 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(bwd_rowtab_kernel<float>, dim3(blocks_for(n), 3), dim3(256), 0, stream, a);
   }
   const int64_t spairs = a.n_units * ((a.T + kIB - 1) / kIB) * a.T;
-  if (bf16)
+  const int64_t qtiles = a.n_units * ((a.T + 31) / 32);
+  const unsigned qgrid = static_cast<unsigned>(qtiles < 65536 ? qtiles : 65536);
+  if (bf16 && a.D == 64)
+    hipLaunchKernelGGL(bwd_scores_mfma_kernel<64>, dim3(qgrid), dim3(64), 0, stream, a);
+  else if (bf16 && a.D == 32)
+    hipLaunchKernelGGL(bwd_scores_mfma_kernel<32>, dim3(qgrid), dim3(64), 0, stream, a);
+  else if (bf16)
     hipLaunchKernelGGL(bwd_scores_kernel<__bf16>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(bwd_scores_kernel<float>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
