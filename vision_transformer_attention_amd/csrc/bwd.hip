@@ -201,6 +201,59 @@ __global__ void __launch_bounds__(256) bwd_scores_kernel(BwdArgs a) {
   }
 }
 
+// Per-row bucket scores on the matrix cores (bf16 inputs, head dim 32 or 64):
+// one wave per (unit, 32-row tile, kind) forms x_t . tab[b] for its rows and
+// every bucket, 32 buckets at a time, from 16-byte chunks of the rows (A) and
+// of the table rows (B); lane l holds bucket l % 32 of rows 8 j + 4 (l / 32) + i,
+// so each store covers 32 consecutive buckets of a row.
+template <int D>
+__global__ void __launch_bounds__(64) bwd_rowtab_mfma_kernel(BwdArgs a) {
+  constexpr int KS = D / 16;
+  const int lane = threadIdx.x, h = lane >> 5, r32 = lane & 31;
+  const int kind = blockIdx.y;
+  const __bf16* const x = static_cast<const __bf16*>(kind == 0 ? a.q : kind == 1 ? a.k : a.dout);
+  const __bf16* const tab = static_cast<const __bf16*>(kind == 0 ? a.rk : kind == 1 ? a.rq : a.rv);
+  float* const out = kind == 0 ? a.Wq : kind == 1 ? a.Wk : a.Wv;
+  if (!tab || !out) return;
+  const int nrt = (a.T + 31) / 32;
+  const int64_t wgs = a.n_units * nrt;
+  for (int64_t wg = blockIdx.x; wg < wgs; wg += gridDim.x) {
+    const int64_t ub = div_idx(wg, nrt);
+    const int t0 = static_cast<int>(wg - ub * nrt) * 32;
+    const Unit u = unit_of(a, ub);
+    const int64_t tbo = (a.tables_per_head ? u.head : 0) * static_cast<int64_t>(a.nb);
+    bf16x8_t xa[KS];
+    {
+      const int tr = t0 + r32 < a.T ? t0 + r32 : a.T - 1;
+      const int64_t ro = u.base + static_cast<int64_t>(token_of(a, u.u, tr)) * D + 8 * h;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 w = *reinterpret_cast<const uint4*>(x + ro + 16 * kk);
+        __builtin_memcpy(&xa[kk], &w, 16);
+      }
+    }
+    for (int b0 = 0; b0 < a.nb; b0 += 32) {
+      const int b = b0 + r32;
+      const int64_t bo = (tbo + (b < a.nb ? b : a.nb - 1)) * D + 8 * h;
+      f32x16_t acc = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 w = *reinterpret_cast<const uint4*>(tab + bo + 16 * kk);
+        bf16x8_t tb;
+        __builtin_memcpy(&tb, &w, 16);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[kk], tb, acc, 0, 0, 0);
+      }
+      if (b < a.nb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int t = t0 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (t < a.T) out[(ub * a.T + t) * a.nb + b] = acc[e];
+        }
+      }
+    }
+  }
+}
+
 // P and dP on the matrix cores (bf16 inputs, head dim 32 or 64): one wave per
 // (unit, 32-query tile) keeps its Q and dO rows in registers (A operands) and
 // walks the unit's keys 32 at a time, S = Q K^T and dO V^T from 16-byte chunks
@@ -323,6 +376,31 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
         if (wq) wq[b] = wq_s[b];
         if (wv) wv[b] = wv_s[b];
       }
+    }
+  }
+}
+
+// Per key column, LDS form: one wave per (unit, 64 key columns), lane l taking
+// column j0 + l (reads of a dL row are coalesced); each lane sums into its own
+// nb floats of the wave's LDS ([nb][64], lane fastest), then writes its row.
+__global__ void __launch_bounds__(64) bwd_cols_lds_kernel(BwdArgs a) {
+  extern __shared__ float wks[];
+  const int lane = threadIdx.x;
+  const int nct = (a.T + 63) / 64;
+  const int64_t wgs = a.n_units * nct;
+  for (int64_t wg = blockIdx.x; wg < wgs; wg += gridDim.x) {
+    const int64_t ub = div_idx(wg, nct);
+    const int j = static_cast<int>(wg - ub * nct) * 64 + lane;
+    const int jc = j < a.T ? j : a.T - 1;
+    for (int b = 0; b < a.nb; ++b) wks[b * 64 + lane] = 0.0f;
+    const float* Lc = a.dL + ub * a.T * a.T + jc;
+    for (int i = 0; i < a.T; ++i) {
+      const int bkt = a.bmap[static_cast<int64_t>(i) * a.T + jc];
+      if (bkt >= 0) wks[bkt * 64 + lane] += Lc[static_cast<int64_t>(i) * a.T];
+    }
+    if (j < a.T) {
+      float* wk = a.Wk + (ub * a.T + j) * a.nb;
+      for (int b = 0; b < a.nb; ++b) wk[b] = wks[b * 64 + lane];
     }
   }
 }
@@ -831,7 +909,13 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const bool bf16 = a.bf16 != 0;
   if (a.rk || a.rq || a.rv) {
     const int64_t n = rows * a.nb;
-    if (bf16)
+    const int64_t rtiles = a.n_units * ((a.T + 31) / 32);
+    const unsigned rgrid = static_cast<unsigned>(rtiles < 65536 ? rtiles : 65536);
+    if (bf16 && a.D == 64)
+      hipLaunchKernelGGL(bwd_rowtab_mfma_kernel<64>, dim3(rgrid, 3), dim3(64), 0, stream, a);
+    else if (bf16 && a.D == 32)
+      hipLaunchKernelGGL(bwd_rowtab_mfma_kernel<32>, dim3(rgrid, 3), dim3(64), 0, stream, a);
+    else if (bf16)
       hipLaunchKernelGGL(bwd_rowtab_kernel<__bf16>, dim3(blocks_for(n), 3), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL(bwd_rowtab_kernel<float>, dim3(blocks_for(n), 3), dim3(256), 0, stream, a);
@@ -859,7 +943,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
       }
     hipLaunchKernelGGL(bwd_rows_kernel<false>, dim3(blocks_for(rows * 64)), dim3(256), 0, stream, a);
   }
-  if (a.Wk) hipLaunchKernelGGL(bwd_cols_kernel, dim3(blocks_for(rows)), dim3(256), 0, stream, a);
+  if (a.Wk) {
+    if (a.nb <= 256) {
+      const int64_t ct = a.n_units * ((a.T + 63) / 64);
+      hipLaunchKernelGGL(bwd_cols_lds_kernel, dim3(static_cast<unsigned>(ct < 65536 ? ct : 65536)), dim3(64),
+                         static_cast<size_t>(a.nb) * 64 * sizeof(float), stream, a);
+    } else {
+      hipLaunchKernelGGL(bwd_cols_kernel, dim3(blocks_for(rows)), dim3(256), 0, stream, a);
+    }
+  }
   const int64_t tiles = a.n_units * ((a.T + 31) / 32);
   const unsigned tgrid = static_cast<unsigned>(tiles < 65536 ? tiles : 65536);
   if (bf16 && a.D == 64)
