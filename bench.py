@@ -299,7 +299,7 @@ def main():
         fb, _ = flops_bytes(w)
         backward = {"workload": w.description, "us_per_call": mb * 1e3,
                     "tflops": 2.5 * fb / (mb * 1e-3) / 1e12, "finite": okb,
-                    "note": "float32 per-element reference kernels; TFLOP/s counts 2.5x the forward's FLOP"}
+                    "note": "kernel sequence over a workspace (matrix-core products for bf16); TFLOP/s counts 2.5x the forward's FLOP"}
         print(f"backward {args.workload}: {mb * 1e3:.1f} us per call", file=sys.stderr, flush=True)
     if args.copy_probe > 0:
         n = args.copy_probe << 20

@@ -205,7 +205,10 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
  *   workspace     : device, at least rpe_attn_bwd_workspace_size() bytes, caller-owned;
  *                   it holds the weights and score gradients of every unit (2 B H U T^2
  *                   floats) and per-row bucket sums
- * Computed in float32 with per-element kernels (not a fused pass).  The table
+ * A sequence of kernels (not a fused pass) with float32 results.  For bf16 inputs with
+ * head dim 32 or 64 the dense products run on the matrix cores with float32
+ * accumulation; dL, P and the bucket sums enter them split into two bf16 parts (about
+ * 16 bits kept).  fp32 inputs and head dim 16 are computed in float32 throughout.  The table
  * gradients are summed over units in a fixed order when the per-unit partial sums fit
  * in the workspace's weight region (B H U nb (terms x d + 1) <= B H U T^2 floats), and
  * with float atomics otherwise, when their last bits can vary from call to call.

@@ -1,4 +1,4 @@
-// Backward pass of the 2D relative-position attention forward, in float32,
+// Backward pass of the 2D relative-position attention forward (float32 results),
 // written directly from the gradient of the per-pair definition (iRPE summary
 // page, "Rethinking and Improving Relative Position Encoding for Vision
 // Transformer", Method, eqs. 13-17; Swin relative-bias record, "The claim").
@@ -7,8 +7,10 @@
 //   dq_i  = s sum_j dL_ij (k_j + [K] rK[b]),  dk_j = s sum_i dL_ij (q_i + [Q] rQ[b])
 //   dv_j  = sum_i P_ij dO_i
 //   drK[b] = s sum dL_ij q_i,  drQ[b] = s sum dL_ij k_j,  drV[b] = sum P_ij dO_i,  dB[b] = sum dL_ij
-// Per-element kernels (threads take a few outputs each to reuse their loads).
-// P and dL of every unit live in the caller's workspace, with the per-row
+// Dense products run on the matrix cores for bf16 inputs of head dim 32 / 64
+// (the *_mfma kernels); the per-element kernels (threads take a few outputs each
+// to reuse their loads) serve the rest.  P and dL of every unit live in the
+// caller's workspace, with the per-row
 // bucket sums W (sum_j dL_ij, sum_i dL_ij and sum_j P_ij per bucket) that turn
 // the table terms into small contractions; before the row pass the same
 // buffers hold the per-row bucket scores q_i . rK[b], k_j . rQ[b], dO_i . rV[b].
