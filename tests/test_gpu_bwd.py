@@ -52,6 +52,12 @@ CASES = [
                                                        terms=frozenset("kqv"))),
     ("no position terms, 9x9 + cls, fp32", _D.resized(batch=1, heads=2, grid_h=9, grid_w=9, mode="none",
                                                       terms=frozenset(), map="swin", dtype="fp32")),
+    # the matrix-core kernels on windowed units with per-head tables
+    ("contextual KQV, 7x7 windows, per head, bf16 d32", _D.resized(batch=2, heads=2, head_dim=32, grid_h=14,
+                                                                   grid_w=14, window=7, prefix=0,
+                                                                   terms=frozenset("kqv"), tables_per_head=True)),
+    ("contextual K, 9x9 + 2 prefix, per head, bf16 d64", _D.resized(batch=1, heads=3, grid_h=9, grid_w=9, prefix=2,
+                                                                    tables_per_head=True)),
     # 47 x 47 = 2209 table entries: the row pass sums into global memory (more than its LDS takes)
     ("bias, one 24x24 window, fp32 d16", _S.resized(batch=1, heads=1, head_dim=16, grid_h=24, grid_w=24,
                                                      window=24, dtype="fp32")),
