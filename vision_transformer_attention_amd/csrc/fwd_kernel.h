@@ -802,6 +802,9 @@ rpe_fwd_kernel(Params p) {
 
   // One key block: logits, lazy online softmax, PV (and the value-term scatter).
   // INTERIOR: every slot is a grid key of rows < R-1 or a padding column.
+  // Kind 2 (ROWMASK): interior addressing with the row parts of the rows
+  // clamped to R-1, and the slots of whole padding rows (rows >= R) masked: a
+  // tail block when no prefix keys sit in padding columns.
   // FIRST: the first block of the stream sets the running maximum.
   // Row parts ry(yq - y) of this lane's keys 8j + 4h + i of interior block g.
   auto load_ry = [&](int g, int (&r)[4]) {
@@ -811,7 +814,9 @@ rpe_fwd_kernel(Params p) {
   // (always inlined: an outlined call would move every captured variable to scratch)
   auto process_block = [&](auto interior_c, auto first_c, auto ph_c, const char* ktile, const char* vtile,
                            int gblk, bool prefix_blk, const int (&ryv)[4]) __attribute__((always_inline)) {
-    constexpr bool INTERIOR = decltype(interior_c)::value;
+    constexpr int IKIND = static_cast<int>(decltype(interior_c)::value);
+    constexpr bool INTERIOR = IKIND != 0;
+    constexpr bool ROWMASK = IKIND == 2;
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr int PH = decltype(ph_c)::value;
     const f32x16 s = s_tile(ktile, FIRST ? f32x16{} : mneg);
@@ -828,6 +833,12 @@ rpe_fwd_kernel(Params p) {
         for (int i = 0; i < 4; ++i) {
           ab[j][i] = ryb + cxb[PH][j][i];
           x[j][i] = logit(s[4 * j + i], ab[j][i], TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0);
+        }
+        if constexpr (ROWMASK) {
+          if (((gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp) >= p.R) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[j][i] = -INFINITY;
+          }
         }
       }
     } else {
@@ -1240,7 +1251,24 @@ rpe_fwd_kernel(Params p) {
           block_query_scores(ktile_of(s));
           lds_barrier();
         }
-        if (active) process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ry_unused);
+        if (active) {
+          // (small units, several per workgroup: there the tail is half the key stream;
+          // elsewhere the extra instance costs registers for little)
+          if constexpr (MULTI && !WIDE) {
+            if (!p.prefix_in_tail) {
+              // rows past R are whole padding rows: interior addressing with clamped row parts
+              int ryc[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int yj = (gb * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
+                ryc[j] = ryt[-(yj < p.R ? yj : p.R - 1)];
+              }
+              process(std::integral_constant<int, 2>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ryc);
+              continue;
+            }
+          }
+          process(bool_c<false>{}, bool_c<false>{}, ktile_of(s), vtile_of(s), gb, false, ry_unused);
+        }
       }
     }
     // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
