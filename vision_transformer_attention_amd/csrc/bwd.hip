@@ -292,11 +292,14 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
       }
     }
     // this lane's 16 query rows: 8 j + 4 h + i (clamped), their tokens' log-sum-exp
+    // (in log2 units: P = 2^(logit log2(e) - lse log2(e)) with the hardware exp2)
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float scale2 = a.scale * kLog2e;
     float lse[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-      lse[e] = a.lse[x.bh * a.N + token_of(a, x.u, i < a.T ? i : a.T - 1)];
+      lse[e] = a.lse[x.bh * a.N + token_of(a, x.u, i < a.T ? i : a.T - 1)] * kLog2e;
     }
     for (int j0 = 0; j0 < a.T; j0 += 32) {
       const int j = j0 + r32;
@@ -313,23 +316,39 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kb, sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vb, pacc, 0, 0, 0);
       }
+      // epilogue in rounds (bucket ids, then the row scores they select, then the
+      // results), branch-free so that each round's loads are in flight together;
+      // rows and keys past T read clamped entries and are not stored
+      int bk[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
+        bk[e] = a.bmap[static_cast<int64_t>(i < a.T ? i : a.T - 1) * a.T + jr];
+      }
+      float add[16], badd[16], dvt[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
+        const int ic = i < a.T ? i : a.T - 1;
+        const int bc = bk[e] < 0 ? 0 : bk[e];
+        float r = 0.0f, u = 0.0f, bb = 0.0f;
+        if (a.rk) r += a.Wq[(ub * a.T + ic) * a.nb + bc];
+        if (a.rq) r += a.Wk[(ub * a.T + jr) * a.nb + bc];
+        if (a.rv) u = a.Wv[(ub * a.T + ic) * a.nb + bc];
+        if (a.bias) bb = a.bias[tb + bc] * kLog2e;
+        add[e] = bk[e] >= 0 ? r : 0.0f;
+        badd[e] = bk[e] >= 0 ? bb : 0.0f;
+        dvt[e] = bk[e] >= 0 ? u : 0.0f;
+      }
       if (j < a.T) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (i >= a.T) continue;
-          const int bkt = a.bmap[static_cast<int64_t>(i) * a.T + j];
-          float rho = 0.0f, dpm = pacc[e];
-          if (bkt >= 0) {
-            if (a.rk) rho += a.Wq[(ub * a.T + i) * a.nb + bkt];
-            if (a.rq) rho += a.Wk[(ub * a.T + j) * a.nb + bkt];
-            if (a.rv) dpm += a.Wv[(ub * a.T + i) * a.nb + bkt];
+          if (i < a.T) {
+            const int64_t o = (ub * a.T + i) * a.T + j;
+            a.P[o] = __builtin_amdgcn_exp2f((sacc[e] + add[e]) * scale2 + badd[e] - lse[e]);
+            a.dL[o] = pacc[e] + dvt[e];
           }
-          float logit = (sacc[e] + rho) * a.scale;
-          if (a.bias && bkt >= 0) logit += a.bias[tb + bkt];
-          const int64_t o = (ub * a.T + i) * a.T + j;
-          a.P[o] = expf(logit - lse[e]);
-          a.dL[o] = dpm;
         }
       }
     }
