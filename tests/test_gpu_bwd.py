@@ -52,6 +52,9 @@ CASES = [
                                                        terms=frozenset("kqv"))),
     ("no position terms, 9x9 + cls, fp32", _D.resized(batch=1, heads=2, grid_h=9, grid_w=9, mode="none",
                                                       terms=frozenset(), map="swin", dtype="fp32")),
+    # bf16 with head dim 16: the per-element kernels
+    ("contextual KQV, 6x7 + cls, bf16 d16", _D.resized(batch=2, heads=2, head_dim=16, grid_h=6, grid_w=7,
+                                                       terms=frozenset("kqv"))),
     # the matrix-core kernels on windowed units with per-head tables
     ("contextual KQV, 7x7 windows, per head, bf16 d32", _D.resized(batch=2, heads=2, head_dim=32, grid_h=14,
                                                                    grid_w=14, window=7, prefix=0,
