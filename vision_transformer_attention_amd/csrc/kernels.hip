@@ -136,15 +136,17 @@ __global__ void __launch_bounds__(256) undirected_to_product_kernel(const T* __r
     __syncthreads();
   }
   const int Sp = 2 * Hp + 1;
-  const int64_t per_table = static_cast<int64_t>(Sp) * Sp * width;
+  const int64_t per_table = static_cast<int64_t>(Sp) * Sp;   // cells of one expanded table
   const int S = 2 * half + 1;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+  // one thread per (table, cell): the index of the cell's offset is evaluated
+  // once, then the selected row (width entries) is copied
+  const int64_t cells = total / width;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < cells;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t t = e / per_table;
-    const int64_t r = e - t * per_table;
-    const int cell = static_cast<int>(r / width), w = static_cast<int>(r - static_cast<int64_t>(cell) * width);
+    const int cell = static_cast<int>(e - t * per_table);
     const int dy = cell / Sp - Hp, dx = cell - (cell / Sp) * Sp - Hp;
-    T val = static_cast<T>(0.0f);
+    T* const dst = product + e * width;
     if (dy > -R && dy < R && dx > -C && dx < C) {
       const int k = dy * dy + dx * dx;
       int u;
@@ -159,9 +161,11 @@ __global__ void __launch_bounds__(256) undirected_to_product_kernel(const T* __r
         u = axis_index(k, RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
       }
       u = u < 0 ? 0 : (u > half ? half : u);   // in [0, H] by construction
-      val = table[t * static_cast<int64_t>(S) * width + static_cast<int64_t>(u + half) * width + w];
+      const T* const src = table + (t * static_cast<int64_t>(S) + (u + half)) * width;
+      for (int w = 0; w < width; ++w) dst[w] = src[w];
+    } else {
+      for (int w = 0; w < width; ++w) dst[w] = static_cast<T>(0.0f);
     }
-    product[e] = val;
   }
 }
 
@@ -169,7 +173,7 @@ hipError_t launch_undirected_to_product(bool bf16, bool f32, const void* table, 
                                         int Hp, int half, int map, int rounding, double alpha, double beta,
                                         double gamma, int width, int64_t total, hipStream_t stream) {
   if ((R - 1) * (R - 1) + (C - 1) * (C - 1) >= kMaxSquares) return hipErrorInvalidValue;
-  int64_t blocks = (total + 255) / 256;
+  int64_t blocks = (total / (width > 0 ? width : 1) + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
   (void)f32;
