@@ -5,13 +5,16 @@ contextual Product keys: batch 64, 14 x 14 grid + class token, 6 heads,
 d = 64, bf16, an 81 x 64 key table shared by the heads) over one batch of
 synthetic input already in HBM.  The timed steps cycle through enough input
 copies that the working set is larger than the 256 MB Infinity Cache, so
-every step reads its inputs from HBM; with --warm the same launch on one
-resident buffer set is also reported, as "warm".  The other bf16 workloads (Swin-T stage-1 windows,
-DeiT-S with query/key/value terms, the 56 x 56 high-resolution grid) are
+every step reads its inputs from HBM; the same launch on one resident buffer
+set (inputs held by the Infinity Cache) is also reported, as "warm".  The
+other bf16 workloads (Swin-T stage-1 windows, DeiT-S with query/key/value
+terms, the 56 x 56 high-resolution grid and the mode / mapping variants) are
 timed the same way and reported under "secondary".
 
 Per-launch kernel time comes from HIP events on the stream the kernel is
-launched on.  Algorithmic counts: FLOP = 4 T^2 d per unit (QK^T and PV) +
+launched on, recorded at the ends of up to 10 consecutive batches of the timed
+launches: the mean over all of them is the headline, and the median, p10 and
+p90 of the batch means are reported beside it.  Algorithmic counts: FLOP = 4 T^2 d per unit (QK^T and PV) +
 2 n K d per contextual term (n positioned tokens, K table rows); bytes = q,
 k, v read once + o written once.
 
@@ -19,10 +22,10 @@ The CPU baseline is the fp64 oracle, run in a process pool over (batch,
 head) images of the same workload before the GPU is touched.
 
 HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
-over this script with ``--copy-probe`` (a plain device copy of known size
-calibrates the counters); the figure is read from profiles/ and reported only
-while the forward kernel's sources still hash to the value it was measured
-with.
+over this script with ``--calib-probe`` (a read-only sum and a write-only fill
+of known size calibrate the two counters separately); the figure is read from
+profiles/ and reported only while the forward kernel's sources still hash to
+the value it was measured with.
 """
 
 import argparse
@@ -48,6 +51,7 @@ PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
 MALL_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 COLD_SET_BYTES = 512 << 20   # cycle through at least this much input per step sequence
+CPU_SHARE = 16               # host threads per GPU on the measurement host
 
 
 def flops_bytes(w):
@@ -103,7 +107,9 @@ def cpu_baseline(name, budget_s=20.0):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    # the host shares its CPUs among its GPUs: one GPU's share is 16 threads, whatever
+    # the affinity mask shows, so the pool never takes more than that
+    cores = max(1, min(cores, CPU_SHARE))
     n_img = w.batch * w.heads
     # about budget_s seconds of single-core oracle work, cycling over the workload's images
     n_sample = max(cores, int(budget_s / per_img))
@@ -122,8 +128,21 @@ def cpu_baseline(name, budget_s=20.0):
     return {"value": flop_sample / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} (batch, head) images of {name} (the workload has {n_img}; images repeat "
                       f"when the sample is larger), fp64 NumPy oracle, {wall:.2f} s wall on {cores} "
-                      f"processes (1 BLAS thread each)",
-            "seconds": wall}
+                      f"processes (1 BLAS thread each; at most {CPU_SHARE}, one GPU's share of the host)",
+            "cpu_model": cpu_model(), "seconds": wall}
+
+
+def cpu_model():
+    """The host CPU's model string (from /proc/cpuinfo), or the platform's name."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def measured_traffic(name):
@@ -171,8 +190,41 @@ def _prepared(w, d, o):
                            method=w.method)
 
 
+def _batched_events(launch, steps, stream, batches=10):
+    """Launch `steps` times in up to `batches` consecutive batches with a HIP event
+    on `stream` at each batch boundary.  Returns (mean ms per launch over all
+    steps, [ms per launch of each batch])."""
+    import torch
+    nb = max(1, min(batches, steps))
+    bounds = [round(steps * j / nb) for j in range(nb + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    evs[0].record(stream)
+    for j in range(nb):
+        for i in range(bounds[j], bounds[j + 1]):
+            launch(i)
+        evs[j + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[j].elapsed_time(evs[j + 1]) / (bounds[j + 1] - bounds[j]) for j in range(nb)]
+    return evs[0].elapsed_time(evs[nb]) / steps, per
+
+
+def _quantiles(per):
+    """Median, p10 and p90 (linear interpolation) of per-batch launch times, in us."""
+    import numpy as np
+    a = np.asarray(per, dtype=np.float64) * 1e3
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "batches": len(per)}
+
+
 def time_workload(name, steps, warmup, dev, cold=True):
-    """Average per-launch time (ms) over `steps` launches, HIP events on the launch stream."""
+    """Per-launch time (ms) over `steps` launches, HIP events on the launch stream.
+
+    Cold: the launches cycle through enough HBM-resident input copies that the
+    256 MB Infinity Cache cannot hold them, and the timed launches continue the
+    rotation where the warm-up stopped, so no timed launch reuses a copy the
+    warm-up has just read (with fewer steps than copies none repeats at all).
+    Warm: one resident buffer set.  Returns (mean ms, batch quantiles, wall s,
+    copies, outputs finite)."""
     import torch
     w = WORKLOADS[name]
     _, nbytes = flops_bytes(w)
@@ -184,19 +236,13 @@ def time_workload(name, steps, warmup, dev, cold=True):
     for i in range(warmup):
         calls[i % copies](sp)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(steps):
-        calls[i % copies](sp)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms, per = _batched_events(lambda i: calls[(warmup + i) % copies](sp), steps, stream)
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / steps
     ok = bool(torch.isfinite(outs[0]).all().item())
     del sets, outs, calls
     torch.cuda.empty_cache()
-    return ms, wall, copies, ok
+    return ms, _quantiles(per), wall, copies, ok
 
 
 def time_backward(name, steps, warmup, dev):
@@ -218,16 +264,11 @@ def time_backward(name, steps, warmup, dev):
     for _ in range(warmup):
         call(stream.cuda_stream)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(steps):
-        call(stream.cuda_stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms, _ = _batched_events(lambda i: call(stream.cuda_stream), steps, stream, batches=1)
     ok = all(bool(torch.isfinite(t).all().item()) for t in g.values())
     del sets, outs, g, call
     torch.cuda.empty_cache()
-    return ev0.elapsed_time(ev1) / steps, ok
+    return ms, ok
 
 
 def summarize(name, ms):
@@ -248,9 +289,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--warm-only", action="store_true", help="time one resident buffer set only")
-    ap.add_argument("--warm", action="store_true", help="also time the headline on one resident buffer set")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="after timing, run 3 plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the headline's warm timing (one resident buffer set)")
+    ap.add_argument("--calib-probe", type=int, default=0, metavar="MIB",
+                    help="after timing, run 3 read-only passes (a sum) and 3 write-only passes (a fill) "
+                         "over MIB MiB: the known bytes that calibrate the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -269,13 +312,14 @@ def main():
     pkg.load()
 
     torch.cuda.synchronize()
-    ms_cold, wall, copies, ok = time_workload(args.workload, args.steps, args.warmup, dev,
-                                              cold=not args.warm_only)
-    print(f"{args.workload}: {ms_cold * 1e3:.2f} us/launch over {copies} buffer sets, finite={ok}",
-          file=sys.stderr, flush=True)
-    ms_warm = None
-    if args.warm:
-        ms_warm, _, _, _ = time_workload(args.workload, args.steps, args.warmup, dev, cold=False)
+    ms_cold, q_cold, wall, copies, ok = time_workload(args.workload, args.steps, args.warmup, dev,
+                                                      cold=not args.warm_only)
+    print(f"{args.workload}: {ms_cold * 1e3:.2f} us/launch over {copies} buffer sets (median {q_cold['median']:.2f}, "
+          f"p10 {q_cold['p10']:.2f}, p90 {q_cold['p90']:.2f}), finite={ok}", file=sys.stderr, flush=True)
+    ms_warm = q_warm = None
+    if not args.no_warm and not args.warm_only:
+        ms_warm, q_warm, _, _, _ = time_workload(args.workload, args.steps, args.warmup, dev, cold=False)
+        print(f"{args.workload} warm: {ms_warm * 1e3:.2f} us/launch", file=sys.stderr, flush=True)
     head = summarize(args.workload, ms_cold)
     w = WORKLOADS[args.workload]
     secondary = {}
@@ -283,11 +327,12 @@ def main():
         for name in SECONDARY:
             if name == args.workload:
                 continue
-            mc, _, _, okc = time_workload(name, args.steps, args.warmup, dev, cold=True)
-            mw, _, _, _ = time_workload(name, args.steps, args.warmup, dev, cold=False)
+            mc, qc, _, _, okc = time_workload(name, args.steps, args.warmup, dev, cold=True)
+            mw, _, _, _, _ = time_workload(name, args.steps, args.warmup, dev, cold=False)
             s = summarize(name, mc)
             sw = summarize(name, mw)
             secondary[name] = {"description": WORKLOADS[name].description, "us_per_launch": mc * 1e3,
+                               "us_median": qc["median"], "us_p10": qc["p10"], "us_p90": qc["p90"],
                                "tflops": s["tflops"], "mfma_frac": s["mfma_frac"], "gbs": s["gbs"],
                                "hbm_frac": s["hbm_frac"], "warm_us_per_launch": mw * 1e3,
                                "warm_tflops": sw["tflops"], "warm_mfma_frac": sw["mfma_frac"],
@@ -301,15 +346,19 @@ def main():
                     "tflops": 2.5 * fb / (mb * 1e-3) / 1e12, "finite": okb,
                     "note": "kernel sequence over a workspace (matrix-core products for bf16); TFLOP/s counts 2.5x the forward's FLOP"}
         print(f"backward {args.workload}: {mb * 1e3:.1f} us per call", file=sys.stderr, flush=True)
-    if args.copy_probe > 0:
-        n = args.copy_probe << 20
-        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
+    if args.calib_probe > 0:
+        # known bytes: a sum reads the whole tensor (and writes a few partials), a fill
+        # writes it (and reads nothing)
+        n = args.calib_probe << 20
+        buf = torch.ones(n // 4, dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         for _ in range(3):
-            dst.copy_(src)
+            buf.sum()
         torch.cuda.synchronize()
-        del src, dst
+        for _ in range(3):
+            buf.fill_(2.0)
+        torch.cuda.synchronize()
+        del buf
     flop, nbytes = flops_bytes(w)
     intensity = flop / nbytes
     ridge = PEAK_MFMA_BF16 * 1e12 / (PEAK_HBM * 1e9)
@@ -347,14 +396,19 @@ def main():
         "mfma_frac": head["mfma_frac"],
         "roofline": roof,
         "us_per_launch": ms_cold * 1e3,
+        "us_per_launch_quantiles": dict(q_cold, note=f"per-launch means of {q_cold['batches']} consecutive "
+                                                     "batches of the timed launches (HIP events at batch ends)"),
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
         "secondary": secondary,
         "backward": backward,
     }
     if ms_warm is not None:
         warm = summarize(args.workload, ms_warm)
-        line["warm"] = {"us_per_launch": ms_warm * 1e3, "tflops": warm["tflops"],
-                        "mfma_frac": warm["mfma_frac"], "gbs": warm["gbs"]}
+        line["warm"] = {"us_per_launch": ms_warm * 1e3, "us_median": q_warm["median"], "us_p10": q_warm["p10"],
+                        "us_p90": q_warm["p90"], "tflops": warm["tflops"], "mfma_frac": warm["mfma_frac"],
+                        "gbs": warm["gbs"], "hbm_frac": warm["hbm_frac"],
+                        "note": "one resident buffer set (inputs stay in the 256 MB Infinity Cache); "
+                                "value above is the cold rate"}
     print(json.dumps(line), flush=True)
 
 

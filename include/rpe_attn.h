@@ -37,13 +37,27 @@
  * M x M window of the grid is its own unit (Swin relative-bias record,
  * Conditions), and prefix_tokens must be 0.
  *
+ * Cross mapping (desc.method = RPE_METHOD_CROSS; iRPE page, Method, Cross,
+ * eqs. 22-24): the encoding of a pair is the sum of a row-offset entry and a
+ * column-offset entry, table[g(dy)+H] + table[S + g(dx)+H]; tables then have 2S
+ * rows (row-offset half first).  The kernels never form summed entries: each
+ * product with a table row (q.r, k.r, the weighted sum of r) is taken with both
+ * rows and added in float32.
+ *
  * Memory layout (all device pointers, caller-owned, 16-byte aligned):
- *   q, k, v, o : [batch][heads][N][head_dim], N = prefix_tokens + grid_h*grid_w,
- *                grid tokens row-major, contiguous, dtype = desc.dtype
- *   lse        : [batch][heads][N] float32 natural-log sum-exp of the logits (nullable)
- *   bias       : [heads or 1][S*S] float32 (bias mode)
- *   rq, rk, rv : [heads or 1][S*S][head_dim], dtype = desc.dtype (contextual mode)
- *   "heads or 1": tables_per_head = 1 -> one table per head, 0 -> shared.
+ *   q, k, v    : [batch][heads][N][head_dim] views, N = prefix_tokens + grid_h*grid_w,
+ *                grid tokens row-major, head_dim contiguous, dtype = desc.dtype; element
+ *                strides (stride_b, stride_h, stride_n), shared by the three (all zero:
+ *                contiguous), so that e.g. q, k, v can be the three slices of one fused
+ *                [batch][N][3][heads][head_dim] projection without a copy
+ *   o          : the same shape with its own strides (o_stride_*; all zero: contiguous);
+ *                o must not overlap q, k or v, and distinct (b, h, n) must not share an o row
+ *   lse        : [batch][heads][N] float32 natural-log sum-exp of the logits, contiguous (nullable)
+ *   bias       : [heads or 1][rows] float32 (bias mode)
+ *   rq, rk, rv : [heads or 1][rows][head_dim], dtype = desc.dtype (contextual mode)
+ *   rows = S*S (Product), 2S (Cross), S (undirected maps, see below).
+ *   "heads or 1": tables_per_head = 1 -> one table per head, table_head_stride
+ *   elements apart (0: packed), 0 -> one table shared by all heads.
  *
  * Errors: every entry point validates its arguments first and returns a
  * negative rpe_status without touching the device when they are invalid.
@@ -71,7 +85,9 @@ typedef enum rpe_status {
   RPE_E_BUCKETS = -6,         /* bucket table too large for the kernel's LDS plan  */
   RPE_E_PARAMS = -7,          /* alpha, beta, gamma or scale invalid               */
   RPE_E_UNSUPPORTED = -8,     /* valid but not built (e.g. head_dim)               */
-  RPE_E_HIP = -9              /* HIP launch error                                  */
+  RPE_E_HIP = -9,             /* HIP launch error                                  */
+  RPE_E_ALIGN = -10           /* a pointer or stride breaks the 16-byte alignment
+                                 of the vector loads                               */
 } rpe_status;
 
 enum { RPE_BF16 = 0, RPE_FP32 = 1 };
@@ -96,6 +112,10 @@ enum {
   RPE_MAP_QUANTIZED_SQUARED = 5
 };
 enum { RPE_ROUND_CAPPED = 0, RPE_ROUND_TRUNC = 1 };
+/* How the two per-axis indices of a pair select table rows (directed maps only):
+ * PRODUCT - one row per index pair, (g(dy)+H)*S + g(dx)+H of S*S (iRPE page, eq. 25);
+ * CROSS   - the sum of row g(dy)+H and row S + g(dx)+H of 2S (eqs. 22-24). */
+enum { RPE_METHOD_PRODUCT = 0, RPE_METHOD_CROSS = 1 };
 enum { RPE_TABLE_BIAS = 0, RPE_TABLE_VECTOR = 1 };   /* rpe_attn_cross_to_product */
 
 typedef struct rpe_attn_desc {
@@ -113,14 +133,26 @@ typedef struct rpe_attn_desc {
   double alpha, beta, gamma;/* piecewise map: alpha > 0, gamma > alpha, beta >= alpha */
   float scale;              /* logit scale s; 0 -> 1/sqrt(head_dim)                  */
   int32_t tables_per_head;  /* 0: one table shared by all heads; 1: one per head     */
+  int32_t method;           /* RPE_METHOD_PRODUCT or RPE_METHOD_CROSS                */
+  int64_t table_head_stride;/* elements between the heads' tables (tables_per_head = 1);
+                               0: packed (the table size); else >= the table size     */
+  int64_t stride_b, stride_h, stride_n;       /* elements, q / k / v; all 0: contiguous */
+  int64_t o_stride_b, o_stride_h, o_stride_n; /* elements, o; all 0: contiguous         */
 } rpe_attn_desc;
+/* Strides: either all three of a set are 0 (contiguous [B][H][N][d]) or all are
+ * positive with stride_n >= head_dim; each stride times the element size must be
+ * a multiple of 16 bytes (RPE_E_ALIGN), one (batch, head) slice must span less
+ * than 2^31 bytes, ((N-1) * stride_n + head_dim) * element size, and a token row
+ * stride less than 2^24 bytes (RPE_E_SHAPE).
+ * rpe_attn_fwd takes any strides; rpe_attn_bwd takes contiguous tensors only
+ * (RPE_E_UNSUPPORTED otherwise). */
 
 /* Checks a descriptor; no device access. */
 rpe_status rpe_attn_validate(const rpe_attn_desc* desc);
 
 /* Table geometry of a descriptor: half-width H, S = 2H+1 entries per axis and
- * S*S table rows (S rows for an undirected map).  Host only; any output pointer
- * may be NULL. */
+ * the table rows: S*S (Product), 2S (Cross) or S (undirected map).  Host only;
+ * any output pointer may be NULL. */
 rpe_status rpe_attn_num_buckets(const rpe_attn_desc* desc, int32_t* half_width,
                                 int32_t* per_axis, int32_t* total);
 
@@ -137,16 +169,18 @@ rpe_status rpe_attn_axis_index(const rpe_attn_desc* desc, int32_t length, int16_
 /* Bucket id of every ordered pair of one unit, [T][T] int16 row-major (query
  * rows, key columns), -1 where a prefix token takes part, written to device
  * memory by a kernel on `stream`.  All units of a descriptor share this map
- * (bucket ids depend only on offsets: Swin 2D RPE post, section 2.2).
- * Requires T*T <= 2^31 - 1. */
+ * (bucket ids depend only on offsets: Swin 2D RPE post, section 2.2).  The id
+ * is the Product id (g(dy)+H)*S + g(dx)+H for either method (under Cross it
+ * names the two rows, by id / S and S + id % S).  Requires T*T <= 2^31 - 1. */
 rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void* stream);
 
 /* Cross mapping (iRPE page, Method, "Cross", eqs. 22-24): the encoding of a
  * pair is the sum of a row-offset entry and a column-offset entry.  That is
  * the Product mapping of the same index function with the table
  *     product[by * S + bx] = cross[by] + cross[S + bx]      (by = g(dy)+H, bx = g(dx)+H)
- * so a Cross table runs through rpe_attn_fwd after this conversion, with the
- * same descriptor.
+ * This writes that table (for callers that want Product tables; rpe_attn_fwd
+ * takes Cross tables directly with desc.method = RPE_METHOD_CROSS and then
+ * rounds no sum).  The descriptor may name either method.
  *   cross   : device, [tables][2*S][width]: rows [0, S) hold the row-offset
  *             encodings, rows [S, 2S) the column-offset encodings
  *   product : device, [tables][S*S][width], written (caller-owned; must not
@@ -177,11 +211,17 @@ rpe_status rpe_attn_cross_to_product(const rpe_attn_desc* desc, int32_t kind, co
 rpe_status rpe_attn_undirected_to_product(const rpe_attn_desc* desc, int32_t kind, const void* table,
                                           void* product, void* stream);
 
-/* The attention forward (maps RPE_MAP_SWIN and RPE_MAP_PIECEWISE; RPE_E_MODE for
- * an undirected map).  q, k, v, o required (may be NULL when batch == 0, which
- * launches nothing); bias required in bias mode;
+/* The attention forward (maps RPE_MAP_SWIN and RPE_MAP_PIECEWISE, either method;
+ * RPE_E_MODE for an undirected map).  q, k, v, o required (may be NULL when
+ * batch == 0, which launches nothing); bias required in bias mode;
  * rk / rq / rv required for the contextual terms requested (others ignored);
- * lse nullable.  o must not alias q, k or v.  Asynchronous on `stream`. */
+ * lse nullable.  o must not alias q, k or v.  Asynchronous on `stream`.
+ * Precision: bf16 inputs are multiplied on the matrix cores with float32
+ * accumulation; the softmax weights enter the PV product rounded to bf16.  For
+ * bf16 inputs the key term's per-row bucket scores s * log2(e) * q.rK[b] are
+ * kept as fp16 and clamped to [-65000, 65000] before they are stored: a score
+ * beyond that range saturates (no error is reported).  The query term's scores
+ * stay float32.  With N(0,1) activations and tables the scores are O(sqrt(d)). */
 rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k, const void* v,
                         const float* bias, const void* rq, const void* rk, const void* rv,
                         void* o, float* lse, void* stream);

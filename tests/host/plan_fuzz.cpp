@@ -46,6 +46,7 @@ int main(int argc, char** argv) {
     d.gamma = d.alpha + F(-1.0, 60.0);
     d.scale = U(0, 5) == 0 ? 0.0f : static_cast<float>(F(-2.0, 2.0));
     d.tables_per_head = U(-1, 2);
+    d.method = U(-1, 2);
     if (valid_ish) {
       d.batch = U(0, 8);
       d.heads = U(1, 8);
@@ -59,6 +60,8 @@ int main(int argc, char** argv) {
       d.beta = d.alpha + F(0.0, 8.0);
       d.gamma = d.alpha + F(0.1, 60.0);
       d.tables_per_head = U(0, 1);
+      d.method = U(0, 3) == 0 ? RPE_METHOD_CROSS : RPE_METHOD_PRODUCT;
+      if (d.method == RPE_METHOD_CROSS && d.mode == RPE_MODE_NONE) d.mode = RPE_MODE_BIAS;
       if (U(0, 1)) {
         const int m = U(1, 9);
         d.window = m;
@@ -72,9 +75,23 @@ int main(int argc, char** argv) {
         d.prefix_tokens = U(0, 3) == 0 ? U(0, 16) : U(0, 1);
       }
     }
+    // strides: contiguous, a fused-projection view, or random (sometimes misaligned)
+    {
+      const int64_t N = d.prefix_tokens + static_cast<int64_t>(d.grid_h) * d.grid_w;
+      const int kind = U(0, 5);
+      if (kind == 1) {   // q, k, v as slices of [B][N][3][H][d]; o as [B][N][H][d]
+        d.stride_n = 3LL * d.heads * d.head_dim; d.stride_h = d.head_dim; d.stride_b = N * d.stride_n;
+        d.o_stride_n = static_cast<int64_t>(d.heads) * d.head_dim; d.o_stride_h = d.head_dim;
+        d.o_stride_b = N * d.o_stride_n;
+      } else if (kind == 2) {
+        d.stride_n = d.head_dim + U(-1, 9); d.stride_h = U(0, 5000); d.stride_b = U(0, 90000);
+        d.o_stride_n = d.head_dim * U(1, 3); d.o_stride_h = U(1, 5000); d.o_stride_b = U(1, 90000);
+      }
+      if (U(0, 9) == 0) d.table_head_stride = U(-1, 40000);
+    }
     rpe::Params p;
     const int st = rpe::make_plan(&d, &p);
-    REQUIRE(st <= 0 && st >= -9);
+    REQUIRE(st <= 0 && st >= -10);
     REQUIRE(rpe::validate(&d) == RPE_OK || st == rpe::validate(&d));
     if (st != RPE_OK) continue;
     ++accepted;
@@ -87,7 +104,32 @@ int main(int argc, char** argv) {
     REQUIRE(p.off_stage == 0);
     REQUIRE(p.off_rq >= p.stages * 2 * rpe::kBlockSlots * p.D * p.elem_bytes && p.off_rq % 16 == 0);
     REQUIRE(p.off_rq <= p.off_tab);
-    if (tq) REQUIRE(p.off_rq + p.nbt * rpe::kRowTile * p.kpitch * p.elem_bytes <= p.off_tab);
+    if (tq) REQUIRE(p.off_rq + p.nrq * p.kpitch * p.elem_bytes <= p.off_rkc);
+    REQUIRE(p.off_rkc >= p.off_rq && p.off_rkc % 16 == 0 && p.off_bx >= p.off_rkc && p.off_bx % 16 == 0);
+    REQUIRE(p.off_tab >= p.off_bx);
+    // Cross: 2S table rows (the staged query-term table holds exactly those), the key
+    // term's tiles of them, the bias's 2S entries; Product: S*S rows
+    if (p.cross) {
+      REQUIRE(d.method == RPE_METHOD_CROSS && d.mode != RPE_MODE_NONE && p.ntr == 2 * p.S);
+      if (tq) REQUIRE(p.nrq == 2 * p.S);
+      if (ctx && (d.terms & RPE_TERM_K))
+        REQUIRE(p.off_bx >= p.off_rkc + (2 * p.S + 31) / 32 * 32 * p.D * p.elem_bytes);
+      if (d.mode == RPE_MODE_BIAS) REQUIRE(p.off_tab >= p.off_bx + 2 * p.S * 4);
+      REQUIRE(!p.rk_lds);
+    } else {
+      REQUIRE(p.ntr == (d.mode == RPE_MODE_NONE ? 1 : p.nb));
+      if (tq) REQUIRE(p.nrq == p.nbt * rpe::kRowTile);
+    }
+    // strides: every (batch, head) slice spans less than 2^31 bytes and rows are 16-byte aligned
+    {
+      const int64_t eb = p.elem_bytes;
+      REQUIRE(p.sn >= p.D && p.osn >= p.D && p.sb > 0 && p.sh > 0 && p.osb > 0 && p.osh > 0);
+      REQUIRE(((p.N - 1) * p.sn + p.D) * eb < (int64_t{1} << 31) && ((p.N - 1) * p.osn + p.D) * eb < (int64_t{1} << 31));
+      REQUIRE((p.sn * eb) % 16 == 0 && (p.osn * eb) % 16 == 0 && (p.sb * eb) % 16 == 0 && (p.sh * eb) % 16 == 0);
+      REQUIRE(static_cast<int64_t>(p.rbi) == p.sn * eb && p.sn * eb < (1 << 24) && p.osn * eb < (1 << 24));
+      if (d.stride_b == 0 && d.stride_h == 0 && d.stride_n == 0)
+        REQUIRE(p.sn == p.D && p.sh == static_cast<int64_t>(p.N) * p.D && p.sb == p.sh * p.H);
+    }
     // per-row scores: nb entries in rows of an odd number of words
     REQUIRE(p.p_tab >= p.nb && (p.p_tab * p.gsz) % 4 == 0 && ((p.p_tab * p.gsz / 4) & 1));
     // the thresholds reproduce g on every offset of the unit

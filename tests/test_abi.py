@@ -44,7 +44,7 @@ def _w_desc(w, **over):
     kw = dict(batch=w.batch, heads=w.heads, head_dim=w.head_dim, grid=(w.grid_h, w.grid_w),
               window=w.window, prefix_tokens=w.prefix, dtype=w.dtype, mode=w.mode,
               terms="".join(sorted(w.terms)), map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma,
-              rounding=w.reading, tables_per_head=w.tables_per_head)
+              rounding=w.reading, tables_per_head=w.tables_per_head, method=w.method)
     kw.update(over)
     return pkg.make_desc(**kw)
 
@@ -57,8 +57,8 @@ def test_workload_geometry_matches_oracle(name):
     assert pkg.rpe_attn_validate(d) == 0
     spec = Spec(w.grid_h, w.grid_w, window=w.window, prefix=w.prefix, mode=w.mode, terms=w.terms,
                 map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma, reading=w.reading, method=w.method)
-    h, s, rows = pkg.rpe_attn_num_buckets(d)        # the library's (Product) geometry
-    assert num_buckets(spec) == (h, s, 2 * s if w.method == "cross" else rows)
+    h, s, rows = pkg.rpe_attn_num_buckets(d)        # table rows: S*S, or 2S under Cross
+    assert num_buckets(spec) == (h, s, rows)
     assert num_buckets(spec)[2] == w.table_rows
     n, t, u = pkg.rpe_attn_unit_size(d)
     assert (n, t, u) == (spec.tokens_per_image, spec.unit_tokens, spec.units_per_image)
@@ -203,3 +203,64 @@ def test_bwd_rejects_before_device():
     # workspace too small
     assert lib.rpe_attn_bwd(ctypes.byref(d), *args, one, ctypes.c_uint64(n.value - 1), None) == -2
     assert lib.rpe_attn_bwd(None, *args, one, ctypes.c_uint64(n.value), None) == -1
+
+
+def test_descriptor_layout():
+    # the ctypes mirror matches the C struct: 12 int32 fields, three doubles, the
+    # scale, tables_per_head, method, then seven int64 fields (8-byte aligned)
+    assert ctypes.sizeof(_lib.Desc) == 48 + 24 + 4 + 4 + 4 + 4 + 7 * 8
+    assert _lib.Desc.table_head_stride.offset == 88 and _lib.Desc.o_stride_n.offset == 136
+
+
+STRIDE_BAD = [
+    # (strides, o_strides, code): all-zero or all-positive, stride_n >= head_dim, 16-byte rows
+    ((1, 0, 0), None, -2), ((0, 0, 32), None, -2), ((6000, 200, 16), None, -2),
+    ((6000, 200, 36), None, -10), (None, (6000, 200, 36), -10), ((6004, 200, 32), None, -10),
+    ((1 << 40, 32, 1 << 30), None, -2),
+]
+
+
+@pytest.mark.parametrize("strides,o_strides,code", STRIDE_BAD)
+def test_stride_validation(strides, o_strides, code):
+    _lib_or_skip()
+    d = pkg.make_desc(batch=2, heads=2, head_dim=32, grid=(8, 8), dtype="bf16", mode="none",
+                      strides=strides, o_strides=o_strides)
+    assert pkg.rpe_attn_validate(d) == code
+
+
+def test_stride_views_accepted():
+    _lib_or_skip()
+    B, N, H, d = 2, 65, 3, 64
+    # q, k, v as slices of a fused [B][N][3][H][d] projection, o as [B][N][H][d]
+    fused = dict(strides=(N * 3 * H * d, d, 3 * H * d), o_strides=(N * H * d, d, H * d))
+    desc = pkg.make_desc(batch=B, heads=H, head_dim=d, grid=(8, 8), prefix_tokens=1, mode="contextual",
+                         terms="k", map="piecewise", alpha=1.9, beta=3.8, gamma=15.2, **fused)
+    assert pkg.rpe_attn_validate(desc) == 0
+
+
+def test_method_validation_and_geometry():
+    lib = _lib_or_skip()
+    one = ctypes.c_void_p(16)
+    kw = dict(batch=1, heads=2, head_dim=64, grid=(14, 14), prefix_tokens=1, alpha=1.9, beta=3.8, gamma=15.2)
+    cross = pkg.make_desc(mode="contextual", terms="k", map="piecewise", method="cross", **kw)
+    assert pkg.rpe_attn_validate(cross) == 0
+    assert pkg.rpe_attn_num_buckets(cross) == (4, 9, 18)
+    # the Cross mapping needs a table and a directed map
+    assert pkg.rpe_attn_validate(pkg.make_desc(mode="none", method="cross", **kw)) == -4
+    assert pkg.rpe_attn_validate(pkg.make_desc(mode="bias", map="euclidean", method="cross", **kw)) == -4
+    assert pkg.rpe_attn_validate(pkg.make_desc(mode="bias", map="piecewise", method=2, **kw)) == -4
+    # the backward takes the Product method and contiguous tensors only
+    n = ctypes.c_uint64()
+    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(cross), ctypes.byref(n)) == -4
+    strided = pkg.make_desc(mode="contextual", terms="k", map="piecewise",
+                            strides=(197 * 3 * 2 * 64, 64, 3 * 2 * 64), **kw)
+    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(strided), ctypes.byref(n)) == -8
+    # misaligned pointers and too-small table head strides are refused before any launch
+    d = pkg.make_desc(mode="contextual", terms="k", map="piecewise", **kw)
+    odd = ctypes.c_void_p(18)
+    assert lib.rpe_attn_fwd(ctypes.byref(d), odd, one, one, None, None, one, None, one, None, None) == -10
+    assert lib.rpe_attn_fwd(ctypes.byref(d), one, one, one, None, None, odd, None, one, None, None) == -10
+    ph = pkg.make_desc(mode="contextual", terms="k", map="piecewise", tables_per_head=True,
+                       table_head_stride=81 * 64 - 8, **kw)
+    assert lib.rpe_attn_fwd(ctypes.byref(ph), one, one, one, None, None, one, None, one, None, None) == -2
+    assert lib.rpe_status_str(-10).decode().startswith("a pointer or stride")

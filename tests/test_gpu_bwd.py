@@ -64,6 +64,14 @@ CASES = [
     # 47 x 47 = 2209 table entries: the row pass sums into global memory (more than its LDS takes)
     ("bias, one 24x24 window, fp32 d16", _S.resized(batch=1, heads=1, head_dim=16, grid_h=24, grid_w=24,
                                                      window=24, dtype="fp32")),
+    # 289 buckets with the query term: the key-column bucket sums take the global-memory
+    # kernel (more than 256 buckets), in fp32 and on the bf16 matrix-core path
+    ("contextual Q, 289 buckets, 9x9 + cls, fp32 d16", _D.resized(batch=1, heads=2, head_dim=16, grid_h=9,
+                                                                   grid_w=9, terms=frozenset("q"), alpha=3.8,
+                                                                   beta=7.6, gamma=30.4, dtype="fp32")),
+    ("contextual Q, 289 buckets, 9x9 + cls, bf16 d64", _D.resized(batch=1, heads=2, grid_h=9, grid_w=9,
+                                                                   terms=frozenset("q"), alpha=3.8, beta=7.6,
+                                                                   gamma=30.4)),
 ]
 
 
@@ -105,3 +113,33 @@ def test_backward_rejects_undirected_map(dev):
                       beta=2.0, gamma=4.0)
     n = ctypes.c_uint64()
     assert pkg.load().rpe_attn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -4
+
+
+def test_backward_binding_rejects_mismatched_inputs(dev):
+    # The C entry point sizes every read and write from the descriptor, so the
+    # binding refuses a grid that does not match q and tables of the wrong
+    # shape, dtype or device before any launch.
+    import torch
+    import vision_transformer_attention_amd as pkg
+    w = _fit(_D.resized(batch=1, heads=2, terms=frozenset("kv")))
+    x = make_inputs(w, seed=9960)
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(dev) for n, a in x.items()}
+    kw = dict(grid=(w.grid_h, w.grid_w), prefix_tokens=w.prefix, mode="contextual", terms="kv", map=w.map,
+              alpha=w.alpha, beta=w.beta, gamma=w.gamma, rk=t["rk"], rv=t["rv"])
+    _, lse = pkg.rpe_attn_fwd(t["q"], t["k"], t["v"], return_lse=True, **kw)
+    dout = torch.ones_like(t["q"])
+    print("[case] backward binding rejects a grid without its class token", flush=True)
+    with pytest.raises(ValueError):
+        pkg.rpe_attn_bwd(t["q"], t["k"], t["v"], dout, lse, **dict(kw, prefix_tokens=0))
+    print("[case] backward binding rejects tables of the wrong shape / dtype / missing", flush=True)
+    with pytest.raises(ValueError):
+        pkg.rpe_attn_bwd(t["q"], t["k"], t["v"], dout, lse, **dict(kw, rk=t["rk"][:, :-1]))
+    with pytest.raises(ValueError):
+        pkg.rpe_attn_bwd(t["q"], t["k"], t["v"], dout, lse, **dict(kw, rv=t["rv"].float()))
+    with pytest.raises(ValueError):
+        pkg.rpe_attn_bwd(t["q"], t["k"], t["v"], dout, lse, **dict(kw, rk=None))
+    with pytest.raises(ValueError):
+        pkg.rpe_attn_bwd(t["q"], t["k"], t["v"], dout, lse, **dict(kw, rk=t["rk"].cpu()))
+    with pytest.raises(ValueError):
+        pkg.rpe_attn_bwd(t["q"].cpu(), t["k"], t["v"], dout, lse, **kw)
+    torch.cuda.synchronize()

@@ -46,7 +46,7 @@ def desc_of(w):
     return pkg.make_desc(batch=w.batch, heads=w.heads, head_dim=w.head_dim, grid=(w.grid_h, w.grid_w),
                          window=w.window, prefix_tokens=w.prefix, dtype=w.dtype, mode=w.mode,
                          terms="".join(sorted(w.terms)), map=w.map, alpha=w.alpha, beta=w.beta,
-                         gamma=w.gamma, rounding=w.reading, tables_per_head=w.tables_per_head)
+                         gamma=w.gamma, rounding=w.reading, tables_per_head=w.tables_per_head, method=w.method)
 
 
 def fit(w):
@@ -88,6 +88,9 @@ def compare(w, x, dev, tol=None, scale=None, **sel):
     assert err <= tol, err
     assert lerr <= tol, lerr
     return err
+
+
+_QKV_DET = WORKLOADS["deit_s_irpe_qkv"]
 
 
 # ------------------------------------------------------------------------------ index + map
@@ -331,51 +334,90 @@ CROSS_CASES = [
     ("cross contextual K, global 14x14 + cls", _D.resized(batch=2, heads=2, method="cross")),
     ("cross contextual KQV, global 14x14 + cls", _D.resized(batch=2, heads=2, terms=frozenset("kqv"),
                                                             method="cross")),
+    ("cross contextual QV, 9x13 no cls, per-head tables, d32",
+     _D.resized(batch=2, heads=3, head_dim=32, grid_h=9, grid_w=13, prefix=0, terms=frozenset("qv"),
+                tables_per_head=True, method="cross")),
+    ("cross contextual KQV, rows of 4 (per-bucket value sums), 11x3 + 2 prefix",
+     _D.resized(batch=2, heads=2, grid_h=11, grid_w=3, prefix=2, terms=frozenset("kqv"), method="cross")),
     ("cross contextual QKV fp32 d16, 7x7 windows",
      _D.resized(batch=2, heads=2, head_dim=16, grid_h=14, grid_w=14, window=7, prefix=0, terms=frozenset("kqv"),
                 dtype="fp32", method="cross")),
     ("cross contextual K, wide 10x40 grid", WORKLOADS["highres_irpe_k"].resized(batch=1, heads=2, grid_h=10,
                                                                                grid_w=40, method="cross")),
+    ("cross contextual KV, wide 6x61 grid + cls", _D.resized(batch=1, heads=2, grid_h=6, grid_w=61,
+                                                             terms=frozenset("kv"), method="cross")),
+    ("cross contextual K, 17 per axis (beta 7.6), 24x24 grid",
+     WORKLOADS["highres_irpe_k"].resized(batch=1, heads=2, grid_h=24, grid_w=24, method="cross")),
+    ("cross contextual KQV, trunc reading", _D.resized(batch=1, heads=2, terms=frozenset("kqv"), reading="trunc",
+                                                       method="cross")),
 ]
-
-
-def _cross_as_product(w, x):
-    """The Product workload and tables the conversion defines: entry by*S + bx is
-    the float32 sum of the two halves' rows, rounded once to the table dtype."""
-    _, s, _ = num_buckets(spec_of(w))
-    nb = s * s
-    by, bx = np.arange(nb) // s, s + np.arange(nb) % s
-    px = dict(x)
-    for n in ("bias", "rq", "rk", "rv"):
-        if n in x:
-            t = x[n].astype(np.float32)
-            px[n] = round_to_dtype((t[:, by] + t[:, bx]).astype(np.float64), "fp32" if n == "bias" else w.dtype)
-    return w.resized(method="product", table_rows=nb), px
 
 
 @pytest.mark.parametrize("label,w", CROSS_CASES)
 def test_cross_mapping(dev, label, w):
-    # The GPU path is held to the usual tolerance against the oracle's Product mapping
-    # on the converted tables (the conversion itself is exact: test_cross_to_product_exact);
-    # the oracle's Cross mapping on the unrounded tables differs from that only by the
-    # one rounding of each summed entry (bf16: <= 2^-8 relative), reported here.
+    # Cross tables (2S rows) go to the forward as they are and are held to the
+    # oracle's own Cross mapping (iRPE page, Method, eqs. 22-24: the sum of a
+    # row-offset and a column-offset encoding per pair) at the usual tolerance.
     w = fit(w)
     say("cross", label, w.qkv_shape, "table rows", w.table_rows)
-    x = make_inputs(w, sigma=1.0, seed=9700)
-    pw, px = _cross_as_product(w, x)
-    go, gl = run_gpu(w, x, dev)
-    ro, rl = run_oracle(pw, px)
-    co, cl = run_oracle(w, x)
-    assert np.isfinite(go).all()
-    err = float(np.abs(go - ro).max())
-    lerr = float(np.abs(gl - rl).max())
-    rnd = float(np.abs(ro - co).max())
-    tol = TOL[w.dtype]
-    print(f"    max|o - oracle(product of converted tables)| = {err:.3e}  lse {lerr:.3e}  (tol {tol});"
-          f" table rounding moves the oracle by {rnd:.3e}", flush=True)
-    assert err <= tol and lerr <= tol, (err, lerr)
-    if w.dtype == "fp32":
-        assert rnd <= 1e-5
+    compare(w, make_inputs(w, sigma=1.0, seed=9700), dev)
+
+
+def test_cross_full_size(dev):
+    # the DeiT-S Cross workload at full size, sigma = 1 tables, sampled (b, h)
+    w = WORKLOADS["deit_s_irpe_k_cross"].resized(terms=frozenset("kqv"))
+    say("cross full size KQV", w.qkv_shape, "sampled (b, h): [5, 60], [1, 4]")
+    compare(w, make_inputs(w, sigma=1.0), dev, batch_sel=[5, 60], heads_sel=[1, 4])
+
+
+# Strided views: q, k, v as the three slices of one fused [B, N, 3, H, d]
+# projection and o written into a [B, N, H, d] tensor, with no copies.
+STRIDED = [
+    ("DeiT-S K, fused qkv", _D.resized(batch=2, heads=3)),
+    ("DeiT-S KQV d32, fused qkv", _D.resized(batch=2, heads=3, head_dim=32, terms=frozenset("kqv"))),
+    ("Swin W7 bias, fused qkv", WORKLOADS["swin_t_w7"].resized(batch=2, heads=3, grid_h=14, grid_w=21)),
+    ("wide 5x40 K fp32 d16, fused qkv", WORKLOADS["highres_irpe_k"].resized(batch=2, heads=2, head_dim=16,
+                                                                           grid_h=5, grid_w=40, dtype="fp32")),
+    ("4x4 windows bias fp32 d16 (several windows per workgroup)",
+     WORKLOADS["swin_tiny"].resized(batch=3, heads=4, grid_h=64, grid_w=64)),
+]
+
+
+@pytest.mark.parametrize("label,w", STRIDED)
+def test_strided_views(dev, label, w):
+    import torch
+    import vision_transformer_attention_amd as pkg
+    w = fit(w)
+    x = make_inputs(w, sigma=1.0, seed=9600)
+    say("strided", label, w.qkv_shape)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    B, H, N, d = w.qkv_shape
+    fused = torch.empty((B, N, 3, H, d), dtype=tdt)
+    for i, n in enumerate("qkv"):
+        fused[:, :, i] = torch.from_numpy(x[n]).to(tdt).permute(0, 2, 1, 3)
+    fused = fused.to(dev)
+    q, k, v = (fused[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    assert not q.is_contiguous()
+    o_buf = torch.full((B, N, H, d), float("nan"), dtype=tdt, device=dev)
+    o = o_buf.permute(0, 2, 1, 3)
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32 if n == "bias" else tdt).to(dev)
+         for n, a in x.items() if n not in "qkv"}
+    _, lse = pkg.rpe_attn_fwd(q, k, v, grid=(w.grid_h, w.grid_w), window=w.window, prefix_tokens=w.prefix,
+                              mode=w.mode, terms="".join(sorted(w.terms)), map=w.map, alpha=w.alpha, beta=w.beta,
+                              gamma=w.gamma, rounding=w.reading, bias=t.get("bias"), rq=t.get("rq"),
+                              rk=t.get("rk"), rv=t.get("rv"), out=o, return_lse=True)
+    torch.cuda.synchronize()
+    go = o.float().cpu().numpy().astype(np.float64)
+    sel = dict(batch_sel=[0, B - 1], heads_sel=[0, H - 1])
+    if w.window:
+        sel["units"] = [0, 1, 255] if w.grid_h == 64 else None
+    ro, rl = run_oracle(w, x, **sel)
+    mask = ~np.isnan(ro)
+    err = float(np.abs(go - ro)[mask].max())
+    lerr = float(np.abs(lse.cpu().numpy() - rl)[~np.isnan(rl)].max())
+    print(f"    max|o - oracle| = {err:.3e}  lse {lerr:.3e}", flush=True)
+    assert np.isfinite(go).all(), "o rows left unwritten or non-finite"
+    assert err <= TOL[w.dtype] and lerr <= TOL[w.dtype], (err, lerr)
 
 
 # Undirected maps (Euclidean, Quantization; page and code readings): the table of
@@ -526,10 +568,22 @@ def test_running_max_moves(dev, label, w, ramp):
     compare(w, x, dev)
 
 
-def test_deterministic(dev):
-    w = SMALL["deit_s_irpe_qkv"]
+DETERMINISM = [
+    ("per-column value sums, 14x14 + cls", SMALL["deit_s_irpe_qkv"]),
+    # the per-bucket layout with LDS float atomics: rows of 4 padded columns and wide rows
+    ("atomic value sums, rows of 4, 11x3 + 2 prefix", _QKV_DET.resized(batch=2, heads=2, grid_h=11, grid_w=3,
+                                                                        prefix=2)),
+    ("atomic value sums, wide rows, 3x61 + cls", _QKV_DET.resized(batch=2, heads=2, grid_h=3, grid_w=61)),
+    ("bias, several windows per workgroup", WORKLOADS["swin_t_w7"].resized(batch=8, heads=3)),
+]
+
+
+@pytest.mark.parametrize("label,w", DETERMINISM)
+def test_deterministic(dev, label, w):
+    # two calls on the same inputs give bit-identical outputs and log-sum-exps
+    w = fit(w)
     x = make_inputs(w, sigma=1.0, seed=9100)
-    say("determinism", w.qkv_shape)
+    say("determinism", label, w.qkv_shape)
     a, la = run_gpu(w, x, dev)
     b, lb = run_gpu(w, x, dev)
     assert (a == b).all() and (la == lb).all()
@@ -575,6 +629,16 @@ FULL_SAMPLES = {
     "detr_irpe_k": ([0, 7], [0, 7]),
     "deit_s_irpe_bias_euclid": ([0, 63], [0, 5]),
 }
+
+
+def test_full_size_highres_sigma1(dev):
+    # The 56 x 56 grid at full size with sigma = 1 tables, one (batch, head)
+    # checked against the oracle: offsets up to 55 reach the outermost row and
+    # column buckets (index 8 of 17, |offset| >= 29) at a scale where the key
+    # term moves the output far more than the tolerance.
+    w = WORKLOADS["highres_irpe_k"]
+    say("full size sigma 1", w.qkv_shape, "sampled (b, h): [1], [3]")
+    compare(w, make_inputs(w, sigma=1.0), dev, batch_sel=[1], heads_sel=[3])
 
 
 @pytest.mark.parametrize("name", list(FULL_SAMPLES))

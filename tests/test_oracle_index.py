@@ -196,3 +196,41 @@ def test_bad_params_rejected():
         Spec(4, 4, window=3)
     with pytest.raises(ValueError):
         Spec(4, 4, mode="bias", terms={"v"})
+
+
+@pytest.mark.parametrize("reading", [ROUND_CAPPED, ROUND_TRUNC])
+@pytest.mark.parametrize("abg", PARAMS)
+def test_step_positions_closed_form(abg, reading):
+    # Where each step of g lies, from the inverse of eq. 18 rather than from
+    # evaluating it.  The page's index grows like log(|x|/alpha)/log(gamma/alpha),
+    # scaled to reach beta at gamma, and is rounded; so beyond alpha the index
+    # reaches k exactly where the real position passes k - 1/2, i.e. at the first
+    # integer offset a > alpha with
+    #     a >= alpha * (gamma/alpha) ** ((k - 1/2 - alpha) / (beta - alpha)),
+    # for every k up to the table half-width (the cap at beta only stops the
+    # count there: capped, H = rh(beta); truncating, H = trunc(beta)).  Inside
+    # |x| <= alpha the index is the offset.  This places every step of both
+    # readings, the capped reading's last one included (offsets 11 at r = 1.9 and
+    # 29 at r = 3.8), with an exponential instead of the oracle's logarithm.
+    a, b, g = abg
+    h = half_width(a, b, g, reading)
+    thresholds = []
+    for k in range(1, h + 1):
+        if k <= math.floor(a):
+            thresholds.append(k)
+            continue
+        if b == a:
+            edge = 0.0                      # the real position is alpha everywhere beyond alpha
+        else:
+            edge = a * (g / a) ** ((k - 0.5 - a) / (b - a))
+            frac = edge - math.floor(edge)
+            assert min(frac, 1 - frac) > 1e-9, "an offset sits on a rounding edge"
+        thresholds.append(max(math.floor(a) + 1, math.ceil(edge)))
+    for x in range(0, 400):
+        want = sum(1 for t in thresholds if t <= x)
+        assert piecewise_index(x, a, b, g, reading) == want, (x, thresholds)
+        assert piecewise_index(-x, a, b, g, reading) == -want
+    if abg == (1.9, 3.8, 15.2) and reading == ROUND_CAPPED:
+        assert thresholds == [1, 2, 4, 11]
+    if abg == (3.8, 7.6, 30.4) and reading == ROUND_CAPPED:
+        assert thresholds[-1] == 29

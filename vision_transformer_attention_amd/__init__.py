@@ -1,6 +1,7 @@
 """MI355X (gfx950) forward pass of multi-head self-attention over a 2D patch
 grid with relative position encoding: Swin-style per-head bias inside M x M
-windows and iRPE contextual Product terms (key, query and value tables).
+windows and iRPE contextual terms (key, query and value tables) under the
+Product or Cross mapping.
 
 The computation lives in librpe_attn.so (HIP kernels behind the C ABI of
 include/rpe_attn.h); this package binds it with ctypes and uses PyTorch only
@@ -25,4 +26,4 @@ from .attention import (  # noqa: F401
 )
 from ._lib import RpeError, load  # noqa: F401
 
-__version__ = "0.1.0"
+__version__ = "0.2.0"

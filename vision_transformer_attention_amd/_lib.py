@@ -19,11 +19,12 @@ RPE_MAP_SWIN, RPE_MAP_PIECEWISE = 0, 1
 RPE_MAP_EUCLIDEAN, RPE_MAP_EUCLIDEAN_ROUNDED, RPE_MAP_QUANTIZED, RPE_MAP_QUANTIZED_SQUARED = 2, 3, 4, 5
 RPE_ROUND_CAPPED, RPE_ROUND_TRUNC = 0, 1
 RPE_TABLE_BIAS, RPE_TABLE_VECTOR = 0, 1
+RPE_METHOD_PRODUCT, RPE_METHOD_CROSS = 0, 1
 
 STATUS_NAMES = {
     0: "RPE_OK", -1: "RPE_E_NULL", -2: "RPE_E_SHAPE", -3: "RPE_E_DTYPE", -4: "RPE_E_MODE",
     -5: "RPE_E_BIAS_ON_VALUES", -6: "RPE_E_BUCKETS", -7: "RPE_E_PARAMS", -8: "RPE_E_UNSUPPORTED",
-    -9: "RPE_E_HIP",
+    -9: "RPE_E_HIP", -10: "RPE_E_ALIGN",
 }
 
 # Every symbol include/rpe_attn.h declares.
@@ -41,7 +42,10 @@ class Desc(ctypes.Structure):
         ("prefix_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32),
         ("terms", ctypes.c_uint32), ("map", ctypes.c_int32), ("rounding", ctypes.c_int32),
         ("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("gamma", ctypes.c_double),
-        ("scale", ctypes.c_float), ("tables_per_head", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("tables_per_head", ctypes.c_int32), ("method", ctypes.c_int32),
+        ("table_head_stride", ctypes.c_int64),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+        ("o_stride_b", ctypes.c_int64), ("o_stride_h", ctypes.c_int64), ("o_stride_n", ctypes.c_int64),
     ]
 
 

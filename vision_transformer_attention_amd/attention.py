@@ -26,10 +26,16 @@ def _torch():
     return torch
 
 
+_METHODS = {"product": _lib.RPE_METHOD_PRODUCT, "cross": _lib.RPE_METHOD_CROSS}
+
+
 def make_desc(*, batch=1, heads=1, head_dim=64, grid=(1, 1), window=0, prefix_tokens=0,
               dtype="bf16", mode="none", terms="", map="swin", alpha=0.0, beta=0.0, gamma=0.0,
-              rounding="capped", scale=None, tables_per_head=False):
-    """Build an ``rpe_attn_desc``.  ``terms`` is a string or set over 'k', 'q', 'v'."""
+              rounding="capped", scale=None, tables_per_head=False, method="product",
+              strides=None, o_strides=None, table_head_stride=0):
+    """Build an ``rpe_attn_desc``.  ``terms`` is a string or set over 'k', 'q', 'v';
+    ``strides`` / ``o_strides`` are the (batch, head, token) element strides of
+    q, k, v and of o (None: contiguous)."""
     d = Desc()
     d.batch, d.heads, d.head_dim = int(batch), int(heads), int(head_dim)
     d.grid_h, d.grid_w = int(grid[0]), int(grid[1])
@@ -45,6 +51,10 @@ def make_desc(*, batch=1, heads=1, head_dim=64, grid=(1, 1), window=0, prefix_to
     d.alpha, d.beta, d.gamma = float(alpha), float(beta), float(gamma)
     d.scale = 0.0 if scale is None else float(scale)
     d.tables_per_head = 1 if tables_per_head else 0
+    d.method = _METHODS[method] if isinstance(method, str) else int(method)
+    d.table_head_stride = int(table_head_stride)
+    d.stride_b, d.stride_h, d.stride_n = (0, 0, 0) if strides is None else (int(x) for x in strides)
+    d.o_stride_b, d.o_stride_h, d.o_stride_n = (0, 0, 0) if o_strides is None else (int(x) for x in o_strides)
     return d
 
 
@@ -103,7 +113,8 @@ def rpe_attn_cross_to_product(desc, table):
     (rows [0, S): row-offset encodings, [S, 2S): column-offset encodings).
     A 2-D float32 table is a bias table, a 3-D one a contextual table."""
     torch = _torch()
-    _, s, nb = rpe_attn_num_buckets(desc)
+    _, s, _ = rpe_attn_num_buckets(desc)
+    nb = s * s
     kind = _lib.RPE_TABLE_BIAS if table.dim() == 2 else _lib.RPE_TABLE_VECTOR
     th = desc.heads if desc.tables_per_head else 1
     want = (th, 2 * s) if kind == _lib.RPE_TABLE_BIAS else (th, 2 * s, desc.head_dim)
@@ -144,166 +155,162 @@ def _swin_desc(desc):
     return d
 
 
+def _check_geometry_and_tables(desc, q, mode, terms, per_head, bias, rq, rk, rv):
+    """Checks shared by the forward and backward bindings, before any launch: the
+    library sizes every read and write from the descriptor alone, so the token
+    count must match the grid and each table the mode and terms use must have
+    the descriptor's shape, dtype and device."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    n_img, _, _ = rpe_attn_unit_size(desc)
+    if n_img != N:
+        raise ValueError(f"N = {N} but prefix_tokens + grid gives {n_img}")
+    use = {"bias": mode == "bias", "rq": mode == "contextual" and "q" in terms,
+           "rk": mode == "contextual" and "k" in terms, "rv": mode == "contextual" and "v" in terms}
+    if mode == "none":
+        return
+    _, _, nb = rpe_attn_num_buckets(desc)
+    th = H if per_head else 1
+    for name, t in (("bias", bias), ("rq", rq), ("rk", rk), ("rv", rv)):
+        if not use[name]:
+            continue
+        if t is None:
+            raise ValueError(f"{name} is required by mode {mode!r} and terms {terms!r}")
+        if name == "bias":
+            if t.dtype != torch.float32 or tuple(t.shape) != (th, nb) or not t.is_contiguous():
+                raise ValueError(f"bias must be contiguous float32 [{th}, {nb}]")
+        elif t.dtype != q.dtype or tuple(t.shape) != (th, nb, d) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous {q.dtype} [{th}, {nb}, {d}]")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be on the device of q")
+
+
+def _view_strides(t, name):
+    """(batch, head, token) element strides of a [B, H, N, d] view whose head dim is contiguous."""
+    if t.dim() != 4 or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be a [B, H, N, d] view with a contiguous last dimension")
+    return tuple(int(x) for x in t.stride()[:3])
+
+
+def _fwd_setup(q, k, v, out, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
+               alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None, rq=None, rk=None,
+               rv=None, method="product"):
+    """Validate a forward call and marshal it: (descriptor of the tables, descriptor of
+    the launch, out, [bias, rq, rk, rv] as launched, [(kind, table, expanded)] of an
+    undirected map's expansions)."""
+    torch = _torch()
+    if method not in _METHODS:
+        raise ValueError(f"method {method!r}")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [B, H, N, d] of one shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be tensors on one device")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    strides = _view_strides(q, "q")
+    if _view_strides(k, "k") != strides or _view_strides(v, "v") != strides:
+        raise ValueError("q, k and v must share their strides (pass .contiguous() copies otherwise)")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must match q in shape, dtype and device")
+    o_strides = _view_strides(out, "out")
+    tabs = [t for t in (bias, rq, rk, rv) if t is not None]
+    per_head = any(t.shape[0] == H and H > 1 for t in tabs)
+    desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
+                     dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms, map=map,
+                     alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale,
+                     tables_per_head=per_head, method=method, strides=strides, o_strides=o_strides)
+    if mode == "none" and method == "cross":
+        raise ValueError("the Cross mapping needs bias or contextual mode")
+    _check_geometry_and_tables(desc, q, mode, terms, per_head, bias, rq, rk, rv)
+    used = {"bias": mode == "bias", "rq": mode == "contextual" and "q" in terms,
+            "rk": mode == "contextual" and "k" in terms, "rv": mode == "contextual" and "v" in terms}
+    launch = [t if used[n] else None for n, t in zip(("bias", "rq", "rk", "rv"), (bias, rq, rk, rv))]
+    expand = []
+    fdesc = desc
+    if map in UNDIRECTED:
+        if mode == "none":
+            raise ValueError("an undirected map needs bias or contextual mode")
+        # the index depends on the offset only: the forward runs with the Swin map
+        # on the tables expanded over raw offsets
+        for i, t in enumerate(launch):
+            if t is not None:
+                launch[i] = rpe_attn_undirected_to_product(desc, t)
+                expand.append((_lib.RPE_TABLE_BIAS if t.dim() == 2 else _lib.RPE_TABLE_VECTOR, t, launch[i]))
+        fdesc = _swin_desc(desc)
+    return desc, fdesc, out, launch, expand
+
+
 def rpe_attn_fwd(q, k, v, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
                  alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None,
                  rq=None, rk=None, rv=None, out=None, return_lse=False, method="product"):
     """Attention forward with 2D relative position terms.
 
-    q, k, v: [B, H, N, d] contiguous device tensors (bfloat16 or float32),
-    N = prefix_tokens + grid[0] * grid[1].  bias: [H or 1, S*S] float32;
-    rq / rk / rv: [H or 1, S*S, d] in the dtype of q.  Returns o (and the
-    float32 log-sum-exp [B, H, N] with ``return_lse``).
-
-    method="cross": the tables are Cross-mapping tables with 2S rows (row-offset
-    half, then column-offset half); they are rewritten as Product tables by
-    ``rpe_attn_cross_to_product`` and the Product forward runs on those.
+    q, k, v: [B, H, N, d] device views (bfloat16 or float32) with a contiguous
+    last dimension and one set of strides (e.g. the three slices of a fused
+    [B, N, 3, H, d] projection, permuted), N = prefix_tokens + grid[0] * grid[1].
+    bias: [H or 1, rows] float32; rq / rk / rv: [H or 1, rows, d] in the dtype
+    of q, contiguous; rows = S*S (method "product") or 2S (method "cross": the
+    row-offset half, then the column-offset half).  ``out`` may be any
+    [B, H, N, d] view with a contiguous last dimension (default: a new
+    contiguous tensor).  Returns o (and the float32 log-sum-exp [B, H, N] with
+    ``return_lse``).
 
     An undirected map ("euclidean", "euclidean_rounded", "quantized",
     "quantized_squared") takes tables of S rows; they are expanded by
     ``rpe_attn_undirected_to_product`` and the forward runs with the Swin map.
     """
     torch = _torch()
-    if map in UNDIRECTED:
-        if mode == "none":
-            raise ValueError("an undirected map needs bias or contextual mode")
-        B, H, _, d = q.shape
-        tabs = [t for t in (bias, rq, rk, rv) if t is not None]
-        per_head = any(t.shape[0] == H and H > 1 for t in tabs)
-        desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
-                         dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms,
-                         map=map, alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale,
-                         tables_per_head=per_head)
-        conv = lambda t, used: rpe_attn_undirected_to_product(desc, t) if (t is not None and used) else None
-        bias = conv(bias, mode == "bias")
-        rq, rk, rv = (conv(t, mode == "contextual" and n in terms) for n, t in (("q", rq), ("k", rk), ("v", rv)))
-        map = "swin"
-    if method == "cross":
-        if mode == "none":
-            raise ValueError("the Cross mapping needs bias or contextual mode")
-        B, H, _, d = q.shape
-        tabs = [t for t in (bias, rq, rk, rv) if t is not None]
-        per_head = any(t.shape[0] == H and H > 1 for t in tabs)
-        desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
-                         dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms,
-                         map=map, alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale,
-                         tables_per_head=per_head)
-        conv = lambda t, used: rpe_attn_cross_to_product(desc, t) if (t is not None and used) else None
-        bias = conv(bias, mode == "bias")
-        rq, rk, rv = (conv(t, mode == "contextual" and n in terms) for n, t in (("q", rq), ("k", rk), ("v", rv)))
-    elif method != "product":
-        raise ValueError(f"method {method!r}")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must be [B, H, N, d] of one shape")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be device tensors")
-    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must all be bfloat16 or all float32")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    B, H, N, d = q.shape
-    dtype = "bf16" if q.dtype == torch.bfloat16 else "fp32"
-    tabs = [t for t in (bias, rq, rk, rv) if t is not None]
-    per_head = any(t.shape[0] == H and H > 1 for t in tabs)
-    desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
-                     dtype=dtype, mode=mode, terms=terms, map=map, alpha=alpha, beta=beta, gamma=gamma,
-                     rounding=rounding, scale=scale, tables_per_head=per_head)
-    n_img, _, _ = rpe_attn_unit_size(desc)
-    if n_img != N:
-        raise ValueError(f"N = {N} but prefix_tokens + grid gives {n_img}")
-    if mode != "none":
-        _, _, nb = rpe_attn_num_buckets(desc)
-        th = H if per_head else 1
-        if bias is not None:
-            if bias.dtype != torch.float32 or tuple(bias.shape) != (th, nb) or not bias.is_contiguous():
-                raise ValueError(f"bias must be contiguous float32 [{th}, {nb}]")
-        for name, t in (("rq", rq), ("rk", rk), ("rv", rv)):
-            if t is not None and name[1] in terms:
-                if t.dtype != q.dtype or tuple(t.shape) != (th, nb, d) or not t.is_contiguous():
-                    raise ValueError(f"{name} must be contiguous {q.dtype} [{th}, {nb}, {d}]")
-    for t in tabs:
-        if not t.is_cuda:
-            raise ValueError("tables must be device tensors")
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must match q")
+    desc, fdesc, out, launch, _ = _fwd_setup(
+        q, k, v, out, grid=grid, window=window, prefix_tokens=prefix_tokens, mode=mode, terms=terms, map=map,
+        alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale, bias=bias, rq=rq, rk=rk, rv=rv,
+        method=method)
+    B, H, N, _ = q.shape
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    b, tq, tk, tv = launch
     check("rpe_attn_fwd",
-          load().rpe_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
-                              _ptr(rq if "q" in terms else None), _ptr(rk if "k" in terms else None),
-                              _ptr(rv if "v" in terms else None), _ptr(out), _ptr(lse),
-                              _stream(q.device)))
+          load().rpe_attn_fwd(ctypes.byref(fdesc), _ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(tq), _ptr(tk),
+                              _ptr(tv), _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if return_lse else out
 
 
 class PreparedFwd:
     """A validated rpe_attn_fwd call with fixed tensors: each call() is one
-    library call with pre-marshalled arguments (for launch loops and timing).
+    library call with pre-marshalled arguments (for launch loops and timing);
+    an undirected map's tables are expanded again on every call first.
 
     The tensors passed to ``prepare_fwd`` must stay alive and keep their
     storage while this object is used.
     """
 
-    def __init__(self, desc, ptrs, keep, device, convert=()):
+    def __init__(self, desc, fdesc, ptrs, keep, device, expand=()):
         self._lib = load()
         self._desc = desc
-        # an undirected map's tables are expanded under its own descriptor; the
-        # forward then runs with the Swin map
-        self._undirected = desc.map in (_lib.RPE_MAP_EUCLIDEAN, _lib.RPE_MAP_EUCLIDEAN_ROUNDED,
-                                        _lib.RPE_MAP_QUANTIZED, _lib.RPE_MAP_QUANTIZED_SQUARED) and desc.mode
-        self._fdesc = _swin_desc(desc) if self._undirected else desc
+        self._fdesc = fdesc
         self._args = ptrs
         self._keep = keep
         self._device = device
-        self._convert = convert    # (kind, cross, product) launches before the forward (Cross mapping)
+        self._expand = expand      # (kind, table, expanded) launches before the forward
 
     def __call__(self, stream=None):
         torch = _torch()
         s = ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream if stream is None else stream)
-        conv = self._lib.rpe_attn_undirected_to_product if self._undirected else self._lib.rpe_attn_cross_to_product
-        for kind, src, dst in self._convert:
-            check("table conversion", conv(ctypes.byref(self._desc), kind, src, dst, s))
+        for kind, src, dst in self._expand:
+            check("rpe_attn_undirected_to_product",
+                  self._lib.rpe_attn_undirected_to_product(ctypes.byref(self._desc), kind, src, dst, s))
         check("rpe_attn_fwd", self._lib.rpe_attn_fwd(ctypes.byref(self._fdesc), *self._args, s))
 
 
 def prepare_fwd(q, k, v, *, out, lse=None, **kw):
-    """Validate once (by running the call) and return a PreparedFwd for repeats.
-
-    With method="cross" every call first rewrites the Cross tables into Product
-    tables held by the PreparedFwd, then runs the forward on those."""
-    torch = _torch()
+    """Validate once (by running the call) and return a PreparedFwd for repeats."""
     rpe_attn_fwd(q, k, v, out=out, **kw)
-    B, H, N, d = q.shape
-    mode, terms = kw.get("mode", "none"), kw.get("terms", "")
-    tabs = [kw.get(n) for n in ("bias", "rq", "rk", "rv") if kw.get(n) is not None]
-    per_head = any(t.shape[0] == H and H > 1 for t in tabs)
-    desc = make_desc(batch=B, heads=H, head_dim=d, grid=kw["grid"], window=kw.get("window", 0),
-                     prefix_tokens=kw.get("prefix_tokens", 0),
-                     dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms,
-                     map=kw.get("map", "swin"), alpha=kw.get("alpha", 0.0), beta=kw.get("beta", 0.0),
-                     gamma=kw.get("gamma", 0.0), rounding=kw.get("rounding", "capped"),
-                     scale=kw.get("scale"), tables_per_head=per_head)
-    bias = kw.get("bias") if mode == "bias" else None
-    rq = kw.get("rq") if "q" in terms else None
-    rk = kw.get("rk") if "k" in terms else None
-    rv = kw.get("rv") if "v" in terms else None
-    convert = []
-    undirected = kw.get("map", "swin") in UNDIRECTED
-    if kw.get("method", "product") == "cross" or undirected:
-        prod = []
-        for t in (bias, rq, rk, rv):
-            if t is None:
-                prod.append(None)
-                continue
-            p = rpe_attn_undirected_to_product(desc, t) if undirected else rpe_attn_cross_to_product(desc, t)
-            kind = _lib.RPE_TABLE_BIAS if t.dim() == 2 else _lib.RPE_TABLE_VECTOR
-            convert.append((kind, _ptr(t), _ptr(p)))
-            prod.append(p)
-        tabs = tabs + [t for t in prod if t is not None]
-        bias, rq, rk, rv = prod
-    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(rq), _ptr(rk), _ptr(rv), _ptr(out), _ptr(lse)]
-    return PreparedFwd(desc, ptrs, (q, k, v, out, lse, tabs), q.device, tuple(convert))
+    kw.pop("return_lse", None)
+    desc, fdesc, out, launch, expand = _fwd_setup(q, k, v, out, **kw)
+    ptrs = [_ptr(q), _ptr(k), _ptr(v)] + [_ptr(t) for t in launch] + [_ptr(out), _ptr(lse)]
+    ex = tuple((kind, _ptr(src), _ptr(dst)) for kind, src, dst in expand)
+    return PreparedFwd(desc, fdesc, ptrs, (q, k, v, out, lse, launch, expand), q.device, ex)
 
 
 class PreparedBwd:
@@ -338,21 +345,30 @@ def rpe_attn_bwd(q, k, v, dout, lse, **kw):
 
 
 def _bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
-                 alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None, rq=None, rk=None,
-                 rv=None):
+         alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None, rq=None, rk=None,
+         rv=None, method="product"):
     torch = _torch()
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, dout)):
         raise ValueError("q, k, v, dout must be [B, H, N, d] of one shape")
-    if any(t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda for t in (k, v, dout)):
-        raise ValueError("q, k, v, dout must be contiguous device tensors of one dtype")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bfloat16 or float32")
+    if any(t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda or t.device != q.device
+           for t in (q, k, v, dout)):
+        raise ValueError("q, k, v, dout must be contiguous device tensors of one dtype and device")
     B, H, N, d = q.shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError("lse must be contiguous float32 [B, H, N] on the device of q")
+    if map in UNDIRECTED:
+        raise ValueError("the backward takes Product maps only (swin or piecewise)")
+    if method != "product":
+        raise ValueError("the backward takes the Product method only")
     tabs = [t for t in (bias, rq, rk, rv) if t is not None]
     per_head = any(t.shape[0] == H and H > 1 for t in tabs)
     desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
                      dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms, map=map,
                      alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale, tables_per_head=per_head)
+    _check_geometry_and_tables(desc, q, mode, terms, per_head, bias, rq, rk, rv)
     nbytes = ctypes.c_uint64()
     check("rpe_attn_bwd_workspace_size", load().rpe_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
     ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)

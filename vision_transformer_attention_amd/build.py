@@ -24,7 +24,9 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]
 SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "bwd.hip", "fwd_dispatch.cpp",
            "fwd_bf16_d16.hip", "fwd_bf16_d32.hip", "fwd_bf16_d64.hip",
-           "fwd_f32_d16.hip", "fwd_f32_d32.hip", "fwd_f32_d64.hip"]
+           "fwd_f32_d16.hip", "fwd_f32_d32.hip", "fwd_f32_d64.hip",
+           "fwd_cross_bf16_d16.hip", "fwd_cross_bf16_d32.hip", "fwd_cross_bf16_d64.hip",
+           "fwd_cross_f32_d16.hip", "fwd_cross_f32_d32.hip", "fwd_cross_f32_d64.hip"]
 
 
 def _run(cmd, verbose):

@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 
 #include "../../include/rpe_attn.h"
 #include "bwd.h"
@@ -21,6 +22,12 @@ hipError_t launch_undirected_to_product(bool bf16, bool f32, const void* table, 
                                         int Hp, int half, int map, int rounding, double alpha, double beta,
                                         double gamma, int width, int64_t total, hipStream_t stream);
 }  // namespace rpe
+
+namespace {
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+}  // namespace
 
 extern "C" {
 
@@ -100,7 +107,7 @@ rpe_status rpe_attn_cross_to_product(const rpe_attn_desc* desc, int32_t kind, co
   if (rpe::is_undirected(desc)) return RPE_E_MODE;
   if (!cross || !product) return RPE_E_NULL;
   const int64_t tables = desc->tables_per_head ? desc->heads : 1;
-  const int64_t total = tables * nb * width;
+  const int64_t total = tables * static_cast<int64_t>(s) * s * width;   // Product rows, either method
   const hipError_t e = rpe::launch_cross_to_product(bf16, cross, product, s, width, total,
                                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RPE_OK : RPE_E_HIP;
@@ -150,6 +157,13 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
     if ((desc->terms & RPE_TERM_Q) && !rq) return RPE_E_NULL;
     if ((desc->terms & RPE_TERM_V) && !rv) return RPE_E_NULL;
   }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return RPE_E_ALIGN;
+  if (desc->mode == RPE_MODE_BIAS && (reinterpret_cast<uintptr_t>(bias) & 3u)) return RPE_E_ALIGN;
+  if (desc->mode == RPE_MODE_CONTEXTUAL) {
+    if (((desc->terms & RPE_TERM_K) && !aligned16(rk)) || ((desc->terms & RPE_TERM_Q) && !aligned16(rq)) ||
+        ((desc->terms & RPE_TERM_V) && !aligned16(rv)))
+      return RPE_E_ALIGN;
+  }
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.bias = bias; p.rq = rq; p.rk = rk; p.rv = rv;
   const hipError_t e = rpe::launch_fwd(p, static_cast<hipStream_t>(stream));
@@ -171,7 +185,16 @@ uint64_t up256(uint64_t v) { return (v + 255) / 256 * 256; }
 int bwd_layout(const rpe_attn_desc* d, BwdLayout* L, int* T_out, int* U_out, int* nb_out) {
   int st = rpe::validate(d);
   if (st != RPE_OK) return st;
-  if (rpe::is_undirected(d)) return RPE_E_MODE;
+  if (rpe::is_undirected(d) || d->method != RPE_METHOD_PRODUCT) return RPE_E_MODE;
+  // the backward reads packed tables and contiguous [B][H][N][d] tensors
+  if (!rpe::contiguous_io(d)) return RPE_E_UNSUPPORTED;
+  if (d->tables_per_head && d->table_head_stride != 0) {
+    int hh = 0, ss = 0, rows = 0;
+    st = rpe::table_geometry(d, &hh, &ss, &rows);
+    if (st != RPE_OK) return st;
+    const int64_t packed = d->mode == RPE_MODE_BIAS ? rows : static_cast<int64_t>(rows) * d->head_dim;
+    if (d->table_head_stride != packed) return RPE_E_UNSUPPORTED;
+  }
   int h = 0, s = 0, nb = 1;
   if (d->mode != RPE_MODE_NONE) {
     st = rpe::table_geometry(d, &h, &s, &nb);
@@ -293,10 +316,11 @@ const char* rpe_status_str(int32_t status) {
     case RPE_E_PARAMS: return "invalid alpha/beta/gamma or scale";
     case RPE_E_UNSUPPORTED: return "configuration not built (head_dim or grid width)";
     case RPE_E_HIP: return "HIP launch error";
+    case RPE_E_ALIGN: return "a pointer or stride breaks 16-byte alignment";
     default: return "unknown status";
   }
 }
 
-const char* rpe_attn_version(void) { return "rpe_attn 0.1.0 gfx950"; }
+const char* rpe_attn_version(void) { return "rpe_attn 0.2.0 gfx950"; }
 
 }  // extern "C"

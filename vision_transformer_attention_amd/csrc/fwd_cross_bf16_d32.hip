@@ -1,0 +1,9 @@
+// Instances of the fused forward for __bf16 inputs, head dim 32, contextual tables under the
+// Cross mapping.
+#include "fwd_kernel.h"
+
+namespace rpe {
+hipError_t launch_fwd_cross_bf16_d32(const Params& p, hipStream_t stream) {
+  return launch_fwd_ctx<__bf16, 32, true>(p, stream);
+}
+}  // namespace rpe

@@ -1,0 +1,9 @@
+// Instances of the fused forward for float inputs, head dim 32, contextual tables under the
+// Cross mapping.
+#include "fwd_kernel.h"
+
+namespace rpe {
+hipError_t launch_fwd_cross_f32_d32(const Params& p, hipStream_t stream) {
+  return launch_fwd_ctx<float, 32, true>(p, stream);
+}
+}  // namespace rpe

@@ -27,8 +27,13 @@
 //       and bucket (eqs. 26-27) with the same MFMA as S^T, kept in LDS (fp16
 //       for bf16 inputs), and gathered per pair (eq. 28);
 //   query term: TQ[j][b] = c * k_j . rQ[b] per key block, gathered per pair;
-//   value term: softmax weights are summed per (row, bucket) into LDS with
-//       float atomics, and O^T += rV^T W^T at the end reuses the PV MFMA;
+//   value term: softmax weights are summed per (query row, row bucket, key
+//       column) in LDS with plain read-modify-writes (each entry has one
+//       owner lane), turned into per-bucket sums by prefix sums over the key
+//       columns, and O^T += rV^T W^T at the end reuses the PV MFMA; grid rows
+//       of 4 or 64 padded columns instead sum per (row, bucket) with LDS float
+//       atomics (a row's entries are only touched by the row's two lanes of one
+//       wave, so the order of the additions is fixed by the instruction stream);
 //   bias mode: the head's (2M-1)^2 table, prescaled by log2(e), is gathered.
 // The bucket of a pair is b = (g(dy)+H)*S + (g(dx)+H) with (dy, dx) = query -
 // key; its LDS address is ry(dy) + cx(lane, key column): ry is read from a
@@ -188,9 +193,13 @@ using bool_c = std::integral_constant<bool, B>;
 
 }  // namespace
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI>
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, bool CROSS>
 __global__ void __launch_bounds__(kThreadsMax) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE, D, MULTI))))
 rpe_fwd_kernel(Params p) {
+  // CROSS: contextual tables under the Cross mapping (2S rows; instances of their
+  // own, so that the Product instances carry none of its code).  Bias tables under
+  // the Cross mapping are summed into the Product layout in the prologue (p.cross).
+  static_assert(!CROSS || MODE == RPE_MODE_CONTEXTUAL, "Cross instances are contextual");
   constexpr bool BF = std::is_same<DT, __bf16>::value;
   constexpr bool CTX = MODE == RPE_MODE_CONTEXTUAL;
   constexpr bool TK = CTX && (TERMS & RPE_TERM_K);
@@ -232,6 +241,7 @@ rpe_fwd_kernel(Params p) {
   asm volatile("" ::"s"(p.Wp), "s"(p.lwp), "s"(p.prefix_block), "s"(p.prefix_in_tail), "s"(p.nb), "s"(p.nbt),
                "s"(p.stages), "s"(p.n_blocks), "s"(p.rk_lds), "s"(p.off_stage), "s"(p.off_tab));
   asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.rk), "s"(p.tab_head_stride));
+  asm volatile("" ::"s"(p.sb), "s"(p.sh), "s"(p.sn), "s"(p.rbi));
 
   const int nth = blockDim.x;
   const int NW = nth >> 6;
@@ -262,7 +272,8 @@ rpe_fwd_kernel(Params p) {
   const uint32_t unit0 = ugrp * static_cast<uint32_t>(p.upw);
   const uint32_t bh = fdiv(unit0, p.dv_U);
   const int w_img0 = static_cast<int>(unit0 - bh * static_cast<uint32_t>(p.U));
-  const int head = static_cast<int>(bh - fdiv(bh, p.dv_H) * static_cast<uint32_t>(p.H));
+  const uint32_t bb = fdiv(bh, p.dv_H);
+  const int head = static_cast<int>(bh - bb * static_cast<uint32_t>(p.H));
   // MULTI instances serve p.upw > 1 (the launch picks them); the others one unit
   constexpr bool multi = MULTI;
   static_assert(!MULTI || MODE != RPE_MODE_CONTEXTUAL, "multi-unit workgroups have no contextual terms");
@@ -278,11 +289,17 @@ rpe_fwd_kernel(Params p) {
   const int rt1 = static_cast<int>(fdiv(static_cast<uint32_t>((qc + 1) * p.n_rt), p.dv_qc));
   const bool active = rt0 + wid < rt1;
 
-  const int64_t base = static_cast<int64_t>(bh) * p.N * D;
-  const DT* __restrict__ qg = reinterpret_cast<const DT*>(p.q) + base;
-  const char* __restrict__ kgb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.k) + base);
-  const char* __restrict__ vgb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.v) + base);
-  DT* __restrict__ og = reinterpret_cast<DT*>(p.o) + base;
+  // (batch, head) slices of q, k, v and of o at their element strides; a token
+  // row of q, k, v is RBG bytes after the previous one.  Token indices and row
+  // strides are below 2^24 (the planner checks the strides), so row offsets take
+  // the full-rate 24-bit multiply.
+  const int64_t ibase = static_cast<int64_t>(bb) * p.sb + static_cast<int64_t>(head) * p.sh;
+  const int64_t obase = static_cast<int64_t>(bb) * p.osb + static_cast<int64_t>(head) * p.osh;
+  const uint32_t RBG = p.rbi;
+  const DT* __restrict__ qg = reinterpret_cast<const DT*>(p.q) + ibase;
+  const char* __restrict__ kgb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.k) + ibase);
+  const char* __restrict__ vgb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.v) + ibase);
+  DT* __restrict__ og = reinterpret_cast<DT*>(p.o) + obase;
   const char* rvb = reinterpret_cast<const char*>(reinterpret_cast<const DT*>(p.rv) + head * p.tab_head_stride);
 
   int* const ry_tab = reinterpret_cast<int*>(smem + p.off_ry);
@@ -302,6 +319,8 @@ rpe_fwd_kernel(Params p) {
   const int yi = static_cast<int>(fdiv(static_cast<uint32_t>(qt), p.dv_C)), xi = qt - yi * p.C;
   const int qn = qpos ? wbase + yi * rowstride + xi : (qvalid ? qi : 0);
 
+  // element offset of this lane's query row (a slice spans less than 2^31 bytes)
+  const uint32_t qrow = __umul24(static_cast<uint32_t>(qn), static_cast<uint32_t>(p.sn));
   // Q as the B operand of S^T = K Q^T: lane holds Q[row r32][k-slice h of each step].
   bf16x8 qb[BF ? KS : 1];
   float qf[BF ? 1 : KS];
@@ -311,12 +330,12 @@ rpe_fwd_kernel(Params p) {
     for (int kk = 0; kk < KS; ++kk) {
       const int d0 = 16 * kk + 8 * h;
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (!multi && qvalid && d0 < D) u = ld16(qg + static_cast<int64_t>(qn) * D + d0);
+      if (!multi && qvalid && d0 < D) u = ld16(qg + qrow + d0);
       qb[kk] = as_bf16x8(u);
     }
   } else {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = (!multi && qvalid) ? qg[static_cast<int64_t>(qn) * D + 2 * kk + h] : 0.0f;
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = (!multi && qvalid) ? qg[qrow + 2 * kk + h] : 0.0f;
   }
 
   // rK rows as the A operand of TK^T = rK Q^T.  Small tables (p.rk_lds) are
@@ -345,7 +364,9 @@ rpe_fwd_kernel(Params p) {
       }
     }
   };
-  if (!p.rk_lds) load_rk(0);
+  if constexpr (!CROSS) {
+    if (!p.rk_lds) load_rk(0);
+  }
 
   // ---- the block stream: per unit [Q tiles (multi-unit only)][key/value blocks]
   // [rV tiles]; a Q element carries 64 query rows (32 in each half of a stage)
@@ -380,26 +401,26 @@ rpe_fwd_kernel(Params p) {
   };
   // Interior grid blocks (rows < R-1, Wp <= 32): a slot's column is the same in
   // every block and its row advances by 32/Wp grid rows, so the byte offset of
-  // this wave's first instruction (i = wid) is wbase * RB + ioff0 + block * idoff,
+  // this wave's first instruction (i = wid) is wbase * RBG + ioff0 + block * idoff,
   // with a per-lane part ioff0 and a uniform step idoff.  Padding columns load
   // the row's last token (any token would do: their weights are zero).
   uint32_t ioff0 = 0, idoff = 0;
   // Wide rows (64 slots, two blocks per grid row): per-lane offsets of the
   // even and odd blocks of a row (padding columns load the row's last token);
-  // block gb adds the uniform (gb >> 1) * rowstride * RB.
+  // block gb adds the uniform (gb >> 1) * rowstride * RBG.
   uint32_t ioffe = 0, ioffo = 0;
   if constexpr (WIDE) {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
-    ioffe = static_cast<uint32_t>(row < p.C ? row : p.C - 1) * RB + cb;
-    ioffo = static_cast<uint32_t>(32 + row < p.C ? 32 + row : p.C - 1) * RB + cb;
+    ioffe = __umul24(static_cast<uint32_t>(row < p.C ? row : p.C - 1), RBG) + cb;
+    ioffo = __umul24(static_cast<uint32_t>(32 + row < p.C ? 32 + row : p.C - 1), RBG) + cb;
   }
   if constexpr (!WIDE) {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
     const int x = row & (p.Wp - 1), y0 = row >> p.lwp;
-    ioff0 = static_cast<uint32_t>(y0 * rowstride + (x < p.C ? x : p.C - 1)) * RB + cb;
-    idoff = static_cast<uint32_t>((kBlockSlots >> p.lwp) * rowstride * RB);
+    ioff0 = __umul24(static_cast<uint32_t>(y0 * rowstride + (x < p.C ? x : p.C - 1)), RBG) + cb;
+    idoff = static_cast<uint32_t>((kBlockSlots >> p.lwp) * rowstride) * RBG;
   }
   // Copy 32 rows into a swizzled row-major tile: instruction i covers rows
   // [i*RPI, (i+1)*RPI); lane l fills chunk position l % CPR of row l / CPR with
@@ -416,7 +437,7 @@ rpe_fwd_kernel(Params p) {
         // query rows 64 loc + row (first half) and 64 loc + 32 + row (second half)
         auto q_off = [&](int qi) -> uint32_t {
           const int y = static_cast<int>(fdiv(static_cast<uint32_t>(qi), p.dv_C)), x = qi - y * p.C;
-          return static_cast<uint32_t>(qi < p.T ? wb + y * rowstride + x : wb) * RB + cb;
+          return __umul24(static_cast<uint32_t>(qi < p.T ? wb + y * rowstride + x : wb), RBG) + cb;
         };
         dma16(reinterpret_cast<const char*>(qg) + q_off(64 * loc + row), kt + i * 1024);
         dma16(reinterpret_cast<const char*>(qg) + q_off(64 * loc + 32 + row), vt + i * 1024);
@@ -424,15 +445,25 @@ rpe_fwd_kernel(Params p) {
         const int f = loc - nqe;
         const int gb = f - p.prefix_block;
         const uint32_t off = (!WIDE && i == wid && gb >= 0 && gb < p.first_tail)
-                                 ? static_cast<uint32_t>(wb) * RB + ioff0 + static_cast<uint32_t>(gb) * idoff
-                                 : static_cast<uint32_t>(slot_n(f, row, wb)) * RB + cb;
+                                 ? static_cast<uint32_t>(wb) * RBG + ioff0 + static_cast<uint32_t>(gb) * idoff
+                                 : __umul24(static_cast<uint32_t>(slot_n(f, row, wb)), RBG) + cb;
         dma16(kgb + off, kt + i * 1024);
         dma16(vgb + off, vt + i * 1024);
       } else {
-        const int b = kRowTile * (loc - nqe - nblk) + row;
-        const uint32_t off = static_cast<uint32_t>(b < p.nb ? b : 0) * RB + cb;
-        dma16(rvb + off, kt + i * 1024);
-        dma16(rvb + off, vt + i * 1024);
+        // rV rows of Product bucket b (rows past nb read row 0) into both halves of
+        // the stage; Cross: the row-offset row b / S into the K half and the
+        // column-offset row S + b % S into the V half, each contracted with the
+        // bucket's weight in the epilogue
+        const int b0 = kRowTile * (loc - nqe - nblk) + row;
+        const int b = b0 < p.nb ? b0 : 0;
+        uint32_t offk = static_cast<uint32_t>(b) * RB + cb, offv = offk;
+        if constexpr (CROSS) {
+          const int a = static_cast<int>(fdiv(static_cast<uint32_t>(b), p.dv_S));
+          offk = static_cast<uint32_t>(a) * RB + cb;
+          offv = static_cast<uint32_t>(p.S + b - a * p.S) * RB + cb;
+        }
+        dma16(rvb + offk, kt + i * 1024);
+        dma16(rvb + offv, vt + i * 1024);
       }
     }
   };
@@ -445,20 +476,20 @@ rpe_fwd_kernel(Params p) {
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
     const int y = WIDE ? gb >> 1 : (gb * kBlockSlots + row) >> p.lwp;
     const int x = WIDE ? ((gb & 1) << 5) + row : (gb * kBlockSlots + row) & (p.Wp - 1);
-    return static_cast<uint32_t>(x < p.C ? wbase + y * rowstride + x : wbase) * RB + cb;
+    return __umul24(static_cast<uint32_t>(x < p.C ? wbase + y * rowstride + x : wbase), RBG) + cb;
   };
   auto issue_interior = [&](int gb, int stage) {
     const uint32_t kt = lds_ring + stage * (2 * TILE);
     const uint32_t vt = kt + TILE;
     if (wid < IPB) {
       if constexpr (WIDE) {
-        const uint32_t ub = (static_cast<uint32_t>(wbase) + static_cast<uint32_t>(gb >> 1) * rowstride) * RB;
+        const uint32_t ub = (static_cast<uint32_t>(wbase) + static_cast<uint32_t>(gb >> 1) * rowstride) * RBG;
         const uint32_t vo = (gb & 1) ? ioffo : ioffe;
         dma16s(kgb + ub, vo, kt + wid * 1024);
         dma16s(vgb + ub, vo, vt + wid * 1024);
       } else {
         // uniform part in the scalar base, per-lane part fixed across blocks
-        const uint32_t ub = static_cast<uint32_t>(wbase) * RB + static_cast<uint32_t>(gb) * idoff;
+        const uint32_t ub = static_cast<uint32_t>(wbase) * RBG + static_cast<uint32_t>(gb) * idoff;
         dma16s(kgb + ub, ioff0, kt + wid * 1024);
         dma16s(vgb + ub, ioff0, vt + wid * 1024);
       }
@@ -485,14 +516,34 @@ rpe_fwd_kernel(Params p) {
     }
   }
 
+  // ---- Cross key term: the table's 2S rows go to LDS as swizzled 32-row tiles
+  // (read per lane by the scores below), issued with Q.
+  if constexpr (TK && CROSS) {
+    {
+      const uint32_t lds_rkc = lds_ring - p.off_stage + p.off_rkc;
+      const int ntt = (p.ntr + kRowTile - 1) / kRowTile;
+      for (int ii = wid; ii < ntt * IPB; ii += NW) {
+        const int t = ii / IPB, i = ii - t * IPB;
+        const int row = i * RPI + lane / CPR;
+        const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
+        const int b = kRowTile * t + row;
+        dma16(reinterpret_cast<const char*>(rkt) + static_cast<uint32_t>(b < p.ntr ? b : 0) * RB + cb,
+              lds_rkc + t * TILE + i * 1024);
+      }
+    }
+  }
+
   // ---- bias mode: the head's table goes straight to LDS (64 entries per
   // instruction, instruction k from wave k % NW); each lane scales its own
   // entries by log2(e) once its copies have landed, before the prologue barrier.
+  // Cross: the 2S entries go to their own area and are summed into the S*S
+  // Product entries after a barrier.
   if constexpr (MODE == RPE_MODE_BIAS) {
     const char* bt = reinterpret_cast<const char*>(p.bias + head * p.tab_head_stride);
-    const uint32_t lds_tab = lds_ring - p.off_stage + p.off_tab;
-    for (int k = wid; k * 64 < p.nb; k += NW)
-      if (k * 64 + lane < p.nb) dma4(bt + (k * 64 + lane) * 4, lds_tab + k * 256);
+    const int nent = p.cross ? p.ntr : p.nb;
+    const uint32_t lds_tab = lds_ring - p.off_stage + (p.cross ? p.off_bx : p.off_tab);
+    for (int k = wid; k * 64 < nent; k += NW)
+      if (k * 64 + lane < nent) dma4(bt + (k * 64 + lane) * 4, lds_tab + k * 256);
   }
 
   // ---- start the ring now (the prologue below overlaps its latency); the Q,
@@ -568,12 +619,12 @@ rpe_fwd_kernel(Params p) {
     for (int i = tid; i < NW * kRowTile * p.p_tab; i += nth) gtab[i] = static_cast<GT>(0.0f);
   }
   if constexpr (TQ) {
-    // rQ staged as [nbt*32][kpitch] (rows past nb zero)
+    // rQ staged as [nrq][kpitch]: nbt*32 rows (rows past nb zero), or the 2S Cross rows
     const DT* rq = reinterpret_cast<const DT*>(p.rq) + head * p.tab_head_stride;
     constexpr int CH = D / EPC;
-    for (int it = tid; it < p.nbt * kRowTile * CH; it += nth) {
+    for (int it = tid; it < p.nrq * CH; it += nth) {
       const int row = it / CH, ch = it - (it / CH) * CH;
-      const uint4 u = row < p.nb ? ld16(rq + static_cast<int64_t>(row) * D + ch * EPC) : make_uint4(0, 0, 0, 0);
+      const uint4 u = row < p.ntr ? ld16(rq + static_cast<int64_t>(row) * D + ch * EPC) : make_uint4(0, 0, 0, 0);
       if constexpr (BF) {
         *reinterpret_cast<uint4*>(smem + p.off_rq + (row * p.kpitch + ch * EPC) * 2) = u;
       } else {
@@ -603,6 +654,34 @@ rpe_fwd_kernel(Params p) {
     }
     return acc;
   };
+
+  // Q times two table rows R0 and R1 (per lane) of swizzled [32][D] tiles at
+  // `base` (row R in tile R / 32 at row R % 32), summed in one accumulator:
+  // lane holds table-row position 8j + 4h + i of the 32 A rows and query r32.
+  auto rows_tile = [&](const char* base, int R0, int R1) -> f32x16 {
+    f32x16 acc = f32x16{};
+    const char* r0 = base + (R0 >> 5) * TILE + (R0 & 31) * RB;
+    const char* r1 = base + (R1 >> 5) * TILE + (R1 & 31) * RB;
+    const int s0 = R0 & (CPR - 1), s1 = R1 & (CPR - 1);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if constexpr (BF) {
+        const int c = 2 * kk + h;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(r0 + ((c ^ s0) << 4));
+        const uint4 a1 = *reinterpret_cast<const uint4*>(r1 + ((c ^ s1) << 4));
+        acc = mfma32(as_bf16x8(a0), qb[kk], acc);
+        acc = mfma32(as_bf16x8(a1), qb[kk], acc);
+      } else {
+        const int col = (2 * kk + h) * 4;
+        const float a0 = *reinterpret_cast<const float*>(r0 + (((col >> 4) ^ s0) << 4) + (col & 15));
+        const float a1 = *reinterpret_cast<const float*>(r1 + (((col >> 4) ^ s1) << 4) + (col & 15));
+        acc = mfma32(a0, qf[kk], acc);
+        acc = mfma32(a1, qf[kk], acc);
+      }
+    }
+    return acc;
+  };
+  (void)rows_tile;
 
   // O^T += V^T P^T from a swizzled row-major [32 keys][D] tile.  pv[j][i] is this
   // lane's weight for key 8j + 4h + i.  bf16: the k slots 8h..8h+7 of step kk hold
@@ -716,13 +795,24 @@ rpe_fwd_kernel(Params p) {
   (void)vcol;
   if constexpr (TK) {
     // this wave's rK copies are older than its ring loads
-    if (p.rk_lds) wait_vmcnt_floor((L < ST - 1 ? L : ST - 1) * lpe);
+    if (CROSS || p.rk_lds) wait_vmcnt_floor((L < ST - 1 ? L : ST - 1) * lpe);
   }
   if constexpr (MODE == RPE_MODE_BIAS) {
     // this wave's bias copies are older than its ring loads
     wait_vmcnt_floor((L < ST - 1 ? L : ST - 1) * lpe);
-    for (int k = wid; k * 64 < p.nb; k += NW)
-      if (k * 64 + lane < p.nb) gtab[k * 64 + lane] *= p.bias_mul;
+    if (p.cross) {
+      // entry b = (a, c) of the Product layout: row-offset entry a plus
+      // column-offset entry S + c, summed in float32 (every wave's copies first)
+      lds_barrier();
+      const float* bx = reinterpret_cast<const float*>(smem + p.off_bx);
+      for (int e = tid; e < p.nb; e += nth) {
+        const int a = static_cast<int>(fdiv(static_cast<uint32_t>(e), p.dv_S));
+        gtab[e] = (bx[a] + bx[p.S + e - a * p.S]) * p.bias_mul;
+      }
+    } else {
+      for (int k = wid; k * 64 < p.nb; k += NW)
+        if (k * 64 + lane < p.nb) gtab[k * 64 + lane] *= p.bias_mul;
+    }
   }
   lds_barrier();  // prologue tables (and rK / bias copies) visible; ring loads stay in flight
   if constexpr (VW) {
@@ -1034,31 +1124,51 @@ rpe_fwd_kernel(Params p) {
   };
 
   // Query-term scores of a key block: TQ[slot][b] = c * k_slot . rQ[b]; tiles over waves.
-  auto block_query_scores = [&](const char* ktile) {
+  // The A operand of lane r32 is staged row ra (bucket 32t + r32), plus row rb
+  // under Cross (the bucket's row-offset row ra = b / S and column-offset row
+  // rb = S + b % S, both multiplied into the accumulator).
+  auto query_tile = [&](const char* ktile, int t, int ra, int rb) __attribute__((always_inline)) {
     if constexpr (TQ) {
       const int sw = r32 & (CPR - 1);
       const char* rqs = smem + p.off_rq;
-      for (int t = wid; t < p.nbt; t += NW) {
-        f32x16 acc = {};
+      f32x16 acc = {};
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          if constexpr (BF) {
-            const int c = 2 * kk + h, d0 = 16 * kk + 8 * h;
-            const uint4 a = *reinterpret_cast<const uint4*>(rqs + ((kRowTile * t + r32) * p.kpitch + d0) * 2);
-            const uint4 kv = *reinterpret_cast<const uint4*>(ktile + r32 * RB + ((c ^ sw) << 4));
-            acc = mfma32(as_bf16x8(a), as_bf16x8(kv), acc);
-          } else {
-            const int col = (2 * kk + h) * 4;
-            const float kv = *reinterpret_cast<const float*>(ktile + r32 * RB + (((col >> 4) ^ sw) << 4) + (col & 15));
-            acc = mfma32(reinterpret_cast<const float*>(rqs)[(kRowTile * t + r32) * p.kpitch + 2 * kk + h], kv, acc);
+      for (int kk = 0; kk < KS; ++kk) {
+        if constexpr (BF) {
+          const int c = 2 * kk + h, d0 = 16 * kk + 8 * h;
+          const uint4 a = *reinterpret_cast<const uint4*>(rqs + (ra * p.kpitch + d0) * 2);
+          const uint4 kv = *reinterpret_cast<const uint4*>(ktile + r32 * RB + ((c ^ sw) << 4));
+          acc = mfma32(as_bf16x8(a), as_bf16x8(kv), acc);
+          if constexpr (CROSS) {
+            const uint4 a1 = *reinterpret_cast<const uint4*>(rqs + (rb * p.kpitch + d0) * 2);
+            acc = mfma32(as_bf16x8(a1), as_bf16x8(kv), acc);
           }
+        } else {
+          const int col = (2 * kk + h) * 4;
+          const float kv = *reinterpret_cast<const float*>(ktile + r32 * RB + (((col >> 4) ^ sw) << 4) + (col & 15));
+          acc = mfma32(reinterpret_cast<const float*>(rqs)[ra * p.kpitch + 2 * kk + h], kv, acc);
+          if constexpr (CROSS) acc = mfma32(reinterpret_cast<const float*>(rqs)[rb * p.kpitch + 2 * kk + h], kv, acc);
         }
-        // lane holds TQ[slot r32][32t + 8j + 4h + i]; rows hold nbt*32 entries
+      }
+      // lane holds TQ[slot r32][32t + 8j + 4h + i]; rows hold nbt*32 entries
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            tqs[r32 * p.p_tq + kRowTile * t + 8 * j + 4 * h + i] = acc[4 * j + i] * p.c;
+        for (int i = 0; i < 4; ++i)
+          tqs[r32 * p.p_tq + kRowTile * t + 8 * j + 4 * h + i] = acc[4 * j + i] * p.c;
+    }
+  };
+  auto block_query_scores = [&](const char* ktile) {
+    if constexpr (TQ) {
+      if constexpr (CROSS) {
+        for (int t = wid; t < p.nbt; t += NW) {
+          const int b0 = kRowTile * t + r32;
+          const int b = b0 < p.nb ? b0 : p.nb - 1;
+          const int ra = static_cast<int>(fdiv(static_cast<uint32_t>(b), p.dv_S));
+          query_tile(ktile, t, ra, p.S + b - ra * p.S);
+        }
+      } else {
+        for (int t = wid; t < p.nbt; t += NW) query_tile(ktile, t, kRowTile * t + r32, 0);
       }
     }
   };
@@ -1124,43 +1234,62 @@ rpe_fwd_kernel(Params p) {
         }
       }
     };
-    if (p.rk_lds) {
-      // rK sits in the row area: every wave takes all its products (already in
-      // the row format) before any row is written
-      GT tv[KB][16];
+    if constexpr (CROSS) {
+      // Cross: the A operand of Product bucket b = 32t + r32 is row b / S of the
+      // staged table, then row S + b % S, both multiplied into one accumulator,
+      // so the score is q.rK[row half] + q.rK[column half] in float32
+      if (active) {
+        const char* rkc = smem + p.off_rkc;
+        for (int t = 0; t < p.nbt; ++t) {
+          const int b0 = kRowTile * t + r32;
+          const int b = b0 < p.nb ? b0 : p.nb - 1;
+          const int a = static_cast<int>(fdiv(static_cast<uint32_t>(b), p.dv_S));
+          const f32x16 acc = rows_tile(rkc, a, p.S + b - a * p.S);
+          GT v[16];
 #pragma unroll
-      for (int bt = 0; bt < KB; ++bt) {
-        if (bt < p.nbt) {
-          const f32x16 acc = s_tile(smem + p.off_tab + bt * TILE, f32x16{});
-#pragma unroll
-          for (int k = 0; k < 16; ++k) tv[bt][k] = to_gt(acc[k]);
+          for (int k = 0; k < 16; ++k) v[k] = to_gt(acc[k]);
+          store_tile(t, v);
         }
       }
-      lds_barrier();
-      if (active) {
-#pragma unroll
-        for (int bt = 0; bt < KB; ++bt)
-          if (bt < p.nbt) store_tile(bt, tv[bt]);
-      }
     } else {
-      for (int t0 = 0; t0 < p.nbt; t0 += KB) {
-        if (t0 > 0) load_rk(t0);
+      if (p.rk_lds) {
+        // rK sits in the row area: every wave takes all its products (already in
+        // the row format) before any row is written
+        GT tv[KB][16];
 #pragma unroll
         for (int bt = 0; bt < KB; ++bt) {
-          const int t = t0 + bt;
-          if (t < p.nbt && active) {
-            f32x16 acc = {};
+          if (bt < p.nbt) {
+            const f32x16 acc = s_tile(smem + p.off_tab + bt * TILE, f32x16{});
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-              if constexpr (BF)
-                acc = mfma32(rka[bt][kk], qb[kk], acc);
-              else
-                acc = mfma32(rkf[bt][kk], qf[kk], acc);
+            for (int k = 0; k < 16; ++k) tv[bt][k] = to_gt(acc[k]);
+          }
+        }
+        lds_barrier();
+        if (active) {
+#pragma unroll
+          for (int bt = 0; bt < KB; ++bt)
+            if (bt < p.nbt) store_tile(bt, tv[bt]);
+        }
+      } else {
+        for (int t0 = 0; t0 < p.nbt; t0 += KB) {
+          if (t0 > 0) load_rk(t0);
+#pragma unroll
+          for (int bt = 0; bt < KB; ++bt) {
+            const int t = t0 + bt;
+            if (t < p.nbt && active) {
+              f32x16 acc = {};
+#pragma unroll
+              for (int kk = 0; kk < KS; ++kk) {
+                if constexpr (BF)
+                  acc = mfma32(rka[bt][kk], qb[kk], acc);
+                else
+                  acc = mfma32(rkf[bt][kk], qf[kk], acc);
+              }
+              GT v[16];
+#pragma unroll
+              for (int k = 0; k < 16; ++k) v[k] = to_gt(acc[k]);
+              store_tile(t, v);
             }
-            GT v[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) v[k] = to_gt(acc[k]);
-            store_tile(t, v);
           }
         }
       }
@@ -1335,9 +1464,9 @@ rpe_fwd_kernel(Params p) {
             // bucket nb - 1 and are dropped.
             int fa[4][4], fb[4][4];
             bool ok[4][4], lo0[4][4];
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j)
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int b0 = kRowTile * t + 8 * j + 4 * h + i;
                 const int b = b0 < p.nb ? b0 : p.nb - 1;
@@ -1346,9 +1475,9 @@ rpe_fwd_kernel(Params p) {
                 fb[j][i] = cr_tab[b - a * p.S];
               }
             float fh[4][4], fl[4][4];
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j)
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int cr = fb[j][i];
                 const int lo = static_cast<int16_t>(cr & 0xffff), hi = cr >> 16;
@@ -1362,22 +1491,24 @@ rpe_fwd_kernel(Params p) {
                 fh[j][i] = *reinterpret_cast<const float*>(smem + fa[j][i] + 4 * ih);
                 fl[j][i] = *reinterpret_cast<const float*>(smem + fa[j][i] + 4 * il);
               }
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j)
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 4; ++i)
                 wv[j][i] = ok[j][i] ? fh[j][i] - (lo0[j][i] ? 0.0f : fl[j][i]) : 0.0f;
           } else {
             const float* wrow = reinterpret_cast<const float*>(smem + waddr(lds0 + rowbase));
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j)
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int b = kRowTile * t + 8 * j + 4 * h + i;
                 wv[j][i] = b < p.nb ? wrow[b] : 0.0f;
               }
           }
           pv_tile(vtile_of(s), wv, true);
+          // Cross: the row-offset rows sit in the K half of the stage
+          if constexpr (CROSS) pv_tile(ktile_of(s), wv, true);
         }
       }
     }
@@ -1385,21 +1516,21 @@ rpe_fwd_kernel(Params p) {
     if (qvalid) {
     const float l = l_part + __shfl_xor(l_part, 32);
     const float inv = 1.0f / l;
-    DT* orow = og + static_cast<int64_t>(qnk) * D;
-  #pragma unroll
+    DT* orow = og + __umul24(static_cast<uint32_t>(qnk), static_cast<uint32_t>(p.osn));
+#pragma unroll
     for (int c = 0; c < DTL; ++c)
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d0 = 32 * c + 8 * j + 4 * h;
         if (d0 < D) {
           if constexpr (BF) {
             bf16x4 o4;
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) o4[i] = static_cast<__bf16>(oacc[c][4 * j + i] * inv);
             *reinterpret_cast<bf16x4*>(orow + d0) = o4;
           } else {
             f32x4 o4;
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) o4[i] = oacc[c][4 * j + i] * inv;
             *reinterpret_cast<f32x4*>(orow + d0) = o4;
           }
@@ -1413,9 +1544,9 @@ rpe_fwd_kernel(Params p) {
 // ----------------------------------------------------------------------------------------
 // Launch dispatch.
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI>
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, bool CROSS>
 hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
-  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, MULTI>;
+  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, MULTI, CROSS>;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   if (attr != hipSuccess) return attr;
@@ -1424,32 +1555,40 @@ hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename DT, int D, int MODE, unsigned TERMS>
+template <typename DT, int D, int MODE, unsigned TERMS, bool CROSS>
 hipError_t launch_fwd_t(const Params& p, hipStream_t stream) {
   // (several units per workgroup only arise for units of at most 4 query tiles,
   // so never with wide rows)
   if constexpr (MODE != RPE_MODE_CONTEXTUAL) {
-    if (p.upw > 1 && p.Wp != 64) return launch_fwd_w<DT, D, MODE, TERMS, false, true>(p, stream);
+    if (p.upw > 1 && p.Wp != 64) return launch_fwd_w<DT, D, MODE, TERMS, false, true, false>(p, stream);
   }
-  return p.Wp == 64 ? launch_fwd_w<DT, D, MODE, TERMS, true, false>(p, stream)
-                    : launch_fwd_w<DT, D, MODE, TERMS, false, false>(p, stream);
+  return p.Wp == 64 ? launch_fwd_w<DT, D, MODE, TERMS, true, false, CROSS>(p, stream)
+                    : launch_fwd_w<DT, D, MODE, TERMS, false, false, CROSS>(p, stream);
 }
 
-// All mode / term instances of one (dtype, head dim).
-template <typename DT, int D>
-hipError_t launch_fwd_d(const Params& p, hipStream_t stream) {
-  if (p.mode == RPE_MODE_NONE) return launch_fwd_t<DT, D, RPE_MODE_NONE, 0>(p, stream);
-  if (p.mode == RPE_MODE_BIAS) return launch_fwd_t<DT, D, RPE_MODE_BIAS, 0>(p, stream);
+// The contextual instances of one (dtype, head dim) for one method.
+template <typename DT, int D, bool CROSS>
+hipError_t launch_fwd_ctx(const Params& p, hipStream_t stream) {
   switch (p.terms) {
-    case 1: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 1>(p, stream);
-    case 2: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 2>(p, stream);
-    case 3: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 3>(p, stream);
-    case 4: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 4>(p, stream);
-    case 5: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 5>(p, stream);
-    case 6: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 6>(p, stream);
-    case 7: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 7>(p, stream);
+    case 1: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 1, CROSS>(p, stream);
+    case 2: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 2, CROSS>(p, stream);
+    case 3: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 3, CROSS>(p, stream);
+    case 4: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 4, CROSS>(p, stream);
+    case 5: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 5, CROSS>(p, stream);
+    case 6: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 6, CROSS>(p, stream);
+    case 7: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 7, CROSS>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The no-position, bias and contextual Product instances of one (dtype, head
+// dim); the contextual Cross instances are launched by launch_fwd_ctx<.., true>
+// from translation units of their own.
+template <typename DT, int D>
+hipError_t launch_fwd_d(const Params& p, hipStream_t stream) {
+  if (p.mode == RPE_MODE_NONE) return launch_fwd_t<DT, D, RPE_MODE_NONE, 0, false>(p, stream);
+  if (p.mode == RPE_MODE_BIAS) return launch_fwd_t<DT, D, RPE_MODE_BIAS, 0, false>(p, stream);
+  return launch_fwd_ctx<DT, D, false>(p, stream);
 }
 
 }  // namespace rpe

@@ -3,6 +3,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 
 namespace rpe {
 namespace {
@@ -50,7 +51,13 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   p->off_stage = off;
   off += p->stages * 2 * kBlockSlots * p->D * eb;
   p->off_rq = off;
-  if (tq) off += align(p->nbt * kRowTile * p->kpitch * eb, 16);
+  p->nrq = p->cross ? 2 * p->S : p->nbt * kRowTile;
+  if (tq) off += align(p->nrq * p->kpitch * eb, 16);
+  // Cross key term: the table's 2S rows as swizzled [32][D] tiles (read per lane)
+  p->off_rkc = off;
+  if (p->cross && ctx && (d->terms & RPE_TERM_K)) off += ((2 * p->S + kRowTile - 1) / kRowTile) * kRowTile * p->D * eb;
+  p->off_bx = off;
+  if (p->cross && d->mode == RPE_MODE_BIAS) off += align(2 * p->S * 4, 16);
   p->zr = (p->S - 1) * p->S + 1;  // 1 when there is no table
   p->p_tab = odd_word_pitch(p->nb, p->gsz);
   p->off_tab = off;
@@ -116,8 +123,50 @@ int validate(const rpe_attn_desc* d) {
     }
   }
   if (!std::isfinite(d->scale)) return RPE_E_PARAMS;
+  if (d->method != RPE_METHOD_PRODUCT && d->method != RPE_METHOD_CROSS) return RPE_E_MODE;
+  // the Cross mapping sums two per-axis encodings: it needs a table and a directed map
+  if (d->method == RPE_METHOD_CROSS && (d->mode == RPE_MODE_NONE || is_undirected(d))) return RPE_E_MODE;
   if (d->head_dim != 16 && d->head_dim != 32 && d->head_dim != 64) return RPE_E_UNSUPPORTED;
+  if (d->table_head_stride < 0) return RPE_E_SHAPE;
+  int64_t in[3], out[3];
+  return io_strides(d, in, out);
+}
+
+int io_strides(const rpe_attn_desc* d, int64_t in[3], int64_t out[3]) {
+  const int64_t N = d->prefix_tokens + static_cast<int64_t>(d->grid_h) * d->grid_w;
+  const int64_t D = d->head_dim;
+  const int64_t eb = d->dtype == RPE_BF16 ? 2 : 4;
+  const int64_t given[2][3] = {{d->stride_b, d->stride_h, d->stride_n},
+                               {d->o_stride_b, d->o_stride_h, d->o_stride_n}};
+  int64_t* res[2] = {in, out};
+  for (int k = 0; k < 2; ++k) {
+    const int64_t* g = given[k];
+    if (g[0] == 0 && g[1] == 0 && g[2] == 0) {
+      res[k][0] = static_cast<int64_t>(d->heads) * N * D;
+      res[k][1] = N * D;
+      res[k][2] = D;
+    } else {
+      if (g[0] <= 0 || g[1] <= 0 || g[2] < D) return RPE_E_SHAPE;
+      for (int i = 0; i < 3; ++i) res[k][i] = g[i];
+    }
+    for (int i = 0; i < 3; ++i)
+      if ((res[k][i] * eb) % 16) return RPE_E_ALIGN;
+    // one (batch, head) slice is addressed with 32-bit byte offsets, and token
+    // rows with 24-bit multiplies
+    if (((N - 1) * res[k][2] + D) * eb >= (int64_t{1} << 31)) return RPE_E_SHAPE;
+    if (res[k][2] * eb >= (int64_t{1} << 24)) return RPE_E_SHAPE;
+  }
   return RPE_OK;
+}
+
+bool contiguous_io(const rpe_attn_desc* d) {
+  int64_t in[3], out[3];
+  if (io_strides(d, in, out) != RPE_OK) return false;
+  const int64_t N = d->prefix_tokens + static_cast<int64_t>(d->grid_h) * d->grid_w;
+  const int64_t D = d->head_dim;
+  for (const int64_t* s : {in, out})
+    if (s[0] != static_cast<int64_t>(d->heads) * N * D || s[1] != N * D || s[2] != D) return false;
+  return true;
 }
 
 int table_geometry(const rpe_attn_desc* d, int* half, int* S, int* nb) {
@@ -136,7 +185,8 @@ int table_geometry(const rpe_attn_desc* d, int* half, int* S, int* nb) {
   if (static_cast<int64_t>(s) * s > 32767) return RPE_E_BUCKETS;
   if (half) *half = h;
   if (S) *S = s;
-  if (nb) *nb = is_undirected(d) ? s : s * s;   // undirected: one index per pair
+  // undirected: one index per pair; Cross: a row-offset and a column-offset half
+  if (nb) *nb = is_undirected(d) ? s : (d->method == RPE_METHOD_CROSS ? 2 * s : s * s);
   return RPE_OK;
 }
 
@@ -169,9 +219,20 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   std::memset(p, 0, sizeof(*p));
   if (d->mode == RPE_MODE_NONE) {
     p->half = 0; p->S = 1; p->nb = 1;  // no table
+    p->ntr = 1;
   } else {
-    st = table_geometry(d, &p->half, &p->S, &p->nb);
+    st = table_geometry(d, &p->half, &p->S, &p->ntr);
     if (st != RPE_OK) return st;
+    p->nb = p->S * p->S;   // Product buckets (the gather entries of either method)
+  }
+  p->cross = d->method == RPE_METHOD_CROSS ? 1 : 0;
+  {
+    int64_t in[3], out[3];
+    st = io_strides(d, in, out);
+    if (st != RPE_OK) return st;
+    p->sb = in[0]; p->sh = in[1]; p->sn = in[2];
+    p->osb = out[0]; p->osh = out[1]; p->osn = out[2];
+    p->rbi = static_cast<uint32_t>(in[2] * (d->dtype == RPE_BF16 ? 2 : 4));
   }
   p->dtype = d->dtype;
   p->mode = d->mode;
@@ -199,7 +260,11 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   p->c = static_cast<float>(s * log2e);
   p->bias_mul = static_cast<float>(log2e);
   if (d->tables_per_head) {
-    p->tab_head_stride = d->mode == RPE_MODE_BIAS ? (int64_t)p->nb : (int64_t)p->nb * p->D;
+    const int64_t packed = d->mode == RPE_MODE_BIAS ? (int64_t)p->ntr : (int64_t)p->ntr * p->D;
+    if (d->table_head_stride != 0 && d->table_head_stride < packed) return RPE_E_SHAPE;
+    p->tab_head_stride = d->table_head_stride != 0 ? d->table_head_stride : packed;
+    // rows of a vector table are read with 16-byte loads
+    if (d->mode == RPE_MODE_CONTEXTUAL && (p->tab_head_stride * p->elem_bytes) % 16) return RPE_E_ALIGN;
   }
 
   // thresholds of g over the unit's offsets 0 .. max(R, C) - 1
@@ -298,7 +363,7 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   {
     const int tile = kRowTile * best.D * best.elem_bytes;
     // (bf16 only: the kernel holds the products of up to 3 tiles in registers)
-    best.rk_lds = (d->mode == RPE_MODE_CONTEXTUAL && (d->terms & RPE_TERM_K) && d->dtype == RPE_BF16 && best.nbt <= 3 &&
+    best.rk_lds = (!best.cross && d->mode == RPE_MODE_CONTEXTUAL && (d->terms & RPE_TERM_K) && d->dtype == RPE_BF16 && best.nbt <= 3 &&
                    best.nbt * tile <= best.NW * kRowTile * best.p_tab * best.gsz && best.off_tab % 16 == 0)
                       ? 1 : 0;
   }
@@ -311,6 +376,7 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   best.inv_c = 1.0f / best.c;
   best.vw_mg = static_cast<uint32_t>(((uint64_t{1} << 32) + best.S * best.gsz - 1) / (best.S * best.gsz));
   best.vw_ms = static_cast<uint32_t>(((uint64_t{1} << 32) + best.S - 1) / best.S);
+  best.dv_S = make_fastdiv(static_cast<uint32_t>(best.S));
   *p = best;
   return RPE_OK;
 }

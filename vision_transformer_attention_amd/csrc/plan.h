@@ -74,6 +74,16 @@ struct Params {
   float c;                // logit scale * log2(e)   (contextual: applies to all terms)
   float bias_mul;         // log2(e) (bias mode: the bias is added after the scale)
   int64_t tab_head_stride;    // elements between heads of a table (0: shared)
+  // Cross mapping: tables hold 2S rows, the row-offset half then the column-offset
+  // half; every product with the table row of Product bucket b takes rows b / S and
+  // S + b % S instead (never a summed row)
+  int cross;
+  int ntr;                    // table rows: nb (Product) or 2S (Cross)
+  FastDiv dv_S;               // S
+  // element strides of q, k, v (shared) and of o, and the bytes between
+  // consecutive tokens of q, k, v (the direct-to-LDS offsets are 32-bit)
+  int64_t sb, sh, sn, osb, osh, osn;
+  uint32_t rbi;
   // key-slot geometry
   int Wp, lwp;            // padded row width and its log2
   int prefix_in_tail;     // prefix keys live in the pad columns of the last grid row
@@ -97,7 +107,10 @@ struct Params {
   int gsz;
   int off_stage;          // stages x {K tile, V tile}, each [32][D] row-major, swizzled
   int kpitch;             // row pitch (elements) of the staged query-term table
-  int off_rq;             // query-term table staged as [nbt*32][kpitch]
+  int off_rq;             // query-term table staged as [nrq][kpitch]
+  int nrq;                // staged query-term table rows: nbt*32 (Product) or 2S (Cross)
+  int off_rkc;            // Cross key term: the 2S table rows as swizzled 32-row tiles
+  int off_bx;             // Cross bias: the head's 2S entries (float32)
   int off_tab;            // gather target: per-row bucket scores (contextual) or bias table
   int p_tab;              // row pitch (gather entries) of the per-row bucket scores
   int zr;                 // entries of each guard region: (S-1)*S + 1
@@ -133,8 +146,16 @@ inline bool is_undirected(const rpe_attn_desc* d) {
   return d->mode != RPE_MODE_NONE && d->map >= RPE_MAP_EUCLIDEAN && d->map <= RPE_MAP_QUANTIZED_SQUARED;
 }
 
-// Table geometry; returns an rpe_status.
+// Table geometry; returns an rpe_status.  nb = table rows: S*S (Product), 2S
+// (Cross) or S (undirected).
 int table_geometry(const rpe_attn_desc* d, int* half, int* S, int* nb);
+
+// Element strides of q/k/v and of o after the all-zero default; returns an rpe_status
+// (validates sign, alignment and the 31-bit span of one (batch, head) slice).
+int io_strides(const rpe_attn_desc* d, int64_t in[3], int64_t out[3]);
+
+// True when the descriptor's strides are the contiguous [B][H][N][d] ones.
+bool contiguous_io(const rpe_attn_desc* d);
 
 // g(x) of one integer offset in float64 (the same formula the device evaluates).
 int axis_index_host(int x, int map, int rounding, double alpha, double beta, double gamma);

@@ -10,10 +10,11 @@ Two inputs are understood:
   (in dispatch order) of the kernels whose name contains SUBSTR: the timed
   launches of one workload when several workloads share a kernel instance.
 * ``--pmc DIR``: the ``*counter_collection.csv`` of a ``rocprofv3 --pmc
-  FETCH_SIZE`` (or ``WRITE_SIZE``) run of ``bench.py --copy-probe MIB``; prints
-  the counter per dispatch of the attention kernel and of the plain copy
-  probe that ran after it, the copy's scale factor (counter / known bytes) and
-  the attention kernel's scaled bytes per launch.
+  FETCH_SIZE`` (or ``WRITE_SIZE``) run of ``bench.py --calib-probe MIB``;
+  prints the counter per dispatch of the attention kernel and of the probe
+  that calibrates it (a read-only sum for FETCH_SIZE, a write-only fill for
+  WRITE_SIZE), the probe's scale factor (counter / known bytes) and the
+  attention kernel's scaled bytes per launch.
 
 ``kernel_source_hash()`` is the SHA-256 of the sources that decide what the
 forward kernel reads and writes; a traffic figure is only reported for the
@@ -42,7 +43,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-_FWD = re.compile(r"_ZN3rpe14rpe_fwd_kernelI(DF16b|f)Li(\d+)ELi(\d)ELj(\d)ELb(\d)ELb(\d)EEEvNS_6ParamsE")
+_FWD = re.compile(r"_ZN3rpe14rpe_fwd_kernelI(DF16b|f)Li(\d+)ELi(\d)ELj(\d)ELb(\d)ELb(\d)ELb(\d)EEEvNS_6ParamsE")
 _MODES = {"0": "none", "1": "bias", "2": "contextual"}
 
 
@@ -51,11 +52,11 @@ def fwd_name(name):
     m = _FWD.search(name)
     if not m:
         return None
-    dt, d, mode, terms, wide, multi = m.groups()
+    dt, d, mode, terms, wide, multi, cross = m.groups()
     t = "".join(c for bit, c in ((1, "K"), (2, "Q"), (4, "V")) if int(terms) & bit)
     return (f"rpe_fwd_kernel<{'bf16' if dt == 'DF16b' else 'fp32'}, d{d}, {_MODES[mode]}"
             f"{' ' + t if t else ''}{', wide rows' if wide == '1' else ''}"
-            f"{', several units per workgroup' if multi == '1' else ''}>")
+            f"{', several units per workgroup' if multi == '1' else ''}{', Cross' if cross == '1' else ''}>")
 
 
 def demangle(names):
@@ -103,32 +104,43 @@ def trace_summary(d, substr, skip, count):
             f"avg {sum(us) / len(us):.2f} us, min {min(us):.2f}, max {max(us):.2f}")
 
 
-def pmc_summary(d, copy_mib):
+def pmc_summary(d, probe_mib):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the forward kernel, scaled by what the
+    same counter reads for the calibration probes that ran after it (``bench.py
+    --calib-probe MIB``): a sum that reads MIB MiB (FETCH_SIZE) and a fill that
+    writes MIB MiB (WRITE_SIZE)."""
     rows = list(csv.DictReader(open(_one("*counter_collection.csv", d))))
     by = collections.defaultdict(lambda: collections.defaultdict(list))
     last_fwd = max((int(r["Dispatch_Id"]) for r in rows if FWD_KERNEL in r["Kernel_Name"]), default=-1)
     counters = sorted({r["Counter_Name"] for r in rows})
     for r in rows:
         name = r["Kernel_Name"]
+        after = int(r["Dispatch_Id"]) > last_fwd
         if FWD_KERNEL in name:
             key = demangle([name])[0]
-        elif "copyBuffer" in name and int(r["Dispatch_Id"]) > last_fwd:
-            key = "copy probe"
+        elif after and "reduce_kernel" in name:
+            key = "read probe"
+        elif after and "FillFunctor" in name:
+            key = "write probe"
         else:
             continue
         by[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
     out = []
-    copy_bytes = copy_mib * (1 << 20)
+    probe_bytes = probe_mib * (1 << 20)
+    probe_of = {"FETCH_SIZE": "read probe", "WRITE_SIZE": "write probe"}
     for c in counters:
-        copy_vals = by.get("copy probe", {}).get(c, [])
+        probe = probe_of.get(c)
+        vals = by.get(probe, {}).get(c, []) if probe else []
         factor = None
-        if copy_vals:
-            factor = (sum(copy_vals) / len(copy_vals)) * 1024.0 / copy_bytes
-            out.append(f"copy probe ({copy_mib} MiB read + {copy_mib} MiB written): {c} mean "
-                       f"{sum(copy_vals) / len(copy_vals):.1f} KiB over {len(copy_vals)} dispatches; "
+        if vals:
+            # a sum may take more than one dispatch per pass: count per pass (3 passes)
+            per_pass = sum(vals) / 3.0
+            factor = per_pass * 1024.0 / probe_bytes
+            out.append(f"{probe} ({probe_mib} MiB {'read' if probe == 'read probe' else 'written'} per pass, "
+                       f"3 passes, {len(vals)} dispatches): {c} {per_pass:.1f} KiB per pass; "
                        f"factor = {factor:.4f} (counter / known bytes)")
         for k, cs in by.items():
-            if k == "copy probe" or c not in cs:
+            if k in ("read probe", "write probe") or c not in cs:
                 continue
             v = cs[c]
             mean_kib = sum(v) / len(v)
@@ -146,7 +158,7 @@ def main():
     ap.add_argument("--kernel", default=FWD_KERNEL)
     ap.add_argument("--skip", type=int, default=0)
     ap.add_argument("--count", type=int, default=1)
-    ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--probe-mib", type=int, default=256)
     ap.add_argument("--hash", action="store_true", help="print the forward kernel's source hash")
     a = ap.parse_args()
     if a.hash:
@@ -156,7 +168,7 @@ def main():
     if a.trace:
         print(trace_summary(a.trace, a.kernel, a.skip, a.count))
     if a.pmc:
-        print(pmc_summary(a.pmc, a.copy_mib))
+        print(pmc_summary(a.pmc, a.probe_mib))
 
 
 if __name__ == "__main__":
