@@ -261,6 +261,23 @@ rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k,
                         float* drq, float* drk, float* drv, void* workspace, uint64_t workspace_bytes,
                         void* stream);
 
+/* rpe_attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It allocates nothing: its workspace is a device array
+ * of RPE_BWD_NOALLOC_MAX_BYTES that the library holds on every GPU it runs on
+ * from the first load of its device code until the process ends.  Calls whose
+ * rpe_attn_bwd_workspace_size exceeds that return RPE_E_SHAPE before any device
+ * call.  Every call on a GPU shares that GPU's array (the kernels write every
+ * part they read, so nothing carries over between calls): calls that overlap on
+ * one GPU, on different streams or threads, race and give wrong results.  The
+ * stream's device decides which GPU's array is used.  Results, errors and
+ * asynchrony are those of rpe_attn_bwd. */
+#define RPE_BWD_NOALLOC_MAX_BYTES ((uint64_t)64 << 20)
+rpe_status rpe_attn_bwd_noalloc(const rpe_attn_desc* desc, const void* q, const void* k, const void* v,
+                                const void* dout, const float* lse, const float* bias, const void* rq,
+                                const void* rk, const void* rv, float* dq, float* dk, float* dv, float* dbias,
+                                float* drq, float* drk, float* drv, void* stream);
+
 /* Static string for a status code. */
 const char* rpe_status_str(int32_t status);
 

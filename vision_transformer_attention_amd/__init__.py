@@ -17,6 +17,7 @@ from .attention import (  # noqa: F401
     rpe_attn_axis_index,
     rpe_attn_bucket_map,
     rpe_attn_bwd,
+    rpe_attn_bwd_noalloc,
     rpe_attn_cross_to_product,
     rpe_attn_fwd,
     rpe_attn_num_buckets,

@@ -30,7 +30,9 @@ STATUS_NAMES = {
 # Every symbol include/rpe_attn.h declares.
 EXPORTS = ("rpe_attn_validate", "rpe_attn_num_buckets", "rpe_attn_unit_size", "rpe_attn_axis_index",
            "rpe_attn_bucket_map", "rpe_attn_cross_to_product", "rpe_attn_undirected_to_product", "rpe_attn_fwd",
-           "rpe_attn_bwd_workspace_size", "rpe_attn_bwd", "rpe_status_str", "rpe_attn_version")
+           "rpe_attn_bwd_workspace_size", "rpe_attn_bwd", "rpe_attn_bwd_noalloc", "rpe_status_str",
+           "rpe_attn_version")
+BWD_NOALLOC_MAX_BYTES = 64 << 20
 
 
 class Desc(ctypes.Structure):
@@ -92,6 +94,8 @@ def load():
         lib.rpe_attn_bwd_workspace_size.restype = i32
         lib.rpe_attn_bwd.argtypes = [P(Desc)] + [vp] * 17 + [ctypes.c_uint64, vp]
         lib.rpe_attn_bwd.restype = i32
+        lib.rpe_attn_bwd_noalloc.argtypes = [P(Desc)] + [vp] * 16 + [vp]
+        lib.rpe_attn_bwd_noalloc.restype = i32
         lib.rpe_attn_fwd.restype = i32
         lib.rpe_status_str.argtypes = [i32]
         lib.rpe_status_str.restype = ctypes.c_char_p

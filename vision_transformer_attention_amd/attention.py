@@ -335,6 +335,14 @@ def prepare_bwd(q, k, v, dout, lse, **kw):
     return g, PreparedBwd(desc, args, keep, q.device)
 
 
+def rpe_attn_bwd_noalloc(q, k, v, dout, lse, **kw):
+    """rpe_attn_bwd through the allocation-free entry point: the library's own
+    device workspace (at most ``_lib.BWD_NOALLOC_MAX_BYTES``) instead of a
+    caller workspace; only the gradient tensors are allocated here.  Calls that
+    overlap on one GPU race (they share that workspace)."""
+    return _bwd(q, k, v, dout, lse, noalloc=True, **kw)[0]
+
+
 def rpe_attn_bwd(q, k, v, dout, lse, **kw):
     """Gradients of rpe_attn_fwd's output for the output gradient ``dout``.
 
@@ -346,7 +354,7 @@ def rpe_attn_bwd(q, k, v, dout, lse, **kw):
 
 def _bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
          alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None, rq=None, rk=None,
-         rv=None, method="product"):
+         rv=None, method="product", noalloc=False):
     torch = _torch()
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, dout)):
         raise ValueError("q, k, v, dout must be [B, H, N, d] of one shape")
@@ -371,7 +379,7 @@ def _bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="none", te
     _check_geometry_and_tables(desc, q, mode, terms, per_head, bias, rq, rk, rv)
     nbytes = ctypes.c_uint64()
     check("rpe_attn_bwd_workspace_size", load().rpe_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
-    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)
+    ws = None if noalloc else torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=q.device)
     f32 = dict(dtype=torch.float32, device=q.device)
     g = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(q.shape, **f32), "dv": torch.empty(q.shape, **f32)}
     use = {"bias": mode == "bias", "rq": mode == "contextual" and "q" in terms,
@@ -386,7 +394,10 @@ def _bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="none", te
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
             _ptr(bias if use["bias"] else None), _ptr(rq if use["rq"] else None),
             _ptr(rk if use["rk"] else None), _ptr(rv if use["rv"] else None),
-            gp("dq"), gp("dk"), gp("dv"), gp("dbias"), gp("drq"), gp("drk"), gp("drv"),
-            _ptr(ws), ctypes.c_uint64(nbytes.value)]
+            gp("dq"), gp("dk"), gp("dv"), gp("dbias"), gp("drq"), gp("drk"), gp("drv")]
+    if noalloc:
+        check("rpe_attn_bwd_noalloc", load().rpe_attn_bwd_noalloc(ctypes.byref(desc), *args, _stream(q.device)))
+        return g, desc, args, (q, k, v, dout, lse, g, tabs)
+    args += [_ptr(ws), ctypes.c_uint64(nbytes.value)]
     check("rpe_attn_bwd", load().rpe_attn_bwd(ctypes.byref(desc), *args, _stream(q.device)))
     return g, desc, args, (q, k, v, dout, lse, ws, g, tabs)

@@ -304,6 +304,22 @@ rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k,
   return e == hipSuccess ? RPE_OK : RPE_E_HIP;
 }
 
+static_assert(RPE_BWD_NOALLOC_MAX_BYTES == rpe::kBwdScratchBytes, "the header states the scratch size");
+
+rpe_status rpe_attn_bwd_noalloc(const rpe_attn_desc* desc, const void* q, const void* k, const void* v,
+                                const void* dout, const float* lse, const float* bias, const void* rq,
+                                const void* rk, const void* rv, float* dq, float* dk, float* dv, float* dbias,
+                                float* drq, float* drk, float* drv, void* stream) {
+  uint64_t need = 0;
+  const rpe_status st = rpe_attn_bwd_workspace_size(desc, &need);
+  if (st != RPE_OK) return st;
+  if (need > rpe::kBwdScratchBytes) return RPE_E_SHAPE;
+  void* ws = nullptr;
+  if (rpe::bwd_scratch(stream, &ws) != hipSuccess) return RPE_E_HIP;
+  return rpe_attn_bwd(desc, q, k, v, dout, lse, bias, rq, rk, rv, dq, dk, dv, dbias, drq, drk, drv, ws,
+                      rpe::kBwdScratchBytes, stream);
+}
+
 const char* rpe_status_str(int32_t status) {
   switch (status) {
     case RPE_OK: return "ok";

@@ -33,4 +33,12 @@ struct BwdArgs {
   float scale;              // logit scale s
 };
 
+// Workspace of the allocation-free backward (rpe_attn_bwd_noalloc): a device
+// array of this many bytes per GPU, owned by the library (bwd.hip).
+constexpr uint64_t kBwdScratchBytes = uint64_t{64} << 20;
+
+// Device address of that array on the device `stream` (a hipStream_t, NULL: the
+// current device) belongs to; looked up once per device.  Returns a hipError_t.
+int bwd_scratch(void* stream, void** ptr);
+
 }  // namespace rpe

@@ -16,6 +16,8 @@
 // buffers hold the per-row bucket scores q_i . rK[b], k_j . rQ[b], dO_i . rV[b].
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include <cmath>
 #include <cstdint>
 
@@ -921,6 +923,51 @@ unsigned blocks_for(int64_t n) {
 }
 
 }  // namespace
+
+// The allocation-free backward's workspace: one array per GPU, allocated with
+// the library's device code and held until the process ends.  Host code must
+// not pass the array's name to a kernel (that is a host-side stand-in): it uses
+// the device address bwd_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+int bwd_scratch(void* stream, void** ptr) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd);
+    if (e != hipSuccess) return e;
+    dev = static_cast<int>(sd);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the symbol's address on `dev`, looked up with that device current
+    if (dev != cur) {
+      e = hipSetDevice(dev);
+      if (e != hipSuccess) return e;
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.n_units == 0) return hipSuccess;
