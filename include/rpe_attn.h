@@ -169,9 +169,13 @@ rpe_status rpe_attn_axis_index(const rpe_attn_desc* desc, int32_t length, int16_
 /* Bucket id of every ordered pair of one unit, [T][T] int16 row-major (query
  * rows, key columns), -1 where a prefix token takes part, written to device
  * memory by a kernel on `stream`.  All units of a descriptor share this map
- * (bucket ids depend only on offsets: Swin 2D RPE post, section 2.2).  The id
- * is the Product id (g(dy)+H)*S + g(dx)+H for either method (under Cross it
- * names the two rows, by id / S and S + id % S).  Requires T*T <= 2^31 - 1. */
+ * (bucket ids depend only on offsets: Swin 2D RPE post, section 2.2).  For a
+ * directed map the id is the Product id (g(dy)+H)*S + g(dx)+H for either method
+ * (under Cross it names the two rows, by id / S and S + id % S); for an
+ * undirected map it is the table row u(dy, dx) + H (iRPE page, eqs. 19-21,
+ * indices in float64).  Requires T*T <= 2^31 - 1 (RPE_E_SHAPE); undirected
+ * maps also S'*S' <= 32767 as for rpe_attn_undirected_to_product
+ * (RPE_E_BUCKETS). */
 rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void* stream);
 
 /* Cross mapping (iRPE page, Method, "Cross", eqs. 22-24): the encoding of a
@@ -227,21 +231,25 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
                         void* o, float* lse, void* stream);
 
 /* Backward pass: gradients of o = rpe_attn_fwd(...) for a given dO = dL/do, with
- * respect to q, k, v and every table the descriptor uses (product maps, i.e.
- * RPE_MAP_SWIN or RPE_MAP_PIECEWISE; RPE_E_MODE for an undirected map).  Per
- * unit, with P the softmax weights recomputed from `lse` and s the logit scale:
+ * respect to q, k, v and every table the descriptor uses, for every map and
+ * method (an undirected map's tables as they are, not expanded).  Per unit, with
+ * P the softmax weights recomputed from `lse`, s the logit scale and b the
+ * table row a pair reads (Cross: each pair reads two rows, its row-offset row
+ * and its column-offset row, and every term below goes to both):
  *   dP_ij = dO_i . (v_j + [V] rV[b]),  dL_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
  *   dq_i = s sum_j dL_ij (k_j + [K] rK[b]),  dk_j = s sum_i dL_ij (q_i + [Q] rQ[b]),
  *   dv_j = sum_i P_ij dO_i,  drK[b] = s sum dL_ij q_i,  drQ[b] = s sum dL_ij k_j,
- *   drV[b] = sum P_ij dO_i,  dbias[b] = sum dL_ij     (sums over the pairs of bucket b;
- *   a shared table sums over heads)
- * (the gradient of the definition of iRPE page, Method, eqs. 13-17 and the Swin
- * relative-bias record, "The claim").
+ *   drV[b] = sum P_ij dO_i,  dbias[b] = sum dL_ij     (sums over the pairs that read
+ *   row b; a shared table sums over heads)
+ * (the gradient of the definition of iRPE page, Method, eqs. 13-17 and 22-24, and
+ * the Swin relative-bias record, "The claim").
  *   q, k, v, dout : [B][H][N][d], desc.dtype;  lse: [B][H][N] float32 from rpe_attn_fwd
- *   bias, rq, rk, rv : as for rpe_attn_fwd (NULL where unused)
+ *   bias, rq, rk, rv : as for rpe_attn_fwd, for this descriptor's map and method
+ *                   (rows from rpe_attn_num_buckets; NULL where unused)
  *   dq, dk, dv    : [B][H][N][d] float32, written
- *   dbias         : [H|1][S*S] float32, written in bias mode (else ignored)
- *   drq, drk, drv : [H|1][S*S][d] float32, written for the terms present (else ignored)
+ *   dbias         : [H|1][rows] float32, written in bias mode (else ignored)
+ *   drq, drk, drv : [H|1][rows][d] float32, written for the terms present (else
+ *                   ignored); rows no pair reads get 0
  *   workspace     : device, at least rpe_attn_bwd_workspace_size() bytes, caller-owned;
  *                   it holds the weights and score gradients of every unit (2 B H U T^2
  *                   floats) and per-row bucket sums
@@ -253,7 +261,9 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
  * in the workspace's weight region (B H U nb (terms x d + 1) <= B H U T^2 floats), and
  * with float atomics otherwise, when their last bits can vary from call to call.
  * Asynchronous on `stream`.  Errors: descriptor validation; RPE_E_NULL for a
- * missing pointer; RPE_E_SHAPE if the workspace is too small or T*T >= 2^31. */
+ * missing pointer; RPE_E_SHAPE if the workspace is too small or T*T >= 2^31;
+ * RPE_E_BUCKETS for an undirected map with S'*S' > 32767 (see
+ * rpe_attn_undirected_to_product). */
 rpe_status rpe_attn_bwd_workspace_size(const rpe_attn_desc* desc, uint64_t* bytes);
 rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* bias, const void* rq,

@@ -167,10 +167,13 @@ def test_undirected_maps_geometry_and_rejections(m):
     assert pkg.rpe_attn_validate(d) == 0
     spec = Spec(14, 14, prefix=1, mode="contextual", terms={"k"}, map=m, alpha=1.9, beta=3.8, gamma=15.2)
     assert pkg.rpe_attn_num_buckets(d) == num_buckets(spec) == (4, 9, 9)
-    # the forward and the per-axis tools take the expanded tables only
+    # the forward and the per-axis tools take the expanded tables only; the pair
+    # map (rows u + H) and the backward take the undirected tables as they are
     assert lib.rpe_attn_fwd(ctypes.byref(d), one, one, one, None, None, one, None, one, None, None) == -4
-    assert lib.rpe_attn_bucket_map(ctypes.byref(d), one, None) == -4
+    assert lib.rpe_attn_bucket_map(ctypes.byref(d), None, None) == -1
     assert lib.rpe_attn_axis_index(ctypes.byref(d), 5, one, None) == -4
+    n = ctypes.c_uint64()
+    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
     assert lib.rpe_attn_cross_to_product(ctypes.byref(d), _lib.RPE_TABLE_VECTOR, one, one, None) == -4
     f = lib.rpe_attn_undirected_to_product
     assert f(ctypes.byref(d), _lib.RPE_TABLE_VECTOR, None, one, None) == -1
@@ -178,6 +181,8 @@ def test_undirected_maps_geometry_and_rejections(m):
     big = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(100, 100), mode="bias", map=m,
                         alpha=1.9, beta=3.8, gamma=15.2)
     assert f(ctypes.byref(big), _lib.RPE_TABLE_BIAS, one, one, None) == -6     # 199^2 raw offsets
+    assert lib.rpe_attn_bucket_map(ctypes.byref(big), one, None) == -6
+    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(big), ctypes.byref(n)) == -6
     pw = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), mode="bias", map="piecewise",
                        alpha=1.9, beta=3.8, gamma=15.2)
     assert f(ctypes.byref(pw), _lib.RPE_TABLE_BIAS, one, one, None) == -4       # not undirected
@@ -249,9 +254,16 @@ def test_method_validation_and_geometry():
     assert pkg.rpe_attn_validate(pkg.make_desc(mode="none", method="cross", **kw)) == -4
     assert pkg.rpe_attn_validate(pkg.make_desc(mode="bias", map="euclidean", method="cross", **kw)) == -4
     assert pkg.rpe_attn_validate(pkg.make_desc(mode="bias", map="piecewise", method=2, **kw)) == -4
-    # the backward takes the Product method and contiguous tensors only
+    # the backward takes either method, and contiguous tensors only; under Cross
+    # its workspace holds a second pair-to-row map ([T][T] int16, 256-byte aligned)
     n = ctypes.c_uint64()
-    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(cross), ctypes.byref(n)) == -4
+    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(cross), ctypes.byref(n)) == 0
+    m = ctypes.c_uint64()
+    prod = pkg.make_desc(mode="contextual", terms="k", map="piecewise", **kw)
+    assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(prod), ctypes.byref(m)) == 0
+    t = 197
+    rows_bytes = lambda rows: (2 * t * rows * 4 + 255) // 256 * 256     # B H U T rows floats
+    assert n.value - m.value == (t * t * 2 + 255) // 256 * 256 + rows_bytes(18) - rows_bytes(81)
     strided = pkg.make_desc(mode="contextual", terms="k", map="piecewise",
                             strides=(197 * 3 * 2 * 64, 64, 3 * 2 * 64), **kw)
     assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(strided), ctypes.byref(n)) == -8

@@ -29,7 +29,8 @@ def dev():
 
 def _spec(w):
     return Spec(w.grid_h, w.grid_w, window=w.window, prefix=w.prefix, mode=w.mode, terms=w.terms, map=w.map,
-                alpha=w.alpha, beta=w.beta, gamma=w.gamma, reading=w.reading, tables_per_head=w.tables_per_head)
+                alpha=w.alpha, beta=w.beta, gamma=w.gamma, reading=w.reading, tables_per_head=w.tables_per_head,
+                method=w.method)
 
 
 def _fit(w):
@@ -72,6 +73,32 @@ CASES = [
     ("contextual Q, 289 buckets, 9x9 + cls, bf16 d64", _D.resized(batch=1, heads=2, grid_h=9, grid_w=9,
                                                                    terms=frozenset("q"), alpha=3.8, beta=7.6,
                                                                    gamma=30.4)),
+    # Cross mapping (2S-row tables, each pair reads a row-offset and a column-offset row)
+    ("cross contextual K, global 14x14 + cls, bf16", _D.resized(batch=1, heads=2, method="cross")),
+    ("cross bias, 7x7 windows, per head, bf16", _S.resized(batch=2, heads=3, grid_h=14, grid_w=14,
+                                                            method="cross")),
+    ("cross contextual KQV, 4x4 windows, fp32 d16", _D.resized(batch=2, heads=2, head_dim=16, grid_h=8,
+                                                                grid_w=8, window=4, prefix=0,
+                                                                terms=frozenset("kqv"), dtype="fp32",
+                                                                method="cross")),
+    ("cross contextual QV, 9x13, per head, bf16 d32", _D.resized(batch=1, heads=3, head_dim=32, grid_h=9,
+                                                                  grid_w=13, prefix=0, terms=frozenset("qv"),
+                                                                  tables_per_head=True, method="cross")),
+    ("cross contextual KQV, 6x7 + cls, bf16 d16", _D.resized(batch=2, heads=2, head_dim=16, grid_h=6, grid_w=7,
+                                                             terms=frozenset("kqv"), method="cross")),
+    # undirected maps (S-row tables, rows u + H; rows below H are read by no pair)
+    ("euclidean bias, 14x14 + cls, per head, bf16", _D.resized(batch=1, heads=2, mode="bias",
+                                                               terms=frozenset(), map="euclidean",
+                                                               tables_per_head=True)),
+    # (the forward runs an undirected map on its expansion over raw offsets: 11 x 11 rows here)
+    ("quantized contextual KV, 5x6 + cls, fp32", _D.resized(batch=2, heads=2, grid_h=5, grid_w=6,
+                                                            terms=frozenset("kv"), map="quantized",
+                                                            dtype="fp32")),
+    ("euclidean (rounded) contextual KQV, 7x7 windows, bf16 d32",
+     _D.resized(batch=1, heads=2, head_dim=32, grid_h=14, grid_w=14, window=7, prefix=0, terms=frozenset("kqv"),
+                map="euclidean_rounded")),
+    ("quantized (squared) contextual K, 14x14 + cls, bf16", _D.resized(batch=1, heads=2,
+                                                                      map="quantized_squared")),
 ]
 
 
@@ -90,7 +117,8 @@ def test_backward_parity(dev, label, w):
     td = torch.from_numpy(dout).to(tdt).to(dev)
     kw = dict(grid=(w.grid_h, w.grid_w), window=w.window, prefix_tokens=w.prefix, mode=w.mode,
               terms="".join(sorted(w.terms)), map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma,
-              rounding=w.reading, bias=t.get("bias"), rq=t.get("rq"), rk=t.get("rk"), rv=t.get("rv"))
+              rounding=w.reading, bias=t.get("bias"), rq=t.get("rq"), rk=t.get("rk"), rv=t.get("rv"),
+              method=w.method)
     _, lse = pkg.rpe_attn_fwd(t["q"], t["k"], t["v"], return_lse=True, **kw)
     g = pkg.rpe_attn_bwd(t["q"], t["k"], t["v"], td, lse, **kw)
     torch.cuda.synchronize()
@@ -104,15 +132,6 @@ def test_backward_parity(dev, label, w):
         err = float(np.abs(got - ref[n]).max())
         print(f"    {n}: max err {err:.3e}  (max |ref| {scale:.3e}, rel tol {REL[w.dtype]})", flush=True)
         assert np.isfinite(got).all() and err <= REL[w.dtype] * scale, (n, err, scale)
-
-
-def test_backward_rejects_undirected_map(dev):
-    import ctypes
-    import vision_transformer_attention_amd as pkg
-    d = pkg.make_desc(batch=1, heads=1, head_dim=16, grid=(4, 4), mode="bias", map="euclidean", alpha=1.0,
-                      beta=2.0, gamma=4.0)
-    n = ctypes.c_uint64()
-    assert pkg.load().rpe_attn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -4
 
 
 def test_backward_binding_rejects_mismatched_inputs(dev):

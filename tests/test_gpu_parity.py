@@ -124,6 +124,51 @@ def test_bucket_map_bit_exact(dev, name, reading):
     assert (got.astype(np.int64) == ref).all()
 
 
+@pytest.mark.parametrize("m", ["euclidean", "euclidean_rounded", "quantized", "quantized_squared"])
+@pytest.mark.parametrize("gh,gw,window,prefix,abg", [(14, 14, 0, 1, (1.9, 3.8, 15.2)),
+                                                     (9, 23, 0, 0, (1.0, 2.0, 8.0)),
+                                                     (14, 14, 7, 0, (1.9, 3.8, 15.2)),
+                                                     (91, 91, 0, 0, (3.8, 7.6, 30.4))])
+def test_undirected_pair_rows_bit_exact(dev, m, gh, gw, window, prefix, abg):
+    # Under an undirected map the bucket map names each pair's table row
+    # u(dy, dx) + H (iRPE page, Method, eqs. 19-21), evaluated on the device in
+    # float64; the oracle evaluates each distinct offset on its own.  91 x 91 is
+    # the largest grid the device tabulation takes.
+    import vision_transformer_attention_amd as pkg
+    from oracle.attention import pair_rows_arrays
+    a, b, g = abg
+    say("undirected pair rows", m, gh, gw, window, prefix, abg)
+    spec = Spec(gh, gw, window=window, prefix=prefix, mode="bias", map=m, alpha=a, beta=b, gamma=g)
+    d = pkg.make_desc(grid=(gh, gw), window=window, prefix_tokens=prefix, mode="bias", map=m, alpha=a, beta=b,
+                      gamma=g)
+    got = pkg.rpe_attn_bucket_map(d, device=dev).cpu().numpy().astype(np.int64)
+    if gh * gw > 4096:
+        # sampled rows of the oracle's map: every offset of the grid appears in
+        # the rows of the four corner tokens
+        t = gh * gw
+        rows = [0, gw - 1, t - gw, t - 1, t // 2]
+        ref = _undirected_rows(spec, rows)
+        assert (got[rows] == ref).all()
+    else:
+        (ref,) = pair_rows_arrays(spec)
+        assert (got == ref).all()
+
+
+def _undirected_rows(spec, rows):
+    from oracle import num_buckets
+    h, _, _ = num_buckets(spec)
+    gw, t = spec.grid_w, spec.grid_h * spec.grid_w
+    out = np.empty((len(rows), t), dtype=np.int64)
+    cache = {}
+    for r, i in enumerate(rows):
+        for j in range(t):
+            key = (abs(i // gw - j // gw), abs(i % gw - j % gw))
+            if key not in cache:
+                cache[key] = spec.u(*key) + h
+            out[r, j] = cache[key]
+    return out
+
+
 @pytest.mark.parametrize("gh,gw,window,prefix", [(1, 1, 0, 0), (3, 7, 0, 2), (9, 4, 0, 1), (6, 6, 3, 0),
                                                  (8, 12, 4, 0), (5, 5, 0, 16)])
 def test_bucket_map_shapes(dev, gh, gw, window, prefix):

@@ -18,6 +18,11 @@ CASES = [
     Spec(2, 4, prefix=1, mode="contextual", terms={"q", "v"}, map="piecewise", alpha=1.0, beta=2.0, gamma=4.0,
          method="cross"),
     Spec(3, 3, mode="none", scale=0.7),
+    Spec(3, 3, prefix=1, mode="contextual", terms={"k"}, map="piecewise", alpha=1.0, beta=2.0, gamma=4.0,
+         method="cross", tables_per_head=True),
+    Spec(3, 4, mode="bias", map="piecewise", alpha=1.0, beta=2.0, gamma=4.0, method="cross"),
+    Spec(3, 3, prefix=1, mode="bias", map="euclidean", alpha=1.0, beta=2.0, gamma=4.0, tables_per_head=True),
+    Spec(3, 4, mode="contextual", terms={"k", "v"}, map="quantized", alpha=1.0, beta=2.0, gamma=4.0),
 ]
 
 

@@ -348,7 +348,9 @@ def rpe_attn_bwd(q, k, v, dout, lse, **kw):
 
     ``lse`` is the float32 log-sum-exp the forward returned (return_lse=True).
     Returns a dict of float32 tensors: dq, dk, dv and, for the tables the mode
-    and terms use, dbias / drq / drk / drv (Product maps only)."""
+    and terms use, dbias / drq / drk / drv, shaped as those tables (for every
+    map and method: Cross tables of 2S rows and undirected tables of S rows
+    are taken and differentiated as they are)."""
     return _bwd(q, k, v, dout, lse, **kw)[0]
 
 
@@ -367,15 +369,12 @@ def _bwd(q, k, v, dout, lse, *, grid, window=0, prefix_tokens=0, mode="none", te
     if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous()
             or lse.device != q.device):
         raise ValueError("lse must be contiguous float32 [B, H, N] on the device of q")
-    if map in UNDIRECTED:
-        raise ValueError("the backward takes Product maps only (swin or piecewise)")
-    if method != "product":
-        raise ValueError("the backward takes the Product method only")
     tabs = [t for t in (bias, rq, rk, rv) if t is not None]
     per_head = any(t.shape[0] == H and H > 1 for t in tabs)
     desc = make_desc(batch=B, heads=H, head_dim=d, grid=grid, window=window, prefix_tokens=prefix_tokens,
                      dtype="bf16" if q.dtype == torch.bfloat16 else "fp32", mode=mode, terms=terms, map=map,
-                     alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale, tables_per_head=per_head)
+                     alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale, tables_per_head=per_head,
+                     method=method)
     _check_geometry_and_tables(desc, q, mode, terms, per_head, bias, rq, rk, rv)
     nbytes = ctypes.c_uint64()
     check("rpe_attn_bwd_workspace_size", load().rpe_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))

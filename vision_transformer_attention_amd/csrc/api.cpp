@@ -13,7 +13,7 @@ hipError_t launch_fwd(const Params& p, hipStream_t stream);
 hipError_t launch_axis_index(int length, int map, int rounding, double alpha, double beta,
                              double gamma, int16_t* out, hipStream_t stream);
 hipError_t launch_bucket_map(int P, int R, int C, int half, int S, int map, int rounding,
-                             double alpha, double beta, double gamma, int16_t* out,
+                             double alpha, double beta, double gamma, int16_t* out, int16_t* out1,
                              hipStream_t stream);
 hipError_t launch_cross_to_product(bool bf16, const void* cross, void* product, int S, int width,
                                    int64_t total, hipStream_t stream);
@@ -26,6 +26,16 @@ hipError_t launch_undirected_to_product(bool bf16, bool f32, const void* table, 
 namespace {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// An undirected map's pair rows are tabulated per squared offset length on the
+// device, (R-1)^2 + (C-1)^2 < 16384: the bound that S'*S' <= 32767 for the
+// Swin-map expansion (H' = max(R, C) - 1, S' = 2H'+1) gives as well.
+bool undirected_fits(const rpe_attn_desc* d) {
+  const int R = d->window ? d->window : d->grid_h;
+  const int C = d->window ? d->window : d->grid_w;
+  const int64_t sp = 2 * static_cast<int64_t>(R > C ? R : C) - 1;
+  return sp * sp <= 32767;
+}
 
 }  // namespace
 
@@ -76,7 +86,7 @@ rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void
   int h = 0, s = 0, nb = 0;
   const int st = rpe::table_geometry(desc, &h, &s, &nb);
   if (st != RPE_OK) return static_cast<rpe_status>(st);
-  if (rpe::is_undirected(desc)) return RPE_E_MODE;
+  if (rpe::is_undirected(desc) && !undirected_fits(desc)) return RPE_E_BUCKETS;
   if (!dev_map) return RPE_E_NULL;
   const int R = desc->window ? desc->window : desc->grid_h;
   const int C = desc->window ? desc->window : desc->grid_w;
@@ -84,7 +94,7 @@ rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void
   if (T * T > 2147483647LL) return RPE_E_SHAPE;
   const int map = desc->mode == RPE_MODE_NONE ? RPE_MAP_SWIN : desc->map;
   const hipError_t e = rpe::launch_bucket_map(desc->prefix_tokens, R, C, h, s, map, desc->rounding,
-                                              desc->alpha, desc->beta, desc->gamma, dev_map,
+                                              desc->alpha, desc->beta, desc->gamma, dev_map, nullptr,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RPE_OK : RPE_E_HIP;
 }
@@ -174,10 +184,11 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
 
 namespace {
 
-// Workspace of rpe_attn_bwd: the unit's bucket map, P and dL of every unit and
-// the per-row bucket sums the present terms need, each 256-byte aligned.
+// Workspace of rpe_attn_bwd: the unit's pair-to-table-row map (two under
+// Cross), P and dL of every unit and the per-row table-row sums the present
+// terms need, each 256-byte aligned.
 struct BwdLayout {
-  uint64_t bmap, P, dL, Wq, Wk, Wv, total;
+  uint64_t bmap, bmap1, P, dL, Wq, Wk, Wv, total;
 };
 
 uint64_t up256(uint64_t v) { return (v + 255) / 256 * 256; }
@@ -185,7 +196,7 @@ uint64_t up256(uint64_t v) { return (v + 255) / 256 * 256; }
 int bwd_layout(const rpe_attn_desc* d, BwdLayout* L, int* T_out, int* U_out, int* nb_out) {
   int st = rpe::validate(d);
   if (st != RPE_OK) return st;
-  if (rpe::is_undirected(d) || d->method != RPE_METHOD_PRODUCT) return RPE_E_MODE;
+  if (rpe::is_undirected(d) && !undirected_fits(d)) return RPE_E_BUCKETS;
   // the backward reads packed tables and contiguous [B][H][N][d] tensors
   if (!rpe::contiguous_io(d)) return RPE_E_UNSUPPORTED;
   if (d->tables_per_head && d->table_head_stride != 0) {
@@ -213,7 +224,9 @@ int bwd_layout(const rpe_attn_desc* d, BwdLayout* L, int* T_out, int* U_out, int
   const bool wv = ctx && (d->terms & RPE_TERM_V);
   const uint64_t rows = units * T * static_cast<uint64_t>(nb) * 4;
   uint64_t off = 0;
+  const bool cross = d->method == RPE_METHOD_CROSS;
   L->bmap = off; off += up256(tt * 2);
+  L->bmap1 = cross ? off : ~0ULL; off += cross ? up256(tt * 2) : 0;
   L->P = off; off += up256(units * tt * 4);
   L->dL = off; off += up256(units * tt * 4);
   L->Wq = wq ? off : ~0ULL; off += wq ? up256(rows) : 0;
@@ -266,6 +279,7 @@ rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k,
   a.dbias = desc->mode == RPE_MODE_BIAS ? dbias : nullptr;
   a.drq = tq ? drq : nullptr; a.drk = tk ? drk : nullptr; a.drv = tv ? drv : nullptr;
   a.bmap = reinterpret_cast<const int16_t*>(ws + L.bmap);
+  a.bmap1 = L.bmap1 != ~0ULL ? reinterpret_cast<const int16_t*>(ws + L.bmap1) : nullptr;
   a.P = reinterpret_cast<float*>(ws + L.P);
   a.dL = reinterpret_cast<float*>(ws + L.dL);
   a.Wq = L.Wq != ~0ULL ? reinterpret_cast<float*>(ws + L.Wq) : nullptr;
@@ -286,7 +300,7 @@ rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k,
   a.tables_per_head = desc->tables_per_head;
   a.n_units = static_cast<int64_t>(units);
   a.scale = desc->scale != 0.0f ? desc->scale : 1.0f / std::sqrt(static_cast<float>(desc->head_dim));
-  // the unit's bucket map (Swin geometry when there is no table)
+  // the unit's pair-to-row map(s) (Swin geometry when there is no table)
   int h = 0, s = 0, nbg = 0;
   rpe_attn_desc g = *desc;
   if (g.mode == RPE_MODE_NONE) {
@@ -298,6 +312,7 @@ rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k,
   const int R = desc->window ? desc->window : desc->grid_h;
   hipError_t e = rpe::launch_bucket_map(desc->prefix_tokens, R, a.C, h, s, g.map, g.rounding, g.alpha, g.beta,
                                         g.gamma, reinterpret_cast<int16_t*>(ws + L.bmap),
+                                        L.bmap1 != ~0ULL ? reinterpret_cast<int16_t*>(ws + L.bmap1) : nullptr,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return RPE_E_HIP;
   e = rpe::launch_bwd(a, static_cast<hipStream_t>(stream));

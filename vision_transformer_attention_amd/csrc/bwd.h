@@ -18,7 +18,8 @@ struct BwdArgs {
   // workspace
   float* P; float* dL;      // [n_units][T][T]
   float* Wq; float* Wk; float* Wv;   // [n_units][T][nb] (null when not needed)
-  const int16_t* bmap;      // [T][T] bucket ids of one unit (-1: prefix pair)
+  const int16_t* bmap;      // [T][T] table row of each pair of one unit (-1: prefix pair)
+  const int16_t* bmap1;     // [T][T] its second table row (Cross), or null: one row per pair
   // geometry
   int bf16;
   int D, N, H, U, T;
@@ -27,7 +28,7 @@ struct BwdArgs {
   int M;                    // window side (0: global)
   int gw;                   // grid width
   int wpr;                  // windows per grid row
-  int nb;                   // table rows
+  int nb;                   // table rows (S*S Product, 2S Cross, S undirected)
   int tables_per_head;
   int64_t n_units;          // B * H * U
   float scale;              // logit scale s

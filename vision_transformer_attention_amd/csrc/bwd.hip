@@ -2,6 +2,10 @@
 // written directly from the gradient of the per-pair definition (iRPE summary
 // page, "Rethinking and Improving Relative Position Encoding for Vision
 // Transformer", Method, eqs. 13-17; Swin relative-bias record, "The claim").
+// A pair's table entry is one table row, or under the Cross mapping (eqs.
+// 22-24) the sum of its row-offset and column-offset rows: every kernel works
+// on table rows, and only the kernels that visit pairs (scores, row and column
+// sums) read the second row.
 // Per unit (b, h, window) with softmax weights P from the saved log-sum-exp:
 //   dP_ij = dO_i . (v_j + [V] rV[b]),  dL_ij = P_ij (dP_ij - sum_j P_ij dP_ij)
 //   dq_i  = s sum_j dL_ij (k_j + [K] rK[b]),  dk_j = s sum_i dL_ij (q_i + [Q] rQ[b])
@@ -188,15 +192,24 @@ __global__ void __launch_bounds__(256) bwd_scores_kernel(BwdArgs a) {
 #pragma unroll
     for (int m = 0; m < kIB; ++m) {
       if (i0 + m >= a.T) break;
-      const int bkt = a.bmap[static_cast<int64_t>(ii[m]) * a.T + j];
-      float rho = 0.0f, dpm = dp[m];
+      const int64_t pij = static_cast<int64_t>(ii[m]) * a.T + j;
+      const int bkt = a.bmap[pij];
+      const int bk1 = a.bmap1 ? a.bmap1[pij] : -1;
+      float rho = 0.0f, dpm = dp[m], bsum = 0.0f;
       if (bkt >= 0) {
-        if (a.rk) rho += a.Wq[(ub * a.T + ii[m]) * a.nb + bkt];
-        if (a.rq) rho += a.Wk[(ub * a.T + j) * a.nb + bkt];
-        if (a.rv) dpm += a.Wv[(ub * a.T + ii[m]) * a.nb + bkt];
+        const int64_t wi = (ub * a.T + ii[m]) * a.nb, wj = (ub * a.T + j) * a.nb;
+        if (a.rk) rho += a.Wq[wi + bkt];
+        if (a.rq) rho += a.Wk[wj + bkt];
+        if (a.rv) dpm += a.Wv[wi + bkt];
+        if (a.bias) bsum = a.bias[tb + bkt];
+        if (bk1 >= 0) {
+          if (a.rk) rho += a.Wq[wi + bk1];
+          if (a.rq) rho += a.Wk[wj + bk1];
+          if (a.rv) dpm += a.Wv[wi + bk1];
+          if (a.bias) bsum += a.bias[tb + bk1];
+        }
       }
-      float logit = (qk[m] + rho) * a.scale;
-      if (a.bias && bkt >= 0) logit += a.bias[tb + bkt];
+      const float logit = (qk[m] + rho) * a.scale + bsum;
       const float p = expf(logit - a.lse[x.bh * a.N + ti[m]]);
       const int64_t o = (ub * a.T + ii[m]) * a.T + j;
       a.P[o] = p;
@@ -321,11 +334,13 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
       // epilogue in rounds (bucket ids, then the row scores they select, then the
       // results), branch-free so that each round's loads are in flight together;
       // rows and keys past T read clamped entries and are not stored
-      int bk[16];
+      int bk[16], bk1[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        bk[e] = a.bmap[static_cast<int64_t>(i < a.T ? i : a.T - 1) * a.T + jr];
+        const int64_t pij = static_cast<int64_t>(i < a.T ? i : a.T - 1) * a.T + jr;
+        bk[e] = a.bmap[pij];
+        bk1[e] = a.bmap1 ? a.bmap1[pij] : -1;
       }
       float add[16], badd[16], dvt[16];
 #pragma unroll
@@ -333,11 +348,20 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
         const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
         const int ic = i < a.T ? i : a.T - 1;
         const int bc = bk[e] < 0 ? 0 : bk[e];
+        const int64_t wi = (ub * a.T + ic) * a.nb, wj = (ub * a.T + jr) * a.nb;
         float r = 0.0f, u = 0.0f, bb = 0.0f;
-        if (a.rk) r += a.Wq[(ub * a.T + ic) * a.nb + bc];
-        if (a.rq) r += a.Wk[(ub * a.T + jr) * a.nb + bc];
-        if (a.rv) u = a.Wv[(ub * a.T + ic) * a.nb + bc];
-        if (a.bias) bb = a.bias[tb + bc] * kLog2e;
+        if (a.rk) r += a.Wq[wi + bc];
+        if (a.rq) r += a.Wk[wj + bc];
+        if (a.rv) u = a.Wv[wi + bc];
+        if (a.bias) bb = a.bias[tb + bc];
+        if (a.bmap1) {
+          const int b1 = bk1[e] < 0 ? 0 : bk1[e];
+          if (a.rk) r += a.Wq[wi + b1];
+          if (a.rq) r += a.Wk[wj + b1];
+          if (a.rv) u += a.Wv[wi + b1];
+          if (a.bias) bb += a.bias[tb + b1];
+        }
+        bb *= kLog2e;
         add[e] = bk[e] >= 0 ? r : 0.0f;
         badd[e] = bk[e] >= 0 ? bb : 0.0f;
         dvt[e] = bk[e] >= 0 ? u : 0.0f;
@@ -357,8 +381,9 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
   }
 }
 
-// Per query row: dL = P (dP - sum_j P dP) in place, and the row's bucket sums
-// Wq[b] = sum_j dL_ij and Wv[b] = sum_j P_ij; one wave per (unit, i), its
+// Per query row: dL = P (dP - sum_j P dP) in place, and the row's per-table-row
+// sums Wq[b] = sum_j dL_ij and Wv[b] = sum_j P_ij over the pairs that read
+// row b; one wave per (unit, i), its
 // lanes over j.  LDS: the sums are formed in the wave's own 2 * nb floats
 // (zeroed, LDS float atomics, then written out in full); global: float
 // atomics into the zeroed rows (tables too large for LDS).
@@ -385,6 +410,7 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
       for (int b = lane; b < 2 * a.nb; b += 64) wq_s[b] = 0.0f;
     }
     const int16_t* brow = a.bmap + static_cast<int64_t>(i) * a.T;
+    const int16_t* brow1 = a.bmap1 ? a.bmap1 + static_cast<int64_t>(i) * a.T : nullptr;
     for (int j = lane; j < a.T; j += 64) {
       const float l = pr[j] * (dr[j] - dsum);
       dr[j] = l;
@@ -392,6 +418,11 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
       if (bkt >= 0) {
         if (wq) atomicAdd((LDS ? wq_s : wq) + bkt, l);
         if (wv) atomicAdd((LDS ? wv_s : wv) + bkt, pr[j]);
+        const int bk1 = brow1 ? brow1[j] : -1;
+        if (bk1 >= 0) {
+          if (wq) atomicAdd((LDS ? wq_s : wq) + bk1, l);
+          if (wv) atomicAdd((LDS ? wv_s : wv) + bk1, pr[j]);
+        }
       }
     }
     if (LDS) {
@@ -418,8 +449,14 @@ __global__ void __launch_bounds__(64) bwd_cols_lds_kernel(BwdArgs a) {
     for (int b = 0; b < a.nb; ++b) wks[b * 64 + lane] = 0.0f;
     const float* Lc = a.dL + ub * a.T * a.T + jc;
     for (int i = 0; i < a.T; ++i) {
-      const int bkt = a.bmap[static_cast<int64_t>(i) * a.T + jc];
-      if (bkt >= 0) wks[bkt * 64 + lane] += Lc[static_cast<int64_t>(i) * a.T];
+      const int64_t pij = static_cast<int64_t>(i) * a.T + jc;
+      const int bkt = a.bmap[pij];
+      if (bkt >= 0) {
+        const float l = Lc[static_cast<int64_t>(i) * a.T];
+        wks[bkt * 64 + lane] += l;
+        const int bk1 = a.bmap1 ? a.bmap1[pij] : -1;
+        if (bk1 >= 0) wks[bk1 * 64 + lane] += l;
+      }
     }
     if (j < a.T) {
       float* wk = a.Wk + (ub * a.T + j) * a.nb;
@@ -438,8 +475,14 @@ __global__ void __launch_bounds__(256) bwd_cols_kernel(BwdArgs a) {
     float* wk = a.Wk + (ub * a.T + j) * a.nb;
     for (int b = 0; b < a.nb; ++b) wk[b] = 0.0f;
     for (int i = 0; i < a.T; ++i) {
-      const int bkt = a.bmap[static_cast<int64_t>(i) * a.T + j];
-      if (bkt >= 0) wk[bkt] += a.dL[(ub * a.T + i) * a.T + j];
+      const int64_t pij = static_cast<int64_t>(i) * a.T + j;
+      const int bkt = a.bmap[pij];
+      if (bkt >= 0) {
+        const float l = a.dL[(ub * a.T + i) * a.T + j];
+        wk[bkt] += l;
+        const int bk1 = a.bmap1 ? a.bmap1[pij] : -1;
+        if (bk1 >= 0) wk[bk1] += l;
+      }
     }
   }
 }

@@ -24,13 +24,16 @@ __global__ void axis_index_kernel(int length, int map, int rounding, double alph
 
 // Bucket id of every ordered pair of one unit; positions of grid tokens are
 // (t / C, t % C) after the P prefix tokens, which carry no position (-1).
+// With out1 == null the id is the Product id (g(dy)+H)*S + g(dx)+H; otherwise
+// (Cross) out names the row-offset row g(dy)+H and out1 the column-offset row
+// S + g(dx)+H of the pair's two table rows.
 __global__ void bucket_map_kernel(int P, int R, int C, int half, int S, int map, int rounding,
-                                  double alpha, double beta, double gamma, int16_t* out) {
+                                  double alpha, double beta, double gamma, int16_t* out, int16_t* out1) {
   extern __shared__ int tabs[];            // [2R-1] row part, [2C-1] column part
   int* ry = tabs;
   int* cx = tabs + (2 * R - 1);
   for (int i = threadIdx.x; i < 2 * R - 1; i += blockDim.x)
-    ry[i] = (axis_index(i - (R - 1), map, rounding, alpha, beta, gamma) + half) * S;
+    ry[i] = axis_index(i - (R - 1), map, rounding, alpha, beta, gamma) + half;
   for (int i = threadIdx.x; i < 2 * C - 1; i += blockDim.x)
     cx[i] = axis_index(i - (C - 1), map, rounding, alpha, beta, gamma) + half;
   __syncthreads();
@@ -39,13 +42,19 @@ __global__ void bucket_map_kernel(int P, int R, int C, int half, int S, int map,
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int i = static_cast<int>(e / T), j = static_cast<int>(e - static_cast<int64_t>(i) * T);
-    int b = -1;
+    int by = -1, bx = -1;
     if (i >= P && j >= P) {
       const int ti = i - P, tj = j - P;
       const int yi = ti / C, xi = ti - yi * C, yj = tj / C, xj = tj - yj * C;
-      b = ry[yi - yj + R - 1] + cx[xi - xj + C - 1];
+      by = ry[yi - yj + R - 1];
+      bx = cx[xi - xj + C - 1];
     }
-    out[e] = static_cast<int16_t>(b);
+    if (out1) {
+      out[e] = static_cast<int16_t>(by);
+      out1[e] = static_cast<int16_t>(by < 0 ? -1 : S + bx);
+    } else {
+      out[e] = static_cast<int16_t>(by < 0 ? -1 : by * S + bx);
+    }
   }
 }
 
@@ -84,13 +93,102 @@ hipError_t launch_cross_to_product(bool bf16, const void* cross, void* product, 
   return hipGetLastError();
 }
 
+// Undirected maps (iRPE page, Method, eqs. 19-21): the index of an offset
+// depends on its squared length k = dy^2 + dx^2 only.  The Quantization map
+// takes the rank of k among the sums of two squares up to kmax (its distance
+// positions); the workgroup numbers them in LDS: is_sum[kmax + 1] (scratch),
+// rank[kmax + 1] (out), part[blockDim.x] (scratch), blockDim.x <= 256.
+constexpr int kMaxSquares = 16384;   // kmax = (R-1)^2 + (C-1)^2 < this (S'*S' <= 32767 keeps R, C <= 91)
+
+__device__ void square_ranks(int kmax, unsigned char* is_sum, unsigned short* rank, int* part) {
+  for (int m = threadIdx.x; m <= kmax; m += blockDim.x) is_sum[m] = 0;
+  __syncthreads();
+  int amax = 0;
+  while ((amax + 1) * (amax + 1) <= kmax) ++amax;
+  const int na = amax + 1;
+  for (int e = threadIdx.x; e < na * na; e += blockDim.x) {
+    const int a = e / na, b = e - (e / na) * na;
+    if (a * a + b * b <= kmax) is_sum[a * a + b * b] = 1;
+  }
+  __syncthreads();
+  // rank[m] = number of sums of two squares below m: chunked count, then a scan
+  const int chunk = (kmax + 1 + blockDim.x - 1) / blockDim.x;
+  const int m0 = threadIdx.x * chunk;
+  int cnt = 0;
+  for (int m = m0; m < m0 + chunk && m <= kmax; ++m) cnt += is_sum[m];
+  part[threadIdx.x] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < static_cast<int>(blockDim.x); ++i) {
+      const int c = part[i];
+      part[i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int run = part[threadIdx.x];
+  for (int m = m0; m < m0 + chunk && m <= kmax; ++m) {
+    rank[m] = static_cast<unsigned short>(run);
+    run += is_sum[m];
+  }
+  __syncthreads();
+}
+
+// Index u in [0, H] of an offset of squared length k under an undirected map
+// (rank: the table square_ranks built, read by the Quantization map only).
+__device__ __forceinline__ int undirected_index(int k, int map, int rounding, double alpha, double beta,
+                                                double gamma, int half, const unsigned short* rank) {
+  int u;
+  if (map == RPE_MAP_EUCLIDEAN) {
+    u = axis_index_real(sqrt(static_cast<double>(k)), rounding, alpha, beta, gamma);
+  } else if (map == RPE_MAP_EUCLIDEAN_ROUNDED) {
+    u = axis_index(static_cast<int>(floor(sqrt(static_cast<double>(k)) + 0.5)), RPE_MAP_PIECEWISE, rounding, alpha,
+                   beta, gamma);
+  } else if (map == RPE_MAP_QUANTIZED) {
+    u = axis_index(rank[k], RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
+  } else {
+    u = axis_index(k, RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
+  }
+  return u < 0 ? 0 : (u > half ? half : u);   // in [0, H] by construction
+}
+
+// Table row u(dy, dx) + H of every ordered pair of one unit under an undirected
+// map (-1 where a prefix token takes part): each workgroup first tabulates
+// u(k) + H for every squared length k in LDS, then writes its share of pairs.
+__global__ void __launch_bounds__(256) undirected_bucket_map_kernel(int P, int R, int C, int half, int map,
+                                                                    int rounding, double alpha, double beta,
+                                                                    double gamma, int16_t* out) {
+  __shared__ unsigned short rank[kMaxSquares];
+  __shared__ unsigned char is_sum[kMaxSquares];
+  __shared__ int part[256];
+  const int kmax = (R - 1) * (R - 1) + (C - 1) * (C - 1);
+  if (map == RPE_MAP_QUANTIZED) square_ranks(kmax, is_sum, rank, part);
+  // in place: entry m of the rank table becomes the row of squared length m
+  // (each thread reads and writes only its own entries)
+  unsigned short* const row_of = rank;
+  for (int m = threadIdx.x; m <= kmax; m += blockDim.x)
+    row_of[m] = static_cast<unsigned short>(undirected_index(m, map, rounding, alpha, beta, gamma, half, rank) + half);
+  __syncthreads();
+  const int T = P + R * C;
+  const int64_t total = static_cast<int64_t>(T) * T;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int i = static_cast<int>(e / T), j = static_cast<int>(e - static_cast<int64_t>(i) * T);
+    int b = -1;
+    if (i >= P && j >= P) {
+      const int ti = i - P, tj = j - P;
+      const int dy = ti / C - tj / C, dx = ti - (ti / C) * C - (tj - (tj / C) * C);
+      b = row_of[dy * dy + dx * dx];
+    }
+    out[e] = static_cast<int16_t>(b);
+  }
+}
+
 // Undirected maps as the Swin map's table over raw offsets (see
 // rpe_attn_undirected_to_product): product[t][(dy+H')*S' + dx+H'][w] =
 // table[t][u(dy, dx) + H][w] for |dy| < R, |dx| < C, else 0.  Each workgroup
-// first numbers the sums of two squares up to (R-1)^2 + (C-1)^2 in LDS (the
-// Quantization map's distance positions, eq. 21), then copies its share.
-constexpr int kMaxSquares = 16384;   // (R-1)^2 + (C-1)^2 < this (S'*S' <= 32767 keeps R, C <= 90)
-
+// first numbers the sums of two squares (square_ranks), then copies its share.
 template <typename T>
 __global__ void __launch_bounds__(256) undirected_to_product_kernel(const T* __restrict__ table,
                                                                     T* __restrict__ product, int R, int C,
@@ -101,40 +199,7 @@ __global__ void __launch_bounds__(256) undirected_to_product_kernel(const T* __r
   __shared__ unsigned char is_sum[kMaxSquares];
   __shared__ int part[256];
   const int kmax = (R - 1) * (R - 1) + (C - 1) * (C - 1);
-  if (map == RPE_MAP_QUANTIZED) {
-    for (int m = threadIdx.x; m <= kmax; m += blockDim.x) is_sum[m] = 0;
-    __syncthreads();
-    int amax = 0;
-    while ((amax + 1) * (amax + 1) <= kmax) ++amax;
-    const int na = amax + 1;
-    for (int e = threadIdx.x; e < na * na; e += blockDim.x) {
-      const int a = e / na, b = e - (e / na) * na;
-      if (a * a + b * b <= kmax) is_sum[a * a + b * b] = 1;
-    }
-    __syncthreads();
-    // rank[m] = number of sums of two squares below m: chunked count, then a scan
-    const int chunk = (kmax + 1 + blockDim.x - 1) / blockDim.x;
-    const int m0 = threadIdx.x * chunk;
-    int cnt = 0;
-    for (int m = m0; m < m0 + chunk && m <= kmax; ++m) cnt += is_sum[m];
-    part[threadIdx.x] = cnt;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int run = 0;
-      for (int i = 0; i < static_cast<int>(blockDim.x); ++i) {
-        const int c = part[i];
-        part[i] = run;
-        run += c;
-      }
-    }
-    __syncthreads();
-    int run = part[threadIdx.x];
-    for (int m = m0; m < m0 + chunk && m <= kmax; ++m) {
-      rank[m] = static_cast<unsigned short>(run);
-      run += is_sum[m];
-    }
-    __syncthreads();
-  }
+  if (map == RPE_MAP_QUANTIZED) square_ranks(kmax, is_sum, rank, part);
   const int Sp = 2 * Hp + 1;
   const int64_t per_table = static_cast<int64_t>(Sp) * Sp;   // cells of one expanded table
   const int S = 2 * half + 1;
@@ -148,19 +213,7 @@ __global__ void __launch_bounds__(256) undirected_to_product_kernel(const T* __r
     const int dy = cell / Sp - Hp, dx = cell - (cell / Sp) * Sp - Hp;
     T* const dst = product + e * width;
     if (dy > -R && dy < R && dx > -C && dx < C) {
-      const int k = dy * dy + dx * dx;
-      int u;
-      if (map == RPE_MAP_EUCLIDEAN) {
-        u = axis_index_real(sqrt(static_cast<double>(k)), rounding, alpha, beta, gamma);
-      } else if (map == RPE_MAP_EUCLIDEAN_ROUNDED) {
-        u = axis_index(static_cast<int>(floor(sqrt(static_cast<double>(k)) + 0.5)), RPE_MAP_PIECEWISE, rounding,
-                       alpha, beta, gamma);
-      } else if (map == RPE_MAP_QUANTIZED) {
-        u = axis_index(rank[k], RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
-      } else {
-        u = axis_index(k, RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
-      }
-      u = u < 0 ? 0 : (u > half ? half : u);   // in [0, H] by construction
+      const int u = undirected_index(dy * dy + dx * dx, map, rounding, alpha, beta, gamma, half, rank);
       const T* const src = table + (t * static_cast<int64_t>(S) + (u + half)) * width;
       for (int w = 0; w < width; ++w) dst[w] = src[w];
     } else {
@@ -197,15 +250,23 @@ hipError_t launch_axis_index(int length, int map, int rounding, double alpha, do
 }
 
 hipError_t launch_bucket_map(int P, int R, int C, int half, int S, int map, int rounding,
-                             double alpha, double beta, double gamma, int16_t* out,
+                             double alpha, double beta, double gamma, int16_t* out, int16_t* out1,
                              hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(P + R * C) * (P + R * C);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
+  if (map >= RPE_MAP_EUCLIDEAN) {
+    if ((R - 1) * (R - 1) + (C - 1) * (C - 1) >= kMaxSquares) return hipErrorInvalidValue;
+    // (each workgroup tabulates every squared length first: fewer, fuller workgroups)
+    if (blocks > 512) blocks = 512;
+    hipLaunchKernelGGL(undirected_bucket_map_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       P, R, C, half, map, rounding, alpha, beta, gamma, out);
+    return hipGetLastError();
+  }
   const size_t lds = static_cast<size_t>(2 * R - 1 + 2 * C - 1) * sizeof(int);
   hipLaunchKernelGGL(bucket_map_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, stream,
-                     P, R, C, half, S, map, rounding, alpha, beta, gamma, out);
+                     P, R, C, half, S, map, rounding, alpha, beta, gamma, out, out1);
   return hipGetLastError();
 }
 
