@@ -350,7 +350,8 @@ def main():
         # known bytes: a sum reads the whole tensor (and writes a few partials), a fill
         # writes it (and reads nothing)
         n = args.calib_probe << 20
-        buf = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        buf = torch.empty(n // 4, dtype=torch.float32, device=dev)
+        buf.fill_(1.0)
         torch.cuda.synchronize()
         for _ in range(3):
             buf.sum()
