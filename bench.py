@@ -257,7 +257,8 @@ def time_backward(name, steps, warmup, dev):
     dout = torch.from_numpy(np.random.default_rng(77).standard_normal(w.qkv_shape)).to(d["q"].dtype).to(dev)
     kw = dict(grid=(w.grid_h, w.grid_w), window=w.window, prefix_tokens=w.prefix, mode=w.mode,
               terms="".join(sorted(w.terms)), map=w.map, alpha=w.alpha, beta=w.beta, gamma=w.gamma,
-              rounding=w.reading, bias=d.get("bias"), rq=d.get("rq"), rk=d.get("rk"), rv=d.get("rv"))
+              rounding=w.reading, bias=d.get("bias"), rq=d.get("rq"), rk=d.get("rk"), rv=d.get("rv"),
+              method=w.method)
     _, lse = pkg.rpe_attn_fwd(d["q"], d["k"], d["v"], return_lse=True, **kw)
     g, call = pkg.prepare_bwd(d["q"], d["k"], d["v"], dout, lse, **kw)
     stream = torch.cuda.current_stream(dev)
