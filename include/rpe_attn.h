@@ -204,8 +204,9 @@ rpe_status rpe_attn_cross_to_product(const rpe_attn_desc* desc, int32_t kind, co
  * pair depends on its offset (dy, dx) only, so the Swin map's table over raw
  * offsets, H' = max(R, C) - 1 for a unit of R x C positions and S' = 2H'+1,
  *     product[(dy + H') * S' + (dx + H')] = table[u(dy, dx) + H]   (|dy| < R, |dx| < C; other rows 0)
- * gives the same attention: call rpe_attn_fwd with this descriptor's map set to
- * RPE_MAP_SWIN and the product table.
+ * gives the same attention under rpe_attn_fwd with this descriptor's map set to
+ * RPE_MAP_SWIN and the product table (rpe_attn_fwd also takes the undirected
+ * descriptor and table directly).
  *   table   : device, [tables][S][width] (S = 2H+1 from rpe_attn_num_buckets)
  *   product : device, [tables][S'*S'][width], written (caller-owned; no overlap)
  *   kind, width, tables: as for rpe_attn_cross_to_product.
@@ -215,8 +216,11 @@ rpe_status rpe_attn_cross_to_product(const rpe_attn_desc* desc, int32_t kind, co
 rpe_status rpe_attn_undirected_to_product(const rpe_attn_desc* desc, int32_t kind, const void* table,
                                           void* product, void* stream);
 
-/* The attention forward (maps RPE_MAP_SWIN and RPE_MAP_PIECEWISE, either method;
- * RPE_E_MODE for an undirected map).  q, k, v, o required (may be NULL when
+/* The attention forward, for every map and method.  Tables: S*S rows (Product),
+ * 2S (Cross) or S (undirected maps: the index of a pair is looked up per offset
+ * in a table the kernel builds from host-computed thresholds of dy^2 + dx^2;
+ * RPE_E_UNSUPPORTED if the index takes more than 64 steps over the unit's
+ * offsets).  q, k, v, o required (may be NULL when
  * batch == 0, which launches nothing); bias required in bias mode;
  * rk / rq / rv required for the contextual terms requested (others ignored);
  * lse nullable.  o must not alias q, k or v.  Asynchronous on `stream`.

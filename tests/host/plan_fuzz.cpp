@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <random>
+#include <vector>
 
 #include "../../vision_transformer_attention_amd/csrc/plan.h"
 
@@ -54,13 +55,13 @@ int main(int argc, char** argv) {
       d.dtype = U(0, 1);
       d.mode = U(0, 2);
       d.terms = d.mode == RPE_MODE_CONTEXTUAL ? static_cast<uint32_t>(U(1, 7)) : 0u;
-      d.map = U(0, 1);
+      d.map = U(0, 3) == 0 ? U(RPE_MAP_EUCLIDEAN, RPE_MAP_QUANTIZED_SQUARED) : U(0, 1);
       d.rounding = U(0, 1);
       d.alpha = F(0.2, 6.0);
       d.beta = d.alpha + F(0.0, 8.0);
       d.gamma = d.alpha + F(0.1, 60.0);
       d.tables_per_head = U(0, 1);
-      d.method = U(0, 3) == 0 ? RPE_METHOD_CROSS : RPE_METHOD_PRODUCT;
+      d.method = (U(0, 3) == 0 && d.map <= RPE_MAP_PIECEWISE) ? RPE_METHOD_CROSS : RPE_METHOD_PRODUCT;
       if (d.method == RPE_METHOD_CROSS && d.mode == RPE_MODE_NONE) d.mode = RPE_MODE_BIAS;
       if (U(0, 1)) {
         const int m = U(1, 9);
@@ -132,6 +133,32 @@ int main(int argc, char** argv) {
     }
     // per-row scores: nb entries in rows of an odd number of words
     REQUIRE(p.p_tab >= p.nb && (p.p_tab * p.gsz) % 4 == 0 && ((p.p_tab * p.gsz / 4) & 1));
+    // undirected maps: S gather entries, the zero and -inf entries past every
+    // target's nbt*32 computed ones, the per-offset index table inside the plan,
+    // the per-bucket value sums, and thresholds that reproduce u on every k
+    REQUIRE(p.und == (d.mode != RPE_MODE_NONE && d.map >= RPE_MAP_EUCLIDEAN));
+    if (p.und) {
+      REQUIRE(p.nb == p.S && p.ntr == p.S && p.zi == p.nbt * rpe::kRowTile && p.zi >= p.nb);
+      REQUIRE(p.p_tab >= p.zi + 2 && !p.vw && !p.cross);
+      if (tq) REQUIRE(p.p_tq >= p.zi + 2);
+      REQUIRE(p.u2w == 2 * p.C + 1 && p.off_u2 % 16 == 0 && p.off_u2 >= p.off_cx + (2 * p.C - 1) * 4);
+      REQUIRE(p.off_u2 + (2 * p.R - 1) * p.u2w * 2 <= p.lds_bytes);
+      REQUIRE(p.zi + 1 < 65536 && p.n_thr >= 0 && p.n_thr <= p.half && p.n_thr <= rpe::kMaxThresholds);
+      const int kmax = (p.R - 1) * (p.R - 1) + (p.C - 1) * (p.C - 1);
+      std::vector<int> rank(kmax + 1, 0);
+      {
+        std::vector<char> is_sum(kmax + 1, 0);
+        for (int a = 0; a * a <= kmax; ++a)
+          for (int b = 0; a * a + b * b <= kmax; ++b) is_sum[a * a + b * b] = 1;
+        for (int m = 1; m <= kmax; ++m) rank[m] = rank[m - 1] + is_sum[m - 1];
+      }
+      for (int k = 0; k <= kmax; ++k) {
+        int cnt = 0;
+        for (int m = 0; m < p.n_thr; ++m) cnt += p.thr[m] <= k;
+        REQUIRE(cnt == rpe::undirected_index_host(k, p.map, p.rounding, p.alpha, p.beta, p.gamma, p.half,
+                                                  rank.data()));
+      }
+    }
     // the thresholds reproduce g on every offset of the unit
     if (d.mode != RPE_MODE_NONE && p.map == RPE_MAP_PIECEWISE && p.n_thr >= 0) {
       const int amax = (p.R > p.C ? p.R : p.C) - 1;
@@ -144,9 +171,9 @@ int main(int argc, char** argv) {
       REQUIRE(p.n_thr <= p.half && p.n_thr <= rpe::kMaxThresholds);
     }
     if (rows) REQUIRE(p.off_zero >= p.off_tab + p.NW * rpe::kRowTile * p.p_tab * p.gsz);
-    if (!ctx) REQUIRE(p.off_zero >= p.off_tab + p.nb * p.gsz);
+    if (!ctx) REQUIRE(p.off_zero >= p.off_tab + (p.und ? p.zi + 2 : p.nb) * p.gsz);
     REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr * p.gsz);
-    REQUIRE(p.zr == (p.S - 1) * p.S + 1);
+    REQUIRE(p.zr == (p.und ? 1 : (p.S - 1) * p.S + 1));
     int end_g = p.off_neg + p.zr * p.gsz;
     if (tv && p.vw) {
       // per-column weight sums: [S][Wp] fp32 rows of an odd number of 16-byte chunks

@@ -167,9 +167,9 @@ def test_undirected_maps_geometry_and_rejections(m):
     assert pkg.rpe_attn_validate(d) == 0
     spec = Spec(14, 14, prefix=1, mode="contextual", terms={"k"}, map=m, alpha=1.9, beta=3.8, gamma=15.2)
     assert pkg.rpe_attn_num_buckets(d) == num_buckets(spec) == (4, 9, 9)
-    # the forward and the per-axis tools take the expanded tables only; the pair
-    # map (rows u + H) and the backward take the undirected tables as they are
-    assert lib.rpe_attn_fwd(ctypes.byref(d), one, one, one, None, None, one, None, one, None, None) == -4
+    # the per-axis tools have no undirected form; the forward, the pair map (rows
+    # u + H) and the backward take the undirected tables as they are
+    assert lib.rpe_attn_fwd(ctypes.byref(d), None, one, one, None, None, one, None, one, None, None) == -1
     assert lib.rpe_attn_bucket_map(ctypes.byref(d), None, None) == -1
     assert lib.rpe_attn_axis_index(ctypes.byref(d), 5, one, None) == -4
     n = ctypes.c_uint64()

@@ -465,10 +465,11 @@ def test_strided_views(dev, label, w):
     assert err <= TOL[w.dtype] and lerr <= TOL[w.dtype], (err, lerr)
 
 
-# Undirected maps (Euclidean, Quantization; page and code readings): the table of
-# S rows is expanded into the Swin map's table over raw offsets by
-# rpe_attn_undirected_to_product (checked exactly: it copies rows chosen by
-# indices computed on the device in fp64), and the forward runs on that.
+# Undirected maps (Euclidean, Quantization; page and code readings).  The forward
+# takes their table of S rows as it is: a per-offset index table gathers the row
+# in two steps.  rpe_attn_undirected_to_product, which expands that table into
+# the Swin map's table over raw offsets, is checked exactly (it copies rows
+# chosen by indices computed on the device in fp64).
 UND_MAPS = ["euclidean", "euclidean_rounded", "quantized", "quantized_squared"]
 
 
@@ -522,6 +523,34 @@ def test_undirected_maps(dev, m, label, w):
     w = fit(w.resized(map=m))
     say("undirected", m, label, w.qkv_shape, "table rows", w.table_rows)
     compare(w, make_inputs(w, sigma=1.0, seed=9900), dev)
+
+
+# Units too large for a table over raw offsets to stay in LDS: 32x32 and 56x56
+# global grids (63x63 and 111x111 offsets), sampled over batch and heads.
+_UND_LARGE = [
+    ("contextual K, global 32x32 + cls", "euclidean",
+     _D.resized(batch=2, heads=2, grid_h=32, grid_w=32)),
+    ("contextual KQV, global 32x32 + cls", "quantized",
+     _D.resized(batch=1, heads=2, grid_h=32, grid_w=32, terms=frozenset("kqv"))),
+    ("contextual KV fp32 d32, global 24x40", "quantized_squared",
+     _D.resized(batch=1, heads=2, head_dim=32, grid_h=24, grid_w=40, prefix=0, terms=frozenset("kv"),
+                dtype="fp32")),
+    ("bias, global 56x56 + cls", "euclidean_rounded",
+     _D.resized(batch=1, heads=3, grid_h=56, grid_w=56, mode="bias", terms=frozenset(), tables_per_head=True,
+                alpha=3.8, beta=7.6, gamma=30.4)),
+    ("contextual QV, 28x28 windows on 56x56", "euclidean",
+     _D.resized(batch=1, heads=2, grid_h=56, grid_w=56, window=28, prefix=0, terms=frozenset("qv"))),
+]
+
+
+@pytest.mark.parametrize("label,m,w", _UND_LARGE)
+def test_undirected_large_units(dev, label, m, w):
+    w = fit(w.resized(map=m))
+    say("undirected large", m, label, w.qkv_shape, "table rows", w.table_rows)
+    sel = dict(batch_sel=[w.batch - 1], heads_sel=[w.heads - 1])
+    if w.window:
+        sel["units"] = [0, 3]
+    compare(w, make_inputs(w, sigma=1.0, seed=9950), dev, **sel)
 
 
 def test_no_position_mode(dev):

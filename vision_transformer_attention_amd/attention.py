@@ -147,14 +147,6 @@ def rpe_attn_undirected_to_product(desc, table):
     return out
 
 
-def _swin_desc(desc):
-    """The same descriptor with the Swin map (the expanded tables' geometry)."""
-    d = Desc()
-    ctypes.memmove(ctypes.byref(d), ctypes.byref(desc), ctypes.sizeof(Desc))
-    d.map = _lib.RPE_MAP_SWIN
-    return d
-
-
 def _check_geometry_and_tables(desc, q, mode, terms, per_head, bias, rq, rk, rv):
     """Checks shared by the forward and backward bindings, before any launch: the
     library sizes every read and write from the descriptor alone, so the token
@@ -195,9 +187,8 @@ def _view_strides(t, name):
 def _fwd_setup(q, k, v, out, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
                alpha=0.0, beta=0.0, gamma=0.0, rounding="capped", scale=None, bias=None, rq=None, rk=None,
                rv=None, method="product"):
-    """Validate a forward call and marshal it: (descriptor of the tables, descriptor of
-    the launch, out, [bias, rq, rk, rv] as launched, [(kind, table, expanded)] of an
-    undirected map's expansions)."""
+    """Validate a forward call and marshal it: (descriptor, out, [bias, rq, rk, rv] as
+    launched)."""
     torch = _torch()
     if method not in _METHODS:
         raise ValueError(f"method {method!r}")
@@ -228,19 +219,9 @@ def _fwd_setup(q, k, v, out, *, grid, window=0, prefix_tokens=0, mode="none", te
     used = {"bias": mode == "bias", "rq": mode == "contextual" and "q" in terms,
             "rk": mode == "contextual" and "k" in terms, "rv": mode == "contextual" and "v" in terms}
     launch = [t if used[n] else None for n, t in zip(("bias", "rq", "rk", "rv"), (bias, rq, rk, rv))]
-    expand = []
-    fdesc = desc
-    if map in UNDIRECTED:
-        if mode == "none":
-            raise ValueError("an undirected map needs bias or contextual mode")
-        # the index depends on the offset only: the forward runs with the Swin map
-        # on the tables expanded over raw offsets
-        for i, t in enumerate(launch):
-            if t is not None:
-                launch[i] = rpe_attn_undirected_to_product(desc, t)
-                expand.append((_lib.RPE_TABLE_BIAS if t.dim() == 2 else _lib.RPE_TABLE_VECTOR, t, launch[i]))
-        fdesc = _swin_desc(desc)
-    return desc, fdesc, out, launch, expand
+    if map in UNDIRECTED and mode == "none":
+        raise ValueError("an undirected map needs bias or contextual mode")
+    return desc, out, launch
 
 
 def rpe_attn_fwd(q, k, v, *, grid, window=0, prefix_tokens=0, mode="none", terms="", map="swin",
@@ -253,17 +234,15 @@ def rpe_attn_fwd(q, k, v, *, grid, window=0, prefix_tokens=0, mode="none", terms
     [B, N, 3, H, d] projection, permuted), N = prefix_tokens + grid[0] * grid[1].
     bias: [H or 1, rows] float32; rq / rk / rv: [H or 1, rows, d] in the dtype
     of q, contiguous; rows = S*S (method "product") or 2S (method "cross": the
-    row-offset half, then the column-offset half).  ``out`` may be any
+    row-offset half, then the column-offset half), or S for an undirected map
+    ("euclidean", "euclidean_rounded", "quantized", "quantized_squared"; rows
+    H .. 2H hold the indices 0 .. H).  ``out`` may be any
     [B, H, N, d] view with a contiguous last dimension (default: a new
     contiguous tensor).  Returns o (and the float32 log-sum-exp [B, H, N] with
     ``return_lse``).
-
-    An undirected map ("euclidean", "euclidean_rounded", "quantized",
-    "quantized_squared") takes tables of S rows; they are expanded by
-    ``rpe_attn_undirected_to_product`` and the forward runs with the Swin map.
     """
     torch = _torch()
-    desc, fdesc, out, launch, _ = _fwd_setup(
+    desc, out, launch = _fwd_setup(
         q, k, v, out, grid=grid, window=window, prefix_tokens=prefix_tokens, mode=mode, terms=terms, map=map,
         alpha=alpha, beta=beta, gamma=gamma, rounding=rounding, scale=scale, bias=bias, rq=rq, rk=rk, rv=rv,
         method=method)
@@ -271,46 +250,39 @@ def rpe_attn_fwd(q, k, v, *, grid, window=0, prefix_tokens=0, mode="none", terms
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
     b, tq, tk, tv = launch
     check("rpe_attn_fwd",
-          load().rpe_attn_fwd(ctypes.byref(fdesc), _ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(tq), _ptr(tk),
+          load().rpe_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(tq), _ptr(tk),
                               _ptr(tv), _ptr(out), _ptr(lse), _stream(q.device)))
     return (out, lse) if return_lse else out
 
 
 class PreparedFwd:
     """A validated rpe_attn_fwd call with fixed tensors: each call() is one
-    library call with pre-marshalled arguments (for launch loops and timing);
-    an undirected map's tables are expanded again on every call first.
+    library call with pre-marshalled arguments (for launch loops and timing).
 
     The tensors passed to ``prepare_fwd`` must stay alive and keep their
     storage while this object is used.
     """
 
-    def __init__(self, desc, fdesc, ptrs, keep, device, expand=()):
+    def __init__(self, desc, ptrs, keep, device):
         self._lib = load()
         self._desc = desc
-        self._fdesc = fdesc
         self._args = ptrs
         self._keep = keep
         self._device = device
-        self._expand = expand      # (kind, table, expanded) launches before the forward
 
     def __call__(self, stream=None):
         torch = _torch()
         s = ctypes.c_void_p(torch.cuda.current_stream(self._device).cuda_stream if stream is None else stream)
-        for kind, src, dst in self._expand:
-            check("rpe_attn_undirected_to_product",
-                  self._lib.rpe_attn_undirected_to_product(ctypes.byref(self._desc), kind, src, dst, s))
-        check("rpe_attn_fwd", self._lib.rpe_attn_fwd(ctypes.byref(self._fdesc), *self._args, s))
+        check("rpe_attn_fwd", self._lib.rpe_attn_fwd(ctypes.byref(self._desc), *self._args, s))
 
 
 def prepare_fwd(q, k, v, *, out, lse=None, **kw):
     """Validate once (by running the call) and return a PreparedFwd for repeats."""
     rpe_attn_fwd(q, k, v, out=out, **kw)
     kw.pop("return_lse", None)
-    desc, fdesc, out, launch, expand = _fwd_setup(q, k, v, out, **kw)
+    desc, out, launch = _fwd_setup(q, k, v, out, **kw)
     ptrs = [_ptr(q), _ptr(k), _ptr(v)] + [_ptr(t) for t in launch] + [_ptr(out), _ptr(lse)]
-    ex = tuple((kind, _ptr(src), _ptr(dst)) for kind, src, dst in expand)
-    return PreparedFwd(desc, fdesc, ptrs, (q, k, v, out, lse, launch, expand), q.device, ex)
+    return PreparedFwd(desc, ptrs, (q, k, v, out, lse, launch), q.device)
 
 
 class PreparedBwd:

@@ -26,7 +26,9 @@ SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "bwd.hip", "fwd_dispatch.cpp",
            "fwd_bf16_d16.hip", "fwd_bf16_d32.hip", "fwd_bf16_d64.hip",
            "fwd_f32_d16.hip", "fwd_f32_d32.hip", "fwd_f32_d64.hip",
            "fwd_cross_bf16_d16.hip", "fwd_cross_bf16_d32.hip", "fwd_cross_bf16_d64.hip",
-           "fwd_cross_f32_d16.hip", "fwd_cross_f32_d32.hip", "fwd_cross_f32_d64.hip"]
+           "fwd_cross_f32_d16.hip", "fwd_cross_f32_d32.hip", "fwd_cross_f32_d64.hip",
+           "fwd_und_bf16_d16.hip", "fwd_und_bf16_d32.hip", "fwd_und_bf16_d64.hip",
+           "fwd_und_f32_d16.hip", "fwd_und_f32_d32.hip", "fwd_und_f32_d64.hip"]
 
 
 def _run(cmd, verbose):

@@ -4,6 +4,6 @@
 
 namespace rpe {
 hipError_t launch_fwd_cross_bf16_d16(const Params& p, hipStream_t stream) {
-  return launch_fwd_ctx<__bf16, 16, true>(p, stream);
+  return launch_fwd_ctx<__bf16, 16, kMapCross>(p, stream);
 }
 }  // namespace rpe

@@ -4,6 +4,6 @@
 
 namespace rpe {
 hipError_t launch_fwd_cross_f32_d32(const Params& p, hipStream_t stream) {
-  return launch_fwd_ctx<float, 32, true>(p, stream);
+  return launch_fwd_ctx<float, 32, kMapCross>(p, stream);
 }
 }  // namespace rpe

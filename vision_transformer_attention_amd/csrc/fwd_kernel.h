@@ -193,13 +193,21 @@ using bool_c = std::integral_constant<bool, B>;
 
 }  // namespace
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, bool CROSS>
+// Map kinds of the kernel instances: Product (and the Cross bias, summed into
+// the Product layout in the prologue), Cross contextual tables, undirected maps.
+constexpr int kMapProduct = 0, kMapCross = 1, kMapUndirected = 2;
+
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, int MK>
 __global__ void __launch_bounds__(kThreadsMax) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE, D, MULTI))))
 rpe_fwd_kernel(Params p) {
   // CROSS: contextual tables under the Cross mapping (2S rows; instances of their
   // own, so that the Product instances carry none of its code).  Bias tables under
   // the Cross mapping are summed into the Product layout in the prologue (p.cross).
+  // UND: undirected maps, gathered through the per-offset index table (p.und).
+  constexpr bool CROSS = MK == kMapCross;
+  constexpr bool UND = MK == kMapUndirected;
   static_assert(!CROSS || MODE == RPE_MODE_CONTEXTUAL, "Cross instances are contextual");
+  static_assert(!UND || MODE != RPE_MODE_NONE, "undirected instances have a table");
   constexpr bool BF = std::is_same<DT, __bf16>::value;
   constexpr bool CTX = MODE == RPE_MODE_CONTEXTUAL;
   constexpr bool TK = CTX && (TERMS & RPE_TERM_K);
@@ -586,10 +594,43 @@ rpe_fwd_kernel(Params p) {
         }
         g += p.half;
       }
-      if (is_row)
-        ry_tab[i] = g * p.S * GSZ;
-      else
-        cx_tab[i - nry] = g;
+      if constexpr (UND) {
+        // byte offset of row dy + R-1 of the index table / column dx + C-1
+        if (is_row)
+          ry_tab[i] = i * p.u2w * 2;
+        else
+          cx_tab[i - nry] = i - nry;
+      } else {
+        if (is_row)
+          ry_tab[i] = g * p.S * GSZ;
+        else
+          cx_tab[i - nry] = g;
+      }
+    }
+  }
+  if constexpr (UND) {
+    // u(dy, dx) + H for every offset of the unit, then the zero and -inf columns
+    uint16_t* const u2 = reinterpret_cast<uint16_t*>(smem + p.off_u2);
+    const int n2 = (2 * p.R - 1) * p.u2w;
+    for (int e = tid; e < n2; e += nth) {
+      const int row = e / p.u2w, col = e - (e / p.u2w) * p.u2w;
+      int v;
+      if (col < 2 * p.C - 1) {
+        const int dy = row - (p.R - 1), dx = col - (p.C - 1);
+        const int k = dy * dy + dx * dx;
+        int cnt = 0;
+        for (int m = 0; m < p.n_thr; ++m) cnt += p.thr[m] <= k ? 1 : 0;
+        v = cnt + p.half;
+      } else {
+        v = col == 2 * p.C - 1 ? p.zi : p.zi + 1;
+      }
+      u2[e] = static_cast<uint16_t>(v);
+    }
+    if constexpr (TQ) {
+      for (int r = tid; r < kRowTile; r += nth) {
+        tqs[r * p.p_tq + p.zi] = 0.0f;
+        tqs[r * p.p_tq + p.zi + 1] = -INFINITY;
+      }
     }
   }
   for (int i = tid; i < p.zr; i += nth) {
@@ -616,7 +657,11 @@ rpe_fwd_kernel(Params p) {
     }
   }
   if constexpr (CTX && GATHER && !TK) {
-    for (int i = tid; i < NW * kRowTile * p.p_tab; i += nth) gtab[i] = static_cast<GT>(0.0f);
+    for (int i = tid; i < NW * kRowTile * p.p_tab; i += nth) {
+      // (undirected maps: each row's entry zi+1 is the -inf of padding keys)
+      const bool neg = UND && i - (i / p.p_tab) * p.p_tab == p.zi + 1;
+      gtab[i] = static_cast<GT>(neg ? -INFINITY : 0.0f);
+    }
   }
   if constexpr (TQ) {
     // rQ staged as [nrq][kpitch]: nbt*32 rows (rows past nb zero), or the 2S Cross rows
@@ -779,6 +824,8 @@ rpe_fwd_kernel(Params p) {
   // 8j + 4h + i of a block at phase ph (ph = block index & 1 when a grid row spans
   // two blocks); cqb the same for the query-term scores (fp32).
   const int rowbase = ROWS ? p.off_tab + (wid * kRowTile + r32) * p.p_tab * GSZ : p.off_tab;
+  // (undirected maps: the absolute LDS address of this lane's gather target)
+  const int rowabs = UND ? lds0 + rowbase : 0;
   // per-bucket weight sums (vw = 0): the entry of a gather address, 4-byte entries
   auto waddr = [&](int ga) -> int { return p.off_w + (ga - lds0 - p.off_tab) * (4 / GSZ); };
   // per-column weight sums (vw = 1): this row's [S][Wp] area, the byte offset of
@@ -812,6 +859,13 @@ rpe_fwd_kernel(Params p) {
     } else {
       for (int k = wid; k * 64 < p.nb; k += NW)
         if (k * 64 + lane < p.nb) gtab[k * 64 + lane] *= p.bias_mul;
+    }
+    if constexpr (UND) {
+      // the entries of pairs without a bias and of padding keys
+      if (tid == 0) {
+        gtab[p.zi] = 0.0f;
+        gtab[p.zi + 1] = -INFINITY;
+      }
     }
   }
   lds_barrier();  // prologue tables (and rK / bias copies) visible; ring loads stay in flight
@@ -860,9 +914,16 @@ rpe_fwd_kernel(Params p) {
           const int xu = ((32 * ph + 8 * j) & (p.Wp - 1)) + i;
           const int cpart = cp[ph][j][i];
           const bool col = hx < p.C - xu;   // xj < C
-          cxb[ph][j][i] = lds0 + (!col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero));
-          if constexpr (TQ)
-            cqb[ph][j][i] = lds0 + (!col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz));
+          if constexpr (UND) {
+            // the column of the index table: dx + C-1, or the zero / -inf column
+            const int ucol = !col ? 2 * p.C : (qpos ? cpart : 2 * p.C - 1);
+            cxb[ph][j][i] = lds0 + p.off_u2 + 2 * ucol;
+            if constexpr (TQ) cqb[ph][j][i] = lds0 + p.off_tq + s * p.p_tq * 4;
+          } else {
+            cxb[ph][j][i] = lds0 + (!col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero));
+            if constexpr (TQ)
+              cqb[ph][j][i] = lds0 + (!col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz));
+          }
         }
   }
   (void)cqb;
@@ -921,8 +982,15 @@ rpe_fwd_kernel(Params p) {
         rp[j] = ryb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ab[j][i] = ryb + cxb[PH][j][i];
-          x[j][i] = logit(s[4 * j + i], ab[j][i], TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0);
+          if constexpr (UND) {
+            // the pair's index from the offset table, then its entries
+            const int u = lds_at<uint16_t>(ryb + cxb[PH][j][i]);
+            ab[j][i] = rowabs + u * GSZ;
+            x[j][i] = logit(s[4 * j + i], ab[j][i], TQ ? cqb[TQ ? PH : 0][j][i] + u * 4 : 0);
+          } else {
+            ab[j][i] = ryb + cxb[PH][j][i];
+            x[j][i] = logit(s[4 * j + i], ab[j][i], TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0);
+          }
         }
         if constexpr (ROWMASK) {
           if (((gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp) >= p.R) {
@@ -945,19 +1013,34 @@ rpe_fwd_kernel(Params p) {
           const int slot = 8 * j + 4 * h + i;
           vz[j][i] = false;
           const int xj = (gblk * kBlockSlots + slot) & (p.Wp - 1);
-          int a = ryb + cxb[PH][j][i];
-          int aq = TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0;
-          if (prefix_blk) {
-            const bool pre = slot < p.P;
-            a = lds0 + (pre ? p.off_zero : p.off_neg);
-            aq = lds0 + (pre ? p.off_tqz : p.off_tqn);
-          } else if (yj >= p.R) {
-            a = lds0 + p.off_neg;
-            aq = lds0 + p.off_tqn;
-          } else if (p.prefix_in_tail && yj == p.R - 1 && xj >= p.C && xj - p.C < p.P) {
-            a = lds0 + p.off_zero;
-            aq = lds0 + p.off_tqz;
-            vz[j][i] = true;
+          int a, aq;
+          if constexpr (UND) {
+            int u = lds_at<uint16_t>(ryb + cxb[PH][j][i]);
+            if (prefix_blk) {
+              u = slot < p.P ? p.zi : p.zi + 1;
+            } else if (yj >= p.R) {
+              u = p.zi + 1;
+            } else if (p.prefix_in_tail && yj == p.R - 1 && xj >= p.C && xj - p.C < p.P) {
+              u = p.zi;
+              vz[j][i] = true;
+            }
+            a = rowabs + u * GSZ;
+            aq = TQ ? cqb[TQ ? PH : 0][j][i] + u * 4 : 0;
+          } else {
+            a = ryb + cxb[PH][j][i];
+            aq = TQ ? tq_row(ryb) + cqb[TQ ? PH : 0][j][i] : 0;
+            if (prefix_blk) {
+              const bool pre = slot < p.P;
+              a = lds0 + (pre ? p.off_zero : p.off_neg);
+              aq = lds0 + (pre ? p.off_tqz : p.off_tqn);
+            } else if (yj >= p.R) {
+              a = lds0 + p.off_neg;
+              aq = lds0 + p.off_tqn;
+            } else if (p.prefix_in_tail && yj == p.R - 1 && xj >= p.C && xj - p.C < p.P) {
+              a = lds0 + p.off_zero;
+              aq = lds0 + p.off_tqz;
+              vz[j][i] = true;
+            }
           }
           ab[j][i] = a;
           x[j][i] = logit(s[4 * j + i], a, aq);
@@ -1295,6 +1378,15 @@ rpe_fwd_kernel(Params p) {
       }
     }
   }
+  if constexpr (TK && UND) {
+    // the row's entries for pairs without a position term and for padding keys
+    // (past the nb scores above, written after them by the same lane)
+    if (active) {
+      GT* const trow = reinterpret_cast<GT*>(smem + rowbase);
+      trow[p.zi] = static_cast<GT>(0.0f);
+      trow[p.zi + 1] = static_cast<GT>(-INFINITY);
+    }
+  }
   // Q is in registers before the ring moves on: otherwise the first use of Q
   // waits for every load issued before it, including ring loads just issued.
   if constexpr (BF) {
@@ -1544,9 +1636,9 @@ rpe_fwd_kernel(Params p) {
 // ----------------------------------------------------------------------------------------
 // Launch dispatch.
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, bool CROSS>
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, int MK>
 hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
-  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, MULTI, CROSS>;
+  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, MULTI, MK>;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   if (attr != hipSuccess) return attr;
@@ -1555,40 +1647,48 @@ hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool CROSS>
+template <typename DT, int D, int MODE, unsigned TERMS, int MK>
 hipError_t launch_fwd_t(const Params& p, hipStream_t stream) {
   // (several units per workgroup only arise for units of at most 4 query tiles,
   // so never with wide rows)
   if constexpr (MODE != RPE_MODE_CONTEXTUAL) {
-    if (p.upw > 1 && p.Wp != 64) return launch_fwd_w<DT, D, MODE, TERMS, false, true, false>(p, stream);
+    if (p.upw > 1 && p.Wp != 64) return launch_fwd_w<DT, D, MODE, TERMS, false, true, MK>(p, stream);
   }
-  return p.Wp == 64 ? launch_fwd_w<DT, D, MODE, TERMS, true, false, CROSS>(p, stream)
-                    : launch_fwd_w<DT, D, MODE, TERMS, false, false, CROSS>(p, stream);
+  return p.Wp == 64 ? launch_fwd_w<DT, D, MODE, TERMS, true, false, MK>(p, stream)
+                    : launch_fwd_w<DT, D, MODE, TERMS, false, false, MK>(p, stream);
 }
 
-// The contextual instances of one (dtype, head dim) for one method.
-template <typename DT, int D, bool CROSS>
+// The contextual instances of one (dtype, head dim) for one map kind.
+template <typename DT, int D, int MK>
 hipError_t launch_fwd_ctx(const Params& p, hipStream_t stream) {
   switch (p.terms) {
-    case 1: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 1, CROSS>(p, stream);
-    case 2: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 2, CROSS>(p, stream);
-    case 3: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 3, CROSS>(p, stream);
-    case 4: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 4, CROSS>(p, stream);
-    case 5: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 5, CROSS>(p, stream);
-    case 6: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 6, CROSS>(p, stream);
-    case 7: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 7, CROSS>(p, stream);
+    case 1: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 1, MK>(p, stream);
+    case 2: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 2, MK>(p, stream);
+    case 3: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 3, MK>(p, stream);
+    case 4: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 4, MK>(p, stream);
+    case 5: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 5, MK>(p, stream);
+    case 6: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 6, MK>(p, stream);
+    case 7: return launch_fwd_t<DT, D, RPE_MODE_CONTEXTUAL, 7, MK>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 // The no-position, bias and contextual Product instances of one (dtype, head
-// dim); the contextual Cross instances are launched by launch_fwd_ctx<.., true>
-// from translation units of their own.
+// dim); the contextual Cross instances (launch_fwd_ctx<.., kMapCross>) and the
+// undirected ones (launch_fwd_und) come from translation units of their own.
 template <typename DT, int D>
 hipError_t launch_fwd_d(const Params& p, hipStream_t stream) {
-  if (p.mode == RPE_MODE_NONE) return launch_fwd_t<DT, D, RPE_MODE_NONE, 0, false>(p, stream);
-  if (p.mode == RPE_MODE_BIAS) return launch_fwd_t<DT, D, RPE_MODE_BIAS, 0, false>(p, stream);
-  return launch_fwd_ctx<DT, D, false>(p, stream);
+  if (p.mode == RPE_MODE_NONE) return launch_fwd_t<DT, D, RPE_MODE_NONE, 0, kMapProduct>(p, stream);
+  if (p.mode == RPE_MODE_BIAS) return launch_fwd_t<DT, D, RPE_MODE_BIAS, 0, kMapProduct>(p, stream);
+  return launch_fwd_ctx<DT, D, kMapProduct>(p, stream);
+}
+
+// Undirected maps: bias or contextual.
+template <typename DT, int D>
+hipError_t launch_fwd_und(const Params& p, hipStream_t stream) {
+  if (p.mode == RPE_MODE_BIAS) return launch_fwd_t<DT, D, RPE_MODE_BIAS, 0, kMapUndirected>(p, stream);
+  if (p.mode == RPE_MODE_CONTEXTUAL) return launch_fwd_ctx<DT, D, kMapUndirected>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace rpe

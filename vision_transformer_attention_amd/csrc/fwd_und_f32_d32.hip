@@ -1,0 +1,8 @@
+// Instances of the fused forward for float inputs, head dim 32, undirected maps.
+#include "fwd_kernel.h"
+
+namespace rpe {
+hipError_t launch_fwd_und_f32_d32(const Params& p, hipStream_t stream) {
+  return launch_fwd_und<float, 32>(p, stream);
+}
+}  // namespace rpe

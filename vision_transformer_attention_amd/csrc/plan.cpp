@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstring>
 #include <initializer_list>
+#include <vector>
 
 namespace rpe {
 namespace {
@@ -58,11 +59,14 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   if (p->cross && ctx && (d->terms & RPE_TERM_K)) off += ((2 * p->S + kRowTile - 1) / kRowTile) * kRowTile * p->D * eb;
   p->off_bx = off;
   if (p->cross && d->mode == RPE_MODE_BIAS) off += align(2 * p->S * 4, 16);
-  p->zr = (p->S - 1) * p->S + 1;  // 1 when there is no table
-  p->p_tab = odd_word_pitch(p->nb, p->gsz);
+  // undirected maps: no guard regions (their pads are entries zi, zi+1 of each target)
+  p->zr = p->und ? 1 : (p->S - 1) * p->S + 1;  // 1 when there is no table
+  p->zi = p->nbt * kRowTile;
+  const int ntab = p->und ? p->zi + 2 : p->nb;   // entries of a gather target row
+  p->p_tab = odd_word_pitch(ntab, p->gsz);
   p->off_tab = off;
   if (d->mode == RPE_MODE_BIAS || d->mode == RPE_MODE_NONE) {
-    off += p->nb * p->gsz;
+    off += ntab * p->gsz;
   } else if (row_area) {
     off += p->NW * kRowTile * p->p_tab * p->gsz;
   }
@@ -83,13 +87,17 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
     off += align((p->off_neg + p->zr * p->gsz - p->off_tab) * (4 / p->gsz), 16);
   }
   if (tq) {
-    p->p_tq = odd_word_pitch(p->nbt * kRowTile, 4);
+    p->p_tq = odd_word_pitch(p->nbt * kRowTile + (p->und ? 2 : 0), 4);
     p->off_tq = off; off += kBlockSlots * p->p_tq * 4;
     p->off_tqz = off; off += p->zr * 4;
     p->off_tqn = off; off += p->zr * 4;
   }
   p->off_ry = off; off += (2 * p->R - 1) * 4;
   p->off_cx = off; off += (2 * p->C - 1) * 4;
+  off = align(off, 16);
+  p->u2w = 2 * p->C + 1;
+  p->off_u2 = off;
+  if (p->und) off += (2 * p->R - 1) * p->u2w * 2;
   p->lds_bytes = align(off, 16);
   return p->lds_bytes > kMaxLdsBytes ? RPE_E_BUCKETS : RPE_OK;
 }
@@ -201,6 +209,32 @@ int axis_index_host(int x, int map, int rounding, double alpha, double beta, dou
   return x > 0 ? mag : -mag;
 }
 
+// Index u in [0, H] of an offset of squared length k under an undirected map
+// (iRPE page, Method, eqs. 19-21; the page and code readings): rank[k] is the
+// number of sums of two squares below k (Quantization).
+int undirected_index_host(int k, int map, int rounding, double alpha, double beta, double gamma, int half,
+                          const int* rank) {
+  int u;
+  if (map == RPE_MAP_EUCLIDEAN) {
+    const double r = std::sqrt(static_cast<double>(k));
+    if (r <= alpha) {
+      u = static_cast<int>(std::floor(r + 0.5));
+    } else {
+      const double sp = alpha + std::log(r / alpha) / std::log(gamma / alpha) * (beta - alpha);
+      const double cap = std::fmin(beta, std::floor(sp + 0.5));
+      u = rounding == RPE_ROUND_CAPPED ? static_cast<int>(std::floor(cap + 0.5)) : static_cast<int>(std::floor(cap));
+    }
+  } else if (map == RPE_MAP_EUCLIDEAN_ROUNDED) {
+    u = axis_index_host(static_cast<int>(std::floor(std::sqrt(static_cast<double>(k)) + 0.5)), RPE_MAP_PIECEWISE,
+                        rounding, alpha, beta, gamma);
+  } else if (map == RPE_MAP_QUANTIZED) {
+    u = axis_index_host(rank[k], RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
+  } else {
+    u = axis_index_host(k, RPE_MAP_PIECEWISE, rounding, alpha, beta, gamma);
+  }
+  return u < 0 ? 0 : (u > half ? half : u);
+}
+
 FastDiv make_fastdiv(uint32_t d) {
   FastDiv f{d, 0u, 0u, 0u};
   if (d == 0) return f;
@@ -215,15 +249,17 @@ FastDiv make_fastdiv(uint32_t d) {
 int make_plan(const rpe_attn_desc* d, Params* p) {
   int st = validate(d);
   if (st != RPE_OK) return st;
-  if (is_undirected(d)) return RPE_E_MODE;   // the forward takes their expanded Product tables
   std::memset(p, 0, sizeof(*p));
+  p->und = is_undirected(d) ? 1 : 0;
   if (d->mode == RPE_MODE_NONE) {
     p->half = 0; p->S = 1; p->nb = 1;  // no table
     p->ntr = 1;
   } else {
     st = table_geometry(d, &p->half, &p->S, &p->ntr);
     if (st != RPE_OK) return st;
-    p->nb = p->S * p->S;   // Product buckets (the gather entries of either method)
+    // gather entries: Product buckets (either directed method), or the S rows of
+    // an undirected table
+    p->nb = p->und ? p->S : p->S * p->S;
   }
   p->cross = d->method == RPE_METHOD_CROSS ? 1 : 0;
   {
@@ -285,6 +321,34 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
     p->n_thr = k;
   }
 
+  // undirected maps: thresholds of u over k = dy^2 + dx^2 in 0 .. (R-1)^2 + (C-1)^2
+  if (p->und) {
+    const int kmax = (p->R - 1) * (p->R - 1) + (p->C - 1) * (p->C - 1);
+    if (kmax > 32767) return RPE_E_UNSUPPORTED;   // (thresholds are int16)
+    std::vector<int> rank;
+    if (p->map == RPE_MAP_QUANTIZED) {
+      // rank[m] = number of sums of two squares below m
+      std::vector<char> is_sum(kmax + 1, 0);
+      for (int a = 0; a * a <= kmax; ++a)
+        for (int b = 0; a * a + b * b <= kmax; ++b) is_sum[a * a + b * b] = 1;
+      rank.assign(kmax + 1, 0);
+      int run = 0;
+      for (int m = 0; m <= kmax; ++m) {
+        rank[m] = run;
+        run += is_sum[m];
+      }
+    }
+    int n = 0;
+    for (int k = 0; k <= kmax; ++k) {
+      const int u = undirected_index_host(k, p->map, p->rounding, p->alpha, p->beta, p->gamma, p->half, rank.data());
+      while (n < u) {
+        if (n == kMaxThresholds) return RPE_E_UNSUPPORTED;
+        p->thr[n++] = static_cast<int16_t>(k);
+      }
+    }
+    p->n_thr = n;
+  }
+
   // key slots
   p->Wp = padded_width(p->C);
   if (p->Wp > kMaxWp) return RPE_E_UNSUPPORTED;
@@ -309,7 +373,7 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   // each) are left to the per-bucket layout.  It is taken unless it halves the
   // resident waves of the per-bucket layout, whose LDS float atomics cost more.
   const bool tv = d->mode == RPE_MODE_CONTEXTUAL && (d->terms & RPE_TERM_V);
-  const bool vw_ok = tv && p->Wp >= 8 && p->Wp <= 32;
+  const bool vw_ok = tv && !p->und && p->Wp >= 8 && p->Wp <= 32;
   Params best;
   int best_waves = -1;
   Params best_vw;

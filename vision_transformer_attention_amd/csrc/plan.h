@@ -136,6 +136,16 @@ struct Params {
   int rk_lds;               // key term: rK (<= 3 tiles) is copied into the row area once per workgroup
   int n_thr;                // piecewise map: number of thresholds, -1: evaluate g on the device
   int16_t thr[kMaxThresholds];
+  // Undirected maps (und = 1): the index u(dy, dx) depends on k = dy^2 + dx^2
+  // only and is non-decreasing in k, so u = #{m : thr[m] <= k} (thr holds those
+  // k thresholds, n_thr of them).  The prologue tabulates u + H for every offset
+  // of the unit as uint16 [2R-1][u2w] at off_u2 (u2w = 2C+1: the 2C-1 column
+  // offsets, then a column of zi and one of zi+1); the gather of a pair reads
+  // that table at ry(dy) + cx(dx) first and then entry u + H of its target.
+  // Every gather target has entries zi (zero) and zi+1 (-inf) past its nbt*32
+  // computed ones, for pairs without a position term and padding keys.
+  int und;
+  int off_u2, u2w, zi;
 };
 
 // Validation only (no derived plan).  Returns an rpe_status.
@@ -159,6 +169,10 @@ bool contiguous_io(const rpe_attn_desc* d);
 
 // g(x) of one integer offset in float64 (the same formula the device evaluates).
 int axis_index_host(int x, int map, int rounding, double alpha, double beta, double gamma);
+// The undirected index u in [0, half] of an offset of squared length k (rank:
+// sums of two squares below each k, read by the Quantization map only).
+int undirected_index_host(int k, int map, int rounding, double alpha, double beta, double gamma, int half,
+                          const int* rank);
 
 // Full plan for rpe_attn_fwd (pointers left null).  Returns an rpe_status.
 int make_plan(const rpe_attn_desc* d, Params* p);

@@ -43,8 +43,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-_FWD = re.compile(r"_ZN3rpe14rpe_fwd_kernelI(DF16b|f)Li(\d+)ELi(\d)ELj(\d)ELb(\d)ELb(\d)ELb(\d)EEEvNS_6ParamsE")
+_FWD = re.compile(r"_ZN3rpe14rpe_fwd_kernelI(DF16b|f)Li(\d+)ELi(\d)ELj(\d)ELb(\d)ELb(\d)ELi(\d)EEEvNS_6ParamsE")
 _MODES = {"0": "none", "1": "bias", "2": "contextual"}
+_MAPS = {"0": "", "1": ", Cross", "2": ", undirected"}
 
 
 def fwd_name(name):
@@ -52,11 +53,11 @@ def fwd_name(name):
     m = _FWD.search(name)
     if not m:
         return None
-    dt, d, mode, terms, wide, multi, cross = m.groups()
+    dt, d, mode, terms, wide, multi, mk = m.groups()
     t = "".join(c for bit, c in ((1, "K"), (2, "Q"), (4, "V")) if int(terms) & bit)
     return (f"rpe_fwd_kernel<{'bf16' if dt == 'DF16b' else 'fp32'}, d{d}, {_MODES[mode]}"
             f"{' ' + t if t else ''}{', wide rows' if wide == '1' else ''}"
-            f"{', several units per workgroup' if multi == '1' else ''}{', Cross' if cross == '1' else ''}>")
+            f"{', several units per workgroup' if multi == '1' else ''}{_MAPS[mk]}>")
 
 
 def demangle(names):
