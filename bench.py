@@ -272,6 +272,65 @@ def time_backward(name, steps, warmup, dev):
     return ms, ok
 
 
+def measure_roofs(dev):
+    """Ceilings measured on this GPU by librpe_roofs.so (include/rpe_roofs.h), each
+    timed with HIP events on the launch stream after an untimed launch: HBM copy
+    and read of 1 GiB buffers, 20 passes per launch over 38 MB and 77 MB buffers
+    that the Infinity Cache holds, bf16 MFMA, scalar fp32 FMA and exp2 rates."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "vision_transformer_attention_amd", "librpe_roofs.so"))
+    vp, i32, i64, dp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
+    lib.rpe_roof_copy.argtypes = [vp, vp, i64, vp, dp]
+    lib.rpe_roof_read.argtypes = [vp, i64, i32, vp, vp, dp]
+    for f in (lib.rpe_roof_mfma_bf16, lib.rpe_roof_fma_f32, lib.rpe_roof_exp2_f32):
+        f.argtypes = [i32, vp, vp, dp]
+    for f in (lib.rpe_roof_copy, lib.rpe_roof_read, lib.rpe_roof_mfma_bf16, lib.rpe_roof_fma_f32,
+              lib.rpe_roof_exp2_f32):
+        f.restype = i32
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    sink = torch.zeros(64, dtype=torch.float32, device=dev)
+    work = ctypes.c_double(0.0)
+
+    def rate(call, launches):
+        def go(_):
+            st = call()
+            if st != 0:
+                raise RuntimeError(f"roof probe failed with status {st}")
+        go(0)
+        torch.cuda.synchronize()
+        ms, _ = _batched_events(go, launches, stream, batches=1)
+        return work.value / (ms * 1e-3)
+
+    out = {}
+    gib = 1 << 30
+    src = torch.ones(gib // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    out["hbm_copy_GBs"] = rate(lambda: lib.rpe_roof_copy(src.data_ptr(), dst.data_ptr(), gib, sp,
+                                                         ctypes.byref(work)), 10) / 1e9
+    out["hbm_read_GBs"] = rate(lambda: lib.rpe_roof_read(src.data_ptr(), gib, 1, sink.data_ptr(), sp,
+                                                         ctypes.byref(work)), 10) / 1e9
+    del src, dst
+    for mb in (38, 77):
+        buf = torch.ones(mb * 1000 * 1000 // 16 * 4, dtype=torch.float32, device=dev)
+        nb = buf.numel() * 4
+        out[f"cache_read_GBs_{mb}MB"] = rate(lambda: lib.rpe_roof_read(buf.data_ptr(), nb, 20, sink.data_ptr(), sp,
+                                                                       ctypes.byref(work)), 10) / 1e9
+        del buf
+    out["mfma_bf16_TFLOPs"] = rate(lambda: lib.rpe_roof_mfma_bf16(2000, sink.data_ptr(), sp,
+                                                                  ctypes.byref(work)), 3) / 1e12
+    out["fma_f32_TFLOPs"] = rate(lambda: lib.rpe_roof_fma_f32(20000, sink.data_ptr(), sp,
+                                                              ctypes.byref(work)), 5) / 1e12
+    out["exp2_f32_Gps"] = rate(lambda: lib.rpe_roof_exp2_f32(20000, sink.data_ptr(), sp,
+                                                             ctypes.byref(work)), 5) / 1e9
+    torch.cuda.synchronize()
+    out["note"] = ("measured on this GPU (librpe_roofs.so, include/rpe_roofs.h); the roofline fractions use "
+                   "the published peaks, measured_frac the measured HBM copy or bf16 MFMA rate; fma_f32 counts "
+                   "scalar (non-packed) FMAs")
+    return out
+
+
 def summarize(name, ms):
     w = WORKLOADS[name]
     flop, nbytes = flops_bytes(w)
@@ -292,6 +351,7 @@ def main():
     ap.add_argument("--warm-only", action="store_true", help="time one resident buffer set only")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the headline's warm timing (one resident buffer set)")
+    ap.add_argument("--no-roofs", action="store_true", help="skip the measured machine roofs")
     ap.add_argument("--calib-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 read-only passes (a sum) and 3 write-only passes (a fill) "
                          "over MIB MiB: the known bytes that calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -347,6 +407,11 @@ def main():
                     "tflops": 2.5 * fb / (mb * 1e-3) / 1e12, "finite": okb,
                     "note": "kernel sequence over a workspace (matrix-core products for bf16); TFLOP/s counts 2.5x the forward's FLOP"}
         print(f"backward {args.workload}: {mb * 1e3:.1f} us per call", file=sys.stderr, flush=True)
+    roofs = None
+    if not args.no_roofs:
+        roofs = measure_roofs(dev)
+        print("measured roofs: " + ", ".join(f"{k} {v:.1f}" for k, v in roofs.items() if k != "note"),
+              file=sys.stderr, flush=True)
     if args.calib_probe > 0:
         # known bytes: a sum reads the whole tensor (and writes a few partials), a fill
         # writes it (and reads nothing)
@@ -376,6 +441,9 @@ def main():
         roof["traffic_fetch"] = traffic["fetch"]
         roof["traffic_write"] = traffic["write"]
     roof["traffic_source"] = tnote if traffic is None else os.path.relpath(tnote, ROOT)
+    if roofs is not None:
+        roof["measured_peak"] = roofs["hbm_copy_GBs"] if roof["bound"] == "hbm" else roofs["mfma_bf16_TFLOPs"]
+        roof["measured_frac"] = roof["achieved"] / roof["measured_peak"]
     roof["kernel"] = "rpe_fwd_kernel"
     roof["algorithmic_bytes_per_launch"] = nbytes
     roof["algorithmic_flop_per_launch"] = flop
@@ -403,6 +471,7 @@ def main():
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
         "secondary": secondary,
         "backward": backward,
+        "measured_roofs": roofs,
     }
     if ms_warm is not None:
         warm = summarize(args.workload, ms_warm)

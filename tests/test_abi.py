@@ -40,6 +40,35 @@ def test_exports_every_declared_symbol():
     assert lib.rpe_attn_version().decode().startswith("rpe_attn")
 
 
+def test_roof_probes_export_their_header():
+    path = os.path.join(ROOT, "vision_transformer_attention_amd", "librpe_roofs.so")
+    if not os.path.exists(path):
+        pytest.skip("librpe_roofs.so not built (run __graft_entry__.build())")
+    header = open(os.path.join(ROOT, "include", "rpe_roofs.h")).read()
+    declared = set(re.findall(r"^int32_t\s+(rpe_roof_\w+)\s*\(", header, re.M))
+    assert declared == {"rpe_roof_copy", "rpe_roof_read", "rpe_roof_mfma_bf16", "rpe_roof_fma_f32",
+                        "rpe_roof_exp2_f32"}
+    lib = ctypes.CDLL(path)
+    for name in declared:
+        assert hasattr(lib, name), name
+    # argument checks return before any device call
+    work = ctypes.c_double(0.0)
+    f = lib.rpe_roof_copy
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    f.restype = ctypes.c_int32
+    assert f(None, None, 16, None, ctypes.byref(work)) == -1
+    assert f(1, 1, 15, None, ctypes.byref(work)) == -1
+    r = lib.rpe_roof_read
+    r.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.POINTER(ctypes.c_double)]
+    r.restype = ctypes.c_int32
+    assert r(1, 16, 0, 1, None, ctypes.byref(work)) == -1
+    g = lib.rpe_roof_mfma_bf16
+    g.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    g.restype = ctypes.c_int32
+    assert g(0, 1, None, ctypes.byref(work)) == -1
+
+
 def _w_desc(w, **over):
     kw = dict(batch=w.batch, heads=w.heads, head_dim=w.head_dim, grid=(w.grid_h, w.grid_w),
               window=w.window, prefix_tokens=w.prefix, dtype=w.dtype, mode=w.mode,

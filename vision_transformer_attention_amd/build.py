@@ -1,7 +1,8 @@
-"""Build librpe_attn.so for gfx950 in-tree with hipcc.
+"""Build librpe_attn.so (and the roof microbenchmarks, librpe_roofs.so) for
+gfx950 in-tree with hipcc.
 
 Run ``python -m vision_transformer_attention_amd.build`` (or call ``build()``).
-The library lands next to this file and is loaded by the ctypes binding.
+The libraries land next to this file and are loaded by the ctypes bindings.
 """
 
 import os
@@ -13,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librpe_attn.so")
+ROOFS_LIB = os.path.join(HERE, "librpe_roofs.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -29,6 +31,7 @@ SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "bwd.hip", "fwd_dispatch.cpp",
            "fwd_cross_f32_d16.hip", "fwd_cross_f32_d32.hip", "fwd_cross_f32_d64.hip",
            "fwd_und_bf16_d16.hip", "fwd_und_bf16_d32.hip", "fwd_und_bf16_d64.hip",
            "fwd_und_f32_d16.hip", "fwd_und_f32_d32.hip", "fwd_und_f32_d64.hip"]
+ROOFS_SOURCES = ["roofs.hip"]
 
 
 def _run(cmd, verbose):
@@ -45,14 +48,16 @@ def _run(cmd, verbose):
 def build(verbose=True):
     os.makedirs(OBJ, exist_ok=True)
     jobs = []
-    for src in SOURCES:
+    for src in SOURCES + ROOFS_SOURCES:
         obj = os.path.join(OBJ, src + ".o")
         jobs.append(([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
     with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs], verbose)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (ROOFS_LIB, ROOFS_SOURCES)):
+        tmp = lib + ".tmp"
+        objs = [os.path.join(OBJ, s + ".o") for s in srcs]
+        _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        os.replace(tmp, lib)
     return LIB
 
 
