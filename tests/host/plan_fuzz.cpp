@@ -175,7 +175,31 @@ int main(int argc, char** argv) {
     REQUIRE(p.off_zero >= p.off_tab && p.off_neg == p.off_zero + p.zr * p.gsz);
     REQUIRE(p.zr == (p.und ? 1 : (p.S - 1) * p.S + 1));
     int end_g = p.off_neg + p.zr * p.gsz;
-    if (tv && p.vw) {
+    REQUIRE(p.skv == (rpe::skv_value_term(&d, p.Wp) ? 1 : 0));
+    if (tv && p.skv) {
+      // value term per key block: bf16 Product tables on rows of <= 32 slots
+      REQUIRE(d.dtype == RPE_BF16 && p.Wp <= 32 && !p.cross && !p.und && !p.vw);
+      REQUIRE(p.nkr * p.Wp == rpe::kBlockSlots);
+      REQUIRE(p.mw >= 2 * p.C - 1 && (p.mw == 16 || p.mw == 32 || p.mw == 64) && (p.mw == 16 || p.mw / 2 < 2 * p.C - 1));
+      REQUIRE(p.C + p.Wp - 2 < p.mw);
+      REQUIRE(p.pb_rs >= p.nkr * p.mw && p.pb_rs % 16 == 8);
+      REQUIRE(p.pb_bytes >= rpe::kRowTile * p.pb_rs * 2 && p.pb_bytes % 16 == 0);
+      REQUIRE(p.off_pb >= end_g && p.off_pb % 16 == 0);
+      REQUIRE(p.off_pz == p.off_pb + p.NW * p.pb_bytes);
+      REQUIRE(p.rvp == p.D * 2 + 16 && p.skv_rymul * p.gsz == p.rvp);
+      REQUIRE(p.off_rvr >= p.off_pz + 16 && p.off_rvr % 16 == 0);
+      end_g = p.off_rvr + (p.nb * p.rvp + 1023) / 1024 * 1024;
+      // each weight write (4 slots at key columns 8j + 4h .. +3 of its row) stays
+      // in its own (column, key row) segment; reads are 16-byte aligned inside it
+      for (int xi = 0; xi < p.C; ++xi)
+        for (int hh = 0; hh < 2; ++hh)
+          for (int j = 0; j < 4; ++j) {
+            const int s0 = 8 * j + 4 * hh, r = s0 >> p.lwp, x = s0 & (p.Wp - 1);
+            const int mi = x - xi + p.C - 1;
+            REQUIRE(r < p.nkr && mi >= 0 && mi + 4 <= p.mw);
+          }
+      REQUIRE((p.pb_rs * 2) % 16 == 0 && (p.mw * 2) % 32 == 0);
+    } else if (tv && p.vw) {
       // per-column weight sums: [S][Wp] fp32 rows of an odd number of 16-byte chunks
       REQUIRE(p.Wp >= 8 && p.Wp <= 32);
       REQUIRE(p.off_vw >= end_g && p.off_vw % 16 == 0);

@@ -27,13 +27,17 @@
 //       and bucket (eqs. 26-27) with the same MFMA as S^T, kept in LDS (fp16
 //       for bf16 inputs), and gathered per pair (eq. 28);
 //   query term: TQ[j][b] = c * k_j . rQ[b] per key block, gathered per pair;
-//   value term: softmax weights are summed per (query row, row bucket, key
-//       column) in LDS with plain read-modify-writes (each entry has one
-//       owner lane), turned into per-bucket sums by prefix sums over the key
-//       columns, and O^T += rV^T W^T at the end reuses the PV MFMA; grid rows
-//       of 4 or 64 padded columns instead sum per (row, bucket) with LDS float
-//       atomics (a row's entries are only touched by the row's two lanes of one
-//       wave, so the order of the additions is fixed by the instruction stream);
+//   value term, bf16 Product instances (SKV): per key block, O^T += rV''^T P''^T
+//       where P'' holds each query's weights indexed by (row offset, key minus
+//       query column) and rV'' the rV rows of those offsets' buckets, so the
+//       product needs no per-query operand; other instances: softmax weights
+//       are summed per (query row, row bucket, key column) in LDS with plain
+//       read-modify-writes (each entry has one owner lane), turned into
+//       per-bucket sums by prefix sums over the key columns, and O^T += rV^T W^T
+//       at the end reuses the PV MFMA; grid rows of 4 or 64 padded columns
+//       instead sum per (row, bucket) with LDS float atomics (a row's entries
+//       are only touched by the row's two lanes of one wave, so the order of the
+//       additions is fixed by the instruction stream);
 //   bias mode: the head's (2M-1)^2 table, prescaled by log2(e), is gathered.
 // The bucket of a pair is b = (g(dy)+H)*S + (g(dx)+H) with (dy, dx) = query -
 // key; its LDS address is ry(dy) + cx(lane, key column): ry is read from a
@@ -71,6 +75,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// 8 bytes written to an LDS address that is only 2-byte aligned (one ds_write_b64)
+typedef __bf16 bf16x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 
 constexpr int kThreadsMax = kMaxWaves * 64;
 constexpr float kLazyTau = 8.0f;
@@ -214,9 +221,18 @@ rpe_fwd_kernel(Params p) {
   constexpr bool TQ = CTX && (TERMS & RPE_TERM_Q);
   constexpr bool TV = CTX && (TERMS & RPE_TERM_V);
   constexpr bool ROWS = TK || TV;                  // per-row bucket area in LDS
+  // SKV: the value term of bf16 inputs under the Product map (rows of at most 32
+  // slots) is contracted per key block, straight into O: each wave keeps the
+  // block's weights per query column in an LDS buffer and reads them back
+  // shifted by the query's column, so that one MFMA product with rV rows
+  // gathered per (row offset, column offset) adds every pair's rV row with its
+  // weight.  TVW: the other value terms sum weights per bucket over the whole
+  // key stream and contract rV at the end.
+  constexpr bool SKV = BF && TV && !WIDE && MK == kMapProduct;
+  constexpr bool TVW = TV && !SKV;
   // value term with per-column weight sums (the launch plan's vw; never with
   // wide rows, whose [S][64] row areas rarely fit)
-  constexpr bool VW = TV && !WIDE;
+  constexpr bool VW = TVW && !WIDE;
   // One gathered addend per pair from the row area / bias table.  Without a key
   // term the row area is zero and the gather only supplies the -inf of padding
   // keys, unless the query-term gather already does that.
@@ -378,7 +394,7 @@ rpe_fwd_kernel(Params p) {
 
   // ---- the block stream: per unit [Q tiles (multi-unit only)][key/value blocks]
   // [rV tiles]; a Q element carries 64 query rows (32 in each half of a stage)
-  const int n_vt = TV ? p.nbt : 0;
+  const int n_vt = TVW ? p.nbt : 0;
   const int nblk = p.n_blocks;
   const int nqe = multi ? (NW + 1) >> 1 : 0;
   const int epu = nqe + nblk + n_vt;            // elements per unit
@@ -554,8 +570,23 @@ rpe_fwd_kernel(Params p) {
       if (k * 64 + lane < nent) dma4(bt + (k * 64 + lane) * 4, lds_tab + k * 256);
   }
 
+  // ---- SKV: the head's rV rows into LDS with a row pitch of rvp bytes.  Each
+  // instruction fills 1 KB of the padded table: lane l's 16 bytes land at
+  // byte 16 l of it, so the lane fetches the row chunk that lives there (the
+  // 16 pad bytes closing each row take any chunk).
+  if constexpr (SKV) {
+    const uint32_t lds_rvr = lds_ring - p.off_stage + p.off_rvr;
+    const int nins = (p.nb * p.rvp + 1023) >> 10;
+    for (int k = wid; k < nins; k += NW) {
+      const int o = k * 1024 + 16 * lane;
+      const int row = o / p.rvp, inr = o - row * p.rvp;
+      const bool ok = row < p.nb && inr < RB;
+      dma16(rvb + (ok ? row * RB + inr : 0), lds_rvr + k * 1024);
+    }
+  }
+
   // ---- start the ring now (the prologue below overlaps its latency); the Q,
-  // rK and bias loads above are older, so waiting for element 0 also covers them.
+  // rK, bias and rV loads above are older, so waiting for element 0 also covers them.
   int st_cur = 0, st_iss = 0;
   int iss_k = 0, iss_loc = 0;   // unit and position of the next element to issue
   auto issue_next = [&]() {
@@ -644,7 +675,7 @@ rpe_fwd_kernel(Params p) {
   if constexpr (MODE == RPE_MODE_NONE) {
     for (int i = tid; i < p.nb; i += nth) gtab[i] = 0.0f;
   }
-  if constexpr (TV) {
+  if constexpr (TVW) {
     if (VW && p.vw) {
       const int nch = NW * kRowTile * p.vw_pitch / 16;
       for (int i = tid; i < nch; i += nth) reinterpret_cast<f32x4*>(smem + p.off_vw)[i] = f32x4{};
@@ -655,6 +686,11 @@ rpe_fwd_kernel(Params p) {
       const int wsz = (p.off_neg + p.zr * GSZ - p.off_tab) * (4 / GSZ) / 4;
       for (int i = tid; i < wsz; i += nth) wsum[i] = 0.0f;
     }
+  }
+  if constexpr (SKV) {
+    // the waves' weight buffers (their gaps stay zero from here on) and the zero chunk
+    const int n16 = (NW * p.pb_bytes + 16) >> 4;
+    for (int i = tid; i < n16; i += nth) reinterpret_cast<uint4*>(smem + p.off_pb)[i] = make_uint4(0, 0, 0, 0);
   }
   if constexpr (CTX && GATHER && !TK) {
     for (int i = tid; i < NW * kRowTile * p.p_tab; i += nth) {
@@ -831,11 +867,11 @@ rpe_fwd_kernel(Params p) {
   // per-column weight sums (vw = 1): this row's [S][Wp] area, the byte offset of
   // this lane's 4-column group j at phase ph within a row bucket, and the lane's
   // 16-byte slot for the writes of merged entries
-  const int vrowoff = TV ? p.off_vw + (wid * kRowTile + r32) * p.vw_pitch : 0;
-  const int vdum = TV ? p.off_vd + (wid * 64 + lane) * 16 : 0;
-  int vcol[TV ? NPH : 1][4];
+  const int vrowoff = TVW ? p.off_vw + (wid * kRowTile + r32) * p.vw_pitch : 0;
+  const int vdum = TVW ? p.off_vd + (wid * 64 + lane) * 16 : 0;
+  int vcol[TVW ? NPH : 1][4];
 #pragma unroll
-  for (int ph = 0; ph < (TV ? NPH : 1); ++ph)
+  for (int ph = 0; ph < (TVW ? NPH : 1); ++ph)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       vcol[ph][j] = vrowoff + 4 * (WIDE ? 32 * ph + 8 * j + 4 * h : (8 * j + 4 * h) & (p.Wp - 1));
@@ -882,6 +918,50 @@ rpe_fwd_kernel(Params p) {
       }
     }
   }
+  // ---- SKV constants.  The wave's query tile spans grid rows yq0..yq1 and a key
+  // block rows yk0..yk0+nkr-1, so the block's pairs have row offsets
+  // dy = yq0 - (yk0 + nkr - 1) + dl, dl in [0, nd), nd = yq1 - yq0 + nkr.  The
+  // contraction index is (dl, mi): mi = xj - xi + C - 1 is the key-minus-query
+  // column offset shifted to [0, mw), so dx = C - 1 - mi does not depend on the
+  // query.  Lane (i, h) writes its weights of key row r at slot mi of that
+  // row's segment in its query column's region, and reads the B operand of
+  // chunk ch (mi = 16 ch + 8 h + 0..7) from key row r = (yi - yq0) + nkr - 1 - dl
+  // of it; the A operand holds the rV rows of bucket (g(dy)+H, g(dx)+H)
+  // (ds_read_tr16_b64: lane (h, m4, a) fetches k slot m4 (first read) and 4 + m4
+  // (second read) of its 8).
+  bool skv_on = false;
+  int skv_yq0 = 0, skv_nd = 0, skv_rho = 0, skv_w = 0, skv_x0 = 0, skv_z = 0;
+  int skv_a[4][2];
+  if constexpr (SKV) {
+    const int qf0 = (rt0 + wid) * kRowTile;
+    const int tf = qf0 > p.P ? qf0 : p.P;
+    const int tl = qf0 + kRowTile - 1 < p.T - 1 ? qf0 + kRowTile - 1 : p.T - 1;
+    skv_on = active && tf <= tl;
+    if (skv_on) {
+      skv_yq0 = static_cast<int>(fdiv(static_cast<uint32_t>(tf - p.P), p.dv_C));
+      const int yq1 = static_cast<int>(fdiv(static_cast<uint32_t>(tl - p.P), p.dv_C));
+      skv_nd = yq1 - skv_yq0 + p.nkr;
+    }
+    skv_rho = yi - skv_yq0;
+    const int region = lds0 + p.off_pb + wid * p.pb_bytes + r32 * p.pb_rs * 2;
+    skv_w = region + (p.C - 1 - xi) * 2;   // (2-byte aligned: xi moves it by one slot)
+    skv_x0 = region + 16 * h;
+    skv_z = lds0 + p.off_pz;
+    const int m4 = (lane & 15) >> 2;
+    int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // head-dim column of the transpose read
+    if (col >= D) col = 0;                                 // beyond the head dim: unused outputs
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int mi = 16 * ch + 8 * h + 4 * k + m4;
+        // (offsets past 2C-2 meet zero weights: any row will do)
+        const int c = mi <= 2 * p.C - 2 ? cx_tab[2 * p.C - 2 - mi] : 0;
+        skv_a[ch][k] = c * p.rvp + col * 2;
+      }
+    }
+  }
+  (void)skv_on;
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
   {
@@ -950,6 +1030,98 @@ rpe_fwd_kernel(Params p) {
   };
   // byte offset of the query-term row part from the gather row part
   auto tq_row = [&](int ryb) -> int { return GSZ == 4 ? ryb : ryb * (4 / GSZ); };
+
+  // SKV: this lane's weights of grid block gblk (pkv, the packed B operands of
+  // PV; prefix keys kept in padding columns zeroed) into its query column's
+  // region (every block writes the same slots, the others stay zero), then
+  // O^T += rV''^T P''^T over the block's offsets (dl, mi).
+  auto skv_block = [&](int gblk, const bf16x8 (&pkv)[2], const bool (&vzm)[4][4], bool use_vz)
+      __attribute__((always_inline)) {
+    if constexpr (SKV) {
+      const int rstr = p.mw * 2;
+      if (qpos) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int s0 = 8 * j + 4 * h;
+          const int r = s0 >> p.lwp, x = s0 & (p.Wp - 1);
+          bf16x4_a2 w4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const __bf16 v = pkv[j >> 1][4 * (j & 1) + i];
+            w4[i] = (use_vz && vzm[j][i]) ? static_cast<__bf16>(0.0f) : v;
+          }
+          *reinterpret_cast<__attribute__((address_space(3))) bf16x4_a2*>(
+              static_cast<uintptr_t>(static_cast<uint32_t>(skv_w + r * rstr + x * 2))) = w4;
+        }
+      }
+      const int dmin = skv_yq0 - (gblk + 1) * p.nkr + 1;
+      // lane dl fetches the row part of offset dmin + dl (rows outside the unit,
+      // whose weights are zero, clamp to its edge): one LDS round trip per block
+      int dd = dmin + (lane < skv_nd ? lane : 0);
+      dd = dd < 1 - p.R ? 1 - p.R : (dd > p.R - 1 ? p.R - 1 : dd);
+      const int ryl = ry_tab[dd + p.R - 1];
+      // Work goes in units of NCU <= 2 chunks of one offset (NPD units per
+      // offset), in pairs through two register sets: the reads of unit u+1 are
+      // issued before the products of unit u, so that LDS latency overlaps the
+      // matrix cores.  NCH = mw / 16 chunks per offset.
+      auto run = [&](auto nch_c) __attribute__((always_inline)) {
+        constexpr int NCH = decltype(nch_c)::value;
+        constexpr int NCU = NCH >= 2 ? 2 : 1;
+        constexpr int NPD = NCH / NCU;
+        bf16x8 bv[2][NCU];
+        bf16x8 av[2][NCU][DTL];
+        auto load = [&](int u, auto buf_c) __attribute__((always_inline)) {
+          constexpr int BUF = decltype(buf_c)::value;
+          const int dl = NPD == 2 ? u >> 1 : u;
+          const bool hi = NPD == 2 && (u & 1);
+          const int ry = __builtin_amdgcn_readlane(ryl, dl);
+          const int abase = lds0 + p.off_rvr + ry * p.skv_rymul;
+          const int r = skv_rho + p.nkr - 1 - dl;
+          const bool bok = qpos && r >= 0 && r < p.nkr;
+          const int b0 = skv_x0 + r * rstr + (hi ? 32 * NCU : 0);
+#pragma unroll
+          for (int ch = 0; ch < NCU; ++ch) {
+            const u32x4 bu = lds_at<u32x4>(bok ? b0 + 32 * ch : skv_z);
+            __builtin_memcpy(&bv[BUF][ch], &bu, 16);
+            const int a0 = hi ? skv_a[NCU + ch][0] : skv_a[ch][0];
+            const int a1 = hi ? skv_a[NCU + ch][1] : skv_a[ch][1];
+#pragma unroll
+            for (int c = 0; c < DTL; ++c) {
+              const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4_t>(
+                  static_cast<uintptr_t>(static_cast<uint32_t>(abase + a0 + 64 * c))));
+              const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4_t>(
+                  static_cast<uintptr_t>(static_cast<uint32_t>(abase + a1 + 64 * c))));
+              __builtin_memcpy(&av[BUF][ch][c], &v0, 8);
+              __builtin_memcpy(reinterpret_cast<char*>(&av[BUF][ch][c]) + 8, &v1, 8);
+            }
+          }
+        };
+        auto product = [&](auto buf_c) __attribute__((always_inline)) {
+          constexpr int BUF = decltype(buf_c)::value;
+#pragma unroll
+          for (int ch = 0; ch < NCU; ++ch)
+#pragma unroll
+            for (int c = 0; c < DTL; ++c) oacc[c] = mfma32(av[BUF][ch][c], bv[BUF][ch], oacc[c]);
+        };
+        const int last = skv_nd * NPD - 1;
+        load(0, std::integral_constant<int, 0>{});
+        for (int u = 0; u <= last; u += 2) {
+          // (past the last unit the reads repeat it and go unused)
+          load(u + 1 <= last ? u + 1 : last, std::integral_constant<int, 1>{});
+          product(std::integral_constant<int, 0>{});
+          load(u + 2 <= last ? u + 2 : last, std::integral_constant<int, 0>{});
+          if (u + 1 <= last) product(std::integral_constant<int, 1>{});
+        }
+      };
+      if (p.mw == 16)
+        run(std::integral_constant<int, 1>{});
+      else if (p.mw == 32)
+        run(std::integral_constant<int, 2>{});
+      else
+        run(std::integral_constant<int, 4>{});
+    }
+  };
+  (void)skv_block;
 
   // One key block: logits, lazy online softmax, PV (and the value-term scatter).
   // INTERIOR: every slot is a grid key of rows < R-1 or a padding column.
@@ -1110,7 +1282,7 @@ rpe_fwd_kernel(Params p) {
         l_part *= alpha;
 #pragma unroll
         for (int c = 0; c < DTL; ++c) oacc[c] *= alpha;
-        if constexpr (TV) {
+        if constexpr (TVW) {
           if (need) {
             if (VW && p.vw) {
               f32x4* const vr = reinterpret_cast<f32x4*>(smem + vrowoff);
@@ -1131,7 +1303,7 @@ rpe_fwd_kernel(Params p) {
       }
     }
     l_part += bsum;
-    if constexpr (TV) {
+    if constexpr (TVW) {
       if (VW && p.vw) {
         // (the prefix block's keys carry no value term)
         if (!prefix_blk) {
@@ -1192,6 +1364,10 @@ rpe_fwd_kernel(Params p) {
       pv_packed(vtile, pk);
     else
       pv_tile(vtile, pr, false);
+    // (the prefix block's keys carry no value term)
+    if constexpr (SKV) {
+      if (!prefix_blk && skv_on) skv_block(gblk, pk, vz, !INTERIOR);
+    }
   };
   // phase dispatch (a 64-slot grid row spans two blocks)
   auto process = [&](auto interior_c, auto first_c, const char* kt, const char* vt, int gblk, bool pre,
@@ -1493,7 +1669,7 @@ rpe_fwd_kernel(Params p) {
       }
     }
     // value term: O^T += rV^T W^T (W split into two bf16 parts for accuracy)
-    if constexpr (TV) {
+    if constexpr (TVW) {
       if (VW && p.vw && active) {
         // per-column sums -> prefix sums over the key columns.  Each lane of the
         // row takes every other row bucket, four at a time as independent add
@@ -1638,6 +1814,11 @@ rpe_fwd_kernel(Params p) {
 
 template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, int MK>
 hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
+  // the instance contracts the value term per block exactly when the plan laid
+  // out its buffers for that
+  constexpr bool kSkv = std::is_same<DT, __bf16>::value && MODE == RPE_MODE_CONTEXTUAL && (TERMS & RPE_TERM_V) &&
+                        !WIDE && MK == kMapProduct;
+  if (kSkv != (p.skv != 0)) return hipErrorInvalidValue;
   auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, MULTI, MK>;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);

@@ -73,7 +73,25 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   p->off_zero = off; off += p->zr * p->gsz;
   p->off_neg = off; off += p->zr * p->gsz;
   off = align(off, 16);
-  if (tv && p->vw) {
+  if (tv && p->skv) {
+    p->nkr = kBlockSlots >> p->lwp;
+    // 1, 2 or 4 chunks of 16 offsets (the kernel's instantiations); the weights of
+    // a key row land at offsets xj - xi + C - 1 in [0, C + Wp - 2], inside mw
+    p->mw = 2 * p->C - 1 <= 16 ? 16 : (2 * p->C - 1 <= 32 ? 32 : 64);
+    if (p->C + p->Wp - 2 >= p->mw) return RPE_E_UNSUPPORTED;
+    // a query column's region, padded to 8 mod 16 slots: consecutive columns
+    // then start 36 mod 64 dwords apart (a 4-dword-aligned bank group each), so
+    // the 16-byte reads of a wave's columns spread over the LDS banks
+    p->pb_rs = p->nkr * p->mw;
+    while (p->pb_rs % 16 != 8) p->pb_rs += 4;
+    p->pb_bytes = align(kRowTile * p->pb_rs * 2, 16);
+    p->off_pb = off; off += p->NW * p->pb_bytes;
+    p->off_pz = off; off += 16;
+    p->rvp = p->D * eb + 16;
+    p->skv_rymul = p->rvp / p->gsz;
+    // copied 1 KB per direct-to-LDS instruction
+    p->off_rvr = off; off += align(p->nb * p->rvp, 1024);
+  } else if (tv && p->vw) {
     // [S][Wp] fp32 per query row; the row pitch is an odd number of 16-byte
     // chunks, so that the 16-byte accesses of consecutive rows fall in
     // different LDS banks
@@ -367,13 +385,16 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   // depths whose LDS plan fits, take the one with the most resident waves per
   // CU (4 SIMDs x waves_per_simd waves, and as many workgroups as LDS allows),
   // then the deeper ring, then the wider workgroup.
-  // The value term sums weights per (row bucket, key column) (vw = 1) when
+  // bf16 value terms under directed Product maps on rows of at most 32 slots are
+  // contracted per key block (skv) and need no weight sums.  Otherwise the
+  // value term sums weights per (row bucket, key column) (vw = 1) when
   // that fits: two lanes share each query row, and with grid rows of 4 padded
   // columns they would share key columns as well; grid rows of 64 (two blocks
   // each) are left to the per-bucket layout.  It is taken unless it halves the
   // resident waves of the per-bucket layout, whose LDS float atomics cost more.
   const bool tv = d->mode == RPE_MODE_CONTEXTUAL && (d->terms & RPE_TERM_V);
-  const bool vw_ok = tv && !p->und && p->Wp >= 8 && p->Wp <= 32;
+  p->skv = skv_value_term(d, p->Wp) ? 1 : 0;
+  const bool vw_ok = tv && !p->skv && !p->und && p->Wp >= 8 && p->Wp <= 32;
   Params best;
   int best_waves = -1;
   Params best_vw;

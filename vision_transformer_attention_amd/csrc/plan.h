@@ -146,10 +146,29 @@ struct Params {
   // computed ones, for pairs without a position term and padding keys.
   int und;
   int off_u2, u2w, zi;
+  // Value term contracted per key block (skv = 1: bf16 inputs, directed map,
+  // Product method, grid rows of at most 32 padded columns).  A key block
+  // covers nkr = 32 / Wp grid rows.  Each wave keeps, per query column i (at
+  // column xi), the bf16 weights of the block's key row r and key column xj at
+  //   off_pb + wave * pb_bytes + (i * pb_rs + r * mw + xj - xi + C - 1) * 2,
+  // i.e. indexed by the key-minus-query column offset shifted to [0, C+Wp-2]:
+  // mw (2C-1 rounded up to 16, 32 or 64) slots per key row, zero where no key
+  // lands, so that 16-byte reads at offsets 16 ch + 8 h are aligned.  off_pz: 16
+  // zero bytes read for key rows outside the block.  rV rows sit at off_rvr with
+  // a pitch of rvp bytes (row bytes + 16); ry_tab entries times skv_rymul give
+  // a row bucket's byte offset there.
+  int skv, nkr, mw, pb_rs, pb_bytes, off_pb, off_pz, rvp, off_rvr, skv_rymul;
 };
 
 // Validation only (no derived plan).  Returns an rpe_status.
 int validate(const rpe_attn_desc* d);
+
+// Whether the forward contracts the value term per key block (the planner's skv):
+// bf16, contextual value term, directed map, Product method, Wp <= 32.
+inline bool skv_value_term(const rpe_attn_desc* d, int Wp) {
+  return d->dtype == RPE_BF16 && d->mode == RPE_MODE_CONTEXTUAL && (d->terms & RPE_TERM_V) &&
+         d->method == RPE_METHOD_PRODUCT && d->map < RPE_MAP_EUCLIDEAN && Wp <= 32;
+}
 
 // A descriptor with a table and an undirected map (Euclidean or Quantization).
 inline bool is_undirected(const rpe_attn_desc* d) {
