@@ -281,23 +281,32 @@ __global__ void __launch_bounds__(64) bwd_rowtab_mfma_kernel(BwdArgs a) {
 template <int D>
 __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
-  const __bf16* const q = static_cast<const __bf16*>(a.q);
-  const __bf16* const k = static_cast<const __bf16*>(a.k);
-  const __bf16* const v = static_cast<const __bf16*>(a.v);
-  const __bf16* const dO = static_cast<const __bf16*>(a.dout);
   const int lane = threadIdx.x, h = lane >> 5, r32 = lane & 31;
   const int nrt = (a.T + 31) / 32;
   const int64_t wgs = a.n_units * nrt;
+  const int T = a.T, nb = a.nb;
   for (int64_t wg = blockIdx.x; wg < wgs; wg += gridDim.x) {
     const int64_t ub = div_idx(wg, nrt);
     const int i0 = static_cast<int>(wg - ub * nrt) * 32;
     const Unit x = unit_of(a, ub);
-    const int64_t tb = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
+    // the unit's slices (wave-uniform bases); offsets inside them are 32-bit
+    // (T * T and T * nb stay below 2^31), which keeps the epilogue's sixteen
+    // pairs per lane in few registers
+    const __bf16* const q = static_cast<const __bf16*>(a.q) + x.base;
+    const __bf16* const k = static_cast<const __bf16*>(a.k) + x.base;
+    const __bf16* const v = static_cast<const __bf16*>(a.v) + x.base;
+    const __bf16* const dO = static_cast<const __bf16*>(a.dout) + x.base;
+    float* const Pu = a.P + ub * T * T;
+    float* const dLu = a.dL + ub * T * T;
+    const float* const Wq = a.rk ? a.Wq + ub * T * nb : nullptr;
+    const float* const Wk = a.rq ? a.Wk + ub * T * nb : nullptr;
+    const float* const Wv = a.rv ? a.Wv + ub * T * nb : nullptr;
+    const float* const bt = a.bias ? a.bias + (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(nb) : nullptr;
     // A operands: query row i0 + r32 (clamped), head-dim slice 16 kk + 8 h
     bf16x8_t qa[KS], da[KS];
     {
-      const int ir = i0 + r32 < a.T ? i0 + r32 : a.T - 1;
-      const int64_t ro = x.base + static_cast<int64_t>(token_of(a, x.u, ir)) * D + 8 * h;
+      const int ir = i0 + r32 < T ? i0 + r32 : T - 1;
+      const int ro = token_of(a, x.u, ir) * D + 8 * h;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const uint4 u = *reinterpret_cast<const uint4*>(q + ro + 16 * kk);
@@ -314,12 +323,12 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-      lse[e] = a.lse[x.bh * a.N + token_of(a, x.u, i < a.T ? i : a.T - 1)] * kLog2e;
+      lse[e] = a.lse[x.bh * a.N + token_of(a, x.u, i < T ? i : T - 1)] * kLog2e;
     }
-    for (int j0 = 0; j0 < a.T; j0 += 32) {
+    for (int j0 = 0; j0 < T; j0 += 32) {
       const int j = j0 + r32;
-      const int jr = j < a.T ? j : a.T - 1;
-      const int64_t co = x.base + static_cast<int64_t>(token_of(a, x.u, jr)) * D + 8 * h;
+      const int jr = j < T ? j : T - 1;
+      const int co = token_of(a, x.u, jr) * D + 8 * h;
       f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
@@ -338,42 +347,41 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        const int64_t pij = static_cast<int64_t>(i < a.T ? i : a.T - 1) * a.T + jr;
+        const int pij = (i < T ? i : T - 1) * T + jr;
         bk[e] = a.bmap[pij];
         bk1[e] = a.bmap1 ? a.bmap1[pij] : -1;
       }
-      float add[16], badd[16], dvt[16];
+      float add[16], dvt[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        const int ic = i < a.T ? i : a.T - 1;
+        const int ic = i < T ? i : T - 1;
         const int bc = bk[e] < 0 ? 0 : bk[e];
-        const int64_t wi = (ub * a.T + ic) * a.nb, wj = (ub * a.T + jr) * a.nb;
+        const int wi = ic * nb, wj = jr * nb;
+        // logit addend in log2 units and the value term's part of dP
         float r = 0.0f, u = 0.0f, bb = 0.0f;
-        if (a.rk) r += a.Wq[wi + bc];
-        if (a.rq) r += a.Wk[wj + bc];
-        if (a.rv) u = a.Wv[wi + bc];
-        if (a.bias) bb = a.bias[tb + bc];
+        if (Wq) r += Wq[wi + bc];
+        if (Wk) r += Wk[wj + bc];
+        if (Wv) u = Wv[wi + bc];
+        if (bt) bb = bt[bc];
         if (a.bmap1) {
           const int b1 = bk1[e] < 0 ? 0 : bk1[e];
-          if (a.rk) r += a.Wq[wi + b1];
-          if (a.rq) r += a.Wk[wj + b1];
-          if (a.rv) u += a.Wv[wi + b1];
-          if (a.bias) bb += a.bias[tb + b1];
+          if (Wq) r += Wq[wi + b1];
+          if (Wk) r += Wk[wj + b1];
+          if (Wv) u += Wv[wi + b1];
+          if (bt) bb += bt[b1];
         }
-        bb *= kLog2e;
-        add[e] = bk[e] >= 0 ? r : 0.0f;
-        badd[e] = bk[e] >= 0 ? bb : 0.0f;
+        add[e] = bk[e] >= 0 ? r * scale2 + bb * kLog2e : 0.0f;
         dvt[e] = bk[e] >= 0 ? u : 0.0f;
       }
-      if (j < a.T) {
+      if (j < T) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (i < a.T) {
-            const int64_t o = (ub * a.T + i) * a.T + j;
-            a.P[o] = __builtin_amdgcn_exp2f((sacc[e] + add[e]) * scale2 + badd[e] - lse[e]);
-            a.dL[o] = pacc[e] + dvt[e];
+          if (i < T) {
+            const int o = i * T + j;
+            Pu[o] = __builtin_amdgcn_exp2f(sacc[e] * scale2 + add[e] - lse[e]);
+            dLu[o] = pacc[e] + dvt[e];
           }
         }
       }
