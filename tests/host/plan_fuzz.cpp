@@ -105,7 +105,10 @@ int main(int argc, char** argv) {
     REQUIRE(p.off_stage == 0);
     REQUIRE(p.off_rq >= p.stages * 2 * rpe::kBlockSlots * p.D * p.elem_bytes && p.off_rq % 16 == 0);
     REQUIRE(p.off_rq <= p.off_tab);
-    if (tq) REQUIRE(p.off_rq + p.nrq * p.kpitch * p.elem_bytes <= p.off_rkc);
+    // the query-term table is staged unless the plan keeps one tile per wave in
+    // registers (bf16, no Cross, rows of at most 32 slots, nbt <= NW)
+    REQUIRE(p.rq_regs == ((tq && d.dtype == RPE_BF16 && !p.cross && p.Wp != 64 && p.nbt <= p.NW) ? 1 : 0));
+    if (tq && !p.rq_regs) REQUIRE(p.off_rq + p.nrq * p.kpitch * p.elem_bytes <= p.off_rkc);
     REQUIRE(p.off_rkc >= p.off_rq && p.off_rkc % 16 == 0 && p.off_bx >= p.off_rkc && p.off_bx % 16 == 0);
     REQUIRE(p.off_tab >= p.off_bx);
     // Cross: 2S table rows (the staged query-term table holds exactly those), the key
@@ -224,7 +227,8 @@ int main(int argc, char** argv) {
       end_g = p.off_w + (p.off_neg + p.zr * p.gsz - p.off_tab) * (4 / p.gsz);
     }
     if (tq) {
-      REQUIRE(p.off_tq >= end_g && p.p_tq >= p.nbt * rpe::kRowTile && (p.p_tq & 1));
+      REQUIRE(p.off_tq >= end_g && p.p_tq >= p.nbt * rpe::kRowTile + (p.und ? 2 : 0));
+      REQUIRE(p.p_tq & 1);   // odd word pitch (fp32 entries)
       REQUIRE(p.off_tqz == p.off_tq + rpe::kBlockSlots * p.p_tq * 4 && p.off_tqn == p.off_tqz + p.zr * 4);
       end_g = p.off_tqn + p.zr * 4;
     }

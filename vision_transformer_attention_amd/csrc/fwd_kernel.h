@@ -391,6 +391,21 @@ rpe_fwd_kernel(Params p) {
   if constexpr (!CROSS) {
     if (!p.rk_lds) load_rk(0);
   }
+  // rQ rows of this wave's query-term tile (buckets 32 wid + r32) as the A operand
+  // of the block scores, in registers when the plan says so (p.rq_regs); rows past
+  // nb are zero (their scores are never read)
+  constexpr bool RQR = TQ && BF && !CROSS && !WIDE;
+  bf16x8 rqa[RQR ? KS : 1];
+  if constexpr (RQR) {
+    const DT* rqt = reinterpret_cast<const DT*>(p.rq) + head * p.tab_head_stride;
+    const int b = kRowTile * wid + r32;
+    const bool ok = p.rq_regs && b < p.nb;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int d0 = 16 * kk + 8 * h;
+      rqa[kk] = as_bf16x8((ok && d0 < D) ? ld16(rqt + static_cast<int64_t>(b) * D + d0) : make_uint4(0, 0, 0, 0));
+    }
+  }
 
   // ---- the block stream: per unit [Q tiles (multi-unit only)][key/value blocks]
   // [rV tiles]; a Q element carries 64 query rows (32 in each half of a stage)
@@ -699,7 +714,7 @@ rpe_fwd_kernel(Params p) {
       gtab[i] = static_cast<GT>(neg ? -INFINITY : 0.0f);
     }
   }
-  if constexpr (TQ) {
+  if (TQ && !p.rq_regs) {
     // rQ staged as [nrq][kpitch]: nbt*32 rows (rows past nb zero), or the 2S Cross rows
     const DT* rq = reinterpret_cast<const DT*>(p.rq) + head * p.tab_head_stride;
     constexpr int CH = D / EPC;
@@ -1068,8 +1083,8 @@ rpe_fwd_kernel(Params p) {
         constexpr int NCH = decltype(nch_c)::value;
         constexpr int NCU = NCH >= 2 ? 2 : 1;
         constexpr int NPD = NCH / NCU;
-        bf16x8 bv[2][NCU];
-        bf16x8 av[2][NCU][DTL];
+        bf16x8 bv[TQ ? 1 : 2][NCU];
+        bf16x8 av[TQ ? 1 : 2][NCU][DTL];
         auto load = [&](int u, auto buf_c) __attribute__((always_inline)) {
           constexpr int BUF = decltype(buf_c)::value;
           const int dl = NPD == 2 ? u >> 1 : u;
@@ -1104,13 +1119,21 @@ rpe_fwd_kernel(Params p) {
             for (int c = 0; c < DTL; ++c) oacc[c] = mfma32(av[BUF][ch][c], bv[BUF][ch], oacc[c]);
         };
         const int last = skv_nd * NPD - 1;
-        load(0, std::integral_constant<int, 0>{});
-        for (int u = 0; u <= last; u += 2) {
-          // (past the last unit the reads repeat it and go unused)
-          load(u + 1 <= last ? u + 1 : last, std::integral_constant<int, 1>{});
-          product(std::integral_constant<int, 0>{});
-          load(u + 2 <= last ? u + 2 : last, std::integral_constant<int, 0>{});
-          if (u + 1 <= last) product(std::integral_constant<int, 1>{});
+        if constexpr (TQ) {
+          // (query-term instances: one register set, for their register budget)
+          for (int u = 0; u <= last; ++u) {
+            load(u, std::integral_constant<int, 0>{});
+            product(std::integral_constant<int, 0>{});
+          }
+        } else {
+          load(0, std::integral_constant<int, 0>{});
+          for (int u = 0; u <= last; u += 2) {
+            // (past the last unit the reads repeat it and go unused)
+            load(u + 1 <= last ? u + 1 : last, std::integral_constant<int, 1>{});
+            product(std::integral_constant<int, 0>{});
+            load(u + 2 <= last ? u + 2 : last, std::integral_constant<int, 0>{});
+            if (u + 1 <= last) product(std::integral_constant<int, 1>{});
+          }
         }
       };
       if (p.mw == 16)
@@ -1386,7 +1409,9 @@ rpe_fwd_kernel(Params p) {
   // The A operand of lane r32 is staged row ra (bucket 32t + r32), plus row rb
   // under Cross (the bucket's row-offset row ra = b / S and column-offset row
   // rb = S + b % S, both multiplied into the accumulator).
-  auto query_tile = [&](const char* ktile, int t, int ra, int rb) __attribute__((always_inline)) {
+  auto query_tile = [&](const char* ktile, int t, int ra, int rb, auto regs_c) __attribute__((always_inline)) {
+    // REGS: the A operand is this wave's rQ tile in registers (t == wid)
+    constexpr bool REGS = decltype(regs_c)::value;
     if constexpr (TQ) {
       const int sw = r32 & (CPR - 1);
       const char* rqs = smem + p.off_rq;
@@ -1395,9 +1420,14 @@ rpe_fwd_kernel(Params p) {
       for (int kk = 0; kk < KS; ++kk) {
         if constexpr (BF) {
           const int c = 2 * kk + h, d0 = 16 * kk + 8 * h;
-          const uint4 a = *reinterpret_cast<const uint4*>(rqs + (ra * p.kpitch + d0) * 2);
+          bf16x8 av;
+          if constexpr (REGS) {
+            av = rqa[kk];
+          } else {
+            av = as_bf16x8(*reinterpret_cast<const uint4*>(rqs + (ra * p.kpitch + d0) * 2));
+          }
           const uint4 kv = *reinterpret_cast<const uint4*>(ktile + r32 * RB + ((c ^ sw) << 4));
-          acc = mfma32(as_bf16x8(a), as_bf16x8(kv), acc);
+          acc = mfma32(av, as_bf16x8(kv), acc);
           if constexpr (CROSS) {
             const uint4 a1 = *reinterpret_cast<const uint4*>(rqs + (rb * p.kpitch + d0) * 2);
             acc = mfma32(as_bf16x8(a1), as_bf16x8(kv), acc);
@@ -1424,10 +1454,14 @@ rpe_fwd_kernel(Params p) {
           const int b0 = kRowTile * t + r32;
           const int b = b0 < p.nb ? b0 : p.nb - 1;
           const int ra = static_cast<int>(fdiv(static_cast<uint32_t>(b), p.dv_S));
-          query_tile(ktile, t, ra, p.S + b - ra * p.S);
+          query_tile(ktile, t, ra, p.S + b - ra * p.S, bool_c<false>{});
         }
       } else {
-        for (int t = wid; t < p.nbt; t += NW) query_tile(ktile, t, kRowTile * t + r32, 0);
+        if (RQR && p.rq_regs) {
+          if (wid < p.nbt) query_tile(ktile, wid, 0, 0, bool_c<RQR>{});
+        } else {
+          for (int t = wid; t < p.nbt; t += NW) query_tile(ktile, t, kRowTile * t + r32, 0, bool_c<false>{});
+        }
       }
     }
   };
@@ -1568,6 +1602,10 @@ rpe_fwd_kernel(Params p) {
   if constexpr (BF) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(qb[kk]));
+    if constexpr (RQR) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(rqa[kk]));
+    }
   } else {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(qf[kk]));

@@ -53,7 +53,12 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   off += p->stages * 2 * kBlockSlots * p->D * eb;
   p->off_rq = off;
   p->nrq = p->cross ? 2 * p->S : p->nbt * kRowTile;
-  if (tq) off += align(p->nrq * p->kpitch * eb, 16);
+  // bf16 tables of at most one 32-row tile per wave: each wave keeps its tile's
+  // rows in registers instead (the Cross rows pair up per bucket and stay
+  // staged, and so do those of rows of 64 slots, whose instances have no
+  // registers to spare)
+  p->rq_regs = (tq && d->dtype == RPE_BF16 && !p->cross && p->Wp != 64 && p->nbt <= p->NW) ? 1 : 0;
+  if (tq && !p->rq_regs) off += align(p->nrq * p->kpitch * eb, 16);
   // Cross key term: the table's 2S rows as swizzled [32][D] tiles (read per lane)
   p->off_rkc = off;
   if (p->cross && ctx && (d->terms & RPE_TERM_K)) off += ((2 * p->S + kRowTile - 1) / kRowTile) * kRowTile * p->D * eb;
@@ -105,10 +110,13 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
     off += align((p->off_neg + p->zr * p->gsz - p->off_tab) * (4 / p->gsz), 16);
   }
   if (tq) {
+    // query-term scores of the current key block, fp32 (fp16 entries measured
+    // slower: the query-term instances run 10-45% longer with them)
     p->p_tq = odd_word_pitch(p->nbt * kRowTile + (p->und ? 2 : 0), 4);
     p->off_tq = off; off += kBlockSlots * p->p_tq * 4;
     p->off_tqz = off; off += p->zr * 4;
     p->off_tqn = off; off += p->zr * 4;
+    off = align(off, 16);
   }
   p->off_ry = off; off += (2 * p->R - 1) * 4;
   p->off_cx = off; off += (2 * p->C - 1) * 4;
