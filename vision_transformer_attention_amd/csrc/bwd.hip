@@ -24,6 +24,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "bwd.h"
 
@@ -393,8 +394,8 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
 // sums Wq[b] = sum_j dL_ij and Wv[b] = sum_j P_ij over the pairs that read
 // row b; one wave per (unit, i), its
 // lanes over j.  LDS: the sums are formed in the wave's own 2 * nb floats
-// (zeroed, LDS float atomics, then written out in full); global: float
-// atomics into the zeroed rows (tables too large for LDS).
+// (zeroed, float atomics of values folded within lane quads, then written out
+// in full); global: float atomics into the zeroed rows (tables too large for LDS).
 template <bool LDS>
 __global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
   extern __shared__ float wsh[];
@@ -419,18 +420,47 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
     }
     const int16_t* brow = a.bmap + static_cast<int64_t>(i) * a.T;
     const int16_t* brow1 = a.bmap1 ? a.bmap1 + static_cast<int64_t>(i) * a.T : nullptr;
-    for (int j = lane; j < a.T; j += 64) {
-      const float l = pr[j] * (dr[j] - dsum);
-      dr[j] = l;
-      const int bkt = brow[j];
-      if (bkt >= 0) {
-        if (wq) atomicAdd((LDS ? wq_s : wq) + bkt, l);
-        if (wv) atomicAdd((LDS ? wv_s : wv) + bkt, pr[j]);
-        const int bk1 = brow1 ? brow1[j] : -1;
-        if (bk1 >= 0) {
-          if (wq) atomicAdd((LDS ? wq_s : wq) + bk1, l);
-          if (wv) atomicAdd((LDS ? wv_s : wv) + bk1, pr[j]);
+    // Along a grid row of keys the column bucket never decreases, so neighbouring
+    // keys mostly share a table row.  LDS atomics cost about the same per active
+    // lane whatever the address, so before them lanes 2m and 2m+1, then 4m+k and
+    // 4m+k+2, fold their values into one lane when their rows match (DPP quad
+    // permutes, no LDS traffic); each value still enters exactly once.
+    auto add_folded = [&](int bkt, float vl, float vp) {
+      auto fold = [&](auto ctrl_c, int bit) {
+        constexpr int CTRL = decltype(ctrl_c)::value;
+        const int ob = __builtin_amdgcn_mov_dpp(bkt, CTRL, 0xF, 0xF, false);
+        const float ol = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vl), CTRL, 0xF, 0xF, false));
+        const float op = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vp), CTRL, 0xF, 0xF, false));
+        if (bkt >= 0 && ob == bkt) {
+          if (lane & bit) {
+            bkt = -1;   // taken by the partner
+          } else {
+            vl += ol;
+            vp += op;
+          }
         }
+      };
+      fold(std::integral_constant<int, 0xB1>{}, 1);   // quad_perm [1,0,3,2]: lanes 2m, 2m+1
+      fold(std::integral_constant<int, 0x4E>{}, 2);   // quad_perm [2,3,0,1]: lanes 4m+k, 4m+k+2
+      if (bkt >= 0) {
+        if (wq) atomicAdd((LDS ? wq_s : wq) + bkt, vl);
+        if (wv) atomicAdd((LDS ? wv_s : wv) + bkt, vp);
+      }
+    };
+    for (int j0 = 0; j0 < a.T; j0 += 64) {
+      const int j = j0 + lane;
+      float l = 0.0f, pj = 0.0f;
+      int bkt = -1, bk1 = -1;
+      if (j < a.T) {
+        pj = pr[j];
+        l = pj * (dr[j] - dsum);
+        dr[j] = l;
+        bkt = brow[j];
+        if (brow1) bk1 = brow1[j];
+      }
+      if (wq || wv) {
+        add_folded(bkt, l, pj);
+        if (brow1) add_folded(bk1, l, pj);
       }
     }
     if (LDS) {
