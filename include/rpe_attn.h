@@ -220,7 +220,10 @@ rpe_status rpe_attn_undirected_to_product(const rpe_attn_desc* desc, int32_t kin
  * 2S (Cross) or S (undirected maps: the index of a pair is looked up per offset
  * in a table the kernel builds from host-computed thresholds of dy^2 + dx^2;
  * RPE_E_UNSUPPORTED if the index takes more than 64 steps over the unit's
- * offsets).  q, k, v, o required (may be NULL when
+ * offsets).  Units (the grid, or a window) at most 256 columns wide
+ * (RPE_E_UNSUPPORTED beyond); RPE_E_BUCKETS when a unit's tables and guard rows
+ * do not fit one CU's LDS (e.g. the Swin map on units wider than about 60
+ * columns).  q, k, v, o required (may be NULL when
  * batch == 0, which launches nothing); bias required in bias mode;
  * rk / rq / rv required for the contextual terms requested (others ignored);
  * lse nullable.  o must not alias q, k or v.  Asynchronous on `stream`.

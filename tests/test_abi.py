@@ -114,7 +114,7 @@ BAD = [
     (dict(mode="contextual", terms="k", map="piecewise", alpha=2.0, beta=3.0, gamma=2.0), -7),
     (dict(mode="contextual", terms="k", map="piecewise", alpha=2.0, beta=3.0, gamma=8.0, rounding=5), -4),
     (dict(head_dim=48), -8), (dict(head_dim=128), -8), (dict(scale=float("nan")), -7),
-    (dict(grid=(4, 70)), -8),
+    (dict(grid=(4, 257)), -8),
 ]
 
 

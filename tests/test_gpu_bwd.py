@@ -99,6 +99,12 @@ CASES = [
                 map="euclidean_rounded")),
     ("quantized (squared) contextual K, 14x14 + cls, bf16", _D.resized(batch=1, heads=2,
                                                                       map="quantized_squared")),
+    # rows wider than 64 columns (the forward's log-sum-exp from its 128-slot rows)
+    ("contextual KQV, 3x100 + cls, bf16 d32", _D.resized(batch=1, heads=2, head_dim=32, grid_h=3, grid_w=100,
+                                                         terms=frozenset("kqv"))),
+    ("bias, 2x130, per head, fp32 d16", _D.resized(batch=1, heads=2, head_dim=16, grid_h=2, grid_w=130, prefix=0,
+                                                    mode="bias", terms=frozenset(), tables_per_head=True,
+                                                    dtype="fp32")),
 ]
 
 

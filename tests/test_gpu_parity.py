@@ -553,6 +553,43 @@ def test_undirected_large_units(dev, label, m, w):
     compare(w, make_inputs(w, sigma=1.0, seed=9950), dev, **sel)
 
 
+# Units more than 64 columns wide: grid rows padded to 128 or 256 key slots span
+# 4 or 8 key blocks, whose column parts are refilled per block (a 50x84
+# detection-style grid, C = 65 just past 64, C = 256 the widest).  (Swin-map
+# units that wide need more LDS than a CU has: their tables have (2C-1)^2 rows.)
+_WIDE_ROWS = [
+    ("contextual K, 6x84 + cls", _D.resized(batch=2, heads=2, grid_h=6, grid_w=84)),
+    ("contextual KQV, 5x100 + cls", _D.resized(batch=1, heads=2, grid_h=5, grid_w=100, terms=frozenset("kqv"))),
+    ("contextual KQV fp32 d32, 4x130", _D.resized(batch=1, heads=2, head_dim=32, grid_h=4, grid_w=130, prefix=0,
+                                                  terms=frozenset("kqv"), dtype="fp32")),
+    ("contextual QV d16, 7x65 + cls", _D.resized(batch=2, heads=2, head_dim=16, grid_h=7, grid_w=65,
+                                                 terms=frozenset("qv"))),
+    ("contextual KQ d32, 2x256 + cls", _D.resized(batch=1, heads=2, head_dim=32, grid_h=2, grid_w=256,
+                                                  terms=frozenset("kq"))),
+    ("iRPE bias, 3x200 + 2 prefix in the row padding, per-head tables",
+     _D.resized(batch=1, heads=3, grid_h=3, grid_w=200, prefix=2, mode="bias", terms=frozenset(),
+                tables_per_head=True)),
+    ("no position terms fp32, 4x150 + cls", _D.resized(batch=1, heads=2, grid_h=4, grid_w=150, mode="none",
+                                                       terms=frozenset(), map="swin", dtype="fp32")),
+    ("cross contextual KV, 5x96 + cls", _D.resized(batch=1, heads=2, grid_h=5, grid_w=96, terms=frozenset("kv"),
+                                                   method="cross")),
+    ("euclidean contextual KQV, 6x90", _D.resized(batch=1, heads=2, grid_h=6, grid_w=90, prefix=0,
+                                                  terms=frozenset("kqv"), map="euclidean")),
+    ("contextual V, 3x70 + cls", _D.resized(batch=2, heads=2, grid_h=3, grid_w=70, terms=frozenset("v"))),
+    ("contextual K, 50x84 detection grid", _D.resized(batch=1, heads=2, grid_h=50, grid_w=84, prefix=0)),
+]
+
+
+@pytest.mark.parametrize("label,w", _WIDE_ROWS)
+def test_wide_rows(dev, label, w):
+    w = fit(w) if w.mode != "none" else w
+    sel = {}
+    if w.grid_h * w.grid_w > 2000:
+        sel = dict(batch_sel=[w.batch - 1], heads_sel=[w.heads - 1])
+    say("wide rows", label, w.qkv_shape, "sampled" if sel else "")
+    compare(w, make_inputs(w, sigma=1.0, seed=9960), dev, **sel)
+
+
 def test_no_position_mode(dev):
     import torch
     import vision_transformer_attention_amd as pkg

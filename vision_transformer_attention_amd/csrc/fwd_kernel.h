@@ -34,16 +34,18 @@
 //       are summed per (query row, row bucket, key column) in LDS with plain
 //       read-modify-writes (each entry has one owner lane), turned into
 //       per-bucket sums by prefix sums over the key columns, and O^T += rV^T W^T
-//       at the end reuses the PV MFMA; grid rows of 4 or 64 padded columns
-//       instead sum per (row, bucket) with LDS float atomics (a row's entries
+//       at the end reuses the PV MFMA; grid rows of 4 or of 64 and more padded
+//       columns instead sum per (row, bucket) with LDS float atomics (a row's entries
 //       are only touched by the row's two lanes of one wave, so the order of the
 //       additions is fixed by the instruction stream);
 //   bias mode: the head's (2M-1)^2 table, prescaled by log2(e), is gathered.
 // The bucket of a pair is b = (g(dy)+H)*S + (g(dx)+H) with (dy, dx) = query -
 // key; its LDS address is ry(dy) + cx(lane, key column): ry is read from a
 // per-axis table once per key grid row and cx is fixed per lane (it already
-// holds the row base and g(dx)+H).  Pairs without a position term address a
-// zero guard region, padding keys a -inf guard region.
+// holds the row base and g(dx)+H), per block phase for grid rows of 64 padded
+// columns (two key blocks each) and refilled per block for wider rows.  Pairs
+// without a position term address a zero guard region, padding keys a -inf
+// guard region.
 //
 // Softmax runs in log2 units against a running row maximum m that the first
 // key block sets and that later blocks move only when their weights could
@@ -204,9 +206,15 @@ using bool_c = std::integral_constant<bool, B>;
 // the Product layout in the prologue), Cross contextual tables, undirected maps.
 constexpr int kMapProduct = 0, kMapCross = 1, kMapUndirected = 2;
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, int MK>
-__global__ void __launch_bounds__(kThreadsMax) __attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE, D, MULTI))))
+// WIDE: grid rows of Wp >= 64 slots, each spanning Wp / 32 key blocks.  The
+// fifth flag means several units per workgroup for rows of at most 32 slots and
+// rows of more than 64 slots (XW) for wide instances.
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI_XW, int MK>
+__global__ void __launch_bounds__(kThreadsMax)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE, D, MULTI_XW && !WIDE))))
 rpe_fwd_kernel(Params p) {
+  constexpr bool MULTI = MULTI_XW && !WIDE;
+  constexpr bool XW = MULTI_XW && WIDE;
   // CROSS: contextual tables under the Cross mapping (2S rows; instances of their
   // own, so that the Product instances carry none of its code).  Bias tables under
   // the Cross mapping are summed into the Product layout in the prologue (p.cross).
@@ -250,7 +258,9 @@ rpe_fwd_kernel(Params p) {
   constexpr int TILE = kBlockSlots * RB;           // bytes per 32-row tile
   constexpr int KS = BF ? (D + 15) / 16 : D / 2;   // MFMA k-steps over the head dim
   constexpr int DTL = (D + 31) / 32;               // 32-row tiles of O^T over the head dim
-  constexpr int NPH = WIDE ? 2 : 1;                // address phases (a 64-slot grid row spans 2 blocks)
+  // address phases whose column parts stay in registers (rows of 64 slots: 2;
+  // wider rows refill one set per block)
+  constexpr int NPH = WIDE && !XW ? 2 : 1;
   static_assert(RPI * CPR == 64 && IPB >= 1, "row size");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -444,16 +454,20 @@ rpe_fwd_kernel(Params p) {
   // with a per-lane part ioff0 and a uniform step idoff.  Padding columns load
   // the row's last token (any token would do: their weights are zero).
   uint32_t ioff0 = 0, idoff = 0;
-  // Wide rows (64 slots, two blocks per grid row): per-lane offsets of the
-  // even and odd blocks of a row (padding columns load the row's last token);
-  // block gb adds the uniform (gb >> 1) * rowstride * RBG.
-  uint32_t ioffe = 0, ioffo = 0;
-  if constexpr (WIDE) {
+  // Wide rows (Wp >= 64 slots, Wp / 32 blocks per grid row; lph = log2 of
+  // that): the per-lane offset of this wave's first instruction in a block of
+  // phase ph (padding columns load the row's last token), kept for both
+  // phases of 64-slot rows; block gb adds the uniform (gb >> lph) * rowstride * RBG.
+  const int lph = XW ? p.lwp - 5 : (WIDE ? 1 : 0);
+  auto wide_off = [&](int ph) -> uint32_t {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
-    ioffe = __umul24(static_cast<uint32_t>(row < p.C ? row : p.C - 1), RBG) + cb;
-    ioffo = __umul24(static_cast<uint32_t>(32 + row < p.C ? 32 + row : p.C - 1), RBG) + cb;
-  }
+    const int x = 32 * ph + row;
+    return __umul24(static_cast<uint32_t>(x < p.C ? x : p.C - 1), RBG) + cb;
+  };
+  const uint32_t ioffe = WIDE && !XW ? wide_off(0) : 0, ioffo = WIDE && !XW ? wide_off(1) : 0;
+  (void)ioffe;
+  (void)ioffo;
   if constexpr (!WIDE) {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
@@ -513,8 +527,8 @@ rpe_fwd_kernel(Params p) {
   auto interior_off = [&](int i, int gb) -> uint32_t {
     const int row = i * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
-    const int y = WIDE ? gb >> 1 : (gb * kBlockSlots + row) >> p.lwp;
-    const int x = WIDE ? ((gb & 1) << 5) + row : (gb * kBlockSlots + row) & (p.Wp - 1);
+    const int y = WIDE ? gb >> lph : (gb * kBlockSlots + row) >> p.lwp;
+    const int x = WIDE ? ((gb & ((1 << lph) - 1)) << 5) + row : (gb * kBlockSlots + row) & (p.Wp - 1);
     return __umul24(static_cast<uint32_t>(x < p.C ? wbase + y * rowstride + x : wbase), RBG) + cb;
   };
   auto issue_interior = [&](int gb, int stage) {
@@ -522,8 +536,8 @@ rpe_fwd_kernel(Params p) {
     const uint32_t vt = kt + TILE;
     if (wid < IPB) {
       if constexpr (WIDE) {
-        const uint32_t ub = (static_cast<uint32_t>(wbase) + static_cast<uint32_t>(gb >> 1) * rowstride) * RBG;
-        const uint32_t vo = (gb & 1) ? ioffo : ioffe;
+        const uint32_t ub = (static_cast<uint32_t>(wbase) + static_cast<uint32_t>(gb >> lph) * rowstride) * RBG;
+        const uint32_t vo = XW ? wide_off(gb & ((1 << lph) - 1)) : ((gb & 1) ? ioffo : ioffe);
         dma16s(kgb + ub, vo, kt + wid * 1024);
         dma16s(vgb + ub, vo, vt + wid * 1024);
       } else {
@@ -979,48 +993,51 @@ rpe_fwd_kernel(Params p) {
   (void)skv_on;
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
-  {
-    // Key column of entry (j, i) at phase ph: xj = (32 ph + 8j + 4h + i) & (Wp-1)
-    // = xu + hx with a wave-uniform part xu = ((32 ph + 8j) & (Wp-1)) + i and the
-    // lane part hx = 4h & (Wp-1) (no carries: Wp >= 4 and 8j has no low bits).
-    // All table reads are issued first, unconditionally (the empty asm keeps the
-    // compiler from moving each read under its own branch), then the selects.
-    const int hx = (4 * h) & (p.Wp - 1);
-    const int bx = xi + p.C - 1 - hx;        // xi - xj + C - 1 = bx - xu
+  // Key column of entry (j, i) at phase ph: xj = (32 ph + 8j + 4h + i) & (Wp-1)
+  // = xu + hx with a wave-uniform part xu = ((32 ph + 8j) & (Wp-1)) + i and the
+  // lane part hx = 4h & (Wp-1) (no carries: Wp >= 4 and 8j has no low bits).
+  // All table reads are issued first, unconditionally (the empty asm keeps the
+  // compiler from moving each read under its own branch), then the selects.
+  // fill_cols(ph0) writes the parts of phases ph0 .. ph0 + NPH - 1 into slots
+  // 0 .. NPH - 1.
+  const int hx = (4 * h) & (p.Wp - 1);
+  const int bx = xi + p.C - 1 - hx;        // xi - xj + C - 1 = bx - xu
+  auto fill_cols = [&](int ph0) __attribute__((always_inline)) {
     int cp[NPH][4][4];
 #pragma unroll
-    for (int ph = 0; ph < NPH; ++ph)
+    for (int sl = 0; sl < NPH; ++sl)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int xu = ((32 * ph + 8 * j) & (p.Wp - 1)) + i;
+          const int xu = ((32 * (ph0 + sl) + 8 * j) & (p.Wp - 1)) + i;
           const int xx = bx - xu;
-          cp[ph][j][i] = cx_tab[xx < 0 ? 0 : xx];
-          asm volatile("" : "+v"(cp[ph][j][i]));
+          cp[sl][j][i] = cx_tab[xx < 0 ? 0 : xx];
+          asm volatile("" : "+v"(cp[sl][j][i]));
         }
 #pragma unroll
-    for (int ph = 0; ph < NPH; ++ph)
+    for (int sl = 0; sl < NPH; ++sl)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 8 * j + 4 * h + i;
-          const int xu = ((32 * ph + 8 * j) & (p.Wp - 1)) + i;
-          const int cpart = cp[ph][j][i];
+          const int xu = ((32 * (ph0 + sl) + 8 * j) & (p.Wp - 1)) + i;
+          const int cpart = cp[sl][j][i];
           const bool col = hx < p.C - xu;   // xj < C
           if constexpr (UND) {
             // the column of the index table: dx + C-1, or the zero / -inf column
             const int ucol = !col ? 2 * p.C : (qpos ? cpart : 2 * p.C - 1);
-            cxb[ph][j][i] = lds0 + p.off_u2 + 2 * ucol;
-            if constexpr (TQ) cqb[ph][j][i] = lds0 + p.off_tq + s * p.p_tq * 4;
+            cxb[sl][j][i] = lds0 + p.off_u2 + 2 * ucol;
+            if constexpr (TQ) cqb[sl][j][i] = lds0 + p.off_tq + s * p.p_tq * 4;
           } else {
-            cxb[ph][j][i] = lds0 + (!col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero));
+            cxb[sl][j][i] = lds0 + (!col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero));
             if constexpr (TQ)
-              cqb[ph][j][i] = lds0 + (!col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz));
+              cqb[sl][j][i] = lds0 + (!col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz));
           }
         }
-  }
+  };
+  fill_cols(0);
   (void)cqb;
   // row part: ry(yq - y) at ry_tab[yq - y + R - 1]
   const int* __restrict__ ryt = ry_tab + (qpos ? yi : 0) + p.R - 1;
@@ -1155,7 +1172,7 @@ rpe_fwd_kernel(Params p) {
   // Row parts ry(yq - y) of this lane's keys 8j + 4h + i of interior block g.
   auto load_ry = [&](int g, int (&r)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = WIDE ? ryt[-(g >> 1)] : ryj[j][-(g * rpb)];
+    for (int j = 0; j < 4; ++j) r[j] = WIDE ? ryt[-(g >> lph)] : ryj[j][-(g * rpb)];
   };
   // (always inlined: an outlined call would move every captured variable to scratch)
   auto process_block = [&](auto interior_c, auto first_c, auto ph_c, const char* ktile, const char* vtile,
@@ -1392,14 +1409,21 @@ rpe_fwd_kernel(Params p) {
       if (!prefix_blk && skv_on) skv_block(gblk, pk, vz, !INTERIOR);
     }
   };
-  // phase dispatch (a 64-slot grid row spans two blocks)
+  // phase dispatch (a grid row of Wp >= 64 slots spans Wp / 32 blocks: the two
+  // phases of 64-slot rows have their column parts kept in registers, wider rows
+  // refill slot 0 for each block's phase)
   auto process = [&](auto interior_c, auto first_c, const char* kt, const char* vt, int gblk, bool pre,
                      const int (&ryv)[4]) __attribute__((always_inline)) {
-    if constexpr (WIDE) {
-      if (gblk & 1)
+    if constexpr (XW) {
+      // (the prefix block's slots take their guard regions instead)
+      if (!pre) fill_cols(gblk & ((p.Wp >> 5) - 1));
+      process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre, ryv);
+    } else if constexpr (WIDE) {
+      if (gblk & 1) {
         process_block(interior_c, first_c, std::integral_constant<int, 1>{}, kt, vt, gblk, pre, ryv);
-      else
+      } else {
         process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre, ryv);
+      }
     } else {
       process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre, ryv);
     }
@@ -1850,14 +1874,14 @@ rpe_fwd_kernel(Params p) {
 // ----------------------------------------------------------------------------------------
 // Launch dispatch.
 
-template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI, int MK>
+template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI_XW, int MK>
 hipError_t launch_fwd_w(const Params& p, hipStream_t stream) {
   // the instance contracts the value term per block exactly when the plan laid
   // out its buffers for that
   constexpr bool kSkv = std::is_same<DT, __bf16>::value && MODE == RPE_MODE_CONTEXTUAL && (TERMS & RPE_TERM_V) &&
                         !WIDE && MK == kMapProduct;
   if (kSkv != (p.skv != 0)) return hipErrorInvalidValue;
-  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, MULTI, MK>;
+  auto kern = rpe_fwd_kernel<DT, D, MODE, TERMS, WIDE, MULTI_XW, MK>;
   static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
   if (attr != hipSuccess) return attr;
@@ -1871,8 +1895,9 @@ hipError_t launch_fwd_t(const Params& p, hipStream_t stream) {
   // (several units per workgroup only arise for units of at most 4 query tiles,
   // so never with wide rows)
   if constexpr (MODE != RPE_MODE_CONTEXTUAL) {
-    if (p.upw > 1 && p.Wp != 64) return launch_fwd_w<DT, D, MODE, TERMS, false, true, MK>(p, stream);
+    if (p.upw > 1 && p.Wp < 64) return launch_fwd_w<DT, D, MODE, TERMS, false, true, MK>(p, stream);
   }
+  if (p.Wp > 64) return launch_fwd_w<DT, D, MODE, TERMS, true, true, MK>(p, stream);
   return p.Wp == 64 ? launch_fwd_w<DT, D, MODE, TERMS, true, false, MK>(p, stream)
                     : launch_fwd_w<DT, D, MODE, TERMS, false, false, MK>(p, stream);
 }

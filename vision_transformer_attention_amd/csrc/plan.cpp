@@ -55,9 +55,9 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   p->nrq = p->cross ? 2 * p->S : p->nbt * kRowTile;
   // bf16 tables of at most one 32-row tile per wave: each wave keeps its tile's
   // rows in registers instead (the Cross rows pair up per bucket and stay
-  // staged, and so do those of rows of 64 slots, whose instances have no
-  // registers to spare)
-  p->rq_regs = (tq && d->dtype == RPE_BF16 && !p->cross && p->Wp != 64 && p->nbt <= p->NW) ? 1 : 0;
+  // staged, and so do those of rows of 64 or more slots, whose instances
+  // have no registers to spare)
+  p->rq_regs = (tq && d->dtype == RPE_BF16 && !p->cross && p->Wp < 64 && p->nbt <= p->NW) ? 1 : 0;
   if (tq && !p->rq_regs) off += align(p->nrq * p->kpitch * eb, 16);
   // Cross key term: the table's 2S rows as swizzled [32][D] tiles (read per lane)
   p->off_rkc = off;
@@ -418,7 +418,7 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
       t.n_wg = t.n_units * t.n_qc;
       t.stages = stages;
       if (lds_layout(d, &t) != RPE_OK) continue;
-      const int by_regs = 4 * waves_per_simd(d->mode, d->terms, t.Wp == 64, d->head_dim) / t.NW;
+      const int by_regs = 4 * waves_per_simd(d->mode, d->terms, t.Wp >= 64, d->head_dim) / t.NW;
       const int by_lds = kMaxLdsBytes / ((t.lds_bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule);
       const int waves = (by_regs < by_lds ? by_regs : by_lds) * t.NW;
       if (vw && waves > best_vw_waves) {
@@ -440,8 +440,8 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   // (batch, head) (a divisor of the units per image), so that its set-up
   // (tables, guards, column offsets) is shared and the grid fits one round.
   best.upw = 1;
-  if (d->mode != RPE_MODE_CONTEXTUAL && best.n_qc == 1 && best.U > 1 && best.Wp != 64) {
-    const int by_regs = 4 * waves_per_simd(d->mode, d->terms, best.Wp == 64, d->head_dim, true) / best.NW;
+  if (d->mode != RPE_MODE_CONTEXTUAL && best.n_qc == 1 && best.U > 1 && best.Wp < 64) {
+    const int by_regs = 4 * waves_per_simd(d->mode, d->terms, best.Wp >= 64, d->head_dim, true) / best.NW;
     const int by_lds = kMaxLdsBytes / ((best.lds_bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule);
     const int64_t cap = static_cast<int64_t>(kNumCUs) * (by_regs < by_lds ? by_regs : by_lds);
     if (best.n_units > cap) {

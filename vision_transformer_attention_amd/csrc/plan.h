@@ -12,12 +12,13 @@ namespace rpe {
 // Keys of a unit are staged through LDS in blocks of 32 "slots" (one 32-key
 // MFMA tile).  Grid keys are laid out row by row with each grid row padded to
 // Wp slots, Wp = the power of two >= the unit width (at least 4), so a block
-// covers whole grid rows (Wp <= 32) or half a row (Wp = 64).  With this layout
-// the column part of a key's bucket id is fixed for a lane across blocks (only
-// the row part changes), which turns the bucket lookup into one add per pair.
+// covers whole grid rows (Wp <= 32) or 32 columns of one row (Wp >= 64).  With
+// this layout the column part of a key's bucket id is fixed for a lane across
+// blocks of the same phase (only the row part changes), which turns the bucket
+// lookup into one add per pair.
 constexpr int kBlockSlots = 32;
 constexpr int kRowTile = 32;        // query rows per wave (one 32x32 MFMA tile)
-constexpr int kMaxWp = 64;          // widest padded grid row the kernel is built for
+constexpr int kMaxWp = 256;         // widest padded grid row the kernel is built for
 constexpr int kMaxWaves = 4;
 constexpr int kMaxStages = 4;       // deepest LDS ring of the block stream
 constexpr int kMinStages = 2;
