@@ -206,6 +206,50 @@ using bool_c = std::integral_constant<bool, B>;
 // the Product layout in the prologue), Cross contextual tables, undirected maps.
 constexpr int kMapProduct = 0, kMapCross = 1, kMapUndirected = 2;
 
+// Column parts of one lane's gather addresses (the kernel's cxb / cqb) for the
+// key phases ph0 .. ph0 + NP - 1 into slots 0 .. NP - 1, as the kernel's
+// prologue computes them for phases 0 .. NP - 1 (the entry layout is described
+// there); bx = xi + C - 1 - hx, so that xi - xj + C - 1 = bx - xu.  Rows of more
+// than 64 slots call it once per key block.
+template <bool UND, bool TQ, int GSZ, int NP, int NQ>
+__device__ __forceinline__ void column_parts(int (&cxb)[NP][4][4], int (&cqb)[NQ][4][4], const int* cx_tab,
+                                             const Params& p, int ph0, int bx, int hx, int h, bool qpos, int lds0,
+                                             int rowbase) {
+  int cp[NP][4][4];
+#pragma unroll
+  for (int sl = 0; sl < NP; ++sl)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int xu = ((32 * (ph0 + sl) + 8 * j) & (p.Wp - 1)) + i;
+        const int xx = bx - xu;
+        cp[sl][j][i] = cx_tab[xx < 0 ? 0 : xx];
+        asm volatile("" : "+v"(cp[sl][j][i]));
+      }
+#pragma unroll
+  for (int sl = 0; sl < NP; ++sl)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 8 * j + 4 * h + i;
+        const int xu = ((32 * (ph0 + sl) + 8 * j) & (p.Wp - 1)) + i;
+        const int cpart = cp[sl][j][i];
+        const bool col = hx < p.C - xu;   // xj < C
+        if constexpr (UND) {
+          // the column of the index table: dx + C-1, or the zero / -inf column
+          const int ucol = !col ? 2 * p.C : (qpos ? cpart : 2 * p.C - 1);
+          cxb[sl][j][i] = lds0 + p.off_u2 + 2 * ucol;
+          if constexpr (TQ) cqb[sl][j][i] = lds0 + p.off_tq + s * p.p_tq * 4;
+        } else {
+          cxb[sl][j][i] = lds0 + (!col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero));
+          if constexpr (TQ)
+            cqb[sl][j][i] = lds0 + (!col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz));
+        }
+      }
+}
+
 // WIDE: grid rows of Wp >= 64 slots, each spanning Wp / 32 key blocks.  The
 // fifth flag means several units per workgroup for rows of at most 32 slots and
 // rows of more than 64 slots (XW) for wide instances.
@@ -465,9 +509,14 @@ rpe_fwd_kernel(Params p) {
     const int x = 32 * ph + row;
     return __umul24(static_cast<uint32_t>(x < p.C ? x : p.C - 1), RBG) + cb;
   };
-  const uint32_t ioffe = WIDE && !XW ? wide_off(0) : 0, ioffo = WIDE && !XW ? wide_off(1) : 0;
-  (void)ioffe;
-  (void)ioffo;
+  (void)wide_off;
+  uint32_t ioffe = 0, ioffo = 0;
+  if constexpr (WIDE && !XW) {
+    const int row = wid * RPI + lane / CPR;
+    const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
+    ioffe = __umul24(static_cast<uint32_t>(row < p.C ? row : p.C - 1), RBG) + cb;
+    ioffo = __umul24(static_cast<uint32_t>(32 + row < p.C ? 32 + row : p.C - 1), RBG) + cb;
+  }
   if constexpr (!WIDE) {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
@@ -993,51 +1042,52 @@ rpe_fwd_kernel(Params p) {
   (void)skv_on;
   int cxb[NPH][4][4];
   int cqb[TQ ? NPH : 1][4][4];
-  // Key column of entry (j, i) at phase ph: xj = (32 ph + 8j + 4h + i) & (Wp-1)
-  // = xu + hx with a wave-uniform part xu = ((32 ph + 8j) & (Wp-1)) + i and the
-  // lane part hx = 4h & (Wp-1) (no carries: Wp >= 4 and 8j has no low bits).
-  // All table reads are issued first, unconditionally (the empty asm keeps the
-  // compiler from moving each read under its own branch), then the selects.
-  // fill_cols(ph0) writes the parts of phases ph0 .. ph0 + NPH - 1 into slots
-  // 0 .. NPH - 1.
+  // Phases 0 .. NPH - 1 (rows of more than 64 slots refill slot 0 per block
+  // through column_parts(), which computes the same).  Key column of entry
+  // (j, i) at phase ph: xj = (32 ph + 8j + 4h + i) & (Wp-1) = xu + hx with a
+  // wave-uniform part xu = ((32 ph + 8j) & (Wp-1)) + i and the lane part
+  // hx = 4h & (Wp-1) (no carries: Wp >= 4 and 8j has no low bits).  All table
+  // reads are issued first, unconditionally (the empty asm keeps the compiler
+  // from moving each read under its own branch), then the selects.  (Written
+  // out here rather than as a call: the inline form schedules the prologue
+  // better, 1-2 us on DeiT-S.)
   const int hx = (4 * h) & (p.Wp - 1);
   const int bx = xi + p.C - 1 - hx;        // xi - xj + C - 1 = bx - xu
-  auto fill_cols = [&](int ph0) __attribute__((always_inline)) {
+  {
     int cp[NPH][4][4];
 #pragma unroll
-    for (int sl = 0; sl < NPH; ++sl)
+    for (int ph = 0; ph < NPH; ++ph)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int xu = ((32 * (ph0 + sl) + 8 * j) & (p.Wp - 1)) + i;
+          const int xu = ((32 * ph + 8 * j) & (p.Wp - 1)) + i;
           const int xx = bx - xu;
-          cp[sl][j][i] = cx_tab[xx < 0 ? 0 : xx];
-          asm volatile("" : "+v"(cp[sl][j][i]));
+          cp[ph][j][i] = cx_tab[xx < 0 ? 0 : xx];
+          asm volatile("" : "+v"(cp[ph][j][i]));
         }
 #pragma unroll
-    for (int sl = 0; sl < NPH; ++sl)
+    for (int ph = 0; ph < NPH; ++ph)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 8 * j + 4 * h + i;
-          const int xu = ((32 * (ph0 + sl) + 8 * j) & (p.Wp - 1)) + i;
-          const int cpart = cp[sl][j][i];
+          const int xu = ((32 * ph + 8 * j) & (p.Wp - 1)) + i;
+          const int cpart = cp[ph][j][i];
           const bool col = hx < p.C - xu;   // xj < C
           if constexpr (UND) {
             // the column of the index table: dx + C-1, or the zero / -inf column
             const int ucol = !col ? 2 * p.C : (qpos ? cpart : 2 * p.C - 1);
-            cxb[sl][j][i] = lds0 + p.off_u2 + 2 * ucol;
-            if constexpr (TQ) cqb[sl][j][i] = lds0 + p.off_tq + s * p.p_tq * 4;
+            cxb[ph][j][i] = lds0 + p.off_u2 + 2 * ucol;
+            if constexpr (TQ) cqb[ph][j][i] = lds0 + p.off_tq + s * p.p_tq * 4;
           } else {
-            cxb[sl][j][i] = lds0 + (!col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero));
+            cxb[ph][j][i] = lds0 + (!col ? p.off_neg : (qpos ? rowbase + cpart * GSZ : p.off_zero));
             if constexpr (TQ)
-              cqb[sl][j][i] = lds0 + (!col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz));
+              cqb[ph][j][i] = lds0 + (!col ? p.off_tqn : (qpos ? p.off_tq + (s * p.p_tq + cpart) * 4 : p.off_tqz));
           }
         }
-  };
-  fill_cols(0);
+  }
   (void)cqb;
   // row part: ry(yq - y) at ry_tab[yq - y + R - 1]
   const int* __restrict__ ryt = ry_tab + (qpos ? yi : 0) + p.R - 1;
@@ -1416,7 +1466,7 @@ rpe_fwd_kernel(Params p) {
                      const int (&ryv)[4]) __attribute__((always_inline)) {
     if constexpr (XW) {
       // (the prefix block's slots take their guard regions instead)
-      if (!pre) fill_cols(gblk & ((p.Wp >> 5) - 1));
+      if (!pre) column_parts<UND, TQ, GSZ>(cxb, cqb, cx_tab, p, gblk & ((p.Wp >> 5) - 1), bx, hx, h, qpos, lds0, rowbase);
       process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre, ryv);
     } else if constexpr (WIDE) {
       if (gblk & 1) {
