@@ -390,12 +390,72 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
   }
 }
 
-// Per query row: dL = P (dP - sum_j P dP) in place, and the row's per-table-row
-// sums Wq[b] = sum_j dL_ij and Wv[b] = sum_j P_ij over the pairs that read
-// row b; one wave per (unit, i), its
-// lanes over j.  LDS: the sums are formed in the wave's own 2 * nb floats
-// (zeroed, float atomics of values folded within lane quads, then written out
-// in full); global: float atomics into the zeroed rows (tables too large for LDS).
+// Adds this lane's (vl, vp) to wq[bkt], wv[bkt] (float atomics; bkt < 0: none).
+// Along a grid row of keys the column bucket never decreases, so neighbouring
+// keys mostly share a table row.  LDS atomics cost about the same per active
+// lane whatever the address, so before them lanes 2m and 2m+1, then 4m+k and
+// 4m+k+2, fold their values into one lane when their rows match (DPP quad
+// permutes, no LDS traffic); each value still enters exactly once.  All lanes
+// of the wave take part.
+__device__ __forceinline__ void fold_add(int lane, int bkt, float vl, float vp, float* wq, float* wv) {
+  auto fold = [&](auto ctrl_c, int bit) {
+    constexpr int CTRL = decltype(ctrl_c)::value;
+    const int ob = __builtin_amdgcn_mov_dpp(bkt, CTRL, 0xF, 0xF, false);
+    const float ol = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vl), CTRL, 0xF, 0xF, false));
+    const float op = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vp), CTRL, 0xF, 0xF, false));
+    if (bkt >= 0 && ob == bkt) {
+      if (lane & bit) {
+        bkt = -1;   // taken by the partner
+      } else {
+        vl += ol;
+        vp += op;
+      }
+    }
+  };
+  fold(std::integral_constant<int, 0xB1>{}, 1);   // quad_perm [1,0,3,2]: lanes 2m, 2m+1
+  fold(std::integral_constant<int, 0x4E>{}, 2);   // quad_perm [2,3,0,1]: lanes 4m+k, 4m+k+2
+  if (bkt >= 0) {
+    if (wq) atomicAdd(wq + bkt, vl);
+    if (wv) atomicAdd(wv + bkt, vp);
+  }
+}
+
+// One query row i of unit ub, one wave (lanes over j): dL = P (dP - sum_j P dP)
+// in place, and the row's per-table-row sums sum_j dL_ij into wq[b] and
+// sum_j P_ij into wv[b] over the pairs that read row b (float atomics, LDS or
+// global; a null pointer: not wanted).
+__device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t ub, int i, int lane, float* wq, float* wv) {
+  float* pr = a.P + (ub * a.T + i) * a.T;
+  float* dr = a.dL + (ub * a.T + i) * a.T;
+  float dsum = 0.0f;
+  for (int j = lane; j < a.T; j += 64) dsum += pr[j] * dr[j];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m);
+  const int16_t* brow = a.bmap + static_cast<int64_t>(i) * a.T;
+  const int16_t* brow1 = a.bmap1 ? a.bmap1 + static_cast<int64_t>(i) * a.T : nullptr;
+  auto add_folded = [&](int bkt, float vl, float vp) { fold_add(lane, bkt, vl, vp, wq, wv); };
+  for (int j0 = 0; j0 < a.T; j0 += 64) {
+    const int j = j0 + lane;
+    float l = 0.0f, pj = 0.0f;
+    int bkt = -1, bk1 = -1;
+    if (j < a.T) {
+      pj = pr[j];
+      l = pj * (dr[j] - dsum);
+      dr[j] = l;
+      bkt = brow[j];
+      if (brow1) bk1 = brow1[j];
+    }
+    if (wq || wv) {
+      add_folded(bkt, l, pj);
+      if (brow1) add_folded(bk1, l, pj);
+    }
+  }
+}
+
+// Per query row: bwd_row for every (unit, i), one wave each, with the row's sums
+// written to Wq[unit][i][b] and Wv[unit][i][b].  LDS: the sums are formed in the
+// wave's own 2 * nb floats (zeroed, then written out in full); global: float
+// atomics into the zeroed rows (tables too large for LDS).
 template <bool LDS>
 __global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
   extern __shared__ float wsh[];
@@ -407,68 +467,76 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); e < rows; e += waves) {
     const int64_t ub = div_idx(e, a.T);
     const int i = static_cast<int>(e - ub * a.T);
-    float* pr = a.P + (ub * a.T + i) * a.T;
-    float* dr = a.dL + (ub * a.T + i) * a.T;
-    float dsum = 0.0f;
-    for (int j = lane; j < a.T; j += 64) dsum += pr[j] * dr[j];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m);
     float* wq = a.Wq ? a.Wq + (ub * a.T + i) * a.nb : nullptr;
     float* wv = a.Wv ? a.Wv + (ub * a.T + i) * a.nb : nullptr;
     if (LDS) {
       for (int b = lane; b < 2 * a.nb; b += 64) wq_s[b] = 0.0f;
     }
-    const int16_t* brow = a.bmap + static_cast<int64_t>(i) * a.T;
-    const int16_t* brow1 = a.bmap1 ? a.bmap1 + static_cast<int64_t>(i) * a.T : nullptr;
-    // Along a grid row of keys the column bucket never decreases, so neighbouring
-    // keys mostly share a table row.  LDS atomics cost about the same per active
-    // lane whatever the address, so before them lanes 2m and 2m+1, then 4m+k and
-    // 4m+k+2, fold their values into one lane when their rows match (DPP quad
-    // permutes, no LDS traffic); each value still enters exactly once.
-    auto add_folded = [&](int bkt, float vl, float vp) {
-      auto fold = [&](auto ctrl_c, int bit) {
-        constexpr int CTRL = decltype(ctrl_c)::value;
-        const int ob = __builtin_amdgcn_mov_dpp(bkt, CTRL, 0xF, 0xF, false);
-        const float ol = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vl), CTRL, 0xF, 0xF, false));
-        const float op = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vp), CTRL, 0xF, 0xF, false));
-        if (bkt >= 0 && ob == bkt) {
-          if (lane & bit) {
-            bkt = -1;   // taken by the partner
-          } else {
-            vl += ol;
-            vp += op;
-          }
-        }
-      };
-      fold(std::integral_constant<int, 0xB1>{}, 1);   // quad_perm [1,0,3,2]: lanes 2m, 2m+1
-      fold(std::integral_constant<int, 0x4E>{}, 2);   // quad_perm [2,3,0,1]: lanes 4m+k, 4m+k+2
-      if (bkt >= 0) {
-        if (wq) atomicAdd((LDS ? wq_s : wq) + bkt, vl);
-        if (wv) atomicAdd((LDS ? wv_s : wv) + bkt, vp);
-      }
-    };
-    for (int j0 = 0; j0 < a.T; j0 += 64) {
-      const int j = j0 + lane;
-      float l = 0.0f, pj = 0.0f;
-      int bkt = -1, bk1 = -1;
-      if (j < a.T) {
-        pj = pr[j];
-        l = pj * (dr[j] - dsum);
-        dr[j] = l;
-        bkt = brow[j];
-        if (brow1) bk1 = brow1[j];
-      }
-      if (wq || wv) {
-        add_folded(bkt, l, pj);
-        if (brow1) add_folded(bk1, l, pj);
-      }
-    }
+    bwd_row(a, ub, i, lane, wq ? (LDS ? wq_s : wq) : nullptr, wv ? (LDS ? wv_s : wv) : nullptr);
     if (LDS) {
       for (int b = lane; b < a.nb; b += 64) {
         if (wq) wq[b] = wq_s[b];
         if (wv) wv[b] = wv_s[b];
       }
     }
+  }
+}
+
+// Bias mode: the table gradient needs only each unit's sums over all its rows,
+// dbias[b] = sum_i sum_j dL_ij over the pairs that read row b.  One workgroup of
+// 4 waves per unit: wave w takes the rows i = w, w + 4, ... into its own nb LDS
+// floats, and the four are added in a fixed order into Wq[b][unit] (the unit's
+// partial, stored [nb][n_units] so that the reduction over units reads whole
+// lines).  No per-row sums reach global memory.
+__global__ void __launch_bounds__(256) bwd_rows_unit_kernel(BwdArgs a) {
+  extern __shared__ float wsh[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float* const ws = wsh + w * a.nb;
+  for (int64_t ub = blockIdx.x; ub < a.n_units; ub += gridDim.x) {
+    for (int b = lane; b < a.nb; b += 64) ws[b] = 0.0f;
+    if (a.T <= 64) {
+      // rows of at most 64 keys: one element per lane; the wave loads four of
+      // its rows at once, then sums them in order
+      const bool on = lane < a.T;
+      const int64_t base = ub * a.T * a.T;
+      for (int i0 = w; i0 < a.T; i0 += 16) {
+        float pj[4], dj[4];
+        int bk[4], bk1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + 4 * r;
+          pj[r] = 0.0f;
+          dj[r] = 0.0f;
+          bk[r] = -1;
+          bk1[r] = -1;
+          if (on && i < a.T) {
+            const int64_t o = static_cast<int64_t>(i) * a.T + lane;
+            pj[r] = a.P[base + o];
+            dj[r] = a.dL[base + o];
+            bk[r] = a.bmap[o];
+            if (a.bmap1) bk1[r] = a.bmap1[o];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + 4 * r;
+          if (i >= a.T) break;
+          float dsum = pj[r] * dj[r];
+#pragma unroll
+          for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m);
+          const float l = pj[r] * (dj[r] - dsum);
+          if (on) a.dL[base + static_cast<int64_t>(i) * a.T + lane] = l;
+          fold_add(lane, bk[r], l, 0.0f, ws, nullptr);
+          if (a.bmap1) fold_add(lane, bk1[r], l, 0.0f, ws, nullptr);
+        }
+      }
+    } else {
+      for (int i = w; i < a.T; i += 4) bwd_row(a, ub, i, lane, ws, nullptr);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < a.nb; b += 256)
+      a.Wq[b * a.n_units + ub] = (wsh[b] + wsh[a.nb + b]) + (wsh[2 * a.nb + b] + wsh[3 * a.nb + b]);
+    __syncthreads();
   }
 }
 
@@ -960,7 +1028,8 @@ __global__ void bwd_tables_kernel(BwdArgs a, float* part) {
 
 // Stage 2: one wave per table-gradient element (kind, table, b, d); its lanes
 // take the table's units in turn, then a fixed shuffle tree adds the lanes.
-__global__ void __launch_bounds__(256) bwd_tables_reduce_kernel(BwdArgs a, const float* part) {
+// bias_t: the bias partials are stored [nb][n_units] (from the bias-mode row pass).
+__global__ void __launch_bounds__(256) bwd_tables_reduce_kernel(BwdArgs a, const float* part, int bias_t) {
   const int lane = threadIdx.x & 63;
   const int G = a.tables_per_head ? a.H : 1;
   const int64_t NU = a.n_units / G;
@@ -970,26 +1039,53 @@ __global__ void __launch_bounds__(256) bwd_tables_reduce_kernel(BwdArgs a, const
   const float* const pv = pq + (a.drq ? region : 0);
   const float* const pb = pv + (a.drv ? region : 0);
   const int64_t ne = static_cast<int64_t>(G) * a.nb * a.D;   // elements per kind
-  const int64_t total = 3 * ne + static_cast<int64_t>(G) * a.nb;
+  // elements of the kinds present, in the order drK, drQ, drV, dbias
+  const int64_t nk = a.drk ? ne : 0, nq = a.drq ? ne : 0, nv = a.drv ? ne : 0;
+  const int64_t total = nk + nq + nv + (a.dbias ? static_cast<int64_t>(G) * a.nb : 0);
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6); e < total; e += waves) {
-    const int kind = e < 3 * ne ? static_cast<int>(div_idx(e, ne)) : 3;
-    const int64_t r = kind < 3 ? e - kind * ne : e - 3 * ne;
+    int kind = 0;
+    int64_t r = e;
+    if (r >= nk) {
+      r -= nk;
+      kind = 1;
+      if (r >= nq) {
+        r -= nq;
+        kind = 2;
+        if (r >= nv) {
+          r -= nv;
+          kind = 3;
+        }
+      }
+    }
     const float* src = kind == 0 ? pk : kind == 1 ? pq : kind == 2 ? pv : pb;
     float* dst = kind == 0 ? a.drk : kind == 1 ? a.drq : kind == 2 ? a.drv : a.dbias;
-    if (!dst) continue;
     const int De = kind < 3 ? a.D : 1;
     const int64_t gbd = r;                      // (table g, b, d) or (table g, b)
     const int64_t g = div_idx(gbd, static_cast<int64_t>(a.nb) * De);
     const int64_t bd = gbd - g * a.nb * De;     // b * De + d
-    float acc = 0.0f;
-    for (int64_t kk = lane; kk < NU; kk += 64) {
+    // Lane l adds the partials of the table's units l, l + 64, ... in that order;
+    // the loads go out eight at a time (the order of the additions is kept).
+    const bool tr = kind == 3 && bias_t;
+    auto addr = [&](int64_t kk) -> int64_t {
       int64_t ub = kk;
       if (a.tables_per_head) {
         const int64_t bb = div_idx(kk, a.U), uu = kk - bb * a.U;
         ub = (bb * a.H + g) * a.U + uu;
       }
-      acc += src[ub * a.nb * De + bd];
+      return tr ? bd * a.n_units + ub : ub * a.nb * De + bd;
+    };
+    float acc = 0.0f;
+    for (int64_t k0 = lane; k0 < NU; k0 += 8 * 64) {
+      float v[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int64_t kk = k0 + 64 * m;
+        v[m] = kk < NU ? src[addr(kk)] : 0.0f;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        if (k0 + 64 * m < NU) acc += v[m];
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
@@ -1080,8 +1176,14 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_scores_kernel<__bf16>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(bwd_scores_kernel<float>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
-  // (LDS sums: 4 waves x 2 x nb floats per block, up to 64 KB)
-  if (a.nb <= 2048) {
+  // bias mode: per-unit sums only (LDS: 4 waves x nb floats, up to 32 KB)
+  const bool unit_sums = a.dbias && a.Wq && !a.Wk && !a.Wv && !a.drk && !a.drq && !a.drv && a.nb <= 2048;
+  if (unit_sums) {
+    const unsigned ugrid = static_cast<unsigned>(a.n_units < 65536 ? a.n_units : 65536);
+    hipLaunchKernelGGL(bwd_rows_unit_kernel, dim3(ugrid), dim3(256), static_cast<size_t>(4 * a.nb) * sizeof(float),
+                       stream, a);
+  } else if (a.nb <= 2048) {
+    // (LDS sums: 4 waves x 2 x nb floats per block, up to 64 KB)
     hipLaunchKernelGGL(bwd_rows_kernel<true>, dim3(blocks_for(rows * 64)), dim3(256),
                        static_cast<size_t>(4 * 2 * a.nb) * sizeof(float), stream, a);
   } else {
@@ -1111,7 +1213,12 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_grads_kernel<__bf16>, dim3(blocks_for(elems), 2), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(bwd_grads_kernel<float>, dim3(blocks_for(elems), 2), dim3(256), 0, stream, a);
-  if (a.drk || a.drq || a.drv || a.dbias) {
+  if (unit_sums) {
+    // the per-unit partials are in Wq already ([nb][n_units]), where the
+    // reduction reads the bias kind's partials when no other kind is present
+    const int64_t nt = static_cast<int64_t>(tables) * a.nb;
+    hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nt * 64)), dim3(256), 0, stream, a, a.Wq, 1);
+  } else if (a.drk || a.drq || a.drv || a.dbias) {
     const int64_t nt = static_cast<int64_t>(tables) * a.nb;
     const int64_t n = a.n_units * ((a.nb + kBB - 1) / kBB) * ((a.drk || a.drq || a.drv) ? a.D : 1);
     // per-unit partial sums in the P buffer (free once dq, dk, dv are formed) when they fit
@@ -1128,8 +1235,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_tables_kernel<__bf16, true>), dim3(blocks_for(n)), dim3(256), 0, stream, a, a.P);
       else
         hipLaunchKernelGGL((bwd_tables_kernel<float, true>), dim3(blocks_for(n)), dim3(256), 0, stream, a, a.P);
-      const int64_t nw = 3 * nt * a.D + nt;
-      hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nw * 64)), dim3(256), 0, stream, a, a.P);
+      const int64_t nw = kinds * nt * a.D + (a.dbias ? nt : 0);
+      hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nw * 64)), dim3(256), 0, stream, a, a.P, 0);
     } else {
       for (float* g : {a.drk, a.drq, a.drv})
         if (g) hipLaunchKernelGGL(bwd_zero_kernel, dim3(blocks_for(nt * a.D)), dim3(256), 0, stream, g, nt * a.D);
