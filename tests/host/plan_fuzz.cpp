@@ -245,7 +245,14 @@ int main(int argc, char** argv) {
       REQUIRE(p.nbt * rpe::kRowTile * p.D * p.elem_bytes <= p.NW * rpe::kRowTile * p.p_tab * p.gsz);
       REQUIRE(p.off_tab % 16 == 0);
     }
-    REQUIRE(p.Wp >= p.C && p.Wp <= rpe::kMaxWp && (1 << p.lwp) == p.Wp && p.Wp >= 4);
+    REQUIRE(p.Wp >= p.C && p.Wp <= rpe::kMaxWp && p.Wp >= 4);
+    if (p.C > 64) {
+      // rows of more than 64 columns: a multiple of 32 slots, less than one block of padding
+      REQUIRE(p.Wp % rpe::kBlockSlots == 0 && p.Wp - p.C < rpe::kBlockSlots && p.nph * rpe::kBlockSlots == p.Wp);
+      REQUIRE(p.dv_nph.d == static_cast<uint32_t>(p.nph));
+    } else {
+      REQUIRE((1 << p.lwp) == p.Wp && p.nph == 1);
+    }
     REQUIRE(p.grid_blocks * rpe::kBlockSlots >= p.R * p.Wp);
     REQUIRE(p.n_rt * rpe::kRowTile >= p.T && p.n_qc * p.NW >= p.n_rt);
     REQUIRE(p.NW >= 2 && p.NW <= rpe::kMaxWaves);

@@ -553,9 +553,10 @@ def test_undirected_large_units(dev, label, m, w):
     compare(w, make_inputs(w, sigma=1.0, seed=9950), dev, **sel)
 
 
-# Units more than 64 columns wide: grid rows padded to 128 or 256 key slots span
-# 4 or 8 key blocks, whose column parts are refilled per block (a 50x84
-# detection-style grid, C = 65 just past 64, C = 256 the widest).  (Swin-map
+# Units more than 64 columns wide: grid rows padded to a multiple of 32 key
+# slots (96 to 256 here) span 3 to 8 key blocks, whose column parts are refilled
+# per block (a 50x84 detection-style grid, C = 65 just past 64, C = 96 with no
+# padding left for the class token, C = 256 the widest).  (Swin-map
 # units that wide need more LDS than a CU has: their tables have (2C-1)^2 rows.)
 _WIDE_ROWS = [
     ("contextual K, 6x84 + cls", _D.resized(batch=2, heads=2, grid_h=6, grid_w=84)),
@@ -739,6 +740,7 @@ FULL_SAMPLES = {
     "deit_s_irpe_k_cross": ([0, 63], [2]),
     "detr_irpe_k": ([0, 7], [0, 7]),
     "deit_s_irpe_bias_euclid": ([0, 63], [0, 5]),
+    "detr_wide_irpe_k": ([1], [7]),
 }
 
 

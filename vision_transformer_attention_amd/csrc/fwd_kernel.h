@@ -209,8 +209,9 @@ constexpr int kMapProduct = 0, kMapCross = 1, kMapUndirected = 2;
 // Column parts of one lane's gather addresses (the kernel's cxb / cqb) for the
 // key phases ph0 .. ph0 + NP - 1 into slots 0 .. NP - 1, as the kernel's
 // prologue computes them for phases 0 .. NP - 1 (the entry layout is described
-// there); bx = xi + C - 1 - hx, so that xi - xj + C - 1 = bx - xu.  Rows of more
-// than 64 slots call it once per key block.
+// there), for rows of more than 64 slots (Wp = 32 nph, ph0 + NP <= nph, so that
+// the key column 32 ph + 8j + 4h + i needs no wrap); bx = xi + C - 1 - hx, so
+// that xi - xj + C - 1 = bx - xu.  Those rows call it once per key block.
 template <bool UND, bool TQ, int GSZ, int NP, int NQ>
 __device__ __forceinline__ void column_parts(int (&cxb)[NP][4][4], int (&cqb)[NQ][4][4], const int* cx_tab,
                                              const Params& p, int ph0, int bx, int hx, int h, bool qpos, int lds0,
@@ -222,7 +223,7 @@ __device__ __forceinline__ void column_parts(int (&cxb)[NP][4][4], int (&cqb)[NQ
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int xu = ((32 * (ph0 + sl) + 8 * j) & (p.Wp - 1)) + i;
+        const int xu = 32 * (ph0 + sl) + 8 * j + i;
         const int xx = bx - xu;
         cp[sl][j][i] = cx_tab[xx < 0 ? 0 : xx];
         asm volatile("" : "+v"(cp[sl][j][i]));
@@ -234,7 +235,7 @@ __device__ __forceinline__ void column_parts(int (&cxb)[NP][4][4], int (&cqb)[NQ
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 8 * j + 4 * h + i;
-        const int xu = ((32 * (ph0 + sl) + 8 * j) & (p.Wp - 1)) + i;
+        const int xu = 32 * (ph0 + sl) + 8 * j + i;
         const int cpart = cp[sl][j][i];
         const bool col = hx < p.C - xu;   // xj < C
         if constexpr (UND) {
@@ -252,10 +253,14 @@ __device__ __forceinline__ void column_parts(int (&cxb)[NP][4][4], int (&cqb)[NQ
 
 // WIDE: grid rows of Wp >= 64 slots, each spanning Wp / 32 key blocks.  The
 // fifth flag means several units per workgroup for rows of at most 32 slots and
-// rows of more than 64 slots (XW) for wide instances.
+// rows of more than 64 slots (XW) for wide instances.  (The register budget of
+// bf16 XW instances is that of rows of at most 32 slots: they keep one set of
+// column parts, not two.)
 template <typename DT, int D, int MODE, unsigned TERMS, bool WIDE, bool MULTI_XW, int MK>
 __global__ void __launch_bounds__(kThreadsMax)
-__attribute__((amdgpu_waves_per_eu(waves_per_simd(MODE, TERMS, WIDE, D, MULTI_XW && !WIDE))))
+__attribute__((amdgpu_waves_per_eu(
+    waves_per_simd(MODE, TERMS, wide_budget(WIDE, WIDE && MULTI_XW, std::is_same<DT, __bf16>::value), D,
+                   MULTI_XW && !WIDE))))
 rpe_fwd_kernel(Params p) {
   constexpr bool MULTI = MULTI_XW && !WIDE;
   constexpr bool XW = MULTI_XW && WIDE;
@@ -486,8 +491,15 @@ rpe_fwd_kernel(Params p) {
       if (blk == 0) return s < p.P ? s : wb;
       blk -= 1;
     }
-    const int sigma = blk * kBlockSlots + s;
-    const int y = sigma >> p.lwp, x = sigma & (p.Wp - 1);
+    int y, x;
+    if constexpr (XW) {
+      y = static_cast<int>(fdiv(static_cast<uint32_t>(blk), p.dv_nph));
+      x = ((blk - y * p.nph) << 5) + s;
+    } else {
+      const int sigma = blk * kBlockSlots + s;
+      y = sigma >> p.lwp;
+      x = sigma & (p.Wp - 1);
+    }
     int n = (y < p.R && x < p.C) ? wb + y * rowstride + x : wb;
     if (p.prefix_in_tail) n = (y == p.R - 1 && x >= p.C && x - p.C < p.P) ? x - p.C : n;
     return n;
@@ -498,11 +510,15 @@ rpe_fwd_kernel(Params p) {
   // with a per-lane part ioff0 and a uniform step idoff.  Padding columns load
   // the row's last token (any token would do: their weights are zero).
   uint32_t ioff0 = 0, idoff = 0;
-  // Wide rows (Wp >= 64 slots, Wp / 32 blocks per grid row; lph = log2 of
-  // that): the per-lane offset of this wave's first instruction in a block of
-  // phase ph (padding columns load the row's last token), kept for both
-  // phases of 64-slot rows; block gb adds the uniform (gb >> lph) * rowstride * RBG.
-  const int lph = XW ? p.lwp - 5 : (WIDE ? 1 : 0);
+  // Wide rows (Wp >= 64 slots, Wp / 32 blocks per grid row): the per-lane
+  // offset of this wave's first instruction in a block of phase ph (padding
+  // columns load the row's last token), kept for both phases of 64-slot rows;
+  // block gb of grid row y adds the uniform y * rowstride * RBG.  wide_row(gb)
+  // is that row: gb >> 1 for 64-slot rows, gb / nph beyond.
+  auto wide_row = [&](int gb) -> int {
+    return XW ? static_cast<int>(fdiv(static_cast<uint32_t>(gb), p.dv_nph)) : gb >> 1;
+  };
+  (void)wide_row;
   auto wide_off = [&](int ph) -> uint32_t {
     const int row = wid * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
@@ -576,8 +592,10 @@ rpe_fwd_kernel(Params p) {
   auto interior_off = [&](int i, int gb) -> uint32_t {
     const int row = i * RPI + lane / CPR;
     const int cb = ((lane % CPR) ^ (row & (CPR - 1))) * 16;
-    const int y = WIDE ? gb >> lph : (gb * kBlockSlots + row) >> p.lwp;
-    const int x = WIDE ? ((gb & ((1 << lph) - 1)) << 5) + row : (gb * kBlockSlots + row) & (p.Wp - 1);
+    const int y = WIDE ? wide_row(gb) : (gb * kBlockSlots + row) >> p.lwp;
+    const int x = XW     ? ((gb - y * p.nph) << 5) + row
+                  : WIDE ? ((gb & 1) << 5) + row
+                         : (gb * kBlockSlots + row) & (p.Wp - 1);
     return __umul24(static_cast<uint32_t>(x < p.C ? wbase + y * rowstride + x : wbase), RBG) + cb;
   };
   auto issue_interior = [&](int gb, int stage) {
@@ -585,8 +603,9 @@ rpe_fwd_kernel(Params p) {
     const uint32_t vt = kt + TILE;
     if (wid < IPB) {
       if constexpr (WIDE) {
-        const uint32_t ub = (static_cast<uint32_t>(wbase) + static_cast<uint32_t>(gb >> lph) * rowstride) * RBG;
-        const uint32_t vo = XW ? wide_off(gb & ((1 << lph) - 1)) : ((gb & 1) ? ioffo : ioffe);
+        const int y = wide_row(gb);
+        const uint32_t ub = (static_cast<uint32_t>(wbase) + static_cast<uint32_t>(y) * rowstride) * RBG;
+        const uint32_t vo = XW ? wide_off(gb - y * p.nph) : ((gb & 1) ? ioffo : ioffe);
         dma16s(kgb + ub, vo, kt + wid * 1024);
         dma16s(vgb + ub, vo, vt + wid * 1024);
       } else {
@@ -1222,7 +1241,7 @@ rpe_fwd_kernel(Params p) {
   // Row parts ry(yq - y) of this lane's keys 8j + 4h + i of interior block g.
   auto load_ry = [&](int g, int (&r)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = WIDE ? ryt[-(g >> lph)] : ryj[j][-(g * rpb)];
+    for (int j = 0; j < 4; ++j) r[j] = WIDE ? ryt[-wide_row(g)] : ryj[j][-(g * rpb)];
   };
   // (always inlined: an outlined call would move every captured variable to scratch)
   auto process_block = [&](auto interior_c, auto first_c, auto ph_c, const char* ktile, const char* vtile,
@@ -1266,7 +1285,11 @@ rpe_fwd_kernel(Params p) {
       // the padding columns of the last row, get their guard regions
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int yj = (gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
+        int yj;
+        if constexpr (XW)
+          yj = gblk < 0 ? -1 : wide_row(gblk);
+        else
+          yj = (gblk * kBlockSlots + 8 * j + 4 * h) >> p.lwp;
         const int yk = yj < 0 ? 0 : (yj < p.R ? yj : p.R - 1);
         const int ryb = ryt[-yk];
         rp[j] = ryb;
@@ -1274,7 +1297,7 @@ rpe_fwd_kernel(Params p) {
         for (int i = 0; i < 4; ++i) {
           const int slot = 8 * j + 4 * h + i;
           vz[j][i] = false;
-          const int xj = (gblk * kBlockSlots + slot) & (p.Wp - 1);
+          const int xj = XW ? ((gblk - yj * p.nph) << 5) + slot : (gblk * kBlockSlots + slot) & (p.Wp - 1);
           int a, aq;
           if constexpr (UND) {
             int u = lds_at<uint16_t>(ryb + cxb[PH][j][i]);
@@ -1466,7 +1489,9 @@ rpe_fwd_kernel(Params p) {
                      const int (&ryv)[4]) __attribute__((always_inline)) {
     if constexpr (XW) {
       // (the prefix block's slots take their guard regions instead)
-      if (!pre) column_parts<UND, TQ, GSZ>(cxb, cqb, cx_tab, p, gblk & ((p.Wp >> 5) - 1), bx, hx, h, qpos, lds0, rowbase);
+      if (!pre)
+        column_parts<UND, TQ, GSZ>(cxb, cqb, cx_tab, p, gblk - wide_row(gblk) * p.nph, bx, hx, h, qpos, lds0,
+                                   rowbase);
       process_block(interior_c, first_c, std::integral_constant<int, 0>{}, kt, vt, gblk, pre, ryv);
     } else if constexpr (WIDE) {
       if (gblk & 1) {

@@ -376,9 +376,13 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
   }
 
   // key slots
-  p->Wp = padded_width(p->C);
+  // rows of more than 64 columns: a multiple of 32 slots (one key block per 32
+  // columns), so that at most 31 slots of a row are padding
+  p->Wp = p->C > 64 ? (p->C + kBlockSlots - 1) / kBlockSlots * kBlockSlots : padded_width(p->C);
   if (p->Wp > kMaxWp) return RPE_E_UNSUPPORTED;
   p->lwp = log2_exact(p->Wp);
+  p->nph = p->Wp > 64 ? p->Wp / kBlockSlots : 1;
+  p->dv_nph = make_fastdiv(static_cast<uint32_t>(p->nph));
   p->prefix_in_tail = (p->P > 0 && p->P <= p->Wp - p->C) ? 1 : 0;
   p->prefix_block = (p->P > 0 && !p->prefix_in_tail) ? 1 : 0;
   p->grid_blocks = (p->R * p->Wp + kBlockSlots - 1) / kBlockSlots;
@@ -387,7 +391,7 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
 
   p->n_rt = (p->T + kRowTile - 1) / kRowTile;
   p->n_units = (int64_t)p->B * p->H * p->U;
-  p->first_tail = ((p->R - 1) << p->lwp) / kBlockSlots;
+  p->first_tail = (p->R - 1) * p->Wp / kBlockSlots;
   // Work split: one 32-row query tile per wave, the unit's tiles spread evenly
   // over its workgroups.  Among workgroup widths (2..kMaxWaves waves) and ring
   // depths whose LDS plan fits, take the one with the most resident waves per
@@ -418,7 +422,9 @@ int make_plan(const rpe_attn_desc* d, Params* p) {
       t.n_wg = t.n_units * t.n_qc;
       t.stages = stages;
       if (lds_layout(d, &t) != RPE_OK) continue;
-      const int by_regs = 4 * waves_per_simd(d->mode, d->terms, t.Wp >= 64, d->head_dim) / t.NW;
+      const int by_regs =
+          4 * waves_per_simd(d->mode, d->terms, wide_budget(t.Wp >= 64, t.Wp > 64, d->dtype == RPE_BF16),
+                             d->head_dim) / t.NW;
       const int by_lds = kMaxLdsBytes / ((t.lds_bytes + kLdsGranule - 1) / kLdsGranule * kLdsGranule);
       const int waves = (by_regs < by_lds ? by_regs : by_lds) * t.NW;
       if (vw && waves > best_vw_waves) {

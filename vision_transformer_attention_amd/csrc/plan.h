@@ -11,8 +11,9 @@ namespace rpe {
 
 // Keys of a unit are staged through LDS in blocks of 32 "slots" (one 32-key
 // MFMA tile).  Grid keys are laid out row by row with each grid row padded to
-// Wp slots, Wp = the power of two >= the unit width (at least 4), so a block
-// covers whole grid rows (Wp <= 32) or 32 columns of one row (Wp >= 64).  With
+// Wp slots, Wp = the power of two >= the unit width (at least 4) up to 64, and
+// the multiple of 32 >= the width beyond, so a block covers whole grid rows
+// (Wp <= 32) or 32 columns of one row (Wp >= 64).  With
 // this layout the column part of a key's bucket id is fixed for a lane across
 // blocks of the same phase (only the row part changes), which turns the bucket
 // lookup into one add per pair.
@@ -32,6 +33,11 @@ constexpr int kLdsGranule = 512;
 // host and passes up to kMaxThresholds thresholds; beyond that the kernel
 // evaluates g itself.
 constexpr int kMaxThresholds = 64;
+// Whether an instance gets the register budget of wide rows: rows of 64 slots,
+// and fp32 rows of more than 64 (bf16 rows of more than 64 slots keep one set
+// of column parts and fit the narrow budget).
+constexpr bool wide_budget(bool wide, bool xw, bool bf16) { return wide && !(xw && bf16); }
+
 // Resident waves per SIMD each forward instance is compiled for (register
 // budget 512 / waves): four for head dims up to 32 and three for 64 with only
 // the key term or a bias; wide rows (two column phases of gather offsets) and
@@ -86,7 +92,7 @@ struct Params {
   int64_t sb, sh, sn, osb, osh, osn;
   uint32_t rbi;
   // key-slot geometry
-  int Wp, lwp;            // padded row width and its log2
+  int Wp, lwp;            // padded row width and log2 of the power of two >= Wp
   int prefix_in_tail;     // prefix keys live in the pad columns of the last grid row
   int prefix_block;       // 1: a separate leading block holds the prefix keys
   int grid_blocks;        // blocks of 32 slots covering R * Wp grid slots
@@ -160,6 +166,9 @@ struct Params {
   // a pitch of rvp bytes (row bytes + 16); ry_tab entries times skv_rymul give
   // a row bucket's byte offset there.
   int skv, nkr, mw, pb_rs, pb_bytes, off_pb, off_pz, rvp, off_rvr, skv_rymul;
+  // rows of more than 64 slots: key blocks per grid row (Wp = 32 nph; else 1)
+  int nph;
+  FastDiv dv_nph;
 };
 
 // Validation only (no derived plan).  Returns an rpe_status.

@@ -107,6 +107,12 @@ WORKLOADS = {
         gamma=15.2, dtype=BF16, table_rows=81, tables_per_head=False,
         description="DETR-like encoder iRPE on keys, non-square 25x38 grid (950 tokens, an 800x1216 "
                     "image at stride 32): B8, h8 d32 bf16, r^K 81x32 shared"),
+    "detr_wide_irpe_k": Workload(
+        10, "detr_wide_irpe_k", batch=2, heads=8, head_dim=32, grid_h=50, grid_w=84, window=0,
+        prefix=0, mode="contextual", terms=frozenset("k"), map="piecewise", alpha=1.9, beta=3.8,
+        gamma=15.2, dtype=BF16, table_rows=81, tables_per_head=False,
+        description="DETR-like encoder iRPE on keys at stride 16: 50x84 grid (4200 tokens, an 800x1344 "
+                    "image; rows of 84 columns), B2, h8 d32 bf16, r^K 81x32 shared"),
     "deit_s_irpe_bias_euclid": Workload(
         9, "deit_s_irpe_bias_euclid", batch=64, heads=6, head_dim=64, grid_h=14, grid_w=14, window=0,
         prefix=1, mode="bias", map="euclidean", alpha=1.9, beta=3.8, gamma=15.2, dtype=BF16,
