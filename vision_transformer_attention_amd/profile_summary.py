@@ -55,9 +55,12 @@ def fwd_name(name):
         return None
     dt, d, mode, terms, wide, multi, mk = m.groups()
     t = "".join(c for bit, c in ((1, "K"), (2, "Q"), (4, "V")) if int(terms) & bit)
+    # the fifth flag: several units per workgroup, or (with wide rows) rows of
+    # more than 64 key slots
+    rows = {("1", "0"): ", 64-slot rows", ("1", "1"): ", rows over 64 slots"}.get((wide, multi), "")
     return (f"rpe_fwd_kernel<{'bf16' if dt == 'DF16b' else 'fp32'}, d{d}, {_MODES[mode]}"
-            f"{' ' + t if t else ''}{', wide rows' if wide == '1' else ''}"
-            f"{', several units per workgroup' if multi == '1' else ''}{_MAPS[mk]}>")
+            f"{' ' + t if t else ''}{rows}"
+            f"{', several units per workgroup' if multi == '1' and wide == '0' else ''}{_MAPS[mk]}>")
 
 
 def demangle(names):
