@@ -427,12 +427,49 @@ __device__ __forceinline__ void fold_add(int lane, int bkt, float vl, float vp, 
 __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t ub, int i, int lane, float* wq, float* wv) {
   float* pr = a.P + (ub * a.T + i) * a.T;
   float* dr = a.dL + (ub * a.T + i) * a.T;
+  const int16_t* brow = a.bmap + static_cast<int64_t>(i) * a.T;
+  const int16_t* brow1 = a.bmap1 ? a.bmap1 + static_cast<int64_t>(i) * a.T : nullptr;
+  if (a.T <= 4 * 64) {
+    // rows of at most 256 keys: all of the row's loads go out at once and its
+    // values stay in registers for the second pass
+    float pv[4], dv[4];
+    int bk[4], bk1[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = 64 * c + lane;
+      pv[c] = 0.0f;
+      dv[c] = 0.0f;
+      bk[c] = -1;
+      bk1[c] = -1;
+      if (j < a.T) {
+        pv[c] = pr[j];
+        dv[c] = dr[j];
+        bk[c] = brow[j];
+        if (brow1) bk1[c] = brow1[j];
+      }
+    }
+    float dsum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dsum += pv[c] * dv[c];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (64 * c >= a.T) break;
+      const int j = 64 * c + lane;
+      const float l = pv[c] * (dv[c] - dsum);
+      if (j < a.T) dr[j] = l;
+      if (wq || wv) {
+        fold_add(lane, bk[c], l, pv[c], wq, wv);
+        if (brow1) fold_add(lane, bk1[c], l, pv[c], wq, wv);
+      }
+    }
+    return;
+  }
   float dsum = 0.0f;
   for (int j = lane; j < a.T; j += 64) dsum += pr[j] * dr[j];
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m);
-  const int16_t* brow = a.bmap + static_cast<int64_t>(i) * a.T;
-  const int16_t* brow1 = a.bmap1 ? a.bmap1 + static_cast<int64_t>(i) * a.T : nullptr;
   auto add_folded = [&](int bkt, float vl, float vp) { fold_add(lane, bkt, vl, vp, wq, wv); };
   for (int j0 = 0; j0 < a.T; j0 += 64) {
     const int j = j0 + lane;
