@@ -11,6 +11,7 @@ import pytest
 from oracle import Spec, num_buckets
 from oracle.backward import attention_backward
 from vision_transformer_attention_amd.workloads import WORKLOADS, make_inputs, round_to_dtype
+from random_configs import random_config
 
 pytestmark = pytest.mark.gpu
 
@@ -110,12 +111,37 @@ CASES = [
 
 @pytest.mark.parametrize("label,w", CASES)
 def test_backward_parity(dev, label, w):
-    import torch
-    import vision_transformer_attention_amd as pkg
     w = _fit(w)
     print("[case] backward", label, w.qkv_shape, flush=True)
-    x = make_inputs(w, sigma=1.0, seed=9950)
-    rng = np.random.default_rng(9951)
+    _check_backward(dev, w, 9950)
+
+
+def _random_backward_configs(n):
+    """The first n seeded random configurations the backward takes (undirected
+    maps: units of at most 91 rows and columns, (2 max(R, C) - 1)^2 <= 32767)."""
+    out, k = [], 100
+    while len(out) < n:
+        w = random_config(k)
+        r, c = (w.window, w.window) if w.window else (w.grid_h, w.grid_w)
+        if not (w.map in ("euclidean", "euclidean_rounded", "quantized", "quantized_squared")
+                and (2 * max(r, c) - 1) ** 2 > 32767):
+            out.append((k, w))
+        k += 1
+    return out
+
+
+@pytest.mark.parametrize("k,w", _random_backward_configs(12))
+def test_backward_random_configs(dev, k, w):
+    print("[case] backward random config", k, w.qkv_shape, w.mode, "".join(sorted(w.terms)), w.map, w.method,
+          w.dtype, "grid", (w.grid_h, w.grid_w), "window", w.window, "prefix", w.prefix, flush=True)
+    _check_backward(dev, w, 12700 + k)
+
+
+def _check_backward(dev, w, seed):
+    import torch
+    import vision_transformer_attention_amd as pkg
+    x = make_inputs(w, sigma=1.0, seed=seed)
+    rng = np.random.default_rng(seed + 1)
     dout = round_to_dtype(rng.standard_normal(w.qkv_shape), w.dtype)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32 if n == "bias" else tdt).to(dev)

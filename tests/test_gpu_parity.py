@@ -13,6 +13,7 @@ import pytest
 from oracle import Spec, attention, axis_index_table, num_buckets
 from oracle.attention import bucket_map_array
 from vision_transformer_attention_amd.workloads import WORKLOADS, make_inputs, round_to_dtype
+from random_configs import random_config
 
 pytestmark = pytest.mark.gpu
 
@@ -589,6 +590,14 @@ def test_wide_rows(dev, label, w):
         sel = dict(batch_sel=[w.batch - 1], heads_sel=[w.heads - 1])
     say("wide rows", label, w.qkv_shape, "sampled" if sel else "")
     compare(w, make_inputs(w, sigma=1.0, seed=9960), dev, **sel)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configs(dev, i):
+    w = random_config(i)
+    say("random config", i, w.qkv_shape, w.mode, "".join(sorted(w.terms)), w.map, w.method, w.dtype,
+        "grid", (w.grid_h, w.grid_w), "window", w.window, "prefix", w.prefix, "per-head", w.tables_per_head)
+    compare(w, make_inputs(w, sigma=1.0, seed=12500 + i), dev)
 
 
 def test_no_position_mode(dev):
