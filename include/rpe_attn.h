@@ -174,8 +174,8 @@ rpe_status rpe_attn_axis_index(const rpe_attn_desc* desc, int32_t length, int16_
  * (under Cross it names the two rows, by id / S and S + id % S); for an
  * undirected map it is the table row u(dy, dx) + H (iRPE page, eqs. 19-21,
  * indices in float64).  Requires T*T <= 2^31 - 1 (RPE_E_SHAPE); undirected
- * maps also S'*S' <= 32767 as for rpe_attn_undirected_to_product
- * (RPE_E_BUCKETS). */
+ * maps also (R-1)^2 + (C-1)^2 < 16384 for a unit of R x C positions (the
+ * squared offset lengths are tabulated in LDS; RPE_E_BUCKETS beyond). */
 rpe_status rpe_attn_bucket_map(const rpe_attn_desc* desc, int16_t* dev_map, void* stream);
 
 /* Cross mapping (iRPE page, Method, "Cross", eqs. 22-24): the encoding of a
@@ -269,8 +269,8 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
  * with float atomics otherwise, when their last bits can vary from call to call.
  * Asynchronous on `stream`.  Errors: descriptor validation; RPE_E_NULL for a
  * missing pointer; RPE_E_SHAPE if the workspace is too small or T*T >= 2^31;
- * RPE_E_BUCKETS for an undirected map with S'*S' > 32767 (see
- * rpe_attn_undirected_to_product). */
+ * RPE_E_BUCKETS for an undirected map on a unit of R x C positions with
+ * (R-1)^2 + (C-1)^2 >= 16384 (as for rpe_attn_bucket_map). */
 rpe_status rpe_attn_bwd_workspace_size(const rpe_attn_desc* desc, uint64_t* bytes);
 rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k, const void* v,
                         const void* dout, const float* lse, const float* bias, const void* rq,

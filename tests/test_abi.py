@@ -212,6 +212,13 @@ def test_undirected_maps_geometry_and_rejections(m):
     assert f(ctypes.byref(big), _lib.RPE_TABLE_BIAS, one, one, None) == -6     # 199^2 raw offsets
     assert lib.rpe_attn_bucket_map(ctypes.byref(big), one, None) == -6
     assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(big), ctypes.byref(n)) == -6
+    # the bound is on the squared offset lengths, (R-1)^2 + (C-1)^2 < 16384: a
+    # 2 x 127 grid (126^2 + 1) is taken, a 2 x 129 grid is not
+    for gw, want in ((127, 0), (129, -6)):
+        wide = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(2, gw), mode="bias", map=m,
+                             alpha=1.9, beta=3.8, gamma=15.2)
+        assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(wide), ctypes.byref(n)) == want
+        assert lib.rpe_attn_bucket_map(ctypes.byref(wide), None, None) == (-1 if want == 0 else want)
     pw = pkg.make_desc(batch=1, heads=2, head_dim=64, grid=(14, 14), mode="bias", map="piecewise",
                        alpha=1.9, beta=3.8, gamma=15.2)
     assert f(ctypes.byref(pw), _lib.RPE_TABLE_BIAS, one, one, None) == -4       # not undirected

@@ -118,13 +118,13 @@ def test_backward_parity(dev, label, w):
 
 def _random_backward_configs(n):
     """The first n seeded random configurations the backward takes (undirected
-    maps: units of at most 91 rows and columns, (2 max(R, C) - 1)^2 <= 32767)."""
+    maps: (R-1)^2 + (C-1)^2 < 16384 for a unit of R x C positions)."""
     out, k = [], 100
     while len(out) < n:
         w = random_config(k)
         r, c = (w.window, w.window) if w.window else (w.grid_h, w.grid_w)
         if not (w.map in ("euclidean", "euclidean_rounded", "quantized", "quantized_squared")
-                and (2 * max(r, c) - 1) ** 2 > 32767):
+                and (r - 1) ** 2 + (c - 1) ** 2 >= 16384):
             out.append((k, w))
         k += 1
     return out

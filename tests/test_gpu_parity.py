@@ -129,12 +129,14 @@ def test_bucket_map_bit_exact(dev, name, reading):
 @pytest.mark.parametrize("gh,gw,window,prefix,abg", [(14, 14, 0, 1, (1.9, 3.8, 15.2)),
                                                      (9, 23, 0, 0, (1.0, 2.0, 8.0)),
                                                      (14, 14, 7, 0, (1.9, 3.8, 15.2)),
-                                                     (91, 91, 0, 0, (3.8, 7.6, 30.4))])
+                                                     (91, 91, 0, 0, (3.8, 7.6, 30.4)),
+                                                     (2, 127, 0, 1, (1.9, 3.8, 15.2))])
 def test_undirected_pair_rows_bit_exact(dev, m, gh, gw, window, prefix, abg):
     # Under an undirected map the bucket map names each pair's table row
     # u(dy, dx) + H (iRPE page, Method, eqs. 19-21), evaluated on the device in
     # float64; the oracle evaluates each distinct offset on its own.  91 x 91 is
-    # the largest grid the device tabulation takes.
+    # the largest square grid the device tabulation takes ((R-1)^2 + (C-1)^2 <
+    # 16384), 2 x 127 the widest two-row one.
     import vision_transformer_attention_amd as pkg
     from oracle.attention import pair_rows_arrays
     a, b, g = abg

@@ -28,13 +28,11 @@ namespace {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 // An undirected map's pair rows are tabulated per squared offset length on the
-// device, (R-1)^2 + (C-1)^2 < 16384: the bound that S'*S' <= 32767 for the
-// Swin-map expansion (H' = max(R, C) - 1, S' = 2H'+1) gives as well.
+// device, one LDS entry per length: (R-1)^2 + (C-1)^2 < 16384.
 bool undirected_fits(const rpe_attn_desc* d) {
-  const int R = d->window ? d->window : d->grid_h;
-  const int C = d->window ? d->window : d->grid_w;
-  const int64_t sp = 2 * static_cast<int64_t>(R > C ? R : C) - 1;
-  return sp * sp <= 32767;
+  const int64_t R = d->window ? d->window : d->grid_h;
+  const int64_t C = d->window ? d->window : d->grid_w;
+  return (R - 1) * (R - 1) + (C - 1) * (C - 1) < 16384;
 }
 
 }  // namespace
