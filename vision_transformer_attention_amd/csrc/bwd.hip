@@ -278,9 +278,13 @@ __global__ void __launch_bounds__(64) bwd_rowtab_mfma_kernel(BwdArgs a) {
 // of the K and V rows (B operands); lane l then holds key column l % 32 of
 // query rows 8 j + 4 (l / 32) + i, so each store of P and dP covers 32
 // consecutive keys of a row.  Position terms, bias and exp as in
-// bwd_scores_kernel.
-template <int D>
-__global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
+// bwd_scores_kernel.  Compiled for three waves per SIMD: the epilogue works in
+// two halves of eight entries, the tile's log-sum-exps sit in LDS, and the
+// second table row of Cross maps (CR) has instances of its own (with head dim
+// 64 some 44 bytes per lane spill, which still beats two waves per SIMD by 9%
+// on DeiT-S).
+template <int D, bool CR>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) bwd_scores_mfma_kernel(BwdArgs a) {
   constexpr int KS = D / 16;
   const int lane = threadIdx.x, h = lane >> 5, r32 = lane & 31;
   const int nrt = (a.T + 31) / 32;
@@ -320,12 +324,14 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
     // (in log2 units: P = 2^(logit log2(e) - lse log2(e)) with the hardware exp2)
     constexpr float kLog2e = 1.4426950408889634f;
     const float scale2 = a.scale * kLog2e;
-    float lse[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-      lse[e] = a.lse[x.bh * a.N + token_of(a, x.u, i < T ? i : T - 1)] * kLog2e;
+    // the tile's 32 log-sum-exps in LDS (lane r reads row i0 + r), read back per entry
+    __shared__ float lse_s[32];
+    __syncthreads();
+    if (h == 0) {
+      const int i = i0 + r32;
+      lse_s[r32] = a.lse[x.bh * a.N + token_of(a, x.u, i < T ? i : T - 1)] * kLog2e;
     }
+    __syncthreads();
     for (int j0 = 0; j0 < T; j0 += 32) {
       const int j = j0 + r32;
       const int jr = j < T ? j : T - 1;
@@ -343,46 +349,52 @@ __global__ void __launch_bounds__(64) bwd_scores_mfma_kernel(BwdArgs a) {
       }
       // epilogue in rounds (bucket ids, then the row scores they select, then the
       // results), branch-free so that each round's loads are in flight together;
-      // rows and keys past T read clamped entries and are not stored
-      int bk[16], bk1[16];
+      // rows and keys past T read clamped entries and are not stored.  Two halves
+      // of eight entries each, to keep the round arrays small.
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        const int pij = (i < T ? i : T - 1) * T + jr;
-        bk[e] = a.bmap[pij];
-        bk1[e] = a.bmap1 ? a.bmap1[pij] : -1;
-      }
-      float add[16], dvt[16];
+      for (int hf = 0; hf < 2; ++hf) {
+        int bk[8], bk1[8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        const int ic = i < T ? i : T - 1;
-        const int bc = bk[e] < 0 ? 0 : bk[e];
-        const int wi = ic * nb, wj = jr * nb;
-        // logit addend in log2 units and the value term's part of dP
-        float r = 0.0f, u = 0.0f, bb = 0.0f;
-        if (Wq) r += Wq[wi + bc];
-        if (Wk) r += Wk[wj + bc];
-        if (Wv) u = Wv[wi + bc];
-        if (bt) bb = bt[bc];
-        if (a.bmap1) {
-          const int b1 = bk1[e] < 0 ? 0 : bk1[e];
-          if (Wq) r += Wq[wi + b1];
-          if (Wk) r += Wk[wj + b1];
-          if (Wv) u += Wv[wi + b1];
-          if (bt) bb += bt[b1];
-        }
-        add[e] = bk[e] >= 0 ? r * scale2 + bb * kLog2e : 0.0f;
-        dvt[e] = bk[e] >= 0 ? u : 0.0f;
-      }
-      if (j < T) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int q8 = 0; q8 < 8; ++q8) {
+          const int e = 8 * hf + q8;
           const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (i < T) {
-            const int o = i * T + j;
-            Pu[o] = __builtin_amdgcn_exp2f(sacc[e] * scale2 + add[e] - lse[e]);
-            dLu[o] = pacc[e] + dvt[e];
+          const int pij = (i < T ? i : T - 1) * T + jr;
+          bk[q8] = a.bmap[pij];
+          bk1[q8] = CR ? a.bmap1[pij] : -1;
+        }
+        float add[8], dvt[8];
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) {
+          const int e = 8 * hf + q8;
+          const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
+          const int ic = i < T ? i : T - 1;
+          const int bc = bk[q8] < 0 ? 0 : bk[q8];
+          const int wi = ic * nb, wj = jr * nb;
+          float r = 0.0f, u = 0.0f, bb = 0.0f;
+          if (Wq) r += Wq[wi + bc];
+          if (Wk) r += Wk[wj + bc];
+          if (Wv) u = Wv[wi + bc];
+          if (bt) bb = bt[bc];
+          if (CR) {
+            const int b1 = bk1[q8] < 0 ? 0 : bk1[q8];
+            if (Wq) r += Wq[wi + b1];
+            if (Wk) r += Wk[wj + b1];
+            if (Wv) u += Wv[wi + b1];
+            if (bt) bb += bt[b1];
+          }
+          add[q8] = bk[q8] >= 0 ? r * scale2 + bb * kLog2e : 0.0f;
+          dvt[q8] = bk[q8] >= 0 ? u : 0.0f;
+        }
+        if (j < T) {
+#pragma unroll
+          for (int q8 = 0; q8 < 8; ++q8) {
+            const int e = 8 * hf + q8;
+            const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (i < T) {
+              const int o = i * T + j;
+              Pu[o] = __builtin_amdgcn_exp2f(sacc[e] * scale2 + add[q8] - lse_s[8 * (e >> 2) + 4 * h + (e & 3)]);
+              dLu[o] = pacc[e] + dvt[q8];
+            }
           }
         }
       }
@@ -1206,9 +1218,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const int64_t qtiles = a.n_units * ((a.T + 31) / 32);
   const unsigned qgrid = static_cast<unsigned>(qtiles < 65536 ? qtiles : 65536);
   if (bf16 && a.D == 64)
-    hipLaunchKernelGGL(bwd_scores_mfma_kernel<64>, dim3(qgrid), dim3(64), 0, stream, a);
+    if (a.bmap1)
+      hipLaunchKernelGGL((bwd_scores_mfma_kernel<64, true>), dim3(qgrid), dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_scores_mfma_kernel<64, false>), dim3(qgrid), dim3(64), 0, stream, a);
   else if (bf16 && a.D == 32)
-    hipLaunchKernelGGL(bwd_scores_mfma_kernel<32>, dim3(qgrid), dim3(64), 0, stream, a);
+    if (a.bmap1)
+      hipLaunchKernelGGL((bwd_scores_mfma_kernel<32, true>), dim3(qgrid), dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_scores_mfma_kernel<32, false>), dim3(qgrid), dim3(64), 0, stream, a);
   else if (bf16)
     hipLaunchKernelGGL(bwd_scores_kernel<__bf16>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
   else
