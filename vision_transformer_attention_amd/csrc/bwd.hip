@@ -603,14 +603,29 @@ __global__ void __launch_bounds__(64) bwd_cols_lds_kernel(BwdArgs a) {
     const int jc = j < a.T ? j : a.T - 1;
     for (int b = 0; b < a.nb; ++b) wks[b * 64 + lane] = 0.0f;
     const float* Lc = a.dL + ub * a.T * a.T + jc;
-    for (int i = 0; i < a.T; ++i) {
-      const int64_t pij = static_cast<int64_t>(i) * a.T + jc;
-      const int bkt = a.bmap[pij];
-      if (bkt >= 0) {
-        const float l = Lc[static_cast<int64_t>(i) * a.T];
-        wks[bkt * 64 + lane] += l;
-        const int bk1 = a.bmap1 ? a.bmap1[pij] : -1;
-        if (bk1 >= 0) wks[bk1 * 64 + lane] += l;
+    // eight rows' loads at a time, then their sums in row order
+    for (int i0 = 0; i0 < a.T; i0 += 8) {
+      int bk[8], bk1[8];
+      float lv[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int i = i0 + m;
+        bk[m] = -1;
+        bk1[m] = -1;
+        lv[m] = 0.0f;
+        if (i < a.T) {
+          const int64_t pij = static_cast<int64_t>(i) * a.T + jc;
+          bk[m] = a.bmap[pij];
+          if (a.bmap1) bk1[m] = a.bmap1[pij];
+          lv[m] = Lc[static_cast<int64_t>(i) * a.T];
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (bk[m] >= 0) {
+          wks[bk[m] * 64 + lane] += lv[m];
+          if (bk1[m] >= 0) wks[bk1[m] * 64 + lane] += lv[m];
+        }
       }
     }
     if (j < a.T) {
