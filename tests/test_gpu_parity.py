@@ -581,6 +581,8 @@ _WIDE_ROWS = [
                                                   terms=frozenset("kqv"), map="euclidean")),
     ("contextual V, 3x70 + cls", _D.resized(batch=2, heads=2, grid_h=3, grid_w=70, terms=frozenset("v"))),
     ("contextual K, 50x84 detection grid", _D.resized(batch=1, heads=2, grid_h=50, grid_w=84, prefix=0)),
+    ("contextual K, 72x72 windows on a 72x144 grid", _D.resized(batch=1, heads=1, grid_h=72, grid_w=144,
+                                                                window=72, prefix=0)),
 ]
 
 
@@ -590,6 +592,8 @@ def test_wide_rows(dev, label, w):
     sel = {}
     if w.grid_h * w.grid_w > 2000:
         sel = dict(batch_sel=[w.batch - 1], heads_sel=[w.heads - 1])
+        if w.window:
+            sel["units"] = [1]
     say("wide rows", label, w.qkv_shape, "sampled" if sel else "")
     compare(w, make_inputs(w, sigma=1.0, seed=9960), dev, **sel)
 
