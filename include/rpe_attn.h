@@ -237,6 +237,31 @@ rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k,
                         const float* bias, const void* rq, const void* rk, const void* rv,
                         void* o, float* lse, void* stream);
 
+/* The launch plan rpe_attn_fwd makes for a descriptor, for inspection and
+ * capacity planning.  Host only, no device access; the same checks as
+ * rpe_attn_fwd's before it touches any pointer (validation, RPE_E_BUCKETS when
+ * the tables do not fit one CU's LDS, RPE_E_UNSUPPORTED for units wider than
+ * 256 columns or head dims other than 16/32/64), RPE_E_NULL for a NULL info.
+ * Key slots: a unit's grid rows are padded to row_slots key slots (the power of
+ * two >= its width up to 64, the multiple of 32 beyond) and streamed in blocks
+ * of 32 slots.  value_term: 0 none, 1 contracted per key block (bf16 Product),
+ * 2 weight sums per (row bucket, key column), 3 weight sums per bucket. */
+typedef struct {
+  int32_t row_slots;          /* key slots per grid row                                  */
+  int32_t key_blocks;         /* 32-slot key blocks per unit (a prefix block included)   */
+  int32_t waves_per_group;    /* waves per workgroup, one 32-row query tile each         */
+  int32_t query_chunks;       /* workgroups per unit                                     */
+  int32_t units_per_group;    /* units one workgroup walks (> 1: bias or plain, small)   */
+  int32_t ring_stages;        /* depth of the LDS ring of key / value blocks             */
+  int32_t lds_bytes;          /* LDS per workgroup                                       */
+  int32_t waves_per_simd;     /* resident waves per SIMD the instance is compiled for    */
+  int32_t value_term;         /* see above                                               */
+  int32_t reserved;           /* 0                                                       */
+  int64_t workgroups;         /* workgroups of the launch                                */
+} rpe_attn_plan_info;
+
+rpe_status rpe_attn_fwd_plan(const rpe_attn_desc* desc, rpe_attn_plan_info* info);
+
 /* Backward pass: gradients of o = rpe_attn_fwd(...) for a given dO = dL/do, with
  * respect to q, k, v and every table the descriptor uses, for every map and
  * method (an undirected map's tables as they are, not expanded).  Per unit, with

@@ -312,3 +312,48 @@ def test_method_validation_and_geometry():
                        table_head_stride=81 * 64 - 8, **kw)
     assert lib.rpe_attn_fwd(ctypes.byref(ph), one, one, one, None, None, one, None, one, None, None) == -2
     assert lib.rpe_status_str(-10).decode().startswith("a pointer or stride")
+
+
+def _plan(**kw):
+    base = dict(batch=2, heads=2, head_dim=64, grid=(14, 14), mode="contextual", terms="k", map="piecewise",
+                alpha=1.9, beta=3.8, gamma=15.2)
+    base.update(kw)
+    return pkg.rpe_attn_fwd_plan(pkg.make_desc(**base))
+
+
+def test_fwd_plan_row_slots_and_blocks():
+    _lib_or_skip()
+    # rows padded to the power of two up to 64 slots, to a multiple of 32 beyond
+    for (gh, gw), slots in (((14, 14), 16), ((56, 56), 64), ((50, 84), 96), ((3, 200), 224), ((2, 256), 256),
+                            ((7, 65), 96)):
+        p = _plan(grid=(gh, gw))
+        assert p["row_slots"] == slots, (gw, p)
+        assert p["key_blocks"] == (gh * slots + 31) // 32   # no prefix tokens
+    # a class token in the row padding adds no block; with no padding left it takes a block of its own
+    assert _plan(grid=(14, 14), prefix_tokens=1)["key_blocks"] == 7
+    assert _plan(grid=(2, 96), prefix_tokens=1)["key_blocks"] == 2 * 3 + 1
+
+
+def test_fwd_plan_fits_and_counts():
+    _lib_or_skip()
+    for kw in (dict(), dict(terms="kqv"), dict(terms="kqv", dtype="fp32", head_dim=32),
+               dict(mode="bias", terms="", grid=(56, 56), window=7, map="swin", tables_per_head=True),
+               dict(grid=(50, 84), head_dim=32), dict(mode="none", terms="", map="swin", grid=(4, 150))):
+        p = _plan(**kw)
+        assert 0 < p["lds_bytes"] <= 160 * 1024
+        assert 2 <= p["waves_per_group"] <= 4 and p["waves_per_simd"] in (2, 3, 4)
+        units = 2 * 2 * ((kw.get("grid", (14, 14))[0] // kw["window"]) ** 2 if kw.get("window") else 1)
+        assert p["workgroups"] * p["units_per_group"] == units * p["query_chunks"]
+    assert _plan()["value_term"] == "none"
+    assert _plan(terms="kqv")["value_term"] == "per key block"
+    assert _plan(terms="v", dtype="fp32", head_dim=32)["value_term"] in ("per (row bucket, key column) sums",
+                                                                          "per-bucket sums")
+
+
+def test_fwd_plan_errors():
+    lib = _lib_or_skip()
+    d = pkg.make_desc(batch=1, heads=1, head_dim=64, grid=(14, 14), mode="none")
+    assert lib.rpe_attn_fwd_plan(ctypes.byref(d), None) == -1
+    wide = pkg.make_desc(batch=1, heads=1, head_dim=64, grid=(2, 257), mode="none")
+    with pytest.raises(pkg.RpeError):
+        pkg.rpe_attn_fwd_plan(wide)

@@ -20,6 +20,7 @@ from .attention import (  # noqa: F401
     rpe_attn_bwd_noalloc,
     rpe_attn_cross_to_product,
     rpe_attn_fwd,
+    rpe_attn_fwd_plan,
     rpe_attn_num_buckets,
     rpe_attn_undirected_to_product,
     rpe_attn_unit_size,

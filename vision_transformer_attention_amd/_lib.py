@@ -30,6 +30,7 @@ STATUS_NAMES = {
 # Every symbol include/rpe_attn.h declares.
 EXPORTS = ("rpe_attn_validate", "rpe_attn_num_buckets", "rpe_attn_unit_size", "rpe_attn_axis_index",
            "rpe_attn_bucket_map", "rpe_attn_cross_to_product", "rpe_attn_undirected_to_product", "rpe_attn_fwd",
+           "rpe_attn_fwd_plan",
            "rpe_attn_bwd_workspace_size", "rpe_attn_bwd", "rpe_attn_bwd_noalloc", "rpe_status_str",
            "rpe_attn_version")
 BWD_NOALLOC_MAX_BYTES = 64 << 20
@@ -55,6 +56,24 @@ class RpeError(RuntimeError):
     def __init__(self, fn, status, text):
         super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} ({text})")
         self.status = status
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``rpe_attn_plan_info``."""
+
+    _fields_ = [
+        ("row_slots", ctypes.c_int32),
+        ("key_blocks", ctypes.c_int32),
+        ("waves_per_group", ctypes.c_int32),
+        ("query_chunks", ctypes.c_int32),
+        ("units_per_group", ctypes.c_int32),
+        ("ring_stages", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32),
+        ("waves_per_simd", ctypes.c_int32),
+        ("value_term", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workgroups", ctypes.c_int64),
+    ]
 
 
 _lib = None
@@ -90,6 +109,8 @@ def load():
         lib.rpe_attn_undirected_to_product.argtypes = [P(Desc), i32, vp, vp, vp]
         lib.rpe_attn_undirected_to_product.restype = i32
         lib.rpe_attn_fwd.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.rpe_attn_fwd_plan.argtypes = [P(Desc), P(PlanInfo)]
+        lib.rpe_attn_fwd_plan.restype = i32
         lib.rpe_attn_bwd_workspace_size.argtypes = [P(Desc), P(ctypes.c_uint64)]
         lib.rpe_attn_bwd_workspace_size.restype = i32
         lib.rpe_attn_bwd.argtypes = [P(Desc)] + [vp] * 17 + [ctypes.c_uint64, vp]

@@ -78,6 +78,19 @@ def rpe_attn_unit_size(desc):
     return n.value, t.value, u.value
 
 
+_VALUE_TERM = {0: "none", 1: "per key block", 2: "per (row bucket, key column) sums", 3: "per-bucket sums"}
+
+
+def rpe_attn_fwd_plan(desc):
+    """The launch plan rpe_attn_fwd makes for ``desc`` (host only), as a dict."""
+    from ._lib import PlanInfo
+    info = PlanInfo()
+    check("rpe_attn_fwd_plan", load().rpe_attn_fwd_plan(ctypes.byref(desc), ctypes.byref(info)))
+    out = {name: getattr(info, name) for name, _ in PlanInfo._fields_ if name != "reserved"}
+    out["value_term"] = _VALUE_TERM[out["value_term"]]
+    return out
+
+
 def _stream(device):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)

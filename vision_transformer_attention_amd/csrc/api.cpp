@@ -151,6 +151,28 @@ rpe_status rpe_attn_undirected_to_product(const rpe_attn_desc* desc, int32_t kin
   return e == hipSuccess ? RPE_OK : RPE_E_HIP;
 }
 
+rpe_status rpe_attn_fwd_plan(const rpe_attn_desc* desc, rpe_attn_plan_info* info) {
+  rpe::Params p;
+  const int st = rpe::make_plan(desc, &p);
+  if (st != RPE_OK) return static_cast<rpe_status>(st);
+  if (!info) return RPE_E_NULL;
+  const bool tv = desc->mode == RPE_MODE_CONTEXTUAL && (desc->terms & RPE_TERM_V);
+  info->row_slots = p.Wp;
+  info->key_blocks = p.n_blocks;
+  info->waves_per_group = p.NW;
+  info->query_chunks = p.n_qc;
+  info->units_per_group = p.upw;
+  info->ring_stages = p.stages;
+  info->lds_bytes = p.lds_bytes;
+  info->waves_per_simd = rpe::waves_per_simd(desc->mode, desc->terms,
+                                             rpe::wide_budget(p.Wp >= 64, p.Wp > 64, desc->dtype == RPE_BF16),
+                                             desc->head_dim, p.upw > 1);
+  info->value_term = !tv ? 0 : (p.skv ? 1 : (p.vw ? 2 : 3));
+  info->reserved = 0;
+  info->workgroups = p.n_wg;
+  return RPE_OK;
+}
+
 rpe_status rpe_attn_fwd(const rpe_attn_desc* desc, const void* q, const void* k, const void* v,
                         const float* bias, const void* rq, const void* rk, const void* rv, void* o,
                         float* lse, void* stream) {
