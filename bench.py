@@ -45,7 +45,7 @@ from vision_transformer_attention_amd.workloads import WORKLOADS, make_inputs  #
 METRIC = "2D-RPE attention fwd TFLOP/s and % bf16 MFMA peak (DeiT-S iRPE-K, Swin-T W7)"
 HEADLINE = "deit_s_irpe_k"
 SECONDARY = ("swin_t_w7", "deit_s_irpe_qkv", "highres_irpe_k", "deit_s_irpe_bias", "deit_s_irpe_k_cross",
-             "detr_irpe_k", "deit_s_irpe_bias_euclid", "detr_wide_irpe_k")
+             "detr_irpe_k", "deit_s_irpe_bias_euclid", "detr_wide_irpe_k", "swin_t_w7_irpe_qkv")
 PEAK_MFMA_BF16 = 2500.0      # TFLOP/s, dense, MI355X
 PEAK_HBM = 8000.0            # GB/s, MI355X HBM3E
 MALL_BYTES = 256 << 20

@@ -756,6 +756,7 @@ FULL_SAMPLES = {
     "detr_irpe_k": ([0, 7], [0, 7]),
     "deit_s_irpe_bias_euclid": ([0, 63], [0, 5]),
     "detr_wide_irpe_k": ([1], [7]),
+    "swin_t_w7_irpe_qkv": ([0, 31], [0, 2]),
 }
 
 

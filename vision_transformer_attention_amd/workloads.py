@@ -113,6 +113,12 @@ WORKLOADS = {
         gamma=15.2, dtype=BF16, table_rows=81, tables_per_head=False,
         description="DETR-like encoder iRPE on keys at stride 16: 50x84 grid (4200 tokens, an 800x1344 "
                     "image; rows of 84 columns), B2, h8 d32 bf16, r^K 81x32 shared"),
+    "swin_t_w7_irpe_qkv": Workload(
+        11, "swin_t_w7_irpe_qkv", batch=32, heads=3, head_dim=32, grid_h=56, grid_w=56, window=7,
+        prefix=0, mode="contextual", terms=frozenset("kqv"), map="piecewise", alpha=1.9, beta=3.8,
+        gamma=15.2, dtype=BF16, table_rows=81, tables_per_head=False,
+        description="Swin-T stage-1 7x7 windows with iRPE contextual product on queries, keys and values: "
+                    "B32, 56x56 grid (64 windows of 49 tokens), h3 d32 bf16, r^Q, r^K, r^V 81x32 shared"),
     "deit_s_irpe_bias_euclid": Workload(
         9, "deit_s_irpe_bias_euclid", batch=64, heads=6, head_dim=64, grid_h=14, grid_w=14, window=0,
         prefix=1, mode="bias", map="euclidean", alpha=1.9, beta=3.8, gamma=15.2, dtype=BF16,
