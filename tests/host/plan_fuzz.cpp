@@ -106,9 +106,11 @@ int main(int argc, char** argv) {
     REQUIRE(p.off_stage == 0);
     REQUIRE(p.off_rq >= p.stages * 2 * rpe::kBlockSlots * p.D * p.elem_bytes && p.off_rq % 16 == 0);
     REQUIRE(p.off_rq <= p.off_tab);
-    // the query-term table is staged unless the plan keeps one tile per wave in
-    // registers (bf16, no Cross, rows of at most 32 slots, nbt <= NW)
-    REQUIRE(p.rq_regs == ((tq && d.dtype == RPE_BF16 && !p.cross && p.Wp < 64 && p.nbt <= p.NW) ? 1 : 0));
+    // the query-term table is staged unless the plan keeps its tiles in registers
+    // (bf16, no Cross, rows of at most 32 slots, one tile per wave, or two for
+    // head dims up to 32)
+    REQUIRE(p.rq_regs == ((tq && d.dtype == RPE_BF16 && !p.cross && p.Wp < 64 &&
+                           (p.nbt <= p.NW || (p.D <= 32 && p.nbt <= 2 * p.NW))) ? 1 : 0));
     if (tq && !p.rq_regs) REQUIRE(p.off_rq + p.nrq * p.kpitch * p.elem_bytes <= p.off_rkc);
     REQUIRE(p.off_rkc >= p.off_rq && p.off_rkc % 16 == 0 && p.off_bx >= p.off_rkc && p.off_bx % 16 == 0);
     REQUIRE(p.off_tab >= p.off_bx);

@@ -453,8 +453,12 @@ rpe_fwd_kernel(Params p) {
   // rQ rows of this wave's query-term tile (buckets 32 wid + r32) as the A operand
   // of the block scores, in registers when the plan says so (p.rq_regs); rows past
   // nb are zero (their scores are never read)
+  // (head dims up to 32: a second tile, wid + NW, when the table has more tiles
+  // than the workgroup has waves)
   constexpr bool RQR = TQ && BF && !CROSS && !WIDE;
+  constexpr bool RQ2 = RQR && D <= 32;
   bf16x8 rqa[RQR ? KS : 1];
+  bf16x8 rqa2[RQ2 ? KS : 1];
   if constexpr (RQR) {
     const DT* rqt = reinterpret_cast<const DT*>(p.rq) + head * p.tab_head_stride;
     const int b = kRowTile * wid + r32;
@@ -464,7 +468,18 @@ rpe_fwd_kernel(Params p) {
       const int d0 = 16 * kk + 8 * h;
       rqa[kk] = as_bf16x8((ok && d0 < D) ? ld16(rqt + static_cast<int64_t>(b) * D + d0) : make_uint4(0, 0, 0, 0));
     }
+    if constexpr (RQ2) {
+      const int b2 = kRowTile * (wid + p.NW) + r32;
+      const bool ok2 = p.rq_regs && b2 < p.nb;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int d0 = 16 * kk + 8 * h;
+        rqa2[kk] =
+            as_bf16x8((ok2 && d0 < D) ? ld16(rqt + static_cast<int64_t>(b2) * D + d0) : make_uint4(0, 0, 0, 0));
+      }
+    }
   }
+  (void)rqa2;
 
   // ---- the block stream: per unit [Q tiles (multi-unit only)][key/value blocks]
   // [rV tiles]; a Q element carries 64 query rows (32 in each half of a stage)
@@ -1509,8 +1524,9 @@ rpe_fwd_kernel(Params p) {
   // under Cross (the bucket's row-offset row ra = b / S and column-offset row
   // rb = S + b % S, both multiplied into the accumulator).
   auto query_tile = [&](const char* ktile, int t, int ra, int rb, auto regs_c) __attribute__((always_inline)) {
-    // REGS: the A operand is this wave's rQ tile in registers (t == wid)
-    constexpr bool REGS = decltype(regs_c)::value;
+    // REGS: the A operand is this wave's rQ tile in registers, 1: tile wid (rqa),
+    // 2: tile wid + NW (rqa2); 0: staged
+    constexpr int REGS = static_cast<int>(decltype(regs_c)::value);
     if constexpr (TQ) {
       const int sw = r32 & (CPR - 1);
       const char* rqs = smem + p.off_rq;
@@ -1520,8 +1536,10 @@ rpe_fwd_kernel(Params p) {
         if constexpr (BF) {
           const int c = 2 * kk + h, d0 = 16 * kk + 8 * h;
           bf16x8 av;
-          if constexpr (REGS) {
+          if constexpr (REGS == 1) {
             av = rqa[kk];
+          } else if constexpr (REGS == 2) {
+            av = rqa2[kk];
           } else {
             av = as_bf16x8(*reinterpret_cast<const uint4*>(rqs + (ra * p.kpitch + d0) * 2));
           }
@@ -1558,6 +1576,9 @@ rpe_fwd_kernel(Params p) {
       } else {
         if (RQR && p.rq_regs) {
           if (wid < p.nbt) query_tile(ktile, wid, 0, 0, bool_c<RQR>{});
+          if constexpr (RQ2) {
+            if (wid + p.NW < p.nbt) query_tile(ktile, wid + p.NW, 0, 0, std::integral_constant<int, 2>{});
+          }
         } else {
           for (int t = wid; t < p.nbt; t += NW) query_tile(ktile, t, kRowTile * t + r32, 0, bool_c<false>{});
         }
@@ -1704,6 +1725,10 @@ rpe_fwd_kernel(Params p) {
     if constexpr (RQR) {
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(rqa[kk]));
+    }
+    if constexpr (RQ2) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(rqa2[kk]));
     }
   } else {
 #pragma unroll

@@ -57,7 +57,10 @@ int lds_layout(const rpe_attn_desc* d, Params* p) {
   // rows in registers instead (the Cross rows pair up per bucket and stay
   // staged, and so do those of rows of 64 or more slots, whose instances
   // have no registers to spare)
-  p->rq_regs = (tq && d->dtype == RPE_BF16 && !p->cross && p->Wp < 64 && p->nbt <= p->NW) ? 1 : 0;
+  // (head dims up to 32: two tiles per wave, tiles w and w + NW)
+  p->rq_regs = (tq && d->dtype == RPE_BF16 && !p->cross && p->Wp < 64 &&
+                (p->nbt <= p->NW || (p->D <= 32 && p->nbt <= 2 * p->NW)))
+                   ? 1 : 0;
   if (tq && !p->rq_regs) off += align(p->nrq * p->kpitch * eb, 16);
   // Cross key term: the table's 2S rows as swizzled [32][D] tiles (read per lane)
   p->off_rkc = off;
