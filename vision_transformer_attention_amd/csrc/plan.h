@@ -115,7 +115,8 @@ struct Params {
   int off_stage;          // stages x {K tile, V tile}, each [32][D] row-major, swizzled
   int kpitch;             // row pitch (elements) of the staged query-term table
   int off_rq;             // query-term table staged as [nrq][kpitch] (unless rq_regs)
-  int rq_regs;            // bf16 Product / undirected, Wp <= 32, nbt <= NW: wave w keeps rQ tile w in registers
+  int rq_regs;            // bf16 Product / undirected, Wp <= 32, nbt <= NW (2 NW for d <= 32):
+                          // wave w keeps rQ tiles w (and w + NW) in registers
   int nrq;                // staged query-term table rows: nbt*32 (Product) or 2S (Cross)
   int off_rkc;            // Cross key term: the 2S table rows as swizzled 32-row tiles
   int off_bx;             // Cross bias: the head's 2S entries (float32)
