@@ -283,8 +283,8 @@ rpe_status rpe_attn_fwd_plan(const rpe_attn_desc* desc, rpe_attn_plan_info* info
  *   drq, drk, drv : [H|1][rows][d] float32, written for the terms present (else
  *                   ignored); rows no pair reads get 0
  *   workspace     : device, at least rpe_attn_bwd_workspace_size() bytes, caller-owned;
- *                   it holds the weights and score gradients of every unit (2 B H U T^2
- *                   floats) and per-row bucket sums
+ *                   it holds the weights and score gradients of every unit (2 B H U T Ts
+ *                   floats, Ts = T rounded up to a multiple of 32) and per-row bucket sums
  * A sequence of kernels (not a fused pass) with float32 results.  For bf16 inputs with
  * head dim 32 or 64 the dense products run on the matrix cores with float32
  * accumulation; dL, P and the bucket sums enter them split into two bf16 parts (about
@@ -293,7 +293,7 @@ rpe_status rpe_attn_fwd_plan(const rpe_attn_desc* desc, rpe_attn_plan_info* info
  * in the workspace's weight region (B H U nb (terms x d + 1) <= B H U T^2 floats), and
  * with float atomics otherwise, when their last bits can vary from call to call.
  * Asynchronous on `stream`.  Errors: descriptor validation; RPE_E_NULL for a
- * missing pointer; RPE_E_SHAPE if the workspace is too small or T*T >= 2^31;
+ * missing pointer; RPE_E_SHAPE if the workspace is too small or T*Ts >= 2^31;
  * RPE_E_BUCKETS for an undirected map on a unit of R x C positions with
  * (R-1)^2 + (C-1)^2 >= 16384 (as for rpe_attn_bucket_map). */
 rpe_status rpe_attn_bwd_workspace_size(const rpe_attn_desc* desc, uint64_t* bytes);

@@ -232,9 +232,11 @@ def test_bwd_rejects_before_device():
     n = ctypes.c_uint64()
     assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
     T = 197
-    # bucket map + P + dL of 2 units, then the K and V bucket sums (81 per row), each 256-B aligned
+    # bucket map + P + dL of 2 units (rows padded to 224 floats), then the K and V bucket sums
+    # (81 per row), each 256-B aligned
     up = lambda v: (v + 255) // 256 * 256
-    assert n.value == up(T * T * 2) + 2 * up(2 * T * T * 4) + 2 * up(2 * T * 81 * 4)
+    Ts = 224
+    assert n.value == up(T * T * 2) + 2 * up(2 * T * Ts * 4) + 2 * up(2 * T * 81 * 4)
     assert lib.rpe_attn_bwd_workspace_size(ctypes.byref(d), None) == -1
     args = [one] * 16
     # the value table's gradient missing (rv given, drv NULL)

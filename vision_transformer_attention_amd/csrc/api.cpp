@@ -206,12 +206,16 @@ namespace {
 
 // Workspace of rpe_attn_bwd: the unit's pair-to-table-row map (two under
 // Cross), P and dL of every unit and the per-row table-row sums the present
-// terms need, each 256-byte aligned.
+// terms need, each 256-byte aligned.  The rows of P and dL are padded to a
+// multiple of 32 floats (128 bytes), so that a 32-column tile of a row is
+// whole and aligned.
 struct BwdLayout {
   uint64_t bmap, bmap1, P, dL, Wq, Wk, Wv, total;
 };
 
 uint64_t up256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+int score_row_stride(int T) { return (T + 31) / 32 * 32; }
 
 int bwd_layout(const rpe_attn_desc* d, BwdLayout* L, int* T_out, int* U_out, int* nb_out) {
   int st = rpe::validate(d);
@@ -237,7 +241,8 @@ int bwd_layout(const rpe_attn_desc* d, BwdLayout* L, int* T_out, int* U_out, int
   const int U = d->window ? (d->grid_h / d->window) * (d->grid_w / d->window) : 1;
   const uint64_t units = static_cast<uint64_t>(d->batch) * d->heads * U;
   const uint64_t tt = static_cast<uint64_t>(T) * T;
-  if (tt > 2147483647ULL) return RPE_E_SHAPE;
+  const uint64_t tts = static_cast<uint64_t>(T) * score_row_stride(T);
+  if (tts > 2147483647ULL) return RPE_E_SHAPE;
   const bool ctx = d->mode == RPE_MODE_CONTEXTUAL;
   const bool wq = d->mode == RPE_MODE_BIAS || (ctx && (d->terms & RPE_TERM_K));
   const bool wk = ctx && (d->terms & RPE_TERM_Q);
@@ -247,8 +252,8 @@ int bwd_layout(const rpe_attn_desc* d, BwdLayout* L, int* T_out, int* U_out, int
   const bool cross = d->method == RPE_METHOD_CROSS;
   L->bmap = off; off += up256(tt * 2);
   L->bmap1 = cross ? off : ~0ULL; off += cross ? up256(tt * 2) : 0;
-  L->P = off; off += up256(units * tt * 4);
-  L->dL = off; off += up256(units * tt * 4);
+  L->P = off; off += up256(units * tts * 4);
+  L->dL = off; off += up256(units * tts * 4);
   L->Wq = wq ? off : ~0ULL; off += wq ? up256(rows) : 0;
   L->Wk = wk ? off : ~0ULL; off += wk ? up256(rows) : 0;
   L->Wv = wv ? off : ~0ULL; off += wv ? up256(rows) : 0;
@@ -311,6 +316,7 @@ rpe_status rpe_attn_bwd(const rpe_attn_desc* desc, const void* q, const void* k,
   a.H = desc->heads;
   a.U = U;
   a.T = T;
+  a.Ts = score_row_stride(T);
   a.npre = desc->prefix_tokens;
   a.C = desc->window ? desc->window : desc->grid_w;
   a.M = desc->window;

@@ -16,13 +16,14 @@ struct BwdArgs {
   float* dq; float* dk; float* dv;
   float* dbias; float* drq; float* drk; float* drv;
   // workspace
-  float* P; float* dL;      // [n_units][T][T]
+  float* P; float* dL;      // [n_units][T][Ts]
   float* Wq; float* Wk; float* Wv;   // [n_units][T][nb] (null when not needed)
   const int16_t* bmap;      // [T][T] table row of each pair of one unit (-1: prefix pair)
   const int16_t* bmap1;     // [T][T] its second table row (Cross), or null: one row per pair
   // geometry
   int bf16;
   int D, N, H, U, T;
+  int Ts;                   // row stride of P and dL: T rounded up to a multiple of 32
   int npre;                 // prefix tokens
   int C;                    // positioned columns of a unit
   int M;                    // window side (0: global)

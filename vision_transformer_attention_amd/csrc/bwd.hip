@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(256) bwd_scores_kernel(BwdArgs a) {
       }
       const float logit = (qk[m] + rho) * a.scale + bsum;
       const float p = expf(logit - a.lse[x.bh * a.N + ti[m]]);
-      const int64_t o = (ub * a.T + ii[m]) * a.T + j;
+      const int64_t o = (ub * a.T + ii[m]) * a.Ts + j;
       a.P[o] = p;
       a.dL[o] = dpm;
     }
@@ -301,8 +301,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) bw
     const __bf16* const k = static_cast<const __bf16*>(a.k) + x.base;
     const __bf16* const v = static_cast<const __bf16*>(a.v) + x.base;
     const __bf16* const dO = static_cast<const __bf16*>(a.dout) + x.base;
-    float* const Pu = a.P + ub * T * T;
-    float* const dLu = a.dL + ub * T * T;
+    float* const Pu = a.P + ub * T * a.Ts;
+    float* const dLu = a.dL + ub * T * a.Ts;
     const float* const Wq = a.rk ? a.Wq + ub * T * nb : nullptr;
     const float* const Wk = a.rq ? a.Wk + ub * T * nb : nullptr;
     const float* const Wv = a.rv ? a.Wv + ub * T * nb : nullptr;
@@ -391,7 +391,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) bw
             const int e = 8 * hf + q8;
             const int i = i0 + 8 * (e >> 2) + 4 * h + (e & 3);
             if (i < T) {
-              const int o = i * T + j;
+              const int o = i * a.Ts + j;
               Pu[o] = __builtin_amdgcn_exp2f(sacc[e] * scale2 + add[q8] - lse_s[8 * (e >> 2) + 4 * h + (e & 3)]);
               dLu[o] = pacc[e] + dvt[q8];
             }
@@ -437,8 +437,8 @@ __device__ __forceinline__ void fold_add(int lane, int bkt, float vl, float vp, 
 // sum_j P_ij into wv[b] over the pairs that read row b (float atomics, LDS or
 // global; a null pointer: not wanted).
 __device__ __forceinline__ void bwd_row(const BwdArgs& a, int64_t ub, int i, int lane, float* wq, float* wv) {
-  float* pr = a.P + (ub * a.T + i) * a.T;
-  float* dr = a.dL + (ub * a.T + i) * a.T;
+  float* pr = a.P + (ub * a.T + i) * a.Ts;
+  float* dr = a.dL + (ub * a.T + i) * a.Ts;
   const int16_t* brow = a.bmap + static_cast<int64_t>(i) * a.T;
   const int16_t* brow1 = a.bmap1 ? a.bmap1 + static_cast<int64_t>(i) * a.T : nullptr;
   if (a.T <= 4 * 64) {
@@ -547,7 +547,7 @@ __global__ void __launch_bounds__(256) bwd_rows_unit_kernel(BwdArgs a) {
       // rows of at most 64 keys: one element per lane; the wave loads four of
       // its rows at once, then sums them in order
       const bool on = lane < a.T;
-      const int64_t base = ub * a.T * a.T;
+      const int64_t base = ub * a.T * a.Ts;
       for (int i0 = w; i0 < a.T; i0 += 16) {
         float pj[4], dj[4];
         int bk[4], bk1[4];
@@ -560,8 +560,9 @@ __global__ void __launch_bounds__(256) bwd_rows_unit_kernel(BwdArgs a) {
           bk1[r] = -1;
           if (on && i < a.T) {
             const int64_t o = static_cast<int64_t>(i) * a.T + lane;
-            pj[r] = a.P[base + o];
-            dj[r] = a.dL[base + o];
+            const int64_t ow = base + static_cast<int64_t>(i) * a.Ts + lane;
+            pj[r] = a.P[ow];
+            dj[r] = a.dL[ow];
             bk[r] = a.bmap[o];
             if (a.bmap1) bk1[r] = a.bmap1[o];
           }
@@ -574,7 +575,7 @@ __global__ void __launch_bounds__(256) bwd_rows_unit_kernel(BwdArgs a) {
 #pragma unroll
           for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m);
           const float l = pj[r] * (dj[r] - dsum);
-          if (on) a.dL[base + static_cast<int64_t>(i) * a.T + lane] = l;
+          if (on) a.dL[base + static_cast<int64_t>(i) * a.Ts + lane] = l;
           fold_add(lane, bk[r], l, 0.0f, ws, nullptr);
           if (a.bmap1) fold_add(lane, bk1[r], l, 0.0f, ws, nullptr);
         }
@@ -602,7 +603,7 @@ __global__ void __launch_bounds__(64) bwd_cols_lds_kernel(BwdArgs a) {
     const int j = static_cast<int>(wg - ub * nct) * 64 + lane;
     const int jc = j < a.T ? j : a.T - 1;
     for (int b = 0; b < a.nb; ++b) wks[b * 64 + lane] = 0.0f;
-    const float* Lc = a.dL + ub * a.T * a.T + jc;
+    const float* Lc = a.dL + ub * a.T * a.Ts + jc;
     // eight rows' loads at a time, then their sums in row order
     for (int i0 = 0; i0 < a.T; i0 += 8) {
       int bk[8], bk1[8];
@@ -617,7 +618,7 @@ __global__ void __launch_bounds__(64) bwd_cols_lds_kernel(BwdArgs a) {
           const int64_t pij = static_cast<int64_t>(i) * a.T + jc;
           bk[m] = a.bmap[pij];
           if (a.bmap1) bk1[m] = a.bmap1[pij];
-          lv[m] = Lc[static_cast<int64_t>(i) * a.T];
+          lv[m] = Lc[static_cast<int64_t>(i) * a.Ts];
         }
       }
 #pragma unroll
@@ -648,7 +649,7 @@ __global__ void __launch_bounds__(256) bwd_cols_kernel(BwdArgs a) {
       const int64_t pij = static_cast<int64_t>(i) * a.T + j;
       const int bkt = a.bmap[pij];
       if (bkt >= 0) {
-        const float l = a.dL[(ub * a.T + i) * a.T + j];
+        const float l = a.dL[(ub * a.T + i) * a.Ts + j];
         wk[bkt] += l;
         const int bk1 = a.bmap1 ? a.bmap1[pij] : -1;
         if (bk1 >= 0) wk[bk1] += l;
@@ -681,8 +682,8 @@ __global__ void __launch_bounds__(256) bwd_grads_kernel(BwdArgs a) {
     const int t0 = tb * kTB;
     const Unit x = unit_of(a, ub);
     const int64_t tbo = (a.tables_per_head ? x.head : 0) * static_cast<int64_t>(a.nb);
-    const float* Pu = a.P + ub * a.T * a.T;
-    const float* Lu = a.dL + ub * a.T * a.T;
+    const float* Pu = a.P + ub * a.T * a.Ts;
+    const float* Lu = a.dL + ub * a.T * a.Ts;
     int tr[kTB];   // this thread's rows / columns (clamped; the extra ones are not written)
 #pragma unroll
     for (int m = 0; m < kTB; ++m) tr[m] = t0 + m < a.T ? t0 + m : a.T - 1;
@@ -697,7 +698,7 @@ __global__ void __launch_bounds__(256) bwd_grads_kernel(BwdArgs a) {
       for (int j = 0; j < a.T; ++j, it.next()) {
         const float kv = ld(kb, static_cast<int64_t>(it.tok) * a.D);
 #pragma unroll
-        for (int m = 0; m < kTB; ++m) g[m] += Lu[static_cast<int64_t>(tr[m]) * a.T + j] * kv;
+        for (int m = 0; m < kTB; ++m) g[m] += Lu[static_cast<int64_t>(tr[m]) * a.Ts + j] * kv;
       }
       if (a.rk) {
         for (int bk = 0; bk < a.nb; ++bk) {
@@ -717,8 +718,8 @@ __global__ void __launch_bounds__(256) bwd_grads_kernel(BwdArgs a) {
       for (int i = 0; i < a.T; ++i, it.next()) {
         const int64_t ti = static_cast<int64_t>(it.tok) * a.D;
         const float qv = ld(qb, ti), ov = ld(ob, ti);
-        const float* Li = Lu + static_cast<int64_t>(i) * a.T;
-        const float* Pi = Pu + static_cast<int64_t>(i) * a.T;
+        const float* Li = Lu + static_cast<int64_t>(i) * a.Ts;
+        const float* Pi = Pu + static_cast<int64_t>(i) * a.Ts;
 #pragma unroll
         for (int m = 0; m < kTB; ++m) {
           gk[m] += Li[tr[m]] * qv;
@@ -852,16 +853,21 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
     const int nc = n < a.T ? n : a.T - 1;
     const bool nok = n < a.T;
     if (kind == 0) {
-      const float* Lr = a.dL + (ub * a.T + nc) * a.T;
+      // row n of dL: 128-byte aligned with room for whole 32-column tiles, so
+      // each group of four k slots is one 16-byte load (columns past T masked)
+      const float* Lr = a.dL + (ub * a.T + nc) * a.Ts;
       for (int jt = 0; jt < nrt; ++jt) {
         stage(tiles[0], k, jt * 32, a.T, false);
+        f32x4_t lq[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) lq[g] = *reinterpret_cast<const f32x4_t*>(Lr + jt * 32 + kslot(g >> 1, 4 * (g & 1), h));
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           float bv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int j = jt * 32 + kslot(kk, e, h);
-            bv[e] = (nok && j < a.T) ? Lr[j] : 0.0f;
+            bv[e] = (nok && j < a.T) ? lq[2 * kk + (e >> 2)][e & 3] : 0.0f;
           }
           mma(acc0, tiles[0], kk, bv);
         }
@@ -885,8 +891,8 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
         }
       }
     } else {
-      const float* Lc = a.dL + ub * a.T * a.T + nc;
-      const float* Pc = a.P + ub * a.T * a.T + nc;
+      const float* Lc = a.dL + ub * a.T * a.Ts + nc;
+      const float* Pc = a.P + ub * a.T * a.Ts + nc;
       for (int it = 0; it < nrt; ++it) {
         stage(tiles[0], q, it * 32, a.T, false);
         stage(tiles[1], dO, it * 32, a.T, false);
@@ -897,7 +903,7 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
           for (int e = 0; e < 8; ++e) {
             const int i = it * 32 + kslot(kk, e, h);
             const bool ok = nok && i < a.T;
-            const int64_t o = static_cast<int64_t>(ok ? i : 0) * a.T;
+            const int64_t o = static_cast<int64_t>(ok ? i : 0) * a.Ts;
             bl[e] = ok ? Lc[o] : 0.0f;
             bp[e] = ok ? Pc[o] : 0.0f;
           }
