@@ -533,11 +533,14 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(BwdArgs a) {
 
 // Bias mode: the table gradient needs only each unit's sums over all its rows,
 // dbias[b] = sum_i sum_j dL_ij over the pairs that read row b.  One workgroup of
-// 4 waves per unit: wave w takes the rows i = w, w + 4, ... into its own nb LDS
-// floats, and the four are added in a fixed order into Wq[b][unit] (the unit's
-// partial, stored [nb][n_units] so that the reduction over units reads whole
-// lines).  No per-row sums reach global memory.
-__global__ void __launch_bounds__(256) bwd_rows_unit_kernel(BwdArgs a) {
+// NW waves per unit: wave w takes the rows i = w, w + NW, ... into its own nb LDS
+// floats, and the NW are added pairwise in a fixed order into Wq[b][unit] (the
+// unit's partial, stored [nb][n_units] so that the reduction over units reads
+// whole lines).  No per-row sums reach global memory.  Units of more than 64
+// tokens take 16 waves, so that few units still fill the chip and each wave
+// walks fewer rows one after another.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) bwd_rows_unit_kernel(BwdArgs a) {
   extern __shared__ float wsh[];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float* const ws = wsh + w * a.nb;
@@ -548,12 +551,12 @@ __global__ void __launch_bounds__(256) bwd_rows_unit_kernel(BwdArgs a) {
       // its rows at once, then sums them in order
       const bool on = lane < a.T;
       const int64_t base = ub * a.T * a.Ts;
-      for (int i0 = w; i0 < a.T; i0 += 16) {
+      for (int i0 = w; i0 < a.T; i0 += 4 * NW) {
         float pj[4], dj[4];
         int bk[4], bk1[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = i0 + 4 * r;
+          const int i = i0 + NW * r;
           pj[r] = 0.0f;
           dj[r] = 0.0f;
           bk[r] = -1;
@@ -569,7 +572,7 @@ __global__ void __launch_bounds__(256) bwd_rows_unit_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = i0 + 4 * r;
+          const int i = i0 + NW * r;
           if (i >= a.T) break;
           float dsum = pj[r] * dj[r];
 #pragma unroll
@@ -581,11 +584,19 @@ __global__ void __launch_bounds__(256) bwd_rows_unit_kernel(BwdArgs a) {
         }
       }
     } else {
-      for (int i = w; i < a.T; i += 4) bwd_row(a, ub, i, lane, ws, nullptr);
+      for (int i = w; i < a.T; i += NW) bwd_row(a, ub, i, lane, ws, nullptr);
     }
     __syncthreads();
-    for (int b = threadIdx.x; b < a.nb; b += 256)
-      a.Wq[b * a.n_units + ub] = (wsh[b] + wsh[a.nb + b]) + (wsh[2 * a.nb + b] + wsh[3 * a.nb + b]);
+    for (int b = threadIdx.x; b < a.nb; b += 64 * NW) {
+      float v[NW];
+#pragma unroll
+      for (int k = 0; k < NW; ++k) v[k] = wsh[k * a.nb + b];
+#pragma unroll
+      for (int st = 1; st < NW; st *= 2)
+#pragma unroll
+        for (int k = 0; k < NW; k += 2 * st) v[k] += v[k + st];
+      a.Wq[b * a.n_units + ub] = v[0];
+    }
     __syncthreads();
   }
 }
@@ -1252,12 +1263,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_scores_kernel<__bf16>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(bwd_scores_kernel<float>, dim3(blocks_for(spairs)), dim3(256), 0, stream, a);
-  // bias mode: per-unit sums only (LDS: 4 waves x nb floats, up to 32 KB)
+  // bias mode: per-unit sums only (LDS: 4 waves x nb floats, up to 32 KB, or
+  // 16 waves x nb floats, up to 64 KB)
   const bool unit_sums = a.dbias && a.Wq && !a.Wk && !a.Wv && !a.drk && !a.drq && !a.drv && a.nb <= 2048;
   if (unit_sums) {
     const unsigned ugrid = static_cast<unsigned>(a.n_units < 65536 ? a.n_units : 65536);
-    hipLaunchKernelGGL(bwd_rows_unit_kernel, dim3(ugrid), dim3(256), static_cast<size_t>(4 * a.nb) * sizeof(float),
-                       stream, a);
+    if (a.T > 64 && a.nb <= 1024)
+      hipLaunchKernelGGL(bwd_rows_unit_kernel<16>, dim3(ugrid), dim3(1024),
+                         static_cast<size_t>(16 * a.nb) * sizeof(float), stream, a);
+    else
+      hipLaunchKernelGGL(bwd_rows_unit_kernel<4>, dim3(ugrid), dim3(256), static_cast<size_t>(4 * a.nb) * sizeof(float),
+                         stream, a);
   } else if (a.nb <= 2048) {
     // (LDS sums: 4 waves x 2 x nb floats per block, up to 64 KB)
     hipLaunchKernelGGL(bwd_rows_kernel<true>, dim3(blocks_for(rows * 64)), dim3(256),
