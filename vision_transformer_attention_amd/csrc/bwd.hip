@@ -1174,6 +1174,73 @@ __global__ void __launch_bounds__(256) bwd_tables_reduce_kernel(BwdArgs a, const
   }
 }
 
+// The same sums for the kinds drK, drQ, drV when their partials are stored
+// [unit][nb][D] (so consecutive (b, d) elements of a unit are adjacent): one
+// workgroup per 16 consecutive (table, b, d) elements of one kind.  Thread
+// (u16, e) adds the partials of the table's units u16, u16 + 16, ... of element
+// e in that order, eight loads in flight, and the sixteen unit groups are then
+// added in order through LDS.  A wave's loads cover four runs of 64 bytes,
+// where one wave per element would read one float from a different line per
+// lane.  Needs D a multiple of 16 (G nb D elements per kind).
+__global__ void __launch_bounds__(256) bwd_tables_reduce_d_kernel(BwdArgs a, const float* part) {
+  __shared__ float red[16][17];
+  const int e = threadIdx.x & 15, u16 = threadIdx.x >> 4;
+  const int G = a.tables_per_head ? a.H : 1;
+  const int64_t NU = a.n_units / G;
+  const int64_t nbd = static_cast<int64_t>(a.nb) * a.D;
+  const int64_t region = a.n_units * nbd;
+  const int64_t cpk = static_cast<int64_t>(G) * nbd / 16;   // chunks per kind
+  const int nkinds = (a.drk ? 1 : 0) + (a.drq ? 1 : 0) + (a.drv ? 1 : 0);
+  const int64_t chunks = nkinds * cpk;
+  for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+    const int64_t kc = div_idx(c, cpk);       // kc-th kind present, in the order drK, drQ, drV
+    const int64_t r0 = (c - kc * cpk) * 16;   // the chunk's first (table, b, d) element
+    int kind;
+    {
+      int64_t k = kc;
+      if (a.drk && k == 0) {
+        kind = 0;
+      } else {
+        if (a.drk) --k;
+        kind = a.drq && k == 0 ? 1 : 2;
+      }
+    }
+    const float* const src = part + kc * region;
+    float* const dst = kind == 0 ? a.drk : kind == 1 ? a.drq : a.drv;
+    const int64_t g = div_idx(r0, nbd);
+    const int64_t bd = r0 - g * nbd + e;
+    auto at = [&](int64_t kk) -> int64_t {
+      int64_t ub = kk;
+      if (a.tables_per_head) {
+        const int64_t bb = div_idx(kk, a.U), uu = kk - bb * a.U;
+        ub = (bb * a.H + g) * a.U + uu;
+      }
+      return ub * nbd + bd;
+    };
+    float acc = 0.0f;
+    for (int64_t k0 = u16; k0 < NU; k0 += 8 * 16) {
+      float v[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int64_t kk = k0 + 16 * m;
+        v[m] = kk < NU ? src[at(kk)] : 0.0f;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        if (k0 + 16 * m < NU) acc += v[m];
+    }
+    red[u16][e] = acc;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      float s = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) s += red[k][threadIdx.x];
+      dst[r0 + threadIdx.x] = kind < 2 ? s * a.scale : s;
+    }
+    __syncthreads();
+  }
+}
+
 unsigned blocks_for(int64_t n) {
   int64_t b = (n + 255) / 256;
   if (b > 65536) b = 65536;
@@ -1327,8 +1394,15 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_tables_kernel<__bf16, true>), dim3(blocks_for(n)), dim3(256), 0, stream, a, a.P);
       else
         hipLaunchKernelGGL((bwd_tables_kernel<float, true>), dim3(blocks_for(n)), dim3(256), 0, stream, a, a.P);
-      const int64_t nw = kinds * nt * a.D + (a.dbias ? nt : 0);
-      hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nw * 64)), dim3(256), 0, stream, a, a.P, 0);
+      // (bias mode has no contextual terms, so kinds > 0 means no dbias)
+      if (kinds > 0 && a.D % 16 == 0 && !a.dbias) {
+        const int64_t chunks = kinds * nt * a.D / 16;
+        const unsigned cgrid = static_cast<unsigned>(chunks < 65536 ? chunks : 65536);
+        hipLaunchKernelGGL(bwd_tables_reduce_d_kernel, dim3(cgrid), dim3(256), 0, stream, a, a.P);
+      } else {
+        const int64_t nw = kinds * nt * a.D + (a.dbias ? nt : 0);
+        hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nw * 64)), dim3(256), 0, stream, a, a.P, 0);
+      }
     } else {
       for (float* g : {a.drk, a.drq, a.drv})
         if (g) hipLaunchKernelGGL(bwd_zero_kernel, dim3(blocks_for(nt * a.D)), dim3(256), 0, stream, g, nt * a.D);
