@@ -970,7 +970,7 @@ __global__ void __launch_bounds__(64) bwd_grads_mfma_kernel(BwdArgs a) {
 // 64): one wave per (unit, 32-bucket tile, kind) forms the unit's
 // drK^T = Q^T Wq (kind 0), drQ^T = K^T Wk (1) or drV^T = dO^T Wv (2) for its
 // buckets, over the unit's rows in tiles of 32, into the partial regions that
-// bwd_tables_reduce_kernel adds up (unscaled, as the other stage-1 kernel).
+// reduction kernels add up (unscaled, as the other stage-1 kernel).
 template <int D>
 __global__ void __launch_bounds__(64) bwd_tables_mfma_kernel(BwdArgs a, float* part) {
   constexpr int RB = D * 2, DTL = D / 32;
@@ -1109,8 +1109,8 @@ __global__ void bwd_tables_kernel(BwdArgs a, float* part) {
 
 // Stage 2: one wave per table-gradient element (kind, table, b, d); its lanes
 // take the table's units in turn, then a fixed shuffle tree adds the lanes.
-// bias_t: the bias partials are stored [nb][n_units] (from the bias-mode row pass).
-__global__ void __launch_bounds__(256) bwd_tables_reduce_kernel(BwdArgs a, const float* part, int bias_t) {
+// Partials stored [unit][nb][D] (bias: [unit][nb]).
+__global__ void __launch_bounds__(256) bwd_tables_reduce_kernel(BwdArgs a, const float* part) {
   const int lane = threadIdx.x & 63;
   const int G = a.tables_per_head ? a.H : 1;
   const int64_t NU = a.n_units / G;
@@ -1147,14 +1147,13 @@ __global__ void __launch_bounds__(256) bwd_tables_reduce_kernel(BwdArgs a, const
     const int64_t bd = gbd - g * a.nb * De;     // b * De + d
     // Lane l adds the partials of the table's units l, l + 64, ... in that order;
     // the loads go out eight at a time (the order of the additions is kept).
-    const bool tr = kind == 3 && bias_t;
     auto addr = [&](int64_t kk) -> int64_t {
       int64_t ub = kk;
       if (a.tables_per_head) {
         const int64_t bb = div_idx(kk, a.U), uu = kk - bb * a.U;
         ub = (bb * a.H + g) * a.U + uu;
       }
-      return tr ? bd * a.n_units + ub : ub * a.nb * De + bd;
+      return ub * a.nb * De + bd;
     };
     float acc = 0.0f;
     for (int64_t k0 = lane; k0 < NU; k0 += 8 * 64) {
@@ -1237,6 +1236,48 @@ __global__ void __launch_bounds__(256) bwd_tables_reduce_d_kernel(BwdArgs a, con
       for (int k = 0; k < 16; ++k) s += red[k][threadIdx.x];
       dst[r0 + threadIdx.x] = kind < 2 ? s * a.scale : s;
     }
+    __syncthreads();
+  }
+}
+
+// dbias from the bias row pass's per-unit sums ([nb][n_units], a table entry's
+// units adjacent): one workgroup of 256 threads per table entry (g, b).  Thread
+// t adds the entry's units t, t + 256, ... in that order (eight loads in
+// flight), each wave folds its lanes, and the four wave sums are added in order.
+__global__ void __launch_bounds__(256) bwd_bias_reduce_kernel(BwdArgs a, const float* part) {
+  __shared__ float wsum[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int G = a.tables_per_head ? a.H : 1;
+  const int64_t NU = a.n_units / G;
+  const int64_t ne = static_cast<int64_t>(G) * a.nb;
+  for (int64_t gb = blockIdx.x; gb < ne; gb += gridDim.x) {
+    const int64_t g = div_idx(gb, a.nb);
+    const int64_t b = gb - g * a.nb;
+    auto at = [&](int64_t kk) -> int64_t {
+      int64_t ub = kk;
+      if (a.tables_per_head) {
+        const int64_t bb = div_idx(kk, a.U), uu = kk - bb * a.U;
+        ub = (bb * a.H + g) * a.U + uu;
+      }
+      return b * a.n_units + ub;
+    };
+    float acc = 0.0f;
+    for (int64_t k0 = threadIdx.x; k0 < NU; k0 += 8 * 256) {
+      float v[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int64_t kk = k0 + 256 * m;
+        v[m] = kk < NU ? part[at(kk)] : 0.0f;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        if (k0 + 256 * m < NU) acc += v[m];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (lane == 0) wsum[w] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) a.dbias[gb] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
     __syncthreads();
   }
 }
@@ -1376,7 +1417,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     // the per-unit partials are in Wq already ([nb][n_units]), where the
     // reduction reads the bias kind's partials when no other kind is present
     const int64_t nt = static_cast<int64_t>(tables) * a.nb;
-    hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nt * 64)), dim3(256), 0, stream, a, a.Wq, 1);
+    hipLaunchKernelGGL(bwd_bias_reduce_kernel, dim3(static_cast<unsigned>(nt < 65536 ? nt : 65536)), dim3(256), 0,
+                       stream, a, a.Wq);
   } else if (a.drk || a.drq || a.drv || a.dbias) {
     const int64_t nt = static_cast<int64_t>(tables) * a.nb;
     const int64_t n = a.n_units * ((a.nb + kBB - 1) / kBB) * ((a.drk || a.drq || a.drv) ? a.D : 1);
@@ -1401,7 +1443,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(bwd_tables_reduce_d_kernel, dim3(cgrid), dim3(256), 0, stream, a, a.P);
       } else {
         const int64_t nw = kinds * nt * a.D + (a.dbias ? nt : 0);
-        hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nw * 64)), dim3(256), 0, stream, a, a.P, 0);
+        hipLaunchKernelGGL(bwd_tables_reduce_kernel, dim3(blocks_for(nw * 64)), dim3(256), 0, stream, a, a.P);
       }
     } else {
       for (float* g : {a.drk, a.drq, a.drv})
